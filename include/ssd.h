@@ -1,0 +1,168 @@
+/*
+ * ssd.h -- C ABI of libssd: the Mamba-2 chunked SSD forward pass on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For every batch b and head h, with group g = h / (nheads /
+ * ngroups), a P x N state s (P = headdim, N = dstate) is carried across the
+ * sequence:
+ *
+ *     s_t = exp(dt_t * A_h) * s_{t-1} + dt_t * x_t (outer) B_t        (P x N)
+ *     y_t = s_t C_t + D_h * x_t                                       (length P)
+ *
+ * The output line is the recurrence y_t = c_t^T h_t + D x_t given in devin.kr
+ * "NVIDIA CUDA Tile로 Mamba-2 순방향 전달 커널 가속화", section "Mamba-2
+ * 아키텍처의 핵심 연산" (core operations); the decay a_t = dt_t A_h and its
+ * running sum G named there drive the state update, which is the standard
+ * discretised Mamba-2 update written above.  The library evaluates it chunk by
+ * chunk in three stages, the decomposition described in the same page's
+ * section "세 가지 핵심 커널 구현" (three kernels) and in brifing.si
+ * "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
+ * CUDA Tile", sections 4-9:
+ *   1. chunk_cumsum   -- within-chunk running sum of a_t, scaled by log2(e);
+ *   2. fwd_pass_state -- per-chunk states by the jump formula and the
+ *                        sequential pass of states across chunks;
+ *   3. compute_out    -- causal-masked decayed interaction tile, carried-state
+ *                        term and D skip fused, nothing chunk x chunk in HBM.
+ * The result equals the token recurrence up to floating-point rounding.
+ *
+ * Layouts.  Every tensor is dense, row-major, with no padding:
+ *     x, y                [batch, seqlen, nheads, headdim]  io dtype
+ *     B, C                [batch, seqlen, ngroups, dstate]  io dtype
+ *     dt                  [batch, seqlen, nheads]           fp32, > 0 (used as given:
+ *                                                            no bias, softplus or clamp)
+ *     A, D                [nheads]                          fp32
+ *     init_state, final_state [batch, nheads, headdim, dstate] fp32
+ * io dtype is SSD_BF16 (bf16 operands, fp32 accumulation) or SSD_F32.
+ *
+ * Ownership and ordering.  Every tensor pointer is DEVICE memory owned by the
+ * caller.  The library allocates nothing, frees nothing, never synchronises
+ * and keeps no pointer after a call returns.  Work is enqueued on `stream`
+ * (a hipStream_t; NULL = the default stream) and its results are valid once
+ * the caller has synchronised with that stream; inputs must stay unchanged
+ * until then.  y must not overlap any input.  final_state may be the same
+ * buffer as init_state (each state tile is read before it is written).
+ * Calls are reentrant; the only global state is a thread-local error message.
+ *
+ * Preconditions that are documented, not checked: dt > 0, A <= 0 (A = 0 is
+ * allowed and gives causal linear attention), all inputs finite.
+ *
+ * Errors.  Every entry point validates on the host before any HIP call and
+ * returns the first failing check in this order: SSD_ERR_NULL_POINTER (a
+ * required pointer is NULL), SSD_ERR_BAD_SHAPE (a size <= 0, nheads not a
+ * multiple of ngroups, or a size product overflowing int64), SSD_ERR_BAD_CHUNK
+ * (chunk_size not one of 32, 64, 128, 256), SSD_ERR_BAD_DTYPE,
+ * SSD_ERR_MISALIGNED (a tensor pointer not 16-byte aligned),
+ * SSD_ERR_UNSUPPORTED (headdim or dstate not a multiple of 16, or dstate >
+ * 256), SSD_ERR_WORKSPACE (workspace too small).  SSD_ERR_HIP reports a failed
+ * kernel launch.  Nothing is enqueued when a call returns an error.  No C++
+ * exception crosses this interface.  ssd_last_error_message() describes the
+ * last error of the calling thread.
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_NULL_POINTER = 1,
+  SSD_ERR_BAD_SHAPE = 2,
+  SSD_ERR_BAD_CHUNK = 3,
+  SSD_ERR_BAD_DTYPE = 4,
+  SSD_ERR_MISALIGNED = 5,
+  SSD_ERR_WORKSPACE = 6,
+  SSD_ERR_UNSUPPORTED = 7,
+  SSD_ERR_HIP = 8,
+  SSD_ERR_INTERNAL = 9
+} ssd_status;
+
+/* Problem description.  chunk_size Q splits the sequence into
+ * T = ceil(seqlen / Q) chunks; a partial last chunk is allowed. */
+typedef struct {
+  int64_t batch;
+  int64_t seqlen;
+  int64_t nheads;
+  int64_t headdim;    /* P */
+  int64_t dstate;     /* N */
+  int64_t ngroups;    /* G */
+  int64_t chunk_size; /* Q */
+  int32_t io_dtype;   /* ssd_dtype: dtype of x, B, C, y and of the chunk states */
+  int32_t reserved;   /* must be 0 */
+} ssd_problem;
+
+/* ABI version of the loaded library (SSD_ABI_VERSION at build time). */
+int ssd_abi_version(void);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* ssd_status_string(int status);
+
+/* Description of the last error returned on the calling thread ("" if none).
+ * The pointer stays valid until the thread's next libssd call. */
+const char* ssd_last_error_message(void);
+
+/* Workspace bytes that ssd_fwd and ssd_fwd_states need for `prob`:
+ * two fp32 [batch, nheads, T*Q] arrays (the base-2 running sums G and dt in
+ * [batch, head, token] order) plus the chunk-start states [batch, nheads, T,
+ * headdim, dstate] in the io dtype, each segment 256-byte aligned.
+ * Writes the size to *bytes.  Errors: NULL_POINTER, BAD_SHAPE, BAD_CHUNK,
+ * BAD_DTYPE, UNSUPPORTED. */
+ssd_status ssd_fwd_workspace_size(const ssd_problem* prob, size_t* bytes);
+
+/* Full forward pass: chunk_cumsum -> fwd_pass_state -> compute_out.
+ *   x, dt, A, B, C : inputs (device), layouts above.
+ *   D              : [nheads] fp32 skip weights, or NULL for no skip term.
+ *   init_state     : [batch, nheads, headdim, dstate] fp32, or NULL for zeros.
+ *   y              : output [batch, seqlen, nheads, headdim] in the io dtype.
+ *   final_state    : output state after the last token (fp32), or NULL.
+ *   workspace      : device scratch of at least ssd_fwd_workspace_size bytes,
+ *                    16-byte aligned, owned by the caller; its contents on
+ *                    entry do not matter.
+ *   stream         : hipStream_t to enqueue on (NULL = default stream). */
+ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                   const void* B, const void* C, const float* D, const float* init_state,
+                   void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Stage 1 alone (the chunk_cumsum step): for every (b, h) and token t in chunk
+ * c = t / Q,
+ *     G_out[b, h, t]  = log2(e) * sum_{k = cQ .. t} dt[b, k, h] * A[h]
+ *     dt_out[b, h, t] = dt[b, t, h]
+ * The within-chunk running sum of the decay a_k in base-2 log space, and dt
+ * moved to [batch, head, token] order so later stages read tokens
+ * contiguously (devin.kr page above, section "세 가지 핵심 커널 구현",
+ * chunk_cumsum, and section "cuTile 기반 성능 최적화 기법" (optimisations),
+ * the [batch, head, token] layout).  G_out, dt_out: [batch, nheads, seqlen]
+ * fp32 device buffers.  Errors as for ssd_fwd (no workspace). */
+ssd_status ssd_chunk_cumsum(const ssd_problem* prob, const float* dt, const float* A,
+                            float* G_out, float* dt_out, void* stream);
+
+/* Stages 1 and 2 (chunk_cumsum and fwd_pass_state): the state at the start of
+ * every chunk and the state after the last token, without computing y
+ * (devin.kr page above, section "세 가지 핵심 커널 구현", fwd_pass_state;
+ * brifing.si page, sections 4, 5 and 8).  Chunk c's contribution is one matrix
+ * product over the chunk's stacked x and B rows, each row weighted by
+ * exp2(G_last - G_j) * dt_j; states pass on as
+ * H_{c+1} = exp2(G_last) * H_c + S_c, with H_0 = init_state (or zero).
+ *   chunk_states : output [batch, nheads, T, headdim, dstate] in the io dtype
+ *                  (H_c for c = 0..T-1), or NULL.
+ *   final_state  : output [batch, nheads, headdim, dstate] fp32 (required).
+ * Other arguments as for ssd_fwd. */
+ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* dt,
+                          const float* A, const void* B, const float* init_state,
+                          float* final_state, void* chunk_states, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

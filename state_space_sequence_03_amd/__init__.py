@@ -1,0 +1,237 @@
+"""libssd Python binding: the Mamba-2 chunked SSD forward pass on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libssd.so`` (built in-tree by ``state_space_sequence_03_amd.build``);
+PyTorch provides device memory and the current stream.  There is no CPU or
+PyTorch fallback: importing works without the library, but every call raises
+if ``libssd.so`` is missing or the tensors are not on a GPU.
+
+Names match the C ABI in include/ssd.h:
+    ssd_fwd, ssd_fwd_states, ssd_chunk_cumsum, ssd_fwd_workspace_size,
+    ssd_status_string, ssd_last_error_message, ssd_abi_version
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["SsdError", "SsdArgumentError", "lib_path", "load_library", "make_problem",
+           "ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
+           "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_states", "ssd_chunk_cumsum",
+           "SSD_F32", "SSD_BF16"]
+
+SSD_F32, SSD_BF16 = 0, 1
+_STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_BAD_SHAPE",
+                 3: "SSD_ERR_BAD_CHUNK", 4: "SSD_ERR_BAD_DTYPE", 5: "SSD_ERR_MISALIGNED",
+                 6: "SSD_ERR_WORKSPACE", 7: "SSD_ERR_UNSUPPORTED", 8: "SSD_ERR_HIP",
+                 9: "SSD_ERR_INTERNAL"}
+_ARG_ERRORS = {1, 2, 3, 4, 5, 6, 7}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssd.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class SsdError(RuntimeError):
+    """A libssd call failed at run time (HIP or internal error)."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__("%s: %s" % (_STATUS_NAMES.get(status, str(status)), message))
+
+
+class SsdArgumentError(SsdError, ValueError):
+    """A libssd call rejected its arguments (nothing was enqueued)."""
+
+
+class ssd_problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk_size", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Open libssd.so and declare its entry points (raises if not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libssd.so is not built (run python -m state_space_sequence_03_amd.build)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, vp, sz = ctypes.POINTER(ssd_problem), ctypes.c_void_p, ctypes.c_size_t
+        lib.ssd_abi_version.restype = ctypes.c_int
+        lib.ssd_abi_version.argtypes = []
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        lib.ssd_status_string.argtypes = [ctypes.c_int]
+        lib.ssd_last_error_message.restype = ctypes.c_char_p
+        lib.ssd_last_error_message.argtypes = []
+        lib.ssd_fwd_workspace_size.restype = ctypes.c_int
+        lib.ssd_fwd_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+        lib.ssd_fwd.restype = ctypes.c_int
+        lib.ssd_fwd.argtypes = [P] + [vp] * 10 + [sz, vp]
+        lib.ssd_chunk_cumsum.restype = ctypes.c_int
+        lib.ssd_chunk_cumsum.argtypes = [P] + [vp] * 5
+        lib.ssd_fwd_states.restype = ctypes.c_int
+        lib.ssd_fwd_states.argtypes = [P] + [vp] * 8 + [sz, vp]
+        _lib = lib
+        return lib
+
+
+def ssd_abi_version() -> int:
+    return int(load_library().ssd_abi_version())
+
+
+def ssd_status_string(status: int) -> str:
+    return load_library().ssd_status_string(int(status)).decode()
+
+
+def ssd_last_error_message() -> str:
+    return load_library().ssd_last_error_message().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = ssd_last_error_message()
+        if status in _ARG_ERRORS:
+            raise SsdArgumentError(status, msg)
+        raise SsdError(status, msg)
+
+
+def make_problem(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, io_dtype) -> ssd_problem:
+    return ssd_problem(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate),
+                       int(ngroups), int(chunk_size), int(io_dtype), 0)
+
+
+def ssd_fwd_workspace_size(prob: ssd_problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ssd_fwd_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _io_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise SsdArgumentError(4, "x, B and C must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SsdArgumentError(1, "%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise SsdArgumentError(2, "%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise SsdArgumentError(4, "%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _problem_of(x, B, chunk_size) -> ssd_problem:
+    if x.dim() != 4 or B.dim() != 4:
+        raise SsdArgumentError(2, "x must be [batch, seqlen, nheads, headdim] and B/C "
+                                  "[batch, seqlen, ngroups, dstate]")
+    bsz, L, H, P = x.shape
+    if B.shape[0] != bsz or B.shape[1] != L:
+        raise SsdArgumentError(2, "B/C batch and seqlen must match x")
+    return make_problem(bsz, L, H, P, B.shape[3], B.shape[2], chunk_size, _io_code(x))
+
+
+def _workspace(prob, device, workspace):
+    need = ssd_fwd_workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+            C: torch.Tensor, D: Optional[torch.Tensor] = None, chunk_size: int = 256,
+            init_state: Optional[torch.Tensor] = None, *, want_final_state: bool = True,
+            out: Optional[torch.Tensor] = None, final_out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Full forward pass on the current stream.  Returns (y, final_state)."""
+    lib = load_library()
+    prob = _problem_of(x, B, chunk_size)
+    if x.dtype != B.dtype or x.dtype != C.dtype:
+        raise SsdArgumentError(4, "x, B and C must share one dtype")
+    if tuple(dt.shape) != tuple(x.shape[:3]) or A.shape != (x.shape[2],):
+        raise SsdArgumentError(2, "dt must be [batch, seqlen, nheads] and A [nheads]")
+    if tuple(C.shape) != tuple(B.shape):
+        raise SsdArgumentError(2, "C must have the shape of B")
+    if D is not None and D.shape != (x.shape[2],):
+        raise SsdArgumentError(2, "D must be [nheads]")
+    state_shape = (x.shape[0], x.shape[2], x.shape[3], B.shape[3])
+    if init_state is not None and tuple(init_state.shape) != state_shape:
+        raise SsdArgumentError(2, "init_state must be [batch, nheads, headdim, dstate]")
+    y = out if out is not None else torch.empty_like(x)
+    if tuple(y.shape) != tuple(x.shape) or y.dtype != x.dtype:
+        raise SsdArgumentError(2, "out must match x")
+    fin = None
+    if want_final_state:
+        fin = final_out if final_out is not None else torch.empty(
+            state_shape, dtype=torch.float32, device=x.device)
+    ws, ws_bytes = _workspace(prob, x.device, workspace)
+    st = lib.ssd_fwd(ctypes.byref(prob), _dev(x, "x"), _dev(dt, "dt", torch.float32),
+                     _dev(A, "A", torch.float32), _dev(B, "B"), _dev(C, "C"),
+                     _dev(D, "D", torch.float32), _dev(init_state, "init_state", torch.float32),
+                     _dev(y, "y"), _dev(fin, "final_state", torch.float32), _dev(ws, "workspace"),
+                     ws_bytes, _stream(x.device))
+    _check(st)
+    return y, fin
+
+
+def ssd_fwd_states(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                   chunk_size: int = 256, init_state: Optional[torch.Tensor] = None, *,
+                   want_chunk_states: bool = True,
+                   workspace: Optional[torch.Tensor] = None):
+    """Stages 1-2 only.  Returns (final_state fp32, chunk_states [B,H,T,P,N] or None)."""
+    lib = load_library()
+    prob = _problem_of(x, B, chunk_size)
+    if x.dtype != B.dtype:
+        raise SsdArgumentError(4, "x and B must share one dtype")
+    bsz, L, H, P = x.shape
+    N = B.shape[3]
+    T = -(-L // int(chunk_size)) if chunk_size > 0 else 0
+    fin = torch.empty((bsz, H, P, N), dtype=torch.float32, device=x.device)
+    cs = torch.empty((bsz, H, T, P, N), dtype=x.dtype, device=x.device) if want_chunk_states else None
+    ws, ws_bytes = _workspace(prob, x.device, workspace)
+    st = lib.ssd_fwd_states(ctypes.byref(prob), _dev(x, "x"), _dev(dt, "dt", torch.float32),
+                            _dev(A, "A", torch.float32), _dev(B, "B"),
+                            _dev(init_state, "init_state", torch.float32),
+                            _dev(fin, "final_state", torch.float32), _dev(cs, "chunk_states"),
+                            _dev(ws, "workspace"), ws_bytes, _stream(x.device))
+    _check(st)
+    return fin, cs
+
+
+def ssd_chunk_cumsum(dt: torch.Tensor, A: torch.Tensor, chunk_size: int = 256):
+    """Stage 1 only.  Returns (G, dt_t), both [batch, nheads, seqlen] fp32."""
+    lib = load_library()
+    if dt.dim() != 3:
+        raise SsdArgumentError(2, "dt must be [batch, seqlen, nheads]")
+    bsz, L, H = dt.shape
+    prob = make_problem(bsz, L, H, 16, 16, 1, chunk_size, SSD_F32)
+    G = torch.empty((bsz, H, L), dtype=torch.float32, device=dt.device)
+    dtt = torch.empty_like(G)
+    st = lib.ssd_chunk_cumsum(ctypes.byref(prob), _dev(dt, "dt", torch.float32),
+                              _dev(A, "A", torch.float32), _dev(G, "G_out"), _dev(dtt, "dt_out"),
+                              _stream(dt.device))
+    _check(st)
+    return G, dtt

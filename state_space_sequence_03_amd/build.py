@@ -1,0 +1,65 @@
+"""Build libssd.so (gfx950) in-tree with hipcc.
+
+Usage: python -m state_space_sequence_03_amd.build   (or call build()).
+Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
+generation switched off for device code, and linked with the host-side ABI
+into state_space_sequence_03_amd/libssd.so.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB_PATH = os.path.join(HERE, "libssd.so")
+
+SOURCES = ["chunk_cumsum.hip", "fwd_pass_state.hip", "compute_out.hip", "ssd_api.cpp"]
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON_FLAGS = [
+    "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
+    "--offload-arch=" + ARCH,
+    # keep the compiler from emitting packed fp32 VALU ops in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + os.path.join(ROOT, "include"),
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    cmd = [HIPCC] + COMMON_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in res.stderr.splitlines()
+                     if "packed-fp32-ops" not in l and l.strip())
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, errs))
+    if errs.strip():
+        sys.stderr.write(errs + "\n")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libssd.so; returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + res.stderr)
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print("built", LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,271 @@
+// ssd_api.cpp -- host side of libssd: validation, workspace plan, launches.
+//
+// Every entry point validates its arguments on the host, in the order the
+// public header documents, before making any HIP call; on success it
+// enqueues the stage kernels on the caller's stream and returns without
+// synchronising.  No exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <string>
+
+#include "../../include/ssd.h"
+
+namespace ssd {
+hipError_t launch_chunk_cumsum(const float* dt, const float* A, float* G, float* dtT,
+                               int64_t batch, int64_t L, int64_t H, int Q, int64_t ld,
+                               int64_t Lw, hipStream_t stream);
+hipError_t launch_fwd_pass_state(int io_bf16, const void* x, const void* Bm, const float* Gw,
+                                 const float* dtw, const float* init_state, float* final_state,
+                                 void* Hc, int64_t batch, int64_t L, int64_t H, int64_t P,
+                                 int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
+                                 hipStream_t stream);
+hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
+                              const float* Gw, const float* dtw, const void* Hc, const float* Dv,
+                              void* y, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                              int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream);
+int compute_out_smem_bytes(int io_bf16, int Q, int64_t N);
+}  // namespace ssd
+
+namespace {
+
+constexpr int64_t kMaxLds = 160 * 1024;
+thread_local std::string g_last_error;
+
+ssd_status fail(ssd_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ssd_status fail(ssd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ssd_status ok() {
+  g_last_error.clear();
+  return SSD_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+  int64_t B, L, H, P, N, G, Q, T, Lp;
+  int bf16;
+  size_t esize;
+  size_t g_off, dt_off, hc_off, bytes;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Shape checks shared by every entry point (after the NULL checks).
+ssd_status plan_problem(const ssd_problem* prob, Plan* pl) {
+  const ssd_problem& p = *prob;
+  if (p.batch <= 0 || p.seqlen <= 0 || p.nheads <= 0 || p.headdim <= 0 || p.dstate <= 0 ||
+      p.ngroups <= 0 || p.chunk_size <= 0)
+    return fail(SSD_ERR_BAD_SHAPE, "every size must be positive");
+  if (p.nheads % p.ngroups != 0)
+    return fail(SSD_ERR_BAD_SHAPE, "nheads (%lld) must be a multiple of ngroups (%lld)",
+                (long long)p.nheads, (long long)p.ngroups);
+  int64_t t1, t2, t3;
+  if (!mul_ok(p.batch, p.seqlen, &t1) || !mul_ok(t1, p.nheads, &t2) ||
+      !mul_ok(t2, p.headdim, &t3) || !mul_ok(t1, p.ngroups, &t2) || !mul_ok(t2, p.dstate, &t3))
+    return fail(SSD_ERR_BAD_SHAPE, "tensor size overflows int64");
+  if (p.seqlen > INT64_MAX / 2 - 256)
+    return fail(SSD_ERR_BAD_SHAPE, "seqlen too large");
+  const int64_t Q = p.chunk_size;
+  if (!(Q == 32 || Q == 64 || Q == 128 || Q == 256))
+    return fail(SSD_ERR_BAD_CHUNK, "chunk_size must be 32, 64, 128 or 256 (got %lld)", (long long)Q);
+  if (p.io_dtype != SSD_BF16 && p.io_dtype != SSD_F32)
+    return fail(SSD_ERR_BAD_DTYPE, "io_dtype must be SSD_BF16 or SSD_F32 (got %d)", p.io_dtype);
+  if (p.reserved != 0) return fail(SSD_ERR_BAD_DTYPE, "reserved field must be 0");
+  pl->B = p.batch; pl->L = p.seqlen; pl->H = p.nheads; pl->P = p.headdim; pl->N = p.dstate;
+  pl->G = p.ngroups; pl->Q = Q;
+  pl->T = (p.seqlen + Q - 1) / Q;
+  pl->Lp = pl->T * Q;
+  pl->bf16 = p.io_dtype == SSD_BF16;
+  pl->esize = pl->bf16 ? 2 : 4;
+  return SSD_OK;
+}
+
+// Limits of the kernels (checked after alignment, as the header documents).
+ssd_status check_supported(const Plan& pl) {
+  if (pl.P % 16 != 0 || pl.N % 16 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "headdim (%lld) and dstate (%lld) must be multiples of 16",
+                (long long)pl.P, (long long)pl.N);
+  if (pl.N > 256) return fail(SSD_ERR_UNSUPPORTED, "dstate must be <= 256 (got %lld)", (long long)pl.N);
+  if (pl.B * pl.H > INT32_MAX / 64 || pl.B * pl.T > INT32_MAX / 64 || pl.H > 65535 ||
+      pl.B > 65535 || pl.T > INT32_MAX / 8)
+    return fail(SSD_ERR_UNSUPPORTED, "grid too large for this build");
+  if (ssd::compute_out_smem_bytes(pl.bf16, (int)pl.Q, pl.N) > kMaxLds)
+    return fail(SSD_ERR_UNSUPPORTED, "fp32 io with chunk_size %lld and dstate %lld exceeds LDS",
+                (long long)pl.Q, (long long)pl.N);
+  return SSD_OK;
+}
+
+void workspace_plan(Plan* pl) {
+  const size_t gsz = size_t(pl->B) * pl->H * pl->Lp * sizeof(float);
+  pl->g_off = 0;
+  pl->dt_off = align256(gsz);
+  pl->hc_off = pl->dt_off + align256(gsz);
+  const size_t hcsz = size_t(pl->B) * pl->H * pl->T * pl->P * pl->N * pl->esize;
+  pl->bytes = pl->hc_off + align256(hcsz);
+}
+
+ssd_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(SSD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_status_string(int status) {
+  switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL_POINTER: return "required pointer is NULL";
+    case SSD_ERR_BAD_SHAPE: return "invalid problem shape";
+    case SSD_ERR_BAD_CHUNK: return "unsupported chunk size";
+    case SSD_ERR_BAD_DTYPE: return "invalid io dtype";
+    case SSD_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case SSD_ERR_WORKSPACE: return "workspace too small";
+    case SSD_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case SSD_ERR_HIP: return "HIP runtime error";
+    case SSD_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+const char* ssd_last_error_message(void) { return g_last_error.c_str(); }
+
+ssd_status ssd_fwd_workspace_size(const ssd_problem* prob, size_t* bytes) {
+  try {
+    if (!prob || !bytes) return fail(SSD_ERR_NULL_POINTER, "prob and bytes must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl);
+    if (st != SSD_OK) return st;
+    st = check_supported(pl);
+    if (st != SSD_OK) return st;
+    workspace_plan(&pl);
+    *bytes = pl.bytes;
+    return ok();
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_problem* prob, const float* dt, const float* A,
+                            float* G_out, float* dt_out, void* stream) {
+  try {
+    if (!prob || !dt || !A || !G_out || !dt_out)
+      return fail(SSD_ERR_NULL_POINTER, "prob, dt, A, G_out and dt_out must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl);
+    if (st != SSD_OK) return st;
+    if (!aligned16(dt) || !aligned16(A) || !aligned16(G_out) || !aligned16(dt_out))
+      return fail(SSD_ERR_MISALIGNED, "dt, A, G_out and dt_out must be 16-byte aligned");
+    st = check_supported(pl);
+    if (st != SSD_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(ssd::launch_chunk_cumsum(dt, A, G_out, dt_out, pl.B, pl.L, pl.H, (int)pl.Q,
+                                               pl.L, pl.L, s),
+                      "chunk_cumsum launch");
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+static ssd_status run_states(const Plan& pl, const void* x, const float* dt, const float* A,
+                             const void* B, const float* init_state, float* final_state,
+                             void* chunk_states, void* workspace, hipStream_t s) {
+  char* ws = static_cast<char*>(workspace);
+  float* Gw = reinterpret_cast<float*>(ws + pl.g_off);
+  float* dtw = reinterpret_cast<float*>(ws + pl.dt_off);
+  void* Hc = chunk_states ? chunk_states : static_cast<void*>(ws + pl.hc_off);
+  hipError_t e = ssd::launch_chunk_cumsum(dt, A, Gw, dtw, pl.B, pl.L, pl.H, (int)pl.Q, pl.Lp,
+                                          pl.Lp, s);
+  if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
+  e = ssd::launch_fwd_pass_state(pl.bf16, x, B, Gw, dtw, init_state, final_state, Hc, pl.B, pl.L,
+                                 pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp, s);
+  return hip_status(e, "fwd_pass_state launch");
+}
+
+ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* dt,
+                          const float* A, const void* B, const float* init_state,
+                          float* final_state, void* chunk_states, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  try {
+    if (!prob || !x || !dt || !A || !B || !final_state || !workspace)
+      return fail(SSD_ERR_NULL_POINTER,
+                  "prob, x, dt, A, B, final_state and workspace must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl);
+    if (st != SSD_OK) return st;
+    if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) ||
+        !aligned16(init_state) || !aligned16(final_state) || !aligned16(chunk_states) ||
+        !aligned16(workspace))
+      return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
+    st = check_supported(pl);
+    if (st != SSD_OK) return st;
+    workspace_plan(&pl);
+    if (workspace_bytes < pl.bytes)
+      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+    st = run_states(pl, x, dt, A, B, init_state, final_state, chunk_states, workspace,
+                    static_cast<hipStream_t>(stream));
+    return st;
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                   const void* B, const void* C, const float* D, const float* init_state,
+                   void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  try {
+    if (!prob || !x || !dt || !A || !B || !C || !y || !workspace)
+      return fail(SSD_ERR_NULL_POINTER, "prob, x, dt, A, B, C, y and workspace must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl);
+    if (st != SSD_OK) return st;
+    if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
+        !aligned16(D) || !aligned16(init_state) || !aligned16(y) || !aligned16(final_state) ||
+        !aligned16(workspace))
+      return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
+    st = check_supported(pl);
+    if (st != SSD_OK) return st;
+    workspace_plan(&pl);
+    if (workspace_bytes < pl.bytes)
+      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_states(pl, x, dt, A, B, init_state, final_state, nullptr, workspace, s);
+    if (st != SSD_OK) return st;
+    char* ws = static_cast<char*>(workspace);
+    const float* Gw = reinterpret_cast<const float*>(ws + pl.g_off);
+    const float* dtw = reinterpret_cast<const float*>(ws + pl.dt_off);
+    const void* Hc = ws + pl.hc_off;
+    return hip_status(ssd::launch_compute_out(pl.bf16, x, B, C, Gw, dtw, Hc, D, y, pl.B, pl.L,
+                                              pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp, s),
+                      "compute_out launch");
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+}  // extern "C"
