@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Throughput of the Mamba-2 chunked SSD forward pass (libssd) on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+chunk_cumsum -> fwd_pass_state -> compute_out, enqueued through the C ABI
+(ssd_fwd_states, then ssd_compute_out -- exactly the launches ssd_fwd makes;
+the split lets HIP events bracket the dominant kernel inside the timed loop).
+Inputs are resident in HBM before timing starts.  Prints one JSON line.
+
+Default workload: the Mamba-2 2.7B-shaped layer, batch 2 x seqlen 8192,
+80 heads, headdim 64, dstate 128, 1 group, chunk 256, bf16 x/B/C, fp32
+dt/A/D and a nonzero fp32 initial state.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-probe       (plain copy kernel, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_MFMA = 2.5e15     # dense bf16 MFMA, MI355X published
+PEAK_FP32_MFMA = 157.3e12   # dense fp32 MFMA
+PEAK_HBM = 8.0e12           # HBM3E bytes/s
+METRIC = "SSD fwd tokens/sec (batch·seqlen) at 1 MI355X; % of bf16 MFMA roofline"
+COPY_PROBE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compute_out_{workload}_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "state_space_sequence_03_amd", "csrc", f)
+                  for f in ("compute_out.hip", "ssd_device.hpp")]
+
+
+def counts(p):
+    """Algorithmic flops and bytes (see the measurement section of the design doc)."""
+    Bz, L, H, P, N, G, Q = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups, p.chunk_size
+    T = -(-L // Q)
+    Lp = T * Q
+    e = 2 if p.io_dtype == "bf16" else 4
+    per_chunk_head_intra = Q * (Q + 1) * (N + P)        # causal C B^T and S x
+    per_chunk_head_state = 2 * Q * P * N                # one of: chunk state, C H^T
+    f_path = Bz * H * T * (per_chunk_head_intra + 2 * per_chunk_head_state)
+    f_out = Bz * H * T * (per_chunk_head_intra + per_chunk_head_state)
+    init = 1 if p.init_std is not None else 0
+    b_min = (2 * Bz * L * H * P * e + 2 * Bz * L * G * N * e + 4 * Bz * L * H + 8 * H
+             + 4 * Bz * H * P * N * (1 + init))
+    b_out = (2 * Bz * L * H * P * e            # x read, y written
+             + Bz * H * T * P * N * e          # chunk-start states read
+             + 2 * 4 * Bz * H * Lp             # G and dt in [b, h, token] order
+             + 2 * Bz * L * G * N * e          # B and C rows
+             + 4 * H)                          # D
+    return dict(f_path=f_path, f_out=f_out, b_min=b_min, b_out=b_out,
+                units_out=Bz * H * T, tokens=Bz * L)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per compute_out launch from committed rocprofv3 counters, or None
+    when the file is missing or the kernel source changed since it was taken."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inputs, prob, target_seconds=15.0):
+    """Time the fp64 oracle (the token recurrence, OpenMP over (batch, head)) on
+    the host, on a bounded sample of the workload: the first `nh` heads of every
+    batch over the whole sequence, sized from a short probe to take about
+    `target_seconds`, or the whole workload when that fits.  Tokens/s is scaled
+    to the full head count."""
+    import oracle
+
+    nthreads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    arrs = {k: (None if v is None else oracle.as_f32(v)) for k, v in inputs.items()}
+    H, hpg = prob.nheads, prob.nheads // prob.ngroups
+
+    def run(nh):
+        g = max(1, nh // hpg)
+        sel = lambda a: a[:, :, :nh]
+        init = arrs["init_state"]
+        t0 = time.perf_counter()
+        oracle.recurrence(sel(arrs["x"]), sel(arrs["dt"]), arrs["A"][:nh], arrs["B"][:, :, :g],
+                          arrs["C"][:, :, :g], arrs["D"][:nh],
+                          None if init is None else init[:, :nh], nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    def legal(nh):   # head counts whose group mapping matches the full problem
+        nh = max(1, min(H, nh))
+        return nh if nh <= hpg else nh // hpg * hpg
+
+    probe_heads = legal(min(H, max(1, nthreads // max(1, prob.batch))))
+    probe = run(probe_heads)
+    nh = legal(int(target_seconds / max(probe, 1e-6) * probe_heads))
+    dt = run(nh)
+    tok_s = prob.batch * prob.seqlen * (nh / H) / dt
+    sample = ("full workload: %d (batch, head) pairs x %d tokens" % (prob.batch * H, prob.seqlen)
+              if nh == H else
+              "heads 0..%d of %d in each of %d batches, %d tokens each; tokens/s scaled by %d/%d"
+              % (nh - 1, H, prob.batch, prob.seqlen, nh, H))
+    return {"value": tok_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def copy_probe():
+    import torch
+    n = COPY_PROBE_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": COPY_PROBE_BYTES, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mamba2_2p7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ssd_synth
+    import state_space_sequence_03_amd as ssd
+
+    if args.copy_probe:
+        copy_probe()
+        return
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.workload not in ssd_synth.CONFIGS:
+        print("unknown workload %r (choose from %s)" % (args.workload, ", ".join(ssd_synth.CONFIGS)),
+              file=sys.stderr)
+        sys.exit(2)
+    prob = ssd_synth.CONFIGS[args.workload]
+    seed = ssd_synth.CONFIG_ORDER.index(args.workload)
+    inputs = ssd_synth.make_inputs(prob, seed)
+    dev = torch.device("cuda:0")
+    d = {k: (None if v is None else v.to(dev)) for k, v in inputs.items()}
+    Q = prob.chunk_size
+    pr = ssd.make_problem(prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate,
+                          prob.ngroups, Q, ssd.SSD_BF16 if prob.io_dtype == "bf16" else ssd.SSD_F32)
+    ws = torch.empty(ssd.ssd_fwd_workspace_size(pr), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(d["x"])
+    fin = torch.empty((prob.batch, prob.nheads, prob.headdim, prob.dstate), dtype=torch.float32,
+                      device=dev)
+
+    def step(ev_a=None, ev_b=None, ev_c=None):
+        if ev_a is not None:
+            ev_a.record()
+        ssd.ssd_fwd_states(d["x"], d["dt"], d["A"], d["B"], Q, d["init_state"],
+                           want_chunk_states=False, workspace=ws, final_out=fin)
+        if ev_b is not None:
+            ev_b.record()
+        ssd.ssd_compute_out(d["x"], d["B"], d["C"], d["D"], Q, ws, out=y)
+        if ev_c is not None:
+            ev_c.record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(*ev[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / K
+    ms_states = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    ms_out = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+
+    # same steps with the 256 MB last-level cache flushed before each (event-timed)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for k in range(min(K, 20)):
+        flush.fill_(k & 0xFF)
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        step(a, b, c)
+        torch.cuda.synchronize()
+        cold.append((a.elapsed_time(c), a.elapsed_time(b), b.elapsed_time(c)))
+    del flush
+    cold.sort()
+    cold_med = cold[len(cold) // 2]
+
+    cnt = counts(prob)
+    tok_s = cnt["tokens"] / (ms_step * 1e-3)
+    peak_mfma = PEAK_BF16_MFMA if prob.io_dtype == "bf16" else PEAK_FP32_MFMA
+    t_out = ms_out * 1e-3
+    out_tflops = cnt["f_out"] / t_out
+    out_gbs = cnt["b_out"] / t_out
+    # compute_out's bound: whichever roofline gives the longer lower bound
+    if cnt["b_out"] / PEAK_HBM >= cnt["f_out"] / peak_mfma:
+        bound, achieved, peak, unit = "hbm", out_gbs / 1e9, PEAK_HBM / 1e9, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", out_tflops / 1e12, peak_mfma / 1e12, "TFLOP/s"
+    traffic = read_traffic(args.workload)
+
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prob.io_dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": prob.batch, "seqlen": prob.seqlen,
+                   "nheads": prob.nheads, "headdim": prob.headdim, "dstate": prob.dstate,
+                   "ngroups": prob.ngroups, "chunk_size": Q,
+                   "init_state": prob.init_std is not None, "accumulate": "fp32"},
+        "path_mfma_frac": cnt["f_path"] / (ms_step * 1e-3) / peak_mfma,
+        "path_hbm_frac": cnt["b_min"] / (ms_step * 1e-3) / PEAK_HBM,
+        "path_tflops": cnt["f_path"] / (ms_step * 1e-3) / 1e12,
+        "stage_ms": {"chunk_cumsum+fwd_pass_state": ms_states, "compute_out": ms_out},
+        "cold_ms_per_step": {"median": cold_med[0], "states": cold_med[1], "compute_out": cold_med[2]},
+        "roofline": {"kernel": "compute_out", "bound": bound, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak,
+                     "traffic": traffic,
+                     "mfma_frac": out_tflops / peak_mfma, "hbm_frac": out_gbs / PEAK_HBM},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inputs, prob)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -161,6 +161,24 @@ ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* d
                           float* final_state, void* chunk_states, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Stage 3 alone (compute_out): y from the inputs and from the running sums and
+ * chunk-start states that a preceding ssd_fwd_states call left in `workspace`
+ * (same problem, same workspace, chunk_states == NULL, enqueued earlier on
+ * the same stream or otherwise ordered before this call).  For token i of a
+ * chunk: y_i = sum_{j<=i} (C_i . B_j) exp2(G_i - G_j) dt_j x_j
+ *            + exp2(G_i) H_c C_i + D_h x_i,
+ * the fused carried-state term, causal interaction tile and skip of devin.kr
+ * "NVIDIA CUDA Tile로 Mamba-2 순방향 전달 커널 가속화", section "세 가지 핵심
+ * 커널 구현", compute_out, and brifing.si "Accelerating Mamba-2 ...", sections
+ * 9 and 11; the chunk x chunk tile is never written to memory.
+ * ssd_fwd is exactly ssd_fwd_states followed by ssd_compute_out.
+ *   x, B, C, D, y : as for ssd_fwd (D may be NULL).
+ *   workspace     : read only; at least ssd_fwd_workspace_size bytes.
+ * Errors as for ssd_fwd. */
+ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B, const void* C,
+                           const float* D, void* y, const void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,7 @@ PyTorch fallback: importing works without the library, but every call raises
 if ``libssd.so`` is missing or the tensors are not on a GPU.
 
 Names match the C ABI in include/ssd.h:
-    ssd_fwd, ssd_fwd_states, ssd_chunk_cumsum, ssd_fwd_workspace_size,
+    ssd_fwd, ssd_fwd_states, ssd_compute_out, ssd_chunk_cumsum, ssd_fwd_workspace_size,
     ssd_status_string, ssd_last_error_message, ssd_abi_version
 """
 from __future__ import annotations
@@ -21,7 +21,8 @@ import torch
 
 __all__ = ["SsdError", "SsdArgumentError", "lib_path", "load_library", "make_problem",
            "ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
-           "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_states", "ssd_chunk_cumsum",
+           "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_states", "ssd_compute_out",
+           "ssd_chunk_cumsum",
            "SSD_F32", "SSD_BF16"]
 
 SSD_F32, SSD_BF16 = 0, 1
@@ -85,6 +86,8 @@ def load_library():
         lib.ssd_chunk_cumsum.argtypes = [P] + [vp] * 5
         lib.ssd_fwd_states.restype = ctypes.c_int
         lib.ssd_fwd_states.argtypes = [P] + [vp] * 8 + [sz, vp]
+        lib.ssd_compute_out.restype = ctypes.c_int
+        lib.ssd_compute_out.argtypes = [P] + [vp] * 6 + [sz, vp]
         _lib = lib
         return lib
 
@@ -200,7 +203,8 @@ def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
 def ssd_fwd_states(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                    chunk_size: int = 256, init_state: Optional[torch.Tensor] = None, *,
                    want_chunk_states: bool = True,
-                   workspace: Optional[torch.Tensor] = None):
+                   workspace: Optional[torch.Tensor] = None,
+                   final_out: Optional[torch.Tensor] = None):
     """Stages 1-2 only.  Returns (final_state fp32, chunk_states [B,H,T,P,N] or None)."""
     lib = load_library()
     prob = _problem_of(x, B, chunk_size)
@@ -209,7 +213,8 @@ def ssd_fwd_states(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
     bsz, L, H, P = x.shape
     N = B.shape[3]
     T = -(-L // int(chunk_size)) if chunk_size > 0 else 0
-    fin = torch.empty((bsz, H, P, N), dtype=torch.float32, device=x.device)
+    fin = final_out if final_out is not None else torch.empty((bsz, H, P, N), dtype=torch.float32,
+                                                              device=x.device)
     cs = torch.empty((bsz, H, T, P, N), dtype=x.dtype, device=x.device) if want_chunk_states else None
     ws, ws_bytes = _workspace(prob, x.device, workspace)
     st = lib.ssd_fwd_states(ctypes.byref(prob), _dev(x, "x"), _dev(dt, "dt", torch.float32),
@@ -219,6 +224,23 @@ def ssd_fwd_states(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
                             _dev(ws, "workspace"), ws_bytes, _stream(x.device))
     _check(st)
     return fin, cs
+
+
+def ssd_compute_out(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                    D: Optional[torch.Tensor], chunk_size: int, workspace: torch.Tensor, *,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Stage 3 only, from a workspace filled by ssd_fwd_states(..., workspace=ws,
+    want_chunk_states=False) on the same stream.  Returns y."""
+    lib = load_library()
+    prob = _problem_of(x, B, chunk_size)
+    if x.dtype != B.dtype or x.dtype != C.dtype:
+        raise SsdArgumentError(4, "x, B and C must share one dtype")
+    y = out if out is not None else torch.empty_like(x)
+    st = lib.ssd_compute_out(ctypes.byref(prob), _dev(x, "x"), _dev(B, "B"), _dev(C, "C"),
+                             _dev(D, "D", torch.float32), _dev(y, "y"), _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(x.device))
+    _check(st)
+    return y
 
 
 def ssd_chunk_cumsum(dt: torch.Tensor, A: torch.Tensor, chunk_size: int = 256):

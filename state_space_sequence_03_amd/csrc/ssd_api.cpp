@@ -234,6 +234,40 @@ ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* d
   }
 }
 
+static ssd_status run_out(const Plan& pl, const void* x, const void* B, const void* C,
+                          const float* D, void* y, const void* workspace, hipStream_t s) {
+  const char* ws = static_cast<const char*>(workspace);
+  const float* Gw = reinterpret_cast<const float*>(ws + pl.g_off);
+  const float* dtw = reinterpret_cast<const float*>(ws + pl.dt_off);
+  const void* Hc = ws + pl.hc_off;
+  return hip_status(ssd::launch_compute_out(pl.bf16, x, B, C, Gw, dtw, Hc, D, y, pl.B, pl.L, pl.H,
+                                            pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp, s),
+                    "compute_out launch");
+}
+
+ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B, const void* C,
+                           const float* D, void* y, const void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  try {
+    if (!prob || !x || !B || !C || !y || !workspace)
+      return fail(SSD_ERR_NULL_POINTER, "prob, x, B, C, y and workspace must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl);
+    if (st != SSD_OK) return st;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(D) || !aligned16(y) ||
+        !aligned16(workspace))
+      return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
+    st = check_supported(pl);
+    if (st != SSD_OK) return st;
+    workspace_plan(&pl);
+    if (workspace_bytes < pl.bytes)
+      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+    return run_out(pl, x, B, C, D, y, workspace, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, const float* A,
                    const void* B, const void* C, const float* D, const float* init_state,
                    void* y, float* final_state, void* workspace, size_t workspace_bytes,
@@ -256,13 +290,7 @@ ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, cons
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = run_states(pl, x, dt, A, B, init_state, final_state, nullptr, workspace, s);
     if (st != SSD_OK) return st;
-    char* ws = static_cast<char*>(workspace);
-    const float* Gw = reinterpret_cast<const float*>(ws + pl.g_off);
-    const float* dtw = reinterpret_cast<const float*>(ws + pl.dt_off);
-    const void* Hc = ws + pl.hc_off;
-    return hip_status(ssd::launch_compute_out(pl.bf16, x, B, C, Gw, dtw, Hc, D, y, pl.B, pl.L,
-                                              pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp, s),
-                      "compute_out launch");
+    return run_out(pl, x, B, C, D, y, workspace, s);
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
   }

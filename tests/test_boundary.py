@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(so):
     names = declared_functions()
     assert set(names) == {"ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
                           "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk_cumsum",
-                          "ssd_fwd_states"}
+                          "ssd_fwd_states", "ssd_compute_out"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
@@ -154,3 +154,12 @@ def test_python_binding_rejects_cpu_tensors(so):
     B = torch.zeros(1, 64, 1, 16, dtype=torch.bfloat16)
     with pytest.raises(lib.SsdArgumentError):
         lib.ssd_fwd(x, torch.ones(1, 64, 2), -torch.ones(2), B, B, None, 64)
+
+
+def test_compute_out_validation(so):
+    prob = P()
+    assert so.ssd_compute_out(ctypes.byref(prob), FAKE, FAKE, None, None, FAKE, FAKE, 0, None) == NULLP
+    assert so.ssd_compute_out(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, 0, None) == MISAL
+    assert so.ssd_compute_out(ctypes.byref(prob), FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, None) == WS
+    bad = P(io_dtype=3)
+    assert so.ssd_compute_out(ctypes.byref(bad), FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, None) == DTYPE
