@@ -27,6 +27,10 @@ COMMON_FLAGS = [
     "--offload-arch=" + ARCH,
     # keep the compiler from emitting packed fp32 VALU ops in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the AGPR form gave wrong fp32 tile
+    # results at high register pressure (correct at -O1 or in this form), and
+    # this form also needs fewer registers for the bf16 kernels
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -12,31 +12,41 @@
 // section "세 가지 핵심 커널 구현", compute_out; brifing.si "Accelerating
 // Mamba-2 ...", sections 9 and 11).  Nothing Q x Q is written to HBM.
 //
-// gfx950 design.  One workgroup (4 waves) per (b, h, chunk, 64-wide p slice).
-// Rows are processed in row blocks of 16*RB tokens, dealt to the 4 waves in a
-// snake order so every wave gets the same causal work.  For a row block with
-// first row i0, let jl = 32*floor(i0/32) and r = jl - 1 (the token before the
-// block's last full 32-token column pair; G_{-1} = 0).  Because decays are
-// negative, G is non-increasing, and for j <= r < i
-//     exp2(G_i - G_j) = exp2(G_i - G_r) * exp2(G_r - G_j)
-// with both factors <= 1.  So:
-//   acc  = exp2(G_r) * (C_i . H_c)                       [MFMA over n, then a scalar]
-//   acc += sum_{j<jl} (C_i.B_j) * W_r[j] * x_j          W_r[j] = exp2(G_r - G_j) dt_j from LDS
-//   acc *= exp2(G_i - G_r)                               [one exp2 per row]
-//   acc += sum_{jl<=j<=i} (C_i.B_j) exp2(G_i - G_j) dt_j x_j   [32-wide band, masked exp2]
-// which is the definition above regrouped; the per-element exp2 is only
-// evaluated on the 32-token band next to the diagonal.  The skip term D_h x_i
-// is added to the diagonal of the interaction tile (S_ii += D_h), so x is not
-// read a second time.
+// gfx950 design.  One workgroup (4 waves) per (b, chunk, KH heads of one
+// group, 64-wide p slice, 128-row part of the chunk).  Heads of one group share
+// C, B and therefore the raw tile C B^T, which is computed once for all KH
+// heads; only the decay, x, the carried state and the accumulators are per
+// head.  Its rows are split into 16-row blocks dealt to
+// the waves in a snake order (wave w owns blocks w and 7-w of the part) so
+// causal work is balanced; each wave keeps its blocks' C rows (as MFMA
+// fragments) and output accumulators in registers for the whole chunk.  The
+// workgroup streams the chunk's tokens in pairs of 16-token blocks through a
+// ring of LDS slots filled by asynchronous direct global->LDS loads issued
+// several pairs ahead (global memory latency under load is far longer than
+// one pair's compute), one barrier per pair.
 //
-// MFMA chaining: the interaction tile is produced transposed, S^T = B C^T
-// (A operand = B rows, B operand = C rows, both contiguous along n), so each
-// lane ends up holding one row i and 4+4 token columns j -- exactly an A
-// operand of the next v_mfma_f32_16x16x32_bf16 once the 32 tokens of a pair of
-// 16-token blocks are taken in the order {4g..4g+3, 16+4g..16+4g+3} for lane
-// group g.  x is staged in LDS transposed ([p][token]) in that same token
-// order, so the B operand of S x is one 16-byte read.  The tile never leaves
-// registers between the two products.
+// Decay factorisation.  For a row block starting at i0, let jl = 32*floor(i0/32)
+// and r = jl - 1 (G_{-1} = 0).  Decays are negative, so G is non-increasing and
+// for j <= r < i
+//     exp2(G_i - G_j) = exp2(G_i - G_r) * exp2(G_r - G_j),   both factors <= 1.
+// So the accumulator starts as exp2(G_r) (C_i . H_c), every pair p left of jl
+// adds (C_i . B_j) exp2(G_r - G_j) dt_j x_j, where the weight is the product of
+// a per-token table e_j = exp2(G_e - G_j) dt_j (G_e = running sum at the pair's
+// last token e) and one scalar exp2(G_r - G_e) per (block, pair) -- both <= 1;
+// at the block's own pair (the band) the accumulator is scaled by
+// exp2(G_i - G_r) per row and the band adds the masked per-element
+// exp2(G_i - G_j) dt_j terms.  This is the definition above regrouped; exp2 per
+// tile element is evaluated only on the 32-token band, and no factor exceeds 1.
+// The skip term D_h x_i rides on the tile's diagonal (S_ii += D_h).
+//
+// MFMA chaining: the tile is produced transposed, S^T = B C^T (A operand = B
+// rows, B operand = C rows, both contiguous along n), so each lane ends up
+// holding one row i and the 4+4 token columns {4g..4g+3, 16+4g..16+4g+3} of a
+// token pair -- exactly an A operand of the next v_mfma_f32_16x16x32_bf16 when
+// the pair's tokens are taken in that order.  The matching x operand (8 tokens
+// of one p column per lane) comes from the natural-layout x tile through two
+// transposing LDS reads.  The tile never leaves registers between the two
+// products.
 #include "ssd_device.hpp"
 
 namespace ssd {
@@ -44,358 +54,535 @@ namespace ssd {
 constexpr int kOutThreads = 256;
 constexpr int kOutP = 64;     // p slice per workgroup
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Token held at permuted position k (0..31) of a 32-token pair: position
-// 8g + e holds token 4g + e for e < 4 and 16 + 4g + (e - 4) for e >= 4.
-__device__ __forceinline__ int pair_token(int k) {
-  const int g = k >> 3, e = k & 7;
-  return (e < 4) ? (4 * g + e) : (16 + 4 * g + (e - 4));
-}
-
-struct OutLayout {
-  int xrow, hrow, yrow;     // row lengths (elements)
-  int xs_off, hs_off, g_off, d_off, w_off, ys_off, bytes;
+// One ring slot holds a token pair (32 tokens): B rows over all of n (padded
+// to 32*NK columns) and, for each of the KH heads, x rows over the
+// workgroup's 64 p columns, all in natural [token][feature] order, filled by
+// gfx950's direct global->LDS loads (global_load_lds_dwordx4: lane l's 16
+// bytes land at the wave-uniform LDS base + 16*l, from any global address).
+// 16-byte chunks are XOR-swizzled per row so fragment reads hit distinct banks.
+template <typename T, int NK, int KH>
+struct Slot {
+  static constexpr int V = Vec16<T>::n;                        // elements per chunk
+  static constexpr int BC = 32 * NK / V;                       // chunks per B row
+  static constexpr int BCH = 32 * BC;                          // B chunks per slot
+  static constexpr int XC = kOutP / V;                         // chunks per x row
+  static constexpr int XCH = 32 * XC;                          // x chunks per head
+  static constexpr int BYTES = (BCH + KH * XCH) * 16;
+  static constexpr int BINST = (BCH + kOutThreads - 1) / kOutThreads;   // per wave per pair
+  static constexpr int XINST = (XCH + kOutThreads - 1) / kOutThreads;   // per wave, head, pair
+  static constexpr int LPG = BINST + KH * XINST;               // load instructions per wave per pair
+  static constexpr int BSW = BC < 16 ? BC - 1 : 15;
+  static_assert(BCH % 64 == 0 && XCH % 64 == 0, "slot parts must be whole 64-chunk blocks");
+#ifdef SSD_OUT_FORCE_NSLOT
+  static constexpr int NSLOT = SSD_OUT_FORCE_NSLOT;
+#else
+  static constexpr int NSLOT = BYTES <= 16 * 1024 ? 4 : BYTES <= 28 * 1024 ? 3 : 2;
+#endif
+  static_assert(NSLOT >= 2 && NSLOT <= 4, "the drain-time waits cover up to two pairs ahead");
+  __device__ static int bsw(int r) { return r & BSW; }
+  __device__ static int xsw(int r) { return ((r >> 1) & 3) << 1; }
+  // byte offsets (within a slot) of element (row r, column col) of B / of head k's x
+  __device__ static int boff(int r, int col) {
+    return (r * BC + ((col / V) ^ bsw(r))) * 16 + (col % V) * (int)sizeof(T);
+  }
+  __device__ static int xoff(int k, int r, int col) {
+    return (BCH + k * XCH + r * XC + ((col / V) ^ xsw(r))) * 16 + (col % V) * (int)sizeof(T);
+  }
 };
 
-template <typename T>
-__host__ __device__ inline OutLayout out_layout(int Q, int NK, int RB) {
+struct OutLayout {
+  int yrow;                   // LDS row length of the output staging tile (elements)
+  int g_off, d_off, e_off, ring_off, y_off, bytes, slot_bytes, nslot;
+};
+
+template <typename T, int NK, int KH>
+__host__ __device__ inline OutLayout out_layout(int Q) {
   OutLayout o;
   const int pad = 16 / (int)sizeof(T);
-  o.xrow = Q + pad;
-  o.hrow = 32 * NK + pad;
   o.yrow = kOutP + pad;
+  o.slot_bytes = Slot<T, NK, KH>::BYTES;
+  o.nslot = Slot<T, NK, KH>::NSLOT;
   int off = 0;
-  o.xs_off = off; off += kOutP * o.xrow * (int)sizeof(T);
-  o.hs_off = off; off += kOutP * o.hrow * (int)sizeof(T);
-  o.g_off = off;  off += Q * 4;
-  o.d_off = off;  off += Q * 4;
-  o.w_off = off;  off += (Q / 32) * Q * 4;
-  o.ys_off = off; off += 4 * 16 * RB * o.yrow * (int)sizeof(T);
+  o.g_off = off; off += KH * Q * 4;
+  o.d_off = off; off += KH * Q * 4;
+  o.e_off = off; off += KH * Q * 4;
+  o.ring_off = off; off += o.nslot * o.slot_bytes;
+  o.y_off = off; off += 4 * 16 * o.yrow * (int)sizeof(T);
   o.bytes = off;
   return o;
 }
 
-template <typename T, int NK, int RB>
-__global__ void __launch_bounds__(kOutThreads)
+// s_waitcnt immediate: wait until at most n vector-memory operations of this
+// wave are outstanding (expcnt and lgkmcnt fields at their maxima = no wait).
+constexpr int vmcnt_imm(int n) {
+  return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (0xF << 8);
+}
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Issue the direct-to-LDS loads of token pair `jp` into `slot`.  Every wave
+// issues exactly Slot::LPG instructions (a wave with no block of its own
+// reloads an existing block with identical data), so one vmcnt target is
+// exact for all waves.  Rows past the chunk's valid tokens and columns past
+// N or P read clamped, valid addresses; those values only meet masked tile
+// entries, zero C columns or unstored outputs.
+template <typename T, int NK, int KH>
+__device__ __forceinline__ void issue_pair(unsigned char* slot, const T* __restrict__ Bc,
+                                           int64_t bstride, int N, const T* __restrict__ xc,
+                                           int64_t xstride, int64_t hstep, int p0, int P, int jp,
+                                           int qv, int wave, int lane) {
+  typedef Slot<T, NK, KH> S;
+  constexpr int V = S::V;
+  constexpr int NBB = S::BCH / 64, NXB = S::XCH / 64;   // 64-chunk blocks (whole)
+#pragma unroll
+  for (int k = 0; k < S::BINST; ++k) {
+    const int blk = (k * 4 + wave) % NBB;
+    const int q = blk * 64 + lane;
+    const int r = q / S::BC, pc = q % S::BC;
+    int cl = pc ^ S::bsw(r);
+    const int tok = min(jp * 32 + r, qv - 1);
+    cl = cl * V < N ? cl : 0;
+    __builtin_amdgcn_global_load_lds((gptr_t)(Bc + (int64_t)tok * bstride + cl * V),
+                                     (lptr_t)(slot + blk * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int hh = 0; hh < KH; ++hh)
+#pragma unroll
+    for (int k = 0; k < S::XINST; ++k) {
+      const int blk = (k * 4 + wave) % NXB;
+      const int q = blk * 64 + lane;
+      const int r = q / S::XC, pc = q % S::XC;
+      const int cl = pc ^ S::xsw(r);
+      const int tok = min(jp * 32 + r, qv - 1);
+      int p = p0 + cl * V;
+      p = p < P ? p : p0;
+      __builtin_amdgcn_global_load_lds((gptr_t)(xc + hh * hstep + (int64_t)tok * xstride + p),
+                                       (lptr_t)(slot + (S::BCH + hh * S::XCH) * 16 + blk * 1024),
+                                       16, 0, 0);
+    }
+}
+
+// A operand of S^T = B C^T: lane row j of the pair, n = n0 .. n0+7.
+template <typename T, int NK, int KH>
+__device__ __forceinline__ typename FragOf<T>::type slot_b_frag(const unsigned char* slot, int j,
+                                                                int n0) {
+  typedef Slot<T, NK, KH> S;
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const bf16x8*>(slot + S::boff(j, n0));
+  } else {
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(slot + S::boff(j, n0));
+    const floatx4 hi = *reinterpret_cast<const floatx4*>(slot + S::boff(j, n0 + 4));
+    return floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// B operand of S x for head hh: column p = c0 + lane%16, tokens
+// {4 lg .. 4 lg + 3, 16 + 4 lg .. +3} of the pair.
+template <typename T, int NK, int KH>
+__device__ __forceinline__ typename FragOf<T>::type slot_x_frag(const unsigned char* slot, int hh,
+                                                                int c0, int lane) {
+  typedef Slot<T, NK, KH> S;
+  const int lg = lane / 16;
+  if constexpr (sizeof(T) == 2) {
+    // transposing reads: lane r of each 16-lane group addresses the 4 elements
+    // at [t0 + r/4][c0 + 4 (r%4)]; lane l then holds rows t0..t0+3 of column c0 + l.
+    const int r = lane & 15;
+    const int col = c0 + 4 * (r & 3);
+    const int ta = 4 * lg + (r >> 2), tb = 16 + 4 * lg + (r >> 2);
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(slot + S::xoff(hh, ta, col)));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(slot + S::xoff(hh, tb, col)));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  } else {
+    const int c = c0 + (lane & 15);
+    floatx8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = *reinterpret_cast<const float*>(slot + S::xoff(hh, 4 * lg + e, c));
+      f[4 + e] = *reinterpret_cast<const float*>(slot + S::xoff(hh, 16 + 4 * lg + e, c));
+    }
+    return f;
+  }
+}
+
+// Per-wave state: the wave's row blocks (slot 0 = the later one), their C
+// fragments and the KH heads' accumulators.
+template <typename T, int NK, int IB, int KH>
+struct WaveRows {
+  typedef typename FragOf<T>::type frag_t;
+  int ib[IB], q[IB];
+  frag_t cf[IB][NK];
+  floatx4 acc[KH][IB][4];
+};
+
+// One token pair for the first NS row blocks of the wave; if BAND, the last
+// of them is at its own pair (the band next to the diagonal).
+template <typename T, int NK, int IB, int KH, int NS, bool BAND>
+__device__ __forceinline__ void pair_step(WaveRows<T, NK, IB, KH>& w, const unsigned char* sl,
+                                          int jp, const float* Gs, const float* ds,
+                                          const float* es, int Q, const float* dh, int lane) {
+  typedef typename FragOf<T>::type frag_t;
+  const int lr = lane % 16, lg = lane / 16;
+  // raw tile S^T = B C^T for the active blocks (shared by all heads)
+  floatx4 st[NS][2];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) { st[s][0] = floatx4{0.f, 0.f, 0.f, 0.f}; st[s][1] = st[s][0]; }
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) {
+    const frag_t b0 = slot_b_frag<T, NK, KH>(sl, lr, ks * 32 + lg * 8);
+    const frag_t b1 = slot_b_frag<T, NK, KH>(sl, 16 + lr, ks * 32 + lg * 8);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      st[s][0] = mma(st[s][0], b0, w.cf[s][ks]);
+      st[s][1] = mma(st[s][1], b1, w.cf[s][ks]);
+    }
+  }
+  const int jb = jp * 32;
+#pragma unroll
+  for (int hh = 0; hh < KH; ++hh) {
+    const float* G = Gs + hh * Q;
+    frag_t xf[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) xf[pt] = slot_x_frag<T, NK, KH>(sl, hh, pt * 16, lane);
+    const floatx4 e0 = *reinterpret_cast<const floatx4*>(es + hh * Q + jb + 4 * lg);
+    const floatx4 e1 = *reinterpret_cast<const floatx4*>(es + hh * Q + jb + 16 + 4 * lg);
+    const float g_end = G[jb + 31];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      frag_t af;
+      if (!(BAND && s == NS - 1)) {
+        // left of the block's band: weight exp2(G_r - G_e) * e_j (both <= 1)
+        const float f = fast_exp2(G[32 * w.q[s] - 1] - g_end);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          af[r] = to_io<T>(st[s][0][r] * (e0[r] * f));
+          af[4 + r] = to_io<T>(st[s][1][r] * (e1[r] * f));
+        }
+      } else {
+        // the band: first scale rows i = 16 ib + 4 lg + r by exp2(G_i - G_r)
+        const int ib = w.ib[s], q = w.q[s];
+        const float gref = q >= 1 ? G[32 * q - 1] : 0.0f;
+        const floatx4 gr = *reinterpret_cast<const floatx4*>(G + ib * 16 + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float u = fast_exp2(gr[r] - gref);
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt][r] *= u;
+        }
+        // lane holds row i = 16 ib + lr and tokens j = jb + 16 t + 4 lg + r; the
+        // exponent is masked to -inf before exp2, so no positive exponent is
+        // ever evaluated; the skip weight D_h rides on the diagonal
+        const int i = ib * 16 + lr;
+        const float gi = G[i];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const floatx4 gj = *reinterpret_cast<const floatx4*>(G + jb + 16 * t + 4 * lg);
+          const floatx4 dj = *reinterpret_cast<const floatx4*>(ds + hh * Q + jb + 16 * t + 4 * lg);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = jb + 16 * t + 4 * lg + r;
+            const float ex = j <= i ? gi - gj[r] : -__builtin_inff();
+            float v = st[s][t][r] * (fast_exp2(ex) * dj[r]);
+            v = j == i ? v + dh[hh] : v;
+            af[4 * t + r] = to_io<T>(v);
+          }
+        }
+      }
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt] = mma(w.acc[hh][s][pt], af, xf[pt]);
+    }
+  }
+}
+
+template <typename T, int NK, int IB, int KH>
+__global__ void __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(2)))
 compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
                    const float* __restrict__ Gw, const float* __restrict__ dtw,
                    const T* __restrict__ Hc, const float* __restrict__ Dv, T* __restrict__ y,
                    int64_t L, int H, int P, int N, int G, int Q, int T_, int64_t ldw,
-                   int nbc, int PB) {
+                   int nbc, int PB, int RS) {
   typedef typename FragOf<T>::type frag_t;
+  typedef Slot<T, NK, KH> S;
   constexpr int V = Vec16<T>::n;
+  constexpr int NSLOT = S::NSLOT;
   extern __shared__ __align__(16) unsigned char smem[];
-  const OutLayout lay = out_layout<T>(Q, NK, RB);
-  T* xs = reinterpret_cast<T*>(smem + lay.xs_off);
-  T* hs = reinterpret_cast<T*>(smem + lay.hs_off);
+  const OutLayout lay = out_layout<T, NK, KH>(Q);
   float* Gs = reinterpret_cast<float*>(smem + lay.g_off);
   float* ds = reinterpret_cast<float*>(smem + lay.d_off);
-  float* Ws = reinterpret_cast<float*>(smem + lay.w_off);
-  T* ysall = reinterpret_cast<T*>(smem + lay.ys_off);
+  float* es = reinterpret_cast<float*>(smem + lay.e_off);
+  unsigned char* ring = smem + lay.ring_off;
+  T* ysall = reinterpret_cast<T*>(smem + lay.y_off);
 
-  // XCD-aware placement: every head and p slice of one (b, chunk) gets block
-  // ids congruent mod 8, so they run on one XCD and share its L2 copy of the
-  // chunk's B and C rows.
+  // XCD-aware placement: every head set, p slice and row part of one
+  // (b, chunk) gets block ids congruent mod 8, so they run on one XCD and
+  // share its L2 copy of the chunk's B and C rows.
+  const int NHS = H / KH;                         // head sets (KH heads of one group)
   const int id = blockIdx.x;
-  const int xcd = id % 8, slot = id / 8;
-  const int per = H * PB;
-  const int bc = (slot / per) * 8 + xcd;
+  const int xcd = id % 8, slot_id = id / 8;
+  const int per = NHS * PB * RS;
+  const int bc = (slot_id / per) * 8 + xcd;
   if (bc >= nbc) return;
-  const int hp = slot % per;
-  const int h = hp / PB, pb = hp % PB;
+  const int hp = slot_id % per;
+  const int rsi = hp % RS;
+  const int hs = hp / RS / PB, pb = hp / RS % PB;
+  const int h0 = hs * KH;                         // first head of the set
   const int b = bc / T_, c = bc % T_;
-  const int g = h / (H / G);
+  const int g = h0 / (H / G);
   const int p0 = pb * kOutP;
   const int64_t t0 = (int64_t)c * Q;
   const int qv = (int)min((int64_t)Q, L - t0);
-  const int bh = b * H + h;
+  // this workgroup's 16-row blocks [ib0, ib0 + nibw) and the token pairs they need
+  const int nibw = Q / 16 / RS;
+  const int ib0 = rsi * nibw;
+  const int rows_end = min(qv, (ib0 + nibw) * 16);
+  if (rows_end <= ib0 * 16) return;               // part lies past the sequence end
+  const int npairs = (rows_end + 31) / 32;
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform (SGPR)
   const int lr = lane % 16, lg = lane / 16;
   const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
-  const T* xc = x + ((int64_t)b * L + t0) * xstride + (int64_t)h * P;
+  const T* xc = x + ((int64_t)b * L + t0) * xstride + (int64_t)h0 * P;
   const T* Bc = Bm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N;
   const T* Cc = Cm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N;
-  const float d_h = Dv ? Dv[h] : 0.0f;
+  float dh[KH];
+#pragma unroll
+  for (int hh = 0; hh < KH; ++hh) dh[hh] = Dv ? Dv[h0 + hh] : 0.0f;
 
-  // ---- stage G, dt, x^T (permuted), H_c slice, W table --------------------
-  const float* Grow = Gw + (int64_t)bh * ldw + t0;
-  const float* drow = dtw + (int64_t)bh * ldw + t0;
-  for (int j = tid; j < Q; j += kOutThreads) { Gs[j] = Grow[j]; ds[j] = drow[j]; }
-  {
-    constexpr int FG = kOutP / V;
-    const int tasks = (Q / 8) * FG;
-    for (int task = tid; task < tasks; task += kOutThreads) {
-      const int fg = task % FG, k8 = task / FG;     // k8: 8 permuted positions
-      const int f = p0 + fg * V;
-      const int pair = k8 / 4;
-      T in[8][V];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = pair * 32 + pair_token((k8 % 4) * 8 + e);
-        vec16 v = zero16();
-        if (j < qv && f < P) v = load16(xc + (int64_t)j * xstride + f);
-        const T* pv = reinterpret_cast<const T*>(&v);
-#pragma unroll
-        for (int k = 0; k < V; ++k) in[e][k] = pv[k];
-      }
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-#pragma unroll
-        for (int hh = 0; hh < 8 / V; ++hh) {
-          vec16 pk;
-          T* pp = reinterpret_cast<T*>(&pk);
-#pragma unroll
-          for (int e = 0; e < V; ++e) pp[e] = in[hh * V + e][k];
-          store16(xs + (fg * V + k) * lay.xrow + k8 * 8 + hh * V, pk);
-        }
-      }
-    }
+  // ---- prologue ----------------------------------------------------------------
+  for (int idx = tid; idx < KH * Q; idx += kOutThreads) {
+    const int hh = idx / Q, j = idx % Q;
+    const int64_t row = (int64_t)(b * H + h0 + hh) * ldw + t0;
+    Gs[idx] = Gw[row + j];
+    ds[idx] = dtw[row + j];
   }
-  {
-    const T* hsrc = Hc + ((int64_t)bh * T_ + c) * (int64_t)P * N;
-    const int RV = (32 * NK) / V;                  // 16-byte pieces per hs row
-    for (int idx = tid; idx < kOutP * RV; idx += kOutThreads) {
-      const int pr = idx / RV, piece = idx % RV;
-      const int p = p0 + pr, n = piece * V;
-      vec16 v = zero16();
-      if (p < P && n < N) v = load16(hsrc + (int64_t)p * N + n);
-      store16(hs + pr * lay.hrow + n, v);
-    }
+
+  WaveRows<T, NK, IB, KH> w;
+  bool own[IB];
+#pragma unroll
+  for (int s = 0; s < IB; ++s) {
+    const int sn = IB - 1 - s;
+    const int ib = ib0 + ((sn % 2 == 0) ? 4 * sn + wave : 4 * sn + 3 - wave);
+    own[s] = ib < ib0 + nibw && ib * 16 < qv;
+    w.ib[s] = ib;
+    w.q[s] = ib / 2;
   }
-  __syncthreads();
-  {
-    const int NQ = Q / 32;
-    for (int idx = tid; idx < NQ * Q; idx += kOutThreads) {
-      const int q = idx / Q, j = idx % Q;
-      float w = 0.0f;
-      if (q >= 1 && j < 32 * q) w = fast_exp2(Gs[32 * q - 1] - Gs[j]) * ds[j];
-      Ws[idx] = w;
+  // a wave whose later block is not owned (sequence end) moves its earlier one up
+  int nown = 0;
+#pragma unroll
+  for (int s = 0; s < IB; ++s) nown += own[s] ? 1 : 0;
+  if (IB == 2 && !own[0] && own[1]) { w.ib[0] = w.ib[IB - 1]; w.q[0] = w.q[IB - 1]; }
+#pragma unroll
+  for (int s = 0; s < IB; ++s)
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      const int i = w.ib[s] * 16 + lr, n = ks * 32 + lg * 8;
+      w.cf[s][ks] = (s < nown && i < qv && n < N) ? load_frag(Cc + (int64_t)i * bstride + n)
+                                                   : zero_frag<T>();
     }
-  }
-  __syncthreads();
-
-  T* ys = ysall + wave * (16 * RB) * lay.yrow;
-  const int NRB = Q / (16 * RB);
-  const int npt = min(4, (P - p0 + 15) / 16);   // valid 16-wide p tiles
-
-  for (int k = 0; 4 * k < NRB; ++k) {
-    const int rb = (k % 2 == 0) ? 4 * k + wave : 4 * k + 3 - wave;
-    if (rb >= NRB) continue;
-    const int i0 = rb * 16 * RB;
-    if (i0 >= qv) continue;
-    const int jl = (i0 / 32) * 32;
-    const int q = jl / 32;
-    const float g_ref = jl > 0 ? Gs[jl - 1] : 0.0f;
-
-    // C rows of this block as fragments (A operand for C H^T, B operand for B C^T)
-    frag_t cf[RB][NK];
+  // carried-state term C_i . H_c for every head; H_c is stored fragment-major,
+  // so each fragment load below is one contiguous 1 KiB read for the wave
+  const HcFrag hcl = hc_frag(P, N);
 #pragma unroll
-    for (int ib = 0; ib < RB; ++ib)
+  for (int hh = 0; hh < KH; ++hh) {
+    const T* hsrc = Hc + ((int64_t)(b * H + h0 + hh) * T_ + c) * hcl.state_elems();
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        const int i = i0 + ib * 16 + lr, n = ks * 32 + lg * 8;
-        cf[ib][ks] = (i < qv && n < N) ? load_frag(Cc + (int64_t)i * bstride + n) : zero_frag<T>();
-      }
-
-    // carried-state term
-    floatx4 acc[RB][4];
+    for (int s = 0; s < IB; ++s)
 #pragma unroll
-    for (int ib = 0; ib < RB; ++ib)
+      for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[ib][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        if (pt >= npt) break;
-        const frag_t hf = load_frag(hs + (pt * 16 + lr) * lay.hrow + ks * 32 + lg * 8);
-#pragma unroll
-        for (int ib = 0; ib < RB; ++ib) acc[ib][pt] = mma(acc[ib][pt], cf[ib][ks], hf);
-      }
-    if (jl > 0) {
-      const float sref = fast_exp2(g_ref);
-#pragma unroll
-      for (int ib = 0; ib < RB; ++ib)
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[ib][pt] *= sref;
-    }
-
-    // off-diagonal token pairs: S = (C B^T) * W_r, rounded once, times x
-    const float* Wq = Ws + q * Q;
-    for (int jp = 0; jp < q; ++jp) {
-      floatx4 s[RB][2];
-#pragma unroll
-      for (int ib = 0; ib < RB; ++ib) { s[ib][0] = floatx4{0.f, 0.f, 0.f, 0.f}; s[ib][1] = s[ib][0]; }
+    for (int pt = 0; pt < 4; ++pt) {
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
         const int n = ks * 32 + lg * 8;
-        frag_t b0 = zero_frag<T>(), b1 = zero_frag<T>();
-        if (n < N) {
-          b0 = load_frag(Bc + (int64_t)(jp * 32 + lr) * bstride + n);
-          b1 = load_frag(Bc + (int64_t)(jp * 32 + 16 + lr) * bstride + n);
-        }
+        const frag_t hf = n < N ? load_frag(hsrc + hcl.offset(pb, pt, ks, lane)) : zero_frag<T>();
 #pragma unroll
-        for (int ib = 0; ib < RB; ++ib) {
-          s[ib][0] = mma(s[ib][0], b0, cf[ib][ks]);
-          s[ib][1] = mma(s[ib][1], b1, cf[ib][ks]);
-        }
+        for (int s = 0; s < IB; ++s) w.acc[hh][s][pt] = mma(w.acc[hh][s][pt], w.cf[s][ks], hf);
       }
-      const floatx4 w0 = *reinterpret_cast<const floatx4*>(Wq + jp * 32 + 4 * lg);
-      const floatx4 w1 = *reinterpret_cast<const floatx4*>(Wq + jp * 32 + 16 + 4 * lg);
-      frag_t af[RB];
+    }
+  }
+  // first NSLOT-1 token pairs in flight (only pairs that exist: after the last
+  // one no loads into LDS are outstanding, so the workgroup never has to wait
+  // for its own global stores before it ends)
+  const int64_t hstep = P;
 #pragma unroll
-      for (int ib = 0; ib < RB; ++ib)
+  for (int k = 0; k < NSLOT - 1; ++k)
+    if (k < npairs)
+      issue_pair<T, NK, KH>(ring + k * S::BYTES, Bc, bstride, N, xc, xstride, hstep, p0, P, k,
+                            qv, wave, lane);
+  __syncthreads();                                  // G, dt visible
+  // e_j = exp2(G_e - G_j) dt_j, e = last token of j's pair (<= dt_j)
+  for (int idx = tid; idx < KH * Q; idx += kOutThreads) {
+    const int j = idx % Q;
+    const int e = (j | 31) < Q ? (j | 31) : Q - 1;
+    es[idx] = fast_exp2(Gs[idx - j + e] - Gs[idx]) * ds[idx];
+  }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          af[ib][r] = to_io<T>(s[ib][0][r] * w0[r]);
-          af[ib][4 + r] = to_io<T>(s[ib][1][r] * w1[r]);
-        }
+  for (int hh = 0; hh < KH; ++hh)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        if (pt >= npt) break;
-        const frag_t xf = load_frag(xs + (pt * 16 + lr) * lay.xrow + jp * 32 + lg * 8);
+    for (int s = 0; s < IB; ++s) {
+      const int q = w.q[s];
+      if (q >= 1) {
+        const float sref = fast_exp2(Gs[hh * Q + 32 * q - 1]);
 #pragma unroll
-        for (int ib = 0; ib < RB; ++ib) acc[ib][pt] = mma(acc[ib][pt], af[ib], xf);
+        for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt] *= sref;
       }
     }
 
-    // row scale exp2(G_i - G_r); lane rows are i = i0 + 16 ib + 4 lg + r
-#pragma unroll
-    for (int ib = 0; ib < RB; ++ib)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float u = fast_exp2(Gs[i0 + ib * 16 + 4 * lg + r] - g_ref);
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[ib][pt][r] *= u;
-      }
+  T* ys = ysall + wave * 16 * lay.yrow;
+  const int q0 = nown >= 1 ? w.q[0] : -1;
+  const int q1 = nown >= 2 ? w.q[IB - 1] : -1;
 
-    // band next to the diagonal: tokens jl..jl+31, masked exp2 per element
+  // ---- stream the token pairs ---------------------------------------------------
+  for (int jp = 0; jp < npairs; ++jp) {
+    // pair jp was issued NSLOT-1 pairs ago: wait until at most the loads of the
+    // pairs after it (min(NSLOT-2, npairs-1-jp) of them) are outstanding.  Vector
+    // memory operations retire in issue order, so this covers pair jp; global
+    // stores issued since only make the wait stricter.
     {
-      floatx4 s[RB][2];
+      const int ahead = min(NSLOT - 2, npairs - 1 - jp);
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::LPG));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LPG));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();
+    {
+      const int nxt = jp + NSLOT - 1;               // refill the slot freed by pair jp-1
+      if (nxt < npairs)
+        issue_pair<T, NK, KH>(ring + (nxt % NSLOT) * S::BYTES, Bc, bstride, N, xc, xstride, hstep,
+                              p0, P, nxt, qv, wave, lane);
+    }
+    const unsigned char* sl = ring + (jp % NSLOT) * S::BYTES;
+    int done = -1;                                  // block (slot) finished at this pair
+    if (IB == 2 && jp < q1) {
+      pair_step<T, NK, IB, KH, IB, false>(w, sl, jp, Gs, ds, es, Q, dh, lane);
+    } else if (IB == 2 && jp == q1) {
+      pair_step<T, NK, IB, KH, IB, true>(w, sl, jp, Gs, ds, es, Q, dh, lane);
+      done = IB - 1;
+    } else if (jp < q0) {
+      pair_step<T, NK, IB, KH, 1, false>(w, sl, jp, Gs, ds, es, Q, dh, lane);
+    } else if (jp == q0) {
+      pair_step<T, NK, IB, KH, 1, true>(w, sl, jp, Gs, ds, es, Q, dh, lane);
+      done = 0;
+    }
+    if (done >= 0) {
+      // block finished: accumulators -> LDS (io dtype) -> 16-byte row pieces
+      const int ibd = done == 0 ? w.ib[0] : w.ib[IB - 1];
 #pragma unroll
-      for (int ib = 0; ib < RB; ++ib) { s[ib][0] = floatx4{0.f, 0.f, 0.f, 0.f}; s[ib][1] = s[ib][0]; }
+      for (int hh = 0; hh < KH; ++hh) {
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        const int n = ks * 32 + lg * 8;
-        frag_t b0 = zero_frag<T>(), b1 = zero_frag<T>();
-        if (n < N) {
-          if (jl + lr < qv) b0 = load_frag(Bc + (int64_t)(jl + lr) * bstride + n);
-          if (jl + 16 + lr < qv) b1 = load_frag(Bc + (int64_t)(jl + 16 + lr) * bstride + n);
-        }
-#pragma unroll
-        for (int ib = 0; ib < RB; ++ib) {
-          // a 16-token block that starts after the row block's last row is fully masked
-          s[ib][0] = mma(s[ib][0], b0, cf[ib][ks]);
-          if (jl + 16 <= i0 + ib * 16 + 15) s[ib][1] = mma(s[ib][1], b1, cf[ib][ks]);
-        }
-      }
-      frag_t af[RB];
-#pragma unroll
-      for (int ib = 0; ib < RB; ++ib) {
-        const int i = i0 + ib * 16 + lr;
-        const float gi = Gs[i];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int j = jl + 16 * t + 4 * lg + r;
-            float v = 0.0f;
-            if (j <= i) {
-              v = s[ib][t][r] * (fast_exp2(gi - Gs[j]) * ds[j]);
-              if (j == i) v += d_h;
-            }
-            af[ib][4 * t + r] = to_io<T>(v);
+            const float v = done == 0 ? w.acc[hh][0][pt][r] : w.acc[hh][IB - 1][pt][r];
+            ys[(4 * lg + r) * lay.yrow + pt * 16 + lr] = to_io<T>(v);
           }
-      }
+        wave_sync();
+        constexpr int RV = kOutP / V;
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        if (pt >= npt) break;
-        const frag_t xf = load_frag(xs + (pt * 16 + lr) * lay.xrow + q * 32 + lg * 8);
-#pragma unroll
-        for (int ib = 0; ib < RB; ++ib) acc[ib][pt] = mma(acc[ib][pt], af[ib], xf);
-      }
-    }
-
-    // store: accumulators -> LDS (io dtype) -> 16-byte row pieces
-#pragma unroll
-    for (int ib = 0; ib < RB; ++ib)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          ys[(ib * 16 + 4 * lg + r) * lay.yrow + pt * 16 + lr] = to_io<T>(acc[ib][pt][r]);
-    wave_sync();
-    {
-      constexpr int RV = kOutP / V;
-      for (int idx = lane; idx < 16 * RB * RV; idx += kWave) {
-        const int rr = idx / RV, piece = idx % RV;
-        const int i = i0 + rr, p = p0 + piece * V;
-        if (i < qv && p < P)
-          store16(y + (((int64_t)b * L + t0 + i) * H + h) * P + p, load16(ys + rr * lay.yrow + piece * V));
+        for (int idx = lane; idx < 16 * RV; idx += kWave) {
+          const int rr = idx / RV, piece = idx % RV;
+          const int i2 = ibd * 16 + rr, p = p0 + piece * V;
+          if (i2 < qv && p < P)
+            store16(y + (((int64_t)b * L + t0 + i2) * H + h0 + hh) * P + p,
+                    load16(ys + rr * lay.yrow + piece * V));
+        }
+        wave_sync();
       }
     }
-    wave_sync();
   }
+  // every load into LDS was waited for inside the loop (the last pair with
+  // vmcnt(0)); only global stores may still be in flight here
 }
 
-template <typename T, int NK, int RB>
-static hipError_t launch_out_nk(const void* x, const void* Bm, const void* Cm, const float* Gw,
-                                const float* dtw, const void* Hc, const float* Dv, void* y,
-                                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                                int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
-  const OutLayout lay = out_layout<T>(Q, NK, RB);
+template <typename T, int NK, int IB, int KH>
+static hipError_t launch_out(const void* x, const void* Bm, const void* Cm, const float* Gw,
+                             const float* dtw, const void* Hc, const float* Dv, void* y,
+                             int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                             int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
+  const OutLayout lay = out_layout<T, NK, KH>(Q);
   const int PB = (int)((P + kOutP - 1) / kOutP);
+  const int RS = Q >= 128 ? Q / 128 : 1;   // 128 rows (8 blocks, 2 per wave) per workgroup
   const int64_t nbc = batch * T_;
-  const int64_t nblocks = ((nbc + 7) / 8) * 8 * H * PB;
-  auto kern = compute_out_kernel<T, NK, RB>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lay.bytes);
-  if (e != hipSuccess) return e;
+  const int64_t nblocks = ((nbc + 7) / 8) * 8 * (H / KH) * PB * RS;
+  auto kern = compute_out_kernel<T, NK, IB, KH>;
+  static bool attr_set = false;   // per instantiation
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(kOutThreads), lay.bytes, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm), static_cast<const T*>(Cm),
                      Gw, dtw, static_cast<const T*>(Hc), Dv, static_cast<T*>(y), L, (int)H, (int)P,
-                     (int)N, (int)G, Q, (int)T_, ldw, (int)nbc, PB);
+                     (int)N, (int)G, Q, (int)T_, ldw, (int)nbc, PB, RS);
   return hipGetLastError();
 }
 
-template <typename T, int RB>
-static hipError_t launch_out_rb(const void* x, const void* Bm, const void* Cm, const float* Gw,
-                                const float* dtw, const void* Hc, const float* Dv, void* y,
-                                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                                int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
-  const int64_t nk = (N + 31) / 32;
-  if (nk <= 1) return launch_out_nk<T, 1, RB>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
-  if (nk <= 2) return launch_out_nk<T, 2, RB>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
-  if (nk <= 4) return launch_out_nk<T, 4, RB>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
-  return launch_out_nk<T, 8, RB>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
+// heads per workgroup: two heads of one group share the tile C B^T when the
+// group has an even head count and the accumulators of both fit in registers
+// next to 2 waves per SIMD (bf16, dstate <= 128); one head otherwise
+#ifndef SSD_OUT_MAX_KH
+#define SSD_OUT_MAX_KH 2
+#endif
+static int kh_class(int io_bf16, int64_t H, int64_t G, int64_t N) {
+  return (SSD_OUT_MAX_KH >= 2 && io_bf16 && nk_class(N) <= 4 && (H / G) % 2 == 0) ? 2 : 1;
 }
 
-int compute_out_rows_per_block(int Q) { return Q >= 256 ? 2 : 1; }
+template <typename T, int IB, int KH>
+static hipError_t launch_out_nk(int NK, const void* x, const void* Bm, const void* Cm,
+                                const float* Gw, const float* dtw, const void* Hc, const float* Dv,
+                                void* y, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                                int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
+#define SSD_OUT_ARGS x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream
+  switch (NK) {
+    case 1: return launch_out<T, 1, IB, KH>(SSD_OUT_ARGS);
+    case 2: return launch_out<T, 2, IB, KH>(SSD_OUT_ARGS);
+    case 4: return launch_out<T, 4, IB, KH>(SSD_OUT_ARGS);
+    default: return launch_out<T, 8, IB, KH>(SSD_OUT_ARGS);
+  }
+#undef SSD_OUT_ARGS
+}
 
-int compute_out_smem_bytes(int io_bf16, int Q, int64_t N) {
-  const int nk = (int)((N + 31) / 32);
-  const int NK = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
-  const int RB = compute_out_rows_per_block(Q);
-  return io_bf16 ? out_layout<bf16>(Q, NK, RB).bytes : out_layout<float>(Q, NK, RB).bytes;
+template <typename T>
+static hipError_t launch_out_t(const void* x, const void* Bm, const void* Cm, const float* Gw,
+                               const float* dtw, const void* Hc, const float* Dv, void* y,
+                               int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                               int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
+#define SSD_OUT_ARGS nk_class(N), x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream
+  const bool two = kh_class(sizeof(T) == 2, H, G, N) == 2;
+  if (Q >= 128) return two ? launch_out_nk<T, 2, 2>(SSD_OUT_ARGS) : launch_out_nk<T, 2, 1>(SSD_OUT_ARGS);
+  return two ? launch_out_nk<T, 1, 2>(SSD_OUT_ARGS) : launch_out_nk<T, 1, 1>(SSD_OUT_ARGS);
+#undef SSD_OUT_ARGS
+}
+
+template <typename T>
+static int smem_bytes_t(int Q, int NK, int KH) {
+#define SSD_LAY(nk) (KH == 2 ? out_layout<T, nk, 2>(Q).bytes : out_layout<T, nk, 1>(Q).bytes)
+  switch (NK) {
+    case 1: return SSD_LAY(1);
+    case 2: return SSD_LAY(2);
+    case 4: return SSD_LAY(4);
+    default: return SSD_LAY(8);
+  }
+#undef SSD_LAY
+}
+
+int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int64_t H, int64_t G) {
+  const int NK = nk_class(N), KH = kh_class(io_bf16, H, G, N);
+  return io_bf16 ? smem_bytes_t<bf16>(Q, NK, KH) : smem_bytes_t<float>(Q, NK, KH);
 }
 
 hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
                               void* y, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                               int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
-  const int RB = compute_out_rows_per_block(Q);
-  if (io_bf16) {
-    if (RB == 2) return launch_out_rb<bf16, 2>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
-    return launch_out_rb<bf16, 1>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
-  }
-  if (RB == 2) return launch_out_rb<float, 2>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
-  return launch_out_rb<float, 1>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
+  if (io_bf16)
+    return launch_out_t<bf16>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
+  return launch_out_t<float>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
 }
 
 }  // namespace ssd

@@ -103,7 +103,7 @@ fwd_pass_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                       const float* __restrict__ Gw, const float* __restrict__ dtw,
                       const float* __restrict__ init_state, float* __restrict__ final_state,
                       T* __restrict__ Hc, int64_t L, int H, int P, int N, int G, int Q, int T_,
-                      int64_t ldw, int BH, int NB, int PB) {
+                      int64_t ldw, int BH, int NB, int PB, int frag_major) {
   typedef typename FragOf<T>::type frag_t;
   __shared__ StateSmem<T> sm;
 
@@ -162,7 +162,21 @@ fwd_pass_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
     stage_transposed<T, false>(sm.bs, Bm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N, bstride,
                                n0, N, Q, qv, nullptr, nullptr, 0.0f);
     __syncthreads();
-    {
+    if (frag_major) {
+      // workspace: fragment-major order (see ssd_device.hpp); this tile is p slice
+      // pb and the two 32-column steps 2 nb, 2 nb + 1; 512 pieces of 8 elements
+      const HcFrag hf = hc_frag(P, N);
+      T* hbase = Hc + ((int64_t)bh * T_ + c) * hf.state_elems();
+      for (int idx = tid; idx < 512; idx += kStateThreads) {
+        const int ln = idx % 64, kk = (idx / 64) % 2, pt = idx / 128;
+        const T* src = &sm.hs[pt * 16 + ln % 16][kk * 32 + (ln / 16) * 8];
+        T* dst = hbase + hf.offset(pb, pt, 2 * nb + kk, ln);
+#pragma unroll
+        for (int h2 = 0; h2 < (int)(8 * sizeof(T)) / 16; ++h2)
+          store16(dst + h2 * Vec16<T>::n, load16(src + h2 * Vec16<T>::n));
+      }
+    } else {
+      // caller's buffer: [P][N] rows
       constexpr int V = Vec16<T>::n;
       constexpr int RV = kNT / V;            // 16-byte pieces per row
       T* hbase = Hc + ((int64_t)bh * T_ + c) * (int64_t)P * N;
@@ -211,7 +225,8 @@ template <typename T>
 hipError_t launch_fwd_pass_state_t(const void* x, const void* Bm, const float* Gw, const float* dtw,
                                    const float* init_state, float* final_state, void* Hc,
                                    int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                                   int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
+                                   int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
+                                   hipStream_t stream) {
   const int NB = (int)((N + kNT - 1) / kNT), PB = (int)((P + kPT - 1) / kPT);
   const int64_t BH = batch * H;
   const int64_t groups8 = (BH + 7) / 8;
@@ -219,7 +234,7 @@ hipError_t launch_fwd_pass_state_t(const void* x, const void* Bm, const float* G
   hipLaunchKernelGGL(fwd_pass_state_kernel<T>, dim3((unsigned)nblocks), dim3(kStateThreads), 0,
                      stream, static_cast<const T*>(x), static_cast<const T*>(Bm), Gw, dtw,
                      init_state, final_state, static_cast<T*>(Hc), L, (int)H, (int)P, (int)N,
-                     (int)G, Q, (int)T_, ldw, (int)BH, NB, PB);
+                     (int)G, Q, (int)T_, ldw, (int)BH, NB, PB, frag_major);
   return hipGetLastError();
 }
 
@@ -227,12 +242,12 @@ hipError_t launch_fwd_pass_state(int io_bf16, const void* x, const void* Bm, con
                                  const float* dtw, const float* init_state, float* final_state,
                                  void* Hc, int64_t batch, int64_t L, int64_t H, int64_t P,
                                  int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                                 hipStream_t stream) {
+                                 int frag_major, hipStream_t stream) {
   if (io_bf16)
     return launch_fwd_pass_state_t<bf16>(x, Bm, Gw, dtw, init_state, final_state, Hc, batch, L, H,
-                                         P, N, G, Q, T_, ldw, stream);
+                                         P, N, G, Q, T_, ldw, frag_major, stream);
   return launch_fwd_pass_state_t<float>(x, Bm, Gw, dtw, init_state, final_state, Hc, batch, L, H,
-                                        P, N, G, Q, T_, ldw, stream);
+                                        P, N, G, Q, T_, ldw, frag_major, stream);
 }
 
 }  // namespace ssd

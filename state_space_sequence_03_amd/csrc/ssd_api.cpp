@@ -14,6 +14,7 @@
 #include <string>
 
 #include "../../include/ssd.h"
+#include "ssd_device.hpp"
 
 namespace ssd {
 hipError_t launch_chunk_cumsum(const float* dt, const float* A, float* G, float* dtT,
@@ -23,12 +24,12 @@ hipError_t launch_fwd_pass_state(int io_bf16, const void* x, const void* Bm, con
                                  const float* dtw, const float* init_state, float* final_state,
                                  void* Hc, int64_t batch, int64_t L, int64_t H, int64_t P,
                                  int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                                 hipStream_t stream);
+                                 int frag_major, hipStream_t stream);
 hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
                               void* y, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                               int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream);
-int compute_out_smem_bytes(int io_bf16, int Q, int64_t N);
+int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int64_t H, int64_t G);
 }  // namespace ssd
 
 namespace {
@@ -109,7 +110,7 @@ ssd_status check_supported(const Plan& pl) {
   if (pl.B * pl.H > INT32_MAX / 64 || pl.B * pl.T > INT32_MAX / 64 || pl.H > 65535 ||
       pl.B > 65535 || pl.T > INT32_MAX / 8)
     return fail(SSD_ERR_UNSUPPORTED, "grid too large for this build");
-  if (ssd::compute_out_smem_bytes(pl.bf16, (int)pl.Q, pl.N) > kMaxLds)
+  if (ssd::compute_out_smem_bytes(pl.bf16, (int)pl.Q, pl.N, pl.H, pl.G) > kMaxLds)
     return fail(SSD_ERR_UNSUPPORTED, "fp32 io with chunk_size %lld and dstate %lld exceeds LDS",
                 (long long)pl.Q, (long long)pl.N);
   return SSD_OK;
@@ -120,7 +121,10 @@ void workspace_plan(Plan* pl) {
   pl->g_off = 0;
   pl->dt_off = align256(gsz);
   pl->hc_off = pl->dt_off + align256(gsz);
-  const size_t hcsz = size_t(pl->B) * pl->H * pl->T * pl->P * pl->N * pl->esize;
+  // chunk-start states, fragment-major (padded to whole 64-row slices and
+  // 32-column steps)
+  const size_t hcsz = size_t(pl->B) * pl->H * pl->T * size_t(ssd::hc_frag(pl->P, pl->N).state_elems()) *
+                      pl->esize;
   pl->bytes = pl->hc_off + align256(hcsz);
 }
 
@@ -202,7 +206,8 @@ static ssd_status run_states(const Plan& pl, const void* x, const float* dt, con
                                           pl.Lp, s);
   if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
   e = ssd::launch_fwd_pass_state(pl.bf16, x, B, Gw, dtw, init_state, final_state, Hc, pl.B, pl.L,
-                                 pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp, s);
+                                 pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp,
+                                 chunk_states ? 0 : 1, s);
   return hip_status(e, "fwd_pass_state launch");
 }
 

@@ -78,4 +78,76 @@ template <typename T> __device__ __forceinline__ typename FragOf<T>::type zero_f
   return z;
 }
 
+
+// ---- fragment-major chunk-start states -------------------------------------
+// fwd_pass_state leaves the chunk-start states H_c in the workspace in the order
+// compute_out consumes them as MFMA B operands, so that every fragment load is
+// one contiguous 1 KiB read for the wave.  For chunk state (b, h, c) [P x N],
+// 64-row p slice pb, 16-row tile pt, 32-column step ks and lane l, 8
+// consecutive elements H[64 pb + 16 pt + l%16][32 ks + 8 (l/16) + e] are stored
+// at element offset (((pb * 4 + pt) * KSW + ks) * 64 + l) * 8 of the state.
+// Rows past P and columns past N hold zeros or are never read.
+__host__ __device__ inline int nk_class(int64_t N) {   // 32-column steps, rounded to 1/2/4/8
+  const int nk = (int)((N + 31) / 32);
+  return nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
+}
+struct HcFrag {
+  int PB, KSW;
+  __host__ __device__ int64_t state_elems() const { return (int64_t)PB * 4 * KSW * 512; }
+  __host__ __device__ int64_t offset(int pb, int pt, int ks, int lane) const {
+    return ((((int64_t)pb * 4 + pt) * KSW + ks) * 64 + lane) * 8;
+  }
+};
+__host__ __device__ inline HcFrag hc_frag(int64_t P, int64_t N) {
+  HcFrag f;
+  f.PB = (int)((P + 63) / 64);
+  const int nb2 = 2 * (int)((N + 63) / 64);       // columns written by 64-wide state tiles
+  const int nk = nk_class(N);
+  f.KSW = nk > nb2 ? nk : nb2;
+  return f;
+}
+
+// ---- token-major LDS tiles -------------------------------------------------
+// A tile [token][feature] (row stride `stride` elements) holds operands whose
+// contraction index k is the token.  An MFMA fragment needs 8 tokens of one
+// feature per lane.  gfx950's transposing LDS read (ds_read_b64_tr_b16) does
+// this for 16-bit data: within each 16-lane group, if lane r addresses the 4
+// elements at [t0 + r/4][c0 + 4*(r%4)], lane l receives rows t0..t0+3 of
+// column c0 + l.  Two such reads give the 8 tokens {ta..ta+3, tb..tb+3}.
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x8 frag_tokens(const bf16* tile, int stride, int ta, int tb,
+                                              int c0, int lane) {
+  const int r = lane & 15;
+  const int off = (r >> 2) * stride + c0 + 4 * (r & 3);
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + ta * stride + off));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + tb * stride + off));
+  bf16x8 f;
+  f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+  f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+  return f;
+}
+// fp32 tiles: eight scalar reads (used only by the fp32 io path).
+__device__ __forceinline__ floatx8 frag_tokens(const float* tile, int stride, int ta, int tb,
+                                               int c0, int lane) {
+  const int c = c0 + (lane & 15);
+  floatx8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = tile[(ta + e) * stride + c];
+    f[4 + e] = tile[(tb + e) * stride + c];
+  }
+  return f;
+}
+
+// Exchange through LDS between lanes of one wave: every LDS access of this
+// wave before the call completes before any after it.  The hardware keeps a
+// wave's LDS operations in order; the memory clobber keeps the compiler from
+// moving LDS loads above earlier LDS stores whose addresses differ per lane
+// (which single-thread alias analysis would otherwise allow).
+__device__ __forceinline__ void wave_sync() {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
 }  // namespace ssd

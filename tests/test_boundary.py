@@ -80,8 +80,8 @@ def test_workspace_size_formula(so):
     (dict(headdim=0), SHAPE), (dict(seqlen=2 ** 40, nheads=2 ** 20), SHAPE),
     (dict(chunk_size=16), CHUNK), (dict(chunk_size=100), CHUNK), (dict(chunk_size=512), CHUNK),
     (dict(io_dtype=7), DTYPE), (dict(headdim=72), UNSUP), (dict(dstate=40), UNSUP),
-    (dict(dstate=272), UNSUP), (dict(io_dtype=0, dstate=256), UNSUP),
-    (dict(chunk_size=32), OK), (dict(io_dtype=0, dstate=128), OK),
+    (dict(dstate=272), UNSUP),
+    (dict(chunk_size=32), OK), (dict(io_dtype=0, dstate=128), OK), (dict(io_dtype=0, dstate=256), OK),
 ])
 def test_workspace_size_validation(so, kw, code):
     st, _ = ws_status(P(**kw))

@@ -84,8 +84,6 @@ def test_chunk_cumsum_closed_forms():
 @pytest.mark.parametrize("L,Q,P,N,G,H", [(300, 64, 64, 64, 1, 3), (1000, 128, 64, 128, 2, 4),
                                          (513, 256, 32, 48, 1, 2), (96, 32, 128, 256, 1, 1)])
 def test_chunk_states(io, L, Q, P, N, G, H):
-    if io == "fp32" and Q == 256 and N > 128:
-        pytest.skip("fp32 io at chunk 256 supports dstate <= 128")
     p = prob(seqlen=L, chunk_size=Q, headdim=P, dstate=N, ngroups=G, nheads=H, io_dtype=io)
     inp = ssd_synth.make_inputs(p, seed=7)
     d = to_dev(inp)
@@ -115,8 +113,6 @@ SMALL = [
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "L%d_Q%d_P%d_N%d_G%d_H%d_B%d" % c)
 def test_fwd_small(io, case):
     L, Q, P, N, G, H, bsz = case
-    if io == "fp32" and Q == 256 and N > 128:
-        pytest.skip("fp32 io at chunk 256 supports dstate <= 128")
     p = prob(seqlen=L, chunk_size=Q, headdim=P, dstate=N, ngroups=G, nheads=H, batch=bsz, io_dtype=io)
     inp = ssd_synth.make_inputs(p, seed=L)
     y, fin = gpu_fwd(to_dev(inp), Q)
