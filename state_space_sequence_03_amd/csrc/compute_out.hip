@@ -118,8 +118,26 @@ constexpr int vmcnt_imm(int n) {
   return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (0xF << 8);
 }
 
-typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
+
+// One direct global->LDS load (global_load_lds_dwordx4): lane l's 16 bytes at
+// `gaddr` land at LDS byte address lds + 16 l (lds is wave-uniform, set in M0).
+// Issued as inline assembly so the compiler's wait-count pass does not treat
+// every later LDS read as a possible reader of this write (it cannot tell ring
+// slots apart and would drain all loads before each read, defeating the
+// prefetch); the kernel's own s_waitcnt vmcnt + barrier order the data
+// instead.  Vector-memory operations complete in issue order, so loads the
+// compiler does not see only make its own waits stricter.
+__device__ __forceinline__ void dma16(const void* gaddr, lptr_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gaddr), "s"(base)
+      : "memory", "m0");
+}
 
 // Issue the direct-to-LDS loads of token pair `jp` into `slot`.  Every wave
 // issues exactly Slot::LPG instructions (a wave with no block of its own
@@ -143,8 +161,7 @@ __device__ __forceinline__ void issue_pair(unsigned char* slot, const T* __restr
     int cl = pc ^ S::bsw(r);
     const int tok = min(jp * 32 + r, qv - 1);
     cl = cl * V < N ? cl : 0;
-    __builtin_amdgcn_global_load_lds((gptr_t)(Bc + (int64_t)tok * bstride + cl * V),
-                                     (lptr_t)(slot + blk * 1024), 16, 0, 0);
+    dma16(Bc + (int64_t)tok * bstride + cl * V, (lptr_t)(slot + blk * 1024));
   }
 #pragma unroll
   for (int hh = 0; hh < KH; ++hh)
@@ -157,9 +174,8 @@ __device__ __forceinline__ void issue_pair(unsigned char* slot, const T* __restr
       const int tok = min(jp * 32 + r, qv - 1);
       int p = p0 + cl * V;
       p = p < P ? p : p0;
-      __builtin_amdgcn_global_load_lds((gptr_t)(xc + hh * hstep + (int64_t)tok * xstride + p),
-                                       (lptr_t)(slot + (S::BCH + hh * S::XCH) * 16 + blk * 1024),
-                                       16, 0, 0);
+      dma16(xc + hh * hstep + (int64_t)tok * xstride + p,
+            (lptr_t)(slot + (S::BCH + hh * S::XCH) * 16 + blk * 1024));
     }
 }
 
@@ -347,17 +363,17 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
   const T* xc = x + ((int64_t)b * L + t0) * xstride + (int64_t)h0 * P;
   const T* Bc = Bm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N;
   const T* Cc = Cm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N;
-  float dh[KH];
-#pragma unroll
-  for (int hh = 0; hh < KH; ++hh) dh[hh] = Dv ? Dv[h0 + hh] : 0.0f;
 
   // ---- prologue ----------------------------------------------------------------
-  for (int idx = tid; idx < KH * Q; idx += kOutThreads) {
-    const int hh = idx / Q, j = idx % Q;
-    const int64_t row = (int64_t)(b * H + h0 + hh) * ldw + t0;
-    Gs[idx] = Gw[row + j];
-    ds[idx] = dtw[row + j];
-  }
+  // Every global load of the prologue is issued before any of it is used: the
+  // first ring pairs, the block's C fragments and the chunk-start state
+  // fragments; one memory round trip instead of one per fragment group.
+  const int64_t hstep = P;
+#pragma unroll
+  for (int k = 0; k < NSLOT - 1; ++k)
+    if (k < npairs)
+      issue_pair<T, NK, KH>(ring + k * S::BYTES, Bc, bstride, N, xc, xstride, hstep, p0, P, k,
+                            qv, wave, lane);
 
   WaveRows<T, NK, IB, KH> w;
   bool own[IB];
@@ -382,36 +398,42 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
       w.cf[s][ks] = (s < nown && i < qv && n < N) ? load_frag(Cc + (int64_t)i * bstride + n)
                                                    : zero_frag<T>();
     }
-  // carried-state term C_i . H_c for every head; H_c is stored fragment-major,
-  // so each fragment load below is one contiguous 1 KiB read for the wave
+  // chunk-start states, fragment-major: each load is one contiguous 1 KiB read
   const HcFrag hcl = hc_frag(P, N);
+  frag_t hf[KH][4][NK];
 #pragma unroll
   for (int hh = 0; hh < KH; ++hh) {
     const T* hsrc = Hc + ((int64_t)(b * H + h0 + hh) * T_ + c) * hcl.state_elems();
 #pragma unroll
-    for (int s = 0; s < IB; ++s)
+    for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < NK; ++ks)
+        hf[hh][pt][ks] = (ks * 32 + lg * 8 < N) ? load_frag(hsrc + hcl.offset(pb, pt, ks, lane))
+                                                 : zero_frag<T>();
+  }
+  for (int idx = tid; idx < KH * Q; idx += kOutThreads) {
+    const int hh = idx / Q, j = idx % Q;
+    const int64_t row = (int64_t)(b * H + h0 + hh) * ldw + t0;
+    Gs[idx] = Gw[row + j];
+    ds[idx] = dtw[row + j];
+  }
+  float dh[KH];
+#pragma unroll
+  for (int hh = 0; hh < KH; ++hh) dh[hh] = Dv ? Dv[h0 + hh] : 0.0f;
+  // carried-state term C_i . H_c for every head
+#pragma unroll
+  for (int hh = 0; hh < KH; ++hh)
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
+      floatx4 a = floatx4{0.f, 0.f, 0.f, 0.f}, a2 = a;
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        const int n = ks * 32 + lg * 8;
-        const frag_t hf = n < N ? load_frag(hsrc + hcl.offset(pb, pt, ks, lane)) : zero_frag<T>();
-#pragma unroll
-        for (int s = 0; s < IB; ++s) w.acc[hh][s][pt] = mma(w.acc[hh][s][pt], w.cf[s][ks], hf);
+        a = mma(a, w.cf[0][ks], hf[hh][pt][ks]);
+        if (IB == 2) a2 = mma(a2, w.cf[IB - 1][ks], hf[hh][pt][ks]);
       }
+      w.acc[hh][0][pt] = a;
+      if (IB == 2) w.acc[hh][IB - 1][pt] = a2;
     }
-  }
-  // first NSLOT-1 token pairs in flight (only pairs that exist: after the last
-  // one no loads into LDS are outstanding, so the workgroup never has to wait
-  // for its own global stores before it ends)
-  const int64_t hstep = P;
-#pragma unroll
-  for (int k = 0; k < NSLOT - 1; ++k)
-    if (k < npairs)
-      issue_pair<T, NK, KH>(ring + k * S::BYTES, Bc, bstride, N, xc, xstride, hstep, p0, P, k,
-                            qv, wave, lane);
   __syncthreads();                                  // G, dt visible
   // e_j = exp2(G_e - G_j) dt_j, e = last token of j's pair (<= dt_j)
   for (int idx = tid; idx < KH * Q; idx += kOutThreads) {
