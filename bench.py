@@ -2,7 +2,7 @@
 """Throughput of the Mamba-2 chunked SSD forward pass (libssd) on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-chunk_cumsum -> fwd_pass_state -> compute_out, enqueued through the C ABI
+chunk_cumsum -> chunk_state -> state_pass -> compute_out, enqueued through the C ABI
 (ssd_fwd_states, then ssd_compute_out -- exactly the launches ssd_fwd makes;
 the split lets HIP events bracket the dominant kernel inside the timed loop).
 Inputs are resident in HBM before timing starts.  Prints one JSON line.
@@ -251,7 +251,7 @@ def main():
         "path_mfma_frac": cnt["f_path"] / (ms_step * 1e-3) / peak_mfma,
         "path_hbm_frac": cnt["b_min"] / (ms_step * 1e-3) / PEAK_HBM,
         "path_tflops": cnt["f_path"] / (ms_step * 1e-3) / 1e12,
-        "stage_ms": {"chunk_cumsum+fwd_pass_state": ms_states, "compute_out": ms_out},
+        "stage_ms": {"chunk_cumsum+chunk_state+state_pass": ms_states, "compute_out": ms_out},
         "cold_ms_per_step": {"median": cold_med[0], "states": cold_med[1], "compute_out": cold_med[2]},
         "roofline": {"kernel": "compute_out", "bound": bound, "achieved": achieved, "peak": peak,
                      "unit": unit, "frac": achieved / peak,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libssd.so")
 
-SOURCES = ["chunk_cumsum.hip", "fwd_pass_state.hip", "compute_out.hip", "ssd_api.cpp"]
+SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "state_pass.hip", "compute_out.hip", "ssd_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -31,6 +31,11 @@ COMMON_FLAGS = [
     # results at high register pressure (correct at -O1 or in this form), and
     # this form also needs fewer registers for the bf16 kernels
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # the direct-to-LDS load helper sets M0 in inline assembly and lists it as
+    # clobbered; the compiler warns that it may keep M0 live across such a
+    # statement, and tests/test_boundary.py checks the built code writes M0
+    # nowhere else
+    "-Wno-inline-asm",
     "-I" + os.path.join(ROOT, "include"),
 ]
 
@@ -52,7 +57,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source and link libssd.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs

@@ -1,0 +1,347 @@
+// chunk_state.hip -- stage 2a: every chunk's own contribution to the state.
+//
+// For chunk c of head (b, h) (tokens j = 0..Q-1 of the chunk):
+//     w_j = exp2(G_last - G_j) * dt_j            (decay from token j to the chunk end)
+//     S_c = sum_j w_j x_j (outer) B_j  =  X_c^T diag(w) B_c        (P x N)
+// the jump formula: a chunk's whole effect on the state is one matrix product
+// over its stacked x and B rows, each row first multiplied by its exponential
+// decay so the product stays a plain GEMM (brifing.si "Accelerating Mamba-2
+// ...", sections 4 and 5).  S_c depends on nothing outside its chunk, so all
+// chunks are computed at once here; the sequential recurrence
+// H_{c+1} = exp2(G_last) H_c + S_c is the small elementwise pass in
+// state_pass.hip.
+//
+// gfx950 mapping.  One workgroup per (b, chunk, KH heads of one group, 64-row p
+// slice, n slice of up to 128 columns): the heads share the chunk's B rows, so
+// B is read once per KH heads.  Waves own one head's 64 p rows and 64 (or
+// fewer) n columns.  The product is formed transposed, S^T = B^T X~ on
+// v_mfma_f32_16x16x32_bf16 (A operand = B columns, B operand = scaled x
+// columns, both token-contiguous), so each lane's accumulator holds 4
+// consecutive n of one p row and is stored straight to memory with no LDS
+// transpose.  The chunk streams through a ring of 32-token slots filled by
+// direct global->LDS loads; each wave multiplies the x rows it loaded by w_j
+// in place, one barrier per slot publishes them, and both operands are read
+// with transposing LDS reads (ds_read_b64_tr_b16).
+#include "ssd_device.hpp"
+
+namespace ssd {
+
+constexpr int kCsTok = 32;    // tokens per ring slot (one MFMA K-step)
+constexpr int kCsP = 64;      // p rows per head per workgroup
+
+template <typename T, int KH, int NW>
+struct CsCfg {
+  static constexpr int V = Vec16<T>::n;                 // elements per 16-byte chunk
+  static constexpr int WNT = NW / 16 < 4 ? NW / 16 : 4; // 16-column n tiles per wave
+  static constexpr int WPN = NW / 16 / WNT;             // waves per head
+  static constexpr int NWV = KH * WPN;                  // waves per workgroup
+  static constexpr int THREADS = NWV * kWave;
+  static constexpr int BC = NW / V;                     // chunks per B row
+  static constexpr int BCH = kCsTok * BC;               // B chunks per slot
+  static constexpr int XC = kCsP / V;                   // chunks per x row
+  static constexpr int XCH = kCsTok * XC;               // x chunks per head per slot
+  static constexpr int BYTES = (BCH + KH * XCH) * 16;
+  static constexpr int NBB = (BCH + 63) / 64, NXB = KH * XCH / 64;   // 64-chunk blocks
+  static constexpr int BINST = (NBB + NWV - 1) / NWV;   // B loads per wave per slot
+  static constexpr int XINST = NXB / NWV;               // x loads per wave per slot
+  static constexpr int LPG = BINST + XINST;
+  static constexpr int NSLOT = 3;
+  static constexpr int BSW = BC < 16 ? BC - 1 : 15;
+  static_assert(BCH % 64 == 0, "B part of a slot must be whole 64-chunk blocks");
+  static_assert(NXB % NWV == 0, "x blocks are scaled in place by the wave that loads them");
+  static_assert(XC >= 8, "x swizzle needs 8 chunks per row");
+  __host__ __device__ static int gd_bytes(int Q) {      // G + dt staging, whole 1 KiB blocks
+    return (KH * 2 * Q * 4 + 1023) / 1024 * 1024;
+  }
+  __host__ __device__ static int lds_bytes(int Q) { return NSLOT * BYTES + gd_bytes(Q); }
+  __device__ static int bsw(int r) { return r & BSW; }
+  __device__ static int xsw(int r) { return ((r >> 1) & 3) << 1; }
+  __device__ static int boff(int r, int col) {
+    return (r * BC + ((col / V) ^ bsw(r))) * 16 + (col % V) * (int)sizeof(T);
+  }
+  __device__ static int xoff(int k, int r, int col) {
+    return (BCH + k * XCH + r * XC + ((col / V) ^ xsw(r))) * 16 + (col % V) * (int)sizeof(T);
+  }
+};
+
+// Fragment of a token-major slot tile: column c0 + lane%16, the 8 tokens
+// {4 lg .. 4 lg + 3, 16 + 4 lg .. 16 + 4 lg + 3} (lg = lane / 16).
+template <typename T, typename Off>
+__device__ __forceinline__ typename FragOf<T>::type slot_tok_frag(const unsigned char* slot, Off off,
+                                                                  int c0, int lane) {
+  const int lg = lane / 16;
+  if constexpr (sizeof(T) == 2) {
+    // transposing reads: lane r of each 16-lane group addresses the 4 elements
+    // at [t0 + r/4][c0 + 4 (r%4)]; lane l then holds rows t0..t0+3 of column c0 + l.
+    const int r = lane & 15;
+    const int col = c0 + 4 * (r & 3);
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(slot + off(4 * lg + (r >> 2), col)));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(slot + off(16 + 4 * lg + (r >> 2), col)));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  } else {
+    const int c = c0 + (lane & 15);
+    floatx8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = *reinterpret_cast<const float*>(slot + off(4 * lg + e, c));
+      f[4 + e] = *reinterpret_cast<const float*>(slot + off(16 + 4 * lg + e, c));
+    }
+    return f;
+  }
+}
+
+// Multiply 16 bytes of io elements by w (fp32 arithmetic, one rounding).
+template <typename T>
+__device__ __forceinline__ vec16 scale16(vec16 v, float w) {
+  T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+  for (int k = 0; k < Vec16<T>::n; ++k) e[k] = to_io<T>(to_f32(e[k]) * w);
+  return v;
+}
+
+template <typename T, int KH, int NW>
+__global__ void __launch_bounds__((CsCfg<T, KH, NW>::THREADS))
+chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ Gw,
+                   const float* __restrict__ dtw, T* __restrict__ S, int64_t L, int H, int P, int N,
+                   int G, int Q, int T_, int64_t ldw, int nbc, int PB, int NSL, int frag_major) {
+  typedef CsCfg<T, KH, NW> C;
+  typedef typename FragOf<T>::type frag_t;
+  constexpr int V = C::V;
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* ring = smem;
+  float* gd = reinterpret_cast<float*>(smem + C::NSLOT * C::BYTES);   // [KH][G row | w row]
+
+  // XCD-aware placement: block ids congruent mod 8 run on one XCD, so the
+  // workgroups of one (b, chunk) -- which share its B rows -- are dealt to one
+  // XCD and read B from its L2; neighbouring ids take different chunks.
+  const int id = blockIdx.x;
+  const int xcd = id % 8, sid = id / 8;
+  const int nbx = (nbc + 7) / 8;
+  const int bc = (sid % nbx) * 8 + xcd;
+  if (bc >= nbc) return;
+  const int hp = sid / nbx;                        // (head set, p slice, n slice)
+  const int nsl = hp % NSL, pb = hp / NSL % PB, hs = hp / NSL / PB;
+  const int h0 = hs * KH;
+  const int b = bc / T_, c = bc % T_;
+  const int g = h0 / (H / G);
+  const int p0 = pb * kCsP, n0 = nsl * NW;
+  const int64_t t0 = (int64_t)c * Q;
+  const int qv = (int)min((int64_t)Q, L - t0);
+  const int ns = (qv + kCsTok - 1) / kCsTok;      // slots holding valid tokens
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
+  const T* xc = x + ((int64_t)b * L + t0) * xstride + (int64_t)h0 * P;
+  const T* Bc = Bm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N;
+
+  // Loads of slot k into ring slot k % NSLOT.  Every wave issues exactly LPG
+  // instructions (B blocks beyond the count are reloaded with identical data;
+  // x blocks divide evenly, each loaded by exactly one wave).  Rows past the
+  // chunk's valid tokens and columns past N or P read clamped, valid
+  // addresses: those rows get weight 0, those columns are outputs that are
+  // never consumed.
+  auto issue = [&](int k) {
+    unsigned char* sl = ring + (k % C::NSLOT) * C::BYTES;
+#pragma unroll
+    for (int i = 0; i < C::BINST; ++i) {
+      const int blk = (i * C::NWV + wave) % C::NBB;
+      const int q = blk * 64 + lane;
+      const int r = q / C::BC, pc = q % C::BC;
+      const int tok = min(k * kCsTok + r, qv - 1);
+      int col = n0 + (pc ^ C::bsw(r)) * V;
+      col = col < N ? col : 0;
+      dma16(Bc + (int64_t)tok * bstride + col, (lptr_t)(sl + blk * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < C::XINST; ++i) {
+      const int blk = i * C::NWV + wave;
+      const int q = blk * 64 + lane;
+      const int hh = q / C::XCH, rq = q % C::XCH;
+      const int r = rq / C::XC, pc = rq % C::XC;
+      const int tok = min(k * kCsTok + r, qv - 1);
+      int p = p0 + (pc ^ C::xsw(r)) * V;
+      p = p < P ? p : p0;
+      dma16(xc + hh * P + (int64_t)tok * xstride + p, (lptr_t)(sl + C::BCH * 16 + blk * 1024));
+    }
+  };
+
+  // ---- prologue: G and dt rows of the KH heads, then the first slots ----------
+  {
+    const int nchunk = KH * Q / 2;                 // 16-byte chunks of G + dt
+    const int ngb = (nchunk + 63) / 64;
+    const int ginst = (ngb + C::NWV - 1) / C::NWV;
+    for (int i = 0; i < ginst; ++i) {              // uniform trip count
+      const int blk = (i * C::NWV + wave) % ngb;
+      int q = blk * 64 + lane;
+      q = q < nchunk ? q : nchunk - 1;
+      const int hh = q / (Q / 2), r = q % (Q / 2);
+      const float* src = (r < Q / 4 ? Gw : dtw) + (int64_t)(b * H + h0 + hh) * ldw + t0 + 4 * (r % (Q / 4));
+      dma16(src, (lptr_t)(reinterpret_cast<unsigned char*>(gd) + blk * 1024));
+    }
+  }
+  const int npro = min(C::NSLOT - 1, ns);
+  for (int k = 0; k < npro; ++k) issue(k);
+  wait_groups<C::LPG>(npro);                       // this wave's G/dt loads have landed
+  __syncthreads();
+  // w_j = exp2(G_last - G_j) dt_j in place of dt_j; padding tokens have dt = 0
+  // and G flat past the sequence end, so they get w = 0
+  for (int idx = tid; idx < KH * Q; idx += C::THREADS) {
+    const int hh = idx / Q, j = idx % Q;
+    float* row = gd + hh * 2 * Q;
+    row[Q + j] = fast_exp2(row[Q - 1] - row[j]) * row[Q + j];
+  }
+  __syncthreads();
+
+  // ---- stream the slots ---------------------------------------------------------
+  const int hh = wave / C::WPN;                   // this wave's head and n columns
+  const int nw0 = (wave % C::WPN) * C::WNT * 16;
+  floatx4 acc[C::WNT][4];
+#pragma unroll
+  for (int nt = 0; nt < C::WNT; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) acc[nt][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k = 0; k < ns; ++k) {
+    wait_groups<C::LPG>(min(C::NSLOT - 2, ns - 1 - k));   // this wave's loads of slot k
+    unsigned char* sl = ring + (k % C::NSLOT) * C::BYTES;
+    // scale the x rows this wave loaded by their token's weight, in place
+#pragma unroll
+    for (int i = 0; i < C::XINST; ++i) {
+      const int blk = i * C::NWV + wave;
+      const int q = blk * 64 + lane;
+      const int hq = q / C::XCH, r = q % C::XCH / C::XC;
+      vec16* pch = reinterpret_cast<vec16*>(sl + C::BCH * 16 + q * 16);
+      *pch = scale16<T>(*pch, gd[hq * 2 * Q + Q + k * kCsTok + r]);
+    }
+    __syncthreads();                               // slot k complete; slot k-1 free
+    if (k + C::NSLOT - 1 < ns) issue(k + C::NSLOT - 1);
+    frag_t fb[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+      fb[pt] = slot_tok_frag<T>(sl, [&](int r, int col) { return C::xoff(hh, r, col); }, pt * 16, lane);
+#pragma unroll
+    for (int nt = 0; nt < C::WNT; ++nt) {
+      const frag_t fa = slot_tok_frag<T>(sl, [&](int r, int col) { return C::boff(r, col); },
+                                         nw0 + nt * 16, lane);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) acc[nt][pt] = mma(acc[nt][pt], fa, fb[pt]);
+    }
+  }
+
+  // ---- store S_c: lane holds p = 16 pt + lane%16 and n = n_base + 4 lg .. +3 --
+  const int h = h0 + hh, lr = lane % 16, lg = lane / 16;
+  if (frag_major) {
+    const HcFrag hf = hc_frag(P, N);
+    T* base = S + ((int64_t)(b * H + h) * T_ + c) * hf.state_elems();
+#pragma unroll
+    for (int nt = 0; nt < C::WNT; ++nt) {
+      const int n = n0 + nw0 + nt * 16 + 4 * lg;              // multiple of 4
+      const int ks = n / 32, q = (n % 32) / 8, e0 = n % 8;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        T* dst = base + hf.offset(pb, pt, ks, lr + 16 * q) + e0;
+        if constexpr (sizeof(T) == 2) {
+          const bf16x4 v{to_io<T>(acc[nt][pt][0]), to_io<T>(acc[nt][pt][1]),
+                         to_io<T>(acc[nt][pt][2]), to_io<T>(acc[nt][pt][3])};
+          *reinterpret_cast<bf16x4*>(dst) = v;
+        } else {
+          *reinterpret_cast<floatx4*>(dst) = acc[nt][pt];
+        }
+      }
+    }
+  } else {
+    T* base = S + ((int64_t)(b * H + h) * T_ + c) * (int64_t)P * N;
+#pragma unroll
+    for (int nt = 0; nt < C::WNT; ++nt) {
+      const int n = n0 + nw0 + nt * 16 + 4 * lg;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int p = p0 + pt * 16 + lr;
+        if (p < P && n < N) {
+          T* dst = base + (int64_t)p * N + n;
+          if constexpr (sizeof(T) == 2) {
+            const bf16x4 v{to_io<T>(acc[nt][pt][0]), to_io<T>(acc[nt][pt][1]),
+                           to_io<T>(acc[nt][pt][2]), to_io<T>(acc[nt][pt][3])};
+            *reinterpret_cast<bf16x4*>(dst) = v;
+          } else {
+            *reinterpret_cast<floatx4*>(dst) = acc[nt][pt];
+          }
+        }
+      }
+    }
+  }
+}
+
+// heads per workgroup: 4 (or 2, or 1) heads of one group share the B rows
+static int cs_kh(int64_t H, int64_t G) {
+  const int64_t hg = H / G;
+  return hg % 4 == 0 ? 4 : hg % 2 == 0 ? 2 : 1;
+}
+
+template <typename T, int KH, int NW>
+static hipError_t launch_cs(const void* x, const void* Bm, const float* Gw, const float* dtw,
+                            void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                            int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
+                            hipStream_t stream) {
+  typedef CsCfg<T, KH, NW> C;
+  const int PB = (int)((P + kCsP - 1) / kCsP);
+  const int NSL = (int)(32 * nk_class(N) / NW);
+  const int64_t nbc = batch * T_;
+  const int64_t nblocks = ((nbc + 7) / 8) * 8 * (H / KH) * PB * NSL;
+  const int lds = C::lds_bytes(Q);
+  auto kern = chunk_state_kernel<T, KH, NW>;
+  static bool attr_set = false;   // per instantiation
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(C::THREADS), lds, stream,
+                     static_cast<const T*>(x), static_cast<const T*>(Bm), Gw, dtw,
+                     static_cast<T*>(S), L, (int)H, (int)P, (int)N, (int)G, Q, (int)T_, ldw,
+                     (int)nbc, PB, NSL, frag_major);
+  return hipGetLastError();
+}
+
+template <typename T, int KH>
+static hipError_t launch_cs_nw(const void* x, const void* Bm, const float* Gw, const float* dtw,
+                               void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                               int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
+                               hipStream_t stream) {
+#define SSD_CS_ARGS x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, stream
+  switch (state_nw(N)) {
+    case 32: return launch_cs<T, KH, 32>(SSD_CS_ARGS);
+    case 64: return launch_cs<T, KH, 64>(SSD_CS_ARGS);
+    default: return launch_cs<T, KH, 128>(SSD_CS_ARGS);
+  }
+#undef SSD_CS_ARGS
+}
+
+template <typename T>
+static hipError_t launch_cs_t(const void* x, const void* Bm, const float* Gw, const float* dtw,
+                              void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                              int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
+                              hipStream_t stream) {
+#define SSD_CS_ARGS x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, stream
+  switch (cs_kh(H, G)) {
+    case 4: return launch_cs_nw<T, 4>(SSD_CS_ARGS);
+    case 2: return launch_cs_nw<T, 2>(SSD_CS_ARGS);
+    default: return launch_cs_nw<T, 1>(SSD_CS_ARGS);
+  }
+#undef SSD_CS_ARGS
+}
+
+hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, const float* Gw,
+                              const float* dtw, void* S, int64_t batch, int64_t L, int64_t H,
+                              int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
+                              int frag_major, hipStream_t stream) {
+  if (io_bf16)
+    return launch_cs_t<bf16>(x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, stream);
+  return launch_cs_t<float>(x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, stream);
+}
+
+}  // namespace ssd

@@ -112,33 +112,6 @@ __host__ __device__ inline OutLayout out_layout(int Q) {
   return o;
 }
 
-// s_waitcnt immediate: wait until at most n vector-memory operations of this
-// wave are outstanding (expcnt and lgkmcnt fields at their maxima = no wait).
-constexpr int vmcnt_imm(int n) {
-  return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (0xF << 8);
-}
-
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-// One direct global->LDS load (global_load_lds_dwordx4): lane l's 16 bytes at
-// `gaddr` land at LDS byte address lds + 16 l (lds is wave-uniform, set in M0).
-// Issued as inline assembly so the compiler's wait-count pass does not treat
-// every later LDS read as a possible reader of this write (it cannot tell ring
-// slots apart and would drain all loads before each read, defeating the
-// prefetch); the kernel's own s_waitcnt vmcnt + barrier order the data
-// instead.  Vector-memory operations complete in issue order, so loads the
-// compiler does not see only make its own waits stricter.
-__device__ __forceinline__ void dma16(const void* gaddr, lptr_t lds) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(gaddr), "s"(base)
-      : "memory", "m0");
-}
-
 // Issue the direct-to-LDS loads of token pair `jp` into `slot`.  Every wave
 // issues exactly Slot::LPG instructions (a wave with no block of its own
 // reloads an existing block with identical data), so one vmcnt target is

@@ -20,11 +20,13 @@ namespace ssd {
 hipError_t launch_chunk_cumsum(const float* dt, const float* A, float* G, float* dtT,
                                int64_t batch, int64_t L, int64_t H, int Q, int64_t ld,
                                int64_t Lw, hipStream_t stream);
-hipError_t launch_fwd_pass_state(int io_bf16, const void* x, const void* Bm, const float* Gw,
-                                 const float* dtw, const float* init_state, float* final_state,
-                                 void* Hc, int64_t batch, int64_t L, int64_t H, int64_t P,
-                                 int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                                 int frag_major, hipStream_t stream);
+hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, const float* Gw,
+                              const float* dtw, void* S, int64_t batch, int64_t L, int64_t H,
+                              int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
+                              int frag_major, hipStream_t stream);
+hipError_t launch_state_pass(int io_bf16, void* S, const float* Gw, const float* init_state,
+                             float* final_state, int64_t batch, int64_t H, int64_t P, int64_t N,
+                             int Q, int64_t T_, int64_t ldw, int frag_major, hipStream_t stream);
 hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
                               void* y, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
@@ -205,10 +207,15 @@ static ssd_status run_states(const Plan& pl, const void* x, const float* dt, con
   hipError_t e = ssd::launch_chunk_cumsum(dt, A, Gw, dtw, pl.B, pl.L, pl.H, (int)pl.Q, pl.Lp,
                                           pl.Lp, s);
   if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
-  e = ssd::launch_fwd_pass_state(pl.bf16, x, B, Gw, dtw, init_state, final_state, Hc, pl.B, pl.L,
-                                 pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp,
-                                 chunk_states ? 0 : 1, s);
-  return hip_status(e, "fwd_pass_state launch");
+  // each chunk's own contribution S_c into the state buffer, then the
+  // recurrence turns it, in place, into the chunk-start states H_c
+  const int frag_major = chunk_states ? 0 : 1;
+  e = ssd::launch_chunk_state(pl.bf16, x, B, Gw, dtw, Hc, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
+                              (int)pl.Q, pl.T, pl.Lp, frag_major, s);
+  if (e != hipSuccess) return hip_status(e, "chunk_state launch");
+  e = ssd::launch_state_pass(pl.bf16, Hc, Gw, init_state, final_state, pl.B, pl.H, pl.P, pl.N,
+                             (int)pl.Q, pl.T, pl.Lp, frag_major, s);
+  return hip_status(e, "state_pass launch");
 }
 
 ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* dt,

@@ -101,10 +101,13 @@ struct HcFrag {
 __host__ __device__ inline HcFrag hc_frag(int64_t P, int64_t N) {
   HcFrag f;
   f.PB = (int)((P + 63) / 64);
-  const int nb2 = 2 * (int)((N + 63) / 64);       // columns written by 64-wide state tiles
-  const int nk = nk_class(N);
-  f.KSW = nk > nb2 ? nk : nb2;
+  f.KSW = nk_class(N);     // chunk_state's n slices cover exactly 32 * KSW columns
   return f;
+}
+// n-slice width of chunk_state: 32 * KSW columns, at most 128 per workgroup
+__host__ __device__ inline int state_nw(int64_t N) {
+  const int w = 32 * nk_class(N);
+  return w < 128 ? w : 128;
 }
 
 // ---- token-major LDS tiles -------------------------------------------------
@@ -138,6 +141,44 @@ __device__ __forceinline__ floatx8 frag_tokens(const float* tile, int stride, in
     f[4 + e] = tile[(tb + e) * stride + c];
   }
   return f;
+}
+
+// ---- direct global -> LDS loads ------------------------------------------------
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// s_waitcnt immediate: wait until at most n vector-memory operations of this
+// wave are outstanding (expcnt and lgkmcnt fields at their maxima = no wait).
+constexpr int vmcnt_imm(int n) {
+  return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (0xF << 8);
+}
+
+// One direct global->LDS load (global_load_lds_dwordx4): lane l's 16 bytes at
+// `gaddr` land at LDS byte address lds + 16 l (lds is wave-uniform, set in M0).
+// Issued as inline assembly so the compiler's wait-count pass does not treat
+// every later LDS read as a possible reader of this write (it cannot tell ring
+// slots apart and would drain all loads before each read, defeating the
+// prefetch); the kernels' own s_waitcnt vmcnt + barrier order the data
+// instead.  Vector-memory operations complete in issue order, so loads the
+// compiler does not see only make its own waits stricter.
+__device__ __forceinline__ void dma16(const void* gaddr, lptr_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gaddr), "s"(base)
+      : "memory", "m0");
+}
+
+// Wait for this wave's loads until at most n (0..3) groups of `per` vector
+// memory operations remain outstanding (the immediate must be a constant).
+template <int per>
+__device__ __forceinline__ void wait_groups(int n) {
+  if (n >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * per));
+  else if (n == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per));
+  else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(per));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // Exchange through LDS between lanes of one wave: every LDS access of this
