@@ -19,8 +19,9 @@
  * "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
  * CUDA Tile", sections 4-9:
  *   1. chunk_cumsum   -- within-chunk running sum of a_t, scaled by log2(e);
- *   2. fwd_pass_state -- per-chunk states by the jump formula and the
- *                        sequential pass of states across chunks;
+ *   2. chunk_state    -- every chunk's own state contribution by the jump
+ *                        formula, all chunks at once;
+ *      state_pass     -- the sequential pass of states across chunks;
  *   3. compute_out    -- causal-masked decayed interaction tile, carried-state
  *                        term and D skip fused, nothing chunk x chunk in HBM.
  * The result equals the token recurrence up to floating-point rounding.
@@ -111,13 +112,15 @@ const char* ssd_last_error_message(void);
 
 /* Workspace bytes that ssd_fwd and ssd_fwd_states need for `prob`:
  * two fp32 [batch, nheads, T*Q] arrays (the base-2 running sums G and dt in
- * [batch, head, token] order) plus the chunk-start states [batch, nheads, T,
- * headdim, dstate] in the io dtype, each segment 256-byte aligned.
+ * [batch, head, token] order), the chunk-start states [batch, nheads, T,
+ * headdim, dstate] in the io dtype (in an internal fragment order, padded to
+ * whole 64-row and 32-column tiles), each segment 256-byte aligned, and 4 KiB
+ * of scratch at the end.
  * Writes the size to *bytes.  Errors: NULL_POINTER, BAD_SHAPE, BAD_CHUNK,
  * BAD_DTYPE, UNSUPPORTED. */
 ssd_status ssd_fwd_workspace_size(const ssd_problem* prob, size_t* bytes);
 
-/* Full forward pass: chunk_cumsum -> fwd_pass_state -> compute_out.
+/* Full forward pass: chunk_cumsum -> chunk_state -> state_pass -> compute_out.
  *   x, dt, A, B, C : inputs (device), layouts above.
  *   D              : [nheads] fp32 skip weights, or NULL for no skip term.
  *   init_state     : [batch, nheads, headdim, dstate] fp32, or NULL for zeros.
@@ -145,7 +148,7 @@ ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, cons
 ssd_status ssd_chunk_cumsum(const ssd_problem* prob, const float* dt, const float* A,
                             float* G_out, float* dt_out, void* stream);
 
-/* Stages 1 and 2 (chunk_cumsum and fwd_pass_state): the state at the start of
+/* Stages 1 and 2 (chunk_cumsum, chunk_state, state_pass): the state at the start of
  * every chunk and the state after the last token, without computing y
  * (devin.kr page above, section "세 가지 핵심 커널 구현", fwd_pass_state;
  * brifing.si page, sections 4, 5 and 8).  Chunk c's contribution is one matrix
@@ -173,7 +176,9 @@ ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* d
  * 9 and 11; the chunk x chunk tile is never written to memory.
  * ssd_fwd is exactly ssd_fwd_states followed by ssd_compute_out.
  *   x, B, C, D, y : as for ssd_fwd (D may be NULL).
- *   workspace     : read only; at least ssd_fwd_workspace_size bytes.
+ *   workspace     : at least ssd_fwd_workspace_size bytes; its running sums
+ *                   and states are only read, its last 4 KiB are scratch
+ *                   that the call may overwrite.
  * Errors as for ssd_fwd. */
 ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B, const void* C,
                            const float* D, void* y, const void* workspace,

@@ -306,14 +306,15 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
 
   // XCD-aware placement: every head set, p slice and row part of one
   // (b, chunk) gets block ids congruent mod 8, so they run on one XCD and
-  // share its L2 copy of the chunk's B and C rows.
-  const int NHS = H / KH;                         // head sets (KH heads of one group)
+  // share its L2 copy of the chunk's B and C rows; neighbouring ids take
+  // different chunks, so the workgroups running at one time spread their
+  // reads over several chunks' rows instead of all reading the same lines.
   const int id = blockIdx.x;
   const int xcd = id % 8, slot_id = id / 8;
-  const int per = NHS * PB * RS;
-  const int bc = (slot_id / per) * 8 + xcd;
+  const int nbx = (nbc + 7) / 8;
+  const int bc = (slot_id % nbx) * 8 + xcd;
   if (bc >= nbc) return;
-  const int hp = slot_id % per;
+  const int hp = slot_id / nbx;
   const int rsi = hp % RS;
   const int hs = hp / RS / PB, pb = hp / RS % PB;
   const int h0 = hs * KH;                         // first head of the set
@@ -573,8 +574,9 @@ int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int64_t H, int64_t G) 
 
 hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
-                              void* y, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                              int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
+                              void* y, void* /*sink*/, int64_t batch, int64_t L, int64_t H,
+                              int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
+                              hipStream_t stream) {
   if (io_bf16)
     return launch_out_t<bf16>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
   return launch_out_t<float>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);

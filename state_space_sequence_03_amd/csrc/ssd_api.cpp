@@ -29,14 +29,16 @@ hipError_t launch_state_pass(int io_bf16, void* S, const float* Gw, const float*
                              int Q, int64_t T_, int64_t ldw, int frag_major, hipStream_t stream);
 hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
-                              void* y, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                              int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream);
+                              void* y, void* sink, int64_t batch, int64_t L, int64_t H, int64_t P,
+                              int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
+                              hipStream_t stream);
 int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int64_t H, int64_t G);
 }  // namespace ssd
 
 namespace {
 
 constexpr int64_t kMaxLds = 160 * 1024;
+constexpr size_t kSinkBytes = 4096;
 thread_local std::string g_last_error;
 
 ssd_status fail(ssd_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -68,7 +70,7 @@ struct Plan {
   int64_t B, L, H, P, N, G, Q, T, Lp;
   int bf16;
   size_t esize;
-  size_t g_off, dt_off, hc_off, bytes;
+  size_t g_off, dt_off, hc_off, sink_off, bytes;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -127,7 +129,9 @@ void workspace_plan(Plan* pl) {
   // 32-column steps)
   const size_t hcsz = size_t(pl->B) * pl->H * pl->T * size_t(ssd::hc_frag(pl->P, pl->N).state_elems()) *
                       pl->esize;
-  pl->bytes = pl->hc_off + align256(hcsz);
+  pl->sink_off = pl->hc_off + align256(hcsz);
+  // scratch for stores that are discarded (rows past the sequence end)
+  pl->bytes = pl->sink_off + kSinkBytes;
 }
 
 ssd_status hip_status(hipError_t e, const char* what) {
@@ -252,8 +256,9 @@ static ssd_status run_out(const Plan& pl, const void* x, const void* B, const vo
   const float* Gw = reinterpret_cast<const float*>(ws + pl.g_off);
   const float* dtw = reinterpret_cast<const float*>(ws + pl.dt_off);
   const void* Hc = ws + pl.hc_off;
-  return hip_status(ssd::launch_compute_out(pl.bf16, x, B, C, Gw, dtw, Hc, D, y, pl.B, pl.L, pl.H,
-                                            pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp, s),
+  void* sink = const_cast<char*>(ws) + pl.sink_off;
+  return hip_status(ssd::launch_compute_out(pl.bf16, x, B, C, Gw, dtw, Hc, D, y, sink, pl.B, pl.L,
+                                            pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp, s),
                     "compute_out launch");
 }
 

@@ -70,9 +70,10 @@ def test_workspace_size_formula(so):
     g = 2 * 8 * Lp * 4
     hc = 2 * 8 * T * 64 * 128 * 2
     r = lambda v: (v + 255) // 256 * 256
-    assert n == r(g) + r(g) + r(hc)
+    sink = 4096
+    assert n == r(g) + r(g) + r(hc) + sink
     st, n32 = ws_status(P(io_dtype=0, dstate=64))
-    assert st == OK and n32 == r(g) + r(g) + r(2 * 8 * T * 64 * 64 * 4)
+    assert st == OK and n32 == r(g) + r(g) + r(2 * 8 * T * 64 * 64 * 4) + sink
 
 
 @pytest.mark.parametrize("kw,code", [
