@@ -12,11 +12,12 @@
 // the transposed dt / decay_cumsum layout).
 //
 // Mapping: one workgroup of 256 threads per (chunk, 16-head tile, batch).
-// The [Q tokens x 16 heads] slab of dt is read row by row (16 contiguous
-// floats per token) into LDS, then each wave scans 4 heads: every lane sums
-// Q/64 consecutive tokens serially, a wave-wide inclusive scan over the lane
-// totals (DPP/permute shuffles) adds the carry, and each lane writes its
-// tokens contiguously.
+// The [Q tokens x 16 heads] slab of dt arrives as 16-byte loads (4 heads of
+// one token per lane) and is transposed through LDS to [head][token].  Each
+// wave then scans 4 heads: a lane takes Q/64 consecutive tokens, sums them
+// serially, a wave-wide inclusive scan over the lane totals adds the carry,
+// and the lane writes its tokens' G and dt as one vector store each, so a
+// wave writes a whole row contiguously.
 //
 // Rows are `ld` floats apart in the outputs; tokens in [L, Lw) are padding
 // (dt = 0, so G holds the chunk's last running sum), which lets the later
@@ -28,43 +29,64 @@ namespace ssd {
 constexpr int kCumsumHeads = 16;
 constexpr int kCumsumThreads = 256;
 
+template <int N>
+struct FloatVec;
+template <> struct FloatVec<1> { typedef float type; };
+template <> struct FloatVec<2> { typedef float type __attribute__((ext_vector_type(2))); };
+template <> struct FloatVec<4> { typedef float type __attribute__((ext_vector_type(4))); };
+
+template <int Q>
 __global__ void __launch_bounds__(kCumsumThreads)
 chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
                     float* __restrict__ G, float* __restrict__ dtT,
-                    int64_t L, int H, int Q, int64_t ld, int64_t Lw) {
-  __shared__ float tile[256][kCumsumHeads + 1];
+                    int64_t L, int H, int64_t ld, int64_t Lw) {
+  constexpr int TPL = Q >= kWave ? Q / kWave : 1;       // tokens per lane
+  constexpr int LANES = Q / TPL;                         // lanes holding tokens
+  typedef typename FloatVec<TPL>::type vec_t;
+  __shared__ __align__(16) float tile[kCumsumHeads][Q + 4];
   const int c = blockIdx.x;
   const int h0 = blockIdx.y * kCumsumHeads;
   const int64_t b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)c * Q;
 
-  // Coalesced load of the [Q x 16] slab (zero outside [0, L) x [0, H)).
-  for (int idx = tid; idx < Q * kCumsumHeads; idx += kCumsumThreads) {
-    const int t = idx / kCumsumHeads, hh = idx % kCumsumHeads;
+  // [Q x 16] slab: lane loads 4 heads of one token (zero outside [0, L) x [0, H))
+  const bool full = h0 + kCumsumHeads <= H && (H % 4) == 0;
+#pragma unroll
+  for (int idx = tid; idx < Q * (kCumsumHeads / 4); idx += kCumsumThreads) {
+    const int t = idx / (kCumsumHeads / 4), h4 = (idx % (kCumsumHeads / 4)) * 4;
     const int64_t tok = t0 + t;
-    const int h = h0 + hh;
-    float v = 0.0f;
-    if (tok < L && h < H) v = dt[(b * L + tok) * H + h];
-    tile[t][hh] = v;
+    floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (tok < L) {
+      const float* src = dt + (b * L + tok) * H + h0 + h4;
+      if (full) {
+        v = *reinterpret_cast<const floatx4*>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = h0 + h4 + e < H ? src[e] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[h4 + e][t] = v[e];
   }
   __syncthreads();
 
   const int lane = tid % kWave, wave = tid / kWave;
-  const int tpl = Q >= kWave ? Q / kWave : 1;      // tokens per lane
-  const int first = lane * tpl;                   // first token of this lane
-  for (int hh = wave; hh < kCumsumHeads; hh += kCumsumThreads / kWave) {
+  const int first = lane * TPL;                         // first token of this lane
+  const bool vec_ok = ld % TPL == 0;                    // vector stores stay aligned
+#pragma unroll
+  for (int k = 0; k < kCumsumHeads / (kCumsumThreads / kWave); ++k) {
+    const int hh = wave + k * (kCumsumThreads / kWave);
     const int h = h0 + hh;
     if (h >= H) break;
     const float a2 = A[h] * kLog2e;
-    float part[4];
+    float part[TPL], raw[TPL];
     float run = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float v = 0.0f;
-      if (k < tpl && first + k < Q) v = tile[first + k][hh] * a2;
-      run += v;
-      part[k] = run;
+    for (int e = 0; e < TPL; ++e) {
+      raw[e] = lane < LANES ? tile[hh][first + e] : 0.0f;
+      run += raw[e] * a2;
+      part[e] = run;
     }
     // inclusive scan of lane totals across the wave
     float incl = run;
@@ -74,28 +96,58 @@ chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
       if (lane >= off) incl += o;
     }
     const float carry = incl - run;
-    float* grow = G + ((int64_t)b * H + h) * ld;
-    float* drow = dtT + ((int64_t)b * H + h) * ld;
+    const int64_t row = ((int64_t)b * H + h) * ld + t0 + first;
+    if (lane < LANES && vec_ok && t0 + first + TPL <= Lw) {
+      vec_t g, d;
+      if constexpr (TPL == 1) {
+        g = carry + part[0];
+        d = raw[0];
+      } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = first + k;
-      const int64_t tok = t0 + t;
-      if (k < tpl && t < Q && tok < Lw) {
-        grow[tok] = carry + part[k];
-        drow[tok] = tile[t][hh];
+        for (int e = 0; e < TPL; ++e) {
+          g[e] = carry + part[e];
+          d[e] = raw[e];
+        }
       }
+      *reinterpret_cast<vec_t*>(G + row) = g;
+      *reinterpret_cast<vec_t*>(dtT + row) = d;
+    } else if (lane < LANES) {
+      // rows not vector-aligned, or the end of the row: element by element
+#pragma unroll
+      for (int e = 0; e < TPL; ++e)
+        if (t0 + first + e < Lw) {
+          G[row + e] = carry + part[e];
+          dtT[row + e] = raw[e];
+        }
     }
   }
 }
 
-// Host launcher.  Q in {32, 64, 128, 256}; grid covers ceil(Lw / Q) chunks.
+// Host launcher.  Q in {32, 64, 128, 256}; grid covers ceil(Lw / Q) chunks;
+// rows of G and dtT are `ld` floats apart.
 hipError_t launch_chunk_cumsum(const float* dt, const float* A, float* G, float* dtT,
                                int64_t batch, int64_t L, int64_t H, int Q, int64_t ld,
                                int64_t Lw, hipStream_t stream) {
   const int64_t T = (Lw + Q - 1) / Q;
   dim3 grid((unsigned)T, (unsigned)((H + kCumsumHeads - 1) / kCumsumHeads), (unsigned)batch);
-  hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(kCumsumThreads), 0, stream, dt, A, G, dtT,
-                     L, (int)H, Q, ld, Lw);
+  switch (Q) {
+    case 32:
+      hipLaunchKernelGGL(chunk_cumsum_kernel<32>, grid, dim3(kCumsumThreads), 0, stream, dt, A, G,
+                         dtT, L, (int)H, ld, Lw);
+      break;
+    case 64:
+      hipLaunchKernelGGL(chunk_cumsum_kernel<64>, grid, dim3(kCumsumThreads), 0, stream, dt, A, G,
+                         dtT, L, (int)H, ld, Lw);
+      break;
+    case 128:
+      hipLaunchKernelGGL(chunk_cumsum_kernel<128>, grid, dim3(kCumsumThreads), 0, stream, dt, A, G,
+                         dtT, L, (int)H, ld, Lw);
+      break;
+    default:
+      hipLaunchKernelGGL(chunk_cumsum_kernel<256>, grid, dim3(kCumsumThreads), 0, stream, dt, A, G,
+                         dtT, L, (int)H, ld, Lw);
+      break;
+  }
   return hipGetLastError();
 }
 
