@@ -153,7 +153,7 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
       const int tok = min(k * kCsTok + r, qv - 1);
       int col = n0 + (pc ^ C::bsw(r)) * V;
       col = col < N ? col : 0;
-      dma16(Bc + (int64_t)tok * bstride + col, (lptr_t)(sl + blk * 1024));
+      dma16(Bc + (int64_t)tok * bstride + col, (sl + blk * 1024));
     }
 #pragma unroll
     for (int i = 0; i < C::XINST; ++i) {
@@ -164,7 +164,7 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
       const int tok = min(k * kCsTok + r, qv - 1);
       int p = p0 + (pc ^ C::xsw(r)) * V;
       p = p < P ? p : p0;
-      dma16(xc + hh * P + (int64_t)tok * xstride + p, (lptr_t)(sl + C::BCH * 16 + blk * 1024));
+      dma16(xc + hh * P + (int64_t)tok * xstride + p, (sl + C::BCH * 16 + blk * 1024));
     }
   };
 
@@ -179,7 +179,7 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
       q = q < nchunk ? q : nchunk - 1;
       const int hh = q / (Q / 2), r = q % (Q / 2);
       const float* src = (r < Q / 4 ? Gw : dtw) + (int64_t)(b * H + h0 + hh) * ldw + t0 + 4 * (r % (Q / 4));
-      dma16(src, (lptr_t)(reinterpret_cast<unsigned char*>(gd) + blk * 1024));
+      dma16(src, (reinterpret_cast<unsigned char*>(gd) + blk * 1024));
     }
   }
   const int npro = min(C::NSLOT - 1, ns);

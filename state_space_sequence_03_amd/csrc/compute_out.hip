@@ -134,7 +134,7 @@ __device__ __forceinline__ void issue_pair(unsigned char* slot, const T* __restr
     int cl = pc ^ S::bsw(r);
     const int tok = min(jp * 32 + r, qv - 1);
     cl = cl * V < N ? cl : 0;
-    dma16(Bc + (int64_t)tok * bstride + cl * V, (lptr_t)(slot + blk * 1024));
+    dma16(Bc + (int64_t)tok * bstride + cl * V, (slot + blk * 1024));
   }
 #pragma unroll
   for (int hh = 0; hh < KH; ++hh)
@@ -148,7 +148,7 @@ __device__ __forceinline__ void issue_pair(unsigned char* slot, const T* __restr
       int p = p0 + cl * V;
       p = p < P ? p : p0;
       dma16(xc + hh * hstep + (int64_t)tok * xstride + p,
-            (lptr_t)(slot + (S::BCH + hh * S::XCH) * 16 + blk * 1024));
+            (slot + (S::BCH + hh * S::XCH) * 16 + blk * 1024));
     }
 }
 

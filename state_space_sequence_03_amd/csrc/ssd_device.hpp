@@ -144,7 +144,6 @@ __device__ __forceinline__ floatx8 frag_tokens(const float* tile, int stride, in
 }
 
 // ---- direct global -> LDS loads ------------------------------------------------
-typedef __attribute__((address_space(3))) void* lptr_t;
 
 // s_waitcnt immediate: wait until at most n vector-memory operations of this
 // wave are outstanding (expcnt and lgkmcnt fields at their maxima = no wait).
@@ -154,13 +153,16 @@ constexpr int vmcnt_imm(int n) {
 
 // One direct global->LDS load (global_load_lds_dwordx4): lane l's 16 bytes at
 // `gaddr` land at LDS byte address lds + 16 l (lds is wave-uniform, set in M0).
+// `lds` is a generic pointer into shared memory: its low 32 bits are the LDS
+// byte address (the shared aperture sits on a 4 GiB boundary), which avoids
+// an address-space cast.
 // Issued as inline assembly so the compiler's wait-count pass does not treat
 // every later LDS read as a possible reader of this write (it cannot tell ring
 // slots apart and would drain all loads before each read, defeating the
 // prefetch); the kernels' own s_waitcnt vmcnt + barrier order the data
 // instead.  Vector-memory operations complete in issue order, so loads the
 // compiler does not see only make its own waits stricter.
-__device__ __forceinline__ void dma16(const void* gaddr, lptr_t lds) {
+__device__ __forceinline__ void dma16(const void* gaddr, const void* lds) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile(
       "s_mov_b32 m0, %1\n\t"

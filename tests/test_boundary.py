@@ -164,3 +164,44 @@ def test_compute_out_validation(so):
     assert so.ssd_compute_out(ctypes.byref(prob), FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, None) == WS
     bad = P(io_dtype=3)
     assert so.ssd_compute_out(ctypes.byref(bad), FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, None) == DTYPE
+
+
+# ------------------------------------------------------------ built device code
+
+LLVM = "/opt/rocm/llvm/bin"
+BUILD_DIR = os.path.join(ROOT, "state_space_sequence_03_amd", "_build")
+KERNEL_OBJECTS = ["chunk_cumsum.o", "chunk_state.o", "state_pass.o", "compute_out.o"]
+
+
+def device_disassembly(obj, tmp_path):
+    """gfx950 disassembly of the device code object built into `obj`."""
+    fat = tmp_path / (obj + ".fatbin")
+    dev = tmp_path / (obj + ".co")
+    subprocess.run([f"{LLVM}/llvm-objcopy", "--dump-section", f".hip_fatbin={fat}",
+                    os.path.join(BUILD_DIR, obj), str(tmp_path / (obj + ".host"))], check=True)
+    subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o", f"--input={fat}",
+                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={dev}"], check=True)
+    out = subprocess.run([f"{LLVM}/llvm-objdump", "-d", str(dev)], check=True,
+                         capture_output=True, text=True).stdout
+    return [l.split("//")[0].strip() for l in out.splitlines() if l.startswith("\t")]
+
+
+@pytest.mark.skipif(not os.path.exists(f"{LLVM}/llvm-objdump"), reason="ROCm LLVM tools not installed")
+@pytest.mark.parametrize("obj", KERNEL_OBJECTS)
+def test_device_code_m0_and_scalar_stores(so, obj, tmp_path):
+    # The direct-to-LDS load helper sets M0 in inline assembly; the compiler is
+    # told M0 is clobbered there but may not honour that, so the built code
+    # must write M0 nowhere else: every M0 write is followed (after at most an
+    # s_nop) by the global_load_lds it configures.  No kernel writes memory
+    # through the scalar data cache either.
+    insts = device_disassembly(obj, tmp_path)
+    assert insts, "no device code found"
+    for k, ins in enumerate(insts):
+        op = ins.split()[0] if ins else ""
+        assert not re.match(r"s_(store|atomic|buffer_store|buffer_atomic|scratch_store|dcache_wb|dcache_discard)", op), ins
+        fields = [f.strip() for f in ins[len(op):].split(",")]
+        if fields and fields[0] == "m0" and op.startswith("s_"):
+            nxt = [i for i in insts[k + 1:k + 3] if not i.startswith("s_nop")]
+            assert nxt and nxt[0].startswith("global_load_lds"), (obj, ins, insts[k + 1:k + 3])
+    if obj in ("chunk_state.o", "compute_out.o"):
+        assert any(i.startswith("global_load_lds_dwordx4") for i in insts)
