@@ -152,6 +152,65 @@ __device__ __forceinline__ void issue_pair(unsigned char* slot, const T* __restr
     }
 }
 
+// The same loads for a pair whose 32 tokens all lie inside the sequence: the
+// per-lane parts of the addresses (row within the pair, clamped column) do
+// not depend on the pair, so they are byte offsets computed once, and each
+// pair only moves the wave-uniform row base.
+template <typename T, int NK, int KH>
+struct PairOffsets {
+  uint32_t b[Slot<T, NK, KH>::BINST];
+  uint32_t x[KH][Slot<T, NK, KH>::XINST];
+};
+
+template <typename T, int NK, int KH>
+__device__ __forceinline__ PairOffsets<T, NK, KH> pair_offsets(int64_t bstride, int N,
+                                                               int64_t xstride, int64_t hstep,
+                                                               int p0, int P, int wave, int lane) {
+  typedef Slot<T, NK, KH> S;
+  constexpr int V = S::V;
+  constexpr int NBB = S::BCH / 64, NXB = S::XCH / 64;
+  PairOffsets<T, NK, KH> o;
+#pragma unroll
+  for (int k = 0; k < S::BINST; ++k) {
+    const int q = ((k * 4 + wave) % NBB) * 64 + lane;
+    const int r = q / S::BC, pc = q % S::BC;
+    int cl = pc ^ S::bsw(r);
+    cl = cl * V < N ? cl : 0;
+    o.b[k] = (uint32_t)(((int64_t)r * bstride + cl * V) * (int64_t)sizeof(T));
+  }
+#pragma unroll
+  for (int hh = 0; hh < KH; ++hh)
+#pragma unroll
+    for (int k = 0; k < S::XINST; ++k) {
+      const int q = ((k * 4 + wave) % NXB) * 64 + lane;
+      const int r = q / S::XC, pc = q % S::XC;
+      const int cl = pc ^ S::xsw(r);
+      int p = p0 + cl * V;
+      p = p < P ? p : p0;
+      o.x[hh][k] = (uint32_t)((hh * hstep + (int64_t)r * xstride + p) * (int64_t)sizeof(T));
+    }
+  return o;
+}
+
+template <typename T, int NK, int KH>
+__device__ __forceinline__ void issue_pair_fast(unsigned char* slot, const PairOffsets<T, NK, KH>& o,
+                                                const T* __restrict__ Bc, int64_t bstride,
+                                                const T* __restrict__ xc, int64_t xstride, int jp,
+                                                int wave) {
+  typedef Slot<T, NK, KH> S;
+  constexpr int NBB = S::BCH / 64, NXB = S::XCH / 64;
+  const T* bb = Bc + (int64_t)jp * 32 * bstride;
+  const T* xb = xc + (int64_t)jp * 32 * xstride;
+#pragma unroll
+  for (int k = 0; k < S::BINST; ++k)
+    dma16_so(bb, o.b[k], slot + ((k * 4 + wave) % NBB) * 1024);
+#pragma unroll
+  for (int hh = 0; hh < KH; ++hh)
+#pragma unroll
+    for (int k = 0; k < S::XINST; ++k)
+      dma16_so(xb, o.x[hh][k], slot + (S::BCH + hh * S::XCH) * 16 + ((k * 4 + wave) % NXB) * 1024);
+}
+
 // A operand of S^T = B C^T: lane row j of the pair, n = n0 .. n0+7.
 template <typename T, int NK, int KH>
 __device__ __forceinline__ typename FragOf<T>::type slot_b_frag(const unsigned char* slot, int j,
@@ -197,13 +256,15 @@ __device__ __forceinline__ typename FragOf<T>::type slot_x_frag(const unsigned c
 }
 
 // Per-wave state: the wave's row blocks (slot 0 = the later one), their C
-// fragments and the KH heads' accumulators.
+// fragments, the KH heads' accumulators and each block's reference running
+// sum G_r (r = 32 q - 1, the token before the block's band; 0 for q = 0).
 template <typename T, int NK, int IB, int KH>
 struct WaveRows {
   typedef typename FragOf<T>::type frag_t;
   int ib[IB], q[IB];
   frag_t cf[IB][NK];
   floatx4 acc[KH][IB][4];
+  float gr[KH][IB];
 };
 
 // One token pair for the first NS row blocks of the wave; if BAND, the last
@@ -243,7 +304,7 @@ __device__ __forceinline__ void pair_step(WaveRows<T, NK, IB, KH>& w, const unsi
       frag_t af;
       if (!(BAND && s == NS - 1)) {
         // left of the block's band: weight exp2(G_r - G_e) * e_j (both <= 1)
-        const float f = fast_exp2(G[32 * w.q[s] - 1] - g_end);
+        const float f = fast_exp2(w.gr[hh][s] - g_end);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           af[r] = to_io<T>(st[s][0][r] * (e0[r] * f));
@@ -251,8 +312,8 @@ __device__ __forceinline__ void pair_step(WaveRows<T, NK, IB, KH>& w, const unsi
         }
       } else {
         // the band: first scale rows i = 16 ib + 4 lg + r by exp2(G_i - G_r)
-        const int ib = w.ib[s], q = w.q[s];
-        const float gref = q >= 1 ? G[32 * q - 1] : 0.0f;
+        const int ib = w.ib[s];
+        const float gref = w.gr[hh][s];
         const floatx4 gr = *reinterpret_cast<const floatx4*>(G + ib * 16 + 4 * lg);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -343,11 +404,20 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
   // first ring pairs, the block's C fragments and the chunk-start state
   // fragments; one memory round trip instead of one per fragment group.
   const int64_t hstep = P;
+  const PairOffsets<T, NK, KH> poff =
+      pair_offsets<T, NK, KH>(bstride, N, xstride, hstep, p0, P, wave, lane);
+  // byte offsets within a pair fit 32 bits (checked once, uniform)
+  const bool off32 = (int64_t)32 * (xstride + bstride) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
+  auto issue = [&](int jn) {
+    unsigned char* sl = ring + (jn % NSLOT) * S::BYTES;
+    if (off32 && (jn + 1) * 32 <= qv)
+      issue_pair_fast<T, NK, KH>(sl, poff, Bc, bstride, xc, xstride, jn, wave);
+    else
+      issue_pair<T, NK, KH>(sl, Bc, bstride, N, xc, xstride, hstep, p0, P, jn, qv, wave, lane);
+  };
 #pragma unroll
   for (int k = 0; k < NSLOT - 1; ++k)
-    if (k < npairs)
-      issue_pair<T, NK, KH>(ring + k * S::BYTES, Bc, bstride, N, xc, xstride, hstep, p0, P, k,
-                            qv, wave, lane);
+    if (k < npairs) issue(k);
 
   WaveRows<T, NK, IB, KH> w;
   bool own[IB];
@@ -420,8 +490,9 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
 #pragma unroll
     for (int s = 0; s < IB; ++s) {
       const int q = w.q[s];
+      w.gr[hh][s] = q >= 1 ? Gs[hh * Q + 32 * q - 1] : 0.0f;
       if (q >= 1) {
-        const float sref = fast_exp2(Gs[hh * Q + 32 * q - 1]);
+        const float sref = fast_exp2(w.gr[hh][s]);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt] *= sref;
       }
@@ -431,64 +502,78 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
   const int q0 = nown >= 1 ? w.q[0] : -1;
   const int q1 = nown >= 2 ? w.q[IB - 1] : -1;
 
-  // ---- stream the token pairs ---------------------------------------------------
-  for (int jp = 0; jp < npairs; ++jp) {
-    // pair jp was issued NSLOT-1 pairs ago: wait until at most the loads of the
-    // pairs after it (min(NSLOT-2, npairs-1-jp) of them) are outstanding.  Vector
-    // memory operations retire in issue order, so this covers pair jp; global
-    // stores issued since only make the wait stricter.
-    {
-      const int ahead = min(NSLOT - 2, npairs - 1 - jp);
-      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::LPG));
-      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LPG));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
+  // pair jp was issued NSLOT-1 pairs ago: wait until at most the loads of the
+  // pairs after it (min(NSLOT-2, npairs-1-jp) of them) are outstanding.  Vector
+  // memory operations retire in issue order, so this covers pair jp; global
+  // stores issued since only make the wait stricter.  Then refill the slot
+  // freed by pair jp-1.
+  auto sync_pair = [&](int jp) {
+    const int ahead = min(NSLOT - 2, npairs - 1 - jp);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::LPG));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LPG));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    {
-      const int nxt = jp + NSLOT - 1;               // refill the slot freed by pair jp-1
-      if (nxt < npairs)
-        issue_pair<T, NK, KH>(ring + (nxt % NSLOT) * S::BYTES, Bc, bstride, N, xc, xstride, hstep,
-                              p0, P, nxt, qv, wave, lane);
-    }
-    const unsigned char* sl = ring + (jp % NSLOT) * S::BYTES;
-    int done = -1;                                  // block (slot) finished at this pair
-    if (IB == 2 && jp < q1) {
-      pair_step<T, NK, IB, KH, IB, false>(w, sl, jp, Gs, ds, es, Q, dh, lane);
-    } else if (IB == 2 && jp == q1) {
-      pair_step<T, NK, IB, KH, IB, true>(w, sl, jp, Gs, ds, es, Q, dh, lane);
-      done = IB - 1;
-    } else if (jp < q0) {
-      pair_step<T, NK, IB, KH, 1, false>(w, sl, jp, Gs, ds, es, Q, dh, lane);
-    } else if (jp == q0) {
-      pair_step<T, NK, IB, KH, 1, true>(w, sl, jp, Gs, ds, es, Q, dh, lane);
-      done = 0;
-    }
-    if (done >= 0) {
-      // block finished: accumulators -> LDS (io dtype) -> 16-byte row pieces
-      const int ibd = done == 0 ? w.ib[0] : w.ib[IB - 1];
+    const int nxt = jp + NSLOT - 1;
+    if (nxt < npairs) issue(nxt);
+  };
+  // a finished block: accumulators -> LDS (io dtype) -> 16-byte row pieces
+  auto store_block = [&](int done) {
+    const int ibd = done == 0 ? w.ib[0] : w.ib[IB - 1];
 #pragma unroll
-      for (int hh = 0; hh < KH; ++hh) {
+    for (int hh = 0; hh < KH; ++hh) {
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
+      for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float v = done == 0 ? w.acc[hh][0][pt][r] : w.acc[hh][IB - 1][pt][r];
-            ys[(4 * lg + r) * lay.yrow + pt * 16 + lr] = to_io<T>(v);
-          }
-        wave_sync();
-        constexpr int RV = kOutP / V;
-#pragma unroll
-        for (int idx = lane; idx < 16 * RV; idx += kWave) {
-          const int rr = idx / RV, piece = idx % RV;
-          const int i2 = ibd * 16 + rr, p = p0 + piece * V;
-          if (i2 < qv && p < P)
-            store16(y + (((int64_t)b * L + t0 + i2) * H + h0 + hh) * P + p,
-                    load16(ys + rr * lay.yrow + piece * V));
+        for (int r = 0; r < 4; ++r) {
+          const float v = done == 0 ? w.acc[hh][0][pt][r] : w.acc[hh][IB - 1][pt][r];
+          ys[(4 * lg + r) * lay.yrow + pt * 16 + lr] = to_io<T>(v);
         }
-        wave_sync();
+      wave_sync();
+      constexpr int RV = kOutP / V;
+#pragma unroll
+      for (int idx = lane; idx < 16 * RV; idx += kWave) {
+        const int rr = idx / RV, piece = idx % RV;
+        const int i2 = ibd * 16 + rr, p = p0 + piece * V;
+        if (i2 < qv && p < P)
+          store16(y + (((int64_t)b * L + t0 + i2) * H + h0 + hh) * P + p,
+                  load16(ys + rr * lay.yrow + piece * V));
       }
+      wave_sync();
+    }
+  };
+
+  // ---- stream the token pairs ---------------------------------------------------
+  // Phases with one pair step each, so every loop body keeps the accumulators
+  // in place: both blocks left of the earlier block's band, that band, the
+  // later block alone, its band, then pairs this wave only helps to load.
+  int jp = 0;
+  if constexpr (IB == 2) {
+    if (nown == 2) {
+      for (; jp < q1; ++jp) {
+        sync_pair(jp);
+        pair_step<T, NK, IB, KH, IB, false>(w, ring + (jp % NSLOT) * S::BYTES, jp, Gs, ds, es, Q,
+                                            dh, lane);
+      }
+      sync_pair(jp);
+      pair_step<T, NK, IB, KH, IB, true>(w, ring + (jp % NSLOT) * S::BYTES, jp, Gs, ds, es, Q, dh,
+                                         lane);
+      store_block(IB - 1);
+      ++jp;
     }
   }
+  if (nown >= 1) {
+    for (; jp < q0; ++jp) {
+      sync_pair(jp);
+      pair_step<T, NK, IB, KH, 1, false>(w, ring + (jp % NSLOT) * S::BYTES, jp, Gs, ds, es, Q, dh,
+                                         lane);
+    }
+    sync_pair(jp);
+    pair_step<T, NK, IB, KH, 1, true>(w, ring + (jp % NSLOT) * S::BYTES, jp, Gs, ds, es, Q, dh,
+                                      lane);
+    store_block(0);
+    ++jp;
+  }
+  for (; jp < npairs; ++jp) sync_pair(jp);
   // every load into LDS was waited for inside the loop (the last pair with
   // vmcnt(0)); only global stores may still be in flight here
 }

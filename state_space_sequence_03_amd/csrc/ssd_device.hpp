@@ -173,6 +173,27 @@ __device__ __forceinline__ void dma16(const void* gaddr, const void* lds) {
       : "memory", "m0");
 }
 
+// The same load with a wave-uniform 64-bit base held in SGPRs and a per-lane
+// 32-bit byte offset (the instruction's saddr form): a stream that advances
+// by whole rows only moves the base, so its per-lane offsets stay in
+// registers and no 64-bit address arithmetic is repeated per load.
+__device__ __forceinline__ void dma16_so(const void* base, uint32_t off, const void* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  // the builtin returns a signed int: take each half back as uint32_t before
+  // widening, or a low word with bit 31 set would sign-extend into the high word
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(bs), "s"(m)
+      : "memory", "m0");
+}
+
 // Wait for this wave's loads until at most n (0..3) groups of `per` vector
 // memory operations remain outstanding (the immediate must be a constant).
 template <int per>

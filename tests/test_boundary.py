@@ -205,3 +205,10 @@ def test_device_code_m0_and_scalar_stores(so, obj, tmp_path):
             assert nxt and nxt[0].startswith("global_load_lds"), (obj, ins, insts[k + 1:k + 3])
     if obj in ("chunk_state.o", "compute_out.o"):
         assert any(i.startswith("global_load_lds_dwordx4") for i in insts)
+    # The saddr form of those loads takes a 64-bit SGPR base assembled from two
+    # readfirstlane results.  The builtin returns a signed int, so widening it
+    # directly sign-extends the low word (s_bfe_i64 ..., 0x200000) and the base
+    # is invalid whenever bit 31 of the address is set; no kernel here needs a
+    # signed 64-bit bitfield extract otherwise.
+    if any(re.match(r"global_load_lds_dwordx4 v\d+, s\[", i) for i in insts):
+        assert not any(i.startswith("s_bfe_i64") for i in insts), obj
