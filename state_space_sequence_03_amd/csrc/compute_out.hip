@@ -91,15 +91,12 @@ struct Slot {
 };
 
 struct OutLayout {
-  int yrow;                   // LDS row length of the output staging tile (elements)
-  int g_off, d_off, e_off, ring_off, y_off, bytes, slot_bytes, nslot;
+  int g_off, d_off, e_off, ring_off, bytes, slot_bytes, nslot;
 };
 
 template <typename T, int NK, int KH>
 __host__ __device__ inline OutLayout out_layout(int Q) {
   OutLayout o;
-  const int pad = 16 / (int)sizeof(T);
-  o.yrow = kOutP + pad;
   o.slot_bytes = Slot<T, NK, KH>::BYTES;
   o.nslot = Slot<T, NK, KH>::NSLOT;
   int off = 0;
@@ -107,7 +104,6 @@ __host__ __device__ inline OutLayout out_layout(int Q) {
   o.d_off = off; off += KH * Q * 4;
   o.e_off = off; off += KH * Q * 4;
   o.ring_off = off; off += o.nslot * o.slot_bytes;
-  o.y_off = off; off += 4 * 16 * o.yrow * (int)sizeof(T);
   o.bytes = off;
   return o;
 }
@@ -311,21 +307,17 @@ __device__ __forceinline__ void pair_step(WaveRows<T, NK, IB, KH>& w, const unsi
           af[4 + r] = to_io<T>(st[s][1][r] * (e1[r] * f));
         }
       } else {
-        // the band: first scale rows i = 16 ib + 4 lg + r by exp2(G_i - G_r)
+        // the band: first scale row i = 16 ib + lr (this lane's accumulator
+        // column) by exp2(G_i - G_r)
         const int ib = w.ib[s];
-        const float gref = w.gr[hh][s];
-        const floatx4 gr = *reinterpret_cast<const floatx4*>(G + ib * 16 + 4 * lg);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float u = fast_exp2(gr[r] - gref);
-#pragma unroll
-          for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt][r] *= u;
-        }
-        // lane holds row i = 16 ib + lr and tokens j = jb + 16 t + 4 lg + r; the
-        // exponent is masked to -inf before exp2, so no positive exponent is
-        // ever evaluated; the skip weight D_h rides on the diagonal
         const int i = ib * 16 + lr;
         const float gi = G[i];
+        const float u = fast_exp2(gi - w.gr[hh][s]);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt] *= u;
+        // lane holds row i and tokens j = jb + 16 t + 4 lg + r; the exponent is
+        // masked to -inf before exp2, so no positive exponent is ever
+        // evaluated; the skip weight D_h rides on the diagonal
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const floatx4 gj = *reinterpret_cast<const floatx4*>(G + jb + 16 * t + 4 * lg);
@@ -341,7 +333,7 @@ __device__ __forceinline__ void pair_step(WaveRows<T, NK, IB, KH>& w, const unsi
         }
       }
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt] = mma(w.acc[hh][s][pt], af, xf[pt]);
+      for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt] = mma(w.acc[hh][s][pt], xf[pt], af);
     }
   }
 }
@@ -363,7 +355,6 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
   float* ds = reinterpret_cast<float*>(smem + lay.d_off);
   float* es = reinterpret_cast<float*>(smem + lay.e_off);
   unsigned char* ring = smem + lay.ring_off;
-  T* ysall = reinterpret_cast<T*>(smem + lay.y_off);
 
   // XCD-aware placement: every head set, p slice and row part of one
   // (b, chunk) gets block ids congruent mod 8, so they run on one XCD and
@@ -472,8 +463,8 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
       floatx4 a = floatx4{0.f, 0.f, 0.f, 0.f}, a2 = a;
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        a = mma(a, w.cf[0][ks], hf[hh][pt][ks]);
-        if (IB == 2) a2 = mma(a2, w.cf[IB - 1][ks], hf[hh][pt][ks]);
+        a = mma(a, hf[hh][pt][ks], w.cf[0][ks]);
+        if (IB == 2) a2 = mma(a2, hf[hh][pt][ks], w.cf[IB - 1][ks]);
       }
       w.acc[hh][0][pt] = a;
       if (IB == 2) w.acc[hh][IB - 1][pt] = a2;
@@ -498,7 +489,6 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
       }
     }
 
-  T* ys = ysall + wave * 16 * lay.yrow;
   const int q0 = nown >= 1 ? w.q[0] : -1;
   const int q1 = nown >= 2 ? w.q[IB - 1] : -1;
 
@@ -516,29 +506,27 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
     const int nxt = jp + NSLOT - 1;
     if (nxt < npairs) issue(nxt);
   };
-  // a finished block: accumulators -> LDS (io dtype) -> 16-byte row pieces
+  // a finished block: lane holds row i = 16 ib + lr and the 4 consecutive p
+  // columns 16 pt + 4 lg .. +3 of every tile, stored straight from registers
+  const bool vec4 = (P % 4) == 0;
   auto store_block = [&](int done) {
-    const int ibd = done == 0 ? w.ib[0] : w.ib[IB - 1];
+    const int i2 = (done == 0 ? w.ib[0] : w.ib[IB - 1]) * 16 + lr;
+    if (i2 >= qv) return;
 #pragma unroll
     for (int hh = 0; hh < KH; ++hh) {
+      T* yrow = y + (((int64_t)b * L + t0 + i2) * H + h0 + hh) * P;
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
+      for (int pt = 0; pt < 4; ++pt) {
+        const floatx4 v = done == 0 ? w.acc[hh][0][pt] : w.acc[hh][IB - 1][pt];
+        const int p = p0 + pt * 16 + 4 * lg;
+        if (vec4 && p + 4 <= P) {
+          store4<T>(yrow + p, v);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = done == 0 ? w.acc[hh][0][pt][r] : w.acc[hh][IB - 1][pt][r];
-          ys[(4 * lg + r) * lay.yrow + pt * 16 + lr] = to_io<T>(v);
+          for (int r = 0; r < 4; ++r)
+            if (p + r < P) yrow[p + r] = to_io<T>(v[r]);
         }
-      wave_sync();
-      constexpr int RV = kOutP / V;
-#pragma unroll
-      for (int idx = lane; idx < 16 * RV; idx += kWave) {
-        const int rr = idx / RV, piece = idx % RV;
-        const int i2 = ibd * 16 + rr, p = p0 + piece * V;
-        if (i2 < qv && p < P)
-          store16(y + (((int64_t)b * L + t0 + i2) * H + h0 + hh) * P + p,
-                  load16(ys + rr * lay.yrow + piece * V));
       }
-      wave_sync();
     }
   };
 

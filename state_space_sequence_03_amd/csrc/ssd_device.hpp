@@ -58,6 +58,19 @@ __device__ __forceinline__ vec16 load16(const T* p) { return *reinterpret_cast<c
 template <typename T>
 __device__ __forceinline__ void store16(T* p, vec16 v) { *reinterpret_cast<vec16*>(p) = v; }
 
+// Store 4 consecutive io elements converted from fp32 (8 bytes bf16, 16 bytes
+// fp32); p must be aligned to that size.
+template <typename T> __device__ __forceinline__ void store4(T* p, floatx4 v);
+template <> __device__ __forceinline__ void store4<bf16>(bf16* p, floatx4 v) {
+  bf16x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = static_cast<bf16>(v[e]);
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+template <> __device__ __forceinline__ void store4<float>(float* p, floatx4 v) {
+  *reinterpret_cast<floatx4*>(p) = v;
+}
+
 // Load one fragment (8 consecutive k values) from memory where k is contiguous.
 __device__ __forceinline__ bf16x8 load_frag(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
