@@ -391,9 +391,15 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
   const T* Cc = Cm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N;
 
   // ---- prologue ----------------------------------------------------------------
-  // Every global load of the prologue is issued before any of it is used: the
-  // first ring pairs, the block's C fragments and the chunk-start state
-  // fragments; one memory round trip instead of one per fragment group.
+  // The chunk-start states of the KH heads are staged once per workgroup in
+  // the ring slots the first pairs leave free (slots 2 .. NSLOT-1) when they
+  // fit, instead of every wave reading all of them from global memory; the
+  // first ring pairs are issued at the same time, and every global load of
+  // the prologue is issued before any of it is used.
+  constexpr int kFragBytes = 64 * (int)sizeof(frag_t);
+  constexpr int kHBytes = KH * 4 * NK * kFragBytes;
+  constexpr bool kStageH = NSLOT >= 3 && kHBytes <= (NSLOT - 2) * S::BYTES;
+  constexpr int kPro = kStageH ? 2 : NSLOT - 1;    // pairs issued before the states are used
   const int64_t hstep = P;
   const PairOffsets<T, NK, KH> poff =
       pair_offsets<T, NK, KH>(bstride, N, xstride, hstep, p0, P, wave, lane);
@@ -406,9 +412,6 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
     else
       issue_pair<T, NK, KH>(sl, Bc, bstride, N, xc, xstride, hstep, p0, P, jn, qv, wave, lane);
   };
-#pragma unroll
-  for (int k = 0; k < NSLOT - 1; ++k)
-    if (k < npairs) issue(k);
 
   WaveRows<T, NK, IB, KH> w;
   bool own[IB];
@@ -425,6 +428,8 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
 #pragma unroll
   for (int s = 0; s < IB; ++s) nown += own[s] ? 1 : 0;
   if (IB == 2 && !own[0] && own[1]) { w.ib[0] = w.ib[IB - 1]; w.q[0] = w.q[IB - 1]; }
+  // loads the compiler tracks come first: its own waits for them then never
+  // cover the direct-to-LDS loads issued after them
 #pragma unroll
   for (int s = 0; s < IB; ++s)
 #pragma unroll
@@ -433,28 +438,76 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
       w.cf[s][ks] = (s < nown && i < qv && n < N) ? load_frag(Cc + (int64_t)i * bstride + n)
                                                    : zero_frag<T>();
     }
-  // chunk-start states, fragment-major: each load is one contiguous 1 KiB read
-  const HcFrag hcl = hc_frag(P, N);
-  frag_t hf[KH][4][NK];
+  float gv[2], dv[2];                               // KH * Q <= 2 * kOutThreads
 #pragma unroll
-  for (int hh = 0; hh < KH; ++hh) {
-    const T* hsrc = Hc + ((int64_t)(b * H + h0 + hh) * T_ + c) * hcl.state_elems();
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks)
-        hf[hh][pt][ks] = (ks * 32 + lg * 8 < N) ? load_frag(hsrc + hcl.offset(pb, pt, ks, lane))
-                                                 : zero_frag<T>();
-  }
-  for (int idx = tid; idx < KH * Q; idx += kOutThreads) {
-    const int hh = idx / Q, j = idx % Q;
-    const int64_t row = (int64_t)(b * H + h0 + hh) * ldw + t0;
-    Gs[idx] = Gw[row + j];
-    ds[idx] = dtw[row + j];
+  for (int u = 0; u < 2; ++u) {
+    const int idx = tid + u * kOutThreads;
+    gv[u] = 0.0f;
+    dv[u] = 0.0f;
+    if (idx < KH * Q) {
+      const int64_t row = (int64_t)(b * H + h0 + idx / Q) * ldw + t0;
+      gv[u] = Gw[row + idx % Q];
+      dv[u] = dtw[row + idx % Q];
+    }
   }
   float dh[KH];
 #pragma unroll
   for (int hh = 0; hh < KH; ++hh) dh[hh] = Dv ? Dv[h0 + hh] : 0.0f;
+  const HcFrag hcl = hc_frag(P, N);
+  // chunk-start states, fragment-major: for one head and p slice the 4 x NK
+  // fragments are one contiguous run
+  auto hc_src = [&](int hh) {
+    return Hc + ((int64_t)(b * H + h0 + hh) * T_ + c) * hcl.state_elems() + hcl.offset(pb, 0, 0, 0);
+  };
+#pragma unroll
+  for (int k = 0; k < kPro; ++k)
+    if (k < npairs) issue(k);
+  frag_t hf[KH][4][NK];
+  if constexpr (kStageH) {
+    unsigned char* hstage = ring + 2 * S::BYTES;
+    constexpr int kPer = kHBytes / 1024 / 4;        // 1 KiB loads per wave
+    constexpr int kHeadK = 4 * NK * kFragBytes / 1024;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int g = k * 4 + wave;
+      dma16(reinterpret_cast<const unsigned char*>(hc_src(g / kHeadK)) + (g % kHeadK) * 1024 + lane * 16,
+            hstage + g * 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (tid + u * kOutThreads < KH * Q) {
+        Gs[tid + u * kOutThreads] = gv[u];
+        ds[tid + u * kOutThreads] = dv[u];
+      }
+    __syncthreads();                                // states, G, dt visible
+#pragma unroll
+    for (int hh = 0; hh < KH; ++hh)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          const unsigned char* f = hstage + ((hh * 4 + pt) * NK + ks) * kFragBytes;
+          hf[hh][pt][ks] = (ks * 32 + lg * 8 < N) ? lds_frag<T>(f, lane) : zero_frag<T>();
+        }
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < KH; ++hh)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks)
+          hf[hh][pt][ks] = (ks * 32 + lg * 8 < N)
+                               ? load_frag(hc_src(hh) + hcl.offset(0, pt, ks, lane))
+                               : zero_frag<T>();
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (tid + u * kOutThreads < KH * Q) {
+        Gs[tid + u * kOutThreads] = gv[u];
+        ds[tid + u * kOutThreads] = dv[u];
+      }
+    __syncthreads();                                // G, dt visible
+  }
   // carried-state term C_i . H_c for every head
 #pragma unroll
   for (int hh = 0; hh < KH; ++hh)
@@ -469,7 +522,6 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
       w.acc[hh][0][pt] = a;
       if (IB == 2) w.acc[hh][IB - 1][pt] = a2;
     }
-  __syncthreads();                                  // G, dt visible
   // e_j = exp2(G_e - G_j) dt_j, e = last token of j's pair (<= dt_j)
   for (int idx = tid; idx < KH * Q; idx += kOutThreads) {
     const int j = idx % Q;
@@ -488,6 +540,13 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
         for (int pt = 0; pt < 4; ++pt) w.acc[hh][s][pt] *= sref;
       }
     }
+  if constexpr (kStageH) {
+    // every wave has its states: the staging slots go back to the ring
+    __syncthreads();
+#pragma unroll
+    for (int k = kPro; k < NSLOT - 1; ++k)
+      if (k < npairs) issue(k);
+  }
 
   const int q0 = nown >= 1 ? w.q[0] : -1;
   const int q1 = nown >= 2 ? w.q[IB - 1] : -1;

@@ -84,6 +84,18 @@ __device__ __forceinline__ floatx8 load_frag(const float* p) {
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   return r;
 }
+// A fragment stored lane-contiguously in LDS (the fragment-major order below):
+// lane l's 8 values at f + l * sizeof(fragment).
+template <typename T>
+__device__ __forceinline__ typename FragOf<T>::type lds_frag(const unsigned char* f, int lane);
+template <> __device__ __forceinline__ bf16x8 lds_frag<bf16>(const unsigned char* f, int lane) {
+  return *reinterpret_cast<const bf16x8*>(f + lane * 16);
+}
+template <> __device__ __forceinline__ floatx8 lds_frag<float>(const unsigned char* f, int lane) {
+  const floatx4 lo = *reinterpret_cast<const floatx4*>(f + lane * 32);
+  const floatx4 hi = *reinterpret_cast<const floatx4*>(f + lane * 32 + 16);
+  return floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
 template <typename T> __device__ __forceinline__ typename FragOf<T>::type zero_frag() {
   typename FragOf<T>::type z;
 #pragma unroll
@@ -93,9 +105,9 @@ template <typename T> __device__ __forceinline__ typename FragOf<T>::type zero_f
 
 
 // ---- fragment-major chunk-start states -------------------------------------
-// fwd_pass_state leaves the chunk-start states H_c in the workspace in the order
-// compute_out consumes them as MFMA B operands, so that every fragment load is
-// one contiguous 1 KiB read for the wave.  For chunk state (b, h, c) [P x N],
+// The state stage leaves the chunk-start states H_c in the workspace in the
+// order compute_out consumes them as MFMA operands, so that every fragment
+// load is one contiguous 1 KiB read for the wave.  For chunk state (b, h, c) [P x N],
 // 64-row p slice pb, 16-row tile pt, 32-column step ks and lane l, 8
 // consecutive elements H[64 pb + 16 pt + l%16][32 ks + 8 (l/16) + e] are stored
 // at element offset (((pb * 4 + pt) * KSW + ks) * 64 + l) * 8 of the state.
