@@ -52,7 +52,42 @@
 namespace ssd {
 
 constexpr int kOutThreads = 256;
+constexpr int kOutWaves = kOutThreads / kWave;
 constexpr int kOutP = 64;     // p slice per workgroup
+constexpr int kSpinLimit = 1 << 16;
+constexpr int kOutStaticLds = 256;   // bound on the kernel's static LDS (the slot counters)
+
+// Waves of a workgroup hand ring slots to each other through LDS counters
+// instead of a barrier per token pair, so a wave that finishes a pair early
+// (no band block in it) moves on to the next one while another still works
+// on its band.  Each slot has an arrival count (one per wave whose share of
+// the slot's loads has landed) and a release count (one per wave done
+// reading it); both only grow, by kOutWaves per use of the slot.
+//
+// Wait until an LDS counter reaches `target`.  The wait is bounded: past the
+// bound the wave goes on and sets bit 0 of *flag rather than hang the
+// workgroup (the protocol cannot deadlock, so this marks a bug).
+__device__ __forceinline__ void wait_count(int* ctr, int target, int* flag, int lane) {
+  for (int spins = 0;; ++spins) {
+    // an atomic (not volatile) load, so it stays an LDS read
+    const int v = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (v >= target) break;
+    if (spins >= kSpinLimit) {
+      if (lane == 0) atomicOr(flag, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Add one to an LDS counter after this wave's earlier LDS reads completed.
+__device__ __forceinline__ void bump_count(int* ctr, int lane) {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __asm__ __volatile__("" ::: "memory");
+}
 
 // One ring slot holds a token pair (32 tokens): B rows over all of n (padded
 // to 32*NK columns) and, for each of the KH heads, x rows over the
@@ -343,13 +378,15 @@ __global__ void __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_e
 compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
                    const float* __restrict__ Gw, const float* __restrict__ dtw,
                    const T* __restrict__ Hc, const float* __restrict__ Dv, T* __restrict__ y,
-                   int64_t L, int H, int P, int N, int G, int Q, int T_, int64_t ldw,
-                   int nbc, int PB, int RS) {
+                   int* __restrict__ flag, int64_t L, int H, int P, int N, int G, int Q, int T_,
+                   int64_t ldw, int nbc, int PB, int RS) {
   typedef typename FragOf<T>::type frag_t;
   typedef Slot<T, NK, KH> S;
   constexpr int V = Vec16<T>::n;
   constexpr int NSLOT = S::NSLOT;
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int arrived[NSLOT], released[NSLOT];
+  static_assert(2 * NSLOT * sizeof(int) <= kOutStaticLds, "static LDS bound");
   const OutLayout lay = out_layout<T, NK, KH>(Q);
   float* Gs = reinterpret_cast<float*>(smem + lay.g_off);
   float* ds = reinterpret_cast<float*>(smem + lay.d_off);
@@ -385,6 +422,10 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform (SGPR)
   const int lr = lane % 16, lg = lane / 16;
+  if (tid < NSLOT) {
+    arrived[tid] = 0;
+    released[tid] = 0;
+  }
   const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
   const T* xc = x + ((int64_t)b * L + t0) * xstride + (int64_t)h0 * P;
   const T* Bc = Bm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N;
@@ -474,6 +515,7 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
             hstage + g * 1024);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (npairs > 0) bump_count(&arrived[0], lane);   // this wave's share of pair 0 landed
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       if (tid + u * kOutThreads < KH * Q) {
@@ -500,6 +542,8 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
           hf[hh][pt][ks] = (ks * 32 + lg * 8 < N)
                                ? load_frag(hc_src(hh) + hcl.offset(0, pt, ks, lane))
                                : zero_frag<T>();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (npairs > 0) bump_count(&arrived[0], lane);   // this wave's share of pair 0 landed
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       if (tid + u * kOutThreads < KH * Q) {
@@ -551,20 +595,28 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
   const int q0 = nown >= 1 ? w.q[0] : -1;
   const int q1 = nown >= 2 ? w.q[IB - 1] : -1;
 
-  // pair jp was issued NSLOT-1 pairs ago: wait until at most the loads of the
-  // pairs after it (min(NSLOT-2, npairs-1-jp) of them) are outstanding.  Vector
-  // memory operations retire in issue order, so this covers pair jp; global
-  // stores issued since only make the wait stricter.  Then refill the slot
-  // freed by pair jp-1.
+  // Token pair jp: refill the slot pair jp-1 used (once every wave released
+  // it) with pair jp+NSLOT-1; wait for this wave's own loads of pair jp+1
+  // (vector memory operations retire in issue order, and global stores issued
+  // since only make the wait stricter) and announce them one pair early, so
+  // that a wave reaching pair jp+1 never waits for another wave to reach it;
+  // then wait for every wave's share of pair jp.  release_pair(jp) follows
+  // the wave's last read of the pair.  A wave can so run one pair ahead of
+  // the slowest one.
   auto sync_pair = [&](int jp) {
-    const int ahead = min(NSLOT - 2, npairs - 1 - jp);
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::LPG));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LPG));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
     const int nxt = jp + NSLOT - 1;
-    if (nxt < npairs) issue(nxt);
+    if (nxt < npairs) {
+      if (jp >= 1)
+        wait_count(&released[(jp - 1) % NSLOT], kOutWaves * ((jp - 1) / NSLOT + 1), flag, lane);
+      issue(nxt);
+    }
+    if (jp + 1 < npairs) {
+      wait_groups<S::LPG>(min(NSLOT - 2, npairs - 2 - jp));
+      bump_count(&arrived[(jp + 1) % NSLOT], lane);
+    }
+    wait_count(&arrived[jp % NSLOT], kOutWaves * (jp / NSLOT + 1), flag, lane);
   };
+  auto release_pair = [&](int jp) { bump_count(&released[jp % NSLOT], lane); };
   // a finished block: lane holds row i = 16 ib + lr and the 4 consecutive p
   // columns 16 pt + 4 lg .. +3 of every tile, stored straight from registers
   const bool vec4 = (P % 4) == 0;
@@ -600,10 +652,12 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
         sync_pair(jp);
         pair_step<T, NK, IB, KH, IB, false>(w, ring + (jp % NSLOT) * S::BYTES, jp, Gs, ds, es, Q,
                                             dh, lane);
+        release_pair(jp);
       }
       sync_pair(jp);
       pair_step<T, NK, IB, KH, IB, true>(w, ring + (jp % NSLOT) * S::BYTES, jp, Gs, ds, es, Q, dh,
                                          lane);
+      release_pair(jp);
       store_block(IB - 1);
       ++jp;
     }
@@ -613,21 +667,26 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
       sync_pair(jp);
       pair_step<T, NK, IB, KH, 1, false>(w, ring + (jp % NSLOT) * S::BYTES, jp, Gs, ds, es, Q, dh,
                                          lane);
+      release_pair(jp);
     }
     sync_pair(jp);
     pair_step<T, NK, IB, KH, 1, true>(w, ring + (jp % NSLOT) * S::BYTES, jp, Gs, ds, es, Q, dh,
                                       lane);
+    release_pair(jp);
     store_block(0);
     ++jp;
   }
-  for (; jp < npairs; ++jp) sync_pair(jp);
+  for (; jp < npairs; ++jp) {
+    sync_pair(jp);
+    release_pair(jp);
+  }
   // every load into LDS was waited for inside the loop (the last pair with
   // vmcnt(0)); only global stores may still be in flight here
 }
 
 template <typename T, int NK, int IB, int KH>
 static hipError_t launch_out(const void* x, const void* Bm, const void* Cm, const float* Gw,
-                             const float* dtw, const void* Hc, const float* Dv, void* y,
+                             const float* dtw, const void* Hc, const float* Dv, void* y, int* flag,
                              int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                              int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
   const OutLayout lay = out_layout<T, NK, KH>(Q);
@@ -639,13 +698,14 @@ static hipError_t launch_out(const void* x, const void* Bm, const void* Cm, cons
   static bool attr_set = false;   // per instantiation
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024 - kOutStaticLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(kOutThreads), lay.bytes, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm), static_cast<const T*>(Cm),
-                     Gw, dtw, static_cast<const T*>(Hc), Dv, static_cast<T*>(y), L, (int)H, (int)P,
+                     Gw, dtw, static_cast<const T*>(Hc), Dv, static_cast<T*>(y), flag, L, (int)H, (int)P,
                      (int)N, (int)G, Q, (int)T_, ldw, (int)nbc, PB, RS);
   return hipGetLastError();
 }
@@ -663,9 +723,9 @@ static int kh_class(int io_bf16, int64_t H, int64_t G, int64_t N) {
 template <typename T, int IB, int KH>
 static hipError_t launch_out_nk(int NK, const void* x, const void* Bm, const void* Cm,
                                 const float* Gw, const float* dtw, const void* Hc, const float* Dv,
-                                void* y, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                                void* y, int* flag, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                                 int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
-#define SSD_OUT_ARGS x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream
+#define SSD_OUT_ARGS x, Bm, Cm, Gw, dtw, Hc, Dv, y, flag, batch, L, H, P, N, G, Q, T_, ldw, stream
   switch (NK) {
     case 1: return launch_out<T, 1, IB, KH>(SSD_OUT_ARGS);
     case 2: return launch_out<T, 2, IB, KH>(SSD_OUT_ARGS);
@@ -677,10 +737,10 @@ static hipError_t launch_out_nk(int NK, const void* x, const void* Bm, const voi
 
 template <typename T>
 static hipError_t launch_out_t(const void* x, const void* Bm, const void* Cm, const float* Gw,
-                               const float* dtw, const void* Hc, const float* Dv, void* y,
+                               const float* dtw, const void* Hc, const float* Dv, void* y, int* flag,
                                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                                int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
-#define SSD_OUT_ARGS nk_class(N), x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream
+#define SSD_OUT_ARGS nk_class(N), x, Bm, Cm, Gw, dtw, Hc, Dv, y, flag, batch, L, H, P, N, G, Q, T_, ldw, stream
   const bool two = kh_class(sizeof(T) == 2, H, G, N) == 2;
   if (Q >= 128) return two ? launch_out_nk<T, 2, 2>(SSD_OUT_ARGS) : launch_out_nk<T, 2, 1>(SSD_OUT_ARGS);
   return two ? launch_out_nk<T, 1, 2>(SSD_OUT_ARGS) : launch_out_nk<T, 1, 1>(SSD_OUT_ARGS);
@@ -701,17 +761,17 @@ static int smem_bytes_t(int Q, int NK, int KH) {
 
 int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int64_t H, int64_t G) {
   const int NK = nk_class(N), KH = kh_class(io_bf16, H, G, N);
-  return io_bf16 ? smem_bytes_t<bf16>(Q, NK, KH) : smem_bytes_t<float>(Q, NK, KH);
+  return kOutStaticLds + (io_bf16 ? smem_bytes_t<bf16>(Q, NK, KH) : smem_bytes_t<float>(Q, NK, KH));
 }
 
 hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
-                              void* y, void* /*sink*/, int64_t batch, int64_t L, int64_t H,
+                              void* y, void* sink, int64_t batch, int64_t L, int64_t H,
                               int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
                               hipStream_t stream) {
   if (io_bf16)
-    return launch_out_t<bf16>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
-  return launch_out_t<float>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, batch, L, H, P, N, G, Q, T_, ldw, stream);
+    return launch_out_t<bf16>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, static_cast<int*>(sink), batch, L, H, P, N, G, Q, T_, ldw, stream);
+  return launch_out_t<float>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, static_cast<int*>(sink), batch, L, H, P, N, G, Q, T_, ldw, stream);
 }
 
 }  // namespace ssd

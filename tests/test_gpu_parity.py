@@ -258,3 +258,26 @@ def test_errors_enqueue_nothing():
     ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(lib.SsdArgumentError):
         lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 64, workspace=ws)
+
+
+@pytest.mark.parametrize("kw", [dict(seqlen=300, nheads=3, dstate=64, chunk_size=64),
+                                dict(seqlen=2048, nheads=8, dstate=128, chunk_size=256),
+                                dict(seqlen=1000, nheads=4, dstate=128, chunk_size=128,
+                                     io_dtype="fp32")],
+                         ids=["L300_Q64", "L2048_Q256", "L1000_Q128_fp32"])
+def test_compute_out_wait_flag_clear(kw):
+    # compute_out's waves hand ring slots to each other through bounded waits;
+    # a wait that ran past its bound would set bit 0 of the first word of the
+    # workspace's last 4 KiB (scratch the call owns).  It must stay clear.
+    p = prob(**kw)
+    inp = ssd_synth.make_inputs(p, seed=11)
+    d = to_dev(inp)
+    pr = lib.make_problem(p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups,
+                          p.chunk_size, lib.SSD_BF16 if p.io_dtype == "bf16" else lib.SSD_F32)
+    ws = torch.zeros(lib.ssd_fwd_workspace_size(pr), dtype=torch.uint8, device="cuda")
+    y, fin = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], p.chunk_size,
+                         d["init_state"], workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[-4096:].to(torch.int32).sum()) == 0
+    y_ref, fin_ref, _ = oracle_fwd(inp)
+    assert_close(y, y_ref, p.io_dtype, "y")
