@@ -266,13 +266,15 @@ __device__ __forceinline__ typename FragOf<T>::type slot_x_frag(const unsigned c
   if constexpr (sizeof(T) == 2) {
     // transposing reads: lane r of each 16-lane group addresses the 4 elements
     // at [t0 + r/4][c0 + 4 (r%4)]; lane l then holds rows t0..t0+3 of column c0 + l.
+    // row ta + 16 has the same swizzle as row ta, 16 rows further on; the
+    // head's block sits a whole multiple of rows away, so one lane address
+    // serves all four reads of a column tile
     const int r = lane & 15;
     const int col = c0 + 4 * (r & 3);
-    const int ta = 4 * lg + (r >> 2), tb = 16 + 4 * lg + (r >> 2);
-    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4*)(slot + S::xoff(hh, ta, col)));
-    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4*)(slot + S::xoff(hh, tb, col)));
+    const int ta = 4 * lg + (r >> 2);
+    const unsigned char* pa = slot + S::xoff(0, ta, col) + hh * S::XCH * 16;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + 16 * S::XC * 16));
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   } else {
     const int c = c0 + (lane & 15);
@@ -312,8 +314,16 @@ __device__ __forceinline__ void pair_step(WaveRows<T, NK, IB, KH>& w, const unsi
   for (int s = 0; s < NS; ++s) { st[s][0] = floatx4{0.f, 0.f, 0.f, 0.f}; st[s][1] = st[s][0]; }
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) {
-    const frag_t b0 = slot_b_frag<T, NK, KH>(sl, lr, ks * 32 + lg * 8);
-    const frag_t b1 = slot_b_frag<T, NK, KH>(sl, 16 + lr, ks * 32 + lg * 8);
+    frag_t b0, b1;
+    if constexpr (sizeof(T) == 2) {
+      // row 16 + lr has the same swizzle as row lr, 16 rows further on
+      const unsigned char* bp = sl + Slot<T, NK, KH>::boff(lr, ks * 32 + lg * 8);
+      b0 = *reinterpret_cast<const bf16x8*>(bp);
+      b1 = *reinterpret_cast<const bf16x8*>(bp + 16 * Slot<T, NK, KH>::BC * 16);
+    } else {
+      b0 = slot_b_frag<T, NK, KH>(sl, lr, ks * 32 + lg * 8);
+      b1 = slot_b_frag<T, NK, KH>(sl, 16 + lr, ks * 32 + lg * 8);
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       st[s][0] = mma(st[s][0], b0, w.cf[s][ks]);
