@@ -178,7 +178,12 @@ ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* d
  *   x, B, C, D, y : as for ssd_fwd (D may be NULL).
  *   workspace     : at least ssd_fwd_workspace_size bytes; its running sums
  *                   and states are only read, its last 4 KiB are scratch
- *                   that the call may overwrite.
+ *                   that the call may overwrite.  The kernel's waves hand
+ *                   shared LDS buffers to each other through bounded waits;
+ *                   a wait past its bound (never expected: the hand-off
+ *                   cannot deadlock) sets bit 0 of the scratch's first
+ *                   32-bit word and leaves y undefined.  A caller that wants
+ *                   to check it clears that word before the call.
  * Errors as for ssd_fwd. */
 ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B, const void* C,
                            const float* D, void* y, const void* workspace,
