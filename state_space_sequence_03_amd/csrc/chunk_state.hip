@@ -66,19 +66,21 @@ struct CsCfg {
 
 // Fragment of a token-major slot tile: column c0 + lane%16, the 8 tokens
 // {4 lg .. 4 lg + 3, 16 + 4 lg .. 16 + 4 lg + 3} (lg = lane / 16).
+// `row16` is the byte distance of the same column 16 rows further on: both
+// tiles' swizzles repeat every 16 rows, so the second read reuses the first
+// read's lane address with a constant offset.
 template <typename T, typename Off>
 __device__ __forceinline__ typename FragOf<T>::type slot_tok_frag(const unsigned char* slot, Off off,
-                                                                  int c0, int lane) {
+                                                                  int row16, int c0, int lane) {
   const int lg = lane / 16;
   if constexpr (sizeof(T) == 2) {
     // transposing reads: lane r of each 16-lane group addresses the 4 elements
     // at [t0 + r/4][c0 + 4 (r%4)]; lane l then holds rows t0..t0+3 of column c0 + l.
     const int r = lane & 15;
     const int col = c0 + 4 * (r & 3);
-    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4*)(slot + off(4 * lg + (r >> 2), col)));
-    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4*)(slot + off(16 + 4 * lg + (r >> 2), col)));
+    const unsigned char* pa = slot + off(4 * lg + (r >> 2), col);
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + row16));
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   } else {
     const int c = c0 + (lane & 15);
@@ -92,13 +94,23 @@ __device__ __forceinline__ typename FragOf<T>::type slot_tok_frag(const unsigned
   }
 }
 
-// Multiply 16 bytes of io elements by w (fp32 arithmetic, one rounding).
+// Multiply 16 bytes of io elements by w (fp32 arithmetic, one rounding).  The
+// bf16 form works on an 8-vector so the results are packed two per convert.
 template <typename T>
-__device__ __forceinline__ vec16 scale16(vec16 v, float w) {
-  T* e = reinterpret_cast<T*>(&v);
+__device__ __forceinline__ vec16 scale16(vec16 v, float w);
+template <>
+__device__ __forceinline__ vec16 scale16<bf16>(vec16 v, float w) {
+  const bf16x8 in = __builtin_bit_cast(bf16x8, v);
+  bf16x8 out;
 #pragma unroll
-  for (int k = 0; k < Vec16<T>::n; ++k) e[k] = to_io<T>(to_f32(e[k]) * w);
-  return v;
+  for (int k = 0; k < 8; ++k) out[k] = static_cast<bf16>(static_cast<float>(in[k]) * w);
+  return __builtin_bit_cast(vec16, out);
+}
+template <>
+__device__ __forceinline__ vec16 scale16<float>(vec16 v, float w) {
+  floatx4 f = __builtin_bit_cast(floatx4, v);
+  f *= w;
+  return __builtin_bit_cast(vec16, f);
 }
 
 template <typename T, int KH, int NW>
@@ -143,8 +155,41 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
   // chunk's valid tokens and columns past N or P read clamped, valid
   // addresses: those rows get weight 0, those columns are outputs that are
   // never consumed.
+  // A slot whose 32 tokens all lie inside the sequence: the per-lane parts
+  // of the addresses do not depend on the slot, so they are byte offsets
+  // computed once and each slot only moves the wave-uniform row base.
+  uint32_t ob[C::BINST], ox[C::XINST];
+#pragma unroll
+  for (int i = 0; i < C::BINST; ++i) {
+    const int q = ((i * C::NWV + wave) % C::NBB) * 64 + lane;
+    const int r = q / C::BC, pc = q % C::BC;
+    int col = n0 + (pc ^ C::bsw(r)) * V;
+    col = col < N ? col : 0;
+    ob[i] = (uint32_t)(((int64_t)r * bstride + col) * (int64_t)sizeof(T));
+  }
+#pragma unroll
+  for (int i = 0; i < C::XINST; ++i) {
+    const int q = (i * C::NWV + wave) * 64 + lane;
+    const int hh = q / C::XCH, rq = q % C::XCH;
+    const int r = rq / C::XC, pc = rq % C::XC;
+    int p = p0 + (pc ^ C::xsw(r)) * V;
+    p = p < P ? p : p0;
+    ox[i] = (uint32_t)(((int64_t)hh * P + (int64_t)r * xstride + p) * (int64_t)sizeof(T));
+  }
+  const bool off32 = (int64_t)kCsTok * (xstride + bstride) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
   auto issue = [&](int k) {
     unsigned char* sl = ring + (k % C::NSLOT) * C::BYTES;
+    if (off32 && (k + 1) * kCsTok <= qv) {
+      const T* bb = Bc + (int64_t)k * kCsTok * bstride;
+      const T* xb = xc + (int64_t)k * kCsTok * xstride;
+#pragma unroll
+      for (int i = 0; i < C::BINST; ++i)
+        dma16_so(bb, ob[i], sl + ((i * C::NWV + wave) % C::NBB) * 1024);
+#pragma unroll
+      for (int i = 0; i < C::XINST; ++i)
+        dma16_so(xb, ox[i], sl + C::BCH * 16 + (i * C::NWV + wave) * 1024);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::BINST; ++i) {
       const int blk = (i * C::NWV + wave) % C::NBB;
@@ -221,11 +266,12 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
     frag_t fb[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
-      fb[pt] = slot_tok_frag<T>(sl, [&](int r, int col) { return C::xoff(hh, r, col); }, pt * 16, lane);
+      fb[pt] = slot_tok_frag<T>(sl, [&](int r, int col) { return C::xoff(hh, r, col); },
+                                16 * C::XC * 16, pt * 16, lane);
 #pragma unroll
     for (int nt = 0; nt < C::WNT; ++nt) {
       const frag_t fa = slot_tok_frag<T>(sl, [&](int r, int col) { return C::boff(r, col); },
-                                         nw0 + nt * 16, lane);
+                                         16 * C::BC * 16, nw0 + nt * 16, lane);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[nt][pt] = mma(acc[nt][pt], fa, fb[pt]);
     }
