@@ -23,7 +23,8 @@
 // workgroup streams the chunk's tokens in pairs of 16-token blocks through a
 // ring of LDS slots filled by asynchronous direct global->LDS loads issued
 // several pairs ahead (global memory latency under load is far longer than
-// one pair's compute), one barrier per pair.
+// one pair's compute); the waves hand slots to each other through LDS
+// counters rather than a barrier per pair (see wait_count below).
 //
 // Decay factorisation.  For a row block starting at i0, let jl = 32*floor(i0/32)
 // and r = jl - 1 (G_{-1} = 0).  Decays are negative, so G is non-increasing and
@@ -46,7 +47,10 @@
 // the pair's tokens are taken in that order.  The matching x operand (8 tokens
 // of one p column per lane) comes from the natural-layout x tile through two
 // transposing LDS reads.  The tile never leaves registers between the two
-// products.
+// products.  The output product takes the x fragment as its first operand
+// (y^T = x^T S^T), so each lane's accumulator holds 4 consecutive p of its
+// row i, the band's row rescale is one scalar per lane, and finished rows are
+// stored straight from the accumulators.
 #include "ssd_device.hpp"
 
 namespace ssd {
