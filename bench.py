@@ -34,7 +34,8 @@ METRIC = "SSD fwd tokens/sec (batch·seqlen) at 1 MI355X; % of bf16 MFMA rooflin
 COPY_PROBE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compute_out_{workload}_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "state_space_sequence_03_amd", "csrc", f)
-                  for f in ("compute_out.hip", "ssd_device.hpp")]
+                  for f in ("compute_out.hip", "ssd_device.hpp")] + \
+                 [os.path.join(ROOT, "state_space_sequence_03_amd", "build.py")]   # compile flags
 
 
 def counts(p):
