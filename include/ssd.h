@@ -51,7 +51,8 @@
  * returns the first failing check in this order: SSD_ERR_NULL_POINTER (a
  * required pointer is NULL), SSD_ERR_BAD_SHAPE (a size <= 0, nheads not a
  * multiple of ngroups, or a size product overflowing int64), SSD_ERR_BAD_CHUNK
- * (chunk_size not one of 32, 64, 128, 256), SSD_ERR_BAD_DTYPE,
+ * (chunk_size not one of 32, 64, 128, 256; ssd_step does not use it),
+ * SSD_ERR_BAD_DTYPE, SSD_ERR_BAD_VALUE (an invalid ssd_dt_transform),
  * SSD_ERR_MISALIGNED (a tensor pointer not 16-byte aligned),
  * SSD_ERR_UNSUPPORTED (headdim or dstate not a multiple of 16, or dstate >
  * 256), SSD_ERR_WORKSPACE (workspace too small).  SSD_ERR_HIP reports a failed
@@ -69,7 +70,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
@@ -83,7 +84,8 @@ typedef enum {
   SSD_ERR_WORKSPACE = 6,
   SSD_ERR_UNSUPPORTED = 7,
   SSD_ERR_HIP = 8,
-  SSD_ERR_INTERNAL = 9
+  SSD_ERR_INTERNAL = 9,
+  SSD_ERR_BAD_VALUE = 10
 } ssd_status;
 
 /* Problem description.  chunk_size Q splits the sequence into
@@ -99,6 +101,29 @@ typedef struct {
   int32_t io_dtype;   /* ssd_dtype: dtype of x, B, C, y and of the chunk states */
   int32_t reserved;   /* must be 0 */
 } ssd_problem;
+
+/* Optional preparation of a raw step size, for the entry points that take
+ * one (NULL there = dt is used as given).  A Mamba-2 layer produces its step
+ * size from a projection as softplus(dt_raw + dt_bias), optionally clamped;
+ * the pages leave this preparation out, and the library applies it where dt is
+ * first read (stage 1, or the decode step), so no prepared copy of dt is ever
+ * written or read back:
+ *     v  = dt[b, t, h] + (dt_bias ? dt_bias[h] : 0)
+ *     v  = softplus ? log(1 + exp(v)) : v
+ *     dt' = min(max(v, dt_min), dt_max)
+ * Every later use of dt (decays, input weights) uses dt'.  dt' must satisfy
+ * the positivity precondition; dt_min = 0 and dt_max = INFINITY leave a
+ * positive value unclamped.
+ * Errors (SSD_ERR_BAD_VALUE): softplus not 0 or 1, reserved not 0, dt_min or
+ * dt_max NaN, dt_min > dt_max.  dt_bias, when given, is [nheads] fp32 device
+ * memory, 16-byte aligned (else SSD_ERR_MISALIGNED). */
+typedef struct {
+  const float* dt_bias; /* [nheads] fp32 device, or NULL */
+  int32_t softplus;     /* 1: apply softplus after the bias; 0: do not */
+  int32_t reserved;     /* must be 0 */
+  float dt_min;         /* lower clamp */
+  float dt_max;         /* upper clamp */
+} ssd_dt_transform;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION at build time). */
 int ssd_abi_version(void);
@@ -135,6 +160,14 @@ ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, cons
                    void* y, float* final_state, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* ssd_fwd with the raw step size prepared inside stage 1 (see
+ * ssd_dt_transform; dtx = NULL makes this exactly ssd_fwd).  Same workspace,
+ * arguments, outputs and errors as ssd_fwd. */
+ssd_status ssd_fwd_ex(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                      const float* dt, const float* A, const void* B, const void* C,
+                      const float* D, const float* init_state, void* y, float* final_state,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Stage 1 alone (the chunk_cumsum step): for every (b, h) and token t in chunk
  * c = t / Q,
  *     G_out[b, h, t]  = log2(e) * sum_{k = cQ .. t} dt[b, k, h] * A[h]
@@ -147,6 +180,13 @@ ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, cons
  * fp32 device buffers.  Errors as for ssd_fwd (no workspace). */
 ssd_status ssd_chunk_cumsum(const ssd_problem* prob, const float* dt, const float* A,
                             float* G_out, float* dt_out, void* stream);
+
+/* ssd_chunk_cumsum with the step size prepared first (ssd_dt_transform;
+ * NULL = ssd_chunk_cumsum): G_out and dt_out are built from dt', and dt_out
+ * holds dt' itself. */
+ssd_status ssd_chunk_cumsum_ex(const ssd_problem* prob, const ssd_dt_transform* dtx,
+                               const float* dt, const float* A, float* G_out, float* dt_out,
+                               void* stream);
 
 /* Stages 1 and 2 (chunk_cumsum, chunk_state, state_pass): the state at the start of
  * every chunk and the state after the last token, without computing y
@@ -188,6 +228,31 @@ ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* d
 ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B, const void* C,
                            const float* D, void* y, const void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* Token-sequential mode (decode): advance a resident state through
+ * prob->seqlen tokens one at a time, without chunking.  For every (b, h):
+ *     s = exp(dt_t A_h) s + dt_t x_t (outer) B_t,   y_t = s C_t + D_h x_t
+ * for t = 0 .. seqlen-1, starting from `state` and leaving the state after
+ * the last token in `state`.  This is the per-token recurrence that the
+ * chunked pass evaluates in bulk (devin.kr "NVIDIA CUDA Tile로 Mamba-2 순방향
+ * 전달 커널 가속화", section "Mamba-2 아키텍처의 핵심 연산": the output line
+ * y_t = c_t^T h_t + D x_t, run sequentially at inference); seqlen = 1 is one
+ * decode step.  Results equal ssd_fwd over the same tokens with init_state =
+ * state, up to rounding.
+ *   state   : [batch, nheads, headdim, dstate] fp32 device, read and updated
+ *             in place (required).
+ *   x, y    : [batch, seqlen, nheads, headdim] io dtype; y must not overlap
+ *             any input or the state.
+ *   dt      : [batch, seqlen, nheads] fp32 (raw when dtx is given).
+ *   A, D    : [nheads] fp32 (D may be NULL: no skip term).
+ *   B, C    : [batch, seqlen, ngroups, dstate] io dtype.
+ *   dtx     : optional step-size preparation (NULL = dt used as given).
+ * prob->chunk_size is not used.  No workspace.  Errors as for ssd_fwd, with
+ * the same limits on headdim and dstate; the state must not be read or
+ * written by other work until the call has completed on `stream`. */
+ssd_status ssd_step(const ssd_problem* prob, const ssd_dt_transform* dtx, float* state,
+                    const void* x, const float* dt, const float* A, const void* B, const void* C,
+                    const float* D, void* y, void* stream);
 
 #ifdef __cplusplus
 }

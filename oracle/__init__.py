@@ -9,6 +9,12 @@ Contents
   chunk_cumsum(...)   fp64 within-chunk running sum of a_t = dt_t A, base-2 log.
   dense_matrix(...)   fp64 materialised SSD matrix form (numpy, tiny inputs).
   chunked(...)        fp64 chunked log-space form (numpy, small inputs).
+  dt_transform(...)   fp64 step-size preparation (bias, softplus, clamp) of a
+                      Mamba-2 layer, for the raw-dt entry points.
+
+The token-sequential (decode) mode needs no function of its own: it is the
+recurrence itself, started from a given state (``recurrence`` with
+``init_state``).
 
 All functions take CPU tensors or numpy arrays in the layouts documented in
 ``ssd_synth`` and return numpy float64 arrays.
@@ -24,6 +30,7 @@ import numpy as np
 
 from .dense import dense_matrix, linear_attention
 from .chunked import chunked
+from .dt import dt_transform, softplus
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
@@ -32,7 +39,7 @@ _lock = threading.Lock()
 _lib = None
 
 __all__ = ["build", "load_library", "recurrence", "recurrence_heads", "chunk_cumsum", "dense_matrix",
-           "linear_attention", "chunked", "as_f32"]
+           "linear_attention", "chunked", "as_f32", "dt_transform", "softplus"]
 
 
 def build(force: bool = True) -> str:

@@ -14,6 +14,10 @@ Shapes and layouts (all contiguous, row-major):
     C   [batch, seqlen, ngroups, dstate]   io dtype
     D   [nheads]                           fp32
     init_state [batch, nheads, headdim, dstate] fp32 or None
+    dt_raw  [batch, seqlen, nheads]        fp32, the pre-activation 0.5 * N(0, 1)
+    dt_bias [nheads]                       fp32
+(dt is softplus(dt_raw + dt_bias); dt_raw and dt_bias are returned as well, for
+the entry points that prepare a raw step size themselves.)
 
 Draw order for one problem (CPU ``torch.Generator`` seeded once):
     1. dt_bias[H] = inv_softplus(exp(U(log 1e-3, log 1e-1)))
@@ -106,8 +110,8 @@ def make_inputs(prob: Problem, seed: int) -> Dict[str, Optional[torch.Tensor]]:
     # 4. x ~ N(0, 1)
     x = torch.randn((Bsz, L, H, P), generator=g, dtype=torch.float32)
     # 5. dt = softplus(0.5 * N(0,1) + dt_bias)
-    dt = torch.nn.functional.softplus(
-        0.5 * torch.randn((Bsz, L, H), generator=g, dtype=torch.float32) + dt_bias)
+    dt_raw = 0.5 * torch.randn((Bsz, L, H), generator=g, dtype=torch.float32)
+    dt = torch.nn.functional.softplus(dt_raw + dt_bias)
     # 6, 7. B, C ~ N(0, 1) / sqrt(N)
     scale = 1.0 / math.sqrt(N)
     Bm = torch.randn((Bsz, L, G, N), generator=g, dtype=torch.float32) * scale
@@ -125,6 +129,8 @@ def make_inputs(prob: Problem, seed: int) -> Dict[str, Optional[torch.Tensor]]:
         "C": Cm.to(io).contiguous(),
         "D": D.contiguous(),
         "init_state": init,
+        "dt_raw": dt_raw.contiguous(),
+        "dt_bias": dt_bias.contiguous(),
     }
 
 

@@ -7,8 +7,9 @@ PyTorch fallback: importing works without the library, but every call raises
 if ``libssd.so`` is missing or the tensors are not on a GPU.
 
 Names match the C ABI in include/ssd.h:
-    ssd_fwd, ssd_fwd_states, ssd_compute_out, ssd_chunk_cumsum, ssd_fwd_workspace_size,
-    ssd_status_string, ssd_last_error_message, ssd_abi_version
+    ssd_fwd, ssd_fwd_ex, ssd_fwd_states, ssd_compute_out, ssd_chunk_cumsum,
+    ssd_chunk_cumsum_ex, ssd_step, ssd_fwd_workspace_size, ssd_status_string,
+    ssd_last_error_message, ssd_abi_version
 """
 from __future__ import annotations
 
@@ -22,15 +23,15 @@ import torch
 __all__ = ["SsdError", "SsdArgumentError", "lib_path", "load_library", "make_problem",
            "ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
            "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_states", "ssd_compute_out",
-           "ssd_chunk_cumsum",
+           "ssd_chunk_cumsum", "ssd_fwd_ex", "ssd_chunk_cumsum_ex", "ssd_step",
            "SSD_F32", "SSD_BF16"]
 
 SSD_F32, SSD_BF16 = 0, 1
 _STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_BAD_SHAPE",
                  3: "SSD_ERR_BAD_CHUNK", 4: "SSD_ERR_BAD_DTYPE", 5: "SSD_ERR_MISALIGNED",
                  6: "SSD_ERR_WORKSPACE", 7: "SSD_ERR_UNSUPPORTED", 8: "SSD_ERR_HIP",
-                 9: "SSD_ERR_INTERNAL"}
-_ARG_ERRORS = {1, 2, 3, 4, 5, 6, 7}
+                 9: "SSD_ERR_INTERNAL", 10: "SSD_ERR_BAD_VALUE"}
+_ARG_ERRORS = {1, 2, 3, 4, 5, 6, 7, 10}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssd.so")
@@ -56,6 +57,12 @@ class ssd_problem(ctypes.Structure):
                 ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk_size", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class ssd_dt_transform(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("softplus", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("dt_min", ctypes.c_float),
+                ("dt_max", ctypes.c_float)]
 
 
 def lib_path() -> str:
@@ -88,6 +95,13 @@ def load_library():
         lib.ssd_fwd_states.argtypes = [P] + [vp] * 8 + [sz, vp]
         lib.ssd_compute_out.restype = ctypes.c_int
         lib.ssd_compute_out.argtypes = [P] + [vp] * 6 + [sz, vp]
+        X = ctypes.POINTER(ssd_dt_transform)
+        lib.ssd_fwd_ex.restype = ctypes.c_int
+        lib.ssd_fwd_ex.argtypes = [P, X] + [vp] * 10 + [sz, vp]
+        lib.ssd_chunk_cumsum_ex.restype = ctypes.c_int
+        lib.ssd_chunk_cumsum_ex.argtypes = [P, X] + [vp] * 5
+        lib.ssd_step.restype = ctypes.c_int
+        lib.ssd_step.argtypes = [P, X] + [vp] * 9
         _lib = lib
         return lib
 
@@ -164,12 +178,30 @@ def _workspace(prob, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+def _dt_transform(x_like, H, dt_bias, dt_softplus, dt_limit):
+    """ssd_dt_transform for the given options (None when none is asked for)."""
+    if dt_bias is None and not dt_softplus and dt_limit is None:
+        return None, None
+    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
+        raise SsdArgumentError(2, "dt_bias must be [nheads]")
+    lo, hi = dt_limit if dt_limit is not None else (0.0, float("inf"))
+    xf = ssd_dt_transform(_dev(dt_bias, "dt_bias", torch.float32), 1 if dt_softplus else 0, 0,
+                          float(lo), float(hi))
+    return xf, ctypes.byref(xf)
+
+
 def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
             C: torch.Tensor, D: Optional[torch.Tensor] = None, chunk_size: int = 256,
             init_state: Optional[torch.Tensor] = None, *, want_final_state: bool = True,
             out: Optional[torch.Tensor] = None, final_out: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Full forward pass on the current stream.  Returns (y, final_state)."""
+            workspace: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
+            dt_softplus: bool = False,
+            dt_limit: Optional[Tuple[float, float]] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Full forward pass on the current stream.  Returns (y, final_state).
+
+    With dt_bias, dt_softplus or dt_limit given, ``dt`` is the raw step size and
+    is prepared inside the first stage as clamp(softplus(dt + dt_bias)) (the C
+    entry point ssd_fwd_ex); otherwise ``dt`` is used as given (ssd_fwd)."""
     lib = load_library()
     prob = _problem_of(x, B, chunk_size)
     if x.dtype != B.dtype or x.dtype != C.dtype:
@@ -191,13 +223,25 @@ def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
         fin = final_out if final_out is not None else torch.empty(
             state_shape, dtype=torch.float32, device=x.device)
     ws, ws_bytes = _workspace(prob, x.device, workspace)
-    st = lib.ssd_fwd(ctypes.byref(prob), _dev(x, "x"), _dev(dt, "dt", torch.float32),
-                     _dev(A, "A", torch.float32), _dev(B, "B"), _dev(C, "C"),
-                     _dev(D, "D", torch.float32), _dev(init_state, "init_state", torch.float32),
-                     _dev(y, "y"), _dev(fin, "final_state", torch.float32), _dev(ws, "workspace"),
-                     ws_bytes, _stream(x.device))
+    args = (_dev(x, "x"), _dev(dt, "dt", torch.float32),
+            _dev(A, "A", torch.float32), _dev(B, "B"), _dev(C, "C"),
+            _dev(D, "D", torch.float32), _dev(init_state, "init_state", torch.float32),
+            _dev(y, "y"), _dev(fin, "final_state", torch.float32), _dev(ws, "workspace"),
+            ws_bytes, _stream(x.device))
+    xf, xfp = _dt_transform(x, x.shape[2], dt_bias, dt_softplus, dt_limit)
+    if xf is None:
+        st = lib.ssd_fwd(ctypes.byref(prob), *args)
+    else:
+        st = lib.ssd_fwd_ex(ctypes.byref(prob), xfp, *args)
     _check(st)
     return y, fin
+
+
+def ssd_fwd_ex(x, dt, A, B, C, D=None, chunk_size=256, init_state=None, *, dt_bias=None,
+               dt_softplus=True, dt_limit=(0.0, float("inf")), **kw):
+    """ssd_fwd from a raw step size: dt' = clamp(softplus(dt + dt_bias), *dt_limit)."""
+    return ssd_fwd(x, dt, A, B, C, D, chunk_size, init_state, dt_bias=dt_bias,
+                   dt_softplus=dt_softplus, dt_limit=dt_limit, **kw)
 
 
 def ssd_fwd_states(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
@@ -243,8 +287,12 @@ def ssd_compute_out(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
     return y
 
 
-def ssd_chunk_cumsum(dt: torch.Tensor, A: torch.Tensor, chunk_size: int = 256):
-    """Stage 1 only.  Returns (G, dt_t), both [batch, nheads, seqlen] fp32."""
+def ssd_chunk_cumsum(dt: torch.Tensor, A: torch.Tensor, chunk_size: int = 256, *,
+                     dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False,
+                     dt_limit: Optional[Tuple[float, float]] = None):
+    """Stage 1 only.  Returns (G, dt_t), both [batch, nheads, seqlen] fp32.
+    With dt_bias, dt_softplus or dt_limit, dt is prepared first (ssd_chunk_cumsum_ex)
+    and dt_t holds the prepared values."""
     lib = load_library()
     if dt.dim() != 3:
         raise SsdArgumentError(2, "dt must be [batch, seqlen, nheads]")
@@ -252,8 +300,51 @@ def ssd_chunk_cumsum(dt: torch.Tensor, A: torch.Tensor, chunk_size: int = 256):
     prob = make_problem(bsz, L, H, 16, 16, 1, chunk_size, SSD_F32)
     G = torch.empty((bsz, H, L), dtype=torch.float32, device=dt.device)
     dtt = torch.empty_like(G)
-    st = lib.ssd_chunk_cumsum(ctypes.byref(prob), _dev(dt, "dt", torch.float32),
-                              _dev(A, "A", torch.float32), _dev(G, "G_out"), _dev(dtt, "dt_out"),
-                              _stream(dt.device))
+    args = (_dev(dt, "dt", torch.float32), _dev(A, "A", torch.float32), _dev(G, "G_out"),
+            _dev(dtt, "dt_out"), _stream(dt.device))
+    xf, xfp = _dt_transform(dt, H, dt_bias, dt_softplus, dt_limit)
+    if xf is None:
+        st = lib.ssd_chunk_cumsum(ctypes.byref(prob), *args)
+    else:
+        st = lib.ssd_chunk_cumsum_ex(ctypes.byref(prob), xfp, *args)
     _check(st)
     return G, dtt
+
+
+def ssd_chunk_cumsum_ex(dt, A, chunk_size=256, *, dt_bias=None, dt_softplus=True,
+                        dt_limit=(0.0, float("inf"))):
+    """ssd_chunk_cumsum from a raw step size (prepared as in ssd_fwd_ex)."""
+    return ssd_chunk_cumsum(dt, A, chunk_size, dt_bias=dt_bias, dt_softplus=dt_softplus,
+                            dt_limit=dt_limit)
+
+
+def ssd_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+             B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None, *,
+             dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False,
+             dt_limit: Optional[Tuple[float, float]] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Token-sequential mode: advance ``state`` [batch, nheads, headdim, dstate]
+    (fp32, updated in place) through the seqlen tokens of x [batch, seqlen,
+    nheads, headdim] one at a time.  Returns y (shape and dtype of x)."""
+    lib = load_library()
+    prob = _problem_of(x, B, 256)
+    if x.dtype != B.dtype or x.dtype != C.dtype:
+        raise SsdArgumentError(4, "x, B and C must share one dtype")
+    if tuple(dt.shape) != tuple(x.shape[:3]) or A.shape != (x.shape[2],):
+        raise SsdArgumentError(2, "dt must be [batch, seqlen, nheads] and A [nheads]")
+    if tuple(C.shape) != tuple(B.shape):
+        raise SsdArgumentError(2, "C must have the shape of B")
+    if D is not None and D.shape != (x.shape[2],):
+        raise SsdArgumentError(2, "D must be [nheads]")
+    if tuple(state.shape) != (x.shape[0], x.shape[2], x.shape[3], B.shape[3]):
+        raise SsdArgumentError(2, "state must be [batch, nheads, headdim, dstate]")
+    y = out if out is not None else torch.empty_like(x)
+    if tuple(y.shape) != tuple(x.shape) or y.dtype != x.dtype:
+        raise SsdArgumentError(2, "out must match x")
+    xf, xfp = _dt_transform(x, x.shape[2], dt_bias, dt_softplus, dt_limit)
+    st = lib.ssd_step(ctypes.byref(prob), xfp, _dev(state, "state", torch.float32), _dev(x, "x"),
+                      _dev(dt, "dt", torch.float32), _dev(A, "A", torch.float32), _dev(B, "B"),
+                      _dev(C, "C"), _dev(D, "D", torch.float32), _dev(y, "y"),
+                      _stream(x.device))
+    _check(st)
+    return y

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libssd.so")
 
-SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "state_pass.hip", "compute_out.hip", "ssd_api.cpp"]
+SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "state_pass.hip", "compute_out.hip", "step.hip",
+           "ssd_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

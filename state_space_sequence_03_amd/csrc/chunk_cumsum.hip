@@ -22,6 +22,11 @@
 // Rows are `ld` floats apart in the outputs; tokens in [L, Lw) are padding
 // (dt = 0, so G holds the chunk's last running sum), which lets the later
 // stages read whole chunks without bounds checks.
+//
+// With XF set, every real token's dt first goes through the optional step-size
+// preparation (bias, softplus, clamp; ssd_device.hpp), and both outputs are
+// built from the prepared value: the later stages read dt only from dtT.
+// Padding tokens are not prepared and stay 0.
 #include "ssd_device.hpp"
 
 namespace ssd {
@@ -35,11 +40,11 @@ template <> struct FloatVec<1> { typedef float type; };
 template <> struct FloatVec<2> { typedef float type __attribute__((ext_vector_type(2))); };
 template <> struct FloatVec<4> { typedef float type __attribute__((ext_vector_type(4))); };
 
-template <int Q>
+template <int Q, bool XF>
 __global__ void __launch_bounds__(kCumsumThreads)
 chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
                     float* __restrict__ G, float* __restrict__ dtT,
-                    int64_t L, int H, int64_t ld, int64_t Lw) {
+                    int64_t L, int H, int64_t ld, int64_t Lw, DtXform xf) {
   constexpr int TPL = Q >= kWave ? Q / kWave : 1;       // tokens per lane
   constexpr int LANES = Q / TPL;                         // lanes holding tokens
   typedef typename FloatVec<TPL>::type vec_t;
@@ -64,6 +69,11 @@ chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = h0 + h4 + e < H ? src[e] : 0.0f;
+      }
+      if constexpr (XF) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (h0 + h4 + e < H) v[e] = dt_prepare(xf, v[e], h0 + h4 + e);
       }
     }
 #pragma unroll
@@ -123,30 +133,29 @@ chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
   }
 }
 
+template <int Q>
+static void launch_q(dim3 grid, const float* dt, const float* A, float* G, float* dtT, int64_t L,
+                     int H, int64_t ld, int64_t Lw, const DtXform* xf, hipStream_t stream) {
+  if (xf)
+    hipLaunchKernelGGL((chunk_cumsum_kernel<Q, true>), grid, dim3(kCumsumThreads), 0, stream, dt,
+                       A, G, dtT, L, H, ld, Lw, *xf);
+  else
+    hipLaunchKernelGGL((chunk_cumsum_kernel<Q, false>), grid, dim3(kCumsumThreads), 0, stream, dt,
+                       A, G, dtT, L, H, ld, Lw, DtXform{nullptr, 0, 0.0f, 0.0f});
+}
+
 // Host launcher.  Q in {32, 64, 128, 256}; grid covers ceil(Lw / Q) chunks;
-// rows of G and dtT are `ld` floats apart.
+// rows of G and dtT are `ld` floats apart; xf = nullptr: dt used as given.
 hipError_t launch_chunk_cumsum(const float* dt, const float* A, float* G, float* dtT,
                                int64_t batch, int64_t L, int64_t H, int Q, int64_t ld,
-                               int64_t Lw, hipStream_t stream) {
+                               int64_t Lw, const DtXform* xf, hipStream_t stream) {
   const int64_t T = (Lw + Q - 1) / Q;
   dim3 grid((unsigned)T, (unsigned)((H + kCumsumHeads - 1) / kCumsumHeads), (unsigned)batch);
   switch (Q) {
-    case 32:
-      hipLaunchKernelGGL(chunk_cumsum_kernel<32>, grid, dim3(kCumsumThreads), 0, stream, dt, A, G,
-                         dtT, L, (int)H, ld, Lw);
-      break;
-    case 64:
-      hipLaunchKernelGGL(chunk_cumsum_kernel<64>, grid, dim3(kCumsumThreads), 0, stream, dt, A, G,
-                         dtT, L, (int)H, ld, Lw);
-      break;
-    case 128:
-      hipLaunchKernelGGL(chunk_cumsum_kernel<128>, grid, dim3(kCumsumThreads), 0, stream, dt, A, G,
-                         dtT, L, (int)H, ld, Lw);
-      break;
-    default:
-      hipLaunchKernelGGL(chunk_cumsum_kernel<256>, grid, dim3(kCumsumThreads), 0, stream, dt, A, G,
-                         dtT, L, (int)H, ld, Lw);
-      break;
+    case 32: launch_q<32>(grid, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream); break;
+    case 64: launch_q<64>(grid, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream); break;
+    case 128: launch_q<128>(grid, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream); break;
+    default: launch_q<256>(grid, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream); break;
   }
   return hipGetLastError();
 }

@@ -19,7 +19,11 @@
 namespace ssd {
 hipError_t launch_chunk_cumsum(const float* dt, const float* A, float* G, float* dtT,
                                int64_t batch, int64_t L, int64_t H, int Q, int64_t ld,
-                               int64_t Lw, hipStream_t stream);
+                               int64_t Lw, const DtXform* xf, hipStream_t stream);
+hipError_t launch_step(int io_bf16, float* state, const void* x, const float* dt, const float* A,
+                       const void* Bm, const void* Cm, const float* D, void* y,
+                       const DtXform* xf, int64_t batch, int64_t L, int64_t H, int64_t P,
+                       int64_t N, int64_t G, hipStream_t stream);
 hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, const float* Gw,
                               const float* dtw, void* S, int64_t batch, int64_t L, int64_t H,
                               int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
@@ -75,11 +79,12 @@ struct Plan {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Shape checks shared by every entry point (after the NULL checks).
-ssd_status plan_problem(const ssd_problem* prob, Plan* pl) {
+// Shape checks shared by every entry point (after the NULL checks).  The
+// decode step does not chunk, so it skips the chunk-size check.
+ssd_status plan_problem(const ssd_problem* prob, Plan* pl, bool need_chunk = true) {
   const ssd_problem& p = *prob;
   if (p.batch <= 0 || p.seqlen <= 0 || p.nheads <= 0 || p.headdim <= 0 || p.dstate <= 0 ||
-      p.ngroups <= 0 || p.chunk_size <= 0)
+      p.ngroups <= 0 || (need_chunk && p.chunk_size <= 0))
     return fail(SSD_ERR_BAD_SHAPE, "every size must be positive");
   if (p.nheads % p.ngroups != 0)
     return fail(SSD_ERR_BAD_SHAPE, "nheads (%lld) must be a multiple of ngroups (%lld)",
@@ -90,7 +95,7 @@ ssd_status plan_problem(const ssd_problem* prob, Plan* pl) {
     return fail(SSD_ERR_BAD_SHAPE, "tensor size overflows int64");
   if (p.seqlen > INT64_MAX / 2 - 256)
     return fail(SSD_ERR_BAD_SHAPE, "seqlen too large");
-  const int64_t Q = p.chunk_size;
+  const int64_t Q = need_chunk ? p.chunk_size : 256;
   if (!(Q == 32 || Q == 64 || Q == 128 || Q == 256))
     return fail(SSD_ERR_BAD_CHUNK, "chunk_size must be 32, 64, 128 or 256 (got %lld)", (long long)Q);
   if (p.io_dtype != SSD_BF16 && p.io_dtype != SSD_F32)
@@ -102,6 +107,25 @@ ssd_status plan_problem(const ssd_problem* prob, Plan* pl) {
   pl->Lp = pl->T * Q;
   pl->bf16 = p.io_dtype == SSD_BF16;
   pl->esize = pl->bf16 ? 2 : 4;
+  return SSD_OK;
+}
+
+// The optional step-size preparation: value checks (after the dtype check)
+// and the device-side description the kernels take.
+ssd_status check_dt_transform(const ssd_dt_transform* dtx, ssd::DtXform* xf) {
+  if (!dtx) return SSD_OK;
+  if (dtx->softplus != 0 && dtx->softplus != 1)
+    return fail(SSD_ERR_BAD_VALUE, "dt transform: softplus must be 0 or 1 (got %d)", dtx->softplus);
+  if (dtx->reserved != 0) return fail(SSD_ERR_BAD_VALUE, "dt transform: reserved field must be 0");
+  if (dtx->dt_min != dtx->dt_min || dtx->dt_max != dtx->dt_max)
+    return fail(SSD_ERR_BAD_VALUE, "dt transform: dt_min and dt_max must not be NaN");
+  if (dtx->dt_min > dtx->dt_max)
+    return fail(SSD_ERR_BAD_VALUE, "dt transform: dt_min (%g) exceeds dt_max (%g)",
+                (double)dtx->dt_min, (double)dtx->dt_max);
+  xf->bias = dtx->dt_bias;
+  xf->softplus = dtx->softplus;
+  xf->lo = dtx->dt_min;
+  xf->hi = dtx->dt_max;
   return SSD_OK;
 }
 
@@ -158,6 +182,7 @@ const char* ssd_status_string(int status) {
     case SSD_ERR_UNSUPPORTED: return "shape not supported by this build";
     case SSD_ERR_HIP: return "HIP runtime error";
     case SSD_ERR_INTERNAL: return "internal error";
+    case SSD_ERR_BAD_VALUE: return "invalid argument value";
     default: return "unknown status";
   }
 }
@@ -180,36 +205,47 @@ ssd_status ssd_fwd_workspace_size(const ssd_problem* prob, size_t* bytes) {
   }
 }
 
-ssd_status ssd_chunk_cumsum(const ssd_problem* prob, const float* dt, const float* A,
-                            float* G_out, float* dt_out, void* stream) {
+ssd_status ssd_chunk_cumsum_ex(const ssd_problem* prob, const ssd_dt_transform* dtx,
+                               const float* dt, const float* A, float* G_out, float* dt_out,
+                               void* stream) {
   try {
     if (!prob || !dt || !A || !G_out || !dt_out)
       return fail(SSD_ERR_NULL_POINTER, "prob, dt, A, G_out and dt_out must not be NULL");
     Plan pl;
     ssd_status st = plan_problem(prob, &pl);
     if (st != SSD_OK) return st;
-    if (!aligned16(dt) || !aligned16(A) || !aligned16(G_out) || !aligned16(dt_out))
-      return fail(SSD_ERR_MISALIGNED, "dt, A, G_out and dt_out must be 16-byte aligned");
+    ssd::DtXform xf;
+    st = check_dt_transform(dtx, &xf);
+    if (st != SSD_OK) return st;
+    if (!aligned16(dt) || !aligned16(A) || !aligned16(G_out) || !aligned16(dt_out) ||
+        (dtx && !aligned16(dtx->dt_bias)))
+      return fail(SSD_ERR_MISALIGNED, "dt, A, dt_bias, G_out and dt_out must be 16-byte aligned");
     st = check_supported(pl);
     if (st != SSD_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(ssd::launch_chunk_cumsum(dt, A, G_out, dt_out, pl.B, pl.L, pl.H, (int)pl.Q,
-                                               pl.L, pl.L, s),
+                                               pl.L, pl.L, dtx ? &xf : nullptr, s),
                       "chunk_cumsum launch");
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
   }
 }
 
+ssd_status ssd_chunk_cumsum(const ssd_problem* prob, const float* dt, const float* A,
+                            float* G_out, float* dt_out, void* stream) {
+  return ssd_chunk_cumsum_ex(prob, nullptr, dt, A, G_out, dt_out, stream);
+}
+
 static ssd_status run_states(const Plan& pl, const void* x, const float* dt, const float* A,
                              const void* B, const float* init_state, float* final_state,
-                             void* chunk_states, void* workspace, hipStream_t s) {
+                             void* chunk_states, void* workspace, const ssd::DtXform* xf,
+                             hipStream_t s) {
   char* ws = static_cast<char*>(workspace);
   float* Gw = reinterpret_cast<float*>(ws + pl.g_off);
   float* dtw = reinterpret_cast<float*>(ws + pl.dt_off);
   void* Hc = chunk_states ? chunk_states : static_cast<void*>(ws + pl.hc_off);
   hipError_t e = ssd::launch_chunk_cumsum(dt, A, Gw, dtw, pl.B, pl.L, pl.H, (int)pl.Q, pl.Lp,
-                                          pl.Lp, s);
+                                          pl.Lp, xf, s);
   if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
   // each chunk's own contribution S_c into the state buffer, then the
   // recurrence turns it, in place, into the chunk-start states H_c
@@ -242,7 +278,7 @@ ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* d
     workspace_plan(&pl);
     if (workspace_bytes < pl.bytes)
       return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
-    st = run_states(pl, x, dt, A, B, init_state, final_state, chunk_states, workspace,
+    st = run_states(pl, x, dt, A, B, init_state, final_state, chunk_states, workspace, nullptr,
                     static_cast<hipStream_t>(stream));
     return st;
   } catch (...) {
@@ -285,19 +321,22 @@ ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B
   }
 }
 
-ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, const float* A,
-                   const void* B, const void* C, const float* D, const float* init_state,
-                   void* y, float* final_state, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+ssd_status ssd_fwd_ex(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                      const float* dt, const float* A, const void* B, const void* C,
+                      const float* D, const float* init_state, void* y, float* final_state,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (!prob || !x || !dt || !A || !B || !C || !y || !workspace)
       return fail(SSD_ERR_NULL_POINTER, "prob, x, dt, A, B, C, y and workspace must not be NULL");
     Plan pl;
     ssd_status st = plan_problem(prob, &pl);
     if (st != SSD_OK) return st;
+    ssd::DtXform xf;
+    st = check_dt_transform(dtx, &xf);
+    if (st != SSD_OK) return st;
     if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
         !aligned16(D) || !aligned16(init_state) || !aligned16(y) || !aligned16(final_state) ||
-        !aligned16(workspace))
+        !aligned16(workspace) || (dtx && !aligned16(dtx->dt_bias)))
       return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
     st = check_supported(pl);
     if (st != SSD_OK) return st;
@@ -305,9 +344,48 @@ ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, cons
     if (workspace_bytes < pl.bytes)
       return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_states(pl, x, dt, A, B, init_state, final_state, nullptr, workspace, s);
+    st = run_states(pl, x, dt, A, B, init_state, final_state, nullptr, workspace,
+                    dtx ? &xf : nullptr, s);
     if (st != SSD_OK) return st;
     return run_out(pl, x, B, C, D, y, workspace, s);
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                   const void* B, const void* C, const float* D, const float* init_state,
+                   void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return ssd_fwd_ex(prob, nullptr, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                    workspace_bytes, stream);
+}
+
+ssd_status ssd_step(const ssd_problem* prob, const ssd_dt_transform* dtx, float* state,
+                    const void* x, const float* dt, const float* A, const void* B, const void* C,
+                    const float* D, void* y, void* stream) {
+  try {
+    if (!prob || !state || !x || !dt || !A || !B || !C || !y)
+      return fail(SSD_ERR_NULL_POINTER, "prob, state, x, dt, A, B, C and y must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl, /*need_chunk=*/false);
+    if (st != SSD_OK) return st;
+    ssd::DtXform xf;
+    st = check_dt_transform(dtx, &xf);
+    if (st != SSD_OK) return st;
+    if (!aligned16(state) || !aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) ||
+        !aligned16(C) || !aligned16(D) || !aligned16(y) || (dtx && !aligned16(dtx->dt_bias)))
+      return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
+    if (pl.P % 16 != 0 || pl.N % 16 != 0)
+      return fail(SSD_ERR_UNSUPPORTED, "headdim (%lld) and dstate (%lld) must be multiples of 16",
+                  (long long)pl.P, (long long)pl.N);
+    if (pl.N > 256) return fail(SSD_ERR_UNSUPPORTED, "dstate must be <= 256 (got %lld)", (long long)pl.N);
+    if (pl.H > 65535 || pl.B > 65535 || pl.P > INT32_MAX / 2)
+      return fail(SSD_ERR_UNSUPPORTED, "grid too large for this build");
+    return hip_status(ssd::launch_step(pl.bf16, state, x, dt, A, B, C, D, y, dtx ? &xf : nullptr,
+                                       pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
+                                       static_cast<hipStream_t>(stream)),
+                      "step launch");
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
   }

@@ -47,6 +47,23 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 // Hardware base-2 exponential (v_exp_f32).  exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Optional preparation of the raw step size, applied where dt is first read
+// (chunk_cumsum, or the decode step) so that every later stage sees the
+// prepared value:  v = dt + bias[h];  v = softplus(v) = log(1 + e^v) when
+// asked;  v = min(max(v, lo), hi).  softplus is evaluated as
+// max(v, 0) + log1p(e^{-|v|}), which neither overflows nor loses the small
+// values of strongly negative v.
+struct DtXform {
+  const float* bias;   // [H] or nullptr
+  int softplus;
+  float lo, hi;
+};
+__device__ __forceinline__ float dt_prepare(const DtXform& f, float v, int h) {
+  if (f.bias) v += f.bias[h];
+  if (f.softplus) v = fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+  return fminf(fmaxf(v, f.lo), f.hi);
+}
+
 // 16-byte vector of io elements: 8 bf16 or 4 fp32.
 typedef uint4 vec16;
 template <typename T> struct Vec16 { static constexpr int n = 16 / sizeof(T); };

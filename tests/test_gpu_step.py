@@ -1,0 +1,204 @@
+"""GPU parity of the token-sequential (decode) mode and of the raw step-size
+entry points, called through the C ABI, against the CPU oracle.
+
+ssd_step's reference is the oracle's token recurrence started from the same
+state (the decode mode is that recurrence; the oracle pins it).  The raw-dt
+entry points (ssd_fwd_ex, ssd_chunk_cumsum_ex, ssd_step with a transform)
+are compared with the oracle fed the oracle's own fp64 preparation
+clamp(softplus(dt_raw + dt_bias)), rounded to fp32 where the oracle takes fp32.
+Tolerances as in the forward-pass tests (bf16: rel-L2 <= 5e-3 and max-abs <=
+2e-2 max|ref|; fp32: rel-L2 <= 1e-5; step-size preparation and running sums:
+rel 1e-5 elementwise).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_synth
+from parity_util import assert_close, errors
+
+pytestmark = pytest.mark.gpu
+
+lib = pytest.importorskip("state_space_sequence_03_amd")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print("\n[gpu-case] %s" % request.node.name, flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def to_dev(inp):
+    return {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+
+
+def prob(**kw):
+    base = dict(batch=2, seqlen=1, nheads=4, headdim=64, dstate=128, ngroups=1,
+                chunk_size=256, io_dtype="bf16", init_std=0.1)
+    base.update(kw)
+    return ssd_synth.Problem(**base)
+
+
+def oracle_rec(inp, dt=None, use_D=True):
+    return oracle.recurrence(inp["x"], inp["dt"] if dt is None else dt, inp["A"], inp["B"],
+                             inp["C"], inp["D"] if use_D else None, inp["init_state"])
+
+
+# ------------------------------------------------------------ decode step
+
+STEP_SHAPES = [
+    # (batch, H, P, N, G, io)
+    (2, 80, 64, 128, 1, "bf16"),      # one decode step of the 2.7B-shaped layer
+    (4, 8, 64, 256, 2, "bf16"),       # large state, groups
+    (3, 5, 16, 16, 1, "fp32"),
+    (2, 6, 32, 48, 3, "fp32"),        # dstate not a power of two: idle lanes in each row
+    (1, 3, 80, 96, 1, "bf16"),        # headdim beyond one workgroup's rows
+]
+
+
+@pytest.mark.parametrize("shape", STEP_SHAPES, ids=lambda s: "B%d_H%d_P%d_N%d_G%d_%s" % s)
+def test_step_one_token(shape):
+    bsz, H, P, N, G, io = shape
+    p = prob(batch=bsz, nheads=H, headdim=P, dstate=N, ngroups=G, io_dtype=io)
+    inp = ssd_synth.make_inputs(p, seed=H + N)
+    d = to_dev(inp)
+    state = d["init_state"].clone()
+    y = lib.ssd_step(state, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    y_ref, fin_ref, _ = oracle_rec(inp)
+    assert y.shape == d["x"].shape and y.dtype == d["x"].dtype
+    assert_close(y, y_ref, io, "y")
+    # the state stays fp32 in a decode step: hold it to the fp32 bound
+    assert_close(state, fin_ref, "fp32", "state")
+
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_step_many_tokens(io):
+    p = prob(batch=2, seqlen=37, nheads=6, headdim=32, dstate=64, ngroups=2, io_dtype=io)
+    inp = ssd_synth.make_inputs(p, seed=31)
+    d = to_dev(inp)
+    state = d["init_state"].clone()
+    y = lib.ssd_step(state, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    y_ref, fin_ref, _ = oracle_rec(inp)
+    assert_close(y, y_ref, io, "y")
+    assert_close(state, fin_ref, "fp32", "state")
+
+
+def test_step_without_skip_and_from_zero_state():
+    p = prob(batch=2, seqlen=5, nheads=4, headdim=64, dstate=128, init_std=None)
+    inp = ssd_synth.make_inputs(p, seed=32)
+    d = to_dev(inp)
+    state = torch.zeros((2, 4, 64, 128), dtype=torch.float32, device="cuda")
+    y = lib.ssd_step(state, d["x"], d["dt"], d["A"], d["B"], d["C"], None)
+    y_ref, fin_ref, _ = oracle_rec(inp, use_D=False)
+    assert_close(y, y_ref, "bf16", "y")
+    assert_close(state, fin_ref, "fp32", "state")
+
+
+def test_decode_after_prefill():
+    # prefill 600 tokens with the chunked pass, then decode 8 tokens one call
+    # at a time from its final state; the whole sequence is the reference
+    p = prob(batch=2, seqlen=608, nheads=4, headdim=64, dstate=128, chunk_size=128)
+    inp = ssd_synth.make_inputs(p, seed=33)
+    d = to_dev(inp)
+    y_ref, fin_ref, _ = oracle_rec(inp)
+    L1 = 600
+    sl = lambda t, a, b: t[:, a:b].contiguous()
+    y1, state = lib.ssd_fwd(sl(d["x"], 0, L1), sl(d["dt"], 0, L1), d["A"], sl(d["B"], 0, L1),
+                            sl(d["C"], 0, L1), d["D"], 128, d["init_state"])
+    ys = [y1]
+    for t in range(L1, 608):
+        ys.append(lib.ssd_step(state, sl(d["x"], t, t + 1), sl(d["dt"], t, t + 1), d["A"],
+                               sl(d["B"], t, t + 1), sl(d["C"], t, t + 1), d["D"]))
+    assert_close(torch.cat(ys, 1), y_ref, "bf16", "y")
+    assert_close(ys[-1], y_ref[:, -1:], "bf16", "y of the last decoded token")
+    assert_close(state, fin_ref, "bf16", "state")
+
+
+def test_step_repeatable():
+    p = prob(batch=2, seqlen=3, nheads=8)
+    d = to_dev(ssd_synth.make_inputs(p, seed=34))
+    s1, s2 = d["init_state"].clone(), d["init_state"].clone()
+    y1 = lib.ssd_step(s1, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    y2 = lib.ssd_step(s2, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+
+
+# ------------------------------------------------------------ raw step size
+
+LIMITS = [(0.0, float("inf")), (1e-3, 0.05)]
+
+
+@pytest.mark.parametrize("limit", LIMITS, ids=["unclamped", "clamped"])
+@pytest.mark.parametrize("L,H,Q", [(300, 5, 32), (1000, 17, 128), (777, 80, 256)])
+def test_chunk_cumsum_raw_dt(L, H, Q, limit):
+    p = prob(seqlen=L, nheads=H, chunk_size=Q, batch=2)
+    inp = ssd_synth.make_inputs(p, seed=L + H + 1)
+    G, dtt = lib.ssd_chunk_cumsum_ex(inp["dt_raw"].cuda(), inp["A"].cuda(), Q,
+                                     dt_bias=inp["dt_bias"].cuda(), dt_limit=limit)
+    dt_ref = oracle.dt_transform(inp["dt_raw"], inp["dt_bias"], True, *limit)
+    if limit[1] < 1.0:
+        assert (dt_ref >= limit[1]).mean() > 0.01      # the clamp is exercised
+    d_gpu = dtt.cpu().double().numpy()
+    d_ref = dt_ref.transpose(0, 2, 1)
+    assert np.all(np.abs(d_gpu - d_ref) <= 1e-5 * np.abs(d_ref))
+    Gref = oracle.chunk_cumsum(dt_ref.astype(np.float32), inp["A"], Q)
+    Gg = G.cpu().double().numpy()
+    assert np.all(np.abs(Gg - Gref) <= 1e-5 * np.abs(Gref) + 1e-6)
+
+
+def test_chunk_cumsum_bias_only_and_no_softplus():
+    p = prob(seqlen=500, nheads=8, chunk_size=64)
+    inp = ssd_synth.make_inputs(p, seed=35)
+    raw = inp["dt"] - 0.25 * inp["dt"]           # positive, no softplus needed
+    bias = torch.full((8,), 0.01)
+    _, dtt = lib.ssd_chunk_cumsum(raw.cuda(), inp["A"].cuda(), 64, dt_bias=bias.cuda(),
+                                  dt_softplus=False)
+    ref = oracle.dt_transform(raw, bias, use_softplus=False).transpose(0, 2, 1)
+    assert np.all(np.abs(dtt.cpu().double().numpy() - ref) <= 1e-6 * ref)
+
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", [(1000, 128, 4, 128, 2), (513, 256, 3, 64, 1), (300, 64, 2, 256, 1)],
+                         ids=lambda c: "L%d_Q%d_H%d_N%d_G%d" % c)
+def test_fwd_raw_dt(io, case):
+    L, Q, H, N, G = case
+    p = prob(seqlen=L, chunk_size=Q, nheads=H, dstate=N, ngroups=G, io_dtype=io)
+    inp = ssd_synth.make_inputs(p, seed=L + 2)
+    d = to_dev(inp)
+    limit = (1e-3, 0.08)
+    y, fin = lib.ssd_fwd_ex(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], Q,
+                            d["init_state"], dt_bias=d["dt_bias"], dt_limit=limit)
+    dt_ref = oracle.dt_transform(inp["dt_raw"], inp["dt_bias"], True, *limit).astype(np.float32)
+    y_ref, fin_ref, _ = oracle_rec(inp, dt=dt_ref)
+    assert_close(y, y_ref, io, "y")
+    assert_close(fin, fin_ref, io, "final_state")
+
+
+def test_fwd_raw_dt_matches_prepared_dt():
+    # the generator's dt is softplus(dt_raw + dt_bias): both entry points agree
+    p = prob(seqlen=1024, nheads=8, chunk_size=256)
+    d = to_dev(ssd_synth.make_inputs(p, seed=36))
+    y1, f1 = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 256, d["init_state"])
+    y2, f2 = lib.ssd_fwd_ex(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], 256,
+                            d["init_state"], dt_bias=d["dt_bias"])
+    rl2, _ = errors(y2, y1)
+    assert rl2 < 1e-3
+    rl2, _ = errors(f2, f1)
+    assert rl2 < 1e-4
+
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_step_raw_dt(io):
+    p = prob(batch=3, seqlen=4, nheads=6, headdim=64, dstate=128, ngroups=2, io_dtype=io)
+    inp = ssd_synth.make_inputs(p, seed=37)
+    d = to_dev(inp)
+    limit = (1e-3, 0.05)
+    state = d["init_state"].clone()
+    y = lib.ssd_step(state, d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"],
+                     dt_bias=d["dt_bias"], dt_softplus=True, dt_limit=limit)
+    dt_ref = oracle.dt_transform(inp["dt_raw"], inp["dt_bias"], True, *limit).astype(np.float32)
+    y_ref, fin_ref, _ = oracle_rec(inp, dt=dt_ref)
+    assert_close(y, y_ref, io, "y")
+    assert_close(state, fin_ref, "fp32", "state")

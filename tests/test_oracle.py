@@ -235,3 +235,64 @@ def test_inputs_are_seeded_and_shaped():
     assert torch.all(a["dt"] > 0) and torch.all(a["A"] < 0)
     c2 = ssd_synth.CONFIGS["mamba2_2p7b"]
     assert c2.init_std == 0.1 and c2.nchunks == 32
+
+
+# ------------------------------------------------- step-size preparation pins
+
+def test_softplus_closed_forms():
+    sp = oracle.softplus
+    assert abs(sp(0.0) - math.log(2.0)) < 1e-16
+    v = np.linspace(-30.0, 30.0, 601)
+    # softplus(v) - softplus(-v) = v  (log(1+e^v) - log(1+e^-v) = log e^v)
+    np.testing.assert_allclose(sp(v) - sp(-v), v, rtol=0, atol=1e-13)
+    # inverse of the generator's inv_softplus: softplus(log(e^y - 1)) = y
+    y = np.exp(np.linspace(math.log(1e-4), math.log(20.0), 200))
+    np.testing.assert_allclose(sp(np.log(np.expm1(y))), y, rtol=1e-13)
+    # asymptotes: ~v for large v (difference e^-v), ~e^v for very negative v
+    assert sp(50.0) == 50.0 and abs(sp(800.0) - 800.0) == 0.0
+    np.testing.assert_allclose(sp(-40.0), math.exp(-40.0), rtol=1e-15)
+    assert np.all(sp(v) > 0) and np.all(np.diff(sp(v)) > 0)
+
+
+def test_dt_transform_bias_clamp_and_identity():
+    raw = torch.tensor([[[-3.0, 0.0], [2.0, 40.0]]])           # [1, 2, 2]
+    bias = torch.tensor([1.0, -0.5])
+    got = oracle.dt_transform(raw, bias, use_softplus=True)
+    v = raw.double().numpy() + bias.double().numpy()
+    np.testing.assert_allclose(got, np.log1p(np.exp(np.minimum(v, 30))) + np.maximum(v - 30, 0),
+                               rtol=1e-14)
+    # without softplus the bias is just added; the clamp bounds from both sides
+    np.testing.assert_array_equal(oracle.dt_transform(raw, bias, use_softplus=False,
+                                                      dt_min=-np.inf), v)
+    # the default lower limit 0 removes negative values
+    assert oracle.dt_transform(raw, bias, use_softplus=False).min() == 0.0
+    cl = oracle.dt_transform(raw, bias, use_softplus=False, dt_min=0.25, dt_max=2.0)
+    np.testing.assert_array_equal(cl, np.clip(v, 0.25, 2.0))
+    assert cl.min() == 0.25 and cl.max() == 2.0
+    # values inside the limits are fixed points of the clamp
+    inside = oracle.dt_transform(raw, bias, dt_min=1e-9, dt_max=1e9)
+    np.testing.assert_array_equal(inside, got)
+
+
+def test_dt_transform_reproduces_generated_step_sizes():
+    # the generator draws dt = softplus(dt_raw + dt_bias) in fp32 (a separate
+    # implementation); the fp64 preparation agrees to fp32 rounding
+    inp = inputs_of(small_problem(seqlen=200, nheads=6, ngroups=2), seed=21)
+    got = oracle.dt_transform(inp["dt_raw"], inp["dt_bias"], use_softplus=True)
+    np.testing.assert_allclose(got, inp["dt"].double().numpy(), rtol=2e-6)
+
+
+def test_token_at_a_time_equals_whole_sequence():
+    # the decode mode's reference: L calls of one token each, the state handed
+    # from call to call, against one call over the whole sequence
+    inp = inputs_of(small_problem(seqlen=12), seed=22)
+    y, fin, _ = run_rec(inp)
+    state = inp["init_state"]
+    ys = []
+    for t in range(12):
+        one = {k: (v[:, t:t + 1] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+        one["init_state"] = state
+        yt, ft, _ = run_rec(one)
+        ys.append(yt)
+        state = torch.from_numpy(ft.astype(np.float32))
+    assert rel(np.concatenate(ys, 1), y) < 1e-6 and rel(ft, fin) < 1e-6
