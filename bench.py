@@ -12,7 +12,13 @@ Default workload: the Mamba-2 2.7B-shaped layer, batch 2 x seqlen 8192,
 dt/A/D and a nonzero fp32 initial state.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --mode decode      (token-sequential mode: one ssd_step per step)
   python bench.py --copy-probe       (plain copy kernel, for counter scaling)
+
+Decode mode: the same 2.7B-shaped layer (80 heads, headdim 64, dstate 128,
+1 group, bf16 x/B/C) at batch 128, one token per step, advancing a resident
+fp32 state in place; the kernel streams the state (read + write) and is
+measured against the HBM roofline.
 """
 from __future__ import annotations
 
@@ -31,6 +37,7 @@ PEAK_BF16_MFMA = 2.5e15     # dense bf16 MFMA, MI355X published
 PEAK_FP32_MFMA = 157.3e12   # dense fp32 MFMA
 PEAK_HBM = 8.0e12           # HBM3E bytes/s
 METRIC = "SSD fwd tokens/sec (batch·seqlen) at 1 MI355X; % of bf16 MFMA roofline"
+DECODE_METRIC = "SSD decode tokens/sec (batch, one token per step) at 1 MI355X; % of HBM roofline"
 COPY_PROBE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compute_out_{workload}_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "state_space_sequence_03_amd", "csrc", f)
@@ -134,6 +141,93 @@ def cpu_baseline(inputs, prob, target_seconds=15.0):
             "sample": sample, "seconds": round(dt, 3)}
 
 
+def decode_counts(p):
+    """Algorithmic bytes of one decode step: the fp32 state read and written,
+    x read and y written, the B and C rows, dt, A and D."""
+    Bz, L, H, P, N, G = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups
+    e = 2 if p.io_dtype == "bf16" else 4
+    return (2 * 4 * Bz * H * P * N + 2 * Bz * L * H * P * e + 2 * Bz * L * G * N * e
+            + 4 * Bz * L * H + 8 * H)
+
+
+DECODE_WORKLOADS = {
+    "decode_2p7b_b128": dict(batch=128, seqlen=1, nheads=80, headdim=64, dstate=128, ngroups=1,
+                             chunk_size=256, init_std=0.1, name="decode_2p7b_b128"),
+}
+
+
+def bench_decode(args):
+    import torch
+    import oracle
+    import ssd_synth
+    import state_space_sequence_03_amd as ssd
+
+    name = args.workload if args.workload in DECODE_WORKLOADS else "decode_2p7b_b128"
+    prob = ssd_synth.Problem(**DECODE_WORKLOADS[name])
+    inputs = ssd_synth.make_inputs(prob, 0)
+    dev = torch.device("cuda:0")
+    d = {k: (None if v is None else v.to(dev)) for k, v in inputs.items()}
+    state = d["init_state"].clone()
+    y = torch.empty_like(d["x"])
+
+    def step():
+        ssd.ssd_step(state, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], out=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record()
+        step()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    ms_kernel = sum(a.elapsed_time(b) for a, b in ev) / K
+    nbytes = decode_counts(prob)
+    achieved = nbytes / (ms_kernel * 1e-3)
+    line = {
+        "metric": DECODE_METRIC,
+        "value": prob.batch / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prob.io_dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "batch": prob.batch, "tokens_per_step": prob.seqlen,
+                   "nheads": prob.nheads, "headdim": prob.headdim, "dstate": prob.dstate,
+                   "ngroups": prob.ngroups, "state": "fp32, in place"},
+        "roofline": {"kernel": "step", "bound": "hbm", "achieved": achieved / 1e9,
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": achieved / PEAK_HBM,
+                     "traffic": None, "bytes_per_launch": nbytes,
+                     "kernel_ms": ms_kernel},
+    }
+    if not args.no_cpu_baseline:
+        arrs = {k: (None if v is None else oracle.as_f32(v)) for k, v in inputs.items()}
+        nthreads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+        reps, t = 0, 0.0
+        while t < 10.0 and reps < 2000:
+            t0 = time.perf_counter()
+            oracle.recurrence(arrs["x"], arrs["dt"], arrs["A"], arrs["B"], arrs["C"], arrs["D"],
+                              arrs["init_state"], nthreads=nthreads)
+            t += time.perf_counter() - t0
+            reps += 1
+        line["cpu_baseline"] = {"value": reps * prob.batch / t, "unit": "tokens/s",
+                                "cores": nthreads, "kind": "oracle",
+                                "sample": "whole decode step (%d sequences x 1 token), run %d times"
+                                          % (prob.batch, reps),
+                                "seconds": round(t, 3)}
+    print(json.dumps(line), flush=True)
+
+
 def copy_probe():
     import torch
     n = COPY_PROBE_BYTES // 4
@@ -153,6 +247,7 @@ def main():
     ap.add_argument("--workload", default="mamba2_2p7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -170,6 +265,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.mode == "decode":
+        bench_decode(args)
+        return
     if args.workload not in ssd_synth.CONFIGS:
         print("unknown workload %r (choose from %s)" % (args.workload, ", ".join(ssd_synth.CONFIGS)),
               file=sys.stderr)
