@@ -12,6 +12,7 @@ Default workload: the Mamba-2 2.7B-shaped layer, batch 2 x seqlen 8192,
 dt/A/D and a nonzero fp32 initial state.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --raw-dt           (dt given raw: bias + softplus applied in stage 1)
   python bench.py --mode decode      (token-sequential mode: one ssd_step per step)
   python bench.py --copy-probe       (plain copy kernel, for counter scaling)
 
@@ -248,6 +249,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill")
+    ap.add_argument("--raw-dt", action="store_true",
+                    help="pass the raw step size and let stage 1 apply bias + softplus")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -288,8 +291,13 @@ def main():
     def step(ev_a=None, ev_b=None, ev_c=None):
         if ev_a is not None:
             ev_a.record()
-        ssd.ssd_fwd_states(d["x"], d["dt"], d["A"], d["B"], Q, d["init_state"],
-                           want_chunk_states=False, workspace=ws, final_out=fin)
+        if args.raw_dt:
+            ssd.ssd_fwd_states(d["x"], d["dt_raw"], d["A"], d["B"], Q, d["init_state"],
+                               want_chunk_states=False, workspace=ws, final_out=fin,
+                               dt_bias=d["dt_bias"], dt_softplus=True)
+        else:
+            ssd.ssd_fwd_states(d["x"], d["dt"], d["A"], d["B"], Q, d["init_state"],
+                               want_chunk_states=False, workspace=ws, final_out=fin)
         if ev_b is not None:
             ev_b.record()
         ssd.ssd_compute_out(d["x"], d["B"], d["C"], d["D"], Q, ws, out=y)
@@ -354,7 +362,8 @@ def main():
         "config": {"workload": args.workload, "batch": prob.batch, "seqlen": prob.seqlen,
                    "nheads": prob.nheads, "headdim": prob.headdim, "dstate": prob.dstate,
                    "ngroups": prob.ngroups, "chunk_size": Q,
-                   "init_state": prob.init_std is not None, "accumulate": "fp32"},
+                   "init_state": prob.init_std is not None, "accumulate": "fp32",
+                   "dt": "raw, bias + softplus in chunk_cumsum" if args.raw_dt else "prepared"},
         "path_mfma_frac": cnt["f_path"] / (ms_step * 1e-3) / peak_mfma,
         "path_hbm_frac": cnt["b_min"] / (ms_step * 1e-3) / PEAK_HBM,
         "path_tflops": cnt["f_path"] / (ms_step * 1e-3) / 1e12,

@@ -204,6 +204,15 @@ ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* d
                           float* final_state, void* chunk_states, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* ssd_fwd_states with the raw step size prepared inside stage 1 (see
+ * ssd_dt_transform; dtx = NULL makes this exactly ssd_fwd_states).  A
+ * following ssd_compute_out on the same workspace uses the prepared step
+ * sizes, so the pair equals ssd_fwd_ex. */
+ssd_status ssd_fwd_states_ex(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                             const float* dt, const float* A, const void* B,
+                             const float* init_state, float* final_state, void* chunk_states,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Stage 3 alone (compute_out): y from the inputs and from the running sums and
  * chunk-start states that a preceding ssd_fwd_states call left in `workspace`
  * (same problem, same workspace, chunk_states == NULL, enqueued earlier on

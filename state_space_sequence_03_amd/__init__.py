@@ -7,7 +7,7 @@ PyTorch fallback: importing works without the library, but every call raises
 if ``libssd.so`` is missing or the tensors are not on a GPU.
 
 Names match the C ABI in include/ssd.h:
-    ssd_fwd, ssd_fwd_ex, ssd_fwd_states, ssd_compute_out, ssd_chunk_cumsum,
+    ssd_fwd, ssd_fwd_ex, ssd_fwd_states, ssd_fwd_states_ex, ssd_compute_out, ssd_chunk_cumsum,
     ssd_chunk_cumsum_ex, ssd_step, ssd_fwd_workspace_size, ssd_status_string,
     ssd_last_error_message, ssd_abi_version
 """
@@ -23,7 +23,8 @@ import torch
 __all__ = ["SsdError", "SsdArgumentError", "lib_path", "load_library", "make_problem",
            "ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
            "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_states", "ssd_compute_out",
-           "ssd_chunk_cumsum", "ssd_fwd_ex", "ssd_chunk_cumsum_ex", "ssd_step",
+           "ssd_chunk_cumsum", "ssd_fwd_ex", "ssd_fwd_states_ex", "ssd_chunk_cumsum_ex",
+           "ssd_step",
            "SSD_F32", "SSD_BF16"]
 
 SSD_F32, SSD_BF16 = 0, 1
@@ -98,6 +99,8 @@ def load_library():
         X = ctypes.POINTER(ssd_dt_transform)
         lib.ssd_fwd_ex.restype = ctypes.c_int
         lib.ssd_fwd_ex.argtypes = [P, X] + [vp] * 10 + [sz, vp]
+        lib.ssd_fwd_states_ex.restype = ctypes.c_int
+        lib.ssd_fwd_states_ex.argtypes = [P, X] + [vp] * 8 + [sz, vp]
         lib.ssd_chunk_cumsum_ex.restype = ctypes.c_int
         lib.ssd_chunk_cumsum_ex.argtypes = [P, X] + [vp] * 5
         lib.ssd_step.restype = ctypes.c_int
@@ -248,8 +251,11 @@ def ssd_fwd_states(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
                    chunk_size: int = 256, init_state: Optional[torch.Tensor] = None, *,
                    want_chunk_states: bool = True,
                    workspace: Optional[torch.Tensor] = None,
-                   final_out: Optional[torch.Tensor] = None):
-    """Stages 1-2 only.  Returns (final_state fp32, chunk_states [B,H,T,P,N] or None)."""
+                   final_out: Optional[torch.Tensor] = None,
+                   dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False,
+                   dt_limit: Optional[Tuple[float, float]] = None):
+    """Stages 1-2 only.  Returns (final_state fp32, chunk_states [B,H,T,P,N] or None).
+    dt_bias / dt_softplus / dt_limit: raw step size, as in ssd_fwd (ssd_fwd_states_ex)."""
     lib = load_library()
     prob = _problem_of(x, B, chunk_size)
     if x.dtype != B.dtype:
@@ -261,13 +267,25 @@ def ssd_fwd_states(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
                                                               device=x.device)
     cs = torch.empty((bsz, H, T, P, N), dtype=x.dtype, device=x.device) if want_chunk_states else None
     ws, ws_bytes = _workspace(prob, x.device, workspace)
-    st = lib.ssd_fwd_states(ctypes.byref(prob), _dev(x, "x"), _dev(dt, "dt", torch.float32),
-                            _dev(A, "A", torch.float32), _dev(B, "B"),
-                            _dev(init_state, "init_state", torch.float32),
-                            _dev(fin, "final_state", torch.float32), _dev(cs, "chunk_states"),
-                            _dev(ws, "workspace"), ws_bytes, _stream(x.device))
+    args = (_dev(x, "x"), _dev(dt, "dt", torch.float32),
+            _dev(A, "A", torch.float32), _dev(B, "B"),
+            _dev(init_state, "init_state", torch.float32),
+            _dev(fin, "final_state", torch.float32), _dev(cs, "chunk_states"),
+            _dev(ws, "workspace"), ws_bytes, _stream(x.device))
+    xf, xfp = _dt_transform(x, H, dt_bias, dt_softplus, dt_limit)
+    if xf is None:
+        st = lib.ssd_fwd_states(ctypes.byref(prob), *args)
+    else:
+        st = lib.ssd_fwd_states_ex(ctypes.byref(prob), xfp, *args)
     _check(st)
     return fin, cs
+
+
+def ssd_fwd_states_ex(x, dt, A, B, chunk_size=256, init_state=None, *, dt_bias=None,
+                      dt_softplus=True, dt_limit=(0.0, float("inf")), **kw):
+    """ssd_fwd_states from a raw step size (prepared as in ssd_fwd_ex)."""
+    return ssd_fwd_states(x, dt, A, B, chunk_size, init_state, dt_bias=dt_bias,
+                          dt_softplus=dt_softplus, dt_limit=dt_limit, **kw)
 
 
 def ssd_compute_out(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

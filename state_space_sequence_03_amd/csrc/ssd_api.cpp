@@ -258,10 +258,10 @@ static ssd_status run_states(const Plan& pl, const void* x, const float* dt, con
   return hip_status(e, "state_pass launch");
 }
 
-ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* dt,
-                          const float* A, const void* B, const float* init_state,
-                          float* final_state, void* chunk_states, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+ssd_status ssd_fwd_states_ex(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                             const float* dt, const float* A, const void* B,
+                             const float* init_state, float* final_state, void* chunk_states,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (!prob || !x || !dt || !A || !B || !final_state || !workspace)
       return fail(SSD_ERR_NULL_POINTER,
@@ -269,21 +269,31 @@ ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* d
     Plan pl;
     ssd_status st = plan_problem(prob, &pl);
     if (st != SSD_OK) return st;
+    ssd::DtXform xf;
+    st = check_dt_transform(dtx, &xf);
+    if (st != SSD_OK) return st;
     if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) ||
         !aligned16(init_state) || !aligned16(final_state) || !aligned16(chunk_states) ||
-        !aligned16(workspace))
+        !aligned16(workspace) || (dtx && !aligned16(dtx->dt_bias)))
       return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
     st = check_supported(pl);
     if (st != SSD_OK) return st;
     workspace_plan(&pl);
     if (workspace_bytes < pl.bytes)
       return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
-    st = run_states(pl, x, dt, A, B, init_state, final_state, chunk_states, workspace, nullptr,
-                    static_cast<hipStream_t>(stream));
-    return st;
+    return run_states(pl, x, dt, A, B, init_state, final_state, chunk_states, workspace,
+                      dtx ? &xf : nullptr, static_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
   }
+}
+
+ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* dt,
+                          const float* A, const void* B, const float* init_state,
+                          float* final_state, void* chunk_states, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return ssd_fwd_states_ex(prob, nullptr, x, dt, A, B, init_state, final_state, chunk_states,
+                           workspace, workspace_bytes, stream);
 }
 
 static ssd_status run_out(const Plan& pl, const void* x, const void* B, const void* C,

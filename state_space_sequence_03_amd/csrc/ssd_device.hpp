@@ -47,12 +47,27 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 // Hardware base-2 exponential (v_exp_f32).  exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// log(1 + e^v) as max(v, 0) + log1p(e^{-|v|}): e^{-|v|} <= 1 never
+// overflows, and log1p keeps the small values of strongly negative v.
+// log1p(w) comes from the hardware base-2 log with Kahan's correction
+// (u = 1 + w; log1p(w) = log(u) * w / (u - 1), or w when u rounds to 1;
+// D. Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", 1991, Theorem 4), accurate to a few ulps with
+// no table or polynomial of its own; the quotient uses the hardware
+// reciprocal (1 ulp), since u - 1 is exact.
+__device__ __forceinline__ float softplus_f32(float v) {
+  const float w = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);
+  const float u = 1.0f + w;
+  const float lp = u == 1.0f ? w
+                             : __builtin_amdgcn_logf(u) * (w * __builtin_amdgcn_rcpf(u - 1.0f)) *
+                                   0.6931471805599453f;
+  return fmaxf(v, 0.0f) + lp;
+}
+
 // Optional preparation of the raw step size, applied where dt is first read
 // (chunk_cumsum, or the decode step) so that every later stage sees the
-// prepared value:  v = dt + bias[h];  v = softplus(v) = log(1 + e^v) when
-// asked;  v = min(max(v, lo), hi).  softplus is evaluated as
-// max(v, 0) + log1p(e^{-|v|}), which neither overflows nor loses the small
-// values of strongly negative v.
+// prepared value:  v = dt + bias[h];  v = softplus(v) when asked;
+// v = min(max(v, lo), hi).
 struct DtXform {
   const float* bias;   // [H] or nullptr
   int softplus;
@@ -60,7 +75,7 @@ struct DtXform {
 };
 __device__ __forceinline__ float dt_prepare(const DtXform& f, float v, int h) {
   if (f.bias) v += f.bias[h];
-  if (f.softplus) v = fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+  if (f.softplus) v = softplus_f32(v);
   return fminf(fmaxf(v, f.lo), f.hi);
 }
 

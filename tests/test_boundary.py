@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(so):
     assert set(names) == {"ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
                           "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk_cumsum",
                           "ssd_fwd_states", "ssd_compute_out", "ssd_fwd_ex",
-                          "ssd_chunk_cumsum_ex", "ssd_step"}
+                          "ssd_chunk_cumsum_ex", "ssd_step", "ssd_fwd_states_ex"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
@@ -191,6 +191,8 @@ def test_fwd_ex_rejects_bad_transform(so, xf):
     assert "dt transform" in lib.ssd_last_error_message()
     assert so.ssd_chunk_cumsum_ex(ctypes.byref(P()), ctypes.byref(xf), FAKE, FAKE, FAKE, FAKE,
                                   None) == BADVAL
+    assert so.ssd_fwd_states_ex(ctypes.byref(P()), ctypes.byref(xf), FAKE, FAKE, FAKE, FAKE, None,
+                                FAKE, None, FAKE, 0, None) == BADVAL
 
 
 def test_fwd_ex_check_order(so):

@@ -176,6 +176,21 @@ def test_fwd_raw_dt(io, case):
     assert_close(fin, fin_ref, io, "final_state")
 
 
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_fwd_states_raw_dt(io):
+    p = prob(seqlen=700, chunk_size=128, nheads=3, dstate=64, io_dtype=io)
+    inp = ssd_synth.make_inputs(p, seed=38)
+    d = to_dev(inp)
+    fin, cs = lib.ssd_fwd_states_ex(d["x"], d["dt_raw"], d["A"], d["B"], 128, d["init_state"],
+                                    dt_bias=d["dt_bias"])
+    dt_ref = oracle.dt_transform(inp["dt_raw"], inp["dt_bias"], True).astype(np.float32)
+    _, fin_ref, cs_ref = oracle.recurrence(inp["x"], dt_ref, inp["A"], inp["B"], inp["C"],
+                                           inp["D"], inp["init_state"], chunk_size=128,
+                                           want_chunk_states=True)
+    assert_close(fin, fin_ref, io, "final_state")
+    assert_close(cs, cs_ref, io, "chunk_states")
+
+
 def test_fwd_raw_dt_matches_prepared_dt():
     # the generator's dt is softplus(dt_raw + dt_bias): both entry points agree
     p = prob(seqlen=1024, nheads=8, chunk_size=256)
