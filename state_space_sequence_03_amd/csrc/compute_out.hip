@@ -440,6 +440,7 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
     arrived[tid] = 0;
     released[tid] = 0;
   }
+  __syncthreads();                                // counters cleared before any wave bumps one
   const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
   const T* xc = x + ((int64_t)b * L + t0) * xstride + (int64_t)h0 * P;
   const T* Bc = Bm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N;
