@@ -238,9 +238,11 @@ def test_inputs_are_seeded_and_shaped():
 
 
 # ------------------------------------------------- step-size preparation pins
+# Each check takes the (softplus, dt_transform) pair so the mutant test can
+# run it against altered copies of oracle/dt.py.
 
-def test_softplus_closed_forms():
-    sp = oracle.softplus
+def check_softplus_closed_forms(sp=None, xf=None):
+    sp = sp or oracle.softplus
     assert abs(sp(0.0) - math.log(2.0)) < 1e-16
     v = np.linspace(-30.0, 30.0, 601)
     # softplus(v) - softplus(-v) = v  (log(1+e^v) - log(1+e^-v) = log e^v)
@@ -254,32 +256,41 @@ def test_softplus_closed_forms():
     assert np.all(sp(v) > 0) and np.all(np.diff(sp(v)) > 0)
 
 
-def test_dt_transform_bias_clamp_and_identity():
+def check_dt_transform_bias_and_clamp(sp=None, xf=None):
+    xf = xf or oracle.dt_transform
     raw = torch.tensor([[[-3.0, 0.0], [2.0, 40.0]]])           # [1, 2, 2]
     bias = torch.tensor([1.0, -0.5])
-    got = oracle.dt_transform(raw, bias, use_softplus=True)
+    got = xf(raw, bias, use_softplus=True)
     v = raw.double().numpy() + bias.double().numpy()
     np.testing.assert_allclose(got, np.log1p(np.exp(np.minimum(v, 30))) + np.maximum(v - 30, 0),
                                rtol=1e-14)
     # without softplus the bias is just added; the clamp bounds from both sides
-    np.testing.assert_array_equal(oracle.dt_transform(raw, bias, use_softplus=False,
-                                                      dt_min=-np.inf), v)
+    np.testing.assert_array_equal(xf(raw, bias, use_softplus=False, dt_min=-np.inf), v)
     # the default lower limit 0 removes negative values
-    assert oracle.dt_transform(raw, bias, use_softplus=False).min() == 0.0
-    cl = oracle.dt_transform(raw, bias, use_softplus=False, dt_min=0.25, dt_max=2.0)
+    assert xf(raw, bias, use_softplus=False).min() == 0.0
+    cl = xf(raw, bias, use_softplus=False, dt_min=0.25, dt_max=2.0)
     np.testing.assert_array_equal(cl, np.clip(v, 0.25, 2.0))
     assert cl.min() == 0.25 and cl.max() == 2.0
     # values inside the limits are fixed points of the clamp
-    inside = oracle.dt_transform(raw, bias, dt_min=1e-9, dt_max=1e9)
-    np.testing.assert_array_equal(inside, got)
+    np.testing.assert_array_equal(xf(raw, bias, dt_min=1e-9, dt_max=1e9), got)
 
 
-def test_dt_transform_reproduces_generated_step_sizes():
+def check_dt_transform_reproduces_generated(sp=None, xf=None):
     # the generator draws dt = softplus(dt_raw + dt_bias) in fp32 (a separate
     # implementation); the fp64 preparation agrees to fp32 rounding
+    xf = xf or oracle.dt_transform
     inp = inputs_of(small_problem(seqlen=200, nheads=6, ngroups=2), seed=21)
-    got = oracle.dt_transform(inp["dt_raw"], inp["dt_bias"], use_softplus=True)
+    got = xf(inp["dt_raw"], inp["dt_bias"], use_softplus=True)
     np.testing.assert_allclose(got, inp["dt"].double().numpy(), rtol=2e-6)
+
+
+DT_PINS = [check_softplus_closed_forms, check_dt_transform_bias_and_clamp,
+           check_dt_transform_reproduces_generated]
+
+
+@pytest.mark.parametrize("pin", DT_PINS, ids=lambda f: f.__name__)
+def test_dt_pin(pin):
+    pin()
 
 
 def test_token_at_a_time_equals_whole_sequence():

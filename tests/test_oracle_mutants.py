@@ -3,7 +3,9 @@
 Each case copies oracle/ssd_oracle.c to a temporary directory, plants one
 mistake with a textual substitution (the committed source is never touched),
 compiles the copy with gcc and runs every pin of test_oracle.py against it.
-At least one pin must fail for every mutant.
+At least one pin must fail for every mutant.  The step-size preparation
+(oracle/dt.py) is treated the same way: a mutated copy of its text is
+executed in a fresh namespace and run against the step-size pins.
 """
 import os
 import subprocess
@@ -11,7 +13,7 @@ import subprocess
 import pytest
 
 import oracle
-from test_oracle import ALL_PINS
+from test_oracle import ALL_PINS, DT_PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
 
@@ -64,3 +66,44 @@ def test_unmodified_copy_passes_all_pins(tmp_path):
     lib = _build_mutant(tmp_path, "identity", "int ssd_oracle_fwd(", "int ssd_oracle_fwd(")
     for pin in ALL_PINS:
         pin(lib=lib)
+
+
+DT_SRC = os.path.join(os.path.dirname(oracle.__file__), "dt.py")
+
+DT_MUTANTS = {
+    "softplus_drops_max": ("return np.maximum(v, 0.0) + np.log1p(np.exp(-np.abs(v)))",
+                           "return np.log1p(np.exp(-np.abs(v)))"),
+    "softplus_exp_sign": ("np.log1p(np.exp(-np.abs(v)))", "np.log1p(np.exp(np.abs(v)))"),
+    "softplus_log_not_log1p": ("np.log1p(np.exp(-np.abs(v)))", "np.log(np.exp(-np.abs(v)))"),
+    "bias_dropped": ("v = v + _f64(dt_bias)[None, None, :]", "v = v"),
+    "bias_subtracted": ("v = v + _f64(dt_bias)[None, None, :]", "v = v - _f64(dt_bias)[None, None, :]"),
+    "clamp_swapped": ("np.minimum(np.maximum(v, dt_min), dt_max)",
+                      "np.maximum(np.minimum(v, dt_min), dt_max)"),
+    "softplus_flag_ignored": ("if use_softplus:", "if True:"),
+}
+
+
+def _dt_mutant(old, new):
+    text = open(DT_SRC).read()
+    assert text.count(old) == 1, "mutation anchor not found: %r" % old
+    ns = {"__name__": "dt_mutant"}
+    exec(compile(text.replace(old, new), "dt_mutant.py", "exec"), ns)
+    return ns["softplus"], ns["dt_transform"]
+
+
+@pytest.mark.parametrize("name", sorted(DT_MUTANTS))
+def test_dt_pins_reject_mutant(name):
+    sp, xf = _dt_mutant(*DT_MUTANTS[name])
+    failed = []
+    for pin in DT_PINS:
+        try:
+            pin(sp=sp, xf=xf)
+        except (AssertionError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, "no step-size pin rejects the mutant %s" % name
+
+
+def test_dt_unmodified_copy_passes():
+    sp, xf = _dt_mutant("def softplus(v):", "def softplus(v):")
+    for pin in DT_PINS:
+        pin(sp=sp, xf=xf)
