@@ -181,7 +181,7 @@ def _workspace(prob, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def _dt_transform(x_like, H, dt_bias, dt_softplus, dt_limit):
+def _dt_transform(H, dt_bias, dt_softplus, dt_limit):
     """ssd_dt_transform for the given options (None when none is asked for)."""
     if dt_bias is None and not dt_softplus and dt_limit is None:
         return None, None
@@ -231,7 +231,7 @@ def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
             _dev(D, "D", torch.float32), _dev(init_state, "init_state", torch.float32),
             _dev(y, "y"), _dev(fin, "final_state", torch.float32), _dev(ws, "workspace"),
             ws_bytes, _stream(x.device))
-    xf, xfp = _dt_transform(x, x.shape[2], dt_bias, dt_softplus, dt_limit)
+    xf, xfp = _dt_transform(x.shape[2], dt_bias, dt_softplus, dt_limit)
     if xf is None:
         st = lib.ssd_fwd(ctypes.byref(prob), *args)
     else:
@@ -272,7 +272,7 @@ def ssd_fwd_states(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
             _dev(init_state, "init_state", torch.float32),
             _dev(fin, "final_state", torch.float32), _dev(cs, "chunk_states"),
             _dev(ws, "workspace"), ws_bytes, _stream(x.device))
-    xf, xfp = _dt_transform(x, H, dt_bias, dt_softplus, dt_limit)
+    xf, xfp = _dt_transform(H, dt_bias, dt_softplus, dt_limit)
     if xf is None:
         st = lib.ssd_fwd_states(ctypes.byref(prob), *args)
     else:
@@ -320,7 +320,7 @@ def ssd_chunk_cumsum(dt: torch.Tensor, A: torch.Tensor, chunk_size: int = 256, *
     dtt = torch.empty_like(G)
     args = (_dev(dt, "dt", torch.float32), _dev(A, "A", torch.float32), _dev(G, "G_out"),
             _dev(dtt, "dt_out"), _stream(dt.device))
-    xf, xfp = _dt_transform(dt, H, dt_bias, dt_softplus, dt_limit)
+    xf, xfp = _dt_transform(H, dt_bias, dt_softplus, dt_limit)
     if xf is None:
         st = lib.ssd_chunk_cumsum(ctypes.byref(prob), *args)
     else:
@@ -359,7 +359,7 @@ def ssd_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Te
     y = out if out is not None else torch.empty_like(x)
     if tuple(y.shape) != tuple(x.shape) or y.dtype != x.dtype:
         raise SsdArgumentError(2, "out must match x")
-    xf, xfp = _dt_transform(x, x.shape[2], dt_bias, dt_softplus, dt_limit)
+    xf, xfp = _dt_transform(x.shape[2], dt_bias, dt_softplus, dt_limit)
     st = lib.ssd_step(ctypes.byref(prob), xfp, _dev(state, "state", torch.float32), _dev(x, "x"),
                       _dev(dt, "dt", torch.float32), _dev(A, "A", torch.float32), _dev(B, "B"),
                       _dev(C, "C"), _dev(D, "D", torch.float32), _dev(y, "y"),
