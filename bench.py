@@ -40,6 +40,7 @@ PEAK_HBM = 8.0e12           # HBM3E bytes/s
 METRIC = "SSD fwd tokens/sec (batch·seqlen) at 1 MI355X; % of bf16 MFMA roofline"
 DECODE_METRIC = "SSD decode tokens/sec (batch, one token per step) at 1 MI355X; % of HBM roofline"
 COPY_PROBE_BYTES = 1 << 30
+DEFAULT_WORKLOAD = "mamba2_2p7b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compute_out_{workload}_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "state_space_sequence_03_amd", "csrc", f)
                   for f in ("compute_out.hip", "ssd_device.hpp")] + \
@@ -163,7 +164,14 @@ def bench_decode(args):
     import ssd_synth
     import state_space_sequence_03_amd as ssd
 
-    name = args.workload if args.workload in DECODE_WORKLOADS else "decode_2p7b_b128"
+    if args.workload in DECODE_WORKLOADS:
+        name = args.workload
+    elif args.workload == DEFAULT_WORKLOAD:
+        name = "decode_2p7b_b128"
+    else:
+        print("unknown decode workload %r (choose from %s)" % (args.workload, ", ".join(DECODE_WORKLOADS)),
+              file=sys.stderr)
+        sys.exit(2)
     prob = ssd_synth.Problem(**DECODE_WORKLOADS[name])
     inputs = ssd_synth.make_inputs(prob, 0)
     dev = torch.device("cuda:0")
@@ -245,7 +253,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mamba2_2p7b")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill")
