@@ -11,13 +11,17 @@
 // chunk's tokens contiguously (devin.kr, section "cuTile 기반 성능 최적화 기법",
 // the transposed dt / decay_cumsum layout).
 //
-// Mapping: one workgroup of 256 threads per (chunk, 16-head tile, batch).
-// The [Q tokens x 16 heads] slab of dt arrives as 16-byte loads (4 heads of
-// one token per lane) and is transposed through LDS to [head][token].  Each
-// wave then scans 4 heads: a lane takes Q/64 consecutive tokens, sums them
-// serially, a wave-wide inclusive scan over the lane totals adds the carry,
-// and the lane writes its tokens' G and dt as one vector store each, so a
-// wave writes a whole row contiguously.
+// Mapping: one workgroup of 256 threads per (chunk, 4-head tile, batch) --
+// small tiles, so that even one batch of a long sequence spreads over many
+// more workgroups than the chip has CUs (the kernel is latency-bound: 16-head
+// tiles left 1.25 workgroups per CU at the 2.7B shape and took 7.8 us against
+// 6.8 us, 11.0 against 7.1 with the step-size preparation).  The [Q tokens x
+// 4 heads] slab of dt arrives as 16-byte loads (the 4 heads of one token per
+// lane) and is transposed through LDS to [head][token].  Each wave then scans
+// one head: a lane takes Q/64 consecutive tokens, sums them serially, a
+// wave-wide inclusive scan over the lane totals adds the carry, and the lane
+// writes its tokens' G and dt as one vector store each, so a wave writes a
+// whole row contiguously.
 //
 // Rows are `ld` floats apart in the outputs; tokens in [L, Lw) are padding
 // (dt = 0, so G holds the chunk's last running sum), which lets the later
@@ -31,7 +35,7 @@
 
 namespace ssd {
 
-constexpr int kCumsumHeads = 16;
+constexpr int kCumsumHeads = 4;
 constexpr int kCumsumThreads = 256;
 
 template <int N>
@@ -55,7 +59,7 @@ chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)c * Q;
 
-  // [Q x 16] slab: lane loads 4 heads of one token (zero outside [0, L) x [0, H))
+  // [Q x 4] slab: lane loads the 4 heads of one token (zero outside [0, L) x [0, H))
   const bool full = h0 + kCumsumHeads <= H && (H % 4) == 0;
 #pragma unroll
   for (int idx = tid; idx < Q * (kCumsumHeads / 4); idx += kCumsumThreads) {
