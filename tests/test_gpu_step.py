@@ -217,3 +217,38 @@ def test_step_raw_dt(io):
     y_ref, fin_ref, _ = oracle_rec(inp, dt=dt_ref)
     assert_close(y, y_ref, io, "y")
     assert_close(state, fin_ref, "fp32", "state")
+
+
+# ------------------------------------------------------------ the bench shapes
+
+def test_decode_bench_shape_sampled():
+    # the decode line's launch configuration: 2.7B-shaped layer, batch 128, one
+    # token from a resident state; sampled (batch, head) pairs against the oracle
+    p = ssd_synth.Problem(batch=128, seqlen=1, nheads=80, headdim=64, dstate=128, ngroups=1,
+                          chunk_size=256, init_std=0.1)
+    inp = ssd_synth.make_inputs(p, seed=0)
+    d = to_dev(inp)
+    state = d["init_state"].clone()
+    y = lib.ssd_step(state, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    torch.cuda.synchronize()
+    heads = [(0, 0), (127, 79), (64, 40), (5, 13), (99, 66)]
+    for (b, h), (y_ref, fin_ref) in oracle.recurrence_heads(inp, heads).items():
+        assert_close(y[b, :, h], y_ref, "bf16", "y[b=%d,h=%d]" % (b, h))
+        assert_close(state[b, h], fin_ref, "fp32", "state[b=%d,h=%d]" % (b, h))
+
+
+def test_raw_dt_2p7b_sampled():
+    # bench --raw-dt's workload: the 2.7B shape with the step size prepared in stage 1
+    p = ssd_synth.CONFIGS["mamba2_2p7b"]
+    inp = ssd_synth.make_inputs(p, seed=ssd_synth.CONFIG_ORDER.index("mamba2_2p7b"))
+    d = to_dev(inp)
+    y, fin = lib.ssd_fwd(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], p.chunk_size,
+                         d["init_state"], dt_bias=d["dt_bias"], dt_softplus=True)
+    torch.cuda.synchronize()
+    prepared = dict(inp)
+    prepared["dt"] = torch.from_numpy(
+        oracle.dt_transform(inp["dt_raw"], inp["dt_bias"], True).astype(np.float32))
+    heads = [(0, 0), (1, 79), (1, 33)]
+    for (b, h), (y_ref, fin_ref) in oracle.recurrence_heads(prepared, heads).items():
+        assert_close(y[b, :, h], y_ref, "bf16", "y[b=%d,h=%d]" % (b, h))
+        assert_close(fin[b, h], fin_ref, "bf16", "final[b=%d,h=%d]" % (b, h))
