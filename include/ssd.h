@@ -52,7 +52,8 @@
  * required pointer is NULL), SSD_ERR_BAD_SHAPE (a size <= 0, nheads not a
  * multiple of ngroups, or a size product overflowing int64), SSD_ERR_BAD_CHUNK
  * (chunk_size not one of 32, 64, 128, 256; ssd_step does not use it),
- * SSD_ERR_BAD_DTYPE, SSD_ERR_BAD_VALUE (an invalid ssd_dt_transform),
+ * SSD_ERR_BAD_DTYPE, SSD_ERR_BAD_VALUE (an invalid ssd_dt_transform or
+ * ssd_config),
  * SSD_ERR_MISALIGNED (a tensor pointer not 16-byte aligned),
  * SSD_ERR_UNSUPPORTED (headdim or dstate not a multiple of 16, or dstate >
  * 256), SSD_ERR_WORKSPACE (workspace too small).  SSD_ERR_HIP reports a failed
@@ -70,7 +71,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
@@ -125,6 +126,26 @@ typedef struct {
   float dt_max;         /* upper clamp */
 } ssd_dt_transform;
 
+/* Tile choices of the forward pass's kernels, for shape tuning.  The pages
+ * tune block sizes and occupancy per shape; here the alternatives are ones
+ * the library compiles, chosen per problem at run time:
+ *   cumsum_heads : heads per chunk_cumsum workgroup, 4 or 16;
+ *   state_heads  : heads per chunk_state workgroup (they share the chunk's B
+ *                  rows), 1, 2 or 4, dividing the heads of a group;
+ *   out_heads    : heads per compute_out workgroup (they share the raw tile
+ *                  C B^T), 1, or 2 for bf16 io, dstate <= 128 and an even
+ *                  number of heads per group (two heads' accumulators do not
+ *                  fit the registers otherwise).
+ * Every choice computes the same result up to floating-point summation order.
+ * ssd_default_config gives the static table the plain entry points use;
+ * ssd_tune measures the alternatives. */
+typedef struct {
+  int32_t cumsum_heads;
+  int32_t state_heads;
+  int32_t out_heads;
+  int32_t reserved;     /* must be 0 */
+} ssd_config;
+
 /* ABI version of the loaded library (SSD_ABI_VERSION at build time). */
 int ssd_abi_version(void);
 
@@ -167,6 +188,46 @@ ssd_status ssd_fwd_ex(const ssd_problem* prob, const ssd_dt_transform* dtx, cons
                       const float* dt, const float* A, const void* B, const void* C,
                       const float* D, const float* init_state, void* y, float* final_state,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* The tile choices ssd_fwd makes for `prob` (the static table).
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_CHUNK, BAD_DTYPE, UNSUPPORTED. */
+ssd_status ssd_default_config(const ssd_problem* prob, ssd_config* cfg);
+
+/* ssd_fwd_ex with the kernels' tile choices given (cfg = NULL: the default,
+ * making this exactly ssd_fwd_ex).  An invalid choice is SSD_ERR_BAD_VALUE
+ * (checked with the transform, before alignment).  Same workspace,
+ * arguments, outputs and other errors as ssd_fwd. */
+ssd_status ssd_fwd_config(const ssd_problem* prob, const ssd_config* cfg,
+                          const ssd_dt_transform* dtx, const void* x, const float* dt,
+                          const float* A, const void* B, const void* C, const float* D,
+                          const float* init_state, void* y, float* final_state, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Shape tuning: runs the whole forward pass (as ssd_fwd_config, on the
+ * caller's inputs and buffers) with every valid tile choice for `prob`, once
+ * untimed and then `reps` times between two HIP events on `stream`, and
+ * reports the mean time of each and the fastest choice.  Unlike every other
+ * entry point this one SYNCHRONISES with `stream` (once per choice), creates
+ * and destroys two HIP events, and is meant to run once per shape, outside
+ * any timed or captured region.  On return y and final_state hold the result
+ * of the last run, init_state must not alias final_state (each run reads it),
+ * and `workspace` is as for ssd_fwd.
+ *   reps      : timed runs per choice, 1 .. 1000;
+ *   tried, tried_ms : arrays of max_tried entries receiving the choices in
+ *               the order measured and their mean ms (may be NULL when
+ *               max_tried is 0);
+ *   n_tried   : receives the number of choices measured (all valid ones,
+ *               even beyond max_tried);
+ *   best, best_ms : the fastest choice and its mean ms (best_ms may be NULL).
+ * Errors as for ssd_fwd_ex; SSD_ERR_BAD_VALUE for reps or max_tried out of
+ * range or init_state aliasing final_state; SSD_ERR_HIP if an event or
+ * launch fails. */
+ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                    const float* dt, const float* A, const void* B, const void* C, const float* D,
+                    const float* init_state, void* y, float* final_state, void* workspace,
+                    size_t workspace_bytes, void* stream, int32_t reps, ssd_config* tried,
+                    float* tried_ms, int32_t max_tried, int32_t* n_tried, ssd_config* best,
+                    float* best_ms);
 
 /* Stage 1 alone (the chunk_cumsum step): for every (b, h) and token t in chunk
  * c = t / Q,

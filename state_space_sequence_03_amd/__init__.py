@@ -8,8 +8,9 @@ if ``libssd.so`` is missing or the tensors are not on a GPU.
 
 Names match the C ABI in include/ssd.h:
     ssd_fwd, ssd_fwd_ex, ssd_fwd_states, ssd_fwd_states_ex, ssd_compute_out, ssd_chunk_cumsum,
-    ssd_chunk_cumsum_ex, ssd_step, ssd_fwd_workspace_size, ssd_status_string,
-    ssd_last_error_message, ssd_abi_version
+    ssd_chunk_cumsum_ex, ssd_step, ssd_default_config, ssd_tune, ssd_fwd_workspace_size,
+    ssd_status_string, ssd_last_error_message, ssd_abi_version
+(ssd_fwd_config is reached through ssd_fwd(..., config=...).)
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ __all__ = ["SsdError", "SsdArgumentError", "lib_path", "load_library", "make_pro
            "ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
            "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_states", "ssd_compute_out",
            "ssd_chunk_cumsum", "ssd_fwd_ex", "ssd_fwd_states_ex", "ssd_chunk_cumsum_ex",
-           "ssd_step",
+           "ssd_step", "ssd_default_config", "ssd_tune",
            "SSD_F32", "SSD_BF16"]
 
 SSD_F32, SSD_BF16 = 0, 1
@@ -66,6 +67,21 @@ class ssd_dt_transform(ctypes.Structure):
                 ("dt_max", ctypes.c_float)]
 
 
+class ssd_config(ctypes.Structure):
+    _fields_ = [("cumsum_heads", ctypes.c_int32), ("state_heads", ctypes.c_int32),
+                ("out_heads", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {"cumsum_heads": self.cumsum_heads, "state_heads": self.state_heads,
+                "out_heads": self.out_heads}
+
+
+def _config_of(cfg) -> Optional["ssd_config"]:
+    if cfg is None or isinstance(cfg, ssd_config):
+        return cfg
+    return ssd_config(int(cfg["cumsum_heads"]), int(cfg["state_heads"]), int(cfg["out_heads"]), 0)
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -105,6 +121,14 @@ def load_library():
         lib.ssd_chunk_cumsum_ex.argtypes = [P, X] + [vp] * 5
         lib.ssd_step.restype = ctypes.c_int
         lib.ssd_step.argtypes = [P, X] + [vp] * 9
+        CF = ctypes.POINTER(ssd_config)
+        lib.ssd_default_config.restype = ctypes.c_int
+        lib.ssd_default_config.argtypes = [P, CF]
+        lib.ssd_fwd_config.restype = ctypes.c_int
+        lib.ssd_fwd_config.argtypes = [P, CF, X] + [vp] * 10 + [sz, vp]
+        i32, pi32, pf = ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)
+        lib.ssd_tune.restype = ctypes.c_int
+        lib.ssd_tune.argtypes = [P, X] + [vp] * 10 + [sz, vp, i32, CF, pf, i32, pi32, CF, pf]
         _lib = lib
         return lib
 
@@ -198,13 +222,15 @@ def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
             init_state: Optional[torch.Tensor] = None, *, want_final_state: bool = True,
             out: Optional[torch.Tensor] = None, final_out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
-            dt_softplus: bool = False,
-            dt_limit: Optional[Tuple[float, float]] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            dt_softplus: bool = False, dt_limit: Optional[Tuple[float, float]] = None,
+            config=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Full forward pass on the current stream.  Returns (y, final_state).
 
     With dt_bias, dt_softplus or dt_limit given, ``dt`` is the raw step size and
     is prepared inside the first stage as clamp(softplus(dt + dt_bias)) (the C
-    entry point ssd_fwd_ex); otherwise ``dt`` is used as given (ssd_fwd)."""
+    entry point ssd_fwd_ex); otherwise ``dt`` is used as given (ssd_fwd).
+    ``config`` (a dict with cumsum_heads, state_heads, out_heads, or an
+    ssd_config) selects the kernels' tile choices (ssd_fwd_config)."""
     lib = load_library()
     prob = _problem_of(x, B, chunk_size)
     if x.dtype != B.dtype or x.dtype != C.dtype:
@@ -232,12 +258,51 @@ def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
             _dev(y, "y"), _dev(fin, "final_state", torch.float32), _dev(ws, "workspace"),
             ws_bytes, _stream(x.device))
     xf, xfp = _dt_transform(x.shape[2], dt_bias, dt_softplus, dt_limit)
-    if xf is None:
+    cfg = _config_of(config)
+    if cfg is not None:
+        st = lib.ssd_fwd_config(ctypes.byref(prob), ctypes.byref(cfg), xfp, *args)
+    elif xf is None:
         st = lib.ssd_fwd(ctypes.byref(prob), *args)
     else:
         st = lib.ssd_fwd_ex(ctypes.byref(prob), xfp, *args)
     _check(st)
     return y, fin
+
+
+def ssd_default_config(prob) -> dict:
+    """The tile choices ssd_fwd makes for an ssd_problem (make_problem)."""
+    c = ssd_config()
+    _check(load_library().ssd_default_config(ctypes.byref(prob), ctypes.byref(c)))
+    return c.as_dict()
+
+
+def ssd_tune(x, dt, A, B, C, D=None, chunk_size=256, init_state=None, *, reps: int = 5,
+             dt_bias=None, dt_softplus=False, dt_limit=None, workspace=None):
+    """Time the forward pass with every valid tile choice (synchronises the
+    current stream).  Returns (best config dict, best mean ms,
+    [(config dict, mean ms), ...] in the order measured)."""
+    lib = load_library()
+    prob = _problem_of(x, B, chunk_size)
+    state_shape = (x.shape[0], x.shape[2], x.shape[3], B.shape[3])
+    y = torch.empty_like(x)
+    fin = torch.empty(state_shape, dtype=torch.float32, device=x.device)
+    ws, ws_bytes = _workspace(prob, x.device, workspace)
+    xf, xfp = _dt_transform(x.shape[2], dt_bias, dt_softplus, dt_limit)
+    cap = 32
+    tried = (ssd_config * cap)()
+    tried_ms = (ctypes.c_float * cap)()
+    n = ctypes.c_int32(0)
+    best = ssd_config()
+    best_ms = ctypes.c_float(0.0)
+    st = lib.ssd_tune(ctypes.byref(prob), xfp, _dev(x, "x"), _dev(dt, "dt", torch.float32),
+                      _dev(A, "A", torch.float32), _dev(B, "B"), _dev(C, "C"),
+                      _dev(D, "D", torch.float32), _dev(init_state, "init_state", torch.float32),
+                      _dev(y, "y"), _dev(fin, "final_state", torch.float32), _dev(ws, "workspace"),
+                      ws_bytes, _stream(x.device), int(reps), tried, tried_ms, cap,
+                      ctypes.byref(n), ctypes.byref(best), ctypes.byref(best_ms))
+    _check(st)
+    rows = [(tried[i].as_dict(), float(tried_ms[i])) for i in range(min(n.value, cap))]
+    return best.as_dict(), float(best_ms.value), rows
 
 
 def ssd_fwd_ex(x, dt, A, B, C, D=None, chunk_size=256, init_state=None, *, dt_bias=None,

@@ -11,14 +11,15 @@
 // chunk's tokens contiguously (devin.kr, section "cuTile 기반 성능 최적화 기법",
 // the transposed dt / decay_cumsum layout).
 //
-// Mapping: one workgroup of 256 threads per (chunk, 4-head tile, batch) --
-// small tiles, so that even one batch of a long sequence spreads over many
-// more workgroups than the chip has CUs (the kernel is latency-bound: 16-head
-// tiles left 1.25 workgroups per CU at the 2.7B shape and took 7.8 us against
-// 6.8 us, 11.0 against 7.1 with the step-size preparation).  The [Q tokens x
-// 4 heads] slab of dt arrives as 16-byte loads (the 4 heads of one token per
-// lane) and is transposed through LDS to [head][token].  Each wave then scans
-// one head: a lane takes Q/64 consecutive tokens, sums them serially, a
+// Mapping: one workgroup of 256 threads per (chunk, HT-head tile, batch), HT
+// = 4 by default -- small tiles, so that even one batch of a long sequence
+// spreads over many more workgroups than the chip has CUs (the kernel is
+// latency-bound: 16-head tiles left 1.25 workgroups per CU at the 2.7B shape
+// and took 7.8 us against 6.8 us, 11.0 against 7.1 with the step-size
+// preparation); HT = 16 is kept as a tuning alternative.  The [Q tokens x HT
+// heads] slab of dt arrives as 16-byte loads (4 heads of one token per lane)
+// and is transposed through LDS to [head][token].  Each wave then scans HT/4
+// heads: a lane takes Q/64 consecutive tokens, sums them serially, a
 // wave-wide inclusive scan over the lane totals adds the carry, and the lane
 // writes its tokens' G and dt as one vector store each, so a wave writes a
 // whole row contiguously.
@@ -35,7 +36,6 @@
 
 namespace ssd {
 
-constexpr int kCumsumHeads = 4;
 constexpr int kCumsumThreads = 256;
 
 template <int N>
@@ -44,7 +44,7 @@ template <> struct FloatVec<1> { typedef float type; };
 template <> struct FloatVec<2> { typedef float type __attribute__((ext_vector_type(2))); };
 template <> struct FloatVec<4> { typedef float type __attribute__((ext_vector_type(4))); };
 
-template <int Q, bool XF>
+template <int Q, bool XF, int HT>
 __global__ void __launch_bounds__(kCumsumThreads)
 chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
                     float* __restrict__ G, float* __restrict__ dtT,
@@ -52,18 +52,18 @@ chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
   constexpr int TPL = Q >= kWave ? Q / kWave : 1;       // tokens per lane
   constexpr int LANES = Q / TPL;                         // lanes holding tokens
   typedef typename FloatVec<TPL>::type vec_t;
-  __shared__ __align__(16) float tile[kCumsumHeads][Q + 4];
+  __shared__ __align__(16) float tile[HT][Q + 4];
   const int c = blockIdx.x;
-  const int h0 = blockIdx.y * kCumsumHeads;
+  const int h0 = blockIdx.y * HT;
   const int64_t b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)c * Q;
 
-  // [Q x 4] slab: lane loads the 4 heads of one token (zero outside [0, L) x [0, H))
-  const bool full = h0 + kCumsumHeads <= H && (H % 4) == 0;
+  // [Q x HT] slab: lane loads 4 heads of one token (zero outside [0, L) x [0, H))
+  const bool full = h0 + HT <= H && (H % 4) == 0;
 #pragma unroll
-  for (int idx = tid; idx < Q * (kCumsumHeads / 4); idx += kCumsumThreads) {
-    const int t = idx / (kCumsumHeads / 4), h4 = (idx % (kCumsumHeads / 4)) * 4;
+  for (int idx = tid; idx < Q * (HT / 4); idx += kCumsumThreads) {
+    const int t = idx / (HT / 4), h4 = (idx % (HT / 4)) * 4;
     const int64_t tok = t0 + t;
     floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
     if (tok < L) {
@@ -89,7 +89,7 @@ chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
   const int first = lane * TPL;                         // first token of this lane
   const bool vec_ok = ld % TPL == 0;                    // vector stores stay aligned
 #pragma unroll
-  for (int k = 0; k < kCumsumHeads / (kCumsumThreads / kWave); ++k) {
+  for (int k = 0; k < HT / (kCumsumThreads / kWave); ++k) {
     const int hh = wave + k * (kCumsumThreads / kWave);
     const int h = h0 + hh;
     if (h >= H) break;
@@ -137,30 +137,42 @@ chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
   }
 }
 
-template <int Q>
-static void launch_q(dim3 grid, const float* dt, const float* A, float* G, float* dtT, int64_t L,
-                     int H, int64_t ld, int64_t Lw, const DtXform* xf, hipStream_t stream) {
+template <int Q, int HT>
+static void launch_q(int64_t T, int64_t batch, const float* dt, const float* A, float* G,
+                     float* dtT, int64_t L, int H, int64_t ld, int64_t Lw, const DtXform* xf,
+                     hipStream_t stream) {
+  dim3 grid((unsigned)T, (unsigned)((H + HT - 1) / HT), (unsigned)batch);
   if (xf)
-    hipLaunchKernelGGL((chunk_cumsum_kernel<Q, true>), grid, dim3(kCumsumThreads), 0, stream, dt,
-                       A, G, dtT, L, H, ld, Lw, *xf);
+    hipLaunchKernelGGL((chunk_cumsum_kernel<Q, true, HT>), grid, dim3(kCumsumThreads), 0, stream,
+                       dt, A, G, dtT, L, H, ld, Lw, *xf);
   else
-    hipLaunchKernelGGL((chunk_cumsum_kernel<Q, false>), grid, dim3(kCumsumThreads), 0, stream, dt,
-                       A, G, dtT, L, H, ld, Lw, DtXform{nullptr, 0, 0.0f, 0.0f});
+    hipLaunchKernelGGL((chunk_cumsum_kernel<Q, false, HT>), grid, dim3(kCumsumThreads), 0, stream,
+                       dt, A, G, dtT, L, H, ld, Lw, DtXform{nullptr, 0, 0.0f, 0.0f});
+}
+
+template <int HT>
+static void launch_ht(int Q, int64_t T, int64_t batch, const float* dt, const float* A, float* G,
+                      float* dtT, int64_t L, int H, int64_t ld, int64_t Lw, const DtXform* xf,
+                      hipStream_t stream) {
+  switch (Q) {
+    case 32: launch_q<32, HT>(T, batch, dt, A, G, dtT, L, H, ld, Lw, xf, stream); break;
+    case 64: launch_q<64, HT>(T, batch, dt, A, G, dtT, L, H, ld, Lw, xf, stream); break;
+    case 128: launch_q<128, HT>(T, batch, dt, A, G, dtT, L, H, ld, Lw, xf, stream); break;
+    default: launch_q<256, HT>(T, batch, dt, A, G, dtT, L, H, ld, Lw, xf, stream); break;
+  }
 }
 
 // Host launcher.  Q in {32, 64, 128, 256}; grid covers ceil(Lw / Q) chunks;
-// rows of G and dtT are `ld` floats apart; xf = nullptr: dt used as given.
+// rows of G and dtT are `ld` floats apart; xf = nullptr: dt used as given;
+// heads_tile (4 or 16) is the number of heads per workgroup.
 hipError_t launch_chunk_cumsum(const float* dt, const float* A, float* G, float* dtT,
                                int64_t batch, int64_t L, int64_t H, int Q, int64_t ld,
-                               int64_t Lw, const DtXform* xf, hipStream_t stream) {
+                               int64_t Lw, const DtXform* xf, int heads_tile, hipStream_t stream) {
   const int64_t T = (Lw + Q - 1) / Q;
-  dim3 grid((unsigned)T, (unsigned)((H + kCumsumHeads - 1) / kCumsumHeads), (unsigned)batch);
-  switch (Q) {
-    case 32: launch_q<32>(grid, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream); break;
-    case 64: launch_q<64>(grid, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream); break;
-    case 128: launch_q<128>(grid, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream); break;
-    default: launch_q<256>(grid, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream); break;
-  }
+  if (heads_tile == 16)
+    launch_ht<16>(Q, T, batch, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream);
+  else
+    launch_ht<4>(Q, T, batch, dt, A, G, dtT, L, (int)H, ld, Lw, xf, stream);
   return hipGetLastError();
 }
 

@@ -326,11 +326,12 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
   }
 }
 
-// heads per workgroup: 4 (or 2, or 1) heads of one group share the B rows
-// (2 heads, 2560 workgroups in five full rounds with a 4-slot ring, measured
-// 71.8 us against 68.4 us at the 2.7B shape: the smaller tail does not pay
-// for reading each chunk's B rows twice as often)
-static int cs_kh(int64_t H, int64_t G) {
+// Default heads per workgroup: 4 (or 2, or 1) heads of one group share the B
+// rows (2 heads, 2560 workgroups in five full rounds with a 4-slot ring,
+// measured 71.8 us against 68.4 us at the 2.7B shape: the smaller tail does
+// not pay for reading each chunk's B rows twice as often).  Any count that
+// divides the heads of a group is valid.
+int chunk_state_default_kh(int64_t H, int64_t G) {
   const int64_t hg = H / G;
   return SSD_CS_KH >= 4 && hg % 4 == 0 ? 4 : hg % 2 == 0 ? 2 : 1;
 }
@@ -376,12 +377,12 @@ static hipError_t launch_cs_nw(const void* x, const void* Bm, const float* Gw, c
 }
 
 template <typename T>
-static hipError_t launch_cs_t(const void* x, const void* Bm, const float* Gw, const float* dtw,
-                              void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                              int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
-                              hipStream_t stream) {
+static hipError_t launch_cs_t(int kh, const void* x, const void* Bm, const float* Gw,
+                              const float* dtw, void* S, int64_t batch, int64_t L, int64_t H,
+                              int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
+                              int frag_major, hipStream_t stream) {
 #define SSD_CS_ARGS x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, stream
-  switch (cs_kh(H, G)) {
+  switch (kh) {
     case 4: return launch_cs_nw<T, 4>(SSD_CS_ARGS);
     case 2: return launch_cs_nw<T, 2>(SSD_CS_ARGS);
     default: return launch_cs_nw<T, 1>(SSD_CS_ARGS);
@@ -389,13 +390,17 @@ static hipError_t launch_cs_t(const void* x, const void* Bm, const float* Gw, co
 #undef SSD_CS_ARGS
 }
 
+// kh: heads per workgroup (1, 2 or 4, dividing the heads of a group; checked
+// by the caller).
 hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, const float* Gw,
                               const float* dtw, void* S, int64_t batch, int64_t L, int64_t H,
                               int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                              int frag_major, hipStream_t stream) {
+                              int frag_major, int kh, hipStream_t stream) {
   if (io_bf16)
-    return launch_cs_t<bf16>(x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, stream);
-  return launch_cs_t<float>(x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, stream);
+    return launch_cs_t<bf16>(kh, x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major,
+                             stream);
+  return launch_cs_t<float>(kh, x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major,
+                            stream);
 }
 
 }  // namespace ssd

@@ -727,12 +727,17 @@ static hipError_t launch_out(const void* x, const void* Bm, const void* Cm, cons
 
 // heads per workgroup: two heads of one group share the tile C B^T when the
 // group has an even head count and the accumulators of both fit in registers
-// next to 2 waves per SIMD (bf16, dstate <= 128); one head otherwise
+// next to 2 waves per SIMD (bf16, dstate <= 128); one head otherwise.  Both
+// are valid where two are (the caller may choose one).
+int compute_out_kh_valid(int io_bf16, int64_t H, int64_t G, int64_t N, int kh) {
+  if (kh == 1) return 1;
+  return kh == 2 && io_bf16 && nk_class(N) <= 4 && (H / G) % 2 == 0;
+}
 #ifndef SSD_OUT_MAX_KH
 #define SSD_OUT_MAX_KH 2
 #endif
-static int kh_class(int io_bf16, int64_t H, int64_t G, int64_t N) {
-  return (SSD_OUT_MAX_KH >= 2 && io_bf16 && nk_class(N) <= 4 && (H / G) % 2 == 0) ? 2 : 1;
+int compute_out_default_kh(int io_bf16, int64_t H, int64_t G, int64_t N) {
+  return (SSD_OUT_MAX_KH >= 2 && compute_out_kh_valid(io_bf16, H, G, N, 2)) ? 2 : 1;
 }
 
 template <typename T, int IB, int KH>
@@ -751,12 +756,12 @@ static hipError_t launch_out_nk(int NK, const void* x, const void* Bm, const voi
 }
 
 template <typename T>
-static hipError_t launch_out_t(const void* x, const void* Bm, const void* Cm, const float* Gw,
+static hipError_t launch_out_t(int kh, const void* x, const void* Bm, const void* Cm, const float* Gw,
                                const float* dtw, const void* Hc, const float* Dv, void* y, int* flag,
                                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                                int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
 #define SSD_OUT_ARGS nk_class(N), x, Bm, Cm, Gw, dtw, Hc, Dv, y, flag, batch, L, H, P, N, G, Q, T_, ldw, stream
-  const bool two = kh_class(sizeof(T) == 2, H, G, N) == 2;
+  const bool two = kh == 2;
   if (Q >= 128) return two ? launch_out_nk<T, 2, 2>(SSD_OUT_ARGS) : launch_out_nk<T, 2, 1>(SSD_OUT_ARGS);
   return two ? launch_out_nk<T, 1, 2>(SSD_OUT_ARGS) : launch_out_nk<T, 1, 1>(SSD_OUT_ARGS);
 #undef SSD_OUT_ARGS
@@ -774,8 +779,8 @@ static int smem_bytes_t(int Q, int NK, int KH) {
 #undef SSD_LAY
 }
 
-int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int64_t H, int64_t G) {
-  const int NK = nk_class(N), KH = kh_class(io_bf16, H, G, N);
+int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int kh) {
+  const int NK = nk_class(N), KH = kh;
   return kOutStaticLds + (io_bf16 ? smem_bytes_t<bf16>(Q, NK, KH) : smem_bytes_t<float>(Q, NK, KH));
 }
 
@@ -783,10 +788,10 @@ hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const 
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
                               void* y, void* sink, int64_t batch, int64_t L, int64_t H,
                               int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                              hipStream_t stream) {
+                              int kh, hipStream_t stream) {
   if (io_bf16)
-    return launch_out_t<bf16>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, static_cast<int*>(sink), batch, L, H, P, N, G, Q, T_, ldw, stream);
-  return launch_out_t<float>(x, Bm, Cm, Gw, dtw, Hc, Dv, y, static_cast<int*>(sink), batch, L, H, P, N, G, Q, T_, ldw, stream);
+    return launch_out_t<bf16>(kh, x, Bm, Cm, Gw, dtw, Hc, Dv, y, static_cast<int*>(sink), batch, L, H, P, N, G, Q, T_, ldw, stream);
+  return launch_out_t<float>(kh, x, Bm, Cm, Gw, dtw, Hc, Dv, y, static_cast<int*>(sink), batch, L, H, P, N, G, Q, T_, ldw, stream);
 }
 
 }  // namespace ssd

@@ -19,7 +19,7 @@
 namespace ssd {
 hipError_t launch_chunk_cumsum(const float* dt, const float* A, float* G, float* dtT,
                                int64_t batch, int64_t L, int64_t H, int Q, int64_t ld,
-                               int64_t Lw, const DtXform* xf, hipStream_t stream);
+                               int64_t Lw, const DtXform* xf, int heads_tile, hipStream_t stream);
 hipError_t launch_step(int io_bf16, float* state, const void* x, const float* dt, const float* A,
                        const void* Bm, const void* Cm, const float* D, void* y,
                        const DtXform* xf, int64_t batch, int64_t L, int64_t H, int64_t P,
@@ -27,7 +27,7 @@ hipError_t launch_step(int io_bf16, float* state, const void* x, const float* dt
 hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, const float* Gw,
                               const float* dtw, void* S, int64_t batch, int64_t L, int64_t H,
                               int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                              int frag_major, hipStream_t stream);
+                              int frag_major, int kh, hipStream_t stream);
 hipError_t launch_state_pass(int io_bf16, void* S, const float* Gw, const float* init_state,
                              float* final_state, int64_t batch, int64_t H, int64_t P, int64_t N,
                              int Q, int64_t T_, int64_t ldw, int frag_major, hipStream_t stream);
@@ -35,8 +35,11 @@ hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const 
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
                               void* y, void* sink, int64_t batch, int64_t L, int64_t H, int64_t P,
                               int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                              hipStream_t stream);
-int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int64_t H, int64_t G);
+                              int kh, hipStream_t stream);
+int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int kh);
+int compute_out_kh_valid(int io_bf16, int64_t H, int64_t G, int64_t N, int kh);
+int compute_out_default_kh(int io_bf16, int64_t H, int64_t G, int64_t N);
+int chunk_state_default_kh(int64_t H, int64_t G);
 }  // namespace ssd
 
 namespace {
@@ -129,8 +132,35 @@ ssd_status check_dt_transform(const ssd_dt_transform* dtx, ssd::DtXform* xf) {
   return SSD_OK;
 }
 
+// The kernels' tile choices (ssd_config): the static table, and the checks a
+// caller's choice must pass.
+ssd_config default_config(const Plan& pl) {
+  ssd_config c;
+  c.cumsum_heads = 4;
+  c.state_heads = ssd::chunk_state_default_kh(pl.H, pl.G);
+  c.out_heads = ssd::compute_out_default_kh(pl.bf16, pl.H, pl.G, pl.N);
+  c.reserved = 0;
+  return c;
+}
+
+ssd_status check_config(const Plan& pl, const ssd_config& c) {
+  if (c.reserved != 0) return fail(SSD_ERR_BAD_VALUE, "config: reserved field must be 0");
+  if (c.cumsum_heads != 4 && c.cumsum_heads != 16)
+    return fail(SSD_ERR_BAD_VALUE, "config: cumsum_heads must be 4 or 16 (got %d)", c.cumsum_heads);
+  const int64_t hg = pl.H / pl.G;
+  if (!(c.state_heads == 1 || c.state_heads == 2 || c.state_heads == 4) || hg % c.state_heads != 0)
+    return fail(SSD_ERR_BAD_VALUE,
+                "config: state_heads must be 1, 2 or 4 and divide the %lld heads of a group (got %d)",
+                (long long)hg, c.state_heads);
+  if (!ssd::compute_out_kh_valid(pl.bf16, pl.H, pl.G, pl.N, c.out_heads))
+    return fail(SSD_ERR_BAD_VALUE,
+                "config: out_heads must be 1, or 2 for bf16 io, dstate <= 128 and an even number "
+                "of heads per group (got %d)", c.out_heads);
+  return SSD_OK;
+}
+
 // Limits of the kernels (checked after alignment, as the header documents).
-ssd_status check_supported(const Plan& pl) {
+ssd_status check_supported(const Plan& pl, int out_heads = 0) {
   if (pl.P % 16 != 0 || pl.N % 16 != 0)
     return fail(SSD_ERR_UNSUPPORTED, "headdim (%lld) and dstate (%lld) must be multiples of 16",
                 (long long)pl.P, (long long)pl.N);
@@ -138,7 +168,8 @@ ssd_status check_supported(const Plan& pl) {
   if (pl.B * pl.H > INT32_MAX / 64 || pl.B * pl.T > INT32_MAX / 64 || pl.H > 65535 ||
       pl.B > 65535 || pl.T > INT32_MAX / 8)
     return fail(SSD_ERR_UNSUPPORTED, "grid too large for this build");
-  if (ssd::compute_out_smem_bytes(pl.bf16, (int)pl.Q, pl.N, pl.H, pl.G) > kMaxLds)
+  const int okh = out_heads ? out_heads : ssd::compute_out_default_kh(pl.bf16, pl.H, pl.G, pl.N);
+  if (ssd::compute_out_smem_bytes(pl.bf16, (int)pl.Q, pl.N, okh) > kMaxLds)
     return fail(SSD_ERR_UNSUPPORTED, "fp32 io with chunk_size %lld and dstate %lld exceeds LDS",
                 (long long)pl.Q, (long long)pl.N);
   return SSD_OK;
@@ -224,7 +255,8 @@ ssd_status ssd_chunk_cumsum_ex(const ssd_problem* prob, const ssd_dt_transform* 
     if (st != SSD_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(ssd::launch_chunk_cumsum(dt, A, G_out, dt_out, pl.B, pl.L, pl.H, (int)pl.Q,
-                                               pl.L, pl.L, dtx ? &xf : nullptr, s),
+                                               pl.L, pl.L, dtx ? &xf : nullptr,
+                                               default_config(pl).cumsum_heads, s),
                       "chunk_cumsum launch");
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
@@ -236,22 +268,22 @@ ssd_status ssd_chunk_cumsum(const ssd_problem* prob, const float* dt, const floa
   return ssd_chunk_cumsum_ex(prob, nullptr, dt, A, G_out, dt_out, stream);
 }
 
-static ssd_status run_states(const Plan& pl, const void* x, const float* dt, const float* A,
-                             const void* B, const float* init_state, float* final_state,
-                             void* chunk_states, void* workspace, const ssd::DtXform* xf,
-                             hipStream_t s) {
+static ssd_status run_states(const Plan& pl, const ssd_config& cfg, const void* x, const float* dt,
+                             const float* A, const void* B, const float* init_state,
+                             float* final_state, void* chunk_states, void* workspace,
+                             const ssd::DtXform* xf, hipStream_t s) {
   char* ws = static_cast<char*>(workspace);
   float* Gw = reinterpret_cast<float*>(ws + pl.g_off);
   float* dtw = reinterpret_cast<float*>(ws + pl.dt_off);
   void* Hc = chunk_states ? chunk_states : static_cast<void*>(ws + pl.hc_off);
   hipError_t e = ssd::launch_chunk_cumsum(dt, A, Gw, dtw, pl.B, pl.L, pl.H, (int)pl.Q, pl.Lp,
-                                          pl.Lp, xf, s);
+                                          pl.Lp, xf, cfg.cumsum_heads, s);
   if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
   // each chunk's own contribution S_c into the state buffer, then the
   // recurrence turns it, in place, into the chunk-start states H_c
   const int frag_major = chunk_states ? 0 : 1;
   e = ssd::launch_chunk_state(pl.bf16, x, B, Gw, dtw, Hc, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
-                              (int)pl.Q, pl.T, pl.Lp, frag_major, s);
+                              (int)pl.Q, pl.T, pl.Lp, frag_major, cfg.state_heads, s);
   if (e != hipSuccess) return hip_status(e, "chunk_state launch");
   e = ssd::launch_state_pass(pl.bf16, Hc, Gw, init_state, final_state, pl.B, pl.H, pl.P, pl.N,
                              (int)pl.Q, pl.T, pl.Lp, frag_major, s);
@@ -281,8 +313,8 @@ ssd_status ssd_fwd_states_ex(const ssd_problem* prob, const ssd_dt_transform* dt
     workspace_plan(&pl);
     if (workspace_bytes < pl.bytes)
       return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
-    return run_states(pl, x, dt, A, B, init_state, final_state, chunk_states, workspace,
-                      dtx ? &xf : nullptr, static_cast<hipStream_t>(stream));
+    return run_states(pl, default_config(pl), x, dt, A, B, init_state, final_state, chunk_states,
+                      workspace, dtx ? &xf : nullptr, static_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
   }
@@ -296,15 +328,17 @@ ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* d
                            workspace, workspace_bytes, stream);
 }
 
-static ssd_status run_out(const Plan& pl, const void* x, const void* B, const void* C,
-                          const float* D, void* y, const void* workspace, hipStream_t s) {
+static ssd_status run_out(const Plan& pl, const ssd_config& cfg, const void* x, const void* B,
+                          const void* C, const float* D, void* y, const void* workspace,
+                          hipStream_t s) {
   const char* ws = static_cast<const char*>(workspace);
   const float* Gw = reinterpret_cast<const float*>(ws + pl.g_off);
   const float* dtw = reinterpret_cast<const float*>(ws + pl.dt_off);
   const void* Hc = ws + pl.hc_off;
   void* sink = const_cast<char*>(ws) + pl.sink_off;
   return hip_status(ssd::launch_compute_out(pl.bf16, x, B, C, Gw, dtw, Hc, D, y, sink, pl.B, pl.L,
-                                            pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp, s),
+                                            pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp,
+                                            cfg.out_heads, s),
                     "compute_out launch");
 }
 
@@ -325,7 +359,66 @@ ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B
     workspace_plan(&pl);
     if (workspace_bytes < pl.bytes)
       return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
-    return run_out(pl, x, B, C, D, y, workspace, static_cast<hipStream_t>(stream));
+    return run_out(pl, default_config(pl), x, B, C, D, y, workspace,
+                   static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+// Validation shared by the forward entry points (NULL / shape / chunk / dtype,
+// then the transform and the config values, alignment, limits, workspace).
+static ssd_status check_fwd(const ssd_problem* prob, const ssd_config* cfg,
+                            const ssd_dt_transform* dtx, const void* x, const float* dt,
+                            const float* A, const void* B, const void* C, const float* D,
+                            const float* init_state, void* y, float* final_state,
+                            void* workspace, size_t workspace_bytes, Plan* pl, ssd_config* use,
+                            ssd::DtXform* xf) {
+  if (!prob || !x || !dt || !A || !B || !C || !y || !workspace)
+    return fail(SSD_ERR_NULL_POINTER, "prob, x, dt, A, B, C, y and workspace must not be NULL");
+  ssd_status st = plan_problem(prob, pl);
+  if (st != SSD_OK) return st;
+  st = check_dt_transform(dtx, xf);
+  if (st != SSD_OK) return st;
+  *use = cfg ? *cfg : default_config(*pl);
+  st = check_config(*pl, *use);
+  if (st != SSD_OK) return st;
+  if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
+      !aligned16(D) || !aligned16(init_state) || !aligned16(y) || !aligned16(final_state) ||
+      !aligned16(workspace) || (dtx && !aligned16(dtx->dt_bias)))
+    return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
+  st = check_supported(*pl, use->out_heads);
+  if (st != SSD_OK) return st;
+  workspace_plan(pl);
+  if (workspace_bytes < pl->bytes)
+    return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl->bytes);
+  return SSD_OK;
+}
+
+static ssd_status run_fwd(const Plan& pl, const ssd_config& use, const ssd::DtXform* xf,
+                          const void* x, const float* dt, const float* A, const void* B,
+                          const void* C, const float* D, const float* init_state, void* y,
+                          float* final_state, void* workspace, hipStream_t s) {
+  ssd_status st = run_states(pl, use, x, dt, A, B, init_state, final_state, nullptr, workspace,
+                             xf, s);
+  if (st != SSD_OK) return st;
+  return run_out(pl, use, x, B, C, D, y, workspace, s);
+}
+
+ssd_status ssd_fwd_config(const ssd_problem* prob, const ssd_config* cfg,
+                          const ssd_dt_transform* dtx, const void* x, const float* dt,
+                          const float* A, const void* B, const void* C, const float* D,
+                          const float* init_state, void* y, float* final_state, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  try {
+    Plan pl;
+    ssd_config use;
+    ssd::DtXform xf;
+    ssd_status st = check_fwd(prob, cfg, dtx, x, dt, A, B, C, D, init_state, y, final_state,
+                              workspace, workspace_bytes, &pl, &use, &xf);
+    if (st != SSD_OK) return st;
+    return run_fwd(pl, use, dtx ? &xf : nullptr, x, dt, A, B, C, D, init_state, y, final_state,
+                   workspace, static_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
   }
@@ -335,29 +428,90 @@ ssd_status ssd_fwd_ex(const ssd_problem* prob, const ssd_dt_transform* dtx, cons
                       const float* dt, const float* A, const void* B, const void* C,
                       const float* D, const float* init_state, void* y, float* final_state,
                       void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_fwd_config(prob, nullptr, dtx, x, dt, A, B, C, D, init_state, y, final_state,
+                        workspace, workspace_bytes, stream);
+}
+
+ssd_status ssd_default_config(const ssd_problem* prob, ssd_config* cfg) {
   try {
-    if (!prob || !x || !dt || !A || !B || !C || !y || !workspace)
-      return fail(SSD_ERR_NULL_POINTER, "prob, x, dt, A, B, C, y and workspace must not be NULL");
+    if (!prob || !cfg) return fail(SSD_ERR_NULL_POINTER, "prob and cfg must not be NULL");
     Plan pl;
     ssd_status st = plan_problem(prob, &pl);
     if (st != SSD_OK) return st;
-    ssd::DtXform xf;
-    st = check_dt_transform(dtx, &xf);
-    if (st != SSD_OK) return st;
-    if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
-        !aligned16(D) || !aligned16(init_state) || !aligned16(y) || !aligned16(final_state) ||
-        !aligned16(workspace) || (dtx && !aligned16(dtx->dt_bias)))
-      return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
     st = check_supported(pl);
     if (st != SSD_OK) return st;
-    workspace_plan(&pl);
-    if (workspace_bytes < pl.bytes)
-      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_states(pl, x, dt, A, B, init_state, final_state, nullptr, workspace,
-                    dtx ? &xf : nullptr, s);
+    *cfg = default_config(pl);
+    return ok();
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                    const float* dt, const float* A, const void* B, const void* C, const float* D,
+                    const float* init_state, void* y, float* final_state, void* workspace,
+                    size_t workspace_bytes, void* stream, int32_t reps, ssd_config* tried,
+                    float* tried_ms, int32_t max_tried, int32_t* n_tried, ssd_config* best,
+                    float* best_ms) {
+  try {
+    if (!best || !n_tried) return fail(SSD_ERR_NULL_POINTER, "best and n_tried must not be NULL");
+    Plan pl;
+    ssd_config use;
+    ssd::DtXform xf;
+    ssd_status st = check_fwd(prob, nullptr, dtx, x, dt, A, B, C, D, init_state, y, final_state,
+                              workspace, workspace_bytes, &pl, &use, &xf);
     if (st != SSD_OK) return st;
-    return run_out(pl, x, B, C, D, y, workspace, s);
+    if (reps < 1 || reps > 1000)
+      return fail(SSD_ERR_BAD_VALUE, "reps must be in [1, 1000] (got %d)", reps);
+    if (init_state && static_cast<const void*>(init_state) == static_cast<const void*>(final_state))
+      return fail(SSD_ERR_BAD_VALUE, "tune: init_state must not alias final_state");
+    if (max_tried < 0 || (max_tried > 0 && (!tried || !tried_ms)))
+      return fail(SSD_ERR_BAD_VALUE, "max_tried must be >= 0, with tried and tried_ms given when > 0");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) {
+      if (ev[0]) (void)hipEventDestroy(ev[0]);
+      return fail(SSD_ERR_HIP, "tune: event creation failed");
+    }
+    const ssd::DtXform* xfp = dtx ? &xf : nullptr;
+    int n = 0;
+    float best_t = 0.0f;
+    st = SSD_OK;
+    for (int ch : {4, 16})
+      for (int sh : {4, 2, 1})
+        for (int oh : {2, 1}) {
+          const ssd_config c{ch, sh, oh, 0};
+          if (st != SSD_OK || check_config(pl, c) != SSD_OK || check_supported(pl, oh) != SSD_OK)
+            continue;
+          // one untimed run, then `reps` runs between two events on the stream
+          st = run_fwd(pl, c, xfp, x, dt, A, B, C, D, init_state, y, final_state, workspace, s);
+          if (st == SSD_OK && hipEventRecord(ev[0], s) != hipSuccess)
+            st = fail(SSD_ERR_HIP, "tune: event record failed");
+          for (int r = 0; r < reps && st == SSD_OK; ++r)
+            st = run_fwd(pl, c, xfp, x, dt, A, B, C, D, init_state, y, final_state, workspace, s);
+          float ms = 0.0f;
+          if (st == SSD_OK && (hipEventRecord(ev[1], s) != hipSuccess ||
+                               hipEventSynchronize(ev[1]) != hipSuccess ||
+                               hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess))
+            st = fail(SSD_ERR_HIP, "tune: event timing failed");
+          if (st != SSD_OK) continue;
+          ms /= (float)reps;
+          if (n < max_tried) {
+            tried[n] = c;
+            tried_ms[n] = ms;
+          }
+          if (n == 0 || ms < best_t) {
+            best_t = ms;
+            *best = c;
+          }
+          ++n;
+        }
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (st != SSD_OK) return st;
+    *n_tried = n;
+    if (best_ms) *best_ms = best_t;
+    return ok();
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
   }

@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(so):
     assert set(names) == {"ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
                           "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk_cumsum",
                           "ssd_fwd_states", "ssd_compute_out", "ssd_fwd_ex",
-                          "ssd_chunk_cumsum_ex", "ssd_step", "ssd_fwd_states_ex"}
+                          "ssd_chunk_cumsum_ex", "ssd_step", "ssd_fwd_states_ex",
+                          "ssd_default_config", "ssd_fwd_config", "ssd_tune"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
@@ -46,7 +47,7 @@ def test_exports_every_declared_symbol(so):
 
 
 def test_version_and_strings(so):
-    assert lib.ssd_abi_version() == 2
+    assert lib.ssd_abi_version() == 3
     for code in range(11):
         assert lib.ssd_status_string(code) and lib.ssd_status_string(code) != "unknown status"
     assert lib.ssd_status_string(77) == "unknown status"
@@ -233,6 +234,73 @@ def test_step_ignores_chunk_size(so):
     # (the call stops at the first later check, here the dtype)
     assert call_step(P(chunk_size=48, io_dtype=5)) == DTYPE
     assert call_step(P(chunk_size=0, io_dtype=5)) == DTYPE
+
+
+# ------------------------------------------------------------ tile choices
+
+def CFG(ch=4, sh=4, oh=2, reserved=0):
+    return lib.ssd_config(ch, sh, oh, reserved)
+
+
+def call_fwd_config(prob, cfg, **kw):
+    so = lib.load_library()
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, init=None, y=FAKE, fin=None,
+             ws=FAKE, ws_bytes=0)
+    a.update(kw)
+    return so.ssd_fwd_config(ctypes.byref(prob), None if cfg is None else ctypes.byref(cfg), None,
+                             a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"], a["y"],
+                             a["fin"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,cfg", [
+    (dict(), CFG(ch=8)), (dict(), CFG(sh=3)), (dict(), CFG(oh=3)), (dict(), CFG(reserved=1)),
+    (dict(nheads=4, ngroups=2), CFG(sh=4)),            # 2 heads per group: 4 does not divide
+    (dict(io_dtype=0), CFG(oh=2)),                     # fp32: one head per compute_out workgroup
+    (dict(dstate=256), CFG(oh=2)),                     # dstate 256: accumulators do not fit twice
+    (dict(nheads=6, ngroups=2), CFG(sh=1, oh=2)),      # 3 heads per group: odd
+], ids=["cumsum8", "state3", "out3", "reserved", "state4_hg2", "out2_fp32", "out2_n256", "out2_odd"])
+def test_fwd_config_rejects_bad_choice(so, kw, cfg):
+    assert call_fwd_config(P(**kw), cfg) == BADVAL
+    assert "config" in lib.ssd_last_error_message()
+
+
+def test_fwd_config_check_order_and_default(so):
+    assert call_fwd_config(P(io_dtype=9), CFG(ch=8)) == DTYPE          # dtype first
+    assert call_fwd_config(P(), CFG(ch=8), x=FAKE + 4) == BADVAL       # then the choice
+    assert call_fwd_config(P(), CFG(ch=16, sh=2, oh=1)) == WS           # a valid one passes on
+    assert call_fwd_config(P(), None) == WS                             # NULL = the default
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(batch=2, seqlen=8192, nheads=80, headdim=64, dstate=128, ngroups=1, chunk_size=256),
+     dict(cumsum_heads=4, state_heads=4, out_heads=2)),
+    (dict(batch=8, seqlen=4096, nheads=64, headdim=64, dstate=256, ngroups=8, chunk_size=128),
+     dict(cumsum_heads=4, state_heads=4, out_heads=1)),
+    (dict(nheads=6, ngroups=3), dict(cumsum_heads=4, state_heads=2, out_heads=2)),
+    (dict(nheads=3, ngroups=3, io_dtype=0), dict(cumsum_heads=4, state_heads=1, out_heads=1)),
+])
+def test_default_config_is_the_static_table(so, kw, want):
+    assert lib.ssd_default_config(P(**kw)) == want
+
+
+def test_tune_validation(so):
+    so_ = lib.load_library()
+    prob = P()
+    _, need = ws_status(prob)
+    best, n, ms = lib.ssd_config(), ctypes.c_int32(0), ctypes.c_float(0)
+
+    def tune(reps=3, init=None, fin=FAKE, tried=None, tried_ms=None, max_tried=0, best_p=True,
+             ws_bytes=need):
+        return so_.ssd_tune(ctypes.byref(prob), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, init, FAKE,
+                            fin, FAKE, ws_bytes, None, reps, tried, tried_ms, max_tried,
+                            ctypes.byref(n), ctypes.byref(best) if best_p else None, ctypes.byref(ms))
+    assert tune(best_p=False) == NULLP
+    assert tune(ws_bytes=0) == WS
+    assert tune(reps=0) == BADVAL
+    assert tune(reps=1001) == BADVAL
+    assert tune(max_tried=2) == BADVAL                 # arrays missing
+    assert tune(max_tried=-1) == BADVAL
+    assert tune(init=FAKE, fin=FAKE) == BADVAL         # init_state aliases final_state
 
 
 # ------------------------------------------------------------ built device code
