@@ -14,6 +14,8 @@ dt/A/D and a nonzero fp32 initial state.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --raw-dt           (dt given raw: bias + softplus applied in stage 1)
   python bench.py --mode decode      (token-sequential mode: one ssd_step per step)
+  python bench.py --tune [--workload NAME]   (time every tile choice with ssd_tune; one
+                                      JSON line with each choice's mean ms and the fastest)
   python bench.py --copy-probe       (plain copy kernel, for counter scaling)
 
 Decode mode: the same 2.7B-shaped layer (80 heads, headdim 64, dstate 128,
@@ -252,11 +254,13 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill")
+    ap.add_argument("--tune", action="store_true",
+                    help="time every valid tile choice of the forward pass (ssd_tune)")
     ap.add_argument("--raw-dt", action="store_true",
                     help="pass the raw step size and let stage 1 apply bias + softplus")
     args = ap.parse_args()
@@ -289,6 +293,20 @@ def main():
     dev = torch.device("cuda:0")
     d = {k: (None if v is None else v.to(dev)) for k, v in inputs.items()}
     Q = prob.chunk_size
+    if args.tune:
+        default = ssd.ssd_default_config(ssd.make_problem(
+            prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate, prob.ngroups, Q,
+            ssd.SSD_BF16 if prob.io_dtype == "bf16" else ssd.SSD_F32))
+        best, best_ms, rows = ssd.ssd_tune(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], Q,
+                                           d["init_state"], reps=max(1, args.steps))
+        default_ms = [ms for c, ms in rows if c == default][0]
+        print(json.dumps({"metric": "SSD fwd mean ms per pass for each tile choice (ssd_tune)",
+                          "workload": args.workload, "reps": max(1, args.steps),
+                          "default": default, "default_ms": default_ms,
+                          "best": best, "best_ms": best_ms,
+                          "speedup_vs_default": default_ms / best_ms,
+                          "choices": [dict(c, ms=ms) for c, ms in rows]}), flush=True)
+        return
     pr = ssd.make_problem(prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate,
                           prob.ngroups, Q, ssd.SSD_BF16 if prob.io_dtype == "bf16" else ssd.SSD_F32)
     ws = torch.empty(ssd.ssd_fwd_workspace_size(pr), dtype=torch.uint8, device=dev)
@@ -297,6 +315,8 @@ def main():
                       device=dev)
 
     def step(ev_a=None, ev_b=None, ev_c=None):
+        # events are recorded only where given: the timed loop brackets
+        # compute_out alone (its roofline), each event costing ~4 us per step
         if ev_a is not None:
             ev_a.record()
         if args.raw_dt:
@@ -317,16 +337,16 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        step(*ev[k])
+        step(None, *ev[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / K
-    ms_states = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    ms_out = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    ms_out = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    ms_states = ms_step - ms_out      # the rest of the step: chunk_cumsum, chunk_state, state_pass
 
     # same steps with the 256 MB last-level cache flushed before each (event-timed)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -375,7 +395,8 @@ def main():
         "path_mfma_frac": cnt["f_path"] / (ms_step * 1e-3) / peak_mfma,
         "path_hbm_frac": cnt["b_min"] / (ms_step * 1e-3) / PEAK_HBM,
         "path_tflops": cnt["f_path"] / (ms_step * 1e-3) / 1e12,
-        "stage_ms": {"chunk_cumsum+chunk_state+state_pass": ms_states, "compute_out": ms_out},
+        "stage_ms": {"chunk_cumsum+chunk_state+state_pass (step - compute_out)": ms_states,
+                     "compute_out (events)": ms_out},
         "cold_ms_per_step": {"median": cold_med[0], "states": cold_med[1], "compute_out": cold_med[2]},
         "roofline": {"kernel": "compute_out", "bound": bound, "achieved": achieved, "peak": peak,
                      "unit": unit, "frac": achieved / peak,

@@ -206,7 +206,10 @@ ssd_status ssd_fwd_config(const ssd_problem* prob, const ssd_config* cfg,
 /* Shape tuning: runs the whole forward pass (as ssd_fwd_config, on the
  * caller's inputs and buffers) with every valid tile choice for `prob`, once
  * untimed and then `reps` times between two HIP events on `stream`, and
- * reports the mean time of each and the fastest choice.  Unlike every other
+ * reports the mean time of each and the fastest choice.  The device is first
+ * warmed up with the default choice, and every choice is measured twice (in
+ * forward, then reverse order; the smaller mean is kept) so that clock or
+ * cache drift during the sweep does not favour one end of it.  Unlike every other
  * entry point this one SYNCHRONISES with `stream` (once per choice), creates
  * and destroys two HIP events, and is meant to run once per shape, outside
  * any timed or captured region.  On return y and final_state hold the result

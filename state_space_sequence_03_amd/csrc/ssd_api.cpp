@@ -474,38 +474,51 @@ ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const 
       return fail(SSD_ERR_HIP, "tune: event creation failed");
     }
     const ssd::DtXform* xfp = dtx ? &xf : nullptr;
+    // the valid choices, in a fixed order
+    ssd_config cand[2 * 3 * 2];
     int n = 0;
-    float best_t = 0.0f;
-    st = SSD_OK;
     for (int ch : {4, 16})
       for (int sh : {4, 2, 1})
         for (int oh : {2, 1}) {
           const ssd_config c{ch, sh, oh, 0};
-          if (st != SSD_OK || check_config(pl, c) != SSD_OK || check_supported(pl, oh) != SSD_OK)
-            continue;
-          // one untimed run, then `reps` runs between two events on the stream
-          st = run_fwd(pl, c, xfp, x, dt, A, B, C, D, init_state, y, final_state, workspace, s);
-          if (st == SSD_OK && hipEventRecord(ev[0], s) != hipSuccess)
-            st = fail(SSD_ERR_HIP, "tune: event record failed");
-          for (int r = 0; r < reps && st == SSD_OK; ++r)
-            st = run_fwd(pl, c, xfp, x, dt, A, B, C, D, init_state, y, final_state, workspace, s);
-          float ms = 0.0f;
-          if (st == SSD_OK && (hipEventRecord(ev[1], s) != hipSuccess ||
-                               hipEventSynchronize(ev[1]) != hipSuccess ||
-                               hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess))
-            st = fail(SSD_ERR_HIP, "tune: event timing failed");
-          if (st != SSD_OK) continue;
-          ms /= (float)reps;
-          if (n < max_tried) {
-            tried[n] = c;
-            tried_ms[n] = ms;
-          }
-          if (n == 0 || ms < best_t) {
-            best_t = ms;
-            *best = c;
-          }
-          ++n;
+          if (check_config(pl, c) == SSD_OK && check_supported(pl, oh) == SSD_OK) cand[n++] = c;
         }
+    // mean ms of `reps` runs of choice c between two events (after one untimed run)
+    auto time_one = [&](const ssd_config& c, float* ms) -> ssd_status {
+      ssd_status r = run_fwd(pl, c, xfp, x, dt, A, B, C, D, init_state, y, final_state, workspace, s);
+      if (r == SSD_OK && hipEventRecord(ev[0], s) != hipSuccess)
+        r = fail(SSD_ERR_HIP, "tune: event record failed");
+      for (int k = 0; k < reps && r == SSD_OK; ++k)
+        r = run_fwd(pl, c, xfp, x, dt, A, B, C, D, init_state, y, final_state, workspace, s);
+      if (r == SSD_OK && (hipEventRecord(ev[1], s) != hipSuccess ||
+                          hipEventSynchronize(ev[1]) != hipSuccess ||
+                          hipEventElapsedTime(ms, ev[0], ev[1]) != hipSuccess))
+        r = fail(SSD_ERR_HIP, "tune: event timing failed");
+      *ms /= (float)reps;
+      return r;
+    };
+    // warm the device up with the default choice, then measure every choice
+    // twice, in forward and in reverse order, keeping the smaller mean, so a
+    // drift of clocks or caches during the sweep does not favour one end
+    float warm = 0.0f, t_ms[2 * 3 * 2];
+    st = time_one(use, &warm);
+    for (int i = 0; i < n && st == SSD_OK; ++i) st = time_one(cand[i], &t_ms[i]);
+    for (int i = n - 1; i >= 0 && st == SSD_OK; --i) {
+      float again = 0.0f;
+      st = time_one(cand[i], &again);
+      if (st == SSD_OK && again < t_ms[i]) t_ms[i] = again;
+    }
+    float best_t = 0.0f;
+    for (int i = 0; i < n && st == SSD_OK; ++i) {
+      if (i < max_tried) {
+        tried[i] = cand[i];
+        tried_ms[i] = t_ms[i];
+      }
+      if (i == 0 || t_ms[i] < best_t) {
+        best_t = t_ms[i];
+        *best = cand[i];
+      }
+    }
     (void)hipEventDestroy(ev[0]);
     (void)hipEventDestroy(ev[1]);
     if (st != SSD_OK) return st;
