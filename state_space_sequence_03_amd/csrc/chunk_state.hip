@@ -348,13 +348,8 @@ static hipError_t launch_cs(const void* x, const void* Bm, const float* Gw, cons
   const int64_t nblocks = ((nbc + 7) / 8) * 8 * (H / KH) * PB * NSL;
   const int lds = C::lds_bytes(Q);
   auto kern = chunk_state_kernel<T, KH, NW>;
-  static bool attr_set = false;   // per instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = ensure_dyn_lds<chunk_state_kernel<T, KH, NW>>(160 * 1024);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(C::THREADS), lds, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm), Gw, dtw,
                      static_cast<T*>(S), L, (int)H, (int)P, (int)N, (int)G, Q, (int)T_, ldw,

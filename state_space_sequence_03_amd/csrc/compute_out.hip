@@ -710,14 +710,8 @@ static hipError_t launch_out(const void* x, const void* Bm, const void* Cm, cons
   const int64_t nbc = batch * T_;
   const int64_t nblocks = ((nbc + 7) / 8) * 8 * (H / KH) * PB * RS;
   auto kern = compute_out_kernel<T, NK, IB, KH>;
-  static bool attr_set = false;   // per instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       160 * 1024 - kOutStaticLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = ensure_dyn_lds<compute_out_kernel<T, NK, IB, KH>>(160 * 1024 - kOutStaticLds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(kOutThreads), lay.bytes, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm), static_cast<const T*>(Cm),
                      Gw, dtw, static_cast<const T*>(Hc), Dv, static_cast<T*>(y), flag, L, (int)H, (int)P,

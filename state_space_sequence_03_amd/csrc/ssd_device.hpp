@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace ssd {
 
 typedef __bf16 bf16;
@@ -341,6 +343,24 @@ __device__ __forceinline__ void wait_vm(int n) {
 __device__ __forceinline__ void wave_sync() {
   __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Host side: raise kernel Kern's dynamic-LDS limit to `bytes` once per
+// device.  The attribute belongs to the current device, and launches may come
+// from several host threads at once: each device's first launch sets it (a
+// repeated set is harmless), a per-kernel bit mask records the devices done.
+template <auto Kern>
+inline hipError_t ensure_dyn_lds(int bytes) {
+  static std::atomic<uint64_t> done{0};   // bit d: device d (devices 0..63)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
 }
 
 }  // namespace ssd
