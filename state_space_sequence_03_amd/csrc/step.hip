@@ -13,9 +13,9 @@
 //
 // Work is elementwise in the state plus one dot product per row, and the state
 // (4 P N bytes per head) dominates the bytes moved, so the kernel is a
-// streaming kernel: each lane owns 8 consecutive n of one row p in registers
-// for all L tokens (two 16-byte loads and stores of the state in total), a
-// row is spread over R lanes (R = the power of two >= N / 8), and the row's
+// streaming kernel: each lane owns E = 8 consecutive n of one row p in
+// registers for all L tokens (two 16-byte loads and stores of the state in
+// total), a row is spread over R lanes (R = the power of two >= N / E), and the row's
 // output is a shuffle sum over those R lanes.  One workgroup of 256 threads
 // covers 256 / R rows of one head.  The decay is exp2(dt A log2 e) on the
 // hardware exp2, as in the chunked stages.
@@ -41,7 +41,29 @@ __device__ __forceinline__ void load8(const float* p, float* v) {
   }
 }
 
-template <typename T, int R, bool XF>
+// 4 consecutive io elements as fp32; p is 8-byte (bf16) or 16-byte (fp32) aligned.
+__device__ __forceinline__ void load4(const bf16* p, float* v) {
+  const bf16x4 w = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(w[e]);
+}
+__device__ __forceinline__ void load4(const float* p, float* v) {
+  const floatx4 a = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = a[e];
+}
+// E consecutive io elements (E = 4 or a multiple of 8)
+template <int E, typename T>
+__device__ __forceinline__ void load_e(const T* p, float* v) {
+  if constexpr (E == 4) {
+    load4(p, v);
+  } else {
+#pragma unroll
+    for (int c = 0; c < E; c += 8) load8(p + c, v + c);
+  }
+}
+
+template <typename T, int R, bool XF, int E>
 __global__ void __launch_bounds__(kStepThreads)
 step_kernel(float* __restrict__ state, const T* __restrict__ x, const float* __restrict__ dt,
             const float* __restrict__ A, const T* __restrict__ Bm, const T* __restrict__ Cm,
@@ -54,17 +76,17 @@ step_kernel(float* __restrict__ state, const T* __restrict__ x, const float* __r
   const int h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int g = h / hpg;
-  const int n0 = 8 * r;
+  const int n0 = E * r;
   const bool row_ok = p < P;
   const bool act = row_ok && n0 < N;   // lanes past N only join the row sums
 
-  float s[8];
+  float s[E];
   float* sp = state + (((b * H + h) * P + (row_ok ? p : 0)) * (int64_t)N + n0);
   if (act) {
-    load8(sp, s);
+    load_e<E>(sp, s);
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = 0.0f;
+    for (int e = 0; e < E; ++e) s[e] = 0.0f;
   }
   const float a2 = A[h] * kLog2e;
   const float Dh = D ? D[h] : 0.0f;
@@ -75,19 +97,19 @@ step_kernel(float* __restrict__ state, const T* __restrict__ x, const float* __r
     if constexpr (XF) d = dt_prepare(xf, d, h);
     const float alpha = fast_exp2(d * a2);
     const float xv = row_ok ? to_f32(x[(bt * H + h) * P + p]) : 0.0f;
-    float bv[8], cv[8];
+    float bv[E], cv[E];
     if (act) {
       const int64_t off = (bt * G + g) * N + n0;
-      load8(Bm + off, bv);
-      load8(Cm + off, cv);
+      load_e<E>(Bm + off, bv);
+      load_e<E>(Cm + off, cv);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bv[e] = cv[e] = 0.0f;
+      for (int e = 0; e < E; ++e) bv[e] = cv[e] = 0.0f;
     }
     const float dx = d * xv;
     float part = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < E; ++e) {
       s[e] = fmaf(alpha, s[e], dx * bv[e]);
       part = fmaf(s[e], cv[e], part);
     }
@@ -98,11 +120,17 @@ step_kernel(float* __restrict__ state, const T* __restrict__ x, const float* __r
   }
 
   if (act) {
-    *reinterpret_cast<floatx4*>(sp) = floatx4{s[0], s[1], s[2], s[3]};
-    *reinterpret_cast<floatx4*>(sp + 4) = floatx4{s[4], s[5], s[6], s[7]};
+#pragma unroll
+    for (int c = 0; c < E; c += 4)
+      *reinterpret_cast<floatx4*>(sp + c) = floatx4{s[c], s[c + 1], s[c + 2], s[c + 3]};
   }
 }
 
+// State elements per lane: 8 (two 16-byte pieces of fp32 state).  At batch
+// 128 of the 2.7B shape 8 measured 121-123 us per step; 4 and 16 both ~146 us.
+#ifndef SSD_STEP_E
+#define SSD_STEP_E 8
+#endif
 template <typename T, int R>
 static void launch_r(float* state, const void* x, const float* dt, const float* A, const void* Bm,
                      const void* Cm, const float* D, void* y, const DtXform* xf, int64_t batch,
@@ -115,10 +143,10 @@ static void launch_r(float* state, const void* x, const float* dt, const float* 
   T* yt = static_cast<T*>(y);
   const int hpg = (int)(H / G);
   if (xf)
-    hipLaunchKernelGGL((step_kernel<T, R, true>), grid, dim3(kStepThreads), 0, stream, state, xt,
+    hipLaunchKernelGGL((step_kernel<T, R, true, SSD_STEP_E>), grid, dim3(kStepThreads), 0, stream, state, xt,
                        dt, A, bt, ct, D, yt, *xf, L, (int)H, (int)P, (int)N, (int)G, hpg);
   else
-    hipLaunchKernelGGL((step_kernel<T, R, false>), grid, dim3(kStepThreads), 0, stream, state, xt,
+    hipLaunchKernelGGL((step_kernel<T, R, false, SSD_STEP_E>), grid, dim3(kStepThreads), 0, stream, state, xt,
                        dt, A, bt, ct, D, yt, DtXform{nullptr, 0, 0.0f, 0.0f}, L, (int)H, (int)P,
                        (int)N, (int)G, hpg);
 }
@@ -127,8 +155,10 @@ template <typename T>
 static void launch_t(float* state, const void* x, const float* dt, const float* A, const void* Bm,
                      const void* Cm, const float* D, void* y, const DtXform* xf, int64_t batch,
                      int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, hipStream_t stream) {
-  const int64_t need = N / 8;   // N is a multiple of 16, at most 256: need in 2..32
-  if (need <= 2)
+  const int64_t need = N / SSD_STEP_E;   // N a multiple of 16, at most 256
+  if (need <= 1)
+    launch_r<T, 1>(state, x, dt, A, Bm, Cm, D, y, xf, batch, L, H, P, N, G, stream);
+  else if (need <= 2)
     launch_r<T, 2>(state, x, dt, A, Bm, Cm, D, y, xf, batch, L, H, P, N, G, stream);
   else if (need <= 4)
     launch_r<T, 4>(state, x, dt, A, Bm, Cm, D, y, xf, batch, L, H, P, N, G, stream);
@@ -136,8 +166,10 @@ static void launch_t(float* state, const void* x, const float* dt, const float* 
     launch_r<T, 8>(state, x, dt, A, Bm, Cm, D, y, xf, batch, L, H, P, N, G, stream);
   else if (need <= 16)
     launch_r<T, 16>(state, x, dt, A, Bm, Cm, D, y, xf, batch, L, H, P, N, G, stream);
-  else
+  else if (need <= 32)
     launch_r<T, 32>(state, x, dt, A, Bm, Cm, D, y, xf, batch, L, H, P, N, G, stream);
+  else
+    launch_r<T, 64>(state, x, dt, A, Bm, Cm, D, y, xf, batch, L, H, P, N, G, stream);
 }
 
 // Host launcher.  Shapes as in ssd_step: state [batch, H, P, N] fp32 (in
