@@ -17,6 +17,8 @@ dt/A/D and a nonzero fp32 initial state.
   python bench.py --tune [--workload NAME]   (time every tile choice with ssd_tune; one
                                       JSON line with each choice's mean ms and the fastest)
   python bench.py --copy-probe       (plain copy kernel, for counter scaling)
+  python bench.py --peaks            (achievable peaks on this GPU, for reference: a large
+                                      bf16 GEMM through torch/hipBLASLt and a 1 GiB device copy)
 
 Decode mode: the same 2.7B-shaped layer (80 heads, headdim 64, dstate 128,
 1 group, bf16 x/B/C) at batch 128, one token per step, advancing a resident
@@ -239,6 +241,45 @@ def bench_decode(args):
     print(json.dumps(line), flush=True)
 
 
+def measure_peaks():
+    """Achievable MFMA and HBM rates on this GPU, as references beside the
+    published peaks: a large bf16 GEMM (torch.matmul, i.e. the vendor GEMM
+    library) and a 1 GiB device-to-device copy, each event-timed."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    x = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * COPY_PROBE_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    print(json.dumps({"measured_peaks": {
+        "bf16_gemm_tflops": gemm_tflops, "gemm": "torch.matmul %dx%dx%d bf16" % (n, n, n),
+        "copy_gbs_read_plus_write": copy_gbs, "copy": "1 GiB device copy",
+        "published": {"bf16_mfma_tflops": PEAK_BF16_MFMA / 1e12, "hbm_gbs": PEAK_HBM / 1e9}}}),
+        flush=True)
+
+
 def copy_probe():
     import torch
     n = COPY_PROBE_BYTES // 4
@@ -258,6 +299,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--peaks", action="store_true")
     ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill")
     ap.add_argument("--tune", action="store_true",
                     help="time every valid tile choice of the forward pass (ssd_tune)")
@@ -276,6 +318,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.peaks:
+        measure_peaks()
         return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
