@@ -17,6 +17,8 @@ dt/A/D and a nonzero fp32 initial state.
   python bench.py --tune [--workload NAME]   (time every tile choice with ssd_tune; one
                                       JSON line with each choice's mean ms and the fastest)
   python bench.py --copy-probe       (plain copy kernel, for counter scaling)
+  python bench.py --graph            (each step replays one captured HIP graph of the pass;
+                                      matters for the launch-bound small workloads)
   python bench.py --peaks            (achievable peaks on this GPU, for reference: a large
                                       bf16 GEMM through torch/hipBLASLt and a 1 GiB device copy)
 
@@ -300,6 +302,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--peaks", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one captured HIP graph of the whole pass")
     ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill")
     ap.add_argument("--tune", action="store_true",
                     help="time every valid tile choice of the forward pass (ssd_tune)")
@@ -376,6 +380,35 @@ def main():
         ssd.ssd_compute_out(d["x"], d["B"], d["C"], d["D"], Q, ws, out=y)
         if ev_c is not None:
             ev_c.record()
+
+    if args.graph:
+        # the whole pass captured once; each step is one replay (no per-step
+        # events: the launches are what the graph saves)
+        step()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        cnt = counts(prob)
+        print(json.dumps({"metric": METRIC + " (HIP graph replay)", "value": cnt["tokens"] / (ms_step * 1e-3),
+                          "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+                          "dtype": prob.io_dtype, "data": "synthetic",
+                          "config": {"workload": args.workload, "graph": True}}), flush=True)
+        return
 
     for _ in range(args.warmup):
         step()

@@ -1,0 +1,70 @@
+"""The forward pass under HIP graph capture.
+
+The library enqueues kernels only (no allocation, memset or synchronisation
+on the forward path), so a whole ssd_fwd can be captured once and replayed.
+The graph is replayed several times, with the program's own eager work and
+synchronisations between replays, and every replay is checked against the
+eager result (bitwise: the path is deterministic) and the CPU oracle.
+"""
+import pytest
+import torch
+
+import oracle
+import ssd_synth
+from parity_util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+lib = pytest.importorskip("state_space_sequence_03_amd")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print("\n[gpu-case] %s" % request.node.name, flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=2, seqlen=700, nheads=4, headdim=64, dstate=128, ngroups=2, chunk_size=256,
+         io_dtype="bf16", init_std=0.1),
+    dict(batch=1, seqlen=256, nheads=2, headdim=16, dstate=16, ngroups=1, chunk_size=64,
+         io_dtype="fp32", init_std=None),
+], ids=["bf16_q256", "fp32_tiny"])
+def test_forward_pass_replays_from_a_graph(kw):
+    p = ssd_synth.Problem(**kw)
+    inp = ssd_synth.make_inputs(p, seed=51)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    pr = lib.make_problem(p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups,
+                          p.chunk_size, lib.SSD_BF16 if p.io_dtype == "bf16" else lib.SSD_F32)
+    ws = torch.empty(lib.ssd_fwd_workspace_size(pr), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(d["x"])
+    fin = torch.empty((p.batch, p.nheads, p.headdim, p.dstate), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], p.chunk_size,
+                    d["init_state"], out=y, final_out=fin, workspace=ws)
+
+    fwd()                                   # eager (also sets per-device kernel attributes)
+    torch.cuda.synchronize()
+    y_eager, fin_eager = y.clone(), fin.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fwd()                               # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        fwd()
+    y_ref, fin_ref, _ = oracle.recurrence(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                          inp["D"], inp["init_state"])
+    for rep in range(4):
+        y.zero_()
+        fin.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager) and torch.equal(fin, fin_eager), "replay %d" % rep
+        assert_close(y, y_ref, p.io_dtype, "y (replay %d)" % rep)
+        # eager work of the program's own between replays
+        _ = (d["x"].float() * 2.0).sum().item()
