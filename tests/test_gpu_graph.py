@@ -68,3 +68,40 @@ def test_forward_pass_replays_from_a_graph(kw):
         assert_close(y, y_ref, p.io_dtype, "y (replay %d)" % rep)
         # eager work of the program's own between replays
         _ = (d["x"].float() * 2.0).sum().item()
+
+
+def test_decode_step_replays_from_a_graph():
+    # a captured decode step advances the resident state on every replay:
+    # two replays equal two eager steps, bitwise
+    p = ssd_synth.Problem(batch=4, seqlen=1, nheads=8, headdim=64, dstate=128, ngroups=1,
+                          chunk_size=256, init_std=0.1)
+    d = {k: (None if v is None else v.cuda()) for k, v in ssd_synth.make_inputs(p, seed=52).items()}
+    y = torch.empty_like(d["x"])
+
+    def step(state):
+        lib.ssd_step(state, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], out=y)
+
+    eager = d["init_state"].clone()
+    step(eager)
+    step(eager)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+
+    state = d["init_state"].clone()
+    warm = d["init_state"].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(warm)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(state)
+    # capture recorded the launch without running it: the state is unchanged
+    torch.cuda.synchronize()
+    assert torch.equal(state, d["init_state"])
+    g.replay()
+    _ = (d["x"].float() + 1.0).sum().item()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(state, eager) and torch.equal(y, y_eager)
