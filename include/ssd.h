@@ -25,24 +25,33 @@
  *   3. compute_out    -- causal-masked decayed interaction tile, carried-state
  *                        term and D skip fused, nothing chunk x chunk in HBM.
  * The result equals the token recurrence up to floating-point rounding.
+ * ssd_step runs the same recurrence token by token from a resident state
+ * (decode).
  *
  * Layouts.  Every tensor is dense, row-major, with no padding:
  *     x, y                [batch, seqlen, nheads, headdim]  io dtype
  *     B, C                [batch, seqlen, ngroups, dstate]  io dtype
- *     dt                  [batch, seqlen, nheads]           fp32, > 0 (used as given:
- *                                                            no bias, softplus or clamp)
+ *     dt                  [batch, seqlen, nheads]           fp32, > 0 (used as given;
+ *                                                            the _ex entry points and
+ *                                                            ssd_step can prepare a raw
+ *                                                            one: ssd_dt_transform)
  *     A, D                [nheads]                          fp32
  *     init_state, final_state [batch, nheads, headdim, dstate] fp32
  * io dtype is SSD_BF16 (bf16 operands, fp32 accumulation) or SSD_F32.
  *
  * Ownership and ordering.  Every tensor pointer is DEVICE memory owned by the
  * caller.  The library allocates nothing, frees nothing, never synchronises
- * and keeps no pointer after a call returns.  Work is enqueued on `stream`
+ * and keeps no pointer after a call returns (ssd_tune, a measurement tool,
+ * is the one exception: it creates HIP events and synchronises).  Work is
+ * enqueued on `stream`
  * (a hipStream_t; NULL = the default stream) and its results are valid once
  * the caller has synchronised with that stream; inputs must stay unchanged
  * until then.  y must not overlap any input.  final_state may be the same
  * buffer as init_state (each state tile is read before it is written).
- * Calls are reentrant; the only global state is a thread-local error message.
+ * Calls are reentrant; the only global state is a thread-local error message
+ * and, per kernel, a record of the devices on which its dynamic-LDS limit has
+ * been raised (set once, thread-safely).  The forward path can be captured
+ * into a HIP graph: it enqueues kernels only.
  *
  * Preconditions that are documented, not checked: dt > 0, A <= 0 (A = 0 is
  * allowed and gives causal linear attention), all inputs finite.
