@@ -349,3 +349,13 @@ def test_device_code_m0_and_scalar_stores(so, obj, tmp_path):
     # signed 64-bit bitfield extract otherwise.
     if any(re.match(r"global_load_lds_dwordx4 v\d+, s\[", i) for i in insts):
         assert not any(i.startswith("s_bfe_i64") for i in insts), obj
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    # no fallback path: without libssd.so every entry point raises
+    monkeypatch.setattr(lib, "_LIB_PATH", str(tmp_path / "libssd.so"))
+    monkeypatch.setattr(lib, "_lib", None)
+    with pytest.raises(ImportError):
+        lib.load_library()
+    with pytest.raises(ImportError):
+        lib.ssd_abi_version()
