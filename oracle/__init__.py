@@ -11,6 +11,8 @@ Contents
   chunked(...)        fp64 chunked log-space form (numpy, small inputs).
   dt_transform(...)   fp64 step-size preparation (bias, softplus, clamp) of a
                       Mamba-2 layer, for the raw-dt entry points.
+  recurrence_bwd(...) fp64 gradients of the scan (reverse-mode, token by token).
+  dt_transform_bwd(...) fp64 gradients through the step-size preparation.
 
 The token-sequential (decode) mode needs no function of its own: it is the
 recurrence itself, started from a given state (``recurrence`` with
@@ -31,6 +33,7 @@ import numpy as np
 from .dense import dense_matrix, linear_attention
 from .chunked import chunked
 from .dt import dt_transform, softplus
+from .bwd import dt_transform_bwd, recurrence_bwd
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
@@ -39,7 +42,8 @@ _lock = threading.Lock()
 _lib = None
 
 __all__ = ["build", "load_library", "recurrence", "recurrence_heads", "chunk_cumsum", "dense_matrix",
-           "linear_attention", "chunked", "as_f32", "dt_transform", "softplus"]
+           "linear_attention", "chunked", "as_f32", "dt_transform", "softplus",
+           "recurrence_bwd", "dt_transform_bwd"]
 
 
 def build(force: bool = True) -> str:

@@ -5,7 +5,8 @@ mistake with a textual substitution (the committed source is never touched),
 compiles the copy with gcc and runs every pin of test_oracle.py against it.
 At least one pin must fail for every mutant.  The step-size preparation
 (oracle/dt.py) is treated the same way: a mutated copy of its text is
-executed in a fresh namespace and run against the step-size pins.
+executed in a fresh namespace and run against the step-size pins, and the
+backward oracle (oracle/bwd.py) the same way against the backward pins.
 """
 import os
 import subprocess
@@ -107,3 +108,55 @@ def test_dt_unmodified_copy_passes():
     sp, xf = _dt_mutant("def softplus(v):", "def softplus(v):")
     for pin in DT_PINS:
         pin(sp=sp, xf=xf)
+
+
+BWD_SRC = os.path.join(os.path.dirname(oracle.__file__), "bwd.py")
+
+BWD_MUTANTS = {
+    "dC_from_previous_state": ("dC[t] = s_t.T @ dy[t]", "dC[t] = s_prev.T @ dy[t]"),
+    "skip_gradient_dropped": ("dx[t] = Dh * dy[t] + dt[t] * lam_b", "dx[t] = dt[t] * lam_b"),
+    "dx_without_dt": ("dx[t] = Dh * dy[t] + dt[t] * lam_b", "dx[t] = Dh * dy[t] + lam_b"),
+    "dB_without_dt": ("dB[t] = dt[t] * (lam.T @ x[t])", "dB[t] = (lam.T @ x[t])"),
+    "dl_from_new_state": ("dl = alpha * np.sum(lam * s_prev)", "dl = alpha * np.sum(lam * s_t)"),
+    "dl_without_decay": ("dl = alpha * np.sum(lam * s_prev)", "dl = np.sum(lam * s_prev)"),
+    "ddt_direct_term_dropped": ("ddt[t] = x[t] @ lam_b + a_coef * dl", "ddt[t] = a_coef * dl"),
+    "ddt_decay_term_dropped": ("ddt[t] = x[t] @ lam_b + a_coef * dl", "ddt[t] = x[t] @ lam_b"),
+    "dA_without_dt": ("dA += dt[t] * dl", "dA += dl"),
+    "adjoint_not_decayed": ("lam = alpha * lam", "lam = lam"),
+    "output_adjoint_uses_B": ("lam = lam + np.outer(dy[t], Cg[t])",
+                              "lam = lam + np.outer(dy[t], Bg[t])"),
+    "group_sum_overwritten": ('out["dB"][b, :, g] += dB', 'out["dB"][b, :, g] = dB'),
+    "final_gradient_ignored": ("lam = dS.copy()", "lam = np.zeros_like(dS)"),
+    "recompute_from_first_mark": ("s = marks[start].copy()", "s = marks[0].copy()"),
+    "logistic_wrong": ("g = g * np.exp(v - w)", "g = g * np.exp(-w)"),
+    "clamp_gradient_kept": ("g = g * ((w >= dt_min) & (w <= dt_max))", "g = g"),
+}
+
+
+def _bwd_mutant(old, new):
+    text = open(BWD_SRC).read()
+    assert text.count(old) == 1, "mutation anchor not found: %r" % old
+    text = text.replace(old, new).replace("from .dt import softplus", "from oracle.dt import softplus")
+    ns = {"__name__": "bwd_mutant"}
+    exec(compile(text, "bwd_mutant.py", "exec"), ns)
+    return ns["recurrence_bwd"], ns["dt_transform_bwd"]
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_pins_reject_mutant(name):
+    from test_oracle_bwd import BWD_PINS
+    rb, tb = _bwd_mutant(*BWD_MUTANTS[name])
+    failed = []
+    for pin in BWD_PINS:
+        try:
+            pin(rb=rb, tb=tb)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, "no backward pin rejects the mutant %s" % name
+
+
+def test_bwd_unmodified_copy_passes():
+    from test_oracle_bwd import BWD_PINS
+    rb, tb = _bwd_mutant("def head_bwd(", "def head_bwd(")
+    for pin in BWD_PINS:
+        pin(rb=rb, tb=tb)
