@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
@@ -335,6 +335,55 @@ ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B
 ssd_status ssd_step(const ssd_problem* prob, const ssd_dt_transform* dtx, float* state,
                     const void* x, const float* dt, const float* A, const void* B, const void* C,
                     const float* D, void* y, void* stream);
+
+/* ------------------------------------------------------------------ backward */
+
+/* Workspace bytes that ssd_bwd needs for `prob` (errors as for ssd_bwd's
+ * shape checks). */
+ssd_status ssd_bwd_workspace_size(const ssd_problem* prob, size_t* bytes);
+
+/* Gradients of the scan: given dy = dLoss/dy and, optionally, dfinal =
+ * dLoss/d(final state), the gradients of every input of ssd_fwd_ex.
+ *
+ * The pages stop at the forward pass and name the backward pass as what
+ * end-to-end training still needs (devin.kr "NVIDIA CUDA Tile로 Mamba-2 순방향
+ * 전달 커널 가속화", closing remarks; brifing.si "Accelerating Mamba-2 ...",
+ * limitations); the operation is the derivative of the forward definition
+ * (ssd_fwd), evaluated chunkwise with the forward pass's own decomposition:
+ * the chunk-start states are recomputed (stages 1 and 2), the gradients of
+ * the chunk-boundary states run through the same two stages backwards
+ * (weights exp2(G_i) on dy_i C_i^T, chunks last to first from dfinal), and one
+ * pass per chunk forms dx, dB, dC and the per-token terms of the step-size
+ * gradient, whose reverse running sum over the sequence gives ddt and dA.
+ *
+ *   dtx, x, dt, A, B, C, D, init_state : as for ssd_fwd_ex (D, init_state,
+ *                 dtx optional).
+ *   dy          : [batch, seqlen, nheads, headdim] io dtype.
+ *   dfinal      : [batch, nheads, headdim, dstate] fp32, or NULL (zero).
+ *   dx          : output, layout of x, io dtype.
+ *   ddt         : output [batch, seqlen, nheads] fp32, gradient with respect
+ *                 to the `dt` argument (the raw value when dtx is given: the
+ *                 chain rule through bias, softplus and clamp, the clamp
+ *                 passing the gradient where dt_min <= value <= dt_max).
+ *   dA          : output [nheads] fp32.
+ *   dB, dC      : outputs, layout of B and C, io dtype (summed over the
+ *                 heads of each group).
+ *   dD          : output [nheads] fp32, or NULL (not computed).
+ *   dinit       : output [batch, nheads, headdim, dstate] fp32, or NULL.
+ *   ddt_bias    : output [nheads] fp32, or NULL: the sum of ddt over batch
+ *                 and tokens, i.e. the gradient with respect to a per-head
+ *                 bias added to the dt argument.
+ * Outputs must not overlap inputs or each other.  Every pointer 16-byte
+ * aligned.  Errors as for ssd_fwd_ex (same order: NULL pointers, shape,
+ * chunk, dtype, transform values, alignment, limits, workspace); in
+ * addition SSD_ERR_UNSUPPORTED when headdim exceeds 256 or the per-chunk
+ * tiles of headdim x dstate do not fit the LDS.  Enqueued on `stream`
+ * without synchronising. */
+ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                   const float* dt, const float* A, const void* B, const void* C, const float* D,
+                   const float* init_state, const void* dy, const float* dfinal, void* dx,
+                   float* ddt, float* dA, void* dB, void* dC, float* dD, float* dinit,
+                   float* ddt_bias, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

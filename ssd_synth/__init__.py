@@ -40,7 +40,7 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["Problem", "CONFIGS", "make_inputs", "tensor_digest"]
+__all__ = ["Problem", "CONFIGS", "make_inputs", "make_grads", "tensor_digest"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -132,6 +132,18 @@ def make_inputs(prob: Problem, seed: int) -> Dict[str, Optional[torch.Tensor]]:
         "dt_raw": dt_raw.contiguous(),
         "dt_bias": dt_bias.contiguous(),
     }
+
+
+def make_grads(prob: Problem, seed: int) -> Dict[str, torch.Tensor]:
+    """Upstream gradients for the backward pass, drawn on the CPU from their own
+    generator (seeded with seed + 7919, so the forward inputs of the same seed
+    are unchanged): dy ~ N(0, 1) [batch, seqlen, nheads, headdim] in the io
+    dtype, then dfinal ~ N(0, 1) [batch, nheads, headdim, dstate] fp32."""
+    g = torch.Generator().manual_seed(int(seed) + 7919)
+    Bsz, L, H, P, N = prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate
+    dy = torch.randn((Bsz, L, H, P), generator=g, dtype=torch.float32)
+    dfinal = torch.randn((Bsz, H, P, N), generator=g, dtype=torch.float32)
+    return {"dy": dy.to(prob.torch_io_dtype).contiguous(), "dfinal": dfinal.contiguous()}
 
 
 def tensor_digest(t: Optional[torch.Tensor]) -> Optional[str]:

@@ -25,7 +25,7 @@ __all__ = ["SsdError", "SsdArgumentError", "lib_path", "load_library", "make_pro
            "ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
            "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_states", "ssd_compute_out",
            "ssd_chunk_cumsum", "ssd_fwd_ex", "ssd_fwd_states_ex", "ssd_chunk_cumsum_ex",
-           "ssd_step", "ssd_default_config", "ssd_tune",
+           "ssd_step", "ssd_default_config", "ssd_tune", "ssd_bwd_workspace_size", "ssd_bwd",
            "SSD_F32", "SSD_BF16"]
 
 SSD_F32, SSD_BF16 = 0, 1
@@ -129,6 +129,10 @@ def load_library():
         i32, pi32, pf = ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)
         lib.ssd_tune.restype = ctypes.c_int
         lib.ssd_tune.argtypes = [P, X] + [vp] * 10 + [sz, vp, i32, CF, pf, i32, pi32, CF, pf]
+        lib.ssd_bwd_workspace_size.restype = ctypes.c_int
+        lib.ssd_bwd_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+        lib.ssd_bwd.restype = ctypes.c_int
+        lib.ssd_bwd.argtypes = [P, X] + [vp] * 18 + [sz, vp]
         _lib = lib
         return lib
 
@@ -431,3 +435,60 @@ def ssd_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Te
                       _stream(x.device))
     _check(st)
     return y
+
+
+def ssd_bwd_workspace_size(prob: ssd_problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ssd_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+    return int(n.value)
+
+
+def ssd_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+            C: torch.Tensor, D: Optional[torch.Tensor], chunk_size: int,
+            init_state: Optional[torch.Tensor], dy: torch.Tensor,
+            dfinal: Optional[torch.Tensor] = None, *, dt_bias: Optional[torch.Tensor] = None,
+            dt_softplus: bool = False, dt_limit: Optional[Tuple[float, float]] = None,
+            want_dD: bool = True, want_dinit: bool = True, want_ddt_bias: bool = False,
+            workspace: Optional[torch.Tensor] = None) -> dict:
+    """Backward pass on the current stream (C entry point ssd_bwd).
+
+    Given dy = dLoss/dy and optionally dfinal = dLoss/d(final state), returns a
+    dict with dx, ddt, dA, dB, dC and, when asked, dD, dinit and ddt_bias.  The
+    dt options mean what they mean for ssd_fwd; ddt is then the gradient with
+    respect to the raw ``dt`` argument."""
+    lib = load_library()
+    prob = _problem_of(x, B, chunk_size)
+    if x.dtype != B.dtype or x.dtype != C.dtype or dy.dtype != x.dtype:
+        raise SsdArgumentError(4, "x, B, C and dy must share one dtype")
+    if tuple(dt.shape) != tuple(x.shape[:3]) or A.shape != (x.shape[2],):
+        raise SsdArgumentError(2, "dt must be [batch, seqlen, nheads] and A [nheads]")
+    if tuple(C.shape) != tuple(B.shape) or tuple(dy.shape) != tuple(x.shape):
+        raise SsdArgumentError(2, "C must have the shape of B and dy that of x")
+    if D is not None and D.shape != (x.shape[2],):
+        raise SsdArgumentError(2, "D must be [nheads]")
+    state_shape = (x.shape[0], x.shape[2], x.shape[3], B.shape[3])
+    for name, t in (("init_state", init_state), ("dfinal", dfinal)):
+        if t is not None and tuple(t.shape) != state_shape:
+            raise SsdArgumentError(2, "%s must be [batch, nheads, headdim, dstate]" % name)
+    H = x.shape[2]
+    f32 = dict(dtype=torch.float32, device=x.device)
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty(tuple(dt.shape), **f32),
+           "dA": torch.empty(H, **f32), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+           "dD": torch.empty(H, **f32) if want_dD else None,
+           "dinit": torch.empty(state_shape, **f32) if want_dinit else None,
+           "ddt_bias": torch.empty(H, **f32) if want_ddt_bias else None}
+    need = ssd_bwd_workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    xf, xfp = _dt_transform(H, dt_bias, dt_softplus, dt_limit)
+    st = lib.ssd_bwd(ctypes.byref(prob), xfp, _dev(x, "x"), _dev(dt, "dt", torch.float32),
+                     _dev(A, "A", torch.float32), _dev(B, "B"), _dev(C, "C"),
+                     _dev(D, "D", torch.float32), _dev(init_state, "init_state", torch.float32),
+                     _dev(dy, "dy"), _dev(dfinal, "dfinal", torch.float32),
+                     _dev(out["dx"], "dx"), _dev(out["ddt"], "ddt"), _dev(out["dA"], "dA"),
+                     _dev(out["dB"], "dB"), _dev(out["dC"], "dC"), _dev(out["dD"], "dD"),
+                     _dev(out["dinit"], "dinit"), _dev(out["ddt_bias"], "ddt_bias"),
+                     _dev(workspace, "workspace"),
+                     workspace.numel() * workspace.element_size(), _stream(x.device))
+    _check(st)
+    return out

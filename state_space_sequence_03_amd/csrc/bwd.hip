@@ -1,0 +1,711 @@
+// bwd.hip -- gradients of the chunked scan (the backward pass).
+//
+// The pages stop at the forward pass and name the backward pass as what end-
+// to-end training still needs (devin.kr "NVIDIA CUDA Tile로 Mamba-2 순방향
+// 전달 커널 가속화", closing remarks; brifing.si "Accelerating Mamba-2 ...",
+// limitations).  The gradient itself is fixed by the forward definition; this
+// file evaluates it chunkwise, with the same decomposition the forward pass
+// uses.  For one (b, h), chunk c, tokens i (reading) and j (read), in-chunk
+// log2 running sums G, prepared step sizes dt, a_ij = exp2(G_i - G_j) for
+// j <= i, H_c the state entering the chunk and L_{c+1} the gradient of the
+// state leaving it (dy = gradient of y):
+//
+//   dx_j = D dy_j + dt_j [ sum_{i>=j} a_ij (C_i.B_j) dy_i + exp2(G_last-G_j) L_{c+1} B_j ]
+//   dB_j = dt_j [ sum_{i>=j} a_ij (dy_i.x_j) C_i + exp2(G_last-G_j) L_{c+1}^T x_j ]  (per head)
+//   dC_i = sum_{j<=i} a_ij dt_j (dy_i.x_j) B_j + exp2(G_i) H_c^T dy_i                 (per head)
+//   P_i  = <dy_i, y_i - D x_i>,    Qr_j = <x_j, lam_j B_j>
+//
+// where lam_j is the gradient of the state after token j.  The gradient of
+// the log-decay of token k is  dl_k = <dfinal, s_L> + sum_{t>=k} (P_t - dt_t Qr_t)
+// over the whole sequence (every pair (source, reader) that token k's decay
+// sits between is counted by P at the reader and removed by Q at the source
+// when the source is at or after k), so
+//
+//   ddt_k = A dl_k + Qr_k,     dA = sum_k dt_k dl_k,     dD = sum <dy, x>,
+//
+// and the gradients through the step-size preparation follow by the chain
+// rule.  L_c comes from the forward machinery run backwards: chunk c's own
+// part  S'_c = sum_i exp2(G_i) dy_i C_i^T  is chunk_state with weights
+// exp2(G_i) (x -> dy, B -> C), and  L_c = exp2(G_last(c)) L_{c+1} + S'_c  is
+// state_pass in reverse chunk order, started from dfinal; its last carry is
+// the gradient of the initial state.
+//
+// The states H_c and L_c are computed and kept in fp32 whatever the io dtype
+// (bf16 inputs are widened first and go through the fp32 instantiations of
+// chunk_state and state_pass): dl is a running sum over the whole sequence of
+// terms that largely cancel, and bf16 states would put their rounding, summed
+// over thousands of tokens, straight into ddt and dA.
+//
+// The per-chunk terms here are fp32 FMA on LDS tiles: one workgroup per
+// (chunk, head, batch) walks 64- (or 32-) token blocks of the chunk; two
+// kernels, one for the reading side (dC, P) and one for the read side
+// (dx, dB, Qr), each keeping its outputs in registers across the pairs of
+// blocks.  dB and dC are written per head in fp32 and summed over the heads
+// of a group by a final pass.
+#include "ssd_device.hpp"
+
+namespace ssd {
+
+constexpr int kBwdThreads = 256;
+
+// LDS floats of the two per-chunk kernels for a token block of TB rows
+// (rows padded by one float against bank conflicts).
+__host__ __device__ inline int bwd_union_floats(int TB, int P, int N) {
+  const int a = TB * (N + 1) + TB * (P + 1);
+  const int b = P * (N + 1);
+  return a > b ? a : b;
+}
+__host__ __device__ inline int bwd_target_floats(int TB, int P, int N) {
+  return TB * (N + 1) + TB * (P + 1) + bwd_union_floats(TB, P, N) + TB * (TB + 1) + 2 * TB;
+}
+__host__ __device__ inline int bwd_source_floats(int TB, int P, int N) {
+  return TB * (N + 1) + TB * (P + 1) + bwd_union_floats(TB, P, N) + 2 * TB * (TB + 1) + 3 * TB + 8;
+}
+
+// rows x cols io elements (rows `row_stride` apart) into LDS as fp32 rows of
+// `ld` floats; rows at or past `rows_valid` are zero.
+template <typename T>
+__device__ __forceinline__ void tile_to_lds(float* dst, int ld, const T* src, int64_t row_stride,
+                                            int rows_valid, int rows, int cols) {
+  for (int e = threadIdx.x; e < rows * cols; e += kBwdThreads) {
+    const int r = e / cols, c = e % cols;
+    dst[r * ld + c] = r < rows_valid ? to_f32(src[r * row_stride + c]) : 0.0f;
+  }
+}
+
+__device__ __forceinline__ float sum16(float v) {   // over aligned groups of 16 lanes
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int valid_rows(int64_t L, int64_t t0, int TB) {
+  const int64_t v = L - t0;
+  return v <= 0 ? 0 : (v >= TB ? TB : (int)v);
+}
+
+// Reading side: dC (per head, fp32) and P for every token of one chunk.
+template <typename T, int RI, int NKN>
+__global__ void __launch_bounds__(kBwdThreads)
+bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
+                  const T* __restrict__ dy, const float* __restrict__ Gw,
+                  const float* __restrict__ dtw, const float* __restrict__ Hc,
+                  float* __restrict__ Pout, float* __restrict__ dCh, int64_t L, int H, int P,
+                  int N, int G, int hpg, int Q, int T_, int64_t ldw) {
+  constexpr int TB = 16 * RI;
+  extern __shared__ float sm[];
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int g = h / hpg;
+  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
+  const int ldN = N + 1, ldP = P + 1, ldW = TB + 1;
+  float* Cs = sm;
+  float* gs = Cs + TB * ldN;
+  float* U = gs + TB * ldP;
+  float* Bs = U;
+  float* xs = U + TB * ldN;
+  float* Hs = U;
+  float* Ws = U + bwd_union_floats(TB, P, N);
+  float* Gi = Ws + TB * ldW;
+  float* Gj = Gi + TB;
+  const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
+  const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
+  const int nb = Q / TB, nk = N / 16;
+
+  for (int I = 0; I < nb; ++I) {
+    const int64_t ti0 = (int64_t)c * Q + I * TB;
+    const int vi = valid_rows(L, ti0, TB);
+    if (vi == 0) break;                       // the rest of the chunk is padding
+    __syncthreads();
+    tile_to_lds(Cs, ldN, Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, TB, N);
+    tile_to_lds(gs, ldP, dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, TB, P);
+    if (tid < TB) Gi[tid] = Grow[I * TB + tid];
+    float acc[RI][NKN], pacc[RI];
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+      pacc[r] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NKN; ++k) acc[r][k] = 0.0f;
+    }
+    for (int J = 0; J <= I; ++J) {
+      const int64_t tj0 = (int64_t)c * Q + J * TB;
+      const int vj = valid_rows(L, tj0, TB);
+      __syncthreads();
+      tile_to_lds(Bs, ldN, Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, TB, N);
+      tile_to_lds(xs, ldP, x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, TB, P);
+      if (tid < TB) Gj[tid] = Grow[J * TB + tid];
+      __syncthreads();
+      // rows i = ti*RI + r, columns j = tj*RI + s of the block pair
+      float cb[RI][RI], gx[RI][RI];
+#pragma unroll
+      for (int r = 0; r < RI; ++r)
+#pragma unroll
+        for (int s = 0; s < RI; ++s) cb[r][s] = gx[r][s] = 0.0f;
+      for (int n = 0; n < N; ++n) {
+        float cv[RI], bv[RI];
+#pragma unroll
+        for (int r = 0; r < RI; ++r) cv[r] = Cs[(ti * RI + r) * ldN + n];
+#pragma unroll
+        for (int s = 0; s < RI; ++s) bv[s] = Bs[(tj * RI + s) * ldN + n];
+#pragma unroll
+        for (int r = 0; r < RI; ++r)
+#pragma unroll
+          for (int s = 0; s < RI; ++s) cb[r][s] = fmaf(cv[r], bv[s], cb[r][s]);
+      }
+      for (int p = 0; p < P; ++p) {
+        float gv[RI], xv[RI];
+#pragma unroll
+        for (int r = 0; r < RI; ++r) gv[r] = gs[(ti * RI + r) * ldP + p];
+#pragma unroll
+        for (int s = 0; s < RI; ++s) xv[s] = xs[(tj * RI + s) * ldP + p];
+#pragma unroll
+        for (int r = 0; r < RI; ++r)
+#pragma unroll
+          for (int s = 0; s < RI; ++s) gx[r][s] = fmaf(gv[r], xv[s], gx[r][s]);
+      }
+#pragma unroll
+      for (int r = 0; r < RI; ++r) {
+        const int i = ti * RI + r;
+        float pr = 0.0f;
+#pragma unroll
+        for (int s = 0; s < RI; ++s) {
+          const int j = tj * RI + s;
+          const bool on = J < I || j <= i;
+          // the mask is applied before exp2, so no masked entry is evaluated
+          const float w = on ? fast_exp2(Gi[i] - Gj[j]) * drow[J * TB + j] * gx[r][s] : 0.0f;
+          Ws[i * ldW + j] = w;
+          pr = fmaf(w, cb[r][s], pr);
+        }
+        pacc[r] += sum16(pr);
+      }
+      __syncthreads();
+      for (int j = 0; j < TB; ++j) {
+        float wv[RI];
+#pragma unroll
+        for (int r = 0; r < RI; ++r) wv[r] = Ws[(ti * RI + r) * ldW + j];
+#pragma unroll
+        for (int k = 0; k < NKN; ++k) {
+          if (k < nk) {
+            const float bv = Bs[j * ldN + tj + 16 * k];
+#pragma unroll
+            for (int r = 0; r < RI; ++r) acc[r][k] = fmaf(wv[r], bv, acc[r][k]);
+          }
+        }
+      }
+    }
+    // carried term: exp2(G_i) H_c^T dy_i, and its share of P_i
+    __syncthreads();
+    tile_to_lds(Hs, ldN, Hc + ((b * H + h) * T_ + c) * (int64_t)P * N, (int64_t)N, P, P, N);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+      const int i = ti * RI + r;
+      const float e = fast_exp2(Gi[i]);
+      float cr[NKN];
+#pragma unroll
+      for (int k = 0; k < NKN; ++k) cr[k] = 0.0f;
+      for (int p = 0; p < P; ++p) {
+        const float gv = gs[i * ldP + p];
+#pragma unroll
+        for (int k = 0; k < NKN; ++k)
+          if (k < nk) cr[k] = fmaf(gv, Hs[p * ldN + tj + 16 * k], cr[k]);
+      }
+      float pc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NKN; ++k) {
+        if (k < nk) {
+          const float v = e * cr[k];
+          acc[r][k] += v;
+          pc = fmaf(v, Cs[i * ldN + tj + 16 * k], pc);
+        }
+      }
+      pacc[r] += sum16(pc);
+      if (i < vi) {
+        float* dst = dCh + ((b * L + ti0 + i) * H + h) * (int64_t)N;
+#pragma unroll
+        for (int k = 0; k < NKN; ++k)
+          if (k < nk) dst[tj + 16 * k] = acc[r][k];
+        if (tj == 0) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + i] = pacc[r];
+      }
+    }
+  }
+}
+
+// Read side: dx, dB (per head, fp32), Qr and the chunk's share of dD.
+template <typename T, int RI, int NKN, int NKP>
+__global__ void __launch_bounds__(kBwdThreads)
+bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
+                  const T* __restrict__ dy, const float* __restrict__ Gw,
+                  const float* __restrict__ dtw, const float* __restrict__ Lam,
+                  const float* __restrict__ Dv, T* __restrict__ dx, float* __restrict__ dBh,
+                  float* __restrict__ Qout, float* __restrict__ dDpart, int64_t L, int H, int P,
+                  int N, int G, int hpg, int Q, int T_, int64_t ldw) {
+  constexpr int TB = 16 * RI;
+  extern __shared__ float sm[];
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int g = h / hpg;
+  const int tid = threadIdx.x, tj = tid / 16, ti = tid % 16;
+  const int ldN = N + 1, ldP = P + 1, ldW = TB + 1;
+  float* Bs = sm;
+  float* xs = Bs + TB * ldN;
+  float* U = xs + TB * ldP;
+  float* Cs = U;
+  float* gs = U + TB * ldN;
+  float* Ls = U;
+  float* Us = U + bwd_union_floats(TB, P, N);
+  float* Vs = Us + TB * ldW;
+  float* Gi = Vs + TB * ldW;
+  float* Gj = Gi + TB;
+  float* dj = Gj + TB;
+  float* red = dj + TB;
+  const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
+  const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
+  const int nb = Q / TB, nkn = N / 16, nkp = P / 16;
+  const float Dh = Dv ? Dv[h] : 0.0f;
+  const float Gl = Grow[Q - 1];
+  float dsum = 0.0f;
+
+  for (int J = 0; J < nb; ++J) {
+    const int64_t tj0 = (int64_t)c * Q + J * TB;
+    const int vj = valid_rows(L, tj0, TB);
+    if (vj == 0) break;
+    __syncthreads();
+    tile_to_lds(Bs, ldN, Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, TB, N);
+    tile_to_lds(xs, ldP, x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, TB, P);
+    if (tid < TB) {
+      Gj[tid] = Grow[J * TB + tid];
+      dj[tid] = drow[J * TB + tid];
+    }
+    float dba[RI][NKN], dxa[RI][NKP], qa[RI];
+#pragma unroll
+    for (int s = 0; s < RI; ++s) {
+      qa[s] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NKN; ++k) dba[s][k] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NKP; ++k) dxa[s][k] = 0.0f;
+    }
+    for (int I = J; I < nb; ++I) {
+      const int64_t ti0 = (int64_t)c * Q + I * TB;
+      const int vi = valid_rows(L, ti0, TB);
+      if (vi == 0) break;
+      __syncthreads();
+      tile_to_lds(Cs, ldN, Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, TB, N);
+      tile_to_lds(gs, ldP, dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, TB, P);
+      if (tid < TB) Gi[tid] = Grow[I * TB + tid];
+      __syncthreads();
+      // rows j = tj*RI + s (read), columns i = ti*RI + r (reading)
+      float cb[RI][RI], gx[RI][RI];
+#pragma unroll
+      for (int s = 0; s < RI; ++s)
+#pragma unroll
+        for (int r = 0; r < RI; ++r) cb[s][r] = gx[s][r] = 0.0f;
+      for (int n = 0; n < N; ++n) {
+        float bv[RI], cv[RI];
+#pragma unroll
+        for (int s = 0; s < RI; ++s) bv[s] = Bs[(tj * RI + s) * ldN + n];
+#pragma unroll
+        for (int r = 0; r < RI; ++r) cv[r] = Cs[(ti * RI + r) * ldN + n];
+#pragma unroll
+        for (int s = 0; s < RI; ++s)
+#pragma unroll
+          for (int r = 0; r < RI; ++r) cb[s][r] = fmaf(bv[s], cv[r], cb[s][r]);
+      }
+      for (int p = 0; p < P; ++p) {
+        float xv[RI], gv[RI];
+#pragma unroll
+        for (int s = 0; s < RI; ++s) xv[s] = xs[(tj * RI + s) * ldP + p];
+#pragma unroll
+        for (int r = 0; r < RI; ++r) gv[r] = gs[(ti * RI + r) * ldP + p];
+#pragma unroll
+        for (int s = 0; s < RI; ++s)
+#pragma unroll
+          for (int r = 0; r < RI; ++r) gx[s][r] = fmaf(xv[s], gv[r], gx[s][r]);
+      }
+#pragma unroll
+      for (int s = 0; s < RI; ++s) {
+        const int j = tj * RI + s;
+        float qr = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RI; ++r) {
+          const int i = ti * RI + r;
+          const bool on = I > J || j <= i;
+          const float a = on ? fast_exp2(Gi[i] - Gj[j]) : 0.0f;
+          const float u = a * cb[s][r];
+          Us[j * ldW + i] = u;
+          Vs[j * ldW + i] = a * gx[s][r];
+          qr = fmaf(u, gx[s][r], qr);
+        }
+        qa[s] += sum16(qr);
+      }
+      __syncthreads();
+      for (int i = 0; i < TB; ++i) {
+        float uv[RI], vv[RI];
+#pragma unroll
+        for (int s = 0; s < RI; ++s) {
+          uv[s] = Us[(tj * RI + s) * ldW + i];
+          vv[s] = Vs[(tj * RI + s) * ldW + i];
+        }
+#pragma unroll
+        for (int k = 0; k < NKN; ++k) {
+          if (k < nkn) {
+            const float cv = Cs[i * ldN + ti + 16 * k];
+#pragma unroll
+            for (int s = 0; s < RI; ++s) dba[s][k] = fmaf(vv[s], cv, dba[s][k]);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < NKP; ++k) {
+          if (k < nkp) {
+            const float gv = gs[i * ldP + ti + 16 * k];
+#pragma unroll
+            for (int s = 0; s < RI; ++s) dxa[s][k] = fmaf(uv[s], gv, dxa[s][k]);
+          }
+        }
+      }
+    }
+    // carried term from the gradient of the state leaving the chunk
+    __syncthreads();
+    tile_to_lds(Ls, ldN, Lam + ((b * H + h) * T_ + c) * (int64_t)P * N, (int64_t)N, P, P, N);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < RI; ++s) {
+      const int j = tj * RI + s;
+      const float e = fast_exp2(Gl - Gj[j]);
+      float qx = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NKP; ++k) {
+        if (k < nkp) {
+          const int p = ti + 16 * k;
+          float v = 0.0f;
+          for (int n = 0; n < N; ++n) v = fmaf(Ls[p * ldN + n], Bs[j * ldN + n], v);
+          v *= e;
+          dxa[s][k] += v;
+          qx = fmaf(xs[j * ldP + p], v, qx);
+        }
+      }
+      qa[s] += sum16(qx);
+#pragma unroll
+      for (int k = 0; k < NKN; ++k) {
+        if (k < nkn) {
+          const int n = ti + 16 * k;
+          float v = 0.0f;
+          for (int p = 0; p < P; ++p) v = fmaf(Ls[p * ldN + n], xs[j * ldP + p], v);
+          dba[s][k] = fmaf(e, v, dba[s][k]);
+        }
+      }
+      if (j < vj) {
+        const int64_t t = tj0 + j;
+        const float d = dj[j];
+        const int64_t row = (b * L + t) * H + h;
+#pragma unroll
+        for (int k = 0; k < NKP; ++k) {
+          if (k < nkp) {
+            const int p = ti + 16 * k;
+            const float gv = to_f32(dy[row * P + p]);
+            dx[row * P + p] = to_io<T>(fmaf(d, dxa[s][k], Dh * gv));
+            dsum = fmaf(gv, xs[j * ldP + p], dsum);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < NKN; ++k)
+          if (k < nkn) dBh[row * N + ti + 16 * k] = d * dba[s][k];
+        if (ti == 0) Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + j] = qa[s];
+      }
+    }
+  }
+  // the chunk's share of dD = sum <dy, x>
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, kWave);
+  __syncthreads();
+  if (tid % kWave == 0) red[tid / kWave] = dsum;
+  __syncthreads();
+  if (tid == 0) dDpart[(b * T_ + c) * H + h] = red[0] + red[1] + red[2] + red[3];
+}
+
+// Step-size gradients of one (b, h): the reverse running sum of P - dt Qr over
+// the whole sequence (fp64), then ddt, the (b, h) shares of dA and of the
+// bias gradient, with the step-size preparation's chain rule when XF is set.
+template <bool XF>
+__global__ void __launch_bounds__(kBwdThreads)
+bwd_dt_kernel(const float* __restrict__ Pb, const float* __restrict__ Qb,
+              const float* __restrict__ dtw, const float* __restrict__ dt_in,
+              const float* __restrict__ A, const float* __restrict__ dfinal,
+              const float* __restrict__ fin, DtXform xf, float* __restrict__ ddt,
+              double* __restrict__ dApart, double* __restrict__ dbpart, int64_t L, int H,
+              int64_t PN, int64_t ldw) {
+  __shared__ double seg_sum[kBwdThreads];
+  __shared__ double red[2][kBwdThreads / kWave];
+  const int h = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t bh = b * H + h;
+
+  // <dfinal, final state>: every token's decay lies before the final state
+  double kf = 0.0;
+  if (dfinal)
+    for (int64_t e = tid; e < PN; e += kBwdThreads) kf += (double)dfinal[bh * PN + e] * fin[bh * PN + e];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) kf += __shfl_xor(kf, off, kWave);
+  if (tid % kWave == 0) red[0][tid / kWave] = kf;
+
+  const int64_t seg = (L + kBwdThreads - 1) / kBwdThreads;
+  const int64_t t0 = tid * seg, t1 = t0 + seg < L ? t0 + seg : L;
+  const float* Pr = Pb + bh * ldw;
+  const float* Qr = Qb + bh * ldw;
+  const float* dr = dtw + bh * ldw;
+  double s = 0.0;
+  for (int64_t t = t0; t < t1; ++t) s += (double)Pr[t] - (double)dr[t] * Qr[t];
+  seg_sum[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    double run = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    for (int k = kBwdThreads - 1; k >= 0; --k) {   // seg_sum[k] <- K + sum over later segments
+      const double v = seg_sum[k];
+      seg_sum[k] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  const float a = A[h];
+  double run = seg_sum[tid], da = 0.0, db = 0.0;
+  for (int64_t t = t1 - 1; t >= t0; --t) {
+    run += (double)Pr[t] - (double)dr[t] * Qr[t];
+    const float dl = (float)run;
+    float gdt = fmaf(a, dl, Qr[t]);
+    da += (double)dr[t] * run;
+    if constexpr (XF) {
+      float v = dt_in[(b * L + t) * H + h];
+      if (xf.bias) v += xf.bias[h];
+      float w = v, sig = 1.0f;
+      if (xf.softplus) {
+        w = softplus_f32(v);
+        sig = 1.0f / (1.0f + fast_exp2(-v * kLog2e));
+      }
+      gdt = (w >= xf.lo && w <= xf.hi) ? gdt * sig : 0.0f;
+    }
+    db += gdt;
+    ddt[(b * L + t) * H + h] = gdt;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    da += __shfl_xor(da, off, kWave);
+    db += __shfl_xor(db, off, kWave);
+  }
+  __syncthreads();
+  if (tid % kWave == 0) {
+    red[0][tid / kWave] = da;
+    red[1][tid / kWave] = db;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    dApart[bh] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    dbpart[bh] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  }
+}
+
+// bf16 -> fp32 copy (inputs of the fp32 state stages)
+__global__ void __launch_bounds__(kBwdThreads)
+bwd_widen_kernel(const bf16* __restrict__ src, float* __restrict__ dst, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * kBwdThreads)
+    dst[e] = to_f32(src[e]);
+}
+
+// weights exp2(G) of the reversed chunk contributions (0 on padding tokens),
+// and an all-zero running sum so that chunk_state's exp2(G_last - G_j) is 1
+__global__ void __launch_bounds__(kBwdThreads)
+bwd_prep_kernel(const float* __restrict__ Gw, float* __restrict__ w2, float* __restrict__ Gz,
+                int64_t total, int64_t L, int64_t ldw) {
+  for (int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * kBwdThreads) {
+    w2[e] = e % ldw < L ? fast_exp2(Gw[e]) : 0.0f;
+    Gz[e] = 0.0f;
+  }
+}
+
+// dB and dC: sums over the heads of each group of the per-head fp32 parts
+template <typename T>
+__global__ void __launch_bounds__(kBwdThreads)
+bwd_group_sum_kernel(const float* __restrict__ dBh, const float* __restrict__ dCh,
+                     T* __restrict__ dB, T* __restrict__ dC, int64_t total, int H, int G, int N) {
+  const int hpg = H / G;
+  for (int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * kBwdThreads) {
+    const int n = (int)(e % N);
+    const int64_t bg = e / N;                 // (b*L + t)*G + g
+    const int64_t bt = bg / G;
+    const int g = (int)(bg % G);
+    const int64_t base = (bt * H + (int64_t)g * hpg) * N + n;
+    float sb = 0.0f, sc = 0.0f;
+    for (int k = 0; k < hpg; ++k) {
+      sb += dBh[base + (int64_t)k * N];
+      sc += dCh[base + (int64_t)k * N];
+    }
+    dB[e] = to_io<T>(sb);
+    dC[e] = to_io<T>(sc);
+  }
+}
+
+// dA, dD and the bias gradient: sums of the per-(b, h) and per-(b, c, h) parts
+__global__ void __launch_bounds__(kBwdThreads)
+bwd_scalars_kernel(const double* __restrict__ dApart, const double* __restrict__ dbpart,
+                   const float* __restrict__ dDpart, float* __restrict__ dA, float* __restrict__ dD,
+                   float* __restrict__ dbias, int64_t batch, int H, int T_) {
+  for (int h = threadIdx.x; h < H; h += kBwdThreads) {
+    double sa = 0.0, sb = 0.0, sd = 0.0;
+    for (int64_t b = 0; b < batch; ++b) {
+      sa += dApart[b * H + h];
+      sb += dbpart[b * H + h];
+      for (int c = 0; c < T_; ++c) sd += dDpart[(b * T_ + c) * H + h];
+    }
+    dA[h] = (float)sa;
+    if (dD) dD[h] = (float)sd;
+    if (dbias) dbias[h] = (float)sb;
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+// Token-block rows of the per-chunk kernels: 64 when the chunk allows it and
+// the LDS plan fits, else 32; 0 if neither fits.
+int bwd_block_rows(int Q, int64_t P, int64_t N) {
+  const int64_t lim = 160 * 1024 / 4;
+  for (int TB : {64, 32}) {
+    if (Q % TB != 0) continue;
+    if (bwd_target_floats(TB, (int)P, (int)N) <= lim && bwd_source_floats(TB, (int)P, (int)N) <= lim)
+      return TB;
+  }
+  return 0;
+}
+
+template <typename T, int RI, int NKN, int NKP>
+static hipError_t launch_chunks(const void* x, const void* Bm, const void* Cm, const void* dy,
+                                const float* Gw, const float* dtw, const void* Hc, const void* Lam,
+                                const float* Dv, void* dx, float* Pb, float* Qb, float* dBh,
+                                float* dCh, float* dDpart, int64_t batch, int64_t L, int64_t H,
+                                int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
+                                hipStream_t stream) {
+  constexpr int TB = 16 * RI;
+  const int ta = bwd_target_floats(TB, (int)P, (int)N) * 4;
+  const int sb = bwd_source_floats(TB, (int)P, (int)N) * 4;
+  hipError_t e = ensure_dyn_lds<bwd_target_kernel<T, RI, NKN>>(ta);
+  if (e != hipSuccess) return e;
+  e = ensure_dyn_lds<bwd_source_kernel<T, RI, NKN, NKP>>(sb);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)T_, (unsigned)H, (unsigned)batch);
+  const int hpg = (int)(H / G);
+  hipLaunchKernelGGL((bwd_target_kernel<T, RI, NKN>), grid, dim3(kBwdThreads), ta, stream,
+                     static_cast<const T*>(x), static_cast<const T*>(Bm),
+                     static_cast<const T*>(Cm), static_cast<const T*>(dy), Gw, dtw,
+                     static_cast<const float*>(Hc), Pb, dCh, L, (int)H, (int)P, (int)N, (int)G, hpg, Q,
+                     (int)T_, ldw);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_source_kernel<T, RI, NKN, NKP>), grid, dim3(kBwdThreads), sb, stream,
+                     static_cast<const T*>(x), static_cast<const T*>(Bm),
+                     static_cast<const T*>(Cm), static_cast<const T*>(dy), Gw, dtw,
+                     static_cast<const float*>(Lam), Dv, static_cast<T*>(dx), dBh, Qb, dDpart, L,
+                     (int)H, (int)P, (int)N, (int)G, hpg, Q, (int)T_, ldw);
+  return hipGetLastError();
+}
+
+template <typename T, int RI, int NKN>
+static hipError_t launch_chunks_p(int64_t P, const void* x, const void* Bm, const void* Cm,
+                                  const void* dy, const float* Gw, const float* dtw,
+                                  const void* Hc, const void* Lam, const float* Dv, void* dx,
+                                  float* Pb, float* Qb, float* dBh, float* dCh, float* dDpart,
+                                  int64_t batch, int64_t L, int64_t H, int64_t N, int64_t G, int Q,
+                                  int64_t T_, int64_t ldw, hipStream_t stream) {
+#define SSD_BWD_ARGS x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh, dDpart, batch, L, H, \
+                     P, N, G, Q, T_, ldw, stream
+  if (P <= 64) return launch_chunks<T, RI, NKN, 4>(SSD_BWD_ARGS);
+  if (P <= 128) return launch_chunks<T, RI, NKN, 8>(SSD_BWD_ARGS);
+  return launch_chunks<T, RI, NKN, 16>(SSD_BWD_ARGS);
+#undef SSD_BWD_ARGS
+}
+
+template <typename T>
+static hipError_t launch_chunks_t(int TB, const void* x, const void* Bm, const void* Cm,
+                                  const void* dy, const float* Gw, const float* dtw,
+                                  const void* Hc, const void* Lam, const float* Dv, void* dx,
+                                  float* Pb, float* Qb, float* dBh, float* dCh, float* dDpart,
+                                  int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                                  int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
+#define SSD_BWD_ARGS P, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh, dDpart, batch, L, \
+                     H, N, G, Q, T_, ldw, stream
+  if (TB == 64) {
+    if (N <= 128) return launch_chunks_p<T, 4, 8>(SSD_BWD_ARGS);
+    return launch_chunks_p<T, 4, 16>(SSD_BWD_ARGS);
+  }
+  if (N <= 128) return launch_chunks_p<T, 2, 8>(SSD_BWD_ARGS);
+  return launch_chunks_p<T, 2, 16>(SSD_BWD_ARGS);
+#undef SSD_BWD_ARGS
+}
+
+hipError_t launch_bwd_widen(const void* src, float* dst, int64_t n, hipStream_t stream) {
+  const int64_t blocks = (n + kBwdThreads - 1) / kBwdThreads;
+  hipLaunchKernelGGL(bwd_widen_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)),
+                     dim3(kBwdThreads), 0, stream, static_cast<const bf16*>(src), dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const float* Gw, float* w2, float* Gz, int64_t batch, int64_t H,
+                           int64_t L, int64_t ldw, hipStream_t stream) {
+  const int64_t total = batch * H * ldw;
+  const int64_t blocks = (total + kBwdThreads - 1) / kBwdThreads;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                     dim3(kBwdThreads), 0, stream, Gw, w2, Gz, total, L, ldw);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_chunks(int io_bf16, int TB, const void* x, const void* Bm, const void* Cm,
+                             const void* dy, const float* Gw, const float* dtw, const void* Hc,
+                             const void* Lam, const float* Dv, void* dx, float* Pb, float* Qb,
+                             float* dBh, float* dCh, float* dDpart, int64_t batch, int64_t L,
+                             int64_t H, int64_t P, int64_t N, int64_t G, int Q, int64_t T_,
+                             int64_t ldw, hipStream_t stream) {
+  if (io_bf16)
+    return launch_chunks_t<bf16>(TB, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh,
+                                 dDpart, batch, L, H, P, N, G, Q, T_, ldw, stream);
+  return launch_chunks_t<float>(TB, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh,
+                                dDpart, batch, L, H, P, N, G, Q, T_, ldw, stream);
+}
+
+hipError_t launch_bwd_finish(int io_bf16, const float* Pb, const float* Qb, const float* dtw,
+                             const float* dt_in, const float* A, const float* dfinal,
+                             const float* fin, const DtXform* xf, float* ddt, double* dApart,
+                             double* dbpart, const float* dBh, const float* dCh,
+                             const float* dDpart, void* dB, void* dC, float* dA, float* dD,
+                             float* dbias, int64_t batch, int64_t L, int64_t H, int64_t P,
+                             int64_t N, int64_t G, int64_t T_, int64_t ldw, hipStream_t stream) {
+  const dim3 g1((unsigned)H, (unsigned)batch);
+  if (xf)
+    hipLaunchKernelGGL(bwd_dt_kernel<true>, g1, dim3(kBwdThreads), 0, stream, Pb, Qb, dtw, dt_in,
+                       A, dfinal, fin, *xf, ddt, dApart, dbpart, L, (int)H, P * N, ldw);
+  else
+    hipLaunchKernelGGL(bwd_dt_kernel<false>, g1, dim3(kBwdThreads), 0, stream, Pb, Qb, dtw, dt_in,
+                       A, dfinal, fin, DtXform{nullptr, 0, 0.0f, 0.0f}, ddt, dApart, dbpart, L,
+                       (int)H, P * N, ldw);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = batch * L * G * N;
+  const int64_t blocks = (total + kBwdThreads - 1) / kBwdThreads;
+  const dim3 g2((unsigned)(blocks < 8192 ? blocks : 8192));
+  if (io_bf16)
+    hipLaunchKernelGGL(bwd_group_sum_kernel<bf16>, g2, dim3(kBwdThreads), 0, stream, dBh, dCh,
+                       static_cast<bf16*>(dB), static_cast<bf16*>(dC), total, (int)H, (int)G,
+                       (int)N);
+  else
+    hipLaunchKernelGGL(bwd_group_sum_kernel<float>, g2, dim3(kBwdThreads), 0, stream, dBh, dCh,
+                       static_cast<float*>(dB), static_cast<float*>(dC), total, (int)H, (int)G,
+                       (int)N);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scalars_kernel, dim3(1), dim3(kBwdThreads), 0, stream, dApart, dbpart,
+                     dDpart, dA, dD, dbias, batch, (int)H, (int)T_);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

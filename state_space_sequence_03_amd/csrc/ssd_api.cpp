@@ -30,7 +30,8 @@ hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, const 
                               int frag_major, int kh, hipStream_t stream);
 hipError_t launch_state_pass(int io_bf16, void* S, const float* Gw, const float* init_state,
                              float* final_state, int64_t batch, int64_t H, int64_t P, int64_t N,
-                             int Q, int64_t T_, int64_t ldw, int frag_major, hipStream_t stream);
+                             int Q, int64_t T_, int64_t ldw, int frag_major, int reverse,
+                             hipStream_t stream);
 hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
                               void* y, void* sink, int64_t batch, int64_t L, int64_t H, int64_t P,
@@ -40,6 +41,23 @@ int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int kh);
 int compute_out_kh_valid(int io_bf16, int64_t H, int64_t G, int64_t N, int kh);
 int compute_out_default_kh(int io_bf16, int64_t H, int64_t G, int64_t N);
 int chunk_state_default_kh(int64_t H, int64_t G);
+int bwd_block_rows(int Q, int64_t P, int64_t N);
+hipError_t launch_bwd_widen(const void* src, float* dst, int64_t n, hipStream_t stream);
+hipError_t launch_bwd_prep(const float* Gw, float* w2, float* Gz, int64_t batch, int64_t H,
+                           int64_t L, int64_t ldw, hipStream_t stream);
+hipError_t launch_bwd_chunks(int io_bf16, int TB, const void* x, const void* Bm, const void* Cm,
+                             const void* dy, const float* Gw, const float* dtw, const void* Hc,
+                             const void* Lam, const float* Dv, void* dx, float* Pb, float* Qb,
+                             float* dBh, float* dCh, float* dDpart, int64_t batch, int64_t L,
+                             int64_t H, int64_t P, int64_t N, int64_t G, int Q, int64_t T_,
+                             int64_t ldw, hipStream_t stream);
+hipError_t launch_bwd_finish(int io_bf16, const float* Pb, const float* Qb, const float* dtw,
+                             const float* dt_in, const float* A, const float* dfinal,
+                             const float* fin, const DtXform* xf, float* ddt, double* dApart,
+                             double* dbpart, const float* dBh, const float* dCh,
+                             const float* dDpart, void* dB, void* dC, float* dA, float* dD,
+                             float* dbias, int64_t batch, int64_t L, int64_t H, int64_t P,
+                             int64_t N, int64_t G, int64_t T_, int64_t ldw, hipStream_t stream);
 }  // namespace ssd
 
 namespace {
@@ -189,6 +207,58 @@ void workspace_plan(Plan* pl) {
   pl->bytes = pl->sink_off + kSinkBytes;
 }
 
+// Backward-pass workspace: running sums and step sizes, the reversed-chunk
+// weights, per-token P and Qr, chunk-start states H_c and boundary-state
+// gradients L_{c+1} ([batch, H, T, P, N] fp32), the final state, the
+// per-head dB/dC parts, the per-(b, h) / per-(b, c, h) scalar parts and, for
+// bf16 io, fp32 copies of x, dy, B and C for the fp32 state stages.
+struct BwdPlan {
+  size_t g_off, dt_off, gz_off, w2_off, pb_off, qb_off, hc_off, lam_off, fin_off, dbh_off,
+      dch_off, dap_off, dbp_off, ddp_off, x32_off, dy32_off, b32_off, c32_off, bytes;
+  int TB;
+};
+
+BwdPlan bwd_plan(const Plan& pl) {
+  BwdPlan w;
+  const size_t tok = align256(size_t(pl.B) * pl.H * pl.Lp * sizeof(float));
+  const size_t st = align256(size_t(pl.B) * pl.H * pl.T * pl.P * pl.N * sizeof(float));
+  const size_t per_head = align256(size_t(pl.B) * pl.L * pl.H * pl.N * sizeof(float));
+  size_t o = 0;
+  w.g_off = o; o += tok;
+  w.dt_off = o; o += tok;
+  w.gz_off = o; o += tok;
+  w.w2_off = o; o += tok;
+  w.pb_off = o; o += tok;
+  w.qb_off = o; o += tok;
+  w.hc_off = o; o += st;
+  w.lam_off = o; o += st;
+  w.fin_off = o; o += align256(size_t(pl.B) * pl.H * pl.P * pl.N * sizeof(float));
+  w.dbh_off = o; o += per_head;
+  w.dch_off = o; o += per_head;
+  w.dap_off = o; o += align256(size_t(pl.B) * pl.H * sizeof(double));
+  w.dbp_off = o; o += align256(size_t(pl.B) * pl.H * sizeof(double));
+  w.ddp_off = o; o += align256(size_t(pl.B) * pl.T * pl.H * sizeof(float));
+  const size_t xs = pl.bf16 ? align256(size_t(pl.B) * pl.L * pl.H * pl.P * sizeof(float)) : 0;
+  const size_t bs = pl.bf16 ? align256(size_t(pl.B) * pl.L * pl.G * pl.N * sizeof(float)) : 0;
+  w.x32_off = o; o += xs;
+  w.dy32_off = o; o += xs;
+  w.b32_off = o; o += bs;
+  w.c32_off = o; o += bs;
+  w.bytes = o;
+  w.TB = ssd::bwd_block_rows((int)pl.Q, pl.P, pl.N);
+  return w;
+}
+
+ssd_status check_supported_bwd(const Plan& pl) {
+  ssd_status st = check_supported(pl);
+  if (st != SSD_OK) return st;
+  if (pl.P > 256) return fail(SSD_ERR_UNSUPPORTED, "backward: headdim must be <= 256");
+  if (ssd::bwd_block_rows((int)pl.Q, pl.P, pl.N) == 0)
+    return fail(SSD_ERR_UNSUPPORTED, "backward: headdim %lld and dstate %lld exceed LDS",
+                (long long)pl.P, (long long)pl.N);
+  return SSD_OK;
+}
+
 ssd_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(SSD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -286,7 +356,7 @@ static ssd_status run_states(const Plan& pl, const ssd_config& cfg, const void* 
                               (int)pl.Q, pl.T, pl.Lp, frag_major, cfg.state_heads, s);
   if (e != hipSuccess) return hip_status(e, "chunk_state launch");
   e = ssd::launch_state_pass(pl.bf16, Hc, Gw, init_state, final_state, pl.B, pl.H, pl.P, pl.N,
-                             (int)pl.Q, pl.T, pl.Lp, frag_major, s);
+                             (int)pl.Q, pl.T, pl.Lp, frag_major, 0, s);
   return hip_status(e, "state_pass launch");
 }
 
@@ -563,6 +633,113 @@ ssd_status ssd_step(const ssd_problem* prob, const ssd_dt_transform* dtx, float*
                                        pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
                                        static_cast<hipStream_t>(stream)),
                       "step launch");
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+ssd_status ssd_bwd_workspace_size(const ssd_problem* prob, size_t* bytes) {
+  try {
+    if (!prob || !bytes) return fail(SSD_ERR_NULL_POINTER, "prob and bytes must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl);
+    if (st != SSD_OK) return st;
+    st = check_supported_bwd(pl);
+    if (st != SSD_OK) return st;
+    *bytes = bwd_plan(pl).bytes;
+    return ok();
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                   const float* dt, const float* A, const void* B, const void* C, const float* D,
+                   const float* init_state, const void* dy, const float* dfinal, void* dx,
+                   float* ddt, float* dA, void* dB, void* dC, float* dD, float* dinit,
+                   float* ddt_bias, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!prob || !x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC ||
+        !workspace)
+      return fail(SSD_ERR_NULL_POINTER,
+                  "prob, x, dt, A, B, C, dy, dx, ddt, dA, dB, dC and workspace must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl);
+    if (st != SSD_OK) return st;
+    ssd::DtXform xf;
+    st = check_dt_transform(dtx, &xf);
+    if (st != SSD_OK) return st;
+    const void* ptrs[] = {x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD,
+                          dinit, ddt_bias, workspace, dtx ? dtx->dt_bias : nullptr};
+    for (const void* p : ptrs)
+      if (!aligned16(p)) return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
+    st = check_supported_bwd(pl);
+    if (st != SSD_OK) return st;
+    const BwdPlan w = bwd_plan(pl);
+    if (workspace_bytes < w.bytes)
+      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.bytes);
+    char* ws = static_cast<char*>(workspace);
+    float* Gw = reinterpret_cast<float*>(ws + w.g_off);
+    float* dtw = reinterpret_cast<float*>(ws + w.dt_off);
+    float* Gz = reinterpret_cast<float*>(ws + w.gz_off);
+    float* w2 = reinterpret_cast<float*>(ws + w.w2_off);
+    float* Pb = reinterpret_cast<float*>(ws + w.pb_off);
+    float* Qb = reinterpret_cast<float*>(ws + w.qb_off);
+    void* Hc = ws + w.hc_off;
+    void* Lam = ws + w.lam_off;
+    float* fin = reinterpret_cast<float*>(ws + w.fin_off);
+    float* dBh = reinterpret_cast<float*>(ws + w.dbh_off);
+    float* dCh = reinterpret_cast<float*>(ws + w.dch_off);
+    double* dAp = reinterpret_cast<double*>(ws + w.dap_off);
+    double* dbp = reinterpret_cast<double*>(ws + w.dbp_off);
+    float* dDp = reinterpret_cast<float*>(ws + w.ddp_off);
+    const ssd::DtXform* xfp = dtx ? &xf : nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const ssd_config cfg = default_config(pl);
+    // fp32 operands of the state stages (the io tensors themselves for fp32 io)
+    const void* x32 = x;
+    const void* dy32 = dy;
+    const void* B32 = B;
+    const void* C32 = C;
+    if (pl.bf16) {
+      const int64_t nx = pl.B * pl.L * pl.H * pl.P, nb = pl.B * pl.L * pl.G * pl.N;
+      x32 = ws + w.x32_off;
+      dy32 = ws + w.dy32_off;
+      B32 = ws + w.b32_off;
+      C32 = ws + w.c32_off;
+      hipError_t e = ssd::launch_bwd_widen(x, (float*)x32, nx, s);
+      if (e == hipSuccess) e = ssd::launch_bwd_widen(dy, (float*)dy32, nx, s);
+      if (e == hipSuccess) e = ssd::launch_bwd_widen(B, (float*)B32, nb, s);
+      if (e == hipSuccess) e = ssd::launch_bwd_widen(C, (float*)C32, nb, s);
+      if (e != hipSuccess) return hip_status(e, "bwd_widen launch");
+    }
+    // forward stages: running sums, prepared step sizes, chunk-start states
+    hipError_t e = ssd::launch_chunk_cumsum(dt, A, Gw, dtw, pl.B, pl.L, pl.H, (int)pl.Q, pl.Lp,
+                                            pl.Lp, xfp, cfg.cumsum_heads, s);
+    if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
+    e = ssd::launch_chunk_state(0, x32, B32, Gw, dtw, Hc, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
+                                (int)pl.Q, pl.T, pl.Lp, 0, cfg.state_heads, s);
+    if (e != hipSuccess) return hip_status(e, "chunk_state launch");
+    e = ssd::launch_state_pass(0, Hc, Gw, init_state, dfinal ? fin : nullptr, pl.B, pl.H,
+                               pl.P, pl.N, (int)pl.Q, pl.T, pl.Lp, 0, 0, s);
+    if (e != hipSuccess) return hip_status(e, "state_pass launch");
+    // gradients of the chunk-boundary states: the same two stages run backwards
+    e = ssd::launch_bwd_prep(Gw, w2, Gz, pl.B, pl.H, pl.L, pl.Lp, s);
+    if (e != hipSuccess) return hip_status(e, "bwd_prep launch");
+    e = ssd::launch_chunk_state(0, dy32, C32, Gz, w2, Lam, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
+                                (int)pl.Q, pl.T, pl.Lp, 0, cfg.state_heads, s);
+    if (e != hipSuccess) return hip_status(e, "chunk_state (reverse) launch");
+    e = ssd::launch_state_pass(0, Lam, Gw, dfinal, dinit, pl.B, pl.H, pl.P, pl.N, (int)pl.Q,
+                               pl.T, pl.Lp, 0, 1, s);
+    if (e != hipSuccess) return hip_status(e, "state_pass (reverse) launch");
+    e = ssd::launch_bwd_chunks(pl.bf16, w.TB, x, B, C, dy, Gw, dtw, Hc, Lam, D, dx, Pb, Qb, dBh,
+                               dCh, dDp, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T,
+                               pl.Lp, s);
+    if (e != hipSuccess) return hip_status(e, "bwd chunk kernels launch");
+    e = ssd::launch_bwd_finish(pl.bf16, Pb, Qb, dtw, dt, A, dfinal, fin, xfp, ddt, dAp, dbp, dBh,
+                               dCh, dDp, dB, dC, dA, dD, ddt_bias, pl.B, pl.L, pl.H, pl.P, pl.N,
+                               pl.G, pl.T, pl.Lp, s);
+    return hip_status(e, "bwd finish launch");
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
   }

@@ -10,6 +10,13 @@
 // "NVIDIA CUDA Tile로 Mamba-2 순방향 전달 커널 가속화", section "세 가지 핵심 커널
 // 구현", fwd_pass_state).
 //
+// With `reverse` set the chunks are visited last to first: then the buffer
+// holding S'_c on entry holds, for chunk c, the carry before S'_c is added,
+// i.e. L_{c+1} of  L_c = exp2(G_last(c)) * L_{c+1} + S'_c  started from
+// `init_state` after the last chunk, and the fp32 carry after the first chunk
+// goes to `final_state`.  That is the backward pass's recurrence for the
+// gradient of the chunk-boundary states (bwd.hip).
+//
 // The recurrence is elementwise in the state, so every thread owns 8
 // consecutive elements of one head's state (one 16-byte piece in bf16) for
 // all chunks, keeps them in fp32 registers, and streams the chunks: the loads
@@ -41,7 +48,7 @@ template <typename T>
 __global__ void __launch_bounds__(kSpThreads)
 state_pass_kernel(T* __restrict__ S, const float* __restrict__ Gw, const float* __restrict__ init_state,
                   float* __restrict__ final_state, int H, int P, int N, int Q, int T_, int64_t ldw,
-                  int64_t SE, int frag_major) {
+                  int64_t SE, int frag_major, int reverse) {
   const int nbs = (int)((SE / 8 + kSpThreads - 1) / kSpThreads);   // blocks per state
   const int bh = blockIdx.x / nbs;
   const int64_t q = (int64_t)(blockIdx.x % nbs) * kSpThreads + threadIdx.x;   // piece index
@@ -78,7 +85,8 @@ state_pass_kernel(T* __restrict__ S, const float* __restrict__ Gw, const float* 
     float dec[kSpAhead];
 #pragma unroll
     for (int k = 0; k < kSpAhead; ++k) {
-      const int c = min(c0 + k, T_ - 1);
+      int c = min(c0 + k, T_ - 1);
+      if (reverse) c = T_ - 1 - c;
       in[k] = load_piece<T>(base + (int64_t)c * SE);
       dec[k] = glast[(int64_t)c * Q];
     }
@@ -94,7 +102,7 @@ state_pass_kernel(T* __restrict__ S, const float* __restrict__ Gw, const float* 
           o[e] = to_io<T>(h[e]);
           h[e] = a * h[e] + to_f32(s[e]);
         }
-        T* dst = base + (int64_t)(c0 + k) * SE;
+        T* dst = base + (int64_t)(reverse ? T_ - 1 - (c0 + k) : c0 + k) * SE;
 #pragma unroll
         for (int i = 0; i < (int)(8 * sizeof(T)) / 16; ++i) store16(dst + i * Vec16<T>::n, out.v[i]);
       }
@@ -109,18 +117,19 @@ state_pass_kernel(T* __restrict__ S, const float* __restrict__ Gw, const float* 
 
 hipError_t launch_state_pass(int io_bf16, void* S, const float* Gw, const float* init_state,
                              float* final_state, int64_t batch, int64_t H, int64_t P, int64_t N,
-                             int Q, int64_t T_, int64_t ldw, int frag_major, hipStream_t stream) {
+                             int Q, int64_t T_, int64_t ldw, int frag_major, int reverse,
+                             hipStream_t stream) {
   const int64_t SE = frag_major ? hc_frag(P, N).state_elems() : P * N;
   const int64_t pieces = SE / 8;
   const dim3 grid((unsigned)((pieces + kSpThreads - 1) / kSpThreads * batch * H));
   if (io_bf16)
     hipLaunchKernelGGL(state_pass_kernel<bf16>, grid, dim3(kSpThreads), 0, stream,
                        static_cast<bf16*>(S), Gw, init_state, final_state, (int)H, (int)P, (int)N,
-                       Q, (int)T_, ldw, SE, frag_major);
+                       Q, (int)T_, ldw, SE, frag_major, reverse);
   else
     hipLaunchKernelGGL(state_pass_kernel<float>, grid, dim3(kSpThreads), 0, stream,
                        static_cast<float*>(S), Gw, init_state, final_state, (int)H, (int)P, (int)N,
-                       Q, (int)T_, ldw, SE, frag_major);
+                       Q, (int)T_, ldw, SE, frag_major, reverse);
   return hipGetLastError();
 }
 

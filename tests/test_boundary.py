@@ -37,7 +37,8 @@ def test_exports_every_declared_symbol(so):
                           "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk_cumsum",
                           "ssd_fwd_states", "ssd_compute_out", "ssd_fwd_ex",
                           "ssd_chunk_cumsum_ex", "ssd_step", "ssd_fwd_states_ex",
-                          "ssd_default_config", "ssd_fwd_config", "ssd_tune"}
+                          "ssd_default_config", "ssd_fwd_config", "ssd_tune",
+                          "ssd_bwd_workspace_size", "ssd_bwd"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
@@ -47,7 +48,7 @@ def test_exports_every_declared_symbol(so):
 
 
 def test_version_and_strings(so):
-    assert lib.ssd_abi_version() == 3
+    assert lib.ssd_abi_version() == 4
     for code in range(11):
         assert lib.ssd_status_string(code) and lib.ssd_status_string(code) != "unknown status"
     assert lib.ssd_status_string(77) == "unknown status"
@@ -359,3 +360,72 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         lib.load_library()
     with pytest.raises(ImportError):
         lib.ssd_abi_version()
+
+
+# ---------------------------------------------------------------- backward
+
+BWD_REQUIRED = ("x", "dt", "A", "B", "C", "dy", "dx", "ddt", "dA", "dB", "dC", "ws")
+BWD_OPTIONAL = ("D", "init", "dfinal", "dD", "dinit", "dbias")
+
+
+def call_bwd(prob, xf=None, ws_bytes=0, **kw):
+    so = lib.load_library()
+    a = {k: FAKE for k in BWD_REQUIRED}
+    a.update({k: None for k in BWD_OPTIONAL})
+    a.update(kw)
+    return so.ssd_bwd(ctypes.byref(prob) if prob is not None else None,
+                      None if xf is None else ctypes.byref(xf), a["x"], a["dt"], a["A"], a["B"],
+                      a["C"], a["D"], a["init"], a["dy"], a["dfinal"], a["dx"], a["ddt"], a["dA"],
+                      a["dB"], a["dC"], a["dD"], a["dinit"], a["dbias"], a["ws"], ws_bytes, None)
+
+
+def bwd_ws(prob):
+    n = ctypes.c_size_t(0)
+    st = lib.load_library().ssd_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(n))
+    return st, n.value
+
+
+def test_bwd_validation_order(so):
+    for k in BWD_REQUIRED:
+        assert call_bwd(P(batch=0), **{k: None}) == NULLP, k
+    assert call_bwd(None) == NULLP
+    assert call_bwd(P(batch=0)) == SHAPE
+    assert call_bwd(P(nheads=6, ngroups=4)) == SHAPE
+    assert call_bwd(P(chunk_size=48)) == CHUNK
+    assert call_bwd(P(io_dtype=3)) == DTYPE
+    assert call_bwd(P(), XF(lo=3.0, hi=2.0)) == BADVAL
+    assert call_bwd(P(io_dtype=3), XF(lo=3.0, hi=2.0)) == DTYPE
+    for k in BWD_REQUIRED + BWD_OPTIONAL:
+        assert call_bwd(P(), **{k: FAKE + 8}) == MISAL, k
+    assert call_bwd(P(), XF(bias=FAKE + 8)) == MISAL
+    assert call_bwd(P(headdim=72)) == UNSUP
+    assert call_bwd(P(dstate=272)) == UNSUP
+    assert call_bwd(P(headdim=72), ws=FAKE + 8) == MISAL      # alignment before limits
+    st, need = bwd_ws(P())
+    assert st == OK and need > 0
+    assert call_bwd(P(), ws_bytes=need - 1) == WS
+
+
+def test_bwd_limits(so):
+    # headdim beyond 256, or tiles of headdim x dstate that do not fit the LDS
+    assert bwd_ws(P(headdim=272))[0] == UNSUP
+    assert bwd_ws(P(headdim=256, dstate=256))[0] == UNSUP
+    for pd in (dict(), dict(dstate=256), dict(headdim=128), dict(chunk_size=32),
+               dict(io_dtype=0, chunk_size=128)):
+        assert bwd_ws(P(**pd))[0] == OK, pd
+
+
+def test_bwd_workspace_formula(so):
+    # token rows (6 fp32 [batch, H, T*Q] arrays), two fp32 state sets, the
+    # final state, per-head dB/dC parts, the scalar parts and (bf16 io) fp32
+    # copies of x, dy, B and C, each 256-aligned
+    a = lambda v: (v + 255) // 256 * 256
+    for pd in (dict(), dict(io_dtype=0, seqlen=77, chunk_size=64, ngroups=1)):
+        p = P(**pd)
+        Bt, L, H, Pd, N, Q = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.chunk_size
+        T = -(-L // Q)
+        G = p.ngroups
+        wide = (2 * a(Bt * L * H * Pd * 4) + 2 * a(Bt * L * G * N * 4)) if p.io_dtype == 1 else 0
+        want = (6 * a(Bt * H * T * Q * 4) + 2 * a(Bt * H * T * Pd * N * 4) + a(Bt * H * Pd * N * 4) +
+                2 * a(Bt * L * H * N * 4) + 2 * a(Bt * H * 8) + a(Bt * T * H * 4) + wide)
+        assert bwd_ws(p) == (OK, want)

@@ -1,0 +1,160 @@
+"""GPU parity of the backward pass (ssd_bwd) against the fp64 backward oracle.
+
+Every gradient (dx, ddt, dA, dB, dC, dD, dinit and the bias gradient) is
+compared element by element with oracle.recurrence_bwd on the same seeded
+inputs and upstream gradients, at sizes that span several chunks and token
+blocks with a ragged tail, for both io dtypes, both token-block sizes (64 and
+32 rows), grouped and ungrouped B/C, with and without D, init_state and
+dfinal, and with the step-size preparation.  At the 2.7B layer shape the
+per-head gradients of two (batch, head) pairs are checked against the oracle
+run for those heads alone.
+
+Tolerances (relative L2 over the tensor; max-abs relative to max|ref|).
+Every gradient is computed in fp32 from the (exact) io values, with fp32
+chunk-boundary states; only dx, dB and dC are then stored in the io dtype.
+  dx, dB, dC, bf16 io: 5e-3 / 2e-2 -- the bf16 store alone is up to 2^-9
+      relative per element (about 1.7e-3 rel-L2 measured), as for y.
+  dx, dB, dC, fp32 io: 1e-5 / 1e-4 -- fp32 sums over a chunk of tokens and a
+      state row, and the hardware exp2 (about 1 ulp).
+  ddt, dA, dD, dinit, bias gradient (fp32 outputs, either io dtype): 1e-4 /
+      1e-3 -- as above, plus the running sum of P - dt Qr over the whole
+      sequence: accumulated in fp64, but fed by fp32 terms that largely
+      cancel (up to 2e-5 measured).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_synth
+from parity_util import errors
+
+pytestmark = pytest.mark.gpu
+
+lib = pytest.importorskip("state_space_sequence_03_amd")
+
+TOL = {"bf16": (5e-3, 2e-2), "fp32": (1e-5, 1e-4), "f32out": (1e-4, 1e-3)}
+IO_OUTPUTS = ("dx", "dB", "dC")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print("\n[gpu-case] %s" % request.node.name, flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def check(got, ref, io, what):
+    rl2, mabs = errors(got, ref)
+    tl2, tabs = TOL[io]
+    print("  %-8s rel-L2 %.2e  max-abs %.2e" % (what, rl2, mabs), flush=True)
+    assert rl2 <= tl2 and mabs <= tabs, "%s: rel-L2 %.3e (limit %.1e), max-abs %.3e (limit %.1e)" % (
+        what, rl2, tl2, mabs, tabs)
+
+
+CASES = {
+    # name: (Problem kwargs, use D, use dfinal, dt transform)
+    "bf16_q64_g2_ragged": (dict(batch=2, seqlen=300, nheads=4, headdim=32, dstate=64, ngroups=2,
+                                chunk_size=64, io_dtype="bf16", init_std=0.1), True, True, None),
+    "fp32_q128_g1": (dict(batch=1, seqlen=333, nheads=4, headdim=64, dstate=128, ngroups=1,
+                          chunk_size=128, io_dtype="fp32", init_std=0.1), True, True, None),
+    "bf16_q256_n256": (dict(batch=1, seqlen=520, nheads=2, headdim=64, dstate=256, ngroups=1,
+                            chunk_size=256, io_dtype="bf16", init_std=0.1), True, True, None),
+    "fp32_q32_no_D_init_dfinal": (dict(batch=2, seqlen=70, nheads=2, headdim=16, dstate=16,
+                                       ngroups=2, chunk_size=32, io_dtype="fp32"), False, False,
+                                  None),
+    "fp32_q64_raw_dt": (dict(batch=2, seqlen=150, nheads=4, headdim=32, dstate=32, ngroups=1,
+                             chunk_size=64, io_dtype="fp32", init_std=0.1), True, True,
+                        (True, (0.0, float("inf")))),
+    "bf16_q128_raw_dt_clamped": (dict(batch=1, seqlen=260, nheads=4, headdim=64, dstate=128,
+                                      ngroups=2, chunk_size=128, io_dtype="bf16", init_std=0.1),
+                                 True, True, (True, (0.01, 0.08))),
+}
+
+
+def run_case(p, inp, grads, use_D, use_dfinal, xform):
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    dy = grads["dy"].cuda()
+    dfinal = grads["dfinal"].cuda() if use_dfinal else None
+    D = d["D"] if use_D else None
+    kw = {}
+    dt_arg = d["dt"]
+    if xform is not None:
+        sp, lim = xform
+        kw = dict(dt_bias=d["dt_bias"], dt_softplus=sp, dt_limit=lim)
+        dt_arg = d["dt_raw"]
+    out = lib.ssd_bwd(d["x"], dt_arg, d["A"], d["B"], d["C"], D, p.chunk_size, d["init_state"],
+                      dy, dfinal, want_ddt_bias=True, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_case(p, inp, grads, use_D, use_dfinal, xform):
+    dt = inp["dt"]
+    if xform is not None:
+        sp, (lo, hi) = xform
+        dt = oracle.dt_transform(inp["dt_raw"], inp["dt_bias"], sp, lo, hi)
+    ref = oracle.recurrence_bwd(inp["x"], dt, inp["A"], inp["B"], inp["C"],
+                                inp["D"] if use_D else None, inp["init_state"], grads["dy"],
+                                grads["dfinal"] if use_dfinal else None)
+    if xform is not None:
+        sp, (lo, hi) = xform
+        ref["ddt"], ref["ddt_bias"] = oracle.dt_transform_bwd(inp["dt_raw"], ref["ddt"],
+                                                              inp["dt_bias"], sp, lo, hi)
+    else:
+        ref["ddt_bias"] = ref["ddt"].sum(axis=(0, 1))
+    return ref
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_bwd_matches_oracle(name):
+    kw, use_D, use_dfinal, xform = CASES[name]
+    p = ssd_synth.Problem(**kw)
+    inp = ssd_synth.make_inputs(p, seed=51)
+    grads = ssd_synth.make_grads(p, seed=51)
+    got = run_case(p, inp, grads, use_D, use_dfinal, xform)
+    ref = oracle_case(p, inp, grads, use_D, use_dfinal, xform)
+    for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "dinit", "ddt_bias"):
+        check(got[k], ref[k], p.io_dtype if k in IO_OUTPUTS else "f32out", k)
+
+
+def test_bwd_repeatable_and_workspace_reuse():
+    # same call twice on one caller workspace: bitwise the same results
+    kw, use_D, use_dfinal, xform = CASES["bf16_q64_g2_ragged"]
+    p = ssd_synth.Problem(**kw)
+    inp = {k: (None if v is None else v.cuda()) for k, v in ssd_synth.make_inputs(p, 52).items()}
+    g = ssd_synth.make_grads(p, 52)
+    prob = lib.make_problem(p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups,
+                            p.chunk_size, lib.SSD_BF16)
+    ws = torch.empty(lib.ssd_bwd_workspace_size(prob), dtype=torch.uint8, device="cuda")
+    args = (inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], p.chunk_size,
+            inp["init_state"], g["dy"].cuda(), g["dfinal"].cuda())
+    a = lib.ssd_bwd(*args, workspace=ws)
+    ws.fill_(0x7f)
+    b = lib.ssd_bwd(*args, workspace=ws)
+    torch.cuda.synchronize()
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
+
+
+def test_bwd_2p7b_sampled_heads():
+    # the 2.7B layer shape (batch 2, 8192 tokens, 80 heads, headdim 64, dstate
+    # 128, one group, chunk 256): per-head gradients of head 37 in both batch
+    # rows against the oracle run for those heads alone
+    p = ssd_synth.CONFIGS["mamba2_2p7b"]
+    inp = ssd_synth.make_inputs(p, seed=3)
+    grads = ssd_synth.make_grads(p, seed=3)
+    got = run_case(p, inp, grads, True, True, None)
+    h = 37
+    heads = [(0, h), (1, h)]
+    ref = oracle.recurrence_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                inp["init_state"], grads["dy"], grads["dfinal"], heads=heads)
+    for b, hh in heads:
+        check(got["dx"][b, :, hh], ref["dx"][b, :, hh], "bf16", "dx[%d]" % b)
+        check(got["ddt"][b, :, hh], ref["ddt"][b, :, hh], "f32out", "ddt[%d]" % b)
+        check(got["dinit"][b, hh], ref["dinit"][b, hh], "f32out", "dinit[%d]" % b)
+    check(got["dA"][h:h + 1], ref["dA"][h:h + 1], "f32out", "dA[h]")
+    check(got["dD"][h:h + 1], ref["dD"][h:h + 1], "f32out", "dD[h]")
+    for k in ("dB", "dC"):
+        assert torch.isfinite(got[k].float()).all(), k
