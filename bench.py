@@ -22,6 +22,9 @@ dt/A/D and a nonzero fp32 initial state.
   python bench.py --peaks            (achievable peaks on this GPU, for reference: a large
                                       bf16 GEMM through torch/hipBLASLt and a 1 GiB device copy)
 
+  python bench.py --mode bwd         (backward pass: one ssd_bwd per step, upstream gradients
+                                      dy and dfinal resident like the inputs)
+
 Decode mode: the same 2.7B-shaped layer (80 heads, headdim 64, dstate 128,
 1 group, bf16 x/B/C) at batch 128, one token per step, advancing a resident
 fp32 state in place; the kernel streams the state (read + write) and is
@@ -45,6 +48,8 @@ PEAK_FP32_MFMA = 157.3e12   # dense fp32 MFMA
 PEAK_HBM = 8.0e12           # HBM3E bytes/s
 METRIC = "SSD fwd tokens/sec (batch·seqlen) at 1 MI355X; % of bf16 MFMA roofline"
 DECODE_METRIC = "SSD decode tokens/sec (batch, one token per step) at 1 MI355X; % of HBM roofline"
+BWD_METRIC = "SSD bwd tokens/sec (batch·seqlen) at 1 MI355X; % of fp32 vector ALU roofline"
+PEAK_FP32_VALU = 157.3e12   # fp32 vector FMA: 256 CUs x 2.4 GHz x 256 flop/clk
 COPY_PROBE_BYTES = 1 << 30
 DEFAULT_WORKLOAD = "mamba2_2p7b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compute_out_{workload}_traffic.txt")
@@ -147,6 +152,105 @@ def cpu_baseline(inputs, prob, target_seconds=15.0):
                   % (nh - 1, H, prob.batch, prob.seqlen, nh, H))
     return {"value": tok_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": sample, "seconds": round(dt, 3)}
+
+
+def bwd_counts(p):
+    """Algorithmic flops of the backward pass, per (batch, chunk, head) and in
+    all: the causal chunk x chunk products C B^T and dy x^T (once each), the
+    three products with them (dx, dB, dC inside the chunk), and five chunk x
+    state products (the recomputed chunk state, the reversed one for the
+    state gradients, and the carried terms of dx, dB and dC)."""
+    Bz, L, H, P, N, Q = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.chunk_size
+    T = -(-L // Q)
+    pairs = Q * (Q + 1) // 2
+    per_unit = 2 * (pairs * (3 * N + 2 * P) + 5 * Q * P * N)
+    return dict(per_unit=per_unit, units=Bz * H * T, flops=per_unit * Bz * H * T, tokens=Bz * L)
+
+
+def bench_bwd(args):
+    import torch
+    import oracle
+    import ssd_synth
+    import state_space_sequence_03_amd as ssd
+
+    if args.workload not in ssd_synth.CONFIGS:
+        print("unknown workload %r (choose from %s)" % (args.workload, ", ".join(ssd_synth.CONFIGS)),
+              file=sys.stderr)
+        sys.exit(2)
+    prob = ssd_synth.CONFIGS[args.workload]
+    seed = ssd_synth.CONFIG_ORDER.index(args.workload)
+    inputs = ssd_synth.make_inputs(prob, seed)
+    grads = ssd_synth.make_grads(prob, seed)
+    dev = torch.device("cuda:0")
+    d = {k: (None if v is None else v.to(dev)) for k, v in inputs.items()}
+    dy, dfinal = grads["dy"].to(dev), grads["dfinal"].to(dev)
+    io = ssd.SSD_BF16 if prob.io_dtype == "bf16" else ssd.SSD_F32
+    cprob = ssd.make_problem(prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate,
+                             prob.ngroups, prob.chunk_size, io)
+    ws = torch.empty(ssd.ssd_bwd_workspace_size(cprob), dtype=torch.uint8, device=dev)
+
+    def step():
+        return ssd.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], prob.chunk_size,
+                           d["init_state"], dy, dfinal, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record()
+        step()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    ms_pass = sum(a.elapsed_time(b) for a, b in ev) / K
+    c = bwd_counts(prob)
+    achieved = c["flops"] / (ms_pass * 1e-3)
+    line = {
+        "metric": BWD_METRIC,
+        "value": c["tokens"] / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prob.io_dtype,
+        "data": "synthetic",
+        "config": {"workload": prob.name, "pass": "backward", "batch": prob.batch,
+                   "seqlen": prob.seqlen, "nheads": prob.nheads, "headdim": prob.headdim,
+                   "dstate": prob.dstate, "ngroups": prob.ngroups, "chunk_size": prob.chunk_size,
+                   "init_state": prob.init_std is not None, "dfinal": True},
+        # the whole backward call (every kernel of ssd_bwd) bracketed by events on
+        # the stream it is enqueued on; the per-kernel split is in the kernel trace
+        "roofline": {"kernel": "ssd_bwd (all kernels)", "bound": "alu",
+                     "achieved": achieved / 1e12, "peak": PEAK_FP32_VALU / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU, "traffic": None,
+                     "flops_per_unit": c["per_unit"], "units_per_launch": c["units"],
+                     "pass_ms": ms_pass},
+    }
+    if not args.no_cpu_baseline:
+        arrs = {k: (None if v is None else oracle.as_f32(v)) for k, v in inputs.items()}
+        gy, gf = oracle.as_f32(grads["dy"]), oracle.as_f32(grads["dfinal"])
+        heads, t = 0, 0.0
+        while t < 10.0 and heads < prob.batch * prob.nheads:
+            b, h = heads % prob.batch, heads // prob.batch
+            t0 = time.perf_counter()
+            oracle.recurrence_bwd(arrs["x"], arrs["dt"], arrs["A"], arrs["B"], arrs["C"],
+                                  arrs["D"], arrs["init_state"], gy, gf, heads=[(b, h)])
+            t += time.perf_counter() - t0
+            heads += 1
+        line["cpu_baseline"] = {"value": heads / (prob.batch * prob.nheads) * c["tokens"] / t,
+                                "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                "sample": "%d of the %d (batch, head) sequences, whole length, "
+                                          "scaled to all heads" % (heads, prob.batch * prob.nheads),
+                                "seconds": round(t, 3)}
+    print(json.dumps(line), flush=True)
 
 
 def decode_counts(p):
@@ -304,7 +408,7 @@ def main():
     ap.add_argument("--peaks", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one captured HIP graph of the whole pass")
-    ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill")
+    ap.add_argument("--mode", choices=("prefill", "decode", "bwd"), default="prefill")
     ap.add_argument("--tune", action="store_true",
                     help="time every valid tile choice of the forward pass (ssd_tune)")
     ap.add_argument("--raw-dt", action="store_true",
@@ -331,6 +435,9 @@ def main():
         sys.exit(1)
     if args.mode == "decode":
         bench_decode(args)
+        return
+    if args.mode == "bwd":
+        bench_bwd(args)
         return
     if args.workload not in ssd_synth.CONFIGS:
         print("unknown workload %r (choose from %s)" % (args.workload, ", ".join(ssd_synth.CONFIGS)),

@@ -141,6 +141,7 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       for (int r = 0; r < RI; ++r)
 #pragma unroll
         for (int s = 0; s < RI; ++s) cb[r][s] = gx[r][s] = 0.0f;
+      #pragma unroll 8
       for (int n = 0; n < N; ++n) {
         float cv[RI], bv[RI];
 #pragma unroll
@@ -152,6 +153,7 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 #pragma unroll
           for (int s = 0; s < RI; ++s) cb[r][s] = fmaf(cv[r], bv[s], cb[r][s]);
       }
+      #pragma unroll 8
       for (int p = 0; p < P; ++p) {
         float gv[RI], xv[RI];
 #pragma unroll
@@ -204,6 +206,7 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       float cr[NKN];
 #pragma unroll
       for (int k = 0; k < NKN; ++k) cr[k] = 0.0f;
+      #pragma unroll 8
       for (int p = 0; p < P; ++p) {
         const float gv = gs[i * ldP + p];
 #pragma unroll
@@ -301,6 +304,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       for (int s = 0; s < RI; ++s)
 #pragma unroll
         for (int r = 0; r < RI; ++r) cb[s][r] = gx[s][r] = 0.0f;
+      #pragma unroll 8
       for (int n = 0; n < N; ++n) {
         float bv[RI], cv[RI];
 #pragma unroll
@@ -312,6 +316,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 #pragma unroll
           for (int r = 0; r < RI; ++r) cb[s][r] = fmaf(bv[s], cv[r], cb[s][r]);
       }
+      #pragma unroll 8
       for (int p = 0; p < P; ++p) {
         float xv[RI], gv[RI];
 #pragma unroll
@@ -379,6 +384,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         if (k < nkp) {
           const int p = ti + 16 * k;
           float v = 0.0f;
+#pragma unroll 8
           for (int n = 0; n < N; ++n) v = fmaf(Ls[p * ldN + n], Bs[j * ldN + n], v);
           v *= e;
           dxa[s][k] += v;
@@ -391,6 +397,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         if (k < nkn) {
           const int n = ti + 16 * k;
           float v = 0.0f;
+#pragma unroll 8
           for (int p = 0; p < P; ++p) v = fmaf(Ls[p * ldN + n], xs[j * ldP + p], v);
           dba[s][k] = fmaf(e, v, dba[s][k]);
         }

@@ -47,3 +47,14 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bwd_counts_2p7b():
+    # per (batch, chunk, head): Q(Q+1)/2 causal pairs x (3N + 2P) FMAs for the
+    # chunk x chunk products, 5 Q P N for the state products; 2 flops per FMA
+    import ssd_synth
+    c = bench.bwd_counts(ssd_synth.CONFIGS["mamba2_2p7b"])
+    pairs = 256 * 257 // 2
+    assert c["per_unit"] == 2 * (pairs * (3 * 128 + 2 * 64) + 5 * 256 * 64 * 128) == 54657024
+    assert c["units"] == 2 * 80 * 32
+    assert round(c["flops"] / 1e9, 2) == 279.84

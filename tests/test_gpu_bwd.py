@@ -158,3 +158,38 @@ def test_bwd_2p7b_sampled_heads():
     check(got["dD"][h:h + 1], ref["dD"][h:h + 1], "f32out", "dD[h]")
     for k in ("dB", "dC"):
         assert torch.isfinite(got[k].float()).all(), k
+
+
+def test_bwd_2p7b_dC_dB_properties():
+    # dB and dC sum over all 80 heads of the group, too many for the oracle at
+    # this size; instead two properties that hold at any size.  The loss
+    # <dy, y> + <dfinal, final> is of degree one in C, so <C, dC> equals
+    # <dy, y - D x> (y from the fp64 forward oracle); and of degree one in
+    # (x, init) jointly, so <x, dx> + <init, dinit> equals the loss itself.
+    p = ssd_synth.CONFIGS["mamba2_2p7b"]
+    inp = ssd_synth.make_inputs(p, seed=4)
+    grads = ssd_synth.make_grads(p, seed=4)
+    got = run_case(p, inp, grads, True, True, None)
+    y, fin, _ = oracle.recurrence(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                  inp["init_state"])
+    f64 = lambda t: t.detach().double().cpu().numpy() if isinstance(t, torch.Tensor) else t
+    x, dy = f64(inp["x"]), f64(grads["dy"])
+    skip = float(np.sum(dy * f64(inp["D"])[None, None, :, None] * x))
+    loss = float(np.sum(dy * y) + np.sum(f64(grads["dfinal"]) * fin))
+
+    def bound(terms):
+        # dC and dx are stored in bf16: each element carries a rounding error
+        # of at most 2^-8 of itself, roughly uniform and independent, so the sum
+        # of the terms moves by about 2^-8 / sqrt(3) * ||terms||_2; allow six
+        # of those, plus fp32 accumulation (1e-5 of the absolute sum)
+        return 6 * 2.0 ** -8 / np.sqrt(3) * np.linalg.norm(terms) + 1e-5 * np.abs(terms).sum()
+
+    tc = f64(inp["C"]) * f64(got["dC"])
+    lhs_c, want_c = float(tc.sum()), float(np.sum(dy * y)) - skip
+    print("  <C,dC> %.6e  want %.6e  bound %.3e" % (lhs_c, want_c, bound(tc)), flush=True)
+    assert abs(lhs_c - want_c) <= bound(tc)
+    tx = x * f64(got["dx"])
+    lhs_x = float(tx.sum() + np.sum(f64(inp["init_state"]) * f64(got["dinit"])))
+    print("  <x,dx>+<init,dinit> %.6e  loss %.6e  bound %.3e" % (lhs_x, loss, bound(tx)),
+          flush=True)
+    assert abs(lhs_x - loss) <= bound(tx)
