@@ -37,7 +37,7 @@
 // over thousands of tokens, straight into ddt and dA.
 //
 // The per-chunk terms here are fp32 FMA on LDS tiles: one workgroup per
-// (chunk, head, batch) walks 64- (or 32-) token blocks of the chunk; two
+// (chunk, head, batch) walks 32-token blocks of the chunk; two
 // kernels, one for the reading side (dC, P) and one for the read side
 // (dx, dB, Qr), each keeping its outputs in registers across the pairs of
 // blocks.  dB and dC are written per head in fp32 and summed over the heads
@@ -575,15 +575,18 @@ bwd_scalars_kernel(const double* __restrict__ dApart, const double* __restrict__
 
 // ---------------------------------------------------------------- host side
 
-// Token-block rows of the per-chunk kernels: 64 when the chunk allows it and
-// the LDS plan fits, else 32; 0 if neither fits.
+// Token-block rows of the per-chunk kernels: 32, or 0 when the LDS plan for
+// this headdim and dstate does not fit.  32-row blocks keep the plan near
+// 62 KiB at headdim 64 / dstate 128, so two workgroups share a CU (two waves
+// per SIMD); 64-row blocks (4 x 4 outputs per thread, 116 KiB, one
+// workgroup per CU) measured 37.4 ms against 30.1 ms for the whole backward
+// pass at the 2.7B layer shape.
 int bwd_block_rows(int Q, int64_t P, int64_t N) {
   const int64_t lim = 160 * 1024 / 4;
-  for (int TB : {64, 32}) {
-    if (Q % TB != 0) continue;
-    if (bwd_target_floats(TB, (int)P, (int)N) <= lim && bwd_source_floats(TB, (int)P, (int)N) <= lim)
-      return TB;
-  }
+  const int TB = 32;
+  if (Q % TB == 0 && bwd_target_floats(TB, (int)P, (int)N) <= lim &&
+      bwd_source_floats(TB, (int)P, (int)N) <= lim)
+    return TB;
   return 0;
 }
 
@@ -642,10 +645,7 @@ static hipError_t launch_chunks_t(int TB, const void* x, const void* Bm, const v
                                   int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
 #define SSD_BWD_ARGS P, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh, dDpart, batch, L, \
                      H, N, G, Q, T_, ldw, stream
-  if (TB == 64) {
-    if (N <= 128) return launch_chunks_p<T, 4, 8>(SSD_BWD_ARGS);
-    return launch_chunks_p<T, 4, 16>(SSD_BWD_ARGS);
-  }
+  if (TB != 32) return hipErrorInvalidValue;
   if (N <= 128) return launch_chunks_p<T, 2, 8>(SSD_BWD_ARGS);
   return launch_chunks_p<T, 2, 16>(SSD_BWD_ARGS);
 #undef SSD_BWD_ARGS

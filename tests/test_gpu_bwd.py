@@ -3,8 +3,8 @@
 Every gradient (dx, ddt, dA, dB, dC, dD, dinit and the bias gradient) is
 compared element by element with oracle.recurrence_bwd on the same seeded
 inputs and upstream gradients, at sizes that span several chunks and token
-blocks with a ragged tail, for both io dtypes, both token-block sizes (64 and
-32 rows), grouped and ungrouped B/C, with and without D, init_state and
+blocks with a ragged tail, for both io dtypes, dstate up to 256, chunk sizes
+32 to 256, grouped and ungrouped B/C, with and without D, init_state and
 dfinal, and with the step-size preparation.  At the 2.7B layer shape the
 per-head gradients of two (batch, head) pairs are checked against the oracle
 run for those heads alone.

@@ -105,3 +105,41 @@ def test_decode_step_replays_from_a_graph():
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(state, eager) and torch.equal(y, y_eager)
+
+
+def test_backward_pass_replays_from_a_graph():
+    # ssd_bwd enqueues kernels only as well: captured once (outputs and
+    # workspace from the graph's pool), every replay equals the eager call
+    p = ssd_synth.Problem(batch=2, seqlen=300, nheads=4, headdim=32, dstate=64, ngroups=2,
+                          chunk_size=64, io_dtype="bf16", init_std=0.1)
+    inp = ssd_synth.make_inputs(p, seed=53)
+    gr = ssd_synth.make_grads(p, seed=53)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    dy, dfinal = gr["dy"].cuda(), gr["dfinal"].cuda()
+
+    def bwd():
+        return lib.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], p.chunk_size,
+                           d["init_state"], dy, dfinal, want_ddt_bias=True)
+
+    eager = bwd()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bwd()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = bwd()
+    ref = oracle.recurrence_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                inp["init_state"], gr["dy"], gr["dfinal"])
+    for rep in range(3):
+        for t in out.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(out[k], eager[k]), "%s (replay %d)" % (k, rep)
+        assert_close(out["dx"], ref["dx"], "bf16", "dx (replay %d)" % rep)
+        _ = (d["x"].float() * 2.0).sum().item()
