@@ -36,40 +36,63 @@
 // terms that largely cancel, and bf16 states would put their rounding, summed
 // over thousands of tokens, straight into ddt and dA.
 //
-// The per-chunk terms here are fp32 FMA on LDS tiles: one workgroup per
-// (chunk, head, batch) walks 32-token blocks of the chunk; two
-// kernels, one for the reading side (dC, P) and one for the read side
-// (dx, dB, Qr), each keeping its outputs in registers across the pairs of
-// blocks.  dB and dC are written per head in fp32 and summed over the heads
-// of a group by a final pass.
+// The per-chunk terms: one workgroup per (chunk, head, batch) walks 32-token
+// blocks of the chunk; two kernels, one for the reading side (dC, P) and one
+// for the read side (dx, dB, Qr), each keeping its outputs in registers
+// across the pairs of blocks.  The chunk x chunk products C B^T and dy x^T
+// run on MFMA from io-dtype LDS tiles (bf16 operands are exact and the sums
+// fp32; fp32 io uses the fp32 MFMA), the products with the fp32 weights and
+// the carried terms on the vector ALU.  dB and dC are written per head in
+// fp32 and summed over the heads of a group by a final pass.
 #include "ssd_device.hpp"
 
 namespace ssd {
 
 constexpr int kBwdThreads = 256;
 
-// LDS floats of the two per-chunk kernels for a token block of TB rows
-// (rows padded by one float against bank conflicts).
-__host__ __device__ inline int bwd_union_floats(int TB, int P, int N) {
-  const int a = TB * (N + 1) + TB * (P + 1);
-  const int b = P * (N + 1);
+constexpr int kBwdTB = 32;   // token rows per block of a chunk
+constexpr int kBwdPH = 16;   // state rows per pass of the carried terms
+
+// io-dtype tiles in LDS: rows of K values, K rounded up to whole 32-value MFMA
+// K-steps (zero-filled) plus 16 bytes against bank conflicts.
+__host__ __device__ inline int round32(int v) { return (v + 31) / 32 * 32; }
+template <typename T>
+__host__ __device__ inline int tile_ld(int K) { return round32(K) + 16 / (int)sizeof(T); }
+
+// LDS bytes of the two per-chunk kernels (every region a multiple of 16 bytes)
+template <typename T>
+__host__ __device__ inline int bwd_pair_bytes(int P, int N) {   // two io tiles: N- and P-wide
+  return kBwdTB * (tile_ld<T>(N) + tile_ld<T>(P)) * (int)sizeof(T);
+}
+template <typename T>
+__host__ __device__ inline int bwd_union_bytes(int P, int N) {  // second pair, or a state pass
+  const int a = bwd_pair_bytes<T>(P, N), b = (kBwdPH * (N + 1) * 4 + 15) / 16 * 16;
   return a > b ? a : b;
 }
-__host__ __device__ inline int bwd_target_floats(int TB, int P, int N) {
-  return TB * (N + 1) + TB * (P + 1) + bwd_union_floats(TB, P, N) + TB * (TB + 1) + 2 * TB;
+template <typename T>
+__host__ __device__ inline int bwd_target_bytes(int P, int N) {
+  return bwd_pair_bytes<T>(P, N) + bwd_union_bytes<T>(P, N) + kBwdTB * (kBwdTB + 1) * 4 +
+         5 * kBwdTB * 4;
 }
-__host__ __device__ inline int bwd_source_floats(int TB, int P, int N) {
-  return TB * (N + 1) + TB * (P + 1) + bwd_union_floats(TB, P, N) + 2 * TB * (TB + 1) + 3 * TB + 8;
+template <typename T>
+__host__ __device__ inline int bwd_source_bytes(int P, int N) {
+  return bwd_pair_bytes<T>(P, N) + bwd_union_bytes<T>(P, N) + 2 * kBwdTB * (kBwdTB + 1) * 4 +
+         6 * kBwdTB * 4 + 8 * 4;
 }
 
-// rows x cols io elements (rows `row_stride` apart) into LDS as fp32 rows of
-// `ld` floats; rows at or past `rows_valid` are zero.
+// rows x K io elements (rows `row_stride` apart) into an LDS tile of row
+// stride ld, as 16-byte pieces; rows at or past `rows_valid` and the columns
+// from K to the next multiple of 32 are zero.
 template <typename T>
-__device__ __forceinline__ void tile_to_lds(float* dst, int ld, const T* src, int64_t row_stride,
-                                            int rows_valid, int rows, int cols) {
-  for (int e = threadIdx.x; e < rows * cols; e += kBwdThreads) {
-    const int r = e / cols, c = e % cols;
-    dst[r * ld + c] = r < rows_valid ? to_f32(src[r * row_stride + c]) : 0.0f;
+__device__ __forceinline__ void tile_to_lds(T* dst, int ld, const T* src, int64_t row_stride,
+                                            int rows_valid, int rows, int K) {
+  constexpr int V = 16 / sizeof(T);
+  const int KC = round32(K) / V;
+  for (int e = threadIdx.x; e < rows * KC; e += kBwdThreads) {
+    const int r = e / KC, c = (e % KC) * V;
+    vec16 v = zero16();
+    if (r < rows_valid && c < K) v = load16(src + r * row_stride + c);
+    store16(dst + r * ld + c, v);
   }
 }
 
@@ -84,32 +107,53 @@ __device__ __forceinline__ int valid_rows(int64_t L, int64_t t0, int TB) {
   return v <= 0 ? 0 : (v >= TB ? TB : (int)v);
 }
 
+// 16x16 tile of  sum_k A[row][k] B[col][k]  over K (a multiple of 32 after
+// padding) for one wave: A rows a0.., B rows b0.. of io tiles with row stride
+// ld.  The accumulator holds, in lane l, column l % 16 and rows 4 (l / 16) + r.
+template <typename T>
+__device__ __forceinline__ floatx4 tile_dot(const T* A, const T* B, int ld, int K, int lane) {
+  const T* pa = A + (lane & 15) * ld + 8 * (lane >> 4);
+  const T* pb = B + (lane & 15) * ld + 8 * (lane >> 4);
+  floatx4 c = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < K; k0 += 32) c = mma(c, load_frag(pa + k0), load_frag(pb + k0));
+  return c;
+}
+
 // Reading side: dC (per head, fp32) and P for every token of one chunk.
-template <typename T, int RI, int NKN>
+// Block pairs (I, J <= I) of 32 tokens: the two 32x32 products C B^T and
+// dy x^T on MFMA (one 16x16 tile of each per wave; the io values are exact
+// MFMA operands and the sums are fp32), W = mask exp2(G_i - G_j) dt_j (dy.x)
+// to LDS, then dC += W B on the vector ALU (2 rows x N/16 columns per
+// thread).  The carried term streams H_c through LDS 16 state rows at a time.
+template <typename T, int NKN>
 __global__ void __launch_bounds__(kBwdThreads)
 bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
                   const T* __restrict__ dy, const float* __restrict__ Gw,
                   const float* __restrict__ dtw, const float* __restrict__ Hc,
                   float* __restrict__ Pout, float* __restrict__ dCh, int64_t L, int H, int P,
                   int N, int G, int hpg, int Q, int T_, int64_t ldw) {
-  constexpr int TB = 16 * RI;
-  extern __shared__ float sm[];
+  constexpr int TB = kBwdTB, RI = 2, ldW = TB + 1;
+  extern __shared__ __align__(16) unsigned char smem[];
   const int c = blockIdx.x, h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int g = h / hpg;
   const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
-  const int ldN = N + 1, ldP = P + 1, ldW = TB + 1;
-  float* Cs = sm;
-  float* gs = Cs + TB * ldN;
-  float* U = gs + TB * ldP;
-  float* Bs = U;
-  float* xs = U + TB * ldN;
-  float* Hs = U;
-  float* Ws = U + bwd_union_floats(TB, P, N);
+  const int lane = tid % kWave, wv = tid / kWave, ti2 = wv >> 1, tj2 = wv & 1;
+  const int ldN = tile_ld<T>(N), ldP = tile_ld<T>(P), NR = round32(N), PR = round32(P);
+  T* Ct = reinterpret_cast<T*>(smem);
+  T* gt = Ct + TB * ldN;
+  unsigned char* U = smem + bwd_pair_bytes<T>(P, N);
+  T* Bt = reinterpret_cast<T*>(U);
+  T* xt = Bt + TB * ldN;
+  float* Hs = reinterpret_cast<float*>(U);
+  float* Ws = reinterpret_cast<float*>(U + bwd_union_bytes<T>(P, N));
   float* Gi = Ws + TB * ldW;
   float* Gj = Gi + TB;
+  float* Pp = Gj + TB;          // [2][TB]
+  float* Pacc = Pp + 2 * TB;
   const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
   const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
+  const float* Hrow = Hc + ((b * H + h) * T_ + c) * (int64_t)P * N;
   const int nb = Q / TB, nk = N / 16;
 
   for (int I = 0; I < nb; ++I) {
@@ -117,125 +161,114 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
     const int vi = valid_rows(L, ti0, TB);
     if (vi == 0) break;                       // the rest of the chunk is padding
     __syncthreads();
-    tile_to_lds(Cs, ldN, Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, TB, N);
-    tile_to_lds(gs, ldP, dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, TB, P);
-    if (tid < TB) Gi[tid] = Grow[I * TB + tid];
-    float acc[RI][NKN], pacc[RI];
+    tile_to_lds(Ct, ldN, Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, TB, N);
+    tile_to_lds(gt, ldP, dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, TB, P);
+    if (tid < TB) {
+      Gi[tid] = Grow[I * TB + tid];
+      Pacc[tid] = 0.0f;
+    }
+    float acc[RI][NKN];
 #pragma unroll
-    for (int r = 0; r < RI; ++r) {
-      pacc[r] = 0.0f;
+    for (int r = 0; r < RI; ++r)
 #pragma unroll
       for (int k = 0; k < NKN; ++k) acc[r][k] = 0.0f;
-    }
     for (int J = 0; J <= I; ++J) {
       const int64_t tj0 = (int64_t)c * Q + J * TB;
       const int vj = valid_rows(L, tj0, TB);
       __syncthreads();
-      tile_to_lds(Bs, ldN, Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, TB, N);
-      tile_to_lds(xs, ldP, x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, TB, P);
+      tile_to_lds(Bt, ldN, Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, TB, N);
+      tile_to_lds(xt, ldP, x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, TB, P);
       if (tid < TB) Gj[tid] = Grow[J * TB + tid];
       __syncthreads();
-      // rows i = ti*RI + r, columns j = tj*RI + s of the block pair
-      float cb[RI][RI], gx[RI][RI];
+      // this wave's tile: rows i = 16 ti2 + 4 (lane / 16) + r, column j = 16 tj2 + lane % 16
+      const floatx4 cb = tile_dot(Ct + 16 * ti2 * ldN, Bt + 16 * tj2 * ldN, ldN, NR, lane);
+      const floatx4 gx = tile_dot(gt + 16 * ti2 * ldP, xt + 16 * tj2 * ldP, ldP, PR, lane);
+      const int j = 16 * tj2 + (lane & 15);
+      const float dj = drow[J * TB + j];
 #pragma unroll
-      for (int r = 0; r < RI; ++r)
-#pragma unroll
-        for (int s = 0; s < RI; ++s) cb[r][s] = gx[r][s] = 0.0f;
-      #pragma unroll 8
-      for (int n = 0; n < N; ++n) {
-        float cv[RI], bv[RI];
-#pragma unroll
-        for (int r = 0; r < RI; ++r) cv[r] = Cs[(ti * RI + r) * ldN + n];
-#pragma unroll
-        for (int s = 0; s < RI; ++s) bv[s] = Bs[(tj * RI + s) * ldN + n];
-#pragma unroll
-        for (int r = 0; r < RI; ++r)
-#pragma unroll
-          for (int s = 0; s < RI; ++s) cb[r][s] = fmaf(cv[r], bv[s], cb[r][s]);
-      }
-      #pragma unroll 8
-      for (int p = 0; p < P; ++p) {
-        float gv[RI], xv[RI];
-#pragma unroll
-        for (int r = 0; r < RI; ++r) gv[r] = gs[(ti * RI + r) * ldP + p];
-#pragma unroll
-        for (int s = 0; s < RI; ++s) xv[s] = xs[(tj * RI + s) * ldP + p];
-#pragma unroll
-        for (int r = 0; r < RI; ++r)
-#pragma unroll
-          for (int s = 0; s < RI; ++s) gx[r][s] = fmaf(gv[r], xv[s], gx[r][s]);
-      }
-#pragma unroll
-      for (int r = 0; r < RI; ++r) {
-        const int i = ti * RI + r;
-        float pr = 0.0f;
-#pragma unroll
-        for (int s = 0; s < RI; ++s) {
-          const int j = tj * RI + s;
-          const bool on = J < I || j <= i;
-          // the mask is applied before exp2, so no masked entry is evaluated
-          const float w = on ? fast_exp2(Gi[i] - Gj[j]) * drow[J * TB + j] * gx[r][s] : 0.0f;
-          Ws[i * ldW + j] = w;
-          pr = fmaf(w, cb[r][s], pr);
-        }
-        pacc[r] += sum16(pr);
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti2 + 4 * (lane >> 4) + r;
+        const bool on = J < I || j <= i;
+        // the mask is applied before exp2, so no masked entry is evaluated
+        const float w = on ? fast_exp2(Gi[i] - Gj[j]) * dj * gx[r] : 0.0f;
+        Ws[i * ldW + j] = w;
+        const float pr = sum16(w * cb[r]);
+        if ((lane & 15) == 0) Pp[tj2 * TB + i] = pr;
       }
       __syncthreads();
-      for (int j = 0; j < TB; ++j) {
-        float wv[RI];
+      if (tid < TB) Pacc[tid] += Pp[tid] + Pp[TB + tid];
+#pragma unroll 4
+      for (int jj = 0; jj < TB; ++jj) {
+        float wr[RI];
 #pragma unroll
-        for (int r = 0; r < RI; ++r) wv[r] = Ws[(ti * RI + r) * ldW + j];
+        for (int r = 0; r < RI; ++r) wr[r] = Ws[(ti * RI + r) * ldW + jj];
 #pragma unroll
         for (int k = 0; k < NKN; ++k) {
           if (k < nk) {
-            const float bv = Bs[j * ldN + tj + 16 * k];
+            const float bv = to_f32(Bt[jj * ldN + tj + 16 * k]);
 #pragma unroll
-            for (int r = 0; r < RI; ++r) acc[r][k] = fmaf(wv[r], bv, acc[r][k]);
+            for (int r = 0; r < RI; ++r) acc[r][k] = fmaf(wr[r], bv, acc[r][k]);
           }
         }
       }
     }
-    // carried term: exp2(G_i) H_c^T dy_i, and its share of P_i
-    __syncthreads();
-    tile_to_lds(Hs, ldN, Hc + ((b * H + h) * T_ + c) * (int64_t)P * N, (int64_t)N, P, P, N);
-    __syncthreads();
+    // carried term exp2(G_i) H_c^T dy_i, H_c streamed 16 state rows at a time
+    float cr[RI][NKN];
+#pragma unroll
+    for (int r = 0; r < RI; ++r)
+#pragma unroll
+      for (int k = 0; k < NKN; ++k) cr[r][k] = 0.0f;
+    for (int p0 = 0; p0 < P; p0 += kBwdPH) {
+      __syncthreads();
+      for (int e = tid; e < kBwdPH * N; e += kBwdThreads)
+        Hs[(e / N) * (N + 1) + e % N] = Hrow[(int64_t)p0 * N + e];
+      __syncthreads();
+#pragma unroll 4
+      for (int pp = 0; pp < kBwdPH; ++pp) {
+        float gv[RI];
+#pragma unroll
+        for (int r = 0; r < RI; ++r) gv[r] = to_f32(gt[(ti * RI + r) * ldP + p0 + pp]);
+#pragma unroll
+        for (int k = 0; k < NKN; ++k) {
+          if (k < nk) {
+            const float hv = Hs[pp * (N + 1) + tj + 16 * k];
+#pragma unroll
+            for (int r = 0; r < RI; ++r) cr[r][k] = fmaf(gv[r], hv, cr[r][k]);
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int r = 0; r < RI; ++r) {
       const int i = ti * RI + r;
       const float e = fast_exp2(Gi[i]);
-      float cr[NKN];
-#pragma unroll
-      for (int k = 0; k < NKN; ++k) cr[k] = 0.0f;
-      #pragma unroll 8
-      for (int p = 0; p < P; ++p) {
-        const float gv = gs[i * ldP + p];
-#pragma unroll
-        for (int k = 0; k < NKN; ++k)
-          if (k < nk) cr[k] = fmaf(gv, Hs[p * ldN + tj + 16 * k], cr[k]);
-      }
       float pc = 0.0f;
 #pragma unroll
       for (int k = 0; k < NKN; ++k) {
         if (k < nk) {
-          const float v = e * cr[k];
+          const float v = e * cr[r][k];
           acc[r][k] += v;
-          pc = fmaf(v, Cs[i * ldN + tj + 16 * k], pc);
+          pc = fmaf(v, to_f32(Ct[i * ldN + tj + 16 * k]), pc);
         }
       }
-      pacc[r] += sum16(pc);
+      pc = sum16(pc);
       if (i < vi) {
         float* dst = dCh + ((b * L + ti0 + i) * H + h) * (int64_t)N;
 #pragma unroll
         for (int k = 0; k < NKN; ++k)
           if (k < nk) dst[tj + 16 * k] = acc[r][k];
-        if (tj == 0) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + i] = pacc[r];
+        if (tj == 0) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + i] = Pacc[i] + pc;
       }
     }
   }
 }
 
-// Read side: dx, dB (per head, fp32), Qr and the chunk's share of dD.
-template <typename T, int RI, int NKN, int NKP>
+// Read side: dx, dB (per head, fp32), Qr and the chunk's share of dD.  Block
+// pairs (J, I >= J): B C^T and x dy^T on MFMA as above, U = mask exp2(G_i -
+// G_j) (C.B) and V = mask exp2(G_i - G_j) (dy.x) to LDS, then dx += U^T dy and
+// dB += V^T C on the vector ALU; the carried terms stream L_{c+1} through LDS
+// 16 state rows at a time.
+template <typename T, int NKN, int NKP>
 __global__ void __launch_bounds__(kBwdThreads)
 bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
                   const T* __restrict__ dy, const float* __restrict__ Gw,
@@ -243,27 +276,31 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
                   const float* __restrict__ Dv, T* __restrict__ dx, float* __restrict__ dBh,
                   float* __restrict__ Qout, float* __restrict__ dDpart, int64_t L, int H, int P,
                   int N, int G, int hpg, int Q, int T_, int64_t ldw) {
-  constexpr int TB = 16 * RI;
-  extern __shared__ float sm[];
+  constexpr int TB = kBwdTB, RI = 2, ldW = TB + 1;
+  extern __shared__ __align__(16) unsigned char smem[];
   const int c = blockIdx.x, h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int g = h / hpg;
   const int tid = threadIdx.x, tj = tid / 16, ti = tid % 16;
-  const int ldN = N + 1, ldP = P + 1, ldW = TB + 1;
-  float* Bs = sm;
-  float* xs = Bs + TB * ldN;
-  float* U = xs + TB * ldP;
-  float* Cs = U;
-  float* gs = U + TB * ldN;
-  float* Ls = U;
-  float* Us = U + bwd_union_floats(TB, P, N);
+  const int lane = tid % kWave, wv = tid / kWave, tj2 = wv >> 1, ti2 = wv & 1;
+  const int ldN = tile_ld<T>(N), ldP = tile_ld<T>(P), NR = round32(N), PR = round32(P);
+  T* Bt = reinterpret_cast<T*>(smem);
+  T* xt = Bt + TB * ldN;
+  unsigned char* U = smem + bwd_pair_bytes<T>(P, N);
+  T* Ct = reinterpret_cast<T*>(U);
+  T* gt = Ct + TB * ldN;
+  float* Ls = reinterpret_cast<float*>(U);
+  float* Us = reinterpret_cast<float*>(U + bwd_union_bytes<T>(P, N));
   float* Vs = Us + TB * ldW;
   float* Gi = Vs + TB * ldW;
   float* Gj = Gi + TB;
   float* dj = Gj + TB;
-  float* red = dj + TB;
+  float* Qp = dj + TB;          // [2][TB]
+  float* Qacc = Qp + 2 * TB;
+  float* red = Qacc + TB;
   const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
   const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
+  const float* Lrow = Lam + ((b * H + h) * T_ + c) * (int64_t)P * N;
   const int nb = Q / TB, nkn = N / 16, nkp = P / 16;
   const float Dh = Dv ? Dv[h] : 0.0f;
   const float Gl = Grow[Q - 1];
@@ -274,16 +311,16 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
     const int vj = valid_rows(L, tj0, TB);
     if (vj == 0) break;
     __syncthreads();
-    tile_to_lds(Bs, ldN, Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, TB, N);
-    tile_to_lds(xs, ldP, x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, TB, P);
+    tile_to_lds(Bt, ldN, Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, TB, N);
+    tile_to_lds(xt, ldP, x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, TB, P);
     if (tid < TB) {
       Gj[tid] = Grow[J * TB + tid];
       dj[tid] = drow[J * TB + tid];
+      Qacc[tid] = 0.0f;
     }
-    float dba[RI][NKN], dxa[RI][NKP], qa[RI];
+    float dba[RI][NKN], dxa[RI][NKP];
 #pragma unroll
     for (int s = 0; s < RI; ++s) {
-      qa[s] = 0.0f;
 #pragma unroll
       for (int k = 0; k < NKN; ++k) dba[s][k] = 0.0f;
 #pragma unroll
@@ -294,68 +331,39 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       const int vi = valid_rows(L, ti0, TB);
       if (vi == 0) break;
       __syncthreads();
-      tile_to_lds(Cs, ldN, Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, TB, N);
-      tile_to_lds(gs, ldP, dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, TB, P);
+      tile_to_lds(Ct, ldN, Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, TB, N);
+      tile_to_lds(gt, ldP, dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, TB, P);
       if (tid < TB) Gi[tid] = Grow[I * TB + tid];
       __syncthreads();
-      // rows j = tj*RI + s (read), columns i = ti*RI + r (reading)
-      float cb[RI][RI], gx[RI][RI];
+      // this wave's tile: rows j = 16 tj2 + 4 (lane / 16) + r, column i = 16 ti2 + lane % 16
+      const floatx4 cb = tile_dot(Bt + 16 * tj2 * ldN, Ct + 16 * ti2 * ldN, ldN, NR, lane);
+      const floatx4 gx = tile_dot(xt + 16 * tj2 * ldP, gt + 16 * ti2 * ldP, ldP, PR, lane);
+      const int i = 16 * ti2 + (lane & 15);
 #pragma unroll
-      for (int s = 0; s < RI; ++s)
-#pragma unroll
-        for (int r = 0; r < RI; ++r) cb[s][r] = gx[s][r] = 0.0f;
-      #pragma unroll 8
-      for (int n = 0; n < N; ++n) {
-        float bv[RI], cv[RI];
-#pragma unroll
-        for (int s = 0; s < RI; ++s) bv[s] = Bs[(tj * RI + s) * ldN + n];
-#pragma unroll
-        for (int r = 0; r < RI; ++r) cv[r] = Cs[(ti * RI + r) * ldN + n];
-#pragma unroll
-        for (int s = 0; s < RI; ++s)
-#pragma unroll
-          for (int r = 0; r < RI; ++r) cb[s][r] = fmaf(bv[s], cv[r], cb[s][r]);
-      }
-      #pragma unroll 8
-      for (int p = 0; p < P; ++p) {
-        float xv[RI], gv[RI];
-#pragma unroll
-        for (int s = 0; s < RI; ++s) xv[s] = xs[(tj * RI + s) * ldP + p];
-#pragma unroll
-        for (int r = 0; r < RI; ++r) gv[r] = gs[(ti * RI + r) * ldP + p];
-#pragma unroll
-        for (int s = 0; s < RI; ++s)
-#pragma unroll
-          for (int r = 0; r < RI; ++r) gx[s][r] = fmaf(xv[s], gv[r], gx[s][r]);
-      }
-#pragma unroll
-      for (int s = 0; s < RI; ++s) {
-        const int j = tj * RI + s;
-        float qr = 0.0f;
-#pragma unroll
-        for (int r = 0; r < RI; ++r) {
-          const int i = ti * RI + r;
-          const bool on = I > J || j <= i;
-          const float a = on ? fast_exp2(Gi[i] - Gj[j]) : 0.0f;
-          const float u = a * cb[s][r];
-          Us[j * ldW + i] = u;
-          Vs[j * ldW + i] = a * gx[s][r];
-          qr = fmaf(u, gx[s][r], qr);
-        }
-        qa[s] += sum16(qr);
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * tj2 + 4 * (lane >> 4) + r;
+        const bool on = I > J || j <= i;
+        const float a = on ? fast_exp2(Gi[i] - Gj[j]) : 0.0f;
+        const float u = a * cb[r];
+        Us[j * ldW + i] = u;
+        Vs[j * ldW + i] = a * gx[r];
+        const float q = sum16(u * gx[r]);
+        if ((lane & 15) == 0) Qp[ti2 * TB + j] = q;
       }
       __syncthreads();
-      for (int i = 0; i < TB; ++i) {
+      if (tid < TB) Qacc[tid] += Qp[tid] + Qp[TB + tid];
+#pragma unroll 4
+      for (int ii = 0; ii < TB; ++ii) {
         float uv[RI], vv[RI];
 #pragma unroll
         for (int s = 0; s < RI; ++s) {
-          uv[s] = Us[(tj * RI + s) * ldW + i];
-          vv[s] = Vs[(tj * RI + s) * ldW + i];
+          uv[s] = Us[(tj * RI + s) * ldW + ii];
+          vv[s] = Vs[(tj * RI + s) * ldW + ii];
         }
 #pragma unroll
         for (int k = 0; k < NKN; ++k) {
           if (k < nkn) {
-            const float cv = Cs[i * ldN + ti + 16 * k];
+            const float cv = to_f32(Ct[ii * ldN + ti + 16 * k]);
 #pragma unroll
             for (int s = 0; s < RI; ++s) dba[s][k] = fmaf(vv[s], cv, dba[s][k]);
           }
@@ -363,45 +371,59 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 #pragma unroll
         for (int k = 0; k < NKP; ++k) {
           if (k < nkp) {
-            const float gv = gs[i * ldP + ti + 16 * k];
+            const float gv = to_f32(gt[ii * ldP + ti + 16 * k]);
 #pragma unroll
             for (int s = 0; s < RI; ++s) dxa[s][k] = fmaf(uv[s], gv, dxa[s][k]);
           }
         }
       }
     }
-    // carried term from the gradient of the state leaving the chunk
-    __syncthreads();
-    tile_to_lds(Ls, ldN, Lam + ((b * H + h) * T_ + c) * (int64_t)P * N, (int64_t)N, P, P, N);
-    __syncthreads();
+    // carried terms from L_{c+1}, streamed 16 state rows at a time: pass p0
+    // holds rows p0 .. p0+15, so lane ti's row p = p0 + ti is its k = p0/16
+    // column of dx, and every pass adds its rows' share of dB
+    float e[RI], qx[RI];
+#pragma unroll
+    for (int s = 0; s < RI; ++s) {
+      e[s] = fast_exp2(Gl - Gj[tj * RI + s]);
+      qx[s] = 0.0f;
+    }
+    for (int p0 = 0; p0 < P; p0 += kBwdPH) {
+      __syncthreads();
+      for (int q = tid; q < kBwdPH * N; q += kBwdThreads)
+        Ls[(q / N) * (N + 1) + q % N] = Lrow[(int64_t)p0 * N + q];
+      __syncthreads();
+      const int kp = p0 / kBwdPH;
+#pragma unroll
+      for (int s = 0; s < RI; ++s) {
+        const int j = tj * RI + s;
+        float v = 0.0f;
+#pragma unroll 8
+        for (int n = 0; n < N; ++n) v = fmaf(Ls[ti * (N + 1) + n], to_f32(Bt[j * ldN + n]), v);
+        v *= e[s];
+#pragma unroll
+        for (int k = 0; k < NKP; ++k)
+          if (k == kp) dxa[s][k] += v;
+        qx[s] = fmaf(to_f32(xt[j * ldP + p0 + ti]), v, qx[s]);
+      }
+#pragma unroll 4
+      for (int pp = 0; pp < kBwdPH; ++pp) {
+        float xv[RI];
+#pragma unroll
+        for (int s = 0; s < RI; ++s) xv[s] = e[s] * to_f32(xt[(tj * RI + s) * ldP + p0 + pp]);
+#pragma unroll
+        for (int k = 0; k < NKN; ++k) {
+          if (k < nkn) {
+            const float lv = Ls[pp * (N + 1) + ti + 16 * k];
+#pragma unroll
+            for (int s = 0; s < RI; ++s) dba[s][k] = fmaf(xv[s], lv, dba[s][k]);
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int s = 0; s < RI; ++s) {
       const int j = tj * RI + s;
-      const float e = fast_exp2(Gl - Gj[j]);
-      float qx = 0.0f;
-#pragma unroll
-      for (int k = 0; k < NKP; ++k) {
-        if (k < nkp) {
-          const int p = ti + 16 * k;
-          float v = 0.0f;
-#pragma unroll 8
-          for (int n = 0; n < N; ++n) v = fmaf(Ls[p * ldN + n], Bs[j * ldN + n], v);
-          v *= e;
-          dxa[s][k] += v;
-          qx = fmaf(xs[j * ldP + p], v, qx);
-        }
-      }
-      qa[s] += sum16(qx);
-#pragma unroll
-      for (int k = 0; k < NKN; ++k) {
-        if (k < nkn) {
-          const int n = ti + 16 * k;
-          float v = 0.0f;
-#pragma unroll 8
-          for (int p = 0; p < P; ++p) v = fmaf(Ls[p * ldN + n], xs[j * ldP + p], v);
-          dba[s][k] = fmaf(e, v, dba[s][k]);
-        }
-      }
+      const float q = sum16(qx[s]);
       if (j < vj) {
         const int64_t t = tj0 + j;
         const float d = dj[j];
@@ -412,13 +434,13 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
             const int p = ti + 16 * k;
             const float gv = to_f32(dy[row * P + p]);
             dx[row * P + p] = to_io<T>(fmaf(d, dxa[s][k], Dh * gv));
-            dsum = fmaf(gv, xs[j * ldP + p], dsum);
+            dsum = fmaf(gv, to_f32(xt[j * ldP + p]), dsum);
           }
         }
 #pragma unroll
         for (int k = 0; k < NKN; ++k)
           if (k < nkn) dBh[row * N + ti + 16 * k] = d * dba[s][k];
-        if (ti == 0) Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + j] = qa[s];
+        if (ti == 0) Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + j] = Qacc[j] + q;
       }
     }
   }
@@ -575,45 +597,40 @@ bwd_scalars_kernel(const double* __restrict__ dApart, const double* __restrict__
 
 // ---------------------------------------------------------------- host side
 
-// Token-block rows of the per-chunk kernels: 32, or 0 when the LDS plan for
-// this headdim and dstate does not fit.  32-row blocks keep the plan near
-// 62 KiB at headdim 64 / dstate 128, so two workgroups share a CU (two waves
-// per SIMD); 64-row blocks (4 x 4 outputs per thread, 116 KiB, one
-// workgroup per CU) measured 37.4 ms against 30.1 ms for the whole backward
-// pass at the 2.7B layer shape.
-int bwd_block_rows(int Q, int64_t P, int64_t N) {
-  const int64_t lim = 160 * 1024 / 4;
-  const int TB = 32;
-  if (Q % TB == 0 && bwd_target_floats(TB, (int)P, (int)N) <= lim &&
-      bwd_source_floats(TB, (int)P, (int)N) <= lim)
-    return TB;
-  return 0;
+// Token-block rows of the per-chunk kernels: 32, or 0 when their LDS plan
+// for this headdim and dstate does not fit.  The plans are ~31 and ~35 KiB at
+// headdim 64 / dstate 128 in bf16, so four workgroups share a CU.
+int bwd_block_rows(int io_bf16, int Q, int64_t P, int64_t N) {
+  const int lim = 160 * 1024;
+  if (Q % kBwdTB != 0 || P > 256 || N > 256) return 0;
+  const int a = io_bf16 ? bwd_target_bytes<bf16>((int)P, (int)N) : bwd_target_bytes<float>((int)P, (int)N);
+  const int s = io_bf16 ? bwd_source_bytes<bf16>((int)P, (int)N) : bwd_source_bytes<float>((int)P, (int)N);
+  return a <= lim && s <= lim ? kBwdTB : 0;
 }
 
-template <typename T, int RI, int NKN, int NKP>
+template <typename T, int NKN, int NKP>
 static hipError_t launch_chunks(const void* x, const void* Bm, const void* Cm, const void* dy,
                                 const float* Gw, const float* dtw, const void* Hc, const void* Lam,
                                 const float* Dv, void* dx, float* Pb, float* Qb, float* dBh,
                                 float* dCh, float* dDpart, int64_t batch, int64_t L, int64_t H,
                                 int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
                                 hipStream_t stream) {
-  constexpr int TB = 16 * RI;
-  const int ta = bwd_target_floats(TB, (int)P, (int)N) * 4;
-  const int sb = bwd_source_floats(TB, (int)P, (int)N) * 4;
-  hipError_t e = ensure_dyn_lds<bwd_target_kernel<T, RI, NKN>>(ta);
+  const int ta = bwd_target_bytes<T>((int)P, (int)N);
+  const int sb = bwd_source_bytes<T>((int)P, (int)N);
+  hipError_t e = ensure_dyn_lds<bwd_target_kernel<T, NKN>>(ta);
   if (e != hipSuccess) return e;
-  e = ensure_dyn_lds<bwd_source_kernel<T, RI, NKN, NKP>>(sb);
+  e = ensure_dyn_lds<bwd_source_kernel<T, NKN, NKP>>(sb);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)T_, (unsigned)H, (unsigned)batch);
   const int hpg = (int)(H / G);
-  hipLaunchKernelGGL((bwd_target_kernel<T, RI, NKN>), grid, dim3(kBwdThreads), ta, stream,
+  hipLaunchKernelGGL((bwd_target_kernel<T, NKN>), grid, dim3(kBwdThreads), ta, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm),
                      static_cast<const T*>(Cm), static_cast<const T*>(dy), Gw, dtw,
-                     static_cast<const float*>(Hc), Pb, dCh, L, (int)H, (int)P, (int)N, (int)G, hpg, Q,
-                     (int)T_, ldw);
+                     static_cast<const float*>(Hc), Pb, dCh, L, (int)H, (int)P, (int)N, (int)G,
+                     hpg, Q, (int)T_, ldw);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_source_kernel<T, RI, NKN, NKP>), grid, dim3(kBwdThreads), sb, stream,
+  hipLaunchKernelGGL((bwd_source_kernel<T, NKN, NKP>), grid, dim3(kBwdThreads), sb, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm),
                      static_cast<const T*>(Cm), static_cast<const T*>(dy), Gw, dtw,
                      static_cast<const float*>(Lam), Dv, static_cast<T*>(dx), dBh, Qb, dDpart, L,
@@ -621,7 +638,7 @@ static hipError_t launch_chunks(const void* x, const void* Bm, const void* Cm, c
   return hipGetLastError();
 }
 
-template <typename T, int RI, int NKN>
+template <typename T, int NKN>
 static hipError_t launch_chunks_p(int64_t P, const void* x, const void* Bm, const void* Cm,
                                   const void* dy, const float* Gw, const float* dtw,
                                   const void* Hc, const void* Lam, const float* Dv, void* dx,
@@ -630,9 +647,9 @@ static hipError_t launch_chunks_p(int64_t P, const void* x, const void* Bm, cons
                                   int64_t T_, int64_t ldw, hipStream_t stream) {
 #define SSD_BWD_ARGS x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh, dDpart, batch, L, H, \
                      P, N, G, Q, T_, ldw, stream
-  if (P <= 64) return launch_chunks<T, RI, NKN, 4>(SSD_BWD_ARGS);
-  if (P <= 128) return launch_chunks<T, RI, NKN, 8>(SSD_BWD_ARGS);
-  return launch_chunks<T, RI, NKN, 16>(SSD_BWD_ARGS);
+  if (P <= 64) return launch_chunks<T, NKN, 4>(SSD_BWD_ARGS);
+  if (P <= 128) return launch_chunks<T, NKN, 8>(SSD_BWD_ARGS);
+  return launch_chunks<T, NKN, 16>(SSD_BWD_ARGS);
 #undef SSD_BWD_ARGS
 }
 
@@ -645,9 +662,9 @@ static hipError_t launch_chunks_t(int TB, const void* x, const void* Bm, const v
                                   int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
 #define SSD_BWD_ARGS P, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh, dDpart, batch, L, \
                      H, N, G, Q, T_, ldw, stream
-  if (TB != 32) return hipErrorInvalidValue;
-  if (N <= 128) return launch_chunks_p<T, 2, 8>(SSD_BWD_ARGS);
-  return launch_chunks_p<T, 2, 16>(SSD_BWD_ARGS);
+  if (TB != kBwdTB) return hipErrorInvalidValue;
+  if (N <= 128) return launch_chunks_p<T, 8>(SSD_BWD_ARGS);
+  return launch_chunks_p<T, 16>(SSD_BWD_ARGS);
 #undef SSD_BWD_ARGS
 }
 

@@ -41,7 +41,7 @@ int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int kh);
 int compute_out_kh_valid(int io_bf16, int64_t H, int64_t G, int64_t N, int kh);
 int compute_out_default_kh(int io_bf16, int64_t H, int64_t G, int64_t N);
 int chunk_state_default_kh(int64_t H, int64_t G);
-int bwd_block_rows(int Q, int64_t P, int64_t N);
+int bwd_block_rows(int io_bf16, int Q, int64_t P, int64_t N);
 hipError_t launch_bwd_widen(const void* src, float* dst, int64_t n, hipStream_t stream);
 hipError_t launch_bwd_prep(const float* Gw, float* w2, float* Gz, int64_t batch, int64_t H,
                            int64_t L, int64_t ldw, hipStream_t stream);
@@ -245,7 +245,7 @@ BwdPlan bwd_plan(const Plan& pl) {
   w.b32_off = o; o += bs;
   w.c32_off = o; o += bs;
   w.bytes = o;
-  w.TB = ssd::bwd_block_rows((int)pl.Q, pl.P, pl.N);
+  w.TB = ssd::bwd_block_rows(pl.bf16, (int)pl.Q, pl.P, pl.N);
   return w;
 }
 
@@ -253,7 +253,7 @@ ssd_status check_supported_bwd(const Plan& pl) {
   ssd_status st = check_supported(pl);
   if (st != SSD_OK) return st;
   if (pl.P > 256) return fail(SSD_ERR_UNSUPPORTED, "backward: headdim must be <= 256");
-  if (ssd::bwd_block_rows((int)pl.Q, pl.P, pl.N) == 0)
+  if (ssd::bwd_block_rows(pl.bf16, (int)pl.Q, pl.P, pl.N) == 0)
     return fail(SSD_ERR_UNSUPPORTED, "backward: headdim %lld and dstate %lld exceed LDS",
                 (long long)pl.P, (long long)pl.N);
   return SSD_OK;

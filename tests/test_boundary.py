@@ -407,11 +407,13 @@ def test_bwd_validation_order(so):
 
 
 def test_bwd_limits(so):
-    # headdim beyond 256, or tiles of headdim x dstate that do not fit the LDS
+    # headdim beyond 256 (dstate beyond 256 is the forward pass's limit too);
+    # every headdim x dstate up to 256 x 256 fits the per-chunk kernels' LDS
     assert bwd_ws(P(headdim=272))[0] == UNSUP
-    assert bwd_ws(P(headdim=256, dstate=256))[0] == UNSUP
+    assert bwd_ws(P(dstate=272))[0] == UNSUP
     for pd in (dict(), dict(dstate=256), dict(headdim=128), dict(chunk_size=32),
-               dict(io_dtype=0, chunk_size=128)):
+               dict(io_dtype=0, chunk_size=128), dict(headdim=256, dstate=256),
+               dict(io_dtype=0, headdim=256, dstate=256)):
         assert bwd_ws(P(**pd))[0] == OK, pd
 
 
