@@ -70,11 +70,6 @@ __host__ __device__ inline int bwd_union_bytes(int P, int N) {  // second pair, 
   return a > b ? a : b;
 }
 template <typename T>
-__host__ __device__ inline int bwd_target_bytes(int P, int N) {
-  return bwd_pair_bytes<T>(P, N) + bwd_union_bytes<T>(P, N) + kBwdTB * (kBwdTB + 1) * 4 +
-         5 * kBwdTB * 4;
-}
-template <typename T>
 __host__ __device__ inline int bwd_source_bytes(int P, int N) {
   return bwd_pair_bytes<T>(P, N) + bwd_union_bytes<T>(P, N) + 2 * kBwdTB * (kBwdTB + 1) * 4 +
          6 * kBwdTB * 4 + 8 * 4;
@@ -120,11 +115,31 @@ __device__ __forceinline__ floatx4 tile_dot(const T* A, const T* B, int ld, int 
 }
 
 // Reading side: dC (per head, fp32) and P for every token of one chunk.
-// Block pairs (I, J <= I) of 32 tokens: the two 32x32 products C B^T and
-// dy x^T on MFMA (one 16x16 tile of each per wave; the io values are exact
-// MFMA operands and the sums are fp32), W = mask exp2(G_i - G_j) dt_j (dy.x)
-// to LDS, then dC += W B on the vector ALU (2 rows x N/16 columns per
-// thread).  The carried term streams H_c through LDS 16 state rows at a time.
+// Block pairs (I, J <= I) of 32 tokens.  Every product is on MFMA: C B^T and
+// dy x^T from the io-dtype tiles (one 16x16 tile of each per wave; io values
+// are exact operands, sums fp32), then W = mask exp2(G_i - G_j) dt_j (dy.x)
+// through LDS and dC += W B on the exact fp32 MFMA, each wave owning 16 rows
+// and every other 16-column tile of dC in its accumulators for the whole
+// block.  The carried term exp2(G_i) H_c^T dy_i likewise, H_c streamed
+// through LDS 32 state rows (one K-step) at a time.
+constexpr int kBwdLdW = kBwdTB + 4;   // fp32 weight rows: 16-byte aligned fragments
+
+template <typename T>
+__host__ __device__ inline int bwd_target_bytes(int P, int N) {
+  const int pair = bwd_pair_bytes<T>(P, N), st = (32 * (N + 1) * 4 + 15) / 16 * 16;
+  return pair + (pair > st ? pair : st) + kBwdTB * kBwdLdW * 4 + 7 * kBwdTB * 4;
+}
+
+// 8 io values (k-contiguous) as an fp32 MFMA fragment
+__device__ __forceinline__ floatx8 frag32(const bf16* p) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+  floatx8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<float>(v[e]);
+  return r;
+}
+__device__ __forceinline__ floatx8 frag32(const float* p) { return load_frag(p); }
+
 template <typename T, int NKN>
 __global__ void __launch_bounds__(kBwdThreads)
 bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
@@ -132,29 +147,34 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
                   const float* __restrict__ dtw, const float* __restrict__ Hc,
                   float* __restrict__ Pout, float* __restrict__ dCh, int64_t L, int H, int P,
                   int N, int G, int hpg, int Q, int T_, int64_t ldw) {
-  constexpr int TB = kBwdTB, RI = 2, ldW = TB + 1;
+  constexpr int TB = kBwdTB, ldW = kBwdLdW, NT = NKN / 2;
   extern __shared__ __align__(16) unsigned char smem[];
   const int c = blockIdx.x, h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int g = h / hpg;
-  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
+  const int tid = threadIdx.x;
   const int lane = tid % kWave, wv = tid / kWave, ti2 = wv >> 1, tj2 = wv & 1;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  // second-stage ownership: rows 16 ib .. +15, column tiles nh, nh + 2, ...
+  const int ib = wv & 1, nh = wv >> 1;
   const int ldN = tile_ld<T>(N), ldP = tile_ld<T>(P), NR = round32(N), PR = round32(P);
+  const int pair = bwd_pair_bytes<T>(P, N), st = (32 * (N + 1) * 4 + 15) / 16 * 16;
   T* Ct = reinterpret_cast<T*>(smem);
   T* gt = Ct + TB * ldN;
-  unsigned char* U = smem + bwd_pair_bytes<T>(P, N);
+  unsigned char* U = smem + pair;
   T* Bt = reinterpret_cast<T*>(U);
   T* xt = Bt + TB * ldN;
   float* Hs = reinterpret_cast<float*>(U);
-  float* Ws = reinterpret_cast<float*>(U + bwd_union_bytes<T>(P, N));
+  float* Ws = reinterpret_cast<float*>(U + (pair > st ? pair : st));
   float* Gi = Ws + TB * ldW;
   float* Gj = Gi + TB;
-  float* Pp = Gj + TB;          // [2][TB]
-  float* Pacc = Pp + 2 * TB;
+  float* Pp = Gj + TB;          // [2][TB]: pair shares of P from the two column-half waves
+  float* Pc = Pp + 2 * TB;      // [2][TB]: carried shares of P
+  float* Pacc = Pc + 2 * TB;
   const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
   const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
   const float* Hrow = Hc + ((b * H + h) * T_ + c) * (int64_t)P * N;
-  const int nb = Q / TB, nk = N / 16;
+  const int nb = Q / TB, ntiles = N / 16;
 
   for (int I = 0; I < nb; ++I) {
     const int64_t ti0 = (int64_t)c * Q + I * TB;
@@ -167,11 +187,9 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       Gi[tid] = Grow[I * TB + tid];
       Pacc[tid] = 0.0f;
     }
-    float acc[RI][NKN];
+    floatx4 dc[NT];
 #pragma unroll
-    for (int r = 0; r < RI; ++r)
-#pragma unroll
-      for (int k = 0; k < NKN; ++k) acc[r][k] = 0.0f;
+    for (int q = 0; q < NT; ++q) dc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int J = 0; J <= I; ++J) {
       const int64_t tj0 = (int64_t)c * Q + J * TB;
       const int vj = valid_rows(L, tj0, TB);
@@ -183,83 +201,84 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       // this wave's tile: rows i = 16 ti2 + 4 (lane / 16) + r, column j = 16 tj2 + lane % 16
       const floatx4 cb = tile_dot(Ct + 16 * ti2 * ldN, Bt + 16 * tj2 * ldN, ldN, NR, lane);
       const floatx4 gx = tile_dot(gt + 16 * ti2 * ldP, xt + 16 * tj2 * ldP, ldP, PR, lane);
-      const int j = 16 * tj2 + (lane & 15);
+      const int j = 16 * tj2 + l16;
       const float dj = drow[J * TB + j];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * ti2 + 4 * (lane >> 4) + r;
+        const int i = 16 * ti2 + 4 * g4 + r;
         const bool on = J < I || j <= i;
         // the mask is applied before exp2, so no masked entry is evaluated
         const float w = on ? fast_exp2(Gi[i] - Gj[j]) * dj * gx[r] : 0.0f;
         Ws[i * ldW + j] = w;
         const float pr = sum16(w * cb[r]);
-        if ((lane & 15) == 0) Pp[tj2 * TB + i] = pr;
+        if (l16 == 0) Pp[tj2 * TB + i] = pr;
       }
       __syncthreads();
       if (tid < TB) Pacc[tid] += Pp[tid] + Pp[TB + tid];
-#pragma unroll 4
-      for (int jj = 0; jj < TB; ++jj) {
-        float wr[RI];
+      // dC rows 16 ib + .. += W[rows][0..31] B[0..31][tile columns]
+      const floatx8 a = load_frag(Ws + (16 * ib + l16) * ldW + 8 * g4);
 #pragma unroll
-        for (int r = 0; r < RI; ++r) wr[r] = Ws[(ti * RI + r) * ldW + jj];
+      for (int q = 0; q < NT; ++q) {
+        const int nt = nh + 2 * q;
+        if (nt < ntiles) {
+          floatx8 bq;
 #pragma unroll
-        for (int k = 0; k < NKN; ++k) {
-          if (k < nk) {
-            const float bv = to_f32(Bt[jj * ldN + tj + 16 * k]);
-#pragma unroll
-            for (int r = 0; r < RI; ++r) acc[r][k] = fmaf(wr[r], bv, acc[r][k]);
-          }
+          for (int e = 0; e < 8; ++e) bq[e] = to_f32(Bt[(8 * g4 + e) * ldN + 16 * nt + l16]);
+          dc[q] = mma(dc[q], a, bq);
         }
       }
     }
-    // carried term exp2(G_i) H_c^T dy_i, H_c streamed 16 state rows at a time
-    float cr[RI][NKN];
+    // carried term exp2(G_i) H_c^T dy_i: H_c through LDS 32 state rows at a time
+    floatx4 hc[NT];
 #pragma unroll
-    for (int r = 0; r < RI; ++r)
-#pragma unroll
-      for (int k = 0; k < NKN; ++k) cr[r][k] = 0.0f;
-    for (int p0 = 0; p0 < P; p0 += kBwdPH) {
+    for (int q = 0; q < NT; ++q) hc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p0 = 0; p0 < P; p0 += 32) {
       __syncthreads();
-      for (int e = tid; e < kBwdPH * N; e += kBwdThreads)
-        Hs[(e / N) * (N + 1) + e % N] = Hrow[(int64_t)p0 * N + e];
+      for (int e = tid; e < 32 * N; e += kBwdThreads) {
+        const int pr = e / N;
+        Hs[pr * (N + 1) + e % N] = p0 + pr < P ? Hrow[(int64_t)p0 * N + e] : 0.0f;
+      }
       __syncthreads();
-#pragma unroll 4
-      for (int pp = 0; pp < kBwdPH; ++pp) {
-        float gv[RI];
+      const floatx8 a = frag32(gt + (16 * ib + l16) * ldP + p0 + 8 * g4);
 #pragma unroll
-        for (int r = 0; r < RI; ++r) gv[r] = to_f32(gt[(ti * RI + r) * ldP + p0 + pp]);
+      for (int q = 0; q < NT; ++q) {
+        const int nt = nh + 2 * q;
+        if (nt < ntiles) {
+          floatx8 bq;
 #pragma unroll
-        for (int k = 0; k < NKN; ++k) {
-          if (k < nk) {
-            const float hv = Hs[pp * (N + 1) + tj + 16 * k];
-#pragma unroll
-            for (int r = 0; r < RI; ++r) cr[r][k] = fmaf(gv[r], hv, cr[r][k]);
-          }
+          for (int e = 0; e < 8; ++e) bq[e] = Hs[(8 * g4 + e) * (N + 1) + 16 * nt + l16];
+          hc[q] = mma(hc[q], a, bq);
         }
       }
     }
+    // rows i = 16 ib + 4 (lane / 16) + r, column 16 nt + lane % 16 of each tile
+    float pc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int r = 0; r < RI; ++r) {
-      const int i = ti * RI + r;
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ib + 4 * g4 + r;
       const float e = fast_exp2(Gi[i]);
-      float pc = 0.0f;
 #pragma unroll
-      for (int k = 0; k < NKN; ++k) {
-        if (k < nk) {
-          const float v = e * cr[r][k];
-          acc[r][k] += v;
-          pc = fmaf(v, to_f32(Ct[i * ldN + tj + 16 * k]), pc);
+      for (int q = 0; q < NT; ++q) {
+        const int nt = nh + 2 * q;
+        if (nt < ntiles) {
+          const float v = e * hc[q][r];
+          dc[q][r] += v;
+          pc[r] = fmaf(v, to_f32(Ct[i * ldN + 16 * nt + l16]), pc[r]);
         }
       }
-      pc = sum16(pc);
+      pc[r] = sum16(pc[r]);
+      if (l16 == 0) Pc[nh * TB + i] = pc[r];
       if (i < vi) {
-        float* dst = dCh + ((b * L + ti0 + i) * H + h) * (int64_t)N;
+        float* dst = dCh + ((b * L + ti0 + i) * H + h) * (int64_t)N + l16;
 #pragma unroll
-        for (int k = 0; k < NKN; ++k)
-          if (k < nk) dst[tj + 16 * k] = acc[r][k];
-        if (tj == 0) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + i] = Pacc[i] + pc;
+        for (int q = 0; q < NT; ++q) {
+          const int nt = nh + 2 * q;
+          if (nt < ntiles) dst[16 * nt] = dc[q][r];
+        }
       }
     }
+    __syncthreads();
+    if (tid < vi) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + tid] = Pacc[tid] + Pc[tid] + Pc[TB + tid];
   }
 }
 
