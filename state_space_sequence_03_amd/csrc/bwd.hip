@@ -51,7 +51,6 @@ namespace ssd {
 constexpr int kBwdThreads = 256;
 
 constexpr int kBwdTB = 32;   // token rows per block of a chunk
-constexpr int kBwdPH = 16;   // state rows per pass of the carried terms
 
 // io-dtype tiles in LDS: rows of K values, K rounded up to whole 32-value MFMA
 // K-steps (zero-filled) plus 16 bytes against bank conflicts.
@@ -59,20 +58,11 @@ __host__ __device__ inline int round32(int v) { return (v + 31) / 32 * 32; }
 template <typename T>
 __host__ __device__ inline int tile_ld(int K) { return round32(K) + 16 / (int)sizeof(T); }
 
-// LDS bytes of the two per-chunk kernels (every region a multiple of 16 bytes)
+// LDS bytes of the tile pair both per-chunk kernels stage (every region a
+// multiple of 16 bytes)
 template <typename T>
 __host__ __device__ inline int bwd_pair_bytes(int P, int N) {   // two io tiles: N- and P-wide
   return kBwdTB * (tile_ld<T>(N) + tile_ld<T>(P)) * (int)sizeof(T);
-}
-template <typename T>
-__host__ __device__ inline int bwd_union_bytes(int P, int N) {  // second pair, or a state pass
-  const int a = bwd_pair_bytes<T>(P, N), b = (kBwdPH * (N + 1) * 4 + 15) / 16 * 16;
-  return a > b ? a : b;
-}
-template <typename T>
-__host__ __device__ inline int bwd_source_bytes(int P, int N) {
-  return bwd_pair_bytes<T>(P, N) + bwd_union_bytes<T>(P, N) + 2 * kBwdTB * (kBwdTB + 1) * 4 +
-         6 * kBwdTB * 4 + 8 * 4;
 }
 
 // rows x K io elements (rows `row_stride` apart) into an LDS tile of row
@@ -283,10 +273,20 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 }
 
 // Read side: dx, dB (per head, fp32), Qr and the chunk's share of dD.  Block
-// pairs (J, I >= J): B C^T and x dy^T on MFMA as above, U = mask exp2(G_i -
-// G_j) (C.B) and V = mask exp2(G_i - G_j) (dy.x) to LDS, then dx += U^T dy and
-// dB += V^T C on the vector ALU; the carried terms stream L_{c+1} through LDS
-// 16 state rows at a time.
+// pairs (J, I >= J) of 32 tokens, every product on MFMA: B C^T and x dy^T
+// from the io-dtype tiles, U = mask exp2(G_i - G_j) (C.B) and
+// V = mask exp2(G_i - G_j) (dy.x) through LDS, then dx += U dy and dB += V C
+// on the exact fp32 MFMA, each wave owning 16 rows j and every other
+// 16-column tile of dx and dB for the whole block.  The carried terms come
+// from L_{c+1} streamed through LDS 32 state rows at a time:
+// exp2(G_last - G_j) (B_j L^T) into dx and exp2(G_last - G_j) (x_j L) into
+// dB, the factor folded into the row's operand fragment.
+template <typename T>
+__host__ __device__ inline int bwd_source_bytes(int P, int N) {
+  const int pair = bwd_pair_bytes<T>(P, N), st = (32 * (round32(N) + 1) * 4 + 15) / 16 * 16;
+  return pair + (pair > st ? pair : st) + 2 * kBwdTB * kBwdLdW * 4 + 8 * kBwdTB * 4 + 8 * 4;
+}
+
 template <typename T, int NKN, int NKP>
 __global__ void __launch_bounds__(kBwdThreads)
 bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
@@ -295,32 +295,38 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
                   const float* __restrict__ Dv, T* __restrict__ dx, float* __restrict__ dBh,
                   float* __restrict__ Qout, float* __restrict__ dDpart, int64_t L, int H, int P,
                   int N, int G, int hpg, int Q, int T_, int64_t ldw) {
-  constexpr int TB = kBwdTB, RI = 2, ldW = TB + 1;
+  constexpr int TB = kBwdTB, ldW = kBwdLdW, NT = NKN / 2, PT = NKP / 2;
   extern __shared__ __align__(16) unsigned char smem[];
   const int c = blockIdx.x, h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int g = h / hpg;
-  const int tid = threadIdx.x, tj = tid / 16, ti = tid % 16;
+  const int tid = threadIdx.x;
   const int lane = tid % kWave, wv = tid / kWave, tj2 = wv >> 1, ti2 = wv & 1;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  // second-stage ownership: rows j = 16 jb .. +15, column tiles nh, nh + 2, ...
+  const int jb = wv & 1, nh = wv >> 1;
   const int ldN = tile_ld<T>(N), ldP = tile_ld<T>(P), NR = round32(N), PR = round32(P);
+  const int lsN = NR + 1;       // state-pass rows, zero-padded to whole K-steps
+  const int pair = bwd_pair_bytes<T>(P, N), st = (32 * lsN * 4 + 15) / 16 * 16;
   T* Bt = reinterpret_cast<T*>(smem);
   T* xt = Bt + TB * ldN;
-  unsigned char* U = smem + bwd_pair_bytes<T>(P, N);
+  unsigned char* U = smem + pair;
   T* Ct = reinterpret_cast<T*>(U);
   T* gt = Ct + TB * ldN;
   float* Ls = reinterpret_cast<float*>(U);
-  float* Us = reinterpret_cast<float*>(U + bwd_union_bytes<T>(P, N));
+  float* Us = reinterpret_cast<float*>(U + (pair > st ? pair : st));
   float* Vs = Us + TB * ldW;
   float* Gi = Vs + TB * ldW;
   float* Gj = Gi + TB;
   float* dj = Gj + TB;
-  float* Qp = dj + TB;          // [2][TB]
-  float* Qacc = Qp + 2 * TB;
+  float* Qp = dj + TB;          // [2][TB]: pair shares of Qr from the two column-half waves
+  float* Qc = Qp + 2 * TB;      // [2][TB]: carried shares of Qr
+  float* Qacc = Qc + 2 * TB;
   float* red = Qacc + TB;
   const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
   const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
   const float* Lrow = Lam + ((b * H + h) * T_ + c) * (int64_t)P * N;
-  const int nb = Q / TB, nkn = N / 16, nkp = P / 16;
+  const int nb = Q / TB, ntn = N / 16, ntp = P / 16;
   const float Dh = Dv ? Dv[h] : 0.0f;
   const float Gl = Grow[Q - 1];
   float dsum = 0.0f;
@@ -337,14 +343,11 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       dj[tid] = drow[J * TB + tid];
       Qacc[tid] = 0.0f;
     }
-    float dba[RI][NKN], dxa[RI][NKP];
+    floatx4 dba[NT], dxa[PT];
 #pragma unroll
-    for (int s = 0; s < RI; ++s) {
+    for (int q = 0; q < NT; ++q) dba[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k = 0; k < NKN; ++k) dba[s][k] = 0.0f;
-#pragma unroll
-      for (int k = 0; k < NKP; ++k) dxa[s][k] = 0.0f;
-    }
+    for (int q = 0; q < PT; ++q) dxa[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int I = J; I < nb; ++I) {
       const int64_t ti0 = (int64_t)c * Q + I * TB;
       const int vi = valid_rows(L, ti0, TB);
@@ -357,111 +360,120 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       // this wave's tile: rows j = 16 tj2 + 4 (lane / 16) + r, column i = 16 ti2 + lane % 16
       const floatx4 cb = tile_dot(Bt + 16 * tj2 * ldN, Ct + 16 * ti2 * ldN, ldN, NR, lane);
       const floatx4 gx = tile_dot(xt + 16 * tj2 * ldP, gt + 16 * ti2 * ldP, ldP, PR, lane);
-      const int i = 16 * ti2 + (lane & 15);
+      const int i = 16 * ti2 + l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * tj2 + 4 * (lane >> 4) + r;
+        const int j = 16 * tj2 + 4 * g4 + r;
         const bool on = I > J || j <= i;
         const float a = on ? fast_exp2(Gi[i] - Gj[j]) : 0.0f;
         const float u = a * cb[r];
         Us[j * ldW + i] = u;
         Vs[j * ldW + i] = a * gx[r];
         const float q = sum16(u * gx[r]);
-        if ((lane & 15) == 0) Qp[ti2 * TB + j] = q;
+        if (l16 == 0) Qp[ti2 * TB + j] = q;
       }
       __syncthreads();
       if (tid < TB) Qacc[tid] += Qp[tid] + Qp[TB + tid];
-#pragma unroll 4
-      for (int ii = 0; ii < TB; ++ii) {
-        float uv[RI], vv[RI];
+      // rows 16 jb + ..: dB += V[rows][0..31] C[0..31][tiles], dx += U[rows][..] dy[..][tiles]
+      const floatx8 av = load_frag(Vs + (16 * jb + l16) * ldW + 8 * g4);
+      const floatx8 au = load_frag(Us + (16 * jb + l16) * ldW + 8 * g4);
 #pragma unroll
-        for (int s = 0; s < RI; ++s) {
-          uv[s] = Us[(tj * RI + s) * ldW + ii];
-          vv[s] = Vs[(tj * RI + s) * ldW + ii];
+      for (int q = 0; q < NT; ++q) {
+        const int nt = nh + 2 * q;
+        if (nt < ntn) {
+          floatx8 bq;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bq[e] = to_f32(Ct[(8 * g4 + e) * ldN + 16 * nt + l16]);
+          dba[q] = mma(dba[q], av, bq);
         }
+      }
 #pragma unroll
-        for (int k = 0; k < NKN; ++k) {
-          if (k < nkn) {
-            const float cv = to_f32(Ct[ii * ldN + ti + 16 * k]);
+      for (int q = 0; q < PT; ++q) {
+        const int pt = nh + 2 * q;
+        if (pt < ntp) {
+          floatx8 bq;
 #pragma unroll
-            for (int s = 0; s < RI; ++s) dba[s][k] = fmaf(vv[s], cv, dba[s][k]);
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < NKP; ++k) {
-          if (k < nkp) {
-            const float gv = to_f32(gt[ii * ldP + ti + 16 * k]);
-#pragma unroll
-            for (int s = 0; s < RI; ++s) dxa[s][k] = fmaf(uv[s], gv, dxa[s][k]);
-          }
+          for (int e = 0; e < 8; ++e) bq[e] = to_f32(gt[(8 * g4 + e) * ldP + 16 * pt + l16]);
+          dxa[q] = mma(dxa[q], au, bq);
         }
       }
     }
-    // carried terms from L_{c+1}, streamed 16 state rows at a time: pass p0
-    // holds rows p0 .. p0+15, so lane ti's row p = p0 + ti is its k = p0/16
-    // column of dx, and every pass adds its rows' share of dB
-    float e[RI], qx[RI];
-#pragma unroll
-    for (int s = 0; s < RI; ++s) {
-      e[s] = fast_exp2(Gl - Gj[tj * RI + s]);
-      qx[s] = 0.0f;
-    }
-    for (int p0 = 0; p0 < P; p0 += kBwdPH) {
+    // carried terms, L_{c+1} through LDS 32 state rows (p0 .. p0+31) at a time;
+    // this wave's A-operand row j = 16 jb + lane % 16 carries exp2(G_last - G_j)
+    const float erow = fast_exp2(Gl - Gj[16 * jb + l16]);
+    float qx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p0 = 0; p0 < P; p0 += 32) {
       __syncthreads();
-      for (int q = tid; q < kBwdPH * N; q += kBwdThreads)
-        Ls[(q / N) * (N + 1) + q % N] = Lrow[(int64_t)p0 * N + q];
-      __syncthreads();
-      const int kp = p0 / kBwdPH;
-#pragma unroll
-      for (int s = 0; s < RI; ++s) {
-        const int j = tj * RI + s;
-        float v = 0.0f;
-#pragma unroll 8
-        for (int n = 0; n < N; ++n) v = fmaf(Ls[ti * (N + 1) + n], to_f32(Bt[j * ldN + n]), v);
-        v *= e[s];
-#pragma unroll
-        for (int k = 0; k < NKP; ++k)
-          if (k == kp) dxa[s][k] += v;
-        qx[s] = fmaf(to_f32(xt[j * ldP + p0 + ti]), v, qx[s]);
+      for (int e = tid; e < 32 * NR; e += kBwdThreads) {
+        const int pr = e / NR, n = e % NR;
+        Ls[pr * lsN + n] = (p0 + pr < P && n < N) ? Lrow[(int64_t)(p0 + pr) * N + n] : 0.0f;
       }
-#pragma unroll 4
-      for (int pp = 0; pp < kBwdPH; ++pp) {
-        float xv[RI];
+      __syncthreads();
+      // dx tile (rows j, columns p = p0 + 16 nh + lane % 16) += e_j sum_n B[j][n] L[p][n]
+      const int q = p0 / 32;
+      if (16 * nh + p0 < P) {
+        floatx4 cj = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k0 = 0; k0 < NR; k0 += 32) {
+          floatx8 a = frag32(Bt + (16 * jb + l16) * ldN + k0 + 8 * g4);
 #pragma unroll
-        for (int s = 0; s < RI; ++s) xv[s] = e[s] * to_f32(xt[(tj * RI + s) * ldP + p0 + pp]);
+          for (int e = 0; e < 8; ++e) a[e] *= erow;
+          floatx8 bq;
 #pragma unroll
-        for (int k = 0; k < NKN; ++k) {
-          if (k < nkn) {
-            const float lv = Ls[pp * (N + 1) + ti + 16 * k];
+          for (int e = 0; e < 8; ++e) bq[e] = Ls[(16 * nh + l16) * lsN + k0 + 8 * g4 + e];
+          cj = mma(cj, a, bq);
+        }
 #pragma unroll
-            for (int s = 0; s < RI; ++s) dba[s][k] = fmaf(xv[s], lv, dba[s][k]);
-          }
+        for (int qq = 0; qq < PT; ++qq)
+          if (qq == q) dxa[qq] += cj;
+        // Qr's carried share: sum_p x[j][p] (e_j B_j L^T)[p]
+        const int p = p0 + 16 * nh + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          qx[r] = fmaf(to_f32(xt[(16 * jb + 4 * g4 + r) * ldP + p]), cj[r], qx[r]);
+      }
+      // dB tiles (rows j, columns n) += e_j sum_{p in pass} x[j][p] L[p][n]
+      floatx8 a = frag32(xt + (16 * jb + l16) * ldP + p0 + 8 * g4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] *= erow;
+#pragma unroll
+      for (int qq = 0; qq < NT; ++qq) {
+        const int nt = nh + 2 * qq;
+        if (nt < ntn) {
+          floatx8 bq;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bq[e] = Ls[(8 * g4 + e) * lsN + 16 * nt + l16];
+          dba[qq] = mma(dba[qq], a, bq);
         }
       }
     }
+    // rows j = 16 jb + 4 (lane / 16) + r, column 16 tile + lane % 16
 #pragma unroll
-    for (int s = 0; s < RI; ++s) {
-      const int j = tj * RI + s;
-      const float q = sum16(qx[s]);
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * jb + 4 * g4 + r;
+      const float qs = sum16(qx[r]);
+      if (l16 == 0) Qc[nh * TB + j] = qs;
       if (j < vj) {
-        const int64_t t = tj0 + j;
         const float d = dj[j];
-        const int64_t row = (b * L + t) * H + h;
+        const int64_t row = (b * L + tj0 + j) * H + h;
 #pragma unroll
-        for (int k = 0; k < NKP; ++k) {
-          if (k < nkp) {
-            const int p = ti + 16 * k;
+        for (int q = 0; q < PT; ++q) {
+          const int pt = nh + 2 * q;
+          if (pt < ntp) {
+            const int p = 16 * pt + l16;
             const float gv = to_f32(dy[row * P + p]);
-            dx[row * P + p] = to_io<T>(fmaf(d, dxa[s][k], Dh * gv));
+            dx[row * P + p] = to_io<T>(fmaf(d, dxa[q][r], Dh * gv));
             dsum = fmaf(gv, to_f32(xt[j * ldP + p]), dsum);
           }
         }
 #pragma unroll
-        for (int k = 0; k < NKN; ++k)
-          if (k < nkn) dBh[row * N + ti + 16 * k] = d * dba[s][k];
-        if (ti == 0) Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + j] = Qacc[j] + q;
+        for (int q = 0; q < NT; ++q) {
+          const int nt = nh + 2 * q;
+          if (nt < ntn) dBh[row * N + 16 * nt + l16] = d * dba[q][r];
+        }
       }
     }
+    __syncthreads();
+    if (tid < vj) Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + tid] = Qacc[tid] + Qc[tid] + Qc[TB + tid];
   }
   // the chunk's share of dD = sum <dy, x>
 #pragma unroll
