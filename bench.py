@@ -48,8 +48,7 @@ PEAK_FP32_MFMA = 157.3e12   # dense fp32 MFMA
 PEAK_HBM = 8.0e12           # HBM3E bytes/s
 METRIC = "SSD fwd tokens/sec (batch·seqlen) at 1 MI355X; % of bf16 MFMA roofline"
 DECODE_METRIC = "SSD decode tokens/sec (batch, one token per step) at 1 MI355X; % of HBM roofline"
-BWD_METRIC = "SSD bwd tokens/sec (batch·seqlen) at 1 MI355X; % of fp32 vector ALU roofline"
-PEAK_FP32_VALU = 157.3e12   # fp32 vector FMA: 256 CUs x 2.4 GHz x 256 flop/clk
+BWD_METRIC = "SSD bwd tokens/sec (batch·seqlen) at 1 MI355X; % of MFMA roofline"
 COPY_PROBE_BYTES = 1 << 30
 DEFAULT_WORKLOAD = "mamba2_2p7b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compute_out_{workload}_traffic.txt")
@@ -163,8 +162,17 @@ def bwd_counts(p):
     Bz, L, H, P, N, Q = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.chunk_size
     T = -(-L // Q)
     pairs = Q * (Q + 1) // 2
-    per_unit = 2 * (pairs * (3 * N + 2 * P) + 5 * Q * P * N)
-    return dict(per_unit=per_unit, units=Bz * H * T, flops=per_unit * Bz * H * T, tokens=Bz * L)
+    chunk = 2 * pairs * (3 * N + 2 * P)     # the chunk x chunk products
+    state = 2 * 5 * Q * P * N               # the chunk x state products
+    per_unit = chunk + state
+    units = Bz * H * T
+    # peak for this mix: every flop at the rate of the MFMA that runs it -- the
+    # chunk x chunk products on bf16 MFMA for bf16 io (fp32 MFMA for fp32 io),
+    # the state products on the exact fp32 MFMA
+    chunk_peak = PEAK_BF16_MFMA if p.io_dtype == "bf16" else PEAK_FP32_MFMA
+    peak = per_unit / (chunk / chunk_peak + state / PEAK_FP32_MFMA)
+    return dict(per_unit=per_unit, chunk_per_unit=chunk, state_per_unit=state, units=units,
+                flops=per_unit * units, tokens=Bz * L, peak=peak)
 
 
 def bench_bwd(args):
@@ -228,11 +236,15 @@ def bench_bwd(args):
                    "init_state": prob.init_std is not None, "dfinal": True},
         # the whole backward call (every kernel of ssd_bwd) bracketed by events on
         # the stream it is enqueued on; the per-kernel split is in the kernel trace
-        "roofline": {"kernel": "ssd_bwd (all kernels)", "bound": "alu",
-                     "achieved": achieved / 1e12, "peak": PEAK_FP32_VALU / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU, "traffic": None,
+        "roofline": {"kernel": "ssd_bwd (all kernels)", "bound": "mfma",
+                     "achieved": achieved / 1e12, "peak": c["peak"] / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / c["peak"], "traffic": None,
                      "flops_per_unit": c["per_unit"], "units_per_launch": c["units"],
-                     "pass_ms": ms_pass},
+                     "peak_mix": "chunk x chunk products at %.1f TFLOP/s, state products at "
+                                 "%.1f (fp32 MFMA)" % ((PEAK_BF16_MFMA if prob.io_dtype == "bf16"
+                                                        else PEAK_FP32_MFMA) / 1e12,
+                                                       PEAK_FP32_MFMA / 1e12),
+                     "frac_of_fp32_peak": achieved / PEAK_FP32_MFMA, "pass_ms": ms_pass},
     }
     if not args.no_cpu_baseline:
         arrs = {k: (None if v is None else oracle.as_f32(v)) for k, v in inputs.items()}

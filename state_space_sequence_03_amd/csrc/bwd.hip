@@ -120,6 +120,19 @@ __host__ __device__ inline int bwd_target_bytes(int P, int N) {
   return pair + (pair > st ? pair : st) + kBwdTB * kBwdLdW * 4 + 7 * kBwdTB * 4;
 }
 
+// 8 fp32 weights (k-contiguous) as two bf16 fragments, hi = bf16(w) and
+// lo = bf16(w - hi): hi + lo carries ~16 significant bits of w, so two bf16
+// MFMAs against an exact bf16 operand give the product to ~2^-16 relative
+__device__ __forceinline__ void split_frag(const float* p, bf16x8& hi, bf16x8& lo) {
+  const floatx8 v = load_frag(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 h = static_cast<bf16>(v[e]);
+    hi[e] = h;
+    lo[e] = static_cast<bf16>(v[e] - static_cast<float>(h));
+  }
+}
+
 // 8 io values (k-contiguous) as an fp32 MFMA fragment
 __device__ __forceinline__ floatx8 frag32(const bf16* p) {
   const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
@@ -206,15 +219,31 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       __syncthreads();
       if (tid < TB) Pacc[tid] += Pp[tid] + Pp[TB + tid];
       // dC rows 16 ib + .. += W[rows][0..31] B[0..31][tile columns]
-      const floatx8 a = load_frag(Ws + (16 * ib + l16) * ldW + 8 * g4);
+      if constexpr (sizeof(T) == 2) {
+        // bf16 io: W split into bf16 hi + lo, B's token-major fragment by
+        // transposing LDS reads
+        bf16x8 wh, wl;
+        split_frag(Ws + (16 * ib + l16) * ldW + 8 * g4, wh, wl);
 #pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        const int nt = nh + 2 * q;
-        if (nt < ntiles) {
-          floatx8 bq;
+        for (int q = 0; q < NT; ++q) {
+          const int nt = nh + 2 * q;
+          if (nt < ntiles) {
+            const bf16x8 bq = frag_tokens(reinterpret_cast<const bf16*>(Bt), ldN, 8 * g4,
+                                          8 * g4 + 4, 16 * nt, lane);
+            dc[q] = mma(mma(dc[q], wh, bq), wl, bq);
+          }
+        }
+      } else {
+        const floatx8 a = load_frag(Ws + (16 * ib + l16) * ldW + 8 * g4);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bq[e] = to_f32(Bt[(8 * g4 + e) * ldN + 16 * nt + l16]);
-          dc[q] = mma(dc[q], a, bq);
+        for (int q = 0; q < NT; ++q) {
+          const int nt = nh + 2 * q;
+          if (nt < ntiles) {
+            floatx8 bq;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bq[e] = to_f32(Bt[(8 * g4 + e) * ldN + 16 * nt + l16]);
+            dc[q] = mma(dc[q], a, bq);
+          }
         }
       }
     }
@@ -375,26 +404,52 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       __syncthreads();
       if (tid < TB) Qacc[tid] += Qp[tid] + Qp[TB + tid];
       // rows 16 jb + ..: dB += V[rows][0..31] C[0..31][tiles], dx += U[rows][..] dy[..][tiles]
-      const floatx8 av = load_frag(Vs + (16 * jb + l16) * ldW + 8 * g4);
-      const floatx8 au = load_frag(Us + (16 * jb + l16) * ldW + 8 * g4);
+      if constexpr (sizeof(T) == 2) {
+        // bf16 io: U and V split into bf16 hi + lo, C's and dy's token-major
+        // fragments by transposing LDS reads
+        bf16x8 vh, vl, uh, ul;
+        split_frag(Vs + (16 * jb + l16) * ldW + 8 * g4, vh, vl);
+        split_frag(Us + (16 * jb + l16) * ldW + 8 * g4, uh, ul);
 #pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        const int nt = nh + 2 * q;
-        if (nt < ntn) {
-          floatx8 bq;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bq[e] = to_f32(Ct[(8 * g4 + e) * ldN + 16 * nt + l16]);
-          dba[q] = mma(dba[q], av, bq);
+        for (int q = 0; q < NT; ++q) {
+          const int nt = nh + 2 * q;
+          if (nt < ntn) {
+            const bf16x8 bq = frag_tokens(reinterpret_cast<const bf16*>(Ct), ldN, 8 * g4,
+                                          8 * g4 + 4, 16 * nt, lane);
+            dba[q] = mma(mma(dba[q], vh, bq), vl, bq);
+          }
         }
-      }
 #pragma unroll
-      for (int q = 0; q < PT; ++q) {
-        const int pt = nh + 2 * q;
-        if (pt < ntp) {
-          floatx8 bq;
+        for (int q = 0; q < PT; ++q) {
+          const int pt = nh + 2 * q;
+          if (pt < ntp) {
+            const bf16x8 bq = frag_tokens(reinterpret_cast<const bf16*>(gt), ldP, 8 * g4,
+                                          8 * g4 + 4, 16 * pt, lane);
+            dxa[q] = mma(mma(dxa[q], uh, bq), ul, bq);
+          }
+        }
+      } else {
+        const floatx8 av = load_frag(Vs + (16 * jb + l16) * ldW + 8 * g4);
+        const floatx8 au = load_frag(Us + (16 * jb + l16) * ldW + 8 * g4);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bq[e] = to_f32(gt[(8 * g4 + e) * ldP + 16 * pt + l16]);
-          dxa[q] = mma(dxa[q], au, bq);
+        for (int q = 0; q < NT; ++q) {
+          const int nt = nh + 2 * q;
+          if (nt < ntn) {
+            floatx8 bq;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bq[e] = to_f32(Ct[(8 * g4 + e) * ldN + 16 * nt + l16]);
+            dba[q] = mma(dba[q], av, bq);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < PT; ++q) {
+          const int pt = nh + 2 * q;
+          if (pt < ntp) {
+            floatx8 bq;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bq[e] = to_f32(gt[(8 * g4 + e) * ldP + 16 * pt + l16]);
+            dxa[q] = mma(dxa[q], au, bq);
+          }
         }
       }
     }

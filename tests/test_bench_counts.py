@@ -58,3 +58,7 @@ def test_bwd_counts_2p7b():
     assert c["per_unit"] == 2 * (pairs * (3 * 128 + 2 * 64) + 5 * 256 * 64 * 128) == 54657024
     assert c["units"] == 2 * 80 * 32
     assert round(c["flops"] / 1e9, 2) == 279.84
+    # blended peak: 33.69 MFLOP at 2.5 PFLOP/s plus 20.97 MFLOP at 157.3 TFLOP/s
+    assert c["chunk_per_unit"] == 2 * pairs * (3 * 128 + 2 * 64)
+    t = c["chunk_per_unit"] / 2.5e15 + c["state_per_unit"] / 157.3e12
+    assert abs(c["peak"] - c["per_unit"] / t) < 1.0 and 372e12 < c["peak"] < 373e12
