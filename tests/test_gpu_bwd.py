@@ -7,7 +7,8 @@ blocks with a ragged tail, for both io dtypes, dstate up to 256, chunk sizes
 32 to 256, grouped and ungrouped B/C, with and without D, init_state and
 dfinal, and with the step-size preparation.  At the 2.7B layer shape the
 per-head gradients of two (batch, head) pairs are checked against the oracle
-run for those heads alone.
+run for those heads alone, and at the large-state layer shape one whole group
+of one batch row (its dB and dC included).
 
 Tolerances (relative L2 over the tensor; max-abs relative to max|ref|).
 Every gradient is computed in fp32 from the (exact) io values, with fp32
@@ -193,3 +194,23 @@ def test_bwd_2p7b_dC_dB_properties():
     print("  <x,dx>+<init,dinit> %.6e  loss %.6e  bound %.3e" % (lhs_x, loss, bound(tx)),
           flush=True)
     assert abs(lhs_x - loss) <= bound(tx)
+
+
+def test_bwd_large_state_one_whole_group():
+    # the large-state layer shape (batch 8, 4096 tokens, 64 heads in 8 groups,
+    # headdim 64, dstate 256, chunk 128): the oracle for all 8 heads of group 0
+    # in batch row 0 gives their per-head gradients and, summed over the
+    # group, dB and dC of that (batch, group) exactly
+    p = ssd_synth.CONFIGS["large_state"]
+    inp = ssd_synth.make_inputs(p, seed=5)
+    grads = ssd_synth.make_grads(p, seed=5)
+    got = run_case(p, inp, grads, True, True, None)
+    hpg = p.nheads // p.ngroups
+    heads = [(0, h) for h in range(hpg)]
+    ref = oracle.recurrence_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                inp["init_state"], grads["dy"], grads["dfinal"], heads=heads)
+    check(got["dx"][0, :, :hpg], ref["dx"][0, :, :hpg], "bf16", "dx[0,:,g0]")
+    check(got["ddt"][0, :, :hpg], ref["ddt"][0, :, :hpg], "f32out", "ddt[0,:,g0]")
+    check(got["dinit"][0, :hpg], ref["dinit"][0, :hpg], "f32out", "dinit[0,g0]")
+    check(got["dB"][0, :, 0], ref["dB"][0, :, 0], "bf16", "dB[0,:,0]")
+    check(got["dC"][0, :, 0], ref["dC"][0, :, 0], "bf16", "dC[0,:,0]")
