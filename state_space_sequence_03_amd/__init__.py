@@ -1,4 +1,5 @@
-"""libssd Python binding: the Mamba-2 chunked SSD forward pass on MI355X.
+"""libssd Python binding: the Mamba-2 chunked SSD scan on MI355X (forward pass,
+decode step and backward pass).
 
 Argument marshalling only.  Every step of the computation runs in the HIP
 kernels of ``libssd.so`` (built in-tree by ``state_space_sequence_03_amd.build``);
@@ -9,7 +10,8 @@ if ``libssd.so`` is missing or the tensors are not on a GPU.
 Names match the C ABI in include/ssd.h:
     ssd_fwd, ssd_fwd_ex, ssd_fwd_states, ssd_fwd_states_ex, ssd_compute_out, ssd_chunk_cumsum,
     ssd_chunk_cumsum_ex, ssd_step, ssd_default_config, ssd_tune, ssd_fwd_workspace_size,
-    ssd_status_string, ssd_last_error_message, ssd_abi_version
+    ssd_bwd, ssd_bwd_workspace_size, ssd_status_string, ssd_last_error_message,
+    ssd_abi_version
 (ssd_fwd_config is reached through ssd_fwd(..., config=...).)
 """
 from __future__ import annotations
