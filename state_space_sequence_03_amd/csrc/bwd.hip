@@ -143,8 +143,16 @@ __device__ __forceinline__ floatx8 frag32(const bf16* p) {
 }
 __device__ __forceinline__ floatx8 frag32(const float* p) { return load_frag(p); }
 
+// Occupancy: both per-chunk kernels fit four workgroups per CU in LDS but
+// need ~150-160 VGPRs (three waves per SIMD).  For bf16 io up to dstate 128 /
+// headdim 64 they are built for four waves per SIMD (128 VGPRs, a ~90-byte
+// spill per lane): 4.90 against 5.10 ms at the 2.7B shape.  The wider
+// instantiations would spill several hundred bytes and keep the default.
+template <typename T, int NKN, int NKP>
+constexpr int bwd_min_waves() { return sizeof(T) == 2 && NKN <= 8 && NKP <= 4 ? 4 : 1; }
+
 template <typename T, int NKN>
-__global__ void __launch_bounds__(kBwdThreads)
+__global__ void __launch_bounds__(kBwdThreads, (bwd_min_waves<T, NKN, 4>()))
 bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
                   const T* __restrict__ dy, const float* __restrict__ Gw,
                   const float* __restrict__ dtw, const float* __restrict__ Hc,
@@ -317,7 +325,7 @@ __host__ __device__ inline int bwd_source_bytes(int P, int N) {
 }
 
 template <typename T, int NKN, int NKP>
-__global__ void __launch_bounds__(kBwdThreads)
+__global__ void __launch_bounds__(kBwdThreads, (bwd_min_waves<T, NKN, NKP>()))
 bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
                   const T* __restrict__ dy, const float* __restrict__ Gw,
                   const float* __restrict__ dtw, const float* __restrict__ Lam,
