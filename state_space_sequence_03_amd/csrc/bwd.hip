@@ -39,11 +39,13 @@
 // The per-chunk terms: one workgroup per (chunk, head, batch) walks 32-token
 // blocks of the chunk; two kernels, one for the reading side (dC, P) and one
 // for the read side (dx, dB, Qr), each keeping its outputs in registers
-// across the pairs of blocks.  The chunk x chunk products C B^T and dy x^T
-// run on MFMA from io-dtype LDS tiles (bf16 operands are exact and the sums
-// fp32; fp32 io uses the fp32 MFMA), the products with the fp32 weights and
-// the carried terms on the vector ALU.  dB and dC are written per head in
-// fp32 and summed over the heads of a group by a final pass.
+// across the pairs of blocks.  Every product runs on MFMA: the chunk x chunk
+// products C B^T and dy x^T from io-dtype LDS tiles (bf16 operands are exact
+// and the sums fp32; fp32 io uses the fp32 MFMA); the products with the fp32
+// weights W, U, V as split-bf16 MFMAs for bf16 io (fp32 MFMA for fp32 io);
+// the carried terms, which feed the step-size gradient, on the exact fp32
+// MFMA.  dB and dC are written per head in fp32 and summed over the heads of
+// a group by a final pass.
 #include "ssd_device.hpp"
 
 namespace ssd {
