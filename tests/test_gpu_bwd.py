@@ -70,6 +70,15 @@ CASES = {
     "bf16_q128_raw_dt_clamped": (dict(batch=1, seqlen=260, nheads=4, headdim=64, dstate=128,
                                       ngroups=2, chunk_size=128, io_dtype="bf16", init_std=0.1),
                                  True, True, (True, (0.01, 0.08))),
+    # headdim / dstate not multiples of 32: zero-padded MFMA K-steps and a
+    # half-empty last state pass
+    "bf16_p48_n48": (dict(batch=1, seqlen=100, nheads=2, headdim=48, dstate=48, ngroups=1,
+                          chunk_size=64, io_dtype="bf16", init_std=0.1), True, True, None),
+    "fp32_p80_n80_g2": (dict(batch=2, seqlen=90, nheads=4, headdim=80, dstate=80, ngroups=2,
+                             chunk_size=32, io_dtype="fp32", init_std=0.1), True, True, None),
+    # fewer tokens than one 32-token block
+    "bf16_seq5": (dict(batch=3, seqlen=5, nheads=2, headdim=16, dstate=16, ngroups=1,
+                       chunk_size=64, io_dtype="bf16", init_std=0.1), True, True, None),
 }
 
 
