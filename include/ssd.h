@@ -373,6 +373,13 @@ ssd_status ssd_bwd_workspace_size(const ssd_problem* prob, size_t* bytes);
  *   ddt_bias    : output [nheads] fp32, or NULL: the sum of ddt over batch
  *                 and tokens, i.e. the gradient with respect to a per-head
  *                 bias added to the dt argument.
+ * Precision: every gradient is formed in fp32 from the io values, with the
+ * chunk-boundary states and their gradients kept in fp32 (the step-size
+ * gradient sums terms that largely cancel over the whole sequence); for bf16
+ * io the chunk x chunk products run on bf16 MFMA (exact operands, fp32 sums)
+ * and the products with fp32 weights as two bf16 MFMAs on a hi/lo split of
+ * the weights (~16 significant bits); only dx, dB and dC are rounded to the
+ * io dtype.  Deterministic: the same call gives bitwise the same results.
  * Outputs must not overlap inputs or each other.  Every pointer 16-byte
  * aligned.  Errors as for ssd_fwd_ex (same order: NULL pointers, shape,
  * chunk, dtype, transform values, alignment, limits, workspace); in
