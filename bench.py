@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Throughput of the Mamba-2 chunked SSD forward pass (libssd) on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input:
-chunk_cumsum -> chunk_state -> state_pass -> compute_out, enqueued through the C ABI
-(ssd_fwd_states, then ssd_compute_out -- exactly the launches ssd_fwd makes;
-the split lets HIP events bracket the dominant kernel inside the timed loop).
-Inputs are resident in HBM before timing starts.  Prints one JSON line.
+One step = one ssd_fwd through the C ABI: the whole hot path over one batch of
+synthetic input (the single-pass fused kernel where it is built, else
+chunk_cumsum -> chunk_state -> state_pass -> compute_out).  Inputs are resident
+in HBM before timing starts.  The headline is the median of the timed steps
+with the 256 MB last-level cache flushed before each (the fill is outside the
+events); p10/p90, the mean and the warm back-to-back rate are reported beside
+it.  Prints one JSON line.
 
 Default workload: the Mamba-2 2.7B-shaped layer, batch 2 x seqlen 8192,
 80 heads, headdim 64, dstate 128, 1 group, chunk 256, bf16 x/B/C, fp32
@@ -51,10 +53,12 @@ DECODE_METRIC = "SSD decode tokens/sec (batch, one token per step) at 1 MI355X; 
 BWD_METRIC = "SSD bwd tokens/sec (batch·seqlen) at 1 MI355X; % of MFMA roofline"
 COPY_PROBE_BYTES = 1 << 30
 DEFAULT_WORKLOAD = "mamba2_2p7b"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compute_out_{workload}_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "state_space_sequence_03_amd", "csrc", f)
-                  for f in ("compute_out.hip", "ssd_device.hpp")] + \
-                 [os.path.join(ROOT, "state_space_sequence_03_amd", "build.py")]   # compile flags
+# committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries of the dominant kernel,
+# valid while the sources they were taken from are unchanged
+TRAFFIC = {
+    "fused_fwd_kernel": ("fused_fwd_{workload}_traffic.txt", ["fused_fwd.hip", "ssd_device.hpp"]),
+    "compute_out": ("compute_out_{workload}_traffic.txt", ["compute_out.hip", "ssd_device.hpp"]),
+}
 
 
 def counts(p):
@@ -79,18 +83,20 @@ def counts(p):
                 units_out=Bz * H * T, tokens=Bz * L)
 
 
-def source_digest():
+def source_digest(kernel):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    files = [os.path.join(ROOT, "state_space_sequence_03_amd", "csrc", f) for f in TRAFFIC[kernel][1]]
+    files.append(os.path.join(ROOT, "state_space_sequence_03_amd", "build.py"))   # compile flags
+    for f in files:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
-    """HBM bytes per compute_out launch from committed rocprofv3 counters, or None
-    when the file is missing or the kernel source changed since it was taken."""
-    path = TRAFFIC_FILE.format(workload=workload)
+def read_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counters, or
+    None when the file is missing or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC[kernel][0].format(workload=workload))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -98,7 +104,7 @@ def read_traffic(workload):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_digest") != source_digest():
+    if vals.get("source_digest") != source_digest(kernel):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -106,12 +112,15 @@ def read_traffic(workload):
         return None
 
 
-def cpu_baseline(inputs, prob, target_seconds=15.0):
+def cpu_baseline(inputs, prob, target_seconds=15.0, gpu_out=None, raw_dt=False):
     """Time the fp64 oracle (the token recurrence, OpenMP over (batch, head)) on
     the host, on a bounded sample of the workload: the first `nh` heads of every
     batch over the whole sequence, sized from a short probe to take about
     `target_seconds`, or the whole workload when that fits.  Tokens/s is scaled
-    to the full head count."""
+    to the full head count.  With gpu_out = (y, final_state) from the GPU
+    run, the oracle's outputs of the sampled heads are also compared with it
+    (rel-L2 over the sampled part, max-abs / max|ref|)."""
+    import numpy as np
     import oracle
 
     nthreads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
@@ -123,25 +132,25 @@ def cpu_baseline(inputs, prob, target_seconds=15.0):
         sel = lambda a: a[:, :, :nh]
         init = arrs["init_state"]
         t0 = time.perf_counter()
-        oracle.recurrence(sel(arrs["x"]), sel(arrs["dt"]), arrs["A"][:nh], arrs["B"][:, :, :g],
-                          arrs["C"][:, :, :g], arrs["D"][:nh],
-                          None if init is None else init[:, :nh], nthreads=nthreads)
-        return time.perf_counter() - t0
+        out = oracle.recurrence(sel(arrs["x"]), sel(arrs["dt"]), arrs["A"][:nh], arrs["B"][:, :, :g],
+                                arrs["C"][:, :, :g], arrs["D"][:nh],
+                                None if init is None else init[:, :nh], nthreads=nthreads)
+        return time.perf_counter() - t0, out
 
     def legal(nh):   # head counts whose group mapping matches the full problem
         nh = max(1, min(H, nh))
         return nh if nh <= hpg else nh // hpg * hpg
 
     probe_heads = legal(min(H, max(1, nthreads // max(1, prob.batch))))
-    probe = run(probe_heads)
+    probe, _ = run(probe_heads)
     nh = legal(int(target_seconds / max(probe, 1e-6) * probe_heads))
-    dt = run(nh)
+    dt, out = run(nh)
     reps = 1
     if nh == H and dt < target_seconds:
         # the whole workload takes less than the target: repeat it, so the
         # figure averages over about target_seconds of host work
         reps = max(1, min(200, int(round(target_seconds / max(dt, 1e-6)))))
-        dt = sum(run(nh) for _ in range(reps))
+        dt = dt + sum(run(nh)[0] for _ in range(reps - 1))
     tok_s = reps * prob.batch * prob.seqlen * (nh / H) / dt
     if nh == H:
         sample = ("full workload: %d (batch, head) pairs x %d tokens, run %d times"
@@ -149,8 +158,24 @@ def cpu_baseline(inputs, prob, target_seconds=15.0):
     else:
         sample = ("heads 0..%d of %d in each of %d batches, %d tokens each; tokens/s scaled by %d/%d"
                   % (nh - 1, H, prob.batch, prob.seqlen, nh, H))
-    return {"value": tok_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 3)}
+    res = {"value": tok_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+           "sample": sample, "seconds": round(dt, 3)}
+    if gpu_out is not None and not raw_dt:
+        y_ref, fin_ref, _ = out
+
+        def err(got, ref):
+            g = got.float().cpu().double().numpy()
+            dlt = g - ref
+            return (float(np.linalg.norm(dlt) / max(np.linalg.norm(ref), 1e-300)),
+                    float(np.max(np.abs(dlt)) / max(np.max(np.abs(ref)), 1e-300)))
+        yr, ya = err(gpu_out[0][:, :, :nh], y_ref)
+        fr, fa = err(gpu_out[1][:, :nh], fin_ref)
+        res["parity"] = {"heads_compared": "%d of %d (every batch, whole sequence)" % (nh, H),
+                         "y_rel_l2": yr, "y_max_abs_frac": ya,
+                         "final_rel_l2": fr, "final_max_abs_frac": fa,
+                         "tolerance": {"rel_l2": 5e-3, "max_abs_frac": 2e-2}
+                         if prob.io_dtype == "bf16" else {"rel_l2": 1e-5, "max_abs_frac": 1e-4}}
+    return res
 
 
 def bwd_counts(p):
@@ -413,7 +438,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -477,103 +502,80 @@ def main():
         return
     pr = ssd.make_problem(prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate,
                           prob.ngroups, Q, ssd.SSD_BF16 if prob.io_dtype == "bf16" else ssd.SSD_F32)
+    cfg = ssd.ssd_default_config(pr)
+    fused = bool(cfg["fused"])
     ws = torch.empty(ssd.ssd_fwd_workspace_size(pr), dtype=torch.uint8, device=dev)
     y = torch.empty_like(d["x"])
     fin = torch.empty((prob.batch, prob.nheads, prob.headdim, prob.dstate), dtype=torch.float32,
                       device=dev)
+    dt_kw = dict(dt_bias=d["dt_bias"], dt_softplus=True) if args.raw_dt else {}
+    dt_in = d["dt_raw"] if args.raw_dt else d["dt"]
 
-    def step(ev_a=None, ev_b=None, ev_c=None):
-        # events are recorded only where given: the timed loop brackets
-        # compute_out alone (its roofline), each event costing ~4 us per step
-        if ev_a is not None:
-            ev_a.record()
-        if args.raw_dt:
-            ssd.ssd_fwd_states(d["x"], d["dt_raw"], d["A"], d["B"], Q, d["init_state"],
-                               want_chunk_states=False, workspace=ws, final_out=fin,
-                               dt_bias=d["dt_bias"], dt_softplus=True)
-        else:
-            ssd.ssd_fwd_states(d["x"], d["dt"], d["A"], d["B"], Q, d["init_state"],
-                               want_chunk_states=False, workspace=ws, final_out=fin)
-        if ev_b is not None:
-            ev_b.record()
-        ssd.ssd_compute_out(d["x"], d["B"], d["C"], d["D"], Q, ws, out=y)
-        if ev_c is not None:
-            ev_c.record()
+    def fwd():
+        ssd.ssd_fwd(d["x"], dt_in, d["A"], d["B"], d["C"], d["D"], Q, d["init_state"], out=y,
+                    final_out=fin, workspace=ws, **dt_kw)
 
     if args.graph:
-        # the whole pass captured once; each step is one replay (no per-step
-        # events: the launches are what the graph saves)
-        step()
-        torch.cuda.synchronize()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-        cnt = counts(prob)
-        print(json.dumps({"metric": METRIC + " (HIP graph replay)", "value": cnt["tokens"] / (ms_step * 1e-3),
-                          "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-                          "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-                          "dtype": prob.io_dtype, "data": "synthetic",
-                          "config": {"workload": args.workload, "graph": True}}), flush=True)
+        graph_line(args, prob, fwd)
         return
 
     for _ in range(args.warmup):
-        step()
+        fwd()
     torch.cuda.synchronize()
 
+    # timed region: K steps, each after a 512 MiB fill that evicts the 256 MB
+    # last-level cache (outside the events), each bracketed by HIP events on
+    # the stream the kernels run on (torch's current stream)
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        step(None, *ev[k])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / K
-    ms_out = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    ms_states = ms_step - ms_out      # the rest of the step: chunk_cumsum, chunk_state, state_pass
-
-    # same steps with the 256 MB last-level cache flushed before each (event-timed)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold = []
-    for k in range(min(K, 20)):
         flush.fill_(k & 0xFF)
-        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        step(a, b, c)
-        torch.cuda.synchronize()
-        cold.append((a.elapsed_time(c), a.elapsed_time(b), b.elapsed_time(c)))
+        evs[k][0].record()
+        fwd()
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cold = sorted(a.elapsed_time(b) for a, b in evs)
+    cold_mean = sum(cold) / K
+    ms_step = cold[K // 2] if K % 2 else 0.5 * (cold[K // 2 - 1] + cold[K // 2])
+    p10, p90 = cold[int(0.1 * (K - 1))], cold[int(round(0.9 * (K - 1)))]
     del flush
-    cold.sort()
-    cold_med = cold[len(cold) // 2]
+
+    # secondary: the warm back-to-back rate (inputs partly in the last-level cache)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        fwd()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / K
+    timed_out = ssd.ssd_fwd_status(ws)
 
     cnt = counts(prob)
-    tok_s = cnt["tokens"] / (ms_step * 1e-3)
     peak_mfma = PEAK_BF16_MFMA if prob.io_dtype == "bf16" else PEAK_FP32_MFMA
-    t_out = ms_out * 1e-3
-    out_tflops = cnt["f_out"] / t_out
-    out_gbs = cnt["b_out"] / t_out
-    # compute_out's bound: whichever roofline gives the longer lower bound
-    if cnt["b_out"] / PEAK_HBM >= cnt["f_out"] / peak_mfma:
-        bound, achieved, peak, unit = "hbm", out_gbs / 1e9, PEAK_HBM / 1e9, "GB/s"
+    if fused:
+        # the fused kernel is the whole step: its launch is what the events bracket
+        kname, k_ms, k_flops, k_bytes = "fused_fwd_kernel", cold_mean, cnt["f_path"], cnt["b_min"]
+        units = cnt["units_out"]
+        per_unit = {"flops": cnt["f_path"] / units, "bytes": cnt["b_min"] / units}
     else:
-        bound, achieved, peak, unit = "mfma", out_tflops / 1e12, peak_mfma / 1e12, "TFLOP/s"
-    traffic = read_traffic(args.workload)
+        kname, k_ms = "compute_out", staged_compute_out_ms(args, ssd, prob, d, ws, y, dt_in, dt_kw)
+        k_flops, k_bytes = cnt["f_out"], cnt["b_out"]
+        units = cnt["units_out"]
+        per_unit = {"flops": cnt["f_out"] / units, "bytes": cnt["b_out"] / units}
+    t_k = k_ms * 1e-3
+    if k_bytes / PEAK_HBM >= k_flops / peak_mfma:
+        bound, achieved, peak, unit = "hbm", k_bytes / t_k / 1e9, PEAK_HBM / 1e9, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", k_flops / t_k / 1e12, peak_mfma / 1e12, "TFLOP/s"
 
     line = {
         "metric": METRIC,
-        "value": tok_s,
+        "value": cnt["tokens"] / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
@@ -588,21 +590,80 @@ def main():
                    "nheads": prob.nheads, "headdim": prob.headdim, "dstate": prob.dstate,
                    "ngroups": prob.ngroups, "chunk_size": Q,
                    "init_state": prob.init_std is not None, "accumulate": "fp32",
-                   "dt": "raw, bias + softplus in chunk_cumsum" if args.raw_dt else "prepared"},
+                   "kernels": "fused single pass" if fused else "staged (4 kernels)",
+                   "dt": "raw, bias + softplus in the first stage" if args.raw_dt else "prepared"},
+        "timing": {"ms_per_step": "median of the timed steps, last-level cache flushed before each",
+                   "p10_ms": p10, "p90_ms": p90, "mean_ms": cold_mean,
+                   "warm_ms_per_step": warm_ms, "warm_tokens_per_s": cnt["tokens"] / (warm_ms * 1e-3),
+                   "wall_s": wall},
         "path_mfma_frac": cnt["f_path"] / (ms_step * 1e-3) / peak_mfma,
         "path_hbm_frac": cnt["b_min"] / (ms_step * 1e-3) / PEAK_HBM,
         "path_tflops": cnt["f_path"] / (ms_step * 1e-3) / 1e12,
-        "stage_ms": {"chunk_cumsum+chunk_state+state_pass (step - compute_out)": ms_states,
-                     "compute_out (events)": ms_out},
-        "cold_ms_per_step": {"median": cold_med[0], "states": cold_med[1], "compute_out": cold_med[2]},
-        "roofline": {"kernel": "compute_out", "bound": bound, "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak,
-                     "traffic": traffic,
-                     "mfma_frac": out_tflops / peak_mfma, "hbm_frac": out_gbs / PEAK_HBM},
+        "roofline": {"kernel": kname, "bound": bound, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak, "traffic": read_traffic(kname, args.workload),
+                     "kernel_ms": k_ms, "units_per_launch": units, "per_unit": per_unit,
+                     "mfma_frac": k_flops / t_k / peak_mfma, "hbm_frac": k_bytes / t_k / PEAK_HBM},
+        "inputs_sha256": {k: ssd_synth.tensor_digest(v) for k, v in inputs.items()
+                          if k in ("x", "dt", "dt_raw", "dt_bias", "A", "B", "C", "D", "init_state")},
+        "status_timed_out": timed_out,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inputs, prob)
+        line["cpu_baseline"] = cpu_baseline(inputs, prob, gpu_out=(y, fin),
+                                            raw_dt=args.raw_dt)
     print(json.dumps(line), flush=True)
+
+
+def staged_compute_out_ms(args, ssd, prob, d, ws, y, dt_in, dt_kw):
+    """Mean event-timed compute_out launch on the staged path (stages 1-2 and
+    stage 3 enqueued separately, cache flushed before each step)."""
+    import torch
+    Q = prob.chunk_size
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=d["x"].device)
+    fin = torch.empty((prob.batch, prob.nheads, prob.headdim, prob.dstate), dtype=torch.float32,
+                      device=d["x"].device)
+    tot = 0.0
+    n = max(1, args.steps)
+    for k in range(n):
+        flush.fill_(k & 0xFF)
+        ssd.ssd_fwd_states(d["x"], dt_in, d["A"], d["B"], Q, d["init_state"],
+                           want_chunk_states=False, workspace=ws, final_out=fin, **dt_kw)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ssd.ssd_compute_out(d["x"], d["B"], d["C"], d["D"], Q, ws, out=y)
+        b.record()
+        torch.cuda.synchronize()
+        tot += a.elapsed_time(b)
+    return tot / n
+
+
+def graph_line(args, prob, fwd):
+    """Each step replays one captured HIP graph of the whole pass."""
+    import torch
+    fwd()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    cnt = counts(prob)
+    print(json.dumps({"metric": METRIC + " (HIP graph replay, warm)",
+                      "value": cnt["tokens"] / (ms_step * 1e-3), "unit": "tokens/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": ms_step, "higher_is_better": True,
+                      "dtype": prob.io_dtype, "data": "synthetic",
+                      "config": {"workload": args.workload, "graph": True}}), flush=True)
 
 
 if __name__ == "__main__":

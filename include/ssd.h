@@ -20,10 +20,17 @@
  * CUDA Tile", sections 4-9:
  *   1. chunk_cumsum   -- within-chunk running sum of a_t, scaled by log2(e);
  *   2. chunk_state    -- every chunk's own state contribution by the jump
- *                        formula, all chunks at once;
+ *                        formula;
  *      state_pass     -- the sequential pass of states across chunks;
  *   3. compute_out    -- causal-masked decayed interaction tile, carried-state
  *                        term and D skip fused, nothing chunk x chunk in HBM.
+ * Two builds of these stages exist.  The fused kernel (bf16 io, headdim 64,
+ * dstate 128, chunk_size 256, an even number of heads per group) runs all
+ * stages per (chunk, head pair) in one pass over x, handing each chunk's
+ * state to the next chunk's workgroup through device memory.  The staged
+ * kernels (every supported shape) run them as four kernels with the running
+ * sums and chunk-start states in the workspace.  ssd_fwd takes the fused one
+ * where it is built (ssd_config.fused selects explicitly).
  * The result equals the token recurrence up to floating-point rounding.
  * ssd_step runs the same recurrence token by token from a resident state
  * (decode).
@@ -80,7 +87,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
@@ -138,6 +145,11 @@ typedef struct {
 /* Tile choices of the forward pass's kernels, for shape tuning.  The pages
  * tune block sizes and occupancy per shape; here the alternatives are ones
  * the library compiles, chosen per problem at run time:
+ *   fused        : 1 = the single-pass fused kernel (built for bf16 io,
+ *                  headdim 64, dstate 128, chunk_size 256 and an even number
+ *                  of heads per group), 0 = the staged kernels; the three
+ *                  fields below are checked in both cases and used by the
+ *                  staged kernels only;
  *   cumsum_heads : heads per chunk_cumsum workgroup, 4 or 16;
  *   state_heads  : heads per chunk_state workgroup (they share the chunk's B
  *                  rows), 1, 2 or 4, dividing the heads of a group;
@@ -152,7 +164,7 @@ typedef struct {
   int32_t cumsum_heads;
   int32_t state_heads;
   int32_t out_heads;
-  int32_t reserved;     /* must be 0 */
+  int32_t fused;        /* 0 or 1 */
 } ssd_config;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION at build time). */
@@ -165,15 +177,42 @@ const char* ssd_status_string(int status);
  * The pointer stays valid until the thread's next libssd call. */
 const char* ssd_last_error_message(void);
 
-/* Workspace bytes that ssd_fwd and ssd_fwd_states need for `prob`:
- * two fp32 [batch, nheads, T*Q] arrays (the base-2 running sums G and dt in
- * [batch, head, token] order), the chunk-start states [batch, nheads, T,
- * headdim, dstate] in the io dtype (in an internal fragment order, padded to
- * whole 64-row and 32-column tiles), each segment 256-byte aligned, and 4 KiB
- * of scratch at the end.
+/* Workspace bytes enough for every forward entry point and configuration on
+ * `prob`: the larger of the two layouts below.  Every forward workspace
+ * starts with a 256-byte header: the status word of ssd_fwd_status and the
+ * tag of the latest call.  The staged kernels then use two fp32 [batch,
+ * nheads, T*Q] arrays (the base-2 running sums G and dt in [batch, head,
+ * token] order) and the chunk-start states [batch, nheads, T, headdim,
+ * dstate] in the io dtype (in an internal fragment order, padded to whole
+ * 64-row and 32-column tiles); the fused kernel uses one 8-byte flag per
+ * (batch, head, 32 x 32 state tile) and, when final_state is NULL, an fp32
+ * [batch, nheads, headdim, dstate] state buffer.  Segments are 256-byte
+ * aligned.  No part of a workspace needs to hold anything on entry.
  * Writes the size to *bytes.  Errors: NULL_POINTER, BAD_SHAPE, BAD_CHUNK,
  * BAD_DTYPE, UNSUPPORTED. */
 ssd_status ssd_fwd_workspace_size(const ssd_problem* prob, size_t* bytes);
+
+/* Workspace bytes that ssd_fwd_config needs with configuration `cfg` (NULL =
+ * the default one, what ssd_fwd uses): the header and the layout of that
+ * configuration's kernels only.  ssd_fwd_states, ssd_compute_out and
+ * ssd_tune need the staged layout (cfg with fused = 0).  Errors: as
+ * ssd_fwd_workspace_size, and BAD_VALUE for an invalid configuration. */
+ssd_status ssd_fwd_config_workspace_size(const ssd_problem* prob, const ssd_config* cfg,
+                                         size_t* bytes);
+
+/* Whether the latest forward call on `workspace` gave up a bounded wait.
+ * The forward kernels hand data between workgroups (the fused kernel from
+ * chunk to chunk, compute_out between the waves of a workgroup) through waits
+ * that cannot deadlock when the kernel's workgroups run concurrently, but
+ * are bounded anyway; a wait past its bound marks the call in the workspace
+ * header and leaves y and final_state undefined.  This call copies the
+ * header to the host after synchronising with `stream` (it SYNCHRONISES) and
+ * sets *timed_out to 1 if the latest call that used the workspace timed out,
+ * else 0.  workspace: the one given to that call (16-byte aligned, at least
+ * 16 bytes).  Errors: NULL_POINTER (timed_out or workspace NULL),
+ * MISALIGNED, WORKSPACE (fewer than 16 bytes), HIP. */
+ssd_status ssd_fwd_status(const void* workspace, size_t workspace_bytes, void* stream,
+                          int32_t* timed_out);
 
 /* Full forward pass: chunk_cumsum -> chunk_state -> state_pass -> compute_out.
  *   x, dt, A, B, C : inputs (device), layouts above.
@@ -181,9 +220,11 @@ ssd_status ssd_fwd_workspace_size(const ssd_problem* prob, size_t* bytes);
  *   init_state     : [batch, nheads, headdim, dstate] fp32, or NULL for zeros.
  *   y              : output [batch, seqlen, nheads, headdim] in the io dtype.
  *   final_state    : output state after the last token (fp32), or NULL.
- *   workspace      : device scratch of at least ssd_fwd_workspace_size bytes,
- *                    16-byte aligned, owned by the caller; its contents on
- *                    entry do not matter.
+ *   workspace      : device scratch of at least ssd_fwd_config_workspace_size
+ *                    (prob, NULL) bytes (ssd_fwd_workspace_size is always
+ *                    enough), 16-byte aligned, owned by the caller; its
+ *                    contents on entry do not matter.  One workspace serves
+ *                    one call at a time.
  *   stream         : hipStream_t to enqueue on (NULL = default stream). */
 ssd_status ssd_fwd(const ssd_problem* prob, const void* x, const float* dt, const float* A,
                    const void* B, const void* C, const float* D, const float* init_state,
@@ -204,8 +245,9 @@ ssd_status ssd_default_config(const ssd_problem* prob, ssd_config* cfg);
 
 /* ssd_fwd_ex with the kernels' tile choices given (cfg = NULL: the default,
  * making this exactly ssd_fwd_ex).  An invalid choice is SSD_ERR_BAD_VALUE
- * (checked with the transform, before alignment).  Same workspace,
- * arguments, outputs and other errors as ssd_fwd. */
+ * (checked with the transform, before alignment).  The workspace must hold
+ * ssd_fwd_config_workspace_size(prob, cfg) bytes.  Same arguments, outputs
+ * and other errors as ssd_fwd. */
 ssd_status ssd_fwd_config(const ssd_problem* prob, const ssd_config* cfg,
                           const ssd_dt_transform* dtx, const void* x, const float* dt,
                           const float* A, const void* B, const void* C, const float* D,
@@ -271,7 +313,10 @@ ssd_status ssd_chunk_cumsum_ex(const ssd_problem* prob, const ssd_dt_transform* 
  *   chunk_states : output [batch, nheads, T, headdim, dstate] in the io dtype
  *                  (H_c for c = 0..T-1), or NULL.
  *   final_state  : output [batch, nheads, headdim, dstate] fp32 (required).
- * Other arguments as for ssd_fwd. */
+ *   workspace    : the staged layout (ssd_fwd_config_workspace_size with
+ *                  fused = 0, or ssd_fwd_workspace_size).
+ * Other arguments as for ssd_fwd.  These are the staged kernels whatever the
+ * shape. */
 ssd_status ssd_fwd_states(const ssd_problem* prob, const void* x, const float* dt,
                           const float* A, const void* B, const float* init_state,
                           float* final_state, void* chunk_states, void* workspace,
@@ -296,16 +341,13 @@ ssd_status ssd_fwd_states_ex(const ssd_problem* prob, const ssd_dt_transform* dt
  * "NVIDIA CUDA Tile로 Mamba-2 순방향 전달 커널 가속화", section "세 가지 핵심
  * 커널 구현", compute_out, and brifing.si "Accelerating Mamba-2 ...", sections
  * 9 and 11; the chunk x chunk tile is never written to memory.
- * ssd_fwd is exactly ssd_fwd_states followed by ssd_compute_out.
+ * With the staged kernels (ssd_config.fused = 0) ssd_fwd is exactly
+ * ssd_fwd_states followed by ssd_compute_out.
  *   x, B, C, D, y : as for ssd_fwd (D may be NULL).
- *   workspace     : at least ssd_fwd_workspace_size bytes; its running sums
- *                   and states are only read, its last 4 KiB are scratch
- *                   that the call may overwrite.  The kernel's waves hand
- *                   shared LDS buffers to each other through bounded waits;
- *                   a wait past its bound (never expected: the hand-off
- *                   cannot deadlock) sets bit 0 of the scratch's first
- *                   32-bit word and leaves y undefined.  A caller that wants
- *                   to check it clears that word before the call.
+ *   workspace     : the staged layout (ssd_fwd_config_workspace_size with
+ *                   fused = 0); its running sums and states are only read,
+ *                   its header is written (ssd_fwd_status reports whether
+ *                   the kernel's bounded waits all ended in time).
  * Errors as for ssd_fwd. */
 ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B, const void* C,
                            const float* D, void* y, const void* workspace,

@@ -41,7 +41,8 @@ _LIB = os.path.join(_HERE, "libssd_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-__all__ = ["build", "load_library", "recurrence", "recurrence_heads", "chunk_cumsum", "dense_matrix",
+__all__ = ["build", "load_library", "recurrence", "recurrence_heads", "recurrence_head_ranges",
+           "chunk_cumsum", "dense_matrix",
            "linear_attention", "chunked", "as_f32", "dt_transform", "softplus",
            "recurrence_bwd", "dt_transform_bwd"]
 
@@ -69,12 +70,18 @@ def load_library(path):
 
 
 def _load():
+    """The default build, or the one SSD_ORACLE_LIBRARY names (the host
+    sanitizer tests load an instrumented build that way)."""
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-                build(force=True)
-            _lib = load_library(_LIB)
+            other = os.environ.get("SSD_ORACLE_LIBRARY")
+            if other:
+                _lib = load_library(other)
+            else:
+                if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                    build(force=True)
+                _lib = load_library(_LIB)
     return _lib
 
 
@@ -148,6 +155,31 @@ def recurrence_heads(inputs, heads, nthreads=None):
                                init_bh, nthreads=nthreads)
         out[(b, h)] = (y[0, :, 0], fin[0, 0])
     return out
+
+
+def recurrence_head_ranges(inputs, heads_per_range, nthreads=None):
+    """The recurrence over every head, a range of whole groups at a time.
+
+    Yields (h0, h1, y [batch, seqlen, h1-h0, headdim], final [batch, h1-h0,
+    headdim, dstate]) for consecutive head ranges covering all heads, each
+    range holding whole groups (heads_per_range is rounded up to a multiple
+    of the heads per group).  Every (batch, head) is computed, so a caller
+    can compare a whole output tensor while holding only one range of the
+    fp64 result at a time.  The arithmetic is ``recurrence`` itself: a range
+    of whole groups is the same problem restricted to those heads and
+    groups.
+    """
+    x, dt, A, B, C, D, init = (inputs[k] for k in ("x", "dt", "A", "B", "C", "D", "init_state"))
+    H, G = x.shape[2], B.shape[2]
+    hpg = H // G
+    step = max(hpg, -(-int(heads_per_range) // hpg) * hpg)
+    for h0 in range(0, H, step):
+        h1 = min(H, h0 + step)
+        g0, g1 = h0 // hpg, h1 // hpg
+        y, fin, _ = recurrence(x[:, :, h0:h1], dt[:, :, h0:h1], A[h0:h1], B[:, :, g0:g1],
+                               C[:, :, g0:g1], None if D is None else D[h0:h1],
+                               None if init is None else init[:, h0:h1], nthreads=nthreads)
+        yield h0, h1, y, fin
 
 
 def chunk_cumsum(dt, A, chunk_size):

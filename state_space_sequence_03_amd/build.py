@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libssd.so")
 
 SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "state_pass.hip", "compute_out.hip", "step.hip",
-           "bwd.hip", "ssd_api.cpp"]
+           "bwd.hip", "fused_fwd.hip", "ssd_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -69,7 +69,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source and link libssd.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs

@@ -69,16 +69,17 @@ constexpr int kOutStaticLds = 256;   // bound on the kernel's static LDS (the sl
 // reading it); both only grow, by kOutWaves per use of the slot.
 //
 // Wait until an LDS counter reaches `target`.  The wait is bounded: past the
-// bound the wave goes on and sets bit 0 of *flag rather than hang the
-// workgroup (the protocol cannot deadlock, so this marks a bug).
-__device__ __forceinline__ void wait_count(int* ctr, int target, int* flag, int lane) {
+// bound the wave goes on and reports the timeout in the call's status word
+// rather than hang the workgroup (the protocol cannot deadlock, so this marks
+// a bug).
+__device__ __forceinline__ void wait_count(int* ctr, int target, StatusRef flag, int lane) {
   for (int spins = 0;; ++spins) {
     // an atomic (not volatile) load, so it stays an LDS read
     const int v = __builtin_amdgcn_readfirstlane(
         __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
     if (v >= target) break;
     if (spins >= kSpinLimit) {
-      if (lane == 0) atomicOr(flag, 1);
+      if (lane == 0) report_timeout(flag);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -392,7 +393,7 @@ __global__ void __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_e
 compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
                    const float* __restrict__ Gw, const float* __restrict__ dtw,
                    const T* __restrict__ Hc, const float* __restrict__ Dv, T* __restrict__ y,
-                   int* __restrict__ flag, int64_t L, int H, int P, int N, int G, int Q, int T_,
+                   StatusRef flag, int64_t L, int H, int P, int N, int G, int Q, int T_,
                    int64_t ldw, int nbc, int PB, int RS) {
   typedef typename FragOf<T>::type frag_t;
   typedef Slot<T, NK, KH> S;
@@ -413,6 +414,7 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
   // different chunks, so the workgroups running at one time spread their
   // reads over several chunks' rows instead of all reading the same lines.
   const int id = blockIdx.x;
+  if (id == 0 && threadIdx.x == 0) record_call(flag);
   const int xcd = id % 8, slot_id = id / 8;
   const int nbx = (nbc + 7) / 8;
   const int bc = (slot_id % nbx) * 8 + xcd;
@@ -530,6 +532,7 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
             hstage + g * 1024);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __asm__ __volatile__("" ::: "memory");   // LDS written by the direct loads is read below
     if (npairs > 0) bump_count(&arrived[0], lane);   // this wave's share of pair 0 landed
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -558,6 +561,7 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
                                ? load_frag(hc_src(hh) + hcl.offset(0, pt, ks, lane))
                                : zero_frag<T>();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __asm__ __volatile__("" ::: "memory");   // LDS written by the direct loads is read below
     if (npairs > 0) bump_count(&arrived[0], lane);   // this wave's share of pair 0 landed
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -701,7 +705,7 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
 
 template <typename T, int NK, int IB, int KH>
 static hipError_t launch_out(const void* x, const void* Bm, const void* Cm, const float* Gw,
-                             const float* dtw, const void* Hc, const float* Dv, void* y, int* flag,
+                             const float* dtw, const void* Hc, const float* Dv, void* y, StatusRef flag,
                              int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                              int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
   const OutLayout lay = out_layout<T, NK, KH>(Q);
@@ -737,7 +741,7 @@ int compute_out_default_kh(int io_bf16, int64_t H, int64_t G, int64_t N) {
 template <typename T, int IB, int KH>
 static hipError_t launch_out_nk(int NK, const void* x, const void* Bm, const void* Cm,
                                 const float* Gw, const float* dtw, const void* Hc, const float* Dv,
-                                void* y, int* flag, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                                void* y, StatusRef flag, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                                 int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
 #define SSD_OUT_ARGS x, Bm, Cm, Gw, dtw, Hc, Dv, y, flag, batch, L, H, P, N, G, Q, T_, ldw, stream
   switch (NK) {
@@ -751,7 +755,7 @@ static hipError_t launch_out_nk(int NK, const void* x, const void* Bm, const voi
 
 template <typename T>
 static hipError_t launch_out_t(int kh, const void* x, const void* Bm, const void* Cm, const float* Gw,
-                               const float* dtw, const void* Hc, const float* Dv, void* y, int* flag,
+                               const float* dtw, const void* Hc, const float* Dv, void* y, StatusRef flag,
                                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                                int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
 #define SSD_OUT_ARGS nk_class(N), x, Bm, Cm, Gw, dtw, Hc, Dv, y, flag, batch, L, H, P, N, G, Q, T_, ldw, stream
@@ -780,12 +784,12 @@ int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int kh) {
 
 hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
-                              void* y, void* sink, int64_t batch, int64_t L, int64_t H,
+                              void* y, StatusRef status, int64_t batch, int64_t L, int64_t H,
                               int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
                               int kh, hipStream_t stream) {
   if (io_bf16)
-    return launch_out_t<bf16>(kh, x, Bm, Cm, Gw, dtw, Hc, Dv, y, static_cast<int*>(sink), batch, L, H, P, N, G, Q, T_, ldw, stream);
-  return launch_out_t<float>(kh, x, Bm, Cm, Gw, dtw, Hc, Dv, y, static_cast<int*>(sink), batch, L, H, P, N, G, Q, T_, ldw, stream);
+    return launch_out_t<bf16>(kh, x, Bm, Cm, Gw, dtw, Hc, Dv, y, status, batch, L, H, P, N, G, Q, T_, ldw, stream);
+  return launch_out_t<float>(kh, x, Bm, Cm, Gw, dtw, Hc, Dv, y, status, batch, L, H, P, N, G, Q, T_, ldw, stream);
 }
 
 }  // namespace ssd

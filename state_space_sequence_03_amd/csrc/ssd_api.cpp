@@ -6,6 +6,8 @@
 // synchronising.  No exception leaves this file.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -34,10 +36,17 @@ hipError_t launch_state_pass(int io_bf16, void* S, const float* Gw, const float*
                              hipStream_t stream);
 hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const void* Cm,
                               const float* Gw, const float* dtw, const void* Hc, const float* Dv,
-                              void* y, void* sink, int64_t batch, int64_t L, int64_t H, int64_t P,
+                              void* y, StatusRef status, int64_t batch, int64_t L, int64_t H, int64_t P,
                               int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
                               int kh, hipStream_t stream);
 int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int kh);
+hipError_t launch_fused_fwd(const void* x, const float* dt, const float* A, const void* Bm,
+                            const void* Cm, const float* D, const float* init, float* chain,
+                            void* y, void* flags, void* status, void* last_gen,
+                            const DtXform* xf, int64_t batch, int64_t L, int64_t H, int64_t G,
+                            int Q, int64_t T, unsigned int gen, hipStream_t stream);
+int fused_fwd_supported(int io_bf16, int64_t H, int64_t G, int64_t P, int64_t N, int Q);
+size_t fused_fwd_flag_bytes(int64_t batch, int64_t H, int64_t N);
 int compute_out_kh_valid(int io_bf16, int64_t H, int64_t G, int64_t N, int kh);
 int compute_out_default_kh(int io_bf16, int64_t H, int64_t G, int64_t N);
 int chunk_state_default_kh(int64_t H, int64_t G);
@@ -63,8 +72,28 @@ hipError_t launch_bwd_finish(int io_bf16, const float* Pb, const float* Qb, cons
 namespace {
 
 constexpr int64_t kMaxLds = 160 * 1024;
-constexpr size_t kSinkBytes = 4096;
+// Every forward workspace starts with this header: [0] the status word a
+// kernel writes when a bounded wait gives up ((gen << 32) | 1), [1] the gen
+// of the latest call that used the workspace.
+constexpr size_t kHeaderBytes = 256;
 thread_local std::string g_last_error;
+
+// Call generations.  Each forward call takes a fresh 32-bit value; the fused
+// kernel tags its chunk-to-chunk flags with it (so flags left by an earlier
+// call never match) and both paths tag the status word.  Seeded from the
+// clock so that a workspace reused by another process does not repeat them.
+unsigned int next_gen() {
+  static std::atomic<unsigned int> ctr{0u};
+  static std::atomic<bool> seeded{false};
+  if (!seeded.load(std::memory_order_acquire)) {
+    const auto t = std::chrono::high_resolution_clock::now().time_since_epoch().count();
+    unsigned int expect = 0u;
+    ctr.compare_exchange_strong(expect, (unsigned int)((uint64_t)t ^ ((uint64_t)t >> 32)) | 1u);
+    seeded.store(true, std::memory_order_release);
+  }
+  unsigned int g = ctr.fetch_add(1u, std::memory_order_relaxed);
+  return g ? g : ctr.fetch_add(1u, std::memory_order_relaxed);
+}
 
 ssd_status fail(ssd_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 ssd_status fail(ssd_status st, const char* fmt, ...) {
@@ -95,7 +124,12 @@ struct Plan {
   int64_t B, L, H, P, N, G, Q, T, Lp;
   int bf16;
   size_t esize;
-  size_t g_off, dt_off, hc_off, sink_off, bytes;
+  // staged path: running sums, step sizes, chunk-start states
+  size_t g_off, dt_off, hc_off, staged_bytes;
+  // fused path: chunk-to-chunk flags and the state handed between chunks
+  int fused_ok;
+  size_t flags_off, chain_off, fused_bytes;
+  size_t bytes;   // enough for either path (ssd_fwd_workspace_size)
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -128,6 +162,7 @@ ssd_status plan_problem(const ssd_problem* prob, Plan* pl, bool need_chunk = tru
   pl->Lp = pl->T * Q;
   pl->bf16 = p.io_dtype == SSD_BF16;
   pl->esize = pl->bf16 ? 2 : 4;
+  pl->fused_ok = need_chunk && ssd::fused_fwd_supported(pl->bf16, pl->H, pl->G, pl->P, pl->N, (int)Q);
   return SSD_OK;
 }
 
@@ -157,12 +192,17 @@ ssd_config default_config(const Plan& pl) {
   c.cumsum_heads = 4;
   c.state_heads = ssd::chunk_state_default_kh(pl.H, pl.G);
   c.out_heads = ssd::compute_out_default_kh(pl.bf16, pl.H, pl.G, pl.N);
-  c.reserved = 0;
+  c.fused = pl.fused_ok;
   return c;
 }
 
 ssd_status check_config(const Plan& pl, const ssd_config& c) {
-  if (c.reserved != 0) return fail(SSD_ERR_BAD_VALUE, "config: reserved field must be 0");
+  if (c.fused != 0 && c.fused != 1)
+    return fail(SSD_ERR_BAD_VALUE, "config: fused must be 0 or 1 (got %d)", c.fused);
+  if (c.fused && !pl.fused_ok)
+    return fail(SSD_ERR_BAD_VALUE,
+                "config: the fused kernel is built for bf16 io, headdim 64, dstate 128, "
+                "chunk_size 256 and an even number of heads per group");
   if (c.cumsum_heads != 4 && c.cumsum_heads != 16)
     return fail(SSD_ERR_BAD_VALUE, "config: cumsum_heads must be 4 or 16 (got %d)", c.cumsum_heads);
   const int64_t hg = pl.H / pl.G;
@@ -195,16 +235,23 @@ ssd_status check_supported(const Plan& pl, int out_heads = 0) {
 
 void workspace_plan(Plan* pl) {
   const size_t gsz = size_t(pl->B) * pl->H * pl->Lp * sizeof(float);
-  pl->g_off = 0;
-  pl->dt_off = align256(gsz);
+  pl->g_off = kHeaderBytes;
+  pl->dt_off = pl->g_off + align256(gsz);
   pl->hc_off = pl->dt_off + align256(gsz);
   // chunk-start states, fragment-major (padded to whole 64-row slices and
   // 32-column steps)
   const size_t hcsz = size_t(pl->B) * pl->H * pl->T * size_t(ssd::hc_frag(pl->P, pl->N).state_elems()) *
                       pl->esize;
-  pl->sink_off = pl->hc_off + align256(hcsz);
-  // scratch for stores that are discarded (rows past the sequence end)
-  pl->bytes = pl->sink_off + kSinkBytes;
+  pl->staged_bytes = pl->hc_off + align256(hcsz);
+  pl->flags_off = kHeaderBytes;
+  pl->chain_off = pl->flags_off + align256(ssd::fused_fwd_flag_bytes(pl->B, pl->H, pl->N));
+  pl->fused_bytes = pl->chain_off + align256(size_t(pl->B) * pl->H * pl->P * pl->N * sizeof(float));
+  pl->bytes = pl->staged_bytes;
+  if (pl->fused_ok && pl->fused_bytes > pl->bytes) pl->bytes = pl->fused_bytes;
+}
+
+size_t config_bytes(const Plan& pl, const ssd_config& c) {
+  return c.fused ? pl.fused_bytes : pl.staged_bytes;
 }
 
 // Backward-pass workspace: running sums and step sizes, the reversed-chunk
@@ -306,6 +353,49 @@ ssd_status ssd_fwd_workspace_size(const ssd_problem* prob, size_t* bytes) {
   }
 }
 
+ssd_status ssd_fwd_config_workspace_size(const ssd_problem* prob, const ssd_config* cfg,
+                                        size_t* bytes) {
+  try {
+    if (!prob || !bytes) return fail(SSD_ERR_NULL_POINTER, "prob and bytes must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl);
+    if (st != SSD_OK) return st;
+    workspace_plan(&pl);
+    const ssd_config use = cfg ? *cfg : default_config(pl);
+    st = check_config(pl, use);
+    if (st != SSD_OK) return st;
+    st = check_supported(pl, use.out_heads);
+    if (st != SSD_OK) return st;
+    *bytes = config_bytes(pl, use);
+    return ok();
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+ssd_status ssd_fwd_status(const void* workspace, size_t workspace_bytes, void* stream,
+                          int32_t* timed_out) {
+  try {
+    if (!timed_out || !workspace)
+      return fail(SSD_ERR_NULL_POINTER, "workspace and timed_out must not be NULL");
+    const void* ws = workspace;
+    if (!aligned16(ws)) return fail(SSD_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+    if (workspace_bytes < 16)
+      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, the header needs 16", workspace_bytes);
+    unsigned long long h[2] = {0ull, 0ull};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(h, ws, sizeof(h), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "status read");
+    // the status word is tagged with the gen of the call that timed out;
+    // the latest call recorded its own gen in the next word
+    *timed_out = (h[0] & 0xffffffffull) != 0 && (h[0] >> 32) == (h[1] & 0xffffffffull);
+    return ok();
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 ssd_status ssd_chunk_cumsum_ex(const ssd_problem* prob, const ssd_dt_transform* dtx,
                                const float* dt, const float* A, float* G_out, float* dt_out,
                                void* stream) {
@@ -381,8 +471,9 @@ ssd_status ssd_fwd_states_ex(const ssd_problem* prob, const ssd_dt_transform* dt
     st = check_supported(pl);
     if (st != SSD_OK) return st;
     workspace_plan(&pl);
-    if (workspace_bytes < pl.bytes)
-      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+    if (workspace_bytes < pl.staged_bytes)
+      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                  pl.staged_bytes);
     return run_states(pl, default_config(pl), x, dt, A, B, init_state, final_state, chunk_states,
                       workspace, dtx ? &xf : nullptr, static_cast<hipStream_t>(stream));
   } catch (...) {
@@ -405,8 +496,8 @@ static ssd_status run_out(const Plan& pl, const ssd_config& cfg, const void* x, 
   const float* Gw = reinterpret_cast<const float*>(ws + pl.g_off);
   const float* dtw = reinterpret_cast<const float*>(ws + pl.dt_off);
   const void* Hc = ws + pl.hc_off;
-  void* sink = const_cast<char*>(ws) + pl.sink_off;
-  return hip_status(ssd::launch_compute_out(pl.bf16, x, B, C, Gw, dtw, Hc, D, y, sink, pl.B, pl.L,
+  ssd::StatusRef status{reinterpret_cast<unsigned long long*>(const_cast<char*>(ws)), next_gen()};
+  return hip_status(ssd::launch_compute_out(pl.bf16, x, B, C, Gw, dtw, Hc, D, y, status, pl.B, pl.L,
                                             pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp,
                                             cfg.out_heads, s),
                     "compute_out launch");
@@ -427,8 +518,9 @@ ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B
     st = check_supported(pl);
     if (st != SSD_OK) return st;
     workspace_plan(&pl);
-    if (workspace_bytes < pl.bytes)
-      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+    if (workspace_bytes < pl.staged_bytes)
+      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                  pl.staged_bytes);
     return run_out(pl, default_config(pl), x, B, C, D, y, workspace,
                    static_cast<hipStream_t>(stream));
   } catch (...) {
@@ -460,8 +552,9 @@ static ssd_status check_fwd(const ssd_problem* prob, const ssd_config* cfg,
   st = check_supported(*pl, use->out_heads);
   if (st != SSD_OK) return st;
   workspace_plan(pl);
-  if (workspace_bytes < pl->bytes)
-    return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl->bytes);
+  const size_t need = config_bytes(*pl, *use);
+  if (workspace_bytes < need)
+    return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   return SSD_OK;
 }
 
@@ -469,6 +562,16 @@ static ssd_status run_fwd(const Plan& pl, const ssd_config& use, const ssd::DtXf
                           const void* x, const float* dt, const float* A, const void* B,
                           const void* C, const float* D, const float* init_state, void* y,
                           float* final_state, void* workspace, hipStream_t s) {
+  if (use.fused) {
+    // one kernel; the state handed from chunk to chunk lives in final_state
+    // itself when the caller wants it, else in the workspace
+    char* ws = static_cast<char*>(workspace);
+    float* chain = final_state ? final_state : reinterpret_cast<float*>(ws + pl.chain_off);
+    return hip_status(ssd::launch_fused_fwd(x, dt, A, B, C, D, init_state, chain, y,
+                                            ws + pl.flags_off, ws, ws + 8, xf, pl.B, pl.L, pl.H,
+                                            pl.G, (int)pl.Q, pl.T, next_gen(), s),
+                      "fused forward launch");
+  }
   ssd_status st = run_states(pl, use, x, dt, A, B, init_state, final_state, nullptr, workspace,
                              xf, s);
   if (st != SSD_OK) return st;
@@ -537,6 +640,9 @@ ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const 
       return fail(SSD_ERR_BAD_VALUE, "tune: init_state must not alias final_state");
     if (max_tried < 0 || (max_tried > 0 && (!tried || !tried_ms)))
       return fail(SSD_ERR_BAD_VALUE, "max_tried must be >= 0, with tried and tried_ms given when > 0");
+    if (workspace_bytes < pl.staged_bytes)
+      return fail(SSD_ERR_WORKSPACE, "tune: workspace has %zu bytes, the staged kernels need %zu",
+                  workspace_bytes, pl.staged_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t ev[2] = {nullptr, nullptr};
     if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) {
@@ -544,9 +650,15 @@ ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const 
       return fail(SSD_ERR_HIP, "tune: event creation failed");
     }
     const ssd::DtXform* xfp = dtx ? &xf : nullptr;
-    // the valid choices, in a fixed order
-    ssd_config cand[2 * 3 * 2];
+    // the valid choices, in a fixed order: the fused kernel (where built),
+    // then every staged combination
+    ssd_config cand[1 + 2 * 3 * 2];
     int n = 0;
+    if (pl.fused_ok) {
+      ssd_config c = default_config(pl);
+      c.fused = 1;
+      cand[n++] = c;
+    }
     for (int ch : {4, 16})
       for (int sh : {4, 2, 1})
         for (int oh : {2, 1}) {
@@ -570,7 +682,7 @@ ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const 
     // warm the device up with the default choice, then measure every choice
     // twice, in forward and in reverse order, keeping the smaller mean, so a
     // drift of clocks or caches during the sweep does not favour one end
-    float warm = 0.0f, t_ms[2 * 3 * 2];
+    float warm = 0.0f, t_ms[1 + 2 * 3 * 2];
     st = time_one(use, &warm);
     for (int i = 0; i < n && st == SSD_OK; ++i) st = time_one(cand[i], &t_ms[i]);
     for (int i = n - 1; i >= 0 && st == SSD_OK; --i) {

@@ -255,84 +255,32 @@ __device__ __forceinline__ void dma16_so(const void* base, uint32_t off, const v
 
 // Wait for this wave's loads until at most n (0..3) groups of `per` vector
 // memory operations remain outstanding (the immediate must be a constant).
+// The loads above write LDS behind the compiler's back, so after the wait a
+// compiler fence keeps it from moving the LDS reads of that data above it.
 template <int per>
 __device__ __forceinline__ void wait_groups(int n) {
   if (n >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * per));
   else if (n == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per));
   else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(per));
   else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __asm__ __volatile__("" ::: "memory");
 }
 
-// Wait until at most n of this wave's vector memory operations are
-// outstanding, n known only at run time (s_waitcnt takes an immediate); n
-// above the counter's range waits for 63, which is stricter.
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
-    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
-    case 9: __builtin_amdgcn_s_waitcnt(vmcnt_imm(9)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(vmcnt_imm(10)); break;
-    case 11: __builtin_amdgcn_s_waitcnt(vmcnt_imm(11)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); break;
-    case 13: __builtin_amdgcn_s_waitcnt(vmcnt_imm(13)); break;
-    case 14: __builtin_amdgcn_s_waitcnt(vmcnt_imm(14)); break;
-    case 15: __builtin_amdgcn_s_waitcnt(vmcnt_imm(15)); break;
-    case 16: __builtin_amdgcn_s_waitcnt(vmcnt_imm(16)); break;
-    case 17: __builtin_amdgcn_s_waitcnt(vmcnt_imm(17)); break;
-    case 18: __builtin_amdgcn_s_waitcnt(vmcnt_imm(18)); break;
-    case 19: __builtin_amdgcn_s_waitcnt(vmcnt_imm(19)); break;
-    case 20: __builtin_amdgcn_s_waitcnt(vmcnt_imm(20)); break;
-    case 21: __builtin_amdgcn_s_waitcnt(vmcnt_imm(21)); break;
-    case 22: __builtin_amdgcn_s_waitcnt(vmcnt_imm(22)); break;
-    case 23: __builtin_amdgcn_s_waitcnt(vmcnt_imm(23)); break;
-    case 24: __builtin_amdgcn_s_waitcnt(vmcnt_imm(24)); break;
-    case 25: __builtin_amdgcn_s_waitcnt(vmcnt_imm(25)); break;
-    case 26: __builtin_amdgcn_s_waitcnt(vmcnt_imm(26)); break;
-    case 27: __builtin_amdgcn_s_waitcnt(vmcnt_imm(27)); break;
-    case 28: __builtin_amdgcn_s_waitcnt(vmcnt_imm(28)); break;
-    case 29: __builtin_amdgcn_s_waitcnt(vmcnt_imm(29)); break;
-    case 30: __builtin_amdgcn_s_waitcnt(vmcnt_imm(30)); break;
-    case 31: __builtin_amdgcn_s_waitcnt(vmcnt_imm(31)); break;
-    case 32: __builtin_amdgcn_s_waitcnt(vmcnt_imm(32)); break;
-    case 33: __builtin_amdgcn_s_waitcnt(vmcnt_imm(33)); break;
-    case 34: __builtin_amdgcn_s_waitcnt(vmcnt_imm(34)); break;
-    case 35: __builtin_amdgcn_s_waitcnt(vmcnt_imm(35)); break;
-    case 36: __builtin_amdgcn_s_waitcnt(vmcnt_imm(36)); break;
-    case 37: __builtin_amdgcn_s_waitcnt(vmcnt_imm(37)); break;
-    case 38: __builtin_amdgcn_s_waitcnt(vmcnt_imm(38)); break;
-    case 39: __builtin_amdgcn_s_waitcnt(vmcnt_imm(39)); break;
-    case 40: __builtin_amdgcn_s_waitcnt(vmcnt_imm(40)); break;
-    case 41: __builtin_amdgcn_s_waitcnt(vmcnt_imm(41)); break;
-    case 42: __builtin_amdgcn_s_waitcnt(vmcnt_imm(42)); break;
-    case 43: __builtin_amdgcn_s_waitcnt(vmcnt_imm(43)); break;
-    case 44: __builtin_amdgcn_s_waitcnt(vmcnt_imm(44)); break;
-    case 45: __builtin_amdgcn_s_waitcnt(vmcnt_imm(45)); break;
-    case 46: __builtin_amdgcn_s_waitcnt(vmcnt_imm(46)); break;
-    case 47: __builtin_amdgcn_s_waitcnt(vmcnt_imm(47)); break;
-    case 48: __builtin_amdgcn_s_waitcnt(vmcnt_imm(48)); break;
-    case 49: __builtin_amdgcn_s_waitcnt(vmcnt_imm(49)); break;
-    case 50: __builtin_amdgcn_s_waitcnt(vmcnt_imm(50)); break;
-    case 51: __builtin_amdgcn_s_waitcnt(vmcnt_imm(51)); break;
-    case 52: __builtin_amdgcn_s_waitcnt(vmcnt_imm(52)); break;
-    case 53: __builtin_amdgcn_s_waitcnt(vmcnt_imm(53)); break;
-    case 54: __builtin_amdgcn_s_waitcnt(vmcnt_imm(54)); break;
-    case 55: __builtin_amdgcn_s_waitcnt(vmcnt_imm(55)); break;
-    case 56: __builtin_amdgcn_s_waitcnt(vmcnt_imm(56)); break;
-    case 57: __builtin_amdgcn_s_waitcnt(vmcnt_imm(57)); break;
-    case 58: __builtin_amdgcn_s_waitcnt(vmcnt_imm(58)); break;
-    case 59: __builtin_amdgcn_s_waitcnt(vmcnt_imm(59)); break;
-    case 60: __builtin_amdgcn_s_waitcnt(vmcnt_imm(60)); break;
-    case 61: __builtin_amdgcn_s_waitcnt(vmcnt_imm(61)); break;
-    case 62: __builtin_amdgcn_s_waitcnt(vmcnt_imm(62)); break;
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(63)); break;
-  }
+// Where a kernel reports a bounded wait that gave up: the 64-bit status word
+// of the workspace header.  A timeout stores (gen << 32) | 1 there, and the
+// kernel records gen in the next word, so the host can tell whether the
+// latest call on a workspace timed out without the word ever being cleared.
+struct StatusRef {
+  unsigned long long* word;   // [0] status, [1] gen of the latest call
+  unsigned int gen;
+};
+__device__ __forceinline__ void report_timeout(const StatusRef& s) {
+  __hip_atomic_store(s.word, ((unsigned long long)s.gen << 32) | 1ull, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void record_call(const StatusRef& s) {
+  __hip_atomic_store(s.word + 1, (unsigned long long)s.gen, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Exchange through LDS between lanes of one wave: every LDS access of this

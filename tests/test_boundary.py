@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(so):
                           "ssd_fwd_states", "ssd_compute_out", "ssd_fwd_ex",
                           "ssd_chunk_cumsum_ex", "ssd_step", "ssd_fwd_states_ex",
                           "ssd_default_config", "ssd_fwd_config", "ssd_tune",
-                          "ssd_bwd_workspace_size", "ssd_bwd"}
+                          "ssd_bwd_workspace_size", "ssd_bwd", "ssd_fwd_config_workspace_size",
+                          "ssd_fwd_status"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
@@ -48,7 +49,7 @@ def test_exports_every_declared_symbol(so):
 
 
 def test_version_and_strings(so):
-    assert lib.ssd_abi_version() == 4
+    assert lib.ssd_abi_version() == 5
     for code in range(11):
         assert lib.ssd_status_string(code) and lib.ssd_status_string(code) != "unknown status"
     assert lib.ssd_status_string(77) == "unknown status"
@@ -66,17 +67,54 @@ def ws_status(prob):
     return lib.load_library().ssd_fwd_workspace_size(ctypes.byref(prob), ctypes.byref(n)), n.value
 
 
+def cfg_ws(prob, cfg):
+    n = ctypes.c_size_t(0)
+    st = lib.load_library().ssd_fwd_config_workspace_size(
+        ctypes.byref(prob), None if cfg is None else ctypes.byref(cfg), ctypes.byref(n))
+    return st, n.value
+
+
 def test_workspace_size_formula(so):
-    st, n = ws_status(P())
-    assert st == OK
+    # a 256-byte header, then the staged layout (running sums, step sizes,
+    # chunk-start states) or the fused one (flags per 32x32 state tile, an
+    # fp32 state); the plain size covers both
+    r = lambda v: (v + 255) // 256 * 256
+    hdr = 256
     T, Lp = 4, 1024
     g = 2 * 8 * Lp * 4
     hc = 2 * 8 * T * 64 * 128 * 2
-    r = lambda v: (v + 255) // 256 * 256
-    sink = 4096
-    assert n == r(g) + r(g) + r(hc) + sink
+    staged = hdr + r(g) + r(g) + r(hc)
+    fused = hdr + r(2 * 8 * 4 * 2 * 8) + r(2 * 8 * 64 * 128 * 4)
+    st, n = ws_status(P())
+    assert st == OK and n == max(staged, fused)
+    assert cfg_ws(P(), CFG(fused=0)) == (OK, staged)
+    assert cfg_ws(P(), CFG(fused=1)) == (OK, fused)
+    assert cfg_ws(P(), None) == (OK, fused)              # the default is the fused kernel here
+    # a shape the fused kernel is not built for: the staged layout only
     st, n32 = ws_status(P(io_dtype=0, dstate=64))
-    assert st == OK and n32 == r(g) + r(g) + r(2 * 8 * T * 64 * 64 * 4) + sink
+    staged32 = hdr + r(g) + r(g) + r(2 * 8 * T * 64 * 64 * 4)
+    assert st == OK and n32 == staged32
+    assert cfg_ws(P(io_dtype=0, dstate=64), None) == (OK, staged32)
+
+
+def test_config_workspace_size_errors(so):
+    f = lib.load_library().ssd_fwd_config_workspace_size
+    n = ctypes.c_size_t(0)
+    assert f(None, None, ctypes.byref(n)) == NULLP
+    assert f(ctypes.byref(P()), None, None) == NULLP
+    assert cfg_ws(P(batch=0), None)[0] == SHAPE
+    assert cfg_ws(P(), CFG(fused=2))[0] == BADVAL
+    assert cfg_ws(P(dstate=64), CFG(fused=1))[0] == BADVAL   # not built for dstate 64
+    assert cfg_ws(P(dstate=272), None)[0] == UNSUP
+
+
+def test_status_errors(so):
+    f = lib.load_library().ssd_fwd_status
+    t = ctypes.c_int32(7)
+    assert f(ctypes.c_void_p(FAKE), 256, None, None) == NULLP
+    assert f(ctypes.c_void_p(FAKE + 4), 256, None, ctypes.byref(t)) == MISAL
+    assert f(ctypes.c_void_p(FAKE), 15, None, ctypes.byref(t)) == WS
+    assert t.value == 7          # nothing written on an error
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -127,9 +165,13 @@ def test_fwd_misaligned(so, arg):
 
 
 def test_fwd_workspace_too_small(so):
-    _, need = ws_status(P())
+    # ssd_fwd needs the default configuration's layout (here the fused kernel's)
+    _, need = cfg_ws(P(), None)
     assert call_fwd(P(), ws_bytes=need - 1) == WS
     assert "needs" in lib.ssd_last_error_message()
+    # the staged kernels' larger layout for a shape the fused kernel is not built for
+    _, need = cfg_ws(P(chunk_size=128), None)
+    assert call_fwd(P(chunk_size=128), ws_bytes=need - 1) == WS
 
 
 def test_states_and_cumsum_validation(so):
@@ -239,8 +281,8 @@ def test_step_ignores_chunk_size(so):
 
 # ------------------------------------------------------------ tile choices
 
-def CFG(ch=4, sh=4, oh=2, reserved=0):
-    return lib.ssd_config(ch, sh, oh, reserved)
+def CFG(ch=4, sh=4, oh=2, fused=0):
+    return lib.ssd_config(ch, sh, oh, fused)
 
 
 def call_fwd_config(prob, cfg, **kw):
@@ -254,12 +296,15 @@ def call_fwd_config(prob, cfg, **kw):
 
 
 @pytest.mark.parametrize("kw,cfg", [
-    (dict(), CFG(ch=8)), (dict(), CFG(sh=3)), (dict(), CFG(oh=3)), (dict(), CFG(reserved=1)),
+    (dict(), CFG(ch=8)), (dict(), CFG(sh=3)), (dict(), CFG(oh=3)), (dict(), CFG(fused=2)),
+    (dict(chunk_size=128), CFG(fused=1)),              # the fused kernel is built for chunk 256
+    (dict(nheads=6, ngroups=2), CFG(sh=1, oh=1, fused=1)),   # 3 heads per group: odd
     (dict(nheads=4, ngroups=2), CFG(sh=4)),            # 2 heads per group: 4 does not divide
     (dict(io_dtype=0), CFG(oh=2)),                     # fp32: one head per compute_out workgroup
     (dict(dstate=256), CFG(oh=2)),                     # dstate 256: accumulators do not fit twice
     (dict(nheads=6, ngroups=2), CFG(sh=1, oh=2)),      # 3 heads per group: odd
-], ids=["cumsum8", "state3", "out3", "reserved", "state4_hg2", "out2_fp32", "out2_n256", "out2_odd"])
+], ids=["cumsum8", "state3", "out3", "fused2", "fused_q128", "fused_odd", "state4_hg2", "out2_fp32",
+        "out2_n256", "out2_odd"])
 def test_fwd_config_rejects_bad_choice(so, kw, cfg):
     assert call_fwd_config(P(**kw), cfg) == BADVAL
     assert "config" in lib.ssd_last_error_message()
@@ -274,11 +319,12 @@ def test_fwd_config_check_order_and_default(so):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(batch=2, seqlen=8192, nheads=80, headdim=64, dstate=128, ngroups=1, chunk_size=256),
-     dict(cumsum_heads=4, state_heads=4, out_heads=2)),
+     dict(cumsum_heads=4, state_heads=4, out_heads=2, fused=1)),
     (dict(batch=8, seqlen=4096, nheads=64, headdim=64, dstate=256, ngroups=8, chunk_size=128),
-     dict(cumsum_heads=4, state_heads=4, out_heads=1)),
-    (dict(nheads=6, ngroups=3), dict(cumsum_heads=4, state_heads=2, out_heads=2)),
-    (dict(nheads=3, ngroups=3, io_dtype=0), dict(cumsum_heads=4, state_heads=1, out_heads=1)),
+     dict(cumsum_heads=4, state_heads=4, out_heads=1, fused=0)),
+    (dict(nheads=6, ngroups=3), dict(cumsum_heads=4, state_heads=2, out_heads=2, fused=1)),
+    (dict(nheads=6, ngroups=2), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0)),
+    (dict(nheads=3, ngroups=3, io_dtype=0), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0)),
 ])
 def test_default_config_is_the_static_table(so, kw, want):
     assert lib.ssd_default_config(P(**kw)) == want
@@ -308,7 +354,8 @@ def test_tune_validation(so):
 
 LLVM = "/opt/rocm/llvm/bin"
 BUILD_DIR = os.path.join(ROOT, "state_space_sequence_03_amd", "_build")
-KERNEL_OBJECTS = ["chunk_cumsum.o", "chunk_state.o", "state_pass.o", "compute_out.o", "step.o"]
+KERNEL_OBJECTS = ["chunk_cumsum.o", "chunk_state.o", "state_pass.o", "compute_out.o", "step.o",
+                  "bwd.o", "fused_fwd.o"]
 
 
 def device_disassembly(obj, tmp_path):

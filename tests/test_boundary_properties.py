@@ -15,7 +15,10 @@ def r256(v):
     return (v + 255) // 256 * 256
 
 
-def expected_ws(b, L, H, P, N, Q, bf16):
+HEADER = 256
+
+
+def expected_staged(b, L, H, P, N, Q, bf16):
     T = -(-L // Q)
     Lp = T * Q
     g = b * H * Lp * 4
@@ -24,7 +27,22 @@ def expected_ws(b, L, H, P, N, Q, bf16):
     pb = -(-P // 64)
     state = pb * 4 * ksw * 512                      # fragment-major, padded tiles
     hc = b * H * T * state * (2 if bf16 else 4)
-    return r256(g) + r256(g) + r256(hc) + 4096
+    return HEADER + r256(g) + r256(g) + r256(hc)
+
+
+def fused_built(H, G, P, N, Q, bf16):
+    return bf16 and P == 64 and N == 128 and Q == 256 and (H // G) % 2 == 0
+
+
+def expected_fused(b, H, P, N):
+    return HEADER + r256(b * H * (N // 32) * (P // 32) * 8) + r256(b * H * P * N * 4)
+
+
+def expected_ws(b, L, H, G, P, N, Q, bf16):
+    staged = expected_staged(b, L, H, P, N, Q, bf16)
+    if fused_built(H, G, P, N, Q, bf16):
+        return max(staged, expected_fused(b, H, P, N))
+    return staged
 
 
 valid = st.fixed_dictionaries({
@@ -53,8 +71,18 @@ def test_workspace_size_follows_the_layout(d):
         assert d["io_dtype"] == 0
         return
     assert st_ == OK, lib.ssd_last_error_message()
-    assert n.value == expected_ws(d["batch"], d["seqlen"], d["hpg"] * d["ngroups"], d["headdim"],
-                                  d["dstate"], d["chunk_size"], d["io_dtype"] == 1)
+    H = d["hpg"] * d["ngroups"]
+    args = (d["batch"], d["seqlen"], H, d["ngroups"], d["headdim"], d["dstate"], d["chunk_size"],
+            d["io_dtype"] == 1)
+    assert n.value == expected_ws(*args)
+    # the default configuration's own layout
+    m = ctypes.c_size_t(0)
+    assert so.ssd_fwd_config_workspace_size(ctypes.byref(prob_of(d)), None, ctypes.byref(m)) == OK
+    if fused_built(H, d["ngroups"], d["headdim"], d["dstate"], d["chunk_size"], d["io_dtype"] == 1):
+        assert m.value == expected_fused(d["batch"], H, d["headdim"], d["dstate"])
+    else:
+        assert m.value == expected_staged(d["batch"], d["seqlen"], H, d["headdim"], d["dstate"],
+                                          d["chunk_size"], d["io_dtype"] == 1)
 
 
 @settings(max_examples=300, deadline=None)

@@ -1,0 +1,179 @@
+"""GPU parity of the single-pass fused forward kernel.
+
+The fused kernel is built for bf16 io, headdim 64, dstate 128, chunk 256 and
+an even number of heads per group; ssd_fwd takes it by default there.  Every
+case is compared element by element with the CPU oracle (bf16 operands:
+rel-L2 <= 5e-3 and max-abs <= 2e-2 * max|ref| on y and final_state), over
+shapes that span one chunk, ragged tails, a single token, several batches and
+groups, and chains of many chunks handed from workgroup to workgroup; and
+against the staged kernels on the same inputs.  After every call the
+workspace's status word must report that no bounded wait gave up.
+"""
+import pytest
+import torch
+
+import oracle
+import ssd_synth
+from parity_util import assert_close, errors
+
+pytestmark = pytest.mark.gpu
+
+lib = pytest.importorskip("state_space_sequence_03_amd")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print("\n[gpu-case] %s" % request.node.name, flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def prob(**kw):
+    base = dict(batch=1, seqlen=512, nheads=2, headdim=64, dstate=128, ngroups=1,
+                chunk_size=256, io_dtype="bf16", init_std=0.1)
+    base.update(kw)
+    return ssd_synth.Problem(**base)
+
+
+def to_dev(inp):
+    return {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+
+
+def cproblem(p):
+    return lib.make_problem(p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups,
+                            p.chunk_size, lib.SSD_BF16)
+
+
+def fused_fwd(p, d, use_D=True, use_init=True, want_final=True, **kw):
+    pr = cproblem(p)
+    assert lib.ssd_default_config(pr)["fused"] == 1
+    ws = torch.empty(lib.ssd_fwd_config_workspace_size(pr), dtype=torch.uint8, device="cuda")
+    y, fin = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"] if use_D else None,
+                         p.chunk_size, d["init_state"] if use_init else None, workspace=ws,
+                         want_final_state=want_final, **kw)
+    assert not lib.ssd_fwd_status(ws), "a chain wait gave up"
+    return y, fin
+
+
+def oracle_fwd(inp, use_D=True, use_init=True):
+    return oracle.recurrence(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                             inp["D"] if use_D else None, inp["init_state"] if use_init else None)
+
+
+SHAPES = [
+    # (batch, seqlen, nheads, ngroups)
+    (1, 256, 2, 1),        # one chunk
+    (1, 300, 2, 1),        # ragged second chunk
+    (1, 1, 2, 1),          # a single token
+    (2, 1000, 4, 2),       # two groups of two heads, ragged
+    (3, 777, 6, 3),        # three groups
+    (1, 4096, 8, 1),       # 16 chunks chained
+    (2, 2048, 16, 4),
+    (1, 8448, 2, 1),       # 33 chunks: a long chain on few units
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_L%d_H%d_G%d" % s)
+def test_fused_matches_oracle(shape):
+    b, L, H, G = shape
+    p = prob(batch=b, seqlen=L, nheads=H, ngroups=G)
+    inp = ssd_synth.make_inputs(p, seed=L + 7 * H)
+    y, fin = fused_fwd(p, to_dev(inp))
+    y_ref, fin_ref, _ = oracle_fwd(inp)
+    assert_close(y, y_ref, "bf16", "y")
+    assert_close(fin, fin_ref, "bf16", "final_state")
+
+
+@pytest.mark.parametrize("use_D,use_init,want_final", [(False, True, True), (True, False, True),
+                                                       (True, True, False), (False, False, False)])
+def test_fused_optional_inputs(use_D, use_init, want_final):
+    p = prob(batch=2, seqlen=900, nheads=4, ngroups=1)
+    inp = ssd_synth.make_inputs(p, seed=61)
+    y, fin = fused_fwd(p, to_dev(inp), use_D, use_init, want_final)
+    y_ref, fin_ref, _ = oracle_fwd(inp, use_D, use_init)
+    assert_close(y, y_ref, "bf16", "y")
+    if want_final:
+        assert_close(fin, fin_ref, "bf16", "final_state")
+    else:
+        assert fin is None
+
+
+def test_fused_final_state_aliases_init_state():
+    p = prob(batch=1, seqlen=1300, nheads=4, ngroups=2)
+    inp = ssd_synth.make_inputs(p, seed=62)
+    d = to_dev(inp)
+    state = d["init_state"].clone()
+    y, fin = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 256, state,
+                         final_out=state)
+    y_ref, fin_ref, _ = oracle_fwd(inp)
+    assert_close(y, y_ref, "bf16", "y")
+    assert_close(state, fin_ref, "bf16", "final (in place)")
+
+
+def test_fused_raw_step_size():
+    p = prob(batch=2, seqlen=1024, nheads=4)
+    inp = ssd_synth.make_inputs(p, seed=63)
+    d = to_dev(inp)
+    y, fin = fused_fwd(p, d | {"dt": d["dt_raw"]}, dt_bias=d["dt_bias"], dt_softplus=True)
+    y_ref, fin_ref, _ = oracle_fwd(inp)          # inp["dt"] is the prepared step size
+    assert_close(y, y_ref, "bf16", "y")
+    assert_close(fin, fin_ref, "bf16", "final_state")
+
+
+def test_fused_agrees_with_staged_and_is_deterministic():
+    p = prob(batch=2, seqlen=3000, nheads=8, ngroups=2)
+    d = to_dev(ssd_synth.make_inputs(p, seed=64))
+    y1, f1 = fused_fwd(p, d)
+    y2, f2 = fused_fwd(p, d)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+    staged = lib.ssd_default_config(cproblem(p))
+    staged["fused"] = 0
+    y3, f3 = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 256, d["init_state"],
+                         config=staged)
+    assert errors(y1, y3)[0] < 5e-3 and errors(f1, f3)[0] < 5e-3
+
+
+def test_fused_strong_and_zero_decay():
+    # whole-chunk decays far below fp32 range next to heads with no decay
+    p = prob(batch=1, seqlen=1024, nheads=4)
+    inp = ssd_synth.make_inputs(p, seed=65)
+    inp["A"] = torch.tensor([-1e4, -32.0, 0.0, -0.001])
+    inp["dt"] = inp["dt"] * torch.tensor([10.0, 10.0, 1.0, 1.0])
+    y, fin = fused_fwd(p, to_dev(inp))
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+    y_ref, fin_ref, _ = oracle_fwd(inp)
+    assert_close(y, y_ref, "bf16", "y")
+    assert_close(fin, fin_ref, "bf16", "final_state")
+
+
+def test_fused_continuation_two_calls():
+    p = prob(batch=2, seqlen=2560, nheads=4)
+    inp = ssd_synth.make_inputs(p, seed=66)
+    d = to_dev(inp)
+    y, fin = fused_fwd(p, d)
+    L1 = 1280
+    head = {k: (v[:, :L1].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in d.items()}
+    tail = {k: (v[:, L1:].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in d.items()}
+    y1, f1 = fused_fwd(prob(batch=2, seqlen=L1, nheads=4), head)
+    tail["init_state"] = f1
+    y2, f2 = fused_fwd(prob(batch=2, seqlen=p.seqlen - L1, nheads=4), tail)
+    assert_close(torch.cat([y1, y2], 1), y, "bf16", "chained y")
+    assert_close(f2, fin, "bf16", "chained final")
+
+
+def test_fused_workspace_reused_across_shapes():
+    # one workspace, calls of different lengths in a row: the flags of an
+    # earlier call never release a later one
+    big = prob(batch=2, seqlen=4096, nheads=4)
+    pr = cproblem(big)
+    ws = torch.empty(lib.ssd_fwd_config_workspace_size(pr), dtype=torch.uint8, device="cuda")
+    for L, seed in ((4096, 67), (1000, 68), (4096, 69), (256, 70)):
+        p = prob(batch=2, seqlen=L, nheads=4)
+        inp = ssd_synth.make_inputs(p, seed=seed)
+        d = to_dev(inp)
+        y, fin = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 256,
+                             d["init_state"], workspace=ws)
+        assert not lib.ssd_fwd_status(ws)
+        y_ref, fin_ref, _ = oracle_fwd(inp)
+        assert_close(y, y_ref, "bf16", "y L=%d" % L)
+        assert_close(fin, fin_ref, "bf16", "final L=%d" % L)

@@ -42,15 +42,29 @@ PROBLEMS = {
 }
 
 
+def fused_built(p):
+    hg = p.nheads // p.ngroups
+    return (p.io_dtype == "bf16" and p.headdim == 64 and p.dstate == 128 and p.chunk_size == 256
+            and hg % 2 == 0)
+
+
 def valid_configs(p):
+    """The choices ssd_tune tries, in its order: the fused kernel where it is
+    built (with the default staged fields), then every staged combination."""
     hg = p.nheads // p.ngroups
     out = []
+    if fused_built(p):
+        d = lib.ssd_default_config(lib.make_problem(
+            p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups, p.chunk_size,
+            lib.SSD_BF16))
+        d["fused"] = 1
+        out.append(d)
     for ch, sh, oh in itertools.product((4, 16), (1, 2, 4), (1, 2)):
         if hg % sh:
             continue
         if oh == 2 and not (p.io_dtype == "bf16" and p.dstate <= 128 and hg % 2 == 0):
             continue
-        out.append(dict(cumsum_heads=ch, state_heads=sh, out_heads=oh))
+        out.append(dict(cumsum_heads=ch, state_heads=sh, out_heads=oh, fused=0))
     return out
 
 

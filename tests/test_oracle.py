@@ -225,6 +225,21 @@ def test_recurrence_heads_matches_full():
         np.testing.assert_array_equal(fh, fin[b, h])
 
 
+@pytest.mark.parametrize("heads_per_range", [1, 2, 3, 4, 6, 100])
+def test_recurrence_head_ranges_cover_every_head(heads_per_range):
+    # ranges of whole groups: every head exactly once, equal to the full call
+    prob = small_problem(nheads=6, ngroups=2)
+    inp = inputs_of(prob, seed=13)
+    y, fin, _ = run_rec(inp)
+    seen = np.zeros(6, dtype=int)
+    for h0, h1, yr, fr in oracle.recurrence_head_ranges(inp, heads_per_range):
+        assert h0 % 3 == 0 and h1 % 3 == 0      # 3 heads per group
+        seen[h0:h1] += 1
+        np.testing.assert_array_equal(yr, y[:, :, h0:h1])
+        np.testing.assert_array_equal(fr, fin[:, h0:h1])
+    assert np.all(seen == 1)
+
+
 def test_inputs_are_seeded_and_shaped():
     prob = ssd_synth.CONFIGS["tiny_fp32"]
     a, b = ssd_synth.make_inputs(prob, 0), ssd_synth.make_inputs(prob, 0)
