@@ -209,8 +209,10 @@ ssd_status ssd_fwd_config_workspace_size(const ssd_problem* prob, const ssd_conf
  * header to the host after synchronising with `stream` (it SYNCHRONISES) and
  * sets *timed_out to 1 if the latest call that used the workspace timed out,
  * else 0.  workspace: the one given to that call (16-byte aligned, at least
- * 16 bytes).  Errors: NULL_POINTER (timed_out or workspace NULL),
- * MISALIGNED, WORKSPACE (fewer than 16 bytes), HIP. */
+ * 16 bytes), or NULL for the built-in scratch of ssd_fwd_noalloc on the
+ * current device (*timed_out = 0 if that entry point has not run there).
+ * Errors: NULL_POINTER (timed_out NULL), MISALIGNED, WORKSPACE (fewer than
+ * 16 bytes), HIP. */
 ssd_status ssd_fwd_status(const void* workspace, size_t workspace_bytes, void* stream,
                           int32_t* timed_out);
 
@@ -253,6 +255,24 @@ ssd_status ssd_fwd_config(const ssd_problem* prob, const ssd_config* cfg,
                           const float* A, const void* B, const void* C, const float* D,
                           const float* init_state, void* y, float* final_state, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* ssd_fwd_ex without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The library's own scratch takes the
+ * workspace's place: one 64 MiB array per GPU, part of the library's code
+ * object, held until the process ends; its address is looked up once per
+ * device.  This call allocates nothing.  Problems whose default
+ * configuration needs more than 64 MiB of workspace (ssd_fwd_config_
+ * workspace_size with cfg = NULL) are refused with SSD_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (several streams or threads) race, so the
+ * caller serialises them; nothing in the scratch has to hold anything on
+ * entry.  ssd_fwd_status(NULL, ...) reads its status word.  Same
+ * arguments, outputs and other errors as ssd_fwd_ex. */
+ssd_status ssd_fwd_noalloc(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                           const float* dt, const float* A, const void* B, const void* C,
+                           const float* D, const float* init_state, void* y,
+                           float* final_state, void* stream);
 
 /* Shape tuning: runs the whole forward pass (as ssd_fwd_config, on the
  * caller's inputs and buffers) with every valid tile choice for `prob`, once

@@ -12,7 +12,7 @@ variable SSD_LIBRARY names another build of the library to load instead
 Names match the C ABI in include/ssd.h:
     ssd_fwd, ssd_fwd_ex, ssd_fwd_states, ssd_fwd_states_ex, ssd_compute_out, ssd_chunk_cumsum,
     ssd_chunk_cumsum_ex, ssd_step, ssd_default_config, ssd_tune, ssd_fwd_workspace_size,
-    ssd_fwd_config_workspace_size, ssd_fwd_status, ssd_bwd,
+    ssd_fwd_config_workspace_size, ssd_fwd_status, ssd_fwd_noalloc, ssd_bwd,
     ssd_bwd_workspace_size, ssd_status_string, ssd_last_error_message, ssd_abi_version
 (ssd_fwd_config is reached through ssd_fwd(..., config=...).)
 """
@@ -31,7 +31,7 @@ __all__ = ["SsdError", "SsdArgumentError", "lib_path", "load_library", "make_pro
            "ssd_chunk_cumsum", "ssd_fwd_ex", "ssd_fwd_states_ex", "ssd_chunk_cumsum_ex",
            "ssd_step", "ssd_default_config", "ssd_tune", "ssd_bwd_workspace_size", "ssd_bwd",
            "ssd_fwd_config_workspace_size", "staged_workspace_size", "ssd_fwd_status",
-           "SSD_F32", "SSD_BF16"]
+           "ssd_fwd_noalloc", "SSD_F32", "SSD_BF16"]
 
 SSD_F32, SSD_BF16 = 0, 1
 _STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_BAD_SHAPE",
@@ -139,6 +139,8 @@ def load_library():
         lib.ssd_fwd_config_workspace_size.argtypes = [P, CF, ctypes.POINTER(sz)]
         lib.ssd_fwd_status.restype = ctypes.c_int
         lib.ssd_fwd_status.argtypes = [vp, sz, vp, pi32]
+        lib.ssd_fwd_noalloc.restype = ctypes.c_int
+        lib.ssd_fwd_noalloc.argtypes = [P, X] + [vp] * 10
         lib.ssd_bwd_workspace_size.restype = ctypes.c_int
         lib.ssd_bwd_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
         lib.ssd_bwd.restype = ctypes.c_int
@@ -228,13 +230,18 @@ def staged_workspace_size(prob: ssd_problem) -> int:
     return ssd_fwd_config_workspace_size(prob, cfg)
 
 
-def ssd_fwd_status(workspace: torch.Tensor) -> bool:
+def ssd_fwd_status(workspace: Optional[torch.Tensor] = None, device=None) -> bool:
     """True if the latest forward call on ``workspace`` gave up a bounded wait
-    (its outputs are then undefined).  Synchronises the workspace's stream."""
+    (its outputs are then undefined).  Synchronises the current stream.
+    ``workspace=None`` asks about the scratch of ssd_fwd_noalloc."""
     t = ctypes.c_int32(0)
-    st = load_library().ssd_fwd_status(_dev(workspace, "workspace"),
-                                       workspace.numel() * workspace.element_size(),
-                                       _stream(workspace.device), ctypes.byref(t))
+    if workspace is None:
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        st = load_library().ssd_fwd_status(None, 0, _stream(dev), ctypes.byref(t))
+    else:
+        st = load_library().ssd_fwd_status(_dev(workspace, "workspace"),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(workspace.device), ctypes.byref(t))
     _check(st)
     return bool(t.value)
 
@@ -353,6 +360,32 @@ def ssd_fwd_ex(x, dt, A, B, C, D=None, chunk_size=256, init_state=None, *, dt_bi
     """ssd_fwd from a raw step size: dt' = clamp(softplus(dt + dt_bias), *dt_limit)."""
     return ssd_fwd(x, dt, A, B, C, D, chunk_size, init_state, dt_bias=dt_bias,
                    dt_softplus=dt_softplus, dt_limit=dt_limit, **kw)
+
+
+def ssd_fwd_noalloc(x, dt, A, B, C, D=None, chunk_size=256, init_state=None, *,
+                    want_final_state: bool = True, out=None, final_out=None, dt_bias=None,
+                    dt_softplus: bool = False, dt_limit=None):
+    """ssd_fwd on the library's built-in scratch (no workspace is allocated or
+    passed; for callers that cannot allocate).  Calls that overlap on one GPU
+    share that scratch and race.  Returns (y, final_state)."""
+    lib = load_library()
+    prob = _problem_of(x, B, chunk_size)
+    if x.dtype != B.dtype or x.dtype != C.dtype:
+        raise SsdArgumentError(4, "x, B and C must share one dtype")
+    state_shape = (x.shape[0], x.shape[2], x.shape[3], B.shape[3])
+    y = out if out is not None else torch.empty_like(x)
+    fin = None
+    if want_final_state:
+        fin = final_out if final_out is not None else torch.empty(
+            state_shape, dtype=torch.float32, device=x.device)
+    xf, xfp = _dt_transform(x.shape[2], dt_bias, dt_softplus, dt_limit)
+    st = lib.ssd_fwd_noalloc(ctypes.byref(prob), xfp, _dev(x, "x"), _dev(dt, "dt", torch.float32),
+                             _dev(A, "A", torch.float32), _dev(B, "B"), _dev(C, "C"),
+                             _dev(D, "D", torch.float32),
+                             _dev(init_state, "init_state", torch.float32), _dev(y, "y"),
+                             _dev(fin, "final_state", torch.float32), _stream(x.device))
+    _check(st)
+    return y, fin
 
 
 def ssd_fwd_states(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

@@ -47,6 +47,7 @@ hipError_t launch_fused_fwd(const void* x, const float* dt, const float* A, cons
                             int Q, int64_t T, unsigned int gen, hipStream_t stream);
 int fused_fwd_supported(int io_bf16, int64_t H, int64_t G, int64_t P, int64_t N, int Q);
 size_t fused_fwd_flag_bytes(int64_t batch, int64_t H, int64_t N);
+void* noalloc_scratch_address();
 int compute_out_kh_valid(int io_bf16, int64_t H, int64_t G, int64_t N, int kh);
 int compute_out_default_kh(int io_bf16, int64_t H, int64_t G, int64_t N);
 int chunk_state_default_kh(int64_t H, int64_t G);
@@ -314,6 +315,46 @@ ssd_status hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+static ssd_status check_fwd(const ssd_problem* prob, const ssd_config* cfg,
+                            const ssd_dt_transform* dtx, const void* x, const float* dt,
+                            const float* A, const void* B, const void* C, const float* D,
+                            const float* init_state, void* y, float* final_state,
+                            void* workspace, size_t workspace_bytes, Plan* pl, ssd_config* use,
+                            ssd::DtXform* xf);
+
+namespace ssd {
+
+// Argument checks of the forward entry points without the workspace check,
+// for the entry point that brings its own scratch; reports the bytes the
+// default configuration needs.
+ssd_status fwd_check_scratch(const ssd_problem* prob, const ssd_dt_transform* dtx, const void* x,
+                             const float* dt, const float* A, const void* B, const void* C,
+                             const float* D, const float* init_state, void* y,
+                             float* final_state, size_t* need) {
+  try {
+    Plan pl;
+    ssd_config use;
+    ssd::DtXform xf;
+    // any non-NULL, aligned stand-in passes the workspace pointer checks; the
+    // size check is made against the scratch by the caller
+    alignas(16) static const unsigned char stand_in[16] = {0};
+    ssd_status st = check_fwd(prob, nullptr, dtx, x, dt, A, B, C, D, init_state, y, final_state,
+                              const_cast<unsigned char*>(stand_in), SIZE_MAX, &pl, &use, &xf);
+    if (st != SSD_OK) return st;
+    *need = config_bytes(pl, use);
+    return SSD_OK;
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+ssd_status report(ssd_status st, const char* msg) {
+  if (st == SSD_OK) return ok();
+  return fail(st, "%s", msg);
+}
+
+}  // namespace ssd
+
 extern "C" {
 
 int ssd_abi_version(void) { return SSD_ABI_VERSION; }
@@ -376,12 +417,20 @@ ssd_status ssd_fwd_config_workspace_size(const ssd_problem* prob, const ssd_conf
 ssd_status ssd_fwd_status(const void* workspace, size_t workspace_bytes, void* stream,
                           int32_t* timed_out) {
   try {
-    if (!timed_out || !workspace)
-      return fail(SSD_ERR_NULL_POINTER, "workspace and timed_out must not be NULL");
+    if (!timed_out) return fail(SSD_ERR_NULL_POINTER, "timed_out must not be NULL");
     const void* ws = workspace;
-    if (!aligned16(ws)) return fail(SSD_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-    if (workspace_bytes < 16)
-      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, the header needs 16", workspace_bytes);
+    if (!ws) {
+      ws = ssd::noalloc_scratch_address();
+      if (!ws) {            // the no-allocation entry point has not run on this device
+        *timed_out = 0;
+        return ok();
+      }
+    } else {
+      if (!aligned16(ws)) return fail(SSD_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+      if (workspace_bytes < 16)
+        return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, the header needs 16",
+                    workspace_bytes);
+    }
     unsigned long long h[2] = {0ull, 0ull};
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(h, ws, sizeof(h), hipMemcpyDeviceToHost, s);

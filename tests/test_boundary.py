@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(so):
                           "ssd_chunk_cumsum_ex", "ssd_step", "ssd_fwd_states_ex",
                           "ssd_default_config", "ssd_fwd_config", "ssd_tune",
                           "ssd_bwd_workspace_size", "ssd_bwd", "ssd_fwd_config_workspace_size",
-                          "ssd_fwd_status"}
+                          "ssd_fwd_status", "ssd_fwd_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
@@ -172,6 +172,23 @@ def test_fwd_workspace_too_small(so):
     # the staged kernels' larger layout for a shape the fused kernel is not built for
     _, need = cfg_ws(P(chunk_size=128), None)
     assert call_fwd(P(chunk_size=128), ws_bytes=need - 1) == WS
+
+
+def test_noalloc_validation(so):
+    # argument errors and a problem beyond the built-in 64 MiB scratch are
+    # reported before the scratch is looked up or anything is enqueued
+    def call(prob, x=FAKE, y=FAKE):
+        return so.ssd_fwd_noalloc(ctypes.byref(prob), None, x, FAKE, FAKE, FAKE, FAKE, None, None,
+                                  y, None, None)
+    assert call(P(), x=None) == NULLP
+    assert call(P(), y=None) == NULLP
+    assert call(P(batch=0)) == SHAPE
+    assert call(P(), x=FAKE + 4) == MISAL
+    assert call(P(headdim=72)) == UNSUP
+    big = P(batch=8, seqlen=4096, nheads=64, dstate=256, ngroups=8, chunk_size=128)
+    assert cfg_ws(big, None)[1] > 64 << 20
+    assert call(big) == WS
+    assert "scratch" in lib.ssd_last_error_message()
 
 
 def test_states_and_cumsum_validation(so):

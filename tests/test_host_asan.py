@@ -5,7 +5,7 @@ process with the sanitizer runtime preloaded (a report or a failing test
 fails this test):
   * the C-ABI library with its host code (argument validation, workspace
     plans, the entry points' error paths) built with -fsanitize=address --
-    ssd_api.cpp recompiled, the kernels' objects reused --
+    ssd_api.cpp and noalloc.hip recompiled, the kernels' objects reused --
     under the boundary tests;
   * the C oracle (ssd_oracle.c) built with gcc -fsanitize=address, under the
     oracle's pins.
@@ -62,7 +62,7 @@ def test_library_host_code_under_asan(tmp_path):
         b.build()
     asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
     rebuilt = {}
-    for src in ("ssd_api.cpp",):
+    for src in ("ssd_api.cpp", "noalloc.hip"):
         obj = str(tmp_path / (os.path.splitext(src)[0] + ".o"))
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         subprocess.run([HIPCC] + b.COMMON_FLAGS + b.SOURCE_FLAGS.get(src, []) + asan + lang +
