@@ -448,6 +448,9 @@ def main():
     ap.add_argument("--mode", choices=("prefill", "decode", "bwd"), default="prefill")
     ap.add_argument("--tune", action="store_true",
                     help="time every valid tile choice of the forward pass (ssd_tune)")
+    ap.add_argument("--kernels", choices=("default", "fused", "staged"), default="default",
+                    help="the forward kernels to time: the library's default choice for the "
+                         "shape, the single-pass fused kernel, or the four staged kernels")
     ap.add_argument("--raw-dt", action="store_true",
                     help="pass the raw step size and let stage 1 apply bias + softplus")
     args = ap.parse_args()
@@ -503,6 +506,8 @@ def main():
     pr = ssd.make_problem(prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate,
                           prob.ngroups, Q, ssd.SSD_BF16 if prob.io_dtype == "bf16" else ssd.SSD_F32)
     cfg = ssd.ssd_default_config(pr)
+    if args.kernels != "default":
+        cfg["fused"] = int(args.kernels == "fused")
     fused = bool(cfg["fused"])
     ws = torch.empty(ssd.ssd_fwd_workspace_size(pr), dtype=torch.uint8, device=dev)
     y = torch.empty_like(d["x"])
@@ -513,7 +518,7 @@ def main():
 
     def fwd():
         ssd.ssd_fwd(d["x"], dt_in, d["A"], d["B"], d["C"], d["D"], Q, d["init_state"], out=y,
-                    final_out=fin, workspace=ws, **dt_kw)
+                    final_out=fin, workspace=ws, config=cfg, **dt_kw)
 
     if args.graph:
         graph_line(args, prob, fwd)

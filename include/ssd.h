@@ -29,8 +29,9 @@
  * stages per (chunk, head pair) in one pass over x, handing each chunk's
  * state to the next chunk's workgroup through device memory.  The staged
  * kernels (every supported shape) run them as four kernels with the running
- * sums and chunk-start states in the workspace.  ssd_fwd takes the fused one
- * where it is built (ssd_config.fused selects explicitly).
+ * sums and chunk-start states in the workspace.  ssd_fwd takes the staged
+ * kernels, which measure faster on MI355X; ssd_config.fused = 1 selects the
+ * fused one and ssd_tune times both.
  * The result equals the token recurrence up to floating-point rounding.
  * ssd_step runs the same recurrence token by token from a resident state
  * (decode).

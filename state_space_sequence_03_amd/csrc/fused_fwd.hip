@@ -27,10 +27,16 @@
 //   to chunk stays in that XCD's L2.  Every tile depends only on an earlier
 //   tile of the same list, so with all workgroups resident the walk always
 //   progresses; every wait is bounded anyway.
-// * The chunk's 32-token blocks J stream through a 4-slot LDS ring (B rows
-//   and both heads' x rows, 24 KiB a slot with the scaled copy of x) filled
-//   by direct global->LDS loads issued three blocks ahead, continuing across
-//   tile boundaries.  Rows are XOR-swizzled in 16-byte chunks.
+// * The chunk's 32-token blocks J stream through a 4-slot LDS ring (B rows,
+//   both heads' x rows and the scaled copy of x) filled by direct global->LDS
+//   loads issued three blocks ahead, continuing across tile boundaries.  A
+//   tile has 8 blocks, so block J always sits in slot J mod 4: the 8 block
+//   steps are unrolled and every LDS address is a per-lane base register plus
+//   a constant.  B rows (256 bytes) permute their 16-byte chunks by the
+//   row's key ((r mod 4) << 2 | (r / 4) mod 4); each head's x rows (128
+//   bytes, a tile of their own) by 4 ((r / 2) mod 2).  Both keep the reads
+//   of each kind (row-wise 16-byte reads of B, transposing 8-byte reads of
+//   4-row groups of B and x) free of bank conflicts.
 // * Wave w owns row block I(w) (SIMD s runs blocks s and 7-s, so causal work
 //   balances per SIMD) for both heads, and two 32x32 tiles of the chunk state
 //   (transposed: n x p).  For each block J <= I it forms the raw tile
@@ -44,15 +50,21 @@
 //   exp2(G_i - G_j) dt_j = exp2(G_i - G_e) * [exp2(G_e - G_j) dt_j] with e the
 //   last token of block J; the bracket scales the stored copy of x (once per
 //   token), the first factor is one value per row (per lane).  The diagonal
-//   block takes exp2(G_i - G_j) per element, masked before exp2, on unscaled
-//   x, and carries D_h on its diagonal.  The state accumulates in the frame
-//   of each block's last token and is rescaled by one factor per block.
+//   block takes exp2(G_i - G_j) dt_j per element, masked before exp2, on
+//   unscaled x; every wave computes its own diagonal weights (both heads) in
+//   the tile's prologue and keeps them in bf16 in LDS, so the one block step
+//   per wave that meets its diagonal costs about what the others do (the
+//   steps run in lockstep, and each step has one diagonal wave).  D_h x_i
+//   seeds the y accumulator.  The state accumulates in the frame of each
+//   block's last token and is rescaled by one factor per block.
 // * After the stream each wave hands its state tiles on: wait for the
 //   previous chunk's flag, read H_c, write H_{c+1} = a H_c + S_c in place (the
 //   buffer is final_state itself when given), publish the flag.  The stores
 //   and loads are device-coherent (sc1): the next chunk's tile may run on
 //   another XCD.  H_c (bf16) goes through LDS into the carried product, whose
 //   per-row factor exp2(G_i) is applied in fp32.
+#include <type_traits>
+
 #include "ssd_device.hpp"
 
 namespace ssd {
@@ -75,11 +87,16 @@ struct FL {
   static constexpr int NKS = N / 16;                 // K-steps over n
   static constexpr int NTN = N / 32;                 // 32-row n tiles of the state
   static constexpr int NTP = kFP / 32;               // 32-column p tiles
-  static constexpr int ROW = 256;                    // bytes per B row and per x row
-  static constexpr int SLOT_B = 32 * ROW;
-  static constexpr int SLOT_X = 32 * ROW;
-  static constexpr int SLOT = SLOT_B + 2 * SLOT_X;   // B, x, scaled x
-  static constexpr int OFF_H = kFSlots * SLOT;       // H_c in bf16, both heads
+  static constexpr int ROW = 256;                    // bytes per B row (and per token of x)
+  static constexpr int XROW = kFP * 2;               // bytes per x row of one head
+  static constexpr int XHEAD = 32 * XROW;            // one head's 32 x rows
+  static constexpr int BLK = 32 * ROW;               // one 32-row block
+  static constexpr int OFF_B = 0;                    // B rows, slot s at s * BLK
+  static constexpr int OFF_X = kFSlots * BLK;        // x rows: head 0 tile, then head 1 tile
+  static constexpr int OFF_XT = 2 * kFSlots * BLK;   // scaled x rows
+  static constexpr int OFF_H = 3 * kFSlots * BLK;    // H_c in bf16, both heads; during the
+                                                     // stream: each wave's diagonal weights
+  static constexpr int DIAGW = kFKH * kWave * 32;    // per wave: 16 bf16 per lane per head
   static constexpr int HHEAD = kFP * ROW;
   static constexpr int OFF_G = OFF_H + kFKH * HHEAD; // tables [head][token] fp32
   static constexpr int TAB = kFKH * Q * 4;
@@ -88,8 +105,10 @@ struct FL {
   static constexpr int OFF_RED = OFF_EG + TAB;       // scan partials, one per wave
   static constexpr int BYTES = OFF_RED + 64;
   static_assert(N * 2 == ROW && kFKH * kFP * 2 == ROW, "rows of 16 chunks");
-  static_assert(NI == kFWaves, "one 32-row block per wave");
+  static_assert(NI == kFWaves && NI % kFSlots == 0, "one 32-row block per wave; block J in slot J % 4");
   static_assert(kFKH * NTN * NTP == 2 * kFWaves, "two state tiles per wave");
+  static_assert((OFF_XT - OFF_X) + kFSlots * BLK <= 65536, "x and scaled-x reads: 16-bit ds offsets");
+  static_assert(kFWaves * DIAGW <= kFKH * HHEAD, "diagonal weights fit where H_c goes");
 };
 
 struct FusedArgs {
@@ -112,34 +131,63 @@ struct FusedArgs {
   unsigned int gen;
 };
 
-// byte offset of 16-byte chunk q of row r in a swizzled 256-byte-row tile
-__device__ __forceinline__ int swz(int r, int q) { return r * 256 + ((q ^ (r & 15)) << 4); }
+// Key of row r: its 16-byte chunk q is stored at position q ^ rkey(r).
+__device__ __forceinline__ int rkey(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// byte offset of 16-byte chunk q of row r in a 256-byte-row tile
+__device__ __forceinline__ int swz(int r, int q) { return r * 256 + ((q ^ rkey(r)) << 4); }
+// the same for a 128-byte-row tile (one head's x rows)
+__device__ __forceinline__ int xkey(int r) { return ((r >> 1) & 1) << 2; }
+__device__ __forceinline__ int xswz(int r, int q) { return r * 128 + ((q ^ xkey(r)) << 4); }
 
-// Two transposing reads give the 8-value fragment {rows t0..t0+3, t0+8..t0+11}
-// of columns c0 .. c0+15 of a swizzled tile of 16-bit values (per 16-lane group:
-// lane r addresses 4 values at row t0 + r/4, column c0 + 4 (r%4); lane l
-// receives column c0 + l of the 4 rows).
-__device__ __forceinline__ bf16x8 frag_tr(const unsigned char* tile, int t0, int c0, int lane) {
-  const int r = lane & 15;
-  const int row = t0 + (r >> 2);
-  const int col = c0 + 4 * (r & 3);
-  const unsigned char* p1 = tile + swz(row, col >> 3) + (col & 7) * 2;
-  const unsigned char* p2 = tile + swz(row + 8, col >> 3) + (col & 7) * 2;
-  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
-  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p2);
+// Byte offset (within a tile) of this lane's 8-byte piece of a transposing
+// read: 16-lane group g reads rows t0 + r/4 (r = lane % 16), columns c0 + 4
+// (r % 4) .. +3 of 16-bit values, with t0 = 4 (g / 2) + 8 sec and c0 = cbase +
+// 16 (g % 2); the fragment of 16-row step ks adds ks * 4096 (16 rows keep the
+// key, so it is a constant).
+__device__ __forceinline__ int tr_off(int lane, int sec, int cbase) {
+  const int r = lane & 15, g = lane >> 4;
+  const int row = 4 * (g >> 1) + 8 * sec + (r >> 2);
+  const int col = cbase + 16 * (g & 1) + 4 * (r & 3);
+  return swz(row, col >> 3) + (col & 7) * 2;
+}
+// The same for a head's x tile (128-byte rows); there the key does not
+// change with sec either, so the second read is 1024 bytes further.
+__device__ __forceinline__ int trx_off(int lane, int cbase) {
+  const int r = lane & 15, g = lane >> 4;
+  const int row = 4 * (g >> 1) + (r >> 2);
+  const int col = cbase + 16 * (g & 1) + 4 * (r & 3);
+  return xswz(row, col >> 3) + (col & 7) * 2;
+}
+
+__device__ __forceinline__ bf16x8 tr_pair(const unsigned char* p0, const unsigned char* p1) {
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
   bf16x8 f;
   f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
   f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
   return f;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4 and 8 lanes within each 16-lane row, then the last lane of a row
+// broadcast into the next row(s).  Lanes with no source read 0.
+__device__ __forceinline__ float dpp_add(float v, float t) { return v + t; }
+__device__ __forceinline__ float wave_scan(float v) {
+  v = dpp_add(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true)));
+  v = dpp_add(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true)));
+  v = dpp_add(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true)));
+  v = dpp_add(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true)));
+  v = dpp_add(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false)));
+  v = dpp_add(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false)));
+  return v;
+}
+
 __device__ __forceinline__ floatx16 mma32(floatx16 c, bf16x8 a, bf16x8 b) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// A value the compiler must treat as unknown where it is used: lane-derived
-// indices laundered inside a loop are recomputed there instead of hoisted
-// (dozens of loop-invariant LDS addresses would otherwise stay live).
+// A value the compiler must treat as unknown where it is used, so what is
+// derived from it is computed there instead of hoisted and kept live.
 __device__ __forceinline__ int opaque(int v) {
   __asm__ __volatile__("" : "+v"(v));
   return v;
@@ -159,6 +207,50 @@ __device__ __forceinline__ void wait_ring(int blocks) {
   if (blocks >= 2) __asm__ __volatile__("s_waitcnt vmcnt(4)" ::: "memory");
   else if (blocks == 1) __asm__ __volatile__("s_waitcnt vmcnt(2)" ::: "memory");
   else __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Device-coherent loads of 4 x 16 bytes at byte offsets O0..O3 from one base
+// (the caller's state pieces); the wait sits in the same statement, so the
+// outputs are valid at its end.
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void load4_sc1(const float* p, floatx4* v) {
+  __asm__ __volatile__(
+      "global_load_dwordx4 %0, %4, off offset:%5 sc1\n\t"
+      "global_load_dwordx4 %1, %4, off offset:%6 sc1\n\t"
+      "global_load_dwordx4 %2, %4, off offset:%7 sc1\n\t"
+      "global_load_dwordx4 %3, %4, off offset:%8 sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(p), "i"(O0), "i"(O1), "i"(O2), "i"(O3)
+      : "memory");
+}
+
+// Device-coherent loads of 2 x 4 x 16 bytes at byte offsets 0, 32, 64, 96
+// from each of two bases (a lane's state pieces of both p tiles), all in
+// flight together; the wait sits in the same statement.
+__device__ __forceinline__ void load8x_sc1(const float* p0, const float* p1, floatx4* v) {
+  __asm__ __volatile__(
+      "global_load_dwordx4 %0, %8, off sc1\n\t"
+      "global_load_dwordx4 %1, %8, off offset:32 sc1\n\t"
+      "global_load_dwordx4 %2, %8, off offset:64 sc1\n\t"
+      "global_load_dwordx4 %3, %8, off offset:96 sc1\n\t"
+      "global_load_dwordx4 %4, %9, off sc1\n\t"
+      "global_load_dwordx4 %5, %9, off offset:32 sc1\n\t"
+      "global_load_dwordx4 %6, %9, off offset:64 sc1\n\t"
+      "global_load_dwordx4 %7, %9, off offset:96 sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(p0), "v"(p1)
+      : "memory");
+}
+
+// Device-coherent 16-byte load of the two flags of a wave's state tiles.
+__device__ __forceinline__ floatx4 load_flags_sc1(const unsigned long long* p) {
+  floatx4 v;
+  __asm__ __volatile__("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)"
+                       : "=&v"(v) : "v"(p) : "memory");
+  return v;
 }
 
 // Device-coherent loads of 8 x 16 bytes (the caller's state pieces); the
@@ -220,36 +312,57 @@ __device__ __forceinline__ bool tile_of(const FusedArgs& a, int bid, int k, Tile
 }
 
 // Issue this wave's share of block J of tile t into ring slot `slot`: four
-// B rows and four x rows (both heads), 16 bytes a lane, swizzled.
+// B rows, and eight x rows of head wave/4, 16 bytes a lane, permuted by row key.
 template <int Q, int N>
 __device__ __forceinline__ void issue_block(const FusedArgs& a, const Tile& t, int J, int slot,
                                             unsigned char* lds, int wave, int lane) {
   using F = FL<Q, N>;
   const int r = 4 * wave + (lane >> 4);
-  const int q = (lane & 15) ^ (r & 15);
+  const int q = (lane & 15) ^ rkey(r);
   int tok = t.c * Q + 32 * J + r;
   if (tok > a.L - 1) tok = a.L - 1;       // rows past the end: any finite row (weight 0)
   const int64_t bt = (int64_t)t.b * a.L + tok;
   const int g = (2 * t.hp) / a.hpg;
   const bf16* gb = a.Bm + (bt * a.G + g) * N + q * 8;
-  const bf16* gx = a.x + (bt * a.H + 2 * t.hp) * kFP + q * 8;
-  unsigned char* s = lds + slot * F::SLOT;
-  dma16(gb, s + wave * 1024);
-  dma16(gx, s + F::SLOT_B + wave * 1024);
+  const int xr = 8 * (wave & 3) + (lane >> 3);
+  const int xq = (lane & 7) ^ xkey(xr);
+  int xtok = t.c * Q + 32 * J + xr;
+  if (xtok > a.L - 1) xtok = a.L - 1;
+  const bf16* gx = a.x + (((int64_t)t.b * a.L + xtok) * a.H + 2 * t.hp + (wave >> 2)) * kFP + xq * 8;
+  dma16(gb, lds + F::OFF_B + slot * F::BLK + wave * 1024);
+  dma16(gx, lds + F::OFF_X + slot * F::BLK + wave * 1024);
 }
 
 template <int Q, int N>
 __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
   using F = FL<Q, N>;
   extern __shared__ __align__(16) unsigned char lds[];
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform values in scalar registers, so tests on them are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int I = wave < 4 ? wave : 11 - wave;     // row block of this wave
   const int hs = wave >> 2, ns = wave & 3;       // state tiles: head hs, n tile ns, p tiles 0, 1
+  const int li = lane & 31, kg = lane >> 5;
   const int bid = blockIdx.x;
-  float* Gt = reinterpret_cast<float*>(lds + F::OFF_G);
-  float* GDt = reinterpret_cast<float*>(lds + F::OFF_GD);
-  float* Et = reinterpret_cast<float*>(lds + F::OFF_EG);
   float* red = reinterpret_cast<float*>(lds + F::OFF_RED);
+
+  // ---- per-lane LDS offsets, fixed for the whole kernel
+  // row-wise reads (row li, chunk 2s + kg) of a B slot or of H_c: the key
+  // only permutes, and bits 5-7 of the K-step-0 offset are the K-step's
+  // chunk pair, so K-step s is at ab0 ^ (32 s) (one XOR instead of a register
+  // per K-step)
+  const int ab0 = swz(li, kg);
+  // transposing reads of B (state operand, n tile ns) and of x (head, p tile)
+  const int bb0 = tr_off(lane, 0, 32 * ns), bb1 = tr_off(lane, 1, 32 * ns);
+  const int xb0 = F::OFF_X + trx_off(lane, 0), xb1 = F::OFF_X + trx_off(lane, 32);
+  // this lane's 16 bytes of the wave's eight x rows (head wave/4), and the
+  // tables of that row
+  const int xs = F::OFF_X + wave * 1024 + lane * 16;
+  const int xrow = 8 * (wave & 3) + (lane >> 3);
+  const int xhd = wave >> 2;
+  const int xg = F::OFF_G + xhd * Q * 4 + 31 * 4;      // G of the block's last token
+  const int xgd = F::OFF_GD + xhd * Q * 4 + xrow * 4;  // GD of this row
+  const int dlim = li - 4 * kg;                        // diagonal block: j <= i  <=>  8 q + r <= dlim
 
   if (bid == 0 && tid == 0)
     __hip_atomic_store(a.last_gen, (unsigned long long)a.gen, __ATOMIC_RELAXED,
@@ -258,54 +371,84 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
   Tile cur, nxt;
   if (!tile_of(a, bid, 0, &cur)) return;
   bool has_next = tile_of(a, bid, 1, &nxt);
-  // ring blocks are numbered across tiles: block J of the k-th tile is
-  // k * NI + J and lives in slot (k * NI + J) % 4
-  int gdone = 0;        // blocks of earlier tiles
-  int issued = -1;      // last block issued
-  for (int J = 0; J < kFAhead; ++J) {
-    issue_block<Q, N>(a, cur, J, J % kFSlots, lds, wave, tid & 63);
-    issued = J;
-  }
+  for (int J = 0; J < kFAhead; ++J) issue_block<Q, N>(a, cur, J, J, lds, wave, lane);
+
+  // A tile's step sizes (one thread per (head, token)) and the C rows of
+  // block I as B operands (lane: row li, n = 16 s + 8 kg + e).  The first
+  // tile's are loaded here, every later tile's in the epilogue of the one
+  // before, so they arrive while that tile finishes.
+  const int phd = wave >> 2;   // = tid >> 8
+  float dtv = 0.0f;
+  bf16x8 cf[F::NKS];
+  // (lane offsets are laundered so they are made at each load, not kept live
+  // or spilled through the tile)
+  auto load_dt = [&](const Tile& t) {
+    const int tk = ((wave & 3) << 6) | opaque(lane);   // = tid & 255
+    dtv = 0.0f;
+    if (t.c * Q + tk < a.L)      // padding tokens keep dt = 0
+      dtv = a.dt[((int64_t)t.b * a.L + t.c * Q + tk) * a.H + 2 * t.hp + phd];
+  };
+  auto load_c = [&](const Tile& t) {
+    const int ln = opaque(lane);
+    int tok = t.c * Q + 32 * I + (ln & 31);
+    if (tok > a.L - 1) tok = a.L - 1;
+    const bf16* cr = a.Cm + (((int64_t)t.b * a.L + tok) * a.G + (2 * t.hp) / a.hpg) * N + 8 * (ln >> 5);
+#pragma unroll
+    for (int s = 0; s < F::NKS; ++s) cf[s] = load_frag(cr + 16 * s);
+  };
+  load_dt(cur);
+  load_c(cur);
 
   for (int k = 0;; ++k) {
     const int b = cur.b, c = cur.c, hp = cur.hp;
-    const int g = (2 * hp) / a.hpg;
     // ---- prologue: running sums of both heads (one thread per (head, token))
     {
-      const int lane = tid & 63;
-      const int hd = tid >> 8, tk = tid & 255;
-      const int tok = c * Q + tk;
-      float dtv = 0.0f;
-      if (tok < a.L) {          // padding tokens keep dt = 0
-        dtv = a.dt[((int64_t)b * a.L + tok) * a.H + 2 * hp + hd];
-        if (a.use_xf) dtv = dt_prepare(a.xf, dtv, 2 * hp + hd);
-      }
-      float s = dtv * a.A[2 * hp + hd] * kLog2e;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float v = __shfl_up(s, o, 64);
-        if (lane >= o) s += v;
-      }
+      float* Gt = reinterpret_cast<float*>(lds + F::OFF_G);
+      float* GDt = reinterpret_cast<float*>(lds + F::OFF_GD);
+      float* Et = reinterpret_cast<float*>(lds + F::OFF_EG);
+      const int hd = phd, tk = ((wave & 3) << 6) | lane;
+      if (a.use_xf && c * Q + tk < a.L) dtv = dt_prepare(a.xf, dtv, 2 * hp + hd);
+      float s = wave_scan(dtv * a.A[2 * hp + hd] * kLog2e);
       if (lane == 63) red[wave] = s;
       __syncthreads();
-      for (int w2 = hd * 4; w2 < wave; ++w2) s += red[w2];
+      for (int w2 = wave & ~3; w2 < wave; ++w2) s += red[w2];
       Gt[hd * Q + tk] = s;
       GDt[hd * Q + tk] = s - __builtin_amdgcn_logf(dtv);   // log2(0) = -inf: weight 0
       Et[hd * Q + tk] = fast_exp2(s);
     }
-    // C rows of block I as B operands (lane: row li, n = 16 s + 8 kg + e)
-    bf16x8 cf[F::NKS];
-    {
-      const int lane = tid & 63, li = lane & 31, kg = lane >> 5;
-      int tok = c * Q + 32 * I + li;
-      if (tok > a.L - 1) tok = a.L - 1;
-      const bf16* cr = a.Cm + (((int64_t)b * a.L + tok) * a.G + g) * N + 8 * kg;
-#pragma unroll
-      for (int s = 0; s < F::NKS; ++s) cf[s] = load_frag(cr + 16 * s);
-    }
     __syncthreads();
-    const float Dh0 = a.D ? a.D[2 * hp] : 0.0f;
-    const float Dh1 = a.D ? a.D[2 * hp + 1] : 0.0f;
+    const float* Gt = reinterpret_cast<const float*>(lds + F::OFF_G);
+    // skip weights of the two heads (scalar loads, once per tile)
+    float dh[kFKH];
+#pragma unroll
+    for (int hd = 0; hd < kFKH; ++hd) dh[hd] = a.D ? a.D[2 * hp + hd] : 0.0f;
+    float gi[kFKH];
+#pragma unroll
+    for (int hd = 0; hd < kFKH; ++hd) gi[hd] = Gt[hd * Q + 32 * I + li];
+    // diagonal block weights exp2(G_i - G_j) dt_j = exp2(G_i - GD_j), j <= i,
+    // masked before exp2, in the raw tile's layout (v = 4 q + r <-> j = 8 q +
+    // 4 kg + r), 16 bf16 per lane and head
+    unsigned char* dw = lds + F::OFF_H + wave * F::DIAGW + lane * 32;
+    {
+      const float* GDt = reinterpret_cast<const float*>(lds + F::OFF_GD);
+      // compared here, not kept as 16 lane masks for the whole kernel
+      const int dl = opaque(dlim);
+#pragma unroll
+      for (int hd = 0; hd < kFKH; ++hd) {
+        bf16x8 o[2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const floatx4 gd = *reinterpret_cast<const floatx4*>(GDt + hd * Q + 32 * I + 8 * q + 4 * kg);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ex = 8 * q + r <= dl ? gi[hd] - gd[r] : -INFINITY;
+            o[q >> 1][4 * (q & 1) + r] = static_cast<bf16>(fast_exp2(ex));
+          }
+        }
+        *reinterpret_cast<bf16x8*>(dw + hd * kWave * 32) = o[0];
+        *reinterpret_cast<bf16x8*>(dw + hd * kWave * 32 + 16) = o[1];
+      }
+    }
 
     floatx16 yacc[kFKH][2], sacc[2];
 #pragma unroll
@@ -315,71 +458,68 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
     sacc[0] = floatx16{};
     sacc[1] = floatx16{};
 
-    // ---- the chunk's 32-token blocks through the ring
-    for (int J = 0; J < F::NI; ++J) {
-      const int lane = opaque(tid & 63);
-      const int li = lane & 31, kg = lane >> 5, g4 = lane >> 4;
-      const int gJ = gdone + J;
-      const int slot = gJ & (kFSlots - 1);
-      unsigned char* sb = lds + slot * F::SLOT;
-      unsigned char* sx = sb + F::SLOT_B;
-      unsigned char* st = sx + F::SLOT_X;
-      wait_ring(issued - gJ);
+    // ---- the chunk's 32-token blocks through the ring; block J is in slot J % 4
+    auto step = [&](auto Jc) {
+      constexpr int J = decltype(Jc)::value;
+      constexpr int SL = J % kFSlots;
+      // blocks issued after this one: J+1 and J+2 (those past the tile's end
+      // belong to the next tile, if there is one)
+      if (J == 0) {
+        // everything this wave issued before (the ring's blocks 0-2, issued at
+        // least a tile phase ago, and this tile's C rows and step sizes): a
+        // wait the compiler sees, so it adds none of its own for the C rows
+        // after the next ring block is issued
+        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
+        __asm__ __volatile__("" ::: "memory");
+      } else {
+        wait_ring(J + 2 < F::NI ? 2 : (has_next ? 2 : F::NI - 1 - J));
+      }
       // scale this wave's own x rows of block J into the stored copy:
       // xt_j = exp2(G_e - G_j) dt_j x_j, e = the block's last token
       {
-        const int r = 4 * wave + (lane >> 4);
-        const int hd = ((lane & 15) ^ (r & 15)) >> 3;
-        const int j = 32 * J + r, e = 32 * J + 31;
-        const float f = fast_exp2(Gt[hd * Q + e] - GDt[hd * Q + j]);
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(sx + wave * 1024 + lane * 16);
+        const float f = fast_exp2(*reinterpret_cast<const float*>(lds + xg + 128 * J) -
+                                  *reinterpret_cast<const float*>(lds + xgd + 128 * J));
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(lds + xs + SL * F::BLK);
         bf16x8 o;
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = static_cast<bf16>(static_cast<float>(v[i]) * f);
-        *reinterpret_cast<bf16x8*>(st + wave * 1024 + lane * 16) = o;
+        *reinterpret_cast<bf16x8*>(lds + xs + (F::OFF_XT - F::OFF_X) + SL * F::BLK) = o;
       }
       __syncthreads();
-      // refill the slot every wave is done with (block gJ - 1), three blocks ahead
-      {
-        const int nb = gJ + kFAhead;        // global block to issue
-        const int kb = nb - gdone;          // its index relative to this tile
-        if (kb < F::NI) {
-          issue_block<Q, N>(a, cur, kb, nb & (kFSlots - 1), lds, wave, lane);
-          issued = nb;
-        } else if (has_next) {
-          issue_block<Q, N>(a, nxt, kb - F::NI, nb & (kFSlots - 1), lds, wave, lane);
-          issued = nb;
-        }
-      }
+      // refill the slot every wave is done with (block J - 1), three blocks ahead
+      if (J + kFAhead < F::NI) issue_block<Q, N>(a, cur, J + kFAhead, (J + kFAhead) % kFSlots, lds, wave, lane);
+      else if (has_next) issue_block<Q, N>(a, nxt, J + kFAhead - F::NI, (J + kFAhead) % kFSlots, lds, wave, lane);
+      const unsigned char* sb = lds + F::OFF_B + SL * F::BLK;
       // state product S^T (n tile ns, p tiles 0/1 of head hs) += B_J^T xt_J, in
       // the frame of the block's last token
       bf16x8 bt[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        bt[ks] = frag_tr(sb, 16 * ks + 4 * (g4 >> 1), 32 * ns + 16 * (g4 & 1), lane);
+      for (int ks = 0; ks < 2; ++ks) bt[ks] = tr_pair(sb + bb0 + 4096 * ks, sb + bb1 + 4096 * ks);
       if (J > 0) {
-        const float f = fast_exp2(Gt[hs * Q + 32 * J + 31] - Gt[hs * Q + 32 * J - 1]);
+        const float* gh = Gt + hs * Q;
+        const float f = fast_exp2(gh[32 * J + 31] - gh[32 * J - 1]);
         sacc[0] *= f;
         sacc[1] *= f;
       }
       const bool intra = J <= I;
       floatx16 raw = floatx16{};
       if (intra) {
+        const int a0 = opaque(ab0);     // the XORs are made here, not kept for the kernel
 #pragma unroll
-        for (int s = 0; s < F::NKS; ++s) {
-          const bf16x8 br = *reinterpret_cast<const bf16x8*>(sb + swz(li, 2 * s + kg));
-          raw = mma32(raw, br, cf[s]);
-        }
+        for (int s = 0; s < F::NKS; ++s)
+          raw = mma32(raw, *reinterpret_cast<const bf16x8*>(sb + (a0 ^ (32 * s))), cf[s]);
       }
 #pragma unroll
       for (int hd = 0; hd < kFKH; ++hd) {
         if (!intra && hd != hs) continue;
+        const unsigned char* sx = lds + (F::OFF_XT - F::OFF_X) + SL * F::BLK;
         bf16x8 xt[2][2];
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            xt[pt][ks] = frag_tr(st, 16 * ks + 4 * (g4 >> 1), hd * kFP + 32 * pt + 16 * (g4 & 1), lane);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int o = hd * F::XHEAD + 16 * F::XROW * ks;
+          xt[0][ks] = tr_pair(sx + xb0 + o, sx + xb0 + o + 8 * F::XROW);
+          xt[1][ks] = tr_pair(sx + xb1 + o, sx + xb1 + o + 8 * F::XROW);
+        }
         if (hd == hs) {
 #pragma unroll
           for (int pt = 0; pt < 2; ++pt)
@@ -387,34 +527,27 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
             for (int ks = 0; ks < 2; ++ks) sacc[pt] = mma32(sacc[pt], bt[ks], xt[pt][ks]);
         }
         if (!intra) continue;
-        const float gi = Gt[hd * Q + 32 * I + li];
         floatx16 w;
         if (J < I) {
-          const float u = fast_exp2(gi - Gt[hd * Q + 32 * J + 31]);
+          const float u = fast_exp2(gi[hd] - Gt[hd * Q + 32 * J + 31]);
 #pragma unroll
           for (int v = 0; v < 16; ++v) w[v] = raw[v] * u;
         } else {
-          // diagonal block: exp2(G_i - G_j) dt_j = exp2(G_i - GD_j) for j <= i,
-          // masked before exp2; D_h on the diagonal; unscaled x
-          const float dd = hd ? Dh1 : Dh0;
-          const int d = li - 4 * kg;        // j <= i  <=>  8 q + r <= d
+          // diagonal block: the weights made in the prologue, on unscaled x
+          const bf16x8 d0 = *reinterpret_cast<const bf16x8*>(dw + hd * kWave * 32);
+          const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(dw + hd * kWave * 32 + 16);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const floatx4 gd =
-                *reinterpret_cast<const floatx4*>(GDt + hd * Q + 32 * J + 8 * q + 4 * kg);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float ex = 8 * q + r <= d ? gi - gd[r] : -INFINITY;
-              float wv = raw[4 * q + r] * fast_exp2(ex);
-              if (8 * q + r == d) wv += dd;
-              w[4 * q + r] = wv;
-            }
+          for (int v = 0; v < 8; ++v) {
+            w[v] = raw[v] * static_cast<float>(d0[v]);
+            w[8 + v] = raw[8 + v] * static_cast<float>(d1[v]);
           }
+          const unsigned char* su = lds + SL * F::BLK;
 #pragma unroll
-          for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-              xt[pt][ks] = frag_tr(sx, 16 * ks + 4 * (g4 >> 1), hd * kFP + 32 * pt + 16 * (g4 & 1), lane);
+          for (int ks = 0; ks < 2; ++ks) {
+            const int o = hd * F::XHEAD + 16 * F::XROW * ks;
+            xt[0][ks] = tr_pair(su + xb0 + o, su + xb0 + o + 8 * F::XROW);
+            xt[1][ks] = tr_pair(su + xb1 + o, su + xb1 + o + 8 * F::XROW);
+          }
         }
         const bf16x8 w0 = pack8(w, 0), w1 = pack8(w, 8);
 #pragma unroll
@@ -423,34 +556,47 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
           yacc[hd][pt] = mma32(yacc[hd][pt], xt[pt][1], w1);
         }
       }
-    }
-    gdone += F::NI;
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    step(std::integral_constant<int, 4>{});
+    step(std::integral_constant<int, 5>{});
+    step(std::integral_constant<int, 6>{});
+    step(std::integral_constant<int, 7>{});
+    // every wave is done with its diagonal weights before H_c takes their place
+    __syncthreads();
 
     // ---- hand the state on: H_{c+1} = exp2(G_last) H_c + S_c
     {
-      const int lane = opaque(tid & 63);
-      const int li = lane & 31, kg = lane >> 5;
       const int hg = 2 * hp + hs;
       // this lane's pieces: rows p = 32 pt + li, columns n = 32 ns + 8 q + 4 kg .. +3
-      const int64_t row0 = (((int64_t)b * a.H + hg) * kFP + li) * N + 32 * ns + 4 * kg;
+      // (the lane's offsets are made here, not kept live through the stream)
+      const int ln = opaque(lane);
+      const int64_t row0 = (((int64_t)b * a.H + hg) * kFP + (ln & 31)) * N + 32 * ns + 4 * (ln >> 5);
       unsigned long long* fl = a.flags + (((int64_t)b * a.H + hg) * F::NTN + ns) * F::NTP;
       const float* src = a.chain;
       bool have = true;
       if (c > 0) {
+        // wait for the previous chunk's tile to publish both state tiles
         const unsigned long long want = ((unsigned long long)a.gen << 32) | (unsigned)c;
         int ok = 1;
         if (lane == 0) {
-          for (int pt = 0; pt < 2; ++pt)
-            for (int it = 0;; ++it) {
-              const unsigned long long v =
-                  __hip_atomic_load(fl + pt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              if (v == want) break;
-              if (it >= kMaxPolls) {
-                ok = 0;
-                break;
-              }
-              __builtin_amdgcn_s_sleep(2);
+          // both flags (adjacent 8-byte words) in one load
+          for (int it = 0;; ++it) {
+            const floatx4 f = load_flags_sc1(fl);
+            const unsigned long long f0 =
+                ((unsigned long long)__float_as_uint(f[1]) << 32) | __float_as_uint(f[0]);
+            const unsigned long long f1 =
+                ((unsigned long long)__float_as_uint(f[3]) << 32) | __float_as_uint(f[2]);
+            if (f0 == want && f1 == want) break;
+            if (it >= kMaxPolls) {
+              ok = 0;
+              break;
             }
+            __builtin_amdgcn_s_sleep(2);
+          }
         }
         ok = __builtin_amdgcn_readfirstlane(ok);
         if (!ok && lane == 0)
@@ -462,14 +608,12 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
       }
       floatx4 hv[8];
       if (have) {
-        const float* p0 = src + row0;
-        const float* p1 = p0 + 32 * N;
-        load8_sc1(p0, p0 + 8, p0 + 16, p0 + 24, p1, p1 + 8, p1 + 16, p1 + 24, hv);
+        load8x_sc1(src + row0, src + row0 + 32 * N, hv);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) hv[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
       }
-      const float decay = Et[hs * Q + Q - 1];
+      const float decay = fast_exp2(Gt[hs * Q + Q - 1]);
       unsigned char* hreg = lds + F::OFF_H + hs * F::HHEAD;
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt)
@@ -484,7 +628,7 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
             hb[r] = static_cast<bf16>(h[r]);
           }
           store_sc1(a.chain + row0 + pt * 32 * N + 8 * q, hn);
-          const int p = 32 * pt + li, n0 = 32 * ns + 8 * q + 4 * kg;
+          const int p = 32 * pt + (ln & 31), n0 = 32 * ns + 8 * q + 4 * (ln >> 5);
           *reinterpret_cast<bf16x4*>(hreg + swz(p, n0 >> 3) + (n0 & 7) * 2) = hb;
         }
       // the new state is visible device-wide before the flag says so
@@ -495,12 +639,40 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
         __hip_atomic_store(fl + 1, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+    // x of this lane's row i for the skip term D_h x_i (just streamed through
+    // the ring, so read from L2), in the y accumulator's layout: rows p = 32 pt
+    // + 8 q + 4 kg .. +3 of head hd; and the next tile's step sizes
+    bf16x4 xd[kFKH][2][4];
+    const bool use_d = a.D != nullptr && c * Q + 32 * I + li < a.L;
+    if (use_d) {
+      const int ln = opaque(lane);
+      const bf16* xr = a.x + (((int64_t)b * a.L + c * Q + 32 * I + (ln & 31)) * a.H + 2 * hp) * kFP + 4 * (ln >> 5);
+#pragma unroll
+      for (int hd = 0; hd < kFKH; ++hd)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            xd[hd][pt][q] = *reinterpret_cast<const bf16x4*>(xr + hd * kFP + 32 * pt + 8 * q);
+    }
+    if (has_next) load_dt(nxt);
     __syncthreads();
+    // the skip term first, so its x values are dead before the carried term
+    if (use_d) {
+#pragma unroll
+      for (int hd = 0; hd < kFKH; ++hd)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              yacc[hd][pt][4 * q + r] += dh[hd] * static_cast<float>(xd[hd][pt][q][r]);
+    }
 
     // ---- carried term exp2(G_i) H_c C_i, then store y
     {
-      const int lane = opaque(tid & 63);
-      const int li = lane & 31, kg = lane >> 5;
+      const float* Et = reinterpret_cast<const float*>(lds + F::OFF_EG);
       const int tok = c * Q + 32 * I + li;
 #pragma unroll
       for (int hd = 0; hd < kFKH; ++hd) {
@@ -508,13 +680,14 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
         const float eg = Et[hd * Q + 32 * I + li];
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) {
-          floatx16 z = floatx16{};
-          const int p = 32 * pt + li;
+          bf16x8 hf[F::NKS];
+          const int a0 = opaque(ab0);
 #pragma unroll
-          for (int s = 0; s < F::NKS; ++s) {
-            const bf16x8 hf = *reinterpret_cast<const bf16x8*>(hreg + swz(p, 2 * s + kg));
-            z = mma32(z, hf, cf[s]);
-          }
+          for (int s = 0; s < F::NKS; ++s)
+            hf[s] = *reinterpret_cast<const bf16x8*>(hreg + pt * 32 * 256 + (a0 ^ (32 * s)));
+          floatx16 z = floatx16{};
+#pragma unroll
+          for (int s = 0; s < F::NKS; ++s) z = mma32(z, hf[s], cf[s]);
           yacc[hd][pt] += eg * z;
         }
         if (tok < a.L) {
@@ -532,6 +705,7 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FusedArgs a) {
       }
     }
     if (!has_next) break;
+    load_c(nxt);         // the C rows are free once the carried term is formed
     __syncthreads();     // every wave is done with this tile's tables and H_c
     cur = nxt;
     has_next = tile_of(a, bid, k + 2, &nxt);
@@ -563,8 +737,8 @@ hipError_t launch_fused_fwd(const void* x, const float* dt, const float* A, cons
   a.D = D;
   a.init = init;
   a.chain = chain;
-  a.y = static_cast<bf16*>(y);
   a.flags = static_cast<unsigned long long*>(flags);
+  a.y = static_cast<bf16*>(y);
   a.status = static_cast<unsigned long long*>(status);
   a.last_gen = static_cast<unsigned long long*>(last_gen);
   a.use_xf = xf != nullptr;

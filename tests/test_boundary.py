@@ -89,7 +89,7 @@ def test_workspace_size_formula(so):
     assert st == OK and n == max(staged, fused)
     assert cfg_ws(P(), CFG(fused=0)) == (OK, staged)
     assert cfg_ws(P(), CFG(fused=1)) == (OK, fused)
-    assert cfg_ws(P(), None) == (OK, fused)              # the default is the fused kernel here
+    assert cfg_ws(P(), None) == (OK, staged)             # the default is the staged kernels
     # a shape the fused kernel is not built for: the staged layout only
     st, n32 = ws_status(P(io_dtype=0, dstate=64))
     staged32 = hdr + r(g) + r(g) + r(2 * 8 * T * 64 * 64 * 4)
@@ -165,11 +165,10 @@ def test_fwd_misaligned(so, arg):
 
 
 def test_fwd_workspace_too_small(so):
-    # ssd_fwd needs the default configuration's layout (here the fused kernel's)
+    # ssd_fwd needs the default configuration's layout (the staged kernels')
     _, need = cfg_ws(P(), None)
     assert call_fwd(P(), ws_bytes=need - 1) == WS
     assert "needs" in lib.ssd_last_error_message()
-    # the staged kernels' larger layout for a shape the fused kernel is not built for
     _, need = cfg_ws(P(chunk_size=128), None)
     assert call_fwd(P(chunk_size=128), ws_bytes=need - 1) == WS
 
@@ -336,10 +335,10 @@ def test_fwd_config_check_order_and_default(so):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(batch=2, seqlen=8192, nheads=80, headdim=64, dstate=128, ngroups=1, chunk_size=256),
-     dict(cumsum_heads=4, state_heads=4, out_heads=2, fused=1)),
+     dict(cumsum_heads=4, state_heads=4, out_heads=2, fused=0)),
     (dict(batch=8, seqlen=4096, nheads=64, headdim=64, dstate=256, ngroups=8, chunk_size=128),
      dict(cumsum_heads=4, state_heads=4, out_heads=1, fused=0)),
-    (dict(nheads=6, ngroups=3), dict(cumsum_heads=4, state_heads=2, out_heads=2, fused=1)),
+    (dict(nheads=6, ngroups=3), dict(cumsum_heads=4, state_heads=2, out_heads=2, fused=0)),
     (dict(nheads=6, ngroups=2), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0)),
     (dict(nheads=3, ngroups=3, io_dtype=0), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0)),
 ])

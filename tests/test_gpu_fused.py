@@ -1,7 +1,7 @@
 """GPU parity of the single-pass fused forward kernel.
 
 The fused kernel is built for bf16 io, headdim 64, dstate 128, chunk 256 and
-an even number of heads per group; ssd_fwd takes it by default there.  Every
+an even number of heads per group; ssd_config.fused = 1 selects it.  Every
 case is compared element by element with the CPU oracle (bf16 operands:
 rel-L2 <= 5e-3 and max-abs <= 2e-2 * max|ref| on y and final_state), over
 shapes that span one chunk, ragged tails, a single token, several batches and
@@ -44,13 +44,19 @@ def cproblem(p):
                             p.chunk_size, lib.SSD_BF16)
 
 
+def fused_cfg(pr):
+    cfg = lib.ssd_default_config(pr)
+    cfg["fused"] = 1
+    return cfg
+
+
 def fused_fwd(p, d, use_D=True, use_init=True, want_final=True, **kw):
     pr = cproblem(p)
-    assert lib.ssd_default_config(pr)["fused"] == 1
-    ws = torch.empty(lib.ssd_fwd_config_workspace_size(pr), dtype=torch.uint8, device="cuda")
+    cfg = fused_cfg(pr)
+    ws = torch.empty(lib.ssd_fwd_config_workspace_size(pr, cfg), dtype=torch.uint8, device="cuda")
     y, fin = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"] if use_D else None,
                          p.chunk_size, d["init_state"] if use_init else None, workspace=ws,
-                         want_final_state=want_final, **kw)
+                         want_final_state=want_final, config=cfg, **kw)
     assert not lib.ssd_fwd_status(ws), "a chain wait gave up"
     return y, fin
 
@@ -104,7 +110,7 @@ def test_fused_final_state_aliases_init_state():
     d = to_dev(inp)
     state = d["init_state"].clone()
     y, fin = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 256, state,
-                         final_out=state)
+                         final_out=state, config=fused_cfg(cproblem(p)))
     y_ref, fin_ref, _ = oracle_fwd(inp)
     assert_close(y, y_ref, "bf16", "y")
     assert_close(state, fin_ref, "bf16", "final (in place)")
@@ -166,13 +172,14 @@ def test_fused_workspace_reused_across_shapes():
     # earlier call never release a later one
     big = prob(batch=2, seqlen=4096, nheads=4)
     pr = cproblem(big)
-    ws = torch.empty(lib.ssd_fwd_config_workspace_size(pr), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.ssd_fwd_config_workspace_size(pr, fused_cfg(pr)), dtype=torch.uint8,
+                     device="cuda")
     for L, seed in ((4096, 67), (1000, 68), (4096, 69), (256, 70)):
         p = prob(batch=2, seqlen=L, nheads=4)
         inp = ssd_synth.make_inputs(p, seed=seed)
         d = to_dev(inp)
         y, fin = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 256,
-                             d["init_state"], workspace=ws)
+                             d["init_state"], workspace=ws, config=fused_cfg(cproblem(p)))
         assert not lib.ssd_fwd_status(ws)
         y_ref, fin_ref, _ = oracle_fwd(inp)
         assert_close(y, y_ref, "bf16", "y L=%d" % L)

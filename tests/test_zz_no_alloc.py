@@ -32,14 +32,14 @@ def to_dev(inp):
 
 
 CASES = [
-    # the fused kernel's shape, then a smaller one
+    # the 2.7B shape's kernel choices (bf16, dstate 128, chunk 256), then a smaller problem
     dict(batch=2, seqlen=3000, nheads=8, headdim=64, dstate=128, ngroups=2, chunk_size=256,
          io_dtype="bf16", init_std=0.1),
     dict(batch=1, seqlen=700, nheads=4, headdim=64, dstate=128, ngroups=1, chunk_size=256,
          io_dtype="bf16", init_std=0.1),
 ]
 STAGED = [
-    # shapes that take the staged kernels (their chunk-start states live in the scratch)
+    # other chunk sizes and fp32 io (their chunk-start states live in the scratch)
     dict(batch=2, seqlen=1500, nheads=4, headdim=64, dstate=128, ngroups=2, chunk_size=128,
          io_dtype="bf16", init_std=0.1),
     dict(batch=1, seqlen=300, nheads=2, headdim=32, dstate=64, ngroups=1, chunk_size=64,
@@ -47,7 +47,7 @@ STAGED = [
 ]
 
 
-@pytest.mark.parametrize("cases", [CASES, STAGED], ids=["fused", "staged"])
+@pytest.mark.parametrize("cases", [CASES, STAGED], ids=["q256_bf16", "q128_q64"])
 def test_noalloc_matches_ssd_fwd_twice(cases):
     for i, kw in enumerate(cases):
         p = ssd_synth.Problem(**kw)
