@@ -28,9 +28,10 @@ COMMON_FLAGS = [
     "--offload-arch=" + ARCH,
     # keep the compiler from emitting packed fp32 VALU ops in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in ordinary VGPRs: the AGPR form gave wrong fp32 tile
-    # results at high register pressure (correct at -O1 or in this form), and
-    # this form also needs fewer registers for the bf16 kernels
+    # MFMA accumulators in ordinary VGPRs: in the AGPR form several
+    # compute_out instantiations spill (up to 1000 VGPRs) and the fused kernel
+    # spills 3, and both forward paths measure ~3% slower; the parity suite
+    # passes in either form
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     # the direct-to-LDS load helper sets M0 in inline assembly and lists it as
     # clobbered; the compiler warns that it may keep M0 live across such a
