@@ -269,7 +269,9 @@ def bench_bwd(args):
                                  "%.1f (fp32 MFMA)" % ((PEAK_BF16_MFMA if prob.io_dtype == "bf16"
                                                         else PEAK_FP32_MFMA) / 1e12,
                                                        PEAK_FP32_MFMA / 1e12),
-                     "frac_of_fp32_peak": achieved / PEAK_FP32_MFMA, "pass_ms": ms_pass},
+                     "frac_of_fp32_peak": achieved / PEAK_FP32_MFMA,
+                     # every flop priced at the bf16 dense rate, as the forward pass is
+                     "frac_of_bf16_peak": achieved / PEAK_BF16_MFMA, "pass_ms": ms_pass},
     }
     if not args.no_cpu_baseline:
         arrs = {k: (None if v is None else oracle.as_f32(v)) for k, v in inputs.items()}

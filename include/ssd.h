@@ -68,7 +68,7 @@
  * returns the first failing check in this order: SSD_ERR_NULL_POINTER (a
  * required pointer is NULL), SSD_ERR_BAD_SHAPE (a size <= 0, nheads not a
  * multiple of ngroups, or a size product overflowing int64), SSD_ERR_BAD_CHUNK
- * (chunk_size not one of 32, 64, 128, 256; ssd_step does not use it),
+ * (chunk_size not one of 16, 32, 64, 128, 256; ssd_step does not use it),
  * SSD_ERR_BAD_DTYPE, SSD_ERR_BAD_VALUE (an invalid ssd_dt_transform or
  * ssd_config),
  * SSD_ERR_MISALIGNED (a tensor pointer not 16-byte aligned),
@@ -107,7 +107,14 @@ typedef enum {
 } ssd_status;
 
 /* Problem description.  chunk_size Q splits the sequence into
- * T = ceil(seqlen / Q) chunks; a partial last chunk is allowed. */
+ * T = ceil(seqlen / Q) chunks; a partial last chunk is allowed.  The chunk
+ * size does not change y, the final state or any gradient (the chunked
+ * evaluation equals the recurrence for every chunk size, up to rounding),
+ * and the matrix-core kernels step through tokens 32 at a time, so the
+ * entry points that return only those (ssd_fwd*, ssd_fwd_noalloc, ssd_tune,
+ * ssd_bwd) run chunk_size 16 as 32.  ssd_chunk_cumsum restarts its sums
+ * every 16 tokens for it; ssd_fwd_states and ssd_compute_out, whose
+ * workspace holds per-chunk states, return SSD_ERR_UNSUPPORTED for it. */
 typedef struct {
   int64_t batch;
   int64_t seqlen;

@@ -155,6 +155,7 @@ static void launch_ht(int Q, int64_t T, int64_t batch, const float* dt, const fl
                       float* dtT, int64_t L, int H, int64_t ld, int64_t Lw, const DtXform* xf,
                       hipStream_t stream) {
   switch (Q) {
+    case 16: launch_q<16, HT>(T, batch, dt, A, G, dtT, L, H, ld, Lw, xf, stream); break;
     case 32: launch_q<32, HT>(T, batch, dt, A, G, dtT, L, H, ld, Lw, xf, stream); break;
     case 64: launch_q<64, HT>(T, batch, dt, A, G, dtT, L, H, ld, Lw, xf, stream); break;
     case 128: launch_q<128, HT>(T, batch, dt, A, G, dtT, L, H, ld, Lw, xf, stream); break;
@@ -162,7 +163,7 @@ static void launch_ht(int Q, int64_t T, int64_t batch, const float* dt, const fl
   }
 }
 
-// Host launcher.  Q in {32, 64, 128, 256}; grid covers ceil(Lw / Q) chunks;
+// Host launcher.  Q in {16, 32, 64, 128, 256}; grid covers ceil(Lw / Q) chunks;
 // rows of G and dtT are `ld` floats apart; xf = nullptr: dt used as given;
 // heads_tile (4 or 16) is the number of heads per workgroup.
 hipError_t launch_chunk_cumsum(const float* dt, const float* A, float* G, float* dtT,

@@ -122,7 +122,8 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Plan {
-  int64_t B, L, H, P, N, G, Q, T, Lp;
+  // Q: the chunk the kernels run; Qreq: the caller's chunk_size (16 runs as 32)
+  int64_t B, L, H, P, N, G, Q, T, Lp, Qreq;
   int bf16;
   size_t esize;
   // staged path: running sums, step sizes, chunk-start states
@@ -151,14 +152,21 @@ ssd_status plan_problem(const ssd_problem* prob, Plan* pl, bool need_chunk = tru
     return fail(SSD_ERR_BAD_SHAPE, "tensor size overflows int64");
   if (p.seqlen > INT64_MAX / 2 - 256)
     return fail(SSD_ERR_BAD_SHAPE, "seqlen too large");
-  const int64_t Q = need_chunk ? p.chunk_size : 256;
-  if (!(Q == 32 || Q == 64 || Q == 128 || Q == 256))
-    return fail(SSD_ERR_BAD_CHUNK, "chunk_size must be 32, 64, 128 or 256 (got %lld)", (long long)Q);
+  const int64_t Qreq = need_chunk ? p.chunk_size : 256;
+  if (!(Qreq == 16 || Qreq == 32 || Qreq == 64 || Qreq == 128 || Qreq == 256))
+    return fail(SSD_ERR_BAD_CHUNK, "chunk_size must be 16, 32, 64, 128 or 256 (got %lld)",
+                (long long)Qreq);
+  // The chunk size does not change y, the final state or any gradient (the
+  // chunked evaluation equals the recurrence for every chunk size), and the
+  // MFMA kernels step through tokens 32 at a time: a chunk of 16 runs as 32.
+  // Only the entry points that return per-chunk values (ssd_chunk_cumsum,
+  // ssd_fwd_states, ssd_compute_out) depend on it.
+  const int64_t Q = Qreq < 32 ? 32 : Qreq;
   if (p.io_dtype != SSD_BF16 && p.io_dtype != SSD_F32)
     return fail(SSD_ERR_BAD_DTYPE, "io_dtype must be SSD_BF16 or SSD_F32 (got %d)", p.io_dtype);
   if (p.reserved != 0) return fail(SSD_ERR_BAD_DTYPE, "reserved field must be 0");
   pl->B = p.batch; pl->L = p.seqlen; pl->H = p.nheads; pl->P = p.headdim; pl->N = p.dstate;
-  pl->G = p.ngroups; pl->Q = Q;
+  pl->G = p.ngroups; pl->Q = Q; pl->Qreq = Qreq;
   pl->T = (p.seqlen + Q - 1) / Q;
   pl->Lp = pl->T * Q;
   pl->bf16 = p.io_dtype == SSD_BF16;
@@ -466,7 +474,7 @@ ssd_status ssd_chunk_cumsum_ex(const ssd_problem* prob, const ssd_dt_transform* 
     st = check_supported(pl);
     if (st != SSD_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return hip_status(ssd::launch_chunk_cumsum(dt, A, G_out, dt_out, pl.B, pl.L, pl.H, (int)pl.Q,
+    return hip_status(ssd::launch_chunk_cumsum(dt, A, G_out, dt_out, pl.B, pl.L, pl.H, (int)pl.Qreq,
                                                pl.L, pl.L, dtx ? &xf : nullptr,
                                                default_config(pl).cumsum_heads, s),
                       "chunk_cumsum launch");
@@ -522,6 +530,9 @@ ssd_status ssd_fwd_states_ex(const ssd_problem* prob, const ssd_dt_transform* dt
       return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
     st = check_supported(pl);
     if (st != SSD_OK) return st;
+    if (pl.Qreq != pl.Q)
+      return fail(SSD_ERR_UNSUPPORTED, "chunk_size %lld: the chunk-state kernels are built for "
+                  "32..256 (ssd_fwd and ssd_bwd take 16)", (long long)pl.Qreq);
     workspace_plan(&pl);
     if (workspace_bytes < pl.staged_bytes)
       return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
@@ -569,6 +580,9 @@ ssd_status ssd_compute_out(const ssd_problem* prob, const void* x, const void* B
       return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
     st = check_supported(pl);
     if (st != SSD_OK) return st;
+    if (pl.Qreq != pl.Q)
+      return fail(SSD_ERR_UNSUPPORTED, "chunk_size %lld: the chunk-state kernels are built for "
+                  "32..256 (ssd_fwd and ssd_bwd take 16)", (long long)pl.Qreq);
     workspace_plan(&pl);
     if (workspace_bytes < pl.staged_bytes)
       return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,

@@ -120,7 +120,8 @@ def test_status_errors(so):
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), SHAPE), (dict(seqlen=-1), SHAPE), (dict(nheads=6, ngroups=4), SHAPE),
     (dict(headdim=0), SHAPE), (dict(seqlen=2 ** 40, nheads=2 ** 20), SHAPE),
-    (dict(chunk_size=16), CHUNK), (dict(chunk_size=100), CHUNK), (dict(chunk_size=512), CHUNK),
+    (dict(chunk_size=8), CHUNK), (dict(chunk_size=100), CHUNK), (dict(chunk_size=512), CHUNK),
+    (dict(chunk_size=16), OK),
     (dict(io_dtype=7), DTYPE), (dict(headdim=72), UNSUP), (dict(dstate=40), UNSUP),
     (dict(dstate=272), UNSUP),
     (dict(chunk_size=32), OK), (dict(io_dtype=0, dstate=128), OK), (dict(io_dtype=0, dstate=256), OK),
@@ -202,6 +203,22 @@ def test_states_and_cumsum_validation(so):
     assert so.ssd_chunk_cumsum(ctypes.byref(prob), None, FAKE, FAKE, FAKE, None) == NULLP
     assert so.ssd_chunk_cumsum(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == CHUNK
     assert so.ssd_chunk_cumsum(ctypes.byref(prob), FAKE, FAKE + 4, FAKE, FAKE, None) == MISAL
+
+
+def test_chunk_16_runs_as_32(so):
+    # y, the final state and the gradients do not depend on the chunk size:
+    # the forward and backward entry points run chunk 16 as 32 (same
+    # workspace), the entry points that return per-chunk states refuse it
+    assert ws_status(P(chunk_size=16)) == ws_status(P(chunk_size=32))
+    assert cfg_ws(P(chunk_size=16), None) == cfg_ws(P(chunk_size=32), None)
+    prob = P(chunk_size=16)
+    assert so.ssd_fwd_states(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                             1 << 30, None) == UNSUP
+    assert "chunk_size 16" in lib.ssd_last_error_message()
+    assert so.ssd_compute_out(ctypes.byref(prob), FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30,
+                              None) == UNSUP
+    # ssd_fwd with chunk 16 passes validation up to the workspace check
+    assert call_fwd(P(chunk_size=16)) == WS
 
 
 def test_reserved_field_must_be_zero(so):

@@ -19,6 +19,7 @@ HEADER = 256
 
 
 def expected_staged(b, L, H, P, N, Q, bf16):
+    Q = max(Q, 32)                                  # chunk 16 runs as 32
     T = -(-L // Q)
     Lp = T * Q
     g = b * H * Lp * 4
@@ -50,7 +51,7 @@ valid = st.fixed_dictionaries({
     "hpg": st.integers(1, 8), "ngroups": st.integers(1, 4),
     "headdim": st.sampled_from([16, 32, 64, 80, 128]),
     "dstate": st.sampled_from([16, 32, 48, 64, 128, 256]),
-    "chunk_size": st.sampled_from([32, 64, 128, 256]),
+    "chunk_size": st.sampled_from([16, 32, 64, 128, 256]),
     "io_dtype": st.sampled_from([0, 1]),
 })
 
@@ -75,14 +76,30 @@ def test_workspace_size_follows_the_layout(d):
     args = (d["batch"], d["seqlen"], H, d["ngroups"], d["headdim"], d["dstate"], d["chunk_size"],
             d["io_dtype"] == 1)
     assert n.value == expected_ws(*args)
-    # the default configuration's own layout
+    # the default configuration's own layout (the staged kernels'), and the
+    # fused kernel's where it is built
     m = ctypes.c_size_t(0)
     assert so.ssd_fwd_config_workspace_size(ctypes.byref(prob_of(d)), None, ctypes.byref(m)) == OK
+    assert m.value == expected_staged(d["batch"], d["seqlen"], H, d["headdim"], d["dstate"],
+                                      d["chunk_size"], d["io_dtype"] == 1)
     if fused_built(H, d["ngroups"], d["headdim"], d["dstate"], d["chunk_size"], d["io_dtype"] == 1):
+        cfg = lib.ssd_config(4, 1, 1, 1)
+        assert so.ssd_fwd_config_workspace_size(ctypes.byref(prob_of(d)), ctypes.byref(cfg),
+                                                ctypes.byref(m)) == OK
         assert m.value == expected_fused(d["batch"], H, d["headdim"], d["dstate"])
-    else:
-        assert m.value == expected_staged(d["batch"], d["seqlen"], H, d["headdim"], d["dstate"],
-                                          d["chunk_size"], d["io_dtype"] == 1)
+
+
+@settings(max_examples=50, deadline=None)
+@given(valid)
+def test_fused_layout_where_built(d):
+    # the fused kernel's shapes drawn directly (rare among the examples above)
+    d = dict(d, headdim=64, dstate=128, chunk_size=256, io_dtype=1, hpg=2 * (d["hpg"] % 4 + 1))
+    so = lib.load_library()
+    cfg = lib.ssd_config(4, 1, 1, 1)
+    m = ctypes.c_size_t(0)
+    assert so.ssd_fwd_config_workspace_size(ctypes.byref(prob_of(d)), ctypes.byref(cfg),
+                                            ctypes.byref(m)) == OK, lib.ssd_last_error_message()
+    assert m.value == expected_fused(d["batch"], d["hpg"] * d["ngroups"], 64, 128)
 
 
 @settings(max_examples=300, deadline=None)

@@ -4,7 +4,7 @@ Every gradient (dx, ddt, dA, dB, dC, dD, dinit and the bias gradient) is
 compared element by element with oracle.recurrence_bwd on the same seeded
 inputs and upstream gradients, at sizes that span several chunks and token
 blocks with a ragged tail, for both io dtypes, dstate up to 256, chunk sizes
-32 to 256, grouped and ungrouped B/C, with and without D, init_state and
+16 to 256, grouped and ungrouped B/C, with and without D, init_state and
 dfinal, and with the step-size preparation.  At the 2.7B layer shape the
 per-head gradients of two (batch, head) pairs are checked against the oracle
 run for those heads alone, and at the large-state layer shape one whole group
@@ -61,6 +61,9 @@ CASES = {
                           chunk_size=128, io_dtype="fp32", init_std=0.1), True, True, None),
     "bf16_q256_n256": (dict(batch=1, seqlen=520, nheads=2, headdim=64, dstate=256, ngroups=1,
                             chunk_size=256, io_dtype="bf16", init_std=0.1), True, True, None),
+    # chunk 16 runs as 32 (the gradients do not depend on the chunk size)
+    "fp32_q16": (dict(batch=1, seqlen=90, nheads=2, headdim=32, dstate=32, ngroups=1,
+                      chunk_size=16, io_dtype="fp32", init_std=0.1), True, True, None),
     "fp32_q32_no_D_init_dfinal": (dict(batch=2, seqlen=70, nheads=2, headdim=16, dstate=16,
                                        ngroups=2, chunk_size=32, io_dtype="fp32"), False, False,
                                   None),

@@ -56,7 +56,7 @@ def prob(**kw):
 # ------------------------------------------------------------ stage 1 alone
 
 @pytest.mark.parametrize("L,H,Q", [(256, 2, 64), (300, 5, 32), (1000, 17, 128), (2048, 48, 256),
-                                   (777, 80, 256), (1, 3, 32)])
+                                   (777, 80, 256), (1, 3, 32), (300, 5, 16), (1, 3, 16)])
 def test_chunk_cumsum(L, H, Q):
     p = prob(seqlen=L, nheads=H, chunk_size=Q)
     inp = ssd_synth.make_inputs(p, seed=L + H)
@@ -65,6 +65,22 @@ def test_chunk_cumsum(L, H, Q):
     Gg = G.cpu().double().numpy()
     assert np.all(np.abs(Gg - Gref) <= 1e-5 * np.abs(Gref) + 1e-6)
     np.testing.assert_array_equal(dtt.cpu().numpy(), inp["dt"].permute(0, 2, 1).numpy())
+
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_fwd_chunk_16(io):
+    # chunk 16 runs as 32: the same kernels, so the same bits as chunk 32,
+    # and the recurrence's result (the oracle does not chunk)
+    p = prob(batch=2, seqlen=333, nheads=4, headdim=64, dstate=64, ngroups=2, chunk_size=16,
+             io_dtype=io, init_std=0.1)
+    inp = ssd_synth.make_inputs(p, seed=16)
+    d = to_dev(inp)
+    y16, f16 = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 16, d["init_state"])
+    y32, f32 = lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 32, d["init_state"])
+    assert torch.equal(y16, y32) and torch.equal(f16, f32)
+    y_ref, f_ref, _ = oracle_fwd(inp)
+    assert_close(y16, y_ref, io, "y")
+    assert_close(f16, f_ref, io, "final_state")
 
 
 def test_chunk_cumsum_closed_forms():
