@@ -58,6 +58,7 @@ DEFAULT_WORKLOAD = "mamba2_2p7b"
 TRAFFIC = {
     "fused_fwd_kernel": ("fused_fwd_{workload}_traffic.txt", ["fused_fwd.hip", "ssd_device.hpp"]),
     "compute_out": ("compute_out_{workload}_traffic.txt", ["compute_out.hip", "ssd_device.hpp"]),
+    "out_resident_kernel": ("out_resident_{workload}_traffic.txt", ["out_resident.hip", "ssd_device.hpp"]),
 }
 
 
@@ -570,7 +571,9 @@ def main():
         units = cnt["units_out"]
         per_unit = {"flops": cnt["f_path"] / units, "bytes": cnt["b_min"] / units}
     else:
-        kname, k_ms = "compute_out", staged_compute_out_ms(args, ssd, prob, d, ws, y, dt_in, dt_kw)
+        # stage 3 alone (ssd_compute_out takes the default stage-3 kernel)
+        kname = "out_resident_kernel" if cfg.get("out_resident") else "compute_out"
+        k_ms = staged_compute_out_ms(args, ssd, prob, d, ws, y, dt_in, dt_kw)
         k_flops, k_bytes = cnt["f_out"], cnt["b_out"]
         units = cnt["units_out"]
         per_unit = {"flops": cnt["f_out"] / units, "bytes": cnt["b_out"] / units}
@@ -597,7 +600,10 @@ def main():
                    "nheads": prob.nheads, "headdim": prob.headdim, "dstate": prob.dstate,
                    "ngroups": prob.ngroups, "chunk_size": Q,
                    "init_state": prob.init_std is not None, "accumulate": "fp32",
-                   "kernels": "fused single pass" if fused else "staged (4 kernels)",
+                   "kernels": "fused single pass" if fused else
+                              "staged (4 kernels; stage 3 %s)" % (
+                                  "with the interaction tile resident across heads"
+                                  if cfg.get("out_resident") else "per head pair"),
                    "dt": "raw, bias + softplus in the first stage" if args.raw_dt else "prepared"},
         "timing": {"ms_per_step": "median of the timed steps, last-level cache flushed before each",
                    "p10_ms": p10, "p90_ms": p90, "mean_ms": cold_mean,

@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
@@ -155,7 +155,7 @@ typedef struct {
  * the library compiles, chosen per problem at run time:
  *   fused        : 1 = the single-pass fused kernel (built for bf16 io,
  *                  headdim 64, dstate 128, chunk_size 256 and an even number
- *                  of heads per group), 0 = the staged kernels; the three
+ *                  of heads per group), 0 = the staged kernels; the four
  *                  fields below are checked in both cases and used by the
  *                  staged kernels only;
  *   cumsum_heads : heads per chunk_cumsum workgroup, 4 or 16;
@@ -164,7 +164,15 @@ typedef struct {
  *   out_heads    : heads per compute_out workgroup (they share the raw tile
  *                  C B^T), 1, or 2 for bf16 io, dstate <= 128 and an even
  *                  number of heads per group (two heads' accumulators do not
- *                  fit the registers otherwise).
+ *                  fit the registers otherwise);
+ *   out_resident : 1 = stage 3 as one workgroup per (batch, chunk, run of
+ *                  heads of one group) that builds the raw tile C B^T once,
+ *                  keeps it in registers and streams only each head's x,
+ *                  state and running sums (built for bf16 io, headdim 64,
+ *                  dstate <= 128, chunk_size 256 and nheads * headdim <=
+ *                  2^22; out_heads is then unused but still checked);
+ *                  0 = the head-pair kernel above.  Both give bitwise the
+ *                  same y.
  * Every choice computes the same result up to floating-point summation order.
  * ssd_default_config gives the static table the plain entry points use;
  * ssd_tune measures the alternatives. */
@@ -173,6 +181,7 @@ typedef struct {
   int32_t state_heads;
   int32_t out_heads;
   int32_t fused;        /* 0 or 1 */
+  int32_t out_resident; /* 0 or 1 */
 } ssd_config;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION at build time). */

@@ -42,6 +42,7 @@ _ARG_ERRORS = {1, 2, 3, 4, 5, 6, 7, 10}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.environ.get("SSD_LIBRARY") or os.path.join(_HERE, "libssd.so")
+ABI_VERSION = 6   # SSD_ABI_VERSION of include/ssd.h: the struct layouts declared below
 _lock = threading.Lock()
 _lib = None
 
@@ -74,18 +75,20 @@ class ssd_dt_transform(ctypes.Structure):
 
 class ssd_config(ctypes.Structure):
     _fields_ = [("cumsum_heads", ctypes.c_int32), ("state_heads", ctypes.c_int32),
-                ("out_heads", ctypes.c_int32), ("fused", ctypes.c_int32)]
+                ("out_heads", ctypes.c_int32), ("fused", ctypes.c_int32),
+                ("out_resident", ctypes.c_int32)]
 
     def as_dict(self):
         return {"cumsum_heads": self.cumsum_heads, "state_heads": self.state_heads,
-                "out_heads": self.out_heads, "fused": self.fused}
+                "out_heads": self.out_heads, "fused": self.fused,
+                "out_resident": self.out_resident}
 
 
 def _config_of(cfg) -> Optional["ssd_config"]:
     if cfg is None or isinstance(cfg, ssd_config):
         return cfg
     return ssd_config(int(cfg["cumsum_heads"]), int(cfg["state_heads"]), int(cfg["out_heads"]),
-                      int(cfg.get("fused", 0)))
+                      int(cfg.get("fused", 0)), int(cfg.get("out_resident", 0)))
 
 
 def lib_path() -> str:
@@ -101,6 +104,10 @@ def load_library():
         if not os.path.exists(_LIB_PATH):
             raise ImportError("libssd.so is not built (run python -m state_space_sequence_03_amd.build)")
         lib = ctypes.CDLL(_LIB_PATH)
+        lib.ssd_abi_version.restype = ctypes.c_int
+        if lib.ssd_abi_version() != ABI_VERSION:
+            raise ImportError("%s has ABI version %d, this binding needs %d (rebuild it)"
+                              % (_LIB_PATH, lib.ssd_abi_version(), ABI_VERSION))
         P, vp, sz = ctypes.POINTER(ssd_problem), ctypes.c_void_p, ctypes.c_size_t
         lib.ssd_abi_version.restype = ctypes.c_int
         lib.ssd_abi_version.argtypes = []

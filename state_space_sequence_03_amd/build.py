@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libssd.so")
 
 SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "state_pass.hip", "compute_out.hip", "step.hip",
-           "bwd.hip", "fused_fwd.hip", "noalloc.hip", "ssd_api.cpp"]
+           "bwd.hip", "fused_fwd.hip", "noalloc.hip", "out_resident.hip", "ssd_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

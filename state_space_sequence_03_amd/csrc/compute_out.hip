@@ -58,41 +58,15 @@ namespace ssd {
 constexpr int kOutThreads = 256;
 constexpr int kOutWaves = kOutThreads / kWave;
 constexpr int kOutP = 64;     // p slice per workgroup
-constexpr int kSpinLimit = 1 << 16;
 constexpr int kOutStaticLds = 256;   // bound on the kernel's static LDS (the slot counters)
 
 // Waves of a workgroup hand ring slots to each other through LDS counters
-// instead of a barrier per token pair, so a wave that finishes a pair early
-// (no band block in it) moves on to the next one while another still works
-// on its band.  Each slot has an arrival count (one per wave whose share of
-// the slot's loads has landed) and a release count (one per wave done
-// reading it); both only grow, by kOutWaves per use of the slot.
-//
-// Wait until an LDS counter reaches `target`.  The wait is bounded: past the
-// bound the wave goes on and reports the timeout in the call's status word
-// rather than hang the workgroup (the protocol cannot deadlock, so this marks
-// a bug).
-__device__ __forceinline__ void wait_count(int* ctr, int target, StatusRef flag, int lane) {
-  for (int spins = 0;; ++spins) {
-    // an atomic (not volatile) load, so it stays an LDS read
-    const int v = __builtin_amdgcn_readfirstlane(
-        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-    if (v >= target) break;
-    if (spins >= kSpinLimit) {
-      if (lane == 0) report_timeout(flag);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  __asm__ __volatile__("" ::: "memory");
-}
-
-// Add one to an LDS counter after this wave's earlier LDS reads completed.
-__device__ __forceinline__ void bump_count(int* ctr, int lane) {
-  __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  __asm__ __volatile__("" ::: "memory");
-}
+// (wait_count / bump_count) instead of a barrier per token pair, so a wave
+// that finishes a pair early (no band block in it) moves on to the next one
+// while another still works on its band.  Each slot has an arrival count
+// (one per wave whose share of the slot's loads has landed) and a release
+// count (one per wave done reading it); both only grow, by kOutWaves per use
+// of the slot.
 
 // One ring slot holds a token pair (32 tokens): B rows over all of n (padded
 // to 32*NK columns) and, for each of the KH heads, x rows over the

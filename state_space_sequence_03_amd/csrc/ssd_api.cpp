@@ -40,6 +40,11 @@ hipError_t launch_compute_out(int io_bf16, const void* x, const void* Bm, const 
                               int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
                               int kh, hipStream_t stream);
 int compute_out_smem_bytes(int io_bf16, int Q, int64_t N, int kh);
+hipError_t launch_out_resident(const void* x, const void* Bm, const void* Cm, const float* Gw,
+                               const float* dtw, const void* Hc, const float* Dv, void* y,
+                               StatusRef flag, int64_t batch, int64_t L, int64_t H, int64_t N,
+                               int64_t G, int64_t T_, int64_t ldw, hipStream_t stream);
+int out_resident_supported(int io_bf16, int64_t H, int64_t P, int64_t N, int Q);
 hipError_t launch_fused_fwd(const void* x, const float* dt, const float* A, const void* Bm,
                             const void* Cm, const float* D, const float* init, float* chain,
                             void* y, void* flags, void* status, void* last_gen,
@@ -128,6 +133,8 @@ struct Plan {
   size_t esize;
   // staged path: running sums, step sizes, chunk-start states
   size_t g_off, dt_off, hc_off, staged_bytes;
+  // stage 3 with the interaction tile resident across heads (out_resident)
+  int resident_ok;
   // fused path: chunk-to-chunk flags and the state handed between chunks
   int fused_ok;
   size_t flags_off, chain_off, fused_bytes;
@@ -172,6 +179,7 @@ ssd_status plan_problem(const ssd_problem* prob, Plan* pl, bool need_chunk = tru
   pl->bf16 = p.io_dtype == SSD_BF16;
   pl->esize = pl->bf16 ? 2 : 4;
   pl->fused_ok = need_chunk && ssd::fused_fwd_supported(pl->bf16, pl->H, pl->G, pl->P, pl->N, (int)Q);
+  pl->resident_ok = need_chunk && ssd::out_resident_supported(pl->bf16, pl->H, pl->P, pl->N, (int)Q);
   return SSD_OK;
 }
 
@@ -205,6 +213,10 @@ ssd_config default_config(const Plan& pl) {
   // measure faster on MI355X (2.7B shape, cold cache: 0.29 ms against 0.37
   // ms), so the fused kernel is an explicit choice and a tuning candidate
   c.fused = 0;
+  // stage 3 with the interaction tile resident across heads where it is
+  // built (2.7B shape, cold cache: 0.22 ms for the whole pass against 0.28 ms
+  // with the head-pair kernel)
+  c.out_resident = pl.resident_ok ? 1 : 0;
   return c;
 }
 
@@ -215,6 +227,12 @@ ssd_status check_config(const Plan& pl, const ssd_config& c) {
     return fail(SSD_ERR_BAD_VALUE,
                 "config: the fused kernel is built for bf16 io, headdim 64, dstate 128, "
                 "chunk_size 256 and an even number of heads per group");
+  if (c.out_resident != 0 && c.out_resident != 1)
+    return fail(SSD_ERR_BAD_VALUE, "config: out_resident must be 0 or 1 (got %d)", c.out_resident);
+  if (c.out_resident && !pl.resident_ok)
+    return fail(SSD_ERR_BAD_VALUE,
+                "config: out_resident is built for bf16 io, headdim 64, dstate <= 128, "
+                "chunk_size 256 and nheads * headdim <= 2^22");
   if (c.cumsum_heads != 4 && c.cumsum_heads != 16)
     return fail(SSD_ERR_BAD_VALUE, "config: cumsum_heads must be 4 or 16 (got %d)", c.cumsum_heads);
   const int64_t hg = pl.H / pl.G;
@@ -560,6 +578,10 @@ static ssd_status run_out(const Plan& pl, const ssd_config& cfg, const void* x, 
   const float* dtw = reinterpret_cast<const float*>(ws + pl.dt_off);
   const void* Hc = ws + pl.hc_off;
   ssd::StatusRef status{reinterpret_cast<unsigned long long*>(const_cast<char*>(ws)), next_gen()};
+  if (cfg.out_resident)
+    return hip_status(ssd::launch_out_resident(x, B, C, Gw, dtw, Hc, D, y, status, pl.B, pl.L, pl.H,
+                                               pl.N, pl.G, pl.T, pl.Lp, s),
+                      "compute_out launch");
   return hip_status(ssd::launch_compute_out(pl.bf16, x, B, C, Gw, dtw, Hc, D, y, status, pl.B, pl.L,
                                             pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp,
                                             cfg.out_heads, s),
@@ -718,17 +740,21 @@ ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const 
     const ssd::DtXform* xfp = dtx ? &xf : nullptr;
     // the valid choices, in a fixed order: the fused kernel (where built),
     // then every staged combination
-    ssd_config cand[1 + 2 * 3 * 2];
+    // (the stage-3 choices: head-pair kernel with 2 or 1 heads, resident tile)
+    constexpr int kMaxCand = 1 + 2 * 3 * 3;
+    ssd_config cand[kMaxCand];
     int n = 0;
     if (pl.fused_ok) {
       ssd_config c = default_config(pl);
       c.fused = 1;
       cand[n++] = c;
     }
+    const int okh = ssd::compute_out_default_kh(pl.bf16, pl.H, pl.G, pl.N);
     for (int ch : {4, 16})
       for (int sh : {4, 2, 1})
-        for (int oh : {2, 1}) {
-          const ssd_config c{ch, sh, oh, 0};
+        for (int out = 0; out < 3; ++out) {
+          const int oh = out == 2 ? okh : 2 - out;
+          const ssd_config c{ch, sh, oh, 0, out == 2 ? 1 : 0};
           if (check_config(pl, c) == SSD_OK && check_supported(pl, oh) == SSD_OK) cand[n++] = c;
         }
     // mean ms of `reps` runs of choice c between two events (after one untimed run)
@@ -748,7 +774,7 @@ ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const 
     // warm the device up with the default choice, then measure every choice
     // twice, in forward and in reverse order, keeping the smaller mean, so a
     // drift of clocks or caches during the sweep does not favour one end
-    float warm = 0.0f, t_ms[1 + 2 * 3 * 2];
+    float warm = 0.0f, t_ms[kMaxCand];
     st = time_one(use, &warm);
     for (int i = 0; i < n && st == SSD_OK; ++i) st = time_one(cand[i], &t_ms[i]);
     for (int i = n - 1; i >= 0 && st == SSD_OK; --i) {

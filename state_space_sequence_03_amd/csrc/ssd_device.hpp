@@ -283,6 +283,34 @@ __device__ __forceinline__ void record_call(const StatusRef& s) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Hand-offs between the waves of one workgroup through LDS counters that
+// only grow.  wait_count waits until a counter reaches `target`; the wait is
+// bounded: past the bound the wave goes on and reports the timeout in the
+// call's status word rather than hang the workgroup (the protocols using it
+// cannot deadlock, so a timeout marks a bug).
+constexpr int kSpinLimit = 1 << 16;
+__device__ __forceinline__ void wait_count(int* ctr, int target, StatusRef flag, int lane) {
+  for (int spins = 0;; ++spins) {
+    // an atomic (not volatile) load, so it stays an LDS read
+    const int v = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (v >= target) break;
+    if (spins >= kSpinLimit) {
+      if (lane == 0) report_timeout(flag);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Add one to an LDS counter after this wave's earlier LDS accesses completed.
+__device__ __forceinline__ void bump_count(int* ctr, int lane) {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __asm__ __volatile__("" ::: "memory");
+}
+
 // Exchange through LDS between lanes of one wave: every LDS access of this
 // wave before the call completes before any after it.  The hardware keeps a
 // wave's LDS operations in order; the memory clobber keeps the compiler from

@@ -49,7 +49,7 @@ def test_exports_every_declared_symbol(so):
 
 
 def test_version_and_strings(so):
-    assert lib.ssd_abi_version() == 5
+    assert lib.ssd_abi_version() == 6
     for code in range(11):
         assert lib.ssd_status_string(code) and lib.ssd_status_string(code) != "unknown status"
     assert lib.ssd_status_string(77) == "unknown status"
@@ -314,8 +314,8 @@ def test_step_ignores_chunk_size(so):
 
 # ------------------------------------------------------------ tile choices
 
-def CFG(ch=4, sh=4, oh=2, fused=0):
-    return lib.ssd_config(ch, sh, oh, fused)
+def CFG(ch=4, sh=4, oh=2, fused=0, res=0):
+    return lib.ssd_config(ch, sh, oh, fused, res)
 
 
 def call_fwd_config(prob, cfg, **kw):
@@ -336,8 +336,14 @@ def call_fwd_config(prob, cfg, **kw):
     (dict(io_dtype=0), CFG(oh=2)),                     # fp32: one head per compute_out workgroup
     (dict(dstate=256), CFG(oh=2)),                     # dstate 256: accumulators do not fit twice
     (dict(nheads=6, ngroups=2), CFG(sh=1, oh=2)),      # 3 heads per group: odd
+    (dict(), CFG(res=2)),
+    (dict(chunk_size=128), CFG(res=1)),                # the resident tile is built for chunk 256
+    (dict(io_dtype=0), CFG(oh=1, res=1)),              # ... for bf16 io
+    (dict(dstate=144), CFG(oh=1, res=1)),              # ... for dstate <= 128
+    (dict(headdim=128), CFG(res=1)),                   # ... for headdim 64
 ], ids=["cumsum8", "state3", "out3", "fused2", "fused_q128", "fused_odd", "state4_hg2", "out2_fp32",
-        "out2_n256", "out2_odd"])
+        "out2_n256", "out2_odd", "resident2", "resident_q128", "resident_fp32", "resident_n144",
+        "resident_p128"])
 def test_fwd_config_rejects_bad_choice(so, kw, cfg):
     assert call_fwd_config(P(**kw), cfg) == BADVAL
     assert "config" in lib.ssd_last_error_message()
@@ -352,12 +358,12 @@ def test_fwd_config_check_order_and_default(so):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(batch=2, seqlen=8192, nheads=80, headdim=64, dstate=128, ngroups=1, chunk_size=256),
-     dict(cumsum_heads=4, state_heads=4, out_heads=2, fused=0)),
+     dict(cumsum_heads=4, state_heads=4, out_heads=2, fused=0, out_resident=1)),
     (dict(batch=8, seqlen=4096, nheads=64, headdim=64, dstate=256, ngroups=8, chunk_size=128),
-     dict(cumsum_heads=4, state_heads=4, out_heads=1, fused=0)),
-    (dict(nheads=6, ngroups=3), dict(cumsum_heads=4, state_heads=2, out_heads=2, fused=0)),
-    (dict(nheads=6, ngroups=2), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0)),
-    (dict(nheads=3, ngroups=3, io_dtype=0), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0)),
+     dict(cumsum_heads=4, state_heads=4, out_heads=1, fused=0, out_resident=0)),
+    (dict(nheads=6, ngroups=3), dict(cumsum_heads=4, state_heads=2, out_heads=2, fused=0, out_resident=1)),
+    (dict(nheads=6, ngroups=2), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0, out_resident=1)),
+    (dict(nheads=3, ngroups=3, io_dtype=0), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0, out_resident=0)),
 ])
 def test_default_config_is_the_static_table(so, kw, want):
     assert lib.ssd_default_config(P(**kw)) == want
@@ -388,7 +394,7 @@ def test_tune_validation(so):
 LLVM = "/opt/rocm/llvm/bin"
 BUILD_DIR = os.path.join(ROOT, "state_space_sequence_03_amd", "_build")
 KERNEL_OBJECTS = ["chunk_cumsum.o", "chunk_state.o", "state_pass.o", "compute_out.o", "step.o",
-                  "bwd.o", "fused_fwd.o"]
+                  "bwd.o", "fused_fwd.o", "out_resident.o"]
 
 
 def device_disassembly(obj, tmp_path):
@@ -402,6 +408,26 @@ def device_disassembly(obj, tmp_path):
     out = subprocess.run([f"{LLVM}/llvm-objdump", "-d", str(dev)], check=True,
                          capture_output=True, text=True).stdout
     return [l.split("//")[0].strip() for l in out.splitlines() if l.startswith("\t")]
+
+
+def device_functions(obj, tmp_path):
+    """The disassembly of `obj`'s device code split by function symbol."""
+    fat = tmp_path / (obj + ".fatbin2")
+    dev = tmp_path / (obj + ".co2")
+    subprocess.run([f"{LLVM}/llvm-objcopy", "--dump-section", f".hip_fatbin={fat}",
+                    os.path.join(BUILD_DIR, obj), str(tmp_path / (obj + ".host2"))], check=True)
+    subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o", f"--input={fat}",
+                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={dev}"], check=True)
+    out = subprocess.run([f"{LLVM}/llvm-objdump", "-d", str(dev)], check=True,
+                         capture_output=True, text=True).stdout
+    funcs, cur = {}, None
+    for line in out.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(.+)>:$", line)
+        if m:
+            cur = funcs.setdefault(m.group(1), [])
+        elif line.startswith("\t") and cur is not None:
+            cur.append(line.split("//")[0].strip())
+    return funcs
 
 
 @pytest.mark.skipif(not os.path.exists(f"{LLVM}/llvm-objdump"), reason="ROCm LLVM tools not installed")
@@ -511,3 +537,29 @@ def test_bwd_workspace_formula(so):
         want = (6 * a(Bt * H * T * Q * 4) + 2 * a(Bt * H * T * Pd * N * 4) + a(Bt * H * Pd * N * 4) +
                 2 * a(Bt * L * H * N * 4) + 2 * a(Bt * H * 8) + a(Bt * T * H * 4) + wide)
         assert bwd_ws(p) == (OK, want)
+
+
+@pytest.mark.skipif(not os.path.exists(f"{LLVM}/llvm-objdump"), reason="ROCm LLVM tools not installed")
+def test_resident_kernel_memory_operation_counts(so, tmp_path):
+    # The resident-tile kernel waits for one head's loads with a vmcnt target
+    # that counts the stores and loads issued after them: 8 stores of 8 bytes
+    # per wave and head (never merged, never branched around) and 7 direct
+    # loads (4 x blocks, 2 state blocks, one G or dt block).  The built code
+    # must have exactly that shape: 8 buffer_store_dwordx2; the only other
+    # stores write the status word (the call record before the first load,
+    # and a bounded wait's timeout report, a path that only a bug takes); and
+    # every vector load of the head loop a direct-to-LDS one.
+    funcs = device_functions("out_resident.o", tmp_path)
+    kernels = [f for f in funcs if "out_resident_kernel" in f]
+    assert len(kernels) == 3, list(funcs)             # dstate steps 1, 2 and 4
+    for f in kernels:
+        insts = funcs[f]
+        stores = [i for i in insts if re.match(r"buffer_store", i)]
+        assert len(stores) == 8 and all(i.startswith("buffer_store_dwordx2") for i in stores), (f, stores)
+        first_load = min(k for k, i in enumerate(insts) if i.startswith("global_load"))
+        others = [k for k, i in enumerate(insts) if re.match(r"(global|flat)_store", i)]
+        assert others and others[0] < first_load, (f, [insts[k] for k in others])
+        assert all(re.match(r"global_store_dwordx2 .* sc1$", insts[k]) for k in others), \
+            (f, [insts[k] for k in others])
+        loads = [i.split()[0] for i in insts if re.match(r"(buffer|global|flat)_load", i)]
+        assert set(loads) <= {"global_load_lds_dwordx4", "global_load_dwordx4"}, (f, set(loads))

@@ -48,10 +48,18 @@ def fused_built(p):
             and hg % 2 == 0)
 
 
+def resident_built(p):
+    return (p.io_dtype == "bf16" and p.headdim == 64 and p.dstate <= 128 and p.chunk_size == 256
+            and p.nheads * p.headdim <= 1 << 22)
+
+
 def valid_configs(p):
-    """The choices ssd_tune tries, in its order: the fused kernel where it is
-    built (with the default staged fields), then every staged combination."""
+    """The choices ssd_tune tries: the fused kernel where it is built (with
+    the default staged fields), then every staged combination -- stage 3 as
+    the head-pair kernel with 2 or 1 heads, or as the resident-tile kernel
+    where that is built (out_heads then at its default)."""
     hg = p.nheads // p.ngroups
+    pair2 = p.io_dtype == "bf16" and p.dstate <= 128 and hg % 2 == 0
     out = []
     if fused_built(p):
         d = lib.ssd_default_config(lib.make_problem(
@@ -59,12 +67,17 @@ def valid_configs(p):
             lib.SSD_BF16))
         d["fused"] = 1
         out.append(d)
-    for ch, sh, oh in itertools.product((4, 16), (1, 2, 4), (1, 2)):
+    for ch, sh in itertools.product((4, 16), (1, 2, 4)):
         if hg % sh:
             continue
-        if oh == 2 and not (p.io_dtype == "bf16" and p.dstate <= 128 and hg % 2 == 0):
-            continue
-        out.append(dict(cumsum_heads=ch, state_heads=sh, out_heads=oh, fused=0))
+        for oh in (1, 2):
+            if oh == 2 and not pair2:
+                continue
+            out.append(dict(cumsum_heads=ch, state_heads=sh, out_heads=oh, fused=0,
+                            out_resident=0))
+        if resident_built(p):
+            out.append(dict(cumsum_heads=ch, state_heads=sh, out_heads=2 if pair2 else 1,
+                            fused=0, out_resident=1))
     return out
 
 
