@@ -124,32 +124,47 @@ struct HeadSrc {
   const float* dt;    // dt row of (b, h) from t0
 };
 
-// Per-lane byte offsets of a head's loads (the same for every head).
+// Per-lane byte offsets of a head's loads (the same for every head and
+// block): an x row within a group of 8 rows and its swizzled 16-byte chunk,
+// and lane * 16 for the contiguous state, G and dt blocks.
 struct HeadOffsets {
-  uint32_t x[4];
-  uint32_t h[2];
+  uint32_t x;
+  uint32_t l16;
 };
 
-// The kLoadsPerHead loads of one head into buffer `buf`.  x rows past the
-// chunk's valid tokens read the last valid row (their values meet only
-// masked tile entries or rows that are never stored).
+// The kLoadsPerHead loads of one head into buffer `buf` (load k of this
+// wave).  In a chunk cut by the sequence end, x rows past its last valid
+// token read that token's row instead (their values meet only masked tile
+// entries or rows that are never stored).
 template <int NK>
 __device__ __forceinline__ void issue_load(int k, unsigned char* buf, const HeadSrc& s,
-                                           const HeadOffsets& o, int wave, int lane) {
-  if (k < 4)
-    dma16_so(s.x, o.x[k], buf + kBufX + (wave + 8 * k) * 1024);
-  else if (k < 6)
-    dma16_so(s.hc, o.h[k - 4], buf + kBufH + ((wave + 8 * (k - 4)) % (4 * NK)) * 1024);
-  else if (k == 6)
-    dma16_so(s.g, (uint32_t)lane * 16u, buf + kBufG);
-  else
-    dma16_so(s.dt, (uint32_t)lane * 16u, buf + kBufD);
+                                           const HeadOffsets& o, int64_t xstride, int qv,
+                                           int wave, int lane) {
+  if (k < 4) {
+    const int row0 = (wave + 8 * k) * 8;
+    unsigned char* dst = buf + kBufX + (wave + 8 * k) * 1024;
+    if (qv == kRsQ) {
+      dma16_so(s.x + (int64_t)row0 * xstride, o.x, dst);
+    } else {
+      const int r = row0 + lane / 8;
+      const int gc = (lane % 8) ^ xsw(r);
+      dma16(s.x + (int64_t)min(r, qv - 1) * xstride + gc * 8, dst);
+    }
+  } else if (k < 6) {
+    const int blk = (wave + 8 * (k - 4)) % (4 * NK);
+    dma16_so(s.hc + blk * 512, o.l16, buf + kBufH + blk * 1024);
+  } else if (k == 6) {
+    dma16_so(s.g, o.l16, buf + kBufG);
+  } else {
+    dma16_so(s.dt, o.l16, buf + kBufD);
+  }
 }
 template <int NK>
 __device__ __forceinline__ void issue_head(unsigned char* buf, const HeadSrc& s,
-                                           const HeadOffsets& o, int wave, int lane) {
+                                           const HeadOffsets& o, int64_t xstride, int qv,
+                                           int wave, int lane) {
 #pragma unroll
-  for (int k = 0; k < kLoadsPerHead; ++k) issue_load<NK>(k, buf, s, o, wave, lane);
+  for (int k = 0; k < kLoadsPerHead; ++k) issue_load<NK>(k, buf, s, o, xstride, qv, wave, lane);
 }
 
 // e_j = exp2(G_e - G_j) dt_j (e = last token of j's pair, so e_j <= dt_j)
@@ -229,17 +244,8 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
     return s;
   };
   HeadOffsets ho;
-  // the state's 4 NK blocks; for NK < 4 the second round repeats blocks
-  // (identical data to the same place), so the load count per head is fixed
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave + 8 * i) * 8 + lane / 8;
-    const int tok = min(r, qv - 1);
-    const int gc = (lane % 8) ^ xsw(r);
-    ho.x[i] = (uint32_t)(((int64_t)tok * xstride + gc * 8) * 2);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) ho.h[i] = (uint32_t)(((wave + 8 * i) % (4 * NK)) * 1024 + lane * 16);
+  ho.x = (uint32_t)(((int64_t)(lane / 8) * xstride + ((lane % 8) ^ xsw(lane / 8)) * 8) * 2);
+  ho.l16 = (uint32_t)lane * 16u;
 
   // ---- once per workgroup: C fragments, B rows, the resident tiles --------------
   // loads the compiler tracks first, so its own wait for them stays exact
@@ -265,7 +271,7 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
   lds_barrier();
   // head 0 -> buffer 0 while the tiles are built (issued after the wait: vector
   // memory completes in order, so a wait for C would otherwise wait for it too)
-  issue_head<NK>(smem, head_src(0), ho, wave, lane);
+  issue_head<NK>(smem, head_src(0), ho, xstride, qv, wave, lane);
 
   floatx4 tile[9][2];
 #pragma unroll
@@ -293,13 +299,11 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
   wait_vm_ops(0);                                          // this wave's head-0 loads landed
   weight_table(smem, tid);
   lds_barrier();     // B rows no longer read; every wave's head-0 loads and e table in place
-  if (nh > 1) issue_head<NK>(smem + kBufBytes, head_src(1), ho, wave, lane);
+  if (nh > 1) issue_head<NK>(smem + kBufBytes, head_src(1), ho, xstride, qv, wave, lane);
 
   // per-lane store offsets (bytes, relative to row 0 of the chunk, head 0)
   const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
       y + ((int64_t)b * L + t0) * xstride, (short)0, (int)((int64_t)qv * xstride * 2), 0x00020000);
-  const uint32_t so_e = (uint32_t)(((int64_t)(ib_e * 16 + lr) * xstride + 4 * lg) * 2);
-  const uint32_t so_l = (uint32_t)(((int64_t)(ib_l * 16 + lr) * xstride + 4 * lg) * 2);
 
   // Head hh starts after a barrier that follows every wave's wait for its
   // own loads of hh and the e table of hh (made by the first four waves), so
@@ -316,7 +320,7 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
     unsigned char* pbuf = smem + ((hh + 2) % kNBuf) * kBufBytes;
     const HeadSrc psrc = head_src(hh + 2);
     auto prefetch = [&](int k) {
-      if (pre) issue_load<NK>(k, pbuf, psrc, ho, wave, lane);
+      if (pre) issue_load<NK>(k, pbuf, psrc, ho, xstride, qv, wave, lane);
     };
     unsigned char* buf = smem + (hh % kNBuf) * kBufBytes;
     const float* Gs = reinterpret_cast<const float*>(buf + kBufG);
@@ -358,32 +362,51 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
     // masked per-element weights exp2(G_i - G_j) dt_j (the exponent is masked
     // to -inf before exp2, so no positive exponent is evaluated); D_h rides
     // on the diagonal
-    auto band = [&](const floatx4 (&st)[2], floatx4 (&acc)[4], int ib, float gr, int jb,
-                    const bf16x8 (&xf)[4]) {
+    // Of the band pair's two 16-token halves, an even block (rows = the first
+    // half) sees the second half masked out entirely, and an odd block sees
+    // the first half entirely below its rows (unmasked, no diagonal); only
+    // the half on the diagonal needs the per-element mask.  The values are
+    // those of the full masked evaluation (masked entries are exact zeros).
+    auto band_half = [&](auto oddc, const floatx4 (&st)[2], floatx4 (&acc)[4], int ib, float gr,
+                         int jb, const bf16x8 (&xf)[4]) {
+      constexpr int ODD = decltype(oddc)::value;
       const int i = ib * 16 + lr;
       const float gi = Gs[i];
-      // row minus the lane's first token column, laundered so the masks below
-      // are formed here rather than hoisted out of the head loop
-      const int d = opaque_v(i - jb - 4 * lg);
+      // row minus the lane's first token column of the diagonal half,
+      // laundered so the masks below are formed here rather than hoisted out
+      // of the head loop
+      const int d = opaque_v(i - jb - 16 * ODD - 4 * lg);
       const float u = fast_exp2(gi - gr);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[pt] *= u;
       bf16x8 af;
+      const floatx4 gj = *reinterpret_cast<const floatx4*>(Gs + jb + 16 * ODD + 4 * lg);
+      const floatx4 dj = *reinterpret_cast<const floatx4*>(ds + jb + 16 * ODD + 4 * lg);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const floatx4 gj = *reinterpret_cast<const floatx4*>(Gs + jb + 16 * t + 4 * lg);
-        const floatx4 dj = *reinterpret_cast<const floatx4*>(ds + jb + 16 * t + 4 * lg);
+      for (int r = 0; r < 4; ++r) {
+        const float ex = r <= d ? gi - gj[r] : -__builtin_inff();
+        float v = st[ODD][r] * (fast_exp2(ex) * dj[r]);
+        v = r == d ? v + dh : v;
+        af[4 * ODD + r] = static_cast<bf16>(v);
+      }
+      if constexpr (ODD) {
+        const floatx4 g0 = *reinterpret_cast<const floatx4*>(Gs + jb + 4 * lg);
+        const floatx4 d0 = *reinterpret_cast<const floatx4*>(ds + jb + 4 * lg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int jo = 16 * t + r;   // token j = jb + 4 lg + jo
-          const float ex = jo <= d ? gi - gj[r] : -__builtin_inff();
-          float v = st[t][r] * (fast_exp2(ex) * dj[r]);
-          v = jo == d ? v + dh : v;
-          af[4 * t + r] = static_cast<bf16>(v);
-        }
+        for (int r = 0; r < 4; ++r) af[r] = static_cast<bf16>(st[0][r] * (fast_exp2(gi - g0[r]) * d0[r]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) af[4 + r] = static_cast<bf16>(0.0f);
       }
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[pt] = mma(acc[pt], xf[pt], af);
+    };
+    auto band = [&](const floatx4 (&st)[2], floatx4 (&acc)[4], int ib, float gr, int jb,
+                    const bf16x8 (&xf)[4]) {
+      if (opaque_s(ib) & 1)
+        band_half(std::integral_constant<int, 1>{}, st, acc, ib, gr, jb, xf);
+      else
+        band_half(std::integral_constant<int, 0>{}, st, acc, ib, gr, jb, xf);
     };
 
     // per-pair weights: e of the lane's tokens and G at the pair's last token
@@ -454,7 +477,12 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
     }
 
     // y rows of both blocks: lane holds row i and p = 16 pt + 4 lg .. +3
-    const uint32_t hoff = (uint32_t)h * kRsP * 2;
+    // store offsets (bytes from row 0 of the chunk), formed here from a
+    // laundered lane index rather than kept in registers across the loop
+    const int lrv = opaque_v(lr);
+    const uint32_t hoff = (uint32_t)h * kRsP * 2 + (uint32_t)(4 * lg * 2);
+    const uint32_t so_e = (uint32_t)((ib_e * 16 + lrv) * (int)xstride * 2) + hoff;
+    const uint32_t so_l = (uint32_t)((ib_l * 16 + lrv) * (int)xstride * 2) + hoff;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       bf16x4 ve, vl;
@@ -464,9 +492,9 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
         vl[e] = static_cast<bf16>(acc_l[pt][e]);
       }
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ve), yr,
-                                            (int)(so_e + hoff + pt * 32), 0, 0);
+                                            (int)(so_e + pt * 32), 0, 0);
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, vl), yr,
-                                            (int)(so_l + hoff + pt * 32), 0, 0);
+                                            (int)(so_l + pt * 32), 0, 0);
     }
     if (hh + 1 < nh) {
       // this wave's loads of head hh+1 landed: after them it issued the
