@@ -5,9 +5,11 @@ One step = one ssd_fwd through the C ABI: the whole hot path over one batch of
 synthetic input (the single-pass fused kernel where it is built, else
 chunk_cumsum -> chunk_state -> state_pass -> compute_out).  Inputs are resident
 in HBM before timing starts.  The headline is the median of the timed steps
-with the 256 MB last-level cache flushed before each (the fill is outside the
-events); p10/p90, the mean and the warm back-to-back rate are reported beside
-it.  Prints one JSON line.
+with the 256 MB last-level cache flushed before each by reading a 512 MiB
+buffer (outside the events: the cache then holds clean, unrelated lines);
+p10/p90, the mean, the median after a 512 MiB write instead (whose dirty lines
+the timed step then has to write back) and the warm back-to-back rate are
+reported beside it.  Prints one JSON line.
 
 Default workload: the Mamba-2 2.7B-shaped layer, batch 2 x seqlen 8192,
 80 heads, headdim 64, dstate 128, 1 group, chunk 256, bf16 x/B/C, fp32
@@ -454,6 +456,10 @@ def main():
     ap.add_argument("--kernels", choices=("default", "fused", "staged"), default="default",
                     help="the forward kernels to time: the library's default choice for the "
                          "shape, the single-pass fused kernel, or the four staged kernels")
+    ap.add_argument("--evict", choices=("both", "read", "write"), default="both",
+                    help="cache eviction before each timed step: read 512 MiB (the headline), "
+                         "write 512 MiB (reported beside it), or both (default; a profiler run "
+                         "can restrict the timed steps to one kind)")
     ap.add_argument("--raw-dt", action="store_true",
                     help="pass the raw step size and let stage 1 apply bias + softplus")
     args = ap.parse_args()
@@ -531,26 +537,40 @@ def main():
         fwd()
     torch.cuda.synchronize()
 
-    # timed region: K steps, each after a 512 MiB fill that evicts the 256 MB
-    # last-level cache (outside the events), each bracketed by HIP events on
-    # the stream the kernels run on (torch's current stream)
+    # timed region: K steps, each after a read of a 512 MiB buffer that
+    # evicts the 256 MB last-level cache (outside the events), each bracketed
+    # by HIP events on the stream the kernels run on (torch's current stream)
     K = args.steps
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        flush.fill_(k & 0xFF)
-        evs[k][0].record()
-        fwd()
-        evs[k][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    cold = sorted(a.elapsed_time(b) for a, b in evs)
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+
+    def cold_steps(evict):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for k in range(K):
+            evict(k)
+            evs[k][0].record()
+            fwd()
+            evs[k][1].record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs), time.perf_counter() - t_start
+
+    def median(v):
+        return v[K // 2] if K % 2 else 0.5 * (v[K // 2 - 1] + v[K // 2])
+
+    if args.evict == "write":
+        cold, wall = cold_steps(lambda k: flush.fill_(k & 0xFF))
+    else:
+        cold, wall = cold_steps(lambda k: evict_by_reading(flush))
     cold_mean = sum(cold) / K
-    ms_step = cold[K // 2] if K % 2 else 0.5 * (cold[K // 2 - 1] + cold[K // 2])
+    ms_step = median(cold)
     p10, p90 = cold[int(0.1 * (K - 1))], cold[int(round(0.9 * (K - 1)))]
+    # secondary: the same after a 512 MiB write, which leaves the cache full of
+    # dirty lines that the timed step's own traffic then writes back
+    dirty = None
+    if args.evict == "both":
+        dirty, _ = cold_steps(lambda k: flush.fill_(k & 0xFF))
     del flush
 
     # secondary: the warm back-to-back rate (inputs partly in the last-level cache)
@@ -605,8 +625,13 @@ def main():
                                   "with the interaction tile resident across heads"
                                   if cfg.get("out_resident") else "per head pair"),
                    "dt": "raw, bias + softplus in the first stage" if args.raw_dt else "prepared"},
-        "timing": {"ms_per_step": "median of the timed steps, last-level cache flushed before each",
+        "timing": {"ms_per_step": "median of the timed steps, last-level cache evicted before "
+                                  "each by %s 512 MiB" % ("writing" if args.evict == "write"
+                                                           else "reading"),
                    "p10_ms": p10, "p90_ms": p90, "mean_ms": cold_mean,
+                   "after_write_fill_ms": median(dirty) if dirty else None,
+                   "after_write_fill_p10_p90_ms": [dirty[int(0.1 * (K - 1))],
+                                                   dirty[int(round(0.9 * (K - 1)))]] if dirty else None,
                    "warm_ms_per_step": warm_ms, "warm_tokens_per_s": cnt["tokens"] / (warm_ms * 1e-3),
                    "wall_s": wall},
         "path_mfma_frac": cnt["f_path"] / (ms_step * 1e-3) / peak_mfma,
@@ -626,18 +651,26 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def evict_by_reading(buf):
+    """Evict the last-level cache by reading `buf` (512 MiB, twice the cache):
+    the cache is then full of clean lines of an unrelated buffer, so the next
+    kernels neither hit their inputs nor write back someone else's data."""
+    import torch
+    buf.view(dtype=torch.float32).sum()   # fp32 in, fp32 out: one reduction, no temporary
+
+
 def staged_compute_out_ms(args, ssd, prob, d, ws, y, dt_in, dt_kw):
     """Mean event-timed compute_out launch on the staged path (stages 1-2 and
-    stage 3 enqueued separately, cache flushed before each step)."""
+    stage 3 enqueued separately, cache evicted by reading before each step)."""
     import torch
     Q = prob.chunk_size
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=d["x"].device)
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=d["x"].device)
     fin = torch.empty((prob.batch, prob.nheads, prob.headdim, prob.dstate), dtype=torch.float32,
                       device=d["x"].device)
     tot = 0.0
     n = max(1, args.steps)
     for k in range(n):
-        flush.fill_(k & 0xFF)
+        evict_by_reading(flush)
         ssd.ssd_fwd_states(d["x"], dt_in, d["A"], d["B"], Q, d["init_state"],
                            want_chunk_states=False, workspace=ws, final_out=fin, **dt_kw)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
