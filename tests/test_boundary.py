@@ -563,3 +563,6 @@ def test_resident_kernel_memory_operation_counts(so, tmp_path):
             (f, [insts[k] for k in others])
         loads = [i.split()[0] for i in insts if re.match(r"(buffer|global|flat)_load", i)]
         assert set(loads) <= {"global_load_lds_dwordx4", "global_load_dwordx4"}, (f, set(loads))
+        # no register spills either: their scratch traffic would be vector
+        # memory operations the per-head counts do not include
+        assert not any(i.startswith("scratch_") for i in insts), f
