@@ -223,7 +223,10 @@ def bench_bwd(args):
     io = ssd.SSD_BF16 if prob.io_dtype == "bf16" else ssd.SSD_F32
     cprob = ssd.make_problem(prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate,
                              prob.ngroups, prob.chunk_size, io)
-    ws = torch.empty(ssd.ssd_bwd_workspace_size(cprob), dtype=torch.uint8, device=dev)
+    # the default workspace unless --bwd-workspace-bytes asks for another size
+    # (ssd_bwd batches the heads to fit it; the results do not change)
+    ws_bytes = args.bwd_workspace_bytes or ssd.ssd_bwd_workspace_size(cprob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step():
         return ssd.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], prob.chunk_size,
@@ -261,7 +264,8 @@ def bench_bwd(args):
         "config": {"workload": prob.name, "pass": "backward", "batch": prob.batch,
                    "seqlen": prob.seqlen, "nheads": prob.nheads, "headdim": prob.headdim,
                    "dstate": prob.dstate, "ngroups": prob.ngroups, "chunk_size": prob.chunk_size,
-                   "init_state": prob.init_std is not None, "dfinal": True},
+                   "init_state": prob.init_std is not None, "dfinal": True,
+                   "workspace_bytes": ws_bytes},
         # the whole backward call (every kernel of ssd_bwd) bracketed by events on
         # the stream it is enqueued on; the per-kernel split is in the kernel trace
         "roofline": {"kernel": "ssd_bwd (all kernels)", "bound": "mfma",
@@ -451,6 +455,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one captured HIP graph of the whole pass")
     ap.add_argument("--mode", choices=("prefill", "decode", "bwd"), default="prefill")
+    ap.add_argument("--bwd-workspace-bytes", type=int, default=0,
+                    help="--mode bwd: workspace size to give ssd_bwd (0: its default)")
     ap.add_argument("--tune", action="store_true",
                     help="time every valid tile choice of the forward pass (ssd_tune)")
     ap.add_argument("--kernels", choices=("default", "fused", "staged"), default="default",

@@ -417,9 +417,26 @@ ssd_status ssd_step(const ssd_problem* prob, const ssd_dt_transform* dtx, float*
 
 /* ------------------------------------------------------------------ backward */
 
-/* Workspace bytes that ssd_bwd needs for `prob` (errors as for ssd_bwd's
- * shape checks). */
+/* Default workspace bytes of ssd_bwd for `prob`, and the least it accepts
+ * (errors as for ssd_bwd's shape checks).
+ *
+ * The largest part of the workspace holds per-head fp32 partial gradients of
+ * B and C, which are summed over the heads of each group.  ssd_bwd forms
+ * them for a batch of heads at a time and folds each batch into running
+ * fp32 sums per group before the next, so the workspace it needs shrinks
+ * with the heads per batch.  Given workspace_bytes, ssd_bwd considers the
+ * batchings into equal batches whose layout fits and takes the one whose
+ * per-chunk kernel launches need the fewest rounds of the workgroups the
+ * device runs at once (the fewest batches on a tie).  The default size
+ * keeps each batch's partial gradients within the room of one fp32 copy of x
+ * (all heads in one batch when 2 dstate <= headdim), but keeps enough heads
+ * per batch for about 1024 workgroups per launch; the minimum is the
+ * smallest layout over all head counts.  Larger workspaces allow larger
+ * batches, up to all heads.  Results do not depend on the batching: the
+ * per-group sums add the heads in ascending order either way, so they are
+ * bitwise identical for any accepted workspace size. */
 ssd_status ssd_bwd_workspace_size(const ssd_problem* prob, size_t* bytes);
+ssd_status ssd_bwd_workspace_min_size(const ssd_problem* prob, size_t* bytes);
 
 /* Gradients of the scan: given dy = dLoss/dy and, optionally, dfinal =
  * dLoss/d(final state), the gradients of every input of ssd_fwd_ex.
@@ -461,7 +478,8 @@ ssd_status ssd_bwd_workspace_size(const ssd_problem* prob, size_t* bytes);
  * io dtype.  Deterministic: the same call gives bitwise the same results.
  * Outputs must not overlap inputs or each other.  Every pointer 16-byte
  * aligned.  Errors as for ssd_fwd_ex (same order: NULL pointers, shape,
- * chunk, dtype, transform values, alignment, limits, workspace); in
+ * chunk, dtype, transform values, alignment, limits, workspace, where
+ * SSD_ERR_WORKSPACE means below ssd_bwd_workspace_min_size); in
  * addition SSD_ERR_UNSUPPORTED when headdim exceeds 256 or the per-chunk
  * tiles of headdim x dstate do not fit the LDS.  Enqueued on `stream`
  * without synchronising. */

@@ -13,7 +13,8 @@ Names match the C ABI in include/ssd.h:
     ssd_fwd, ssd_fwd_ex, ssd_fwd_states, ssd_fwd_states_ex, ssd_compute_out, ssd_chunk_cumsum,
     ssd_chunk_cumsum_ex, ssd_step, ssd_default_config, ssd_tune, ssd_fwd_workspace_size,
     ssd_fwd_config_workspace_size, ssd_fwd_status, ssd_fwd_noalloc, ssd_bwd,
-    ssd_bwd_workspace_size, ssd_status_string, ssd_last_error_message, ssd_abi_version
+    ssd_bwd_workspace_size, ssd_bwd_workspace_min_size, ssd_status_string,
+    ssd_last_error_message, ssd_abi_version
 (ssd_fwd_config is reached through ssd_fwd(..., config=...).)
 """
 from __future__ import annotations
@@ -29,7 +30,8 @@ __all__ = ["SsdError", "SsdArgumentError", "lib_path", "load_library", "make_pro
            "ssd_abi_version", "ssd_status_string", "ssd_last_error_message",
            "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_states", "ssd_compute_out",
            "ssd_chunk_cumsum", "ssd_fwd_ex", "ssd_fwd_states_ex", "ssd_chunk_cumsum_ex",
-           "ssd_step", "ssd_default_config", "ssd_tune", "ssd_bwd_workspace_size", "ssd_bwd",
+           "ssd_step", "ssd_default_config", "ssd_tune", "ssd_bwd_workspace_size",
+           "ssd_bwd_workspace_min_size", "ssd_bwd",
            "ssd_fwd_config_workspace_size", "staged_workspace_size", "ssd_fwd_status",
            "ssd_fwd_noalloc", "SSD_F32", "SSD_BF16"]
 
@@ -150,6 +152,8 @@ def load_library():
         lib.ssd_fwd_noalloc.argtypes = [P, X] + [vp] * 10
         lib.ssd_bwd_workspace_size.restype = ctypes.c_int
         lib.ssd_bwd_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+        lib.ssd_bwd_workspace_min_size.restype = ctypes.c_int
+        lib.ssd_bwd_workspace_min_size.argtypes = [P, ctypes.POINTER(sz)]
         lib.ssd_bwd.restype = ctypes.c_int
         lib.ssd_bwd.argtypes = [P, X] + [vp] * 18 + [sz, vp]
         _lib = lib
@@ -522,6 +526,12 @@ def ssd_bwd_workspace_size(prob: ssd_problem) -> int:
     return int(n.value)
 
 
+def ssd_bwd_workspace_min_size(prob: ssd_problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ssd_bwd_workspace_min_size(ctypes.byref(prob), ctypes.byref(n)))
+    return int(n.value)
+
+
 def ssd_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
             C: torch.Tensor, D: Optional[torch.Tensor], chunk_size: int,
             init_state: Optional[torch.Tensor], dy: torch.Tensor,
@@ -556,8 +566,8 @@ def ssd_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
            "dD": torch.empty(H, **f32) if want_dD else None,
            "dinit": torch.empty(state_shape, **f32) if want_dinit else None,
            "ddt_bias": torch.empty(H, **f32) if want_ddt_bias else None}
-    need = ssd_bwd_workspace_size(prob)
     if workspace is None:
+        need = ssd_bwd_workspace_size(prob)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     xf, xfp = _dt_transform(H, dt_bias, dt_softplus, dt_limit)
     st = lib.ssd_bwd(ctypes.byref(prob), xfp, _dev(x, "x"), _dev(dt, "dt", torch.float32),

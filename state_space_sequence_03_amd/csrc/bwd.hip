@@ -159,10 +159,12 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
                   const T* __restrict__ dy, const float* __restrict__ Gw,
                   const float* __restrict__ dtw, const float* __restrict__ Hc,
                   float* __restrict__ Pout, float* __restrict__ dCh, int64_t L, int H, int P,
-                  int N, int G, int hpg, int Q, int T_, int64_t ldw) {
+                  int N, int G, int hpg, int Q, int T_, int64_t ldw, int h0, int hb) {
   constexpr int TB = kBwdTB, ldW = kBwdLdW, NT = NKN / 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int c = blockIdx.x, h = blockIdx.y;
+  // heads h0 .. h0 + gridDim.y - 1 of this launch; their dC parts are rows
+  // of hb heads
+  const int c = blockIdx.x, h = h0 + (int)blockIdx.y;
   const int64_t b = blockIdx.z;
   const int g = h / hpg;
   const int tid = threadIdx.x;
@@ -298,7 +300,7 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       pc[r] = sum16(pc[r]);
       if (l16 == 0) Pc[nh * TB + i] = pc[r];
       if (i < vi) {
-        float* dst = dCh + ((b * L + ti0 + i) * H + h) * (int64_t)N + l16;
+        float* dst = dCh + ((b * L + ti0 + i) * hb + (h - h0)) * (int64_t)N + l16;
 #pragma unroll
         for (int q = 0; q < NT; ++q) {
           const int nt = nh + 2 * q;
@@ -333,10 +335,12 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
                   const float* __restrict__ dtw, const float* __restrict__ Lam,
                   const float* __restrict__ Dv, T* __restrict__ dx, float* __restrict__ dBh,
                   float* __restrict__ Qout, float* __restrict__ dDpart, int64_t L, int H, int P,
-                  int N, int G, int hpg, int Q, int T_, int64_t ldw) {
+                  int N, int G, int hpg, int Q, int T_, int64_t ldw, int h0, int hb) {
   constexpr int TB = kBwdTB, ldW = kBwdLdW, NT = NKN / 2, PT = NKP / 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int c = blockIdx.x, h = blockIdx.y;
+  // heads h0 .. h0 + gridDim.y - 1 of this launch; their dB parts are rows
+  // of hb heads
+  const int c = blockIdx.x, h = h0 + (int)blockIdx.y;
   const int64_t b = blockIdx.z;
   const int g = h / hpg;
   const int tid = threadIdx.x;
@@ -533,7 +537,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 #pragma unroll
         for (int q = 0; q < NT; ++q) {
           const int nt = nh + 2 * q;
-          if (nt < ntn) dBh[row * N + 16 * nt + l16] = d * dba[q][r];
+          if (nt < ntn) dBh[((b * L + tj0 + j) * hb + (h - h0)) * N + 16 * nt + l16] = d * dba[q][r];
         }
       }
     }
@@ -657,11 +661,18 @@ bwd_prep_kernel(const float* __restrict__ Gw, float* __restrict__ w2, float* __r
   }
 }
 
-// dB and dC: sums over the heads of each group of the per-head fp32 parts
+// dB and dC: sums over the heads of each group of the per-head fp32 parts,
+// one batch of heads h0 .. h0 + nb - 1 at a time (parts in rows of hb heads).
+// Each element adds its group's heads of the batch in ascending order to the
+// running fp32 sum (starting from zero at the group's first head) and, at the
+// group's last head, stores the io-dtype result: the order of additions is
+// that of one pass over all the heads, whatever the batches.
 template <typename T>
 __global__ void __launch_bounds__(kBwdThreads)
 bwd_group_sum_kernel(const float* __restrict__ dBh, const float* __restrict__ dCh,
-                     T* __restrict__ dB, T* __restrict__ dC, int64_t total, int H, int G, int N) {
+                     float* __restrict__ accB, float* __restrict__ accC, T* __restrict__ dB,
+                     T* __restrict__ dC, int64_t total, int H, int G, int N, int h0, int nb,
+                     int hb) {
   const int hpg = H / G;
   for (int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * kBwdThreads) {
@@ -669,32 +680,56 @@ bwd_group_sum_kernel(const float* __restrict__ dBh, const float* __restrict__ dC
     const int64_t bg = e / N;                 // (b*L + t)*G + g
     const int64_t bt = bg / G;
     const int g = (int)(bg % G);
-    const int64_t base = (bt * H + (int64_t)g * hpg) * N + n;
-    float sb = 0.0f, sc = 0.0f;
-    for (int k = 0; k < hpg; ++k) {
+    const int ha = max(h0, g * hpg), hz = min(h0 + nb, (g + 1) * hpg);
+    if (ha >= hz) continue;                   // no head of this group in the batch
+    const bool first = ha == g * hpg, last = hz == (g + 1) * hpg;
+    float sb = first ? 0.0f : accB[e], sc = first ? 0.0f : accC[e];
+    const int64_t base = (bt * hb + (ha - h0)) * N + n;
+    for (int k = 0; k < hz - ha; ++k) {
       sb += dBh[base + (int64_t)k * N];
       sc += dCh[base + (int64_t)k * N];
     }
-    dB[e] = to_io<T>(sb);
-    dC[e] = to_io<T>(sc);
+    if (last) {
+      dB[e] = to_io<T>(sb);
+      dC[e] = to_io<T>(sc);
+    } else {
+      accB[e] = sb;
+      accC[e] = sc;
+    }
   }
 }
 
-// dA, dD and the bias gradient: sums of the per-(b, h) and per-(b, c, h) parts
+// dA, dD and the bias gradient: sums of the per-(b, h) and per-(b, c, h)
+// parts.  One workgroup per head; thread i adds parts i, i + 256, ... and a
+// fixed tree adds the threads' sums, so the result is deterministic.
 __global__ void __launch_bounds__(kBwdThreads)
 bwd_scalars_kernel(const double* __restrict__ dApart, const double* __restrict__ dbpart,
                    const float* __restrict__ dDpart, float* __restrict__ dA, float* __restrict__ dD,
                    float* __restrict__ dbias, int64_t batch, int H, int T_) {
-  for (int h = threadIdx.x; h < H; h += kBwdThreads) {
-    double sa = 0.0, sb = 0.0, sd = 0.0;
-    for (int64_t b = 0; b < batch; ++b) {
-      sa += dApart[b * H + h];
-      sb += dbpart[b * H + h];
-      for (int c = 0; c < T_; ++c) sd += dDpart[(b * T_ + c) * H + h];
+  __shared__ double red[3][kBwdThreads];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  double sa = 0.0, sb = 0.0, sd = 0.0;
+  for (int64_t b = tid; b < batch; b += kBwdThreads) {
+    sa += dApart[b * H + h];
+    sb += dbpart[b * H + h];
+  }
+  for (int64_t bc = tid; bc < batch * T_; bc += kBwdThreads) sd += dDpart[bc * H + h];
+  red[0][tid] = sa;
+  red[1][tid] = sb;
+  red[2][tid] = sd;
+  __syncthreads();
+  for (int w = kBwdThreads / 2; w >= 1; w >>= 1) {
+    if (tid < w) {
+      red[0][tid] += red[0][tid + w];
+      red[1][tid] += red[1][tid + w];
+      red[2][tid] += red[2][tid + w];
     }
-    dA[h] = (float)sa;
-    if (dD) dD[h] = (float)sd;
-    if (dbias) dbias[h] = (float)sb;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    dA[h] = (float)red[0][0];
+    if (dD) dD[h] = (float)red[2][0];
+    if (dbias) dbias[h] = (float)red[1][0];
   }
 }
 
@@ -711,33 +746,75 @@ int bwd_block_rows(int io_bf16, int Q, int64_t P, int64_t N) {
   return a <= lim && s <= lim ? kBwdTB : 0;
 }
 
+// Workgroups of the two per-chunk kernels that the device runs at once: the
+// smaller of their resident counts per CU (registers, LDS, waves) times the
+// CU count of the current device; 0 if the runtime cannot say.
+template <typename T, int NKN, int NKP>
+static int64_t chunk_slots_of(int64_t P, int64_t N) {
+  int dev = 0, cus = 0, a = 0, b = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (ensure_dyn_lds<bwd_target_kernel<T, NKN>>(bwd_target_bytes<T>((int)P, (int)N)) != hipSuccess ||
+      ensure_dyn_lds<bwd_source_kernel<T, NKN, NKP>>(bwd_source_bytes<T>((int)P, (int)N)) !=
+          hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, bwd_target_kernel<T, NKN>, kBwdThreads,
+                                                   bwd_target_bytes<T>((int)P, (int)N)) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, bwd_source_kernel<T, NKN, NKP>,
+                                                   kBwdThreads,
+                                                   bwd_source_bytes<T>((int)P, (int)N)) !=
+          hipSuccess)
+    return 0;
+  return (int64_t)cus * (a < b ? a : b);
+}
+
+template <typename T>
+static int64_t chunk_slots_t(int64_t P, int64_t N) {
+  if (N <= 128) {
+    if (P <= 64) return chunk_slots_of<T, 8, 4>(P, N);
+    if (P <= 128) return chunk_slots_of<T, 8, 8>(P, N);
+    return chunk_slots_of<T, 8, 16>(P, N);
+  }
+  if (P <= 64) return chunk_slots_of<T, 16, 4>(P, N);
+  if (P <= 128) return chunk_slots_of<T, 16, 8>(P, N);
+  return chunk_slots_of<T, 16, 16>(P, N);
+}
+
+int64_t bwd_chunk_slots(int io_bf16, int64_t P, int64_t N) {
+  const int64_t s = io_bf16 ? chunk_slots_t<bf16>(P, N) : chunk_slots_t<float>(P, N);
+  (void)hipGetLastError();   // a failed query leaves no error behind for the launches
+  return s;
+}
+
 template <typename T, int NKN, int NKP>
 static hipError_t launch_chunks(const void* x, const void* Bm, const void* Cm, const void* dy,
                                 const float* Gw, const float* dtw, const void* Hc, const void* Lam,
                                 const float* Dv, void* dx, float* Pb, float* Qb, float* dBh,
                                 float* dCh, float* dDpart, int64_t batch, int64_t L, int64_t H,
                                 int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                                hipStream_t stream) {
+                                int h0, int nb, int hb, hipStream_t stream) {
   const int ta = bwd_target_bytes<T>((int)P, (int)N);
   const int sb = bwd_source_bytes<T>((int)P, (int)N);
   hipError_t e = ensure_dyn_lds<bwd_target_kernel<T, NKN>>(ta);
   if (e != hipSuccess) return e;
   e = ensure_dyn_lds<bwd_source_kernel<T, NKN, NKP>>(sb);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)T_, (unsigned)H, (unsigned)batch);
+  const dim3 grid((unsigned)T_, (unsigned)nb, (unsigned)batch);
   const int hpg = (int)(H / G);
   hipLaunchKernelGGL((bwd_target_kernel<T, NKN>), grid, dim3(kBwdThreads), ta, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm),
                      static_cast<const T*>(Cm), static_cast<const T*>(dy), Gw, dtw,
                      static_cast<const float*>(Hc), Pb, dCh, L, (int)H, (int)P, (int)N, (int)G,
-                     hpg, Q, (int)T_, ldw);
+                     hpg, Q, (int)T_, ldw, h0, hb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_source_kernel<T, NKN, NKP>), grid, dim3(kBwdThreads), sb, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm),
                      static_cast<const T*>(Cm), static_cast<const T*>(dy), Gw, dtw,
                      static_cast<const float*>(Lam), Dv, static_cast<T*>(dx), dBh, Qb, dDpart, L,
-                     (int)H, (int)P, (int)N, (int)G, hpg, Q, (int)T_, ldw);
+                     (int)H, (int)P, (int)N, (int)G, hpg, Q, (int)T_, ldw, h0, hb);
   return hipGetLastError();
 }
 
@@ -747,9 +824,10 @@ static hipError_t launch_chunks_p(int64_t P, const void* x, const void* Bm, cons
                                   const void* Hc, const void* Lam, const float* Dv, void* dx,
                                   float* Pb, float* Qb, float* dBh, float* dCh, float* dDpart,
                                   int64_t batch, int64_t L, int64_t H, int64_t N, int64_t G, int Q,
-                                  int64_t T_, int64_t ldw, hipStream_t stream) {
+                                  int64_t T_, int64_t ldw, int h0, int nb, int hb,
+                                  hipStream_t stream) {
 #define SSD_BWD_ARGS x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh, dDpart, batch, L, H, \
-                     P, N, G, Q, T_, ldw, stream
+                     P, N, G, Q, T_, ldw, h0, nb, hb, stream
   if (P <= 64) return launch_chunks<T, NKN, 4>(SSD_BWD_ARGS);
   if (P <= 128) return launch_chunks<T, NKN, 8>(SSD_BWD_ARGS);
   return launch_chunks<T, NKN, 16>(SSD_BWD_ARGS);
@@ -762,9 +840,10 @@ static hipError_t launch_chunks_t(int TB, const void* x, const void* Bm, const v
                                   const void* Hc, const void* Lam, const float* Dv, void* dx,
                                   float* Pb, float* Qb, float* dBh, float* dCh, float* dDpart,
                                   int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                                  int64_t G, int Q, int64_t T_, int64_t ldw, hipStream_t stream) {
+                                  int64_t G, int Q, int64_t T_, int64_t ldw, int h0, int nb, int hb,
+                                  hipStream_t stream) {
 #define SSD_BWD_ARGS P, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh, dDpart, batch, L, \
-                     H, N, G, Q, T_, ldw, stream
+                     H, N, G, Q, T_, ldw, h0, nb, hb, stream
   if (TB != kBwdTB) return hipErrorInvalidValue;
   if (N <= 128) return launch_chunks_p<T, 8>(SSD_BWD_ARGS);
   return launch_chunks_p<T, 16>(SSD_BWD_ARGS);
@@ -794,21 +873,38 @@ hipError_t launch_bwd_chunks(int io_bf16, int TB, const void* x, const void* Bm,
                              const void* Lam, const float* Dv, void* dx, float* Pb, float* Qb,
                              float* dBh, float* dCh, float* dDpart, int64_t batch, int64_t L,
                              int64_t H, int64_t P, int64_t N, int64_t G, int Q, int64_t T_,
-                             int64_t ldw, hipStream_t stream) {
+                             int64_t ldw, int h0, int nb, int hb, hipStream_t stream) {
   if (io_bf16)
     return launch_chunks_t<bf16>(TB, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh,
-                                 dDpart, batch, L, H, P, N, G, Q, T_, ldw, stream);
+                                 dDpart, batch, L, H, P, N, G, Q, T_, ldw, h0, nb, hb, stream);
   return launch_chunks_t<float>(TB, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh,
-                                dDpart, batch, L, H, P, N, G, Q, T_, ldw, stream);
+                                dDpart, batch, L, H, P, N, G, Q, T_, ldw, h0, nb, hb, stream);
 }
 
-hipError_t launch_bwd_finish(int io_bf16, const float* Pb, const float* Qb, const float* dtw,
+hipError_t launch_bwd_group_sum(int io_bf16, const float* dBh, const float* dCh, float* accB,
+                                float* accC, void* dB, void* dC, int64_t batch, int64_t L,
+                                int64_t H, int64_t N, int64_t G, int h0, int nb, int hb,
+                                hipStream_t stream) {
+  const int64_t total = batch * L * G * N;
+  const int64_t blocks = (total + kBwdThreads - 1) / kBwdThreads;
+  const dim3 g2((unsigned)(blocks < 8192 ? blocks : 8192));
+  if (io_bf16)
+    hipLaunchKernelGGL(bwd_group_sum_kernel<bf16>, g2, dim3(kBwdThreads), 0, stream, dBh, dCh,
+                       accB, accC, static_cast<bf16*>(dB), static_cast<bf16*>(dC), total, (int)H,
+                       (int)G, (int)N, h0, nb, hb);
+  else
+    hipLaunchKernelGGL(bwd_group_sum_kernel<float>, g2, dim3(kBwdThreads), 0, stream, dBh, dCh,
+                       accB, accC, static_cast<float*>(dB), static_cast<float*>(dC), total,
+                       (int)H, (int)G, (int)N, h0, nb, hb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_finish(const float* Pb, const float* Qb, const float* dtw,
                              const float* dt_in, const float* A, const float* dfinal,
                              const float* fin, const DtXform* xf, float* ddt, double* dApart,
-                             double* dbpart, const float* dBh, const float* dCh,
-                             const float* dDpart, void* dB, void* dC, float* dA, float* dD,
+                             double* dbpart, const float* dDpart, float* dA, float* dD,
                              float* dbias, int64_t batch, int64_t L, int64_t H, int64_t P,
-                             int64_t N, int64_t G, int64_t T_, int64_t ldw, hipStream_t stream) {
+                             int64_t N, int64_t T_, int64_t ldw, hipStream_t stream) {
   const dim3 g1((unsigned)H, (unsigned)batch);
   if (xf)
     hipLaunchKernelGGL(bwd_dt_kernel<true>, g1, dim3(kBwdThreads), 0, stream, Pb, Qb, dtw, dt_in,
@@ -819,21 +915,8 @@ hipError_t launch_bwd_finish(int io_bf16, const float* Pb, const float* Qb, cons
                        (int)H, P * N, ldw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t total = batch * L * G * N;
-  const int64_t blocks = (total + kBwdThreads - 1) / kBwdThreads;
-  const dim3 g2((unsigned)(blocks < 8192 ? blocks : 8192));
-  if (io_bf16)
-    hipLaunchKernelGGL(bwd_group_sum_kernel<bf16>, g2, dim3(kBwdThreads), 0, stream, dBh, dCh,
-                       static_cast<bf16*>(dB), static_cast<bf16*>(dC), total, (int)H, (int)G,
-                       (int)N);
-  else
-    hipLaunchKernelGGL(bwd_group_sum_kernel<float>, g2, dim3(kBwdThreads), 0, stream, dBh, dCh,
-                       static_cast<float*>(dB), static_cast<float*>(dC), total, (int)H, (int)G,
-                       (int)N);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_scalars_kernel, dim3(1), dim3(kBwdThreads), 0, stream, dApart, dbpart,
-                     dDpart, dA, dD, dbias, batch, (int)H, (int)T_);
+  hipLaunchKernelGGL(bwd_scalars_kernel, dim3((unsigned)H), dim3(kBwdThreads), 0, stream, dApart,
+                     dbpart, dDpart, dA, dD, dbias, batch, (int)H, (int)T_);
   return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 // synchronising.  No exception leaves this file.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cstdarg>
@@ -57,6 +58,7 @@ int compute_out_kh_valid(int io_bf16, int64_t H, int64_t G, int64_t N, int kh);
 int compute_out_default_kh(int io_bf16, int64_t H, int64_t G, int64_t N);
 int chunk_state_default_kh(int64_t H, int64_t G);
 int bwd_block_rows(int io_bf16, int Q, int64_t P, int64_t N);
+int64_t bwd_chunk_slots(int io_bf16, int64_t P, int64_t N);
 hipError_t launch_bwd_widen(const void* src, float* dst, int64_t n, hipStream_t stream);
 hipError_t launch_bwd_prep(const float* Gw, float* w2, float* Gz, int64_t batch, int64_t H,
                            int64_t L, int64_t ldw, hipStream_t stream);
@@ -65,14 +67,17 @@ hipError_t launch_bwd_chunks(int io_bf16, int TB, const void* x, const void* Bm,
                              const void* Lam, const float* Dv, void* dx, float* Pb, float* Qb,
                              float* dBh, float* dCh, float* dDpart, int64_t batch, int64_t L,
                              int64_t H, int64_t P, int64_t N, int64_t G, int Q, int64_t T_,
-                             int64_t ldw, hipStream_t stream);
-hipError_t launch_bwd_finish(int io_bf16, const float* Pb, const float* Qb, const float* dtw,
+                             int64_t ldw, int h0, int nb, int hb, hipStream_t stream);
+hipError_t launch_bwd_group_sum(int io_bf16, const float* dBh, const float* dCh, float* accB,
+                                float* accC, void* dB, void* dC, int64_t batch, int64_t L,
+                                int64_t H, int64_t N, int64_t G, int h0, int nb, int hb,
+                                hipStream_t stream);
+hipError_t launch_bwd_finish(const float* Pb, const float* Qb, const float* dtw,
                              const float* dt_in, const float* A, const float* dfinal,
                              const float* fin, const DtXform* xf, float* ddt, double* dApart,
-                             double* dbpart, const float* dBh, const float* dCh,
-                             const float* dDpart, void* dB, void* dC, float* dA, float* dD,
+                             double* dbpart, const float* dDpart, float* dA, float* dD,
                              float* dbias, int64_t batch, int64_t L, int64_t H, int64_t P,
-                             int64_t N, int64_t G, int64_t T_, int64_t ldw, hipStream_t stream);
+                             int64_t N, int64_t T_, int64_t ldw, hipStream_t stream);
 }  // namespace ssd
 
 namespace {
@@ -290,16 +295,28 @@ size_t config_bytes(const Plan& pl, const ssd_config& c) {
 // per-head dB/dC parts, the per-(b, h) / per-(b, c, h) scalar parts and, for
 // bf16 io, fp32 copies of x, dy, B and C for the fp32 state stages.
 struct BwdPlan {
-  size_t g_off, dt_off, gz_off, w2_off, pb_off, qb_off, hc_off, lam_off, fin_off, dbh_off,
-      dch_off, dap_off, dbp_off, ddp_off, x32_off, dy32_off, b32_off, c32_off, bytes;
+  size_t g_off, dt_off, gz_off, w2_off, pb_off, qb_off, hc_off, lam_off, fin_off, dap_off,
+      dbp_off, ddp_off, b32_off, c32_off, acb_off, acc_off, big_off, dbh_off, dch_off, bytes;
   int TB;
+  int hb;    // heads per batch of the chunk kernels (their dB/dC parts are rows of hb heads)
 };
 
-BwdPlan bwd_plan(const Plan& pl) {
+// Workspace of the backward pass for batches of hb heads.  The per-head fp32
+// dB/dC parts are the largest item (2 x B L H N floats); they are produced
+// for hb heads at a time and folded into running per-group sums after each
+// batch, so only one batch's parts exist at a time.  For bf16 io they share
+// one region with the fp32 copies of x and then dy, which are dead once the
+// two chunk_state launches have read them.
+BwdPlan bwd_plan(const Plan& pl, int64_t hb) {
   BwdPlan w;
   const size_t tok = align256(size_t(pl.B) * pl.H * pl.Lp * sizeof(float));
   const size_t st = align256(size_t(pl.B) * pl.H * pl.T * pl.P * pl.N * sizeof(float));
-  const size_t per_head = align256(size_t(pl.B) * pl.L * pl.H * pl.N * sizeof(float));
+  const size_t xs = size_t(pl.B) * pl.L * pl.H * pl.P * sizeof(float);
+  const size_t head_parts = size_t(pl.B) * pl.L * pl.N * sizeof(float);   // one head, one of dB/dC
+  w.hb = (int)hb;
+  const size_t parts = align256(head_parts * size_t(hb));
+  const size_t bs = pl.bf16 ? align256(size_t(pl.B) * pl.L * pl.G * pl.N * sizeof(float)) : 0;
+  const size_t acc = hb < pl.H ? align256(size_t(pl.B) * pl.L * pl.G * pl.N * sizeof(float)) : 0;
   size_t o = 0;
   w.g_off = o; o += tok;
   w.dt_off = o; o += tok;
@@ -310,20 +327,78 @@ BwdPlan bwd_plan(const Plan& pl) {
   w.hc_off = o; o += st;
   w.lam_off = o; o += st;
   w.fin_off = o; o += align256(size_t(pl.B) * pl.H * pl.P * pl.N * sizeof(float));
-  w.dbh_off = o; o += per_head;
-  w.dch_off = o; o += per_head;
   w.dap_off = o; o += align256(size_t(pl.B) * pl.H * sizeof(double));
   w.dbp_off = o; o += align256(size_t(pl.B) * pl.H * sizeof(double));
   w.ddp_off = o; o += align256(size_t(pl.B) * pl.T * pl.H * sizeof(float));
-  const size_t xs = pl.bf16 ? align256(size_t(pl.B) * pl.L * pl.H * pl.P * sizeof(float)) : 0;
-  const size_t bs = pl.bf16 ? align256(size_t(pl.B) * pl.L * pl.G * pl.N * sizeof(float)) : 0;
-  w.x32_off = o; o += xs;
-  w.dy32_off = o; o += xs;
   w.b32_off = o; o += bs;
   w.c32_off = o; o += bs;
+  w.acb_off = o; o += acc;
+  w.acc_off = o; o += acc;
+  w.big_off = o;
+  w.dbh_off = o;
+  w.dch_off = o + parts;
+  o += std::max(pl.bf16 ? align256(xs) : size_t(0), 2 * parts);
   w.bytes = o;
   w.TB = ssd::bwd_block_rows(pl.bf16, (int)pl.Q, pl.P, pl.N);
   return w;
+}
+
+// Batches of at most `cap` heads, balanced: ceil(H / cap) batches of equal
+// size but for the last.
+int64_t balanced_heads(int64_t H, int64_t cap) {
+  const int64_t nbat = (H + cap - 1) / cap;
+  return (H + nbat - 1) / nbat;
+}
+
+// The default plan (ssd_bwd_workspace_size): all heads in one batch when
+// their dB/dC parts take no more room than one fp32 copy of x (2 N <= P);
+// otherwise the head count whose parts fit that room, but at least enough
+// heads for ~1024 workgroups per chunk-kernel launch.
+BwdPlan bwd_default_plan(const Plan& pl) {
+  int64_t hb = pl.H;
+  if (2 * pl.N > pl.P) {
+    const int64_t fit = std::max<int64_t>(1, pl.H * pl.P / (2 * pl.N));
+    const int64_t wg = pl.B * pl.T;
+    hb = balanced_heads(pl.H, std::min<int64_t>(pl.H, std::max<int64_t>(fit, (1024 + wg - 1) / wg)));
+  }
+  return bwd_plan(pl, hb);
+}
+
+// The plan for a caller's workspace.  Among the head batchings whose layout
+// fits `bytes` (nbat equal batches of hb = ceil(H / nbat) heads), the one
+// whose chunk-kernel launches take the fewest rounds of `slots` concurrent
+// workgroups (B T hb workgroups per batch), the fewest batches on a tie; with
+// slots = 0 (unknown), the most heads per batch that fit.  hb = 0 when not
+// even one head per batch fits.
+BwdPlan bwd_plan_for(const Plan& pl, size_t bytes, int64_t slots) {
+  BwdPlan best{};
+  int64_t best_rounds = -1;
+  for (int64_t nbat = 1; nbat <= pl.H; ++nbat) {
+    const int64_t hb = (pl.H + nbat - 1) / nbat;
+    if ((pl.H + hb - 1) / hb != nbat) continue;    // the same batching as a smaller nbat
+    const BwdPlan w = bwd_plan(pl, hb);
+    if (w.bytes > bytes) continue;
+    if (slots <= 0) return w;
+    const int64_t wg = pl.B * pl.T, full = pl.H / hb, rest = pl.H % hb;
+    const int64_t rounds = full * ((wg * hb + slots - 1) / slots) + (wg * rest + slots - 1) / slots;
+    if (best_rounds < 0 || rounds < best_rounds) {
+      best = w;
+      best_rounds = rounds;
+    }
+  }
+  if (best_rounds < 0) {
+    best = bwd_plan(pl, 1);
+    best.hb = 0;
+  }
+  return best;
+}
+
+// The smallest workspace any head batching needs.
+size_t bwd_min_bytes(const Plan& pl) {
+  size_t m = SIZE_MAX;
+  for (int64_t cap = pl.H; cap >= 1; --cap)
+    m = std::min(m, bwd_plan(pl, balanced_heads(pl.H, cap)).bytes);
+  return m;
 }
 
 ssd_status check_supported_bwd(const Plan& pl) {
@@ -850,7 +925,22 @@ ssd_status ssd_bwd_workspace_size(const ssd_problem* prob, size_t* bytes) {
     if (st != SSD_OK) return st;
     st = check_supported_bwd(pl);
     if (st != SSD_OK) return st;
-    *bytes = bwd_plan(pl).bytes;
+    *bytes = bwd_default_plan(pl).bytes;
+    return ok();
+  } catch (...) {
+    return fail(SSD_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+ssd_status ssd_bwd_workspace_min_size(const ssd_problem* prob, size_t* bytes) {
+  try {
+    if (!prob || !bytes) return fail(SSD_ERR_NULL_POINTER, "prob and bytes must not be NULL");
+    Plan pl;
+    ssd_status st = plan_problem(prob, &pl);
+    if (st != SSD_OK) return st;
+    st = check_supported_bwd(pl);
+    if (st != SSD_OK) return st;
+    *bytes = bwd_min_bytes(pl);
     return ok();
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
@@ -879,9 +969,12 @@ ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const v
       if (!aligned16(p)) return fail(SSD_ERR_MISALIGNED, "every tensor pointer must be 16-byte aligned");
     st = check_supported_bwd(pl);
     if (st != SSD_OK) return st;
-    const BwdPlan w = bwd_plan(pl);
-    if (workspace_bytes < w.bytes)
-      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.bytes);
+    if (bwd_plan_for(pl, workspace_bytes, 0).hb == 0)
+      return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs at least %zu",
+                  workspace_bytes, bwd_min_bytes(pl));
+    // every argument checked: the device's workgroup slots pick the batching
+    const BwdPlan w =
+        bwd_plan_for(pl, workspace_bytes, ssd::bwd_chunk_slots(pl.bf16, pl.P, pl.N));
     char* ws = static_cast<char*>(workspace);
     float* Gw = reinterpret_cast<float*>(ws + w.g_off);
     float* dtw = reinterpret_cast<float*>(ws + w.dt_off);
@@ -894,25 +987,29 @@ ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const v
     float* fin = reinterpret_cast<float*>(ws + w.fin_off);
     float* dBh = reinterpret_cast<float*>(ws + w.dbh_off);
     float* dCh = reinterpret_cast<float*>(ws + w.dch_off);
+    float* acB = reinterpret_cast<float*>(ws + w.acb_off);
+    float* acC = reinterpret_cast<float*>(ws + w.acc_off);
     double* dAp = reinterpret_cast<double*>(ws + w.dap_off);
     double* dbp = reinterpret_cast<double*>(ws + w.dbp_off);
     float* dDp = reinterpret_cast<float*>(ws + w.ddp_off);
     const ssd::DtXform* xfp = dtx ? &xf : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const ssd_config cfg = default_config(pl);
-    // fp32 operands of the state stages (the io tensors themselves for fp32 io)
+    // fp32 operands of the state stages (the io tensors themselves for fp32
+    // io); for bf16 io, x and then dy are widened into one region, which the
+    // dB/dC parts reuse once the two chunk_state launches have read it
+    const int64_t nx = pl.B * pl.L * pl.H * pl.P;
     const void* x32 = x;
     const void* dy32 = dy;
     const void* B32 = B;
     const void* C32 = C;
     if (pl.bf16) {
-      const int64_t nx = pl.B * pl.L * pl.H * pl.P, nb = pl.B * pl.L * pl.G * pl.N;
-      x32 = ws + w.x32_off;
-      dy32 = ws + w.dy32_off;
+      const int64_t nb = pl.B * pl.L * pl.G * pl.N;
+      x32 = ws + w.big_off;
+      dy32 = ws + w.big_off;
       B32 = ws + w.b32_off;
       C32 = ws + w.c32_off;
       hipError_t e = ssd::launch_bwd_widen(x, (float*)x32, nx, s);
-      if (e == hipSuccess) e = ssd::launch_bwd_widen(dy, (float*)dy32, nx, s);
       if (e == hipSuccess) e = ssd::launch_bwd_widen(B, (float*)B32, nb, s);
       if (e == hipSuccess) e = ssd::launch_bwd_widen(C, (float*)C32, nb, s);
       if (e != hipSuccess) return hip_status(e, "bwd_widen launch");
@@ -927,6 +1024,10 @@ ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const v
     e = ssd::launch_state_pass(0, Hc, Gw, init_state, dfinal ? fin : nullptr, pl.B, pl.H,
                                pl.P, pl.N, (int)pl.Q, pl.T, pl.Lp, 0, 0, s);
     if (e != hipSuccess) return hip_status(e, "state_pass launch");
+    if (pl.bf16) {
+      e = ssd::launch_bwd_widen(dy, (float*)dy32, nx, s);     // over the dead x copy
+      if (e != hipSuccess) return hip_status(e, "bwd_widen launch");
+    }
     // gradients of the chunk-boundary states: the same two stages run backwards
     e = ssd::launch_bwd_prep(Gw, w2, Gz, pl.B, pl.H, pl.L, pl.Lp, s);
     if (e != hipSuccess) return hip_status(e, "bwd_prep launch");
@@ -936,13 +1037,20 @@ ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const v
     e = ssd::launch_state_pass(0, Lam, Gw, dfinal, dinit, pl.B, pl.H, pl.P, pl.N, (int)pl.Q,
                                pl.T, pl.Lp, 0, 1, s);
     if (e != hipSuccess) return hip_status(e, "state_pass (reverse) launch");
-    e = ssd::launch_bwd_chunks(pl.bf16, w.TB, x, B, C, dy, Gw, dtw, Hc, Lam, D, dx, Pb, Qb, dBh,
-                               dCh, dDp, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G, (int)pl.Q, pl.T,
-                               pl.Lp, s);
-    if (e != hipSuccess) return hip_status(e, "bwd chunk kernels launch");
-    e = ssd::launch_bwd_finish(pl.bf16, Pb, Qb, dtw, dt, A, dfinal, fin, xfp, ddt, dAp, dbp, dBh,
-                               dCh, dDp, dB, dC, dA, dD, ddt_bias, pl.B, pl.L, pl.H, pl.P, pl.N,
-                               pl.G, pl.T, pl.Lp, s);
+    // per-chunk gradients, hb heads at a time, each batch's dB/dC parts folded
+    // into the per-group sums before the next batch overwrites them
+    for (int h0 = 0; h0 < pl.H; h0 += w.hb) {
+      const int nb = (int)std::min<int64_t>(w.hb, pl.H - h0);
+      e = ssd::launch_bwd_chunks(pl.bf16, w.TB, x, B, C, dy, Gw, dtw, Hc, Lam, D, dx, Pb, Qb,
+                                 dBh, dCh, dDp, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G, (int)pl.Q,
+                                 pl.T, pl.Lp, h0, nb, w.hb, s);
+      if (e != hipSuccess) return hip_status(e, "bwd chunk kernels launch");
+      e = ssd::launch_bwd_group_sum(pl.bf16, dBh, dCh, acB, acC, dB, dC, pl.B, pl.L, pl.H, pl.N,
+                                    pl.G, h0, nb, w.hb, s);
+      if (e != hipSuccess) return hip_status(e, "bwd group sum launch");
+    }
+    e = ssd::launch_bwd_finish(Pb, Qb, dtw, dt, A, dfinal, fin, xfp, ddt, dAp, dbp, dDp, dA, dD,
+                               ddt_bias, pl.B, pl.L, pl.H, pl.P, pl.N, pl.T, pl.Lp, s);
     return hip_status(e, "bwd finish launch");
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");

@@ -9,6 +9,7 @@ import subprocess
 
 import pytest
 
+from bwd_layout import balanced, bwd_layout
 import state_space_sequence_03_amd as lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -38,7 +39,8 @@ def test_exports_every_declared_symbol(so):
                           "ssd_fwd_states", "ssd_compute_out", "ssd_fwd_ex",
                           "ssd_chunk_cumsum_ex", "ssd_step", "ssd_fwd_states_ex",
                           "ssd_default_config", "ssd_fwd_config", "ssd_tune",
-                          "ssd_bwd_workspace_size", "ssd_bwd", "ssd_fwd_config_workspace_size",
+                          "ssd_bwd_workspace_size", "ssd_bwd_workspace_min_size", "ssd_bwd",
+                          "ssd_fwd_config_workspace_size",
                           "ssd_fwd_status", "ssd_fwd_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib.lib_path()], capture_output=True,
                          text=True, check=True).stdout
@@ -485,10 +487,15 @@ def call_bwd(prob, xf=None, ws_bytes=0, **kw):
                       a["dB"], a["dC"], a["dD"], a["dinit"], a["dbias"], a["ws"], ws_bytes, None)
 
 
-def bwd_ws(prob):
+def bwd_ws(prob, fn="ssd_bwd_workspace_size"):
     n = ctypes.c_size_t(0)
-    st = lib.load_library().ssd_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(n))
+    st = getattr(lib.load_library(), fn)(None if prob is None else ctypes.byref(prob),
+                                         ctypes.byref(n))
     return st, n.value
+
+
+def bwd_ws_min(prob):
+    return bwd_ws(prob, "ssd_bwd_workspace_min_size")
 
 
 def test_bwd_validation_order(so):
@@ -507,9 +514,12 @@ def test_bwd_validation_order(so):
     assert call_bwd(P(headdim=72)) == UNSUP
     assert call_bwd(P(dstate=272)) == UNSUP
     assert call_bwd(P(headdim=72), ws=FAKE + 8) == MISAL      # alignment before limits
-    st, need = bwd_ws(P())
+    st, need = bwd_ws_min(P())
     assert st == OK and need > 0
     assert call_bwd(P(), ws_bytes=need - 1) == WS
+    assert call_bwd(P(nheads=6, ngroups=4), ws_bytes=0) == SHAPE
+    assert bwd_ws_min(None)[0] == NULLP
+    assert bwd_ws_min(P(headdim=272))[0] == UNSUP
 
 
 def test_bwd_limits(so):
@@ -524,19 +534,28 @@ def test_bwd_limits(so):
 
 
 def test_bwd_workspace_formula(so):
-    # token rows (6 fp32 [batch, H, T*Q] arrays), two fp32 state sets, the
-    # final state, per-head dB/dC parts, the scalar parts and (bf16 io) fp32
-    # copies of x, dy, B and C, each 256-aligned
-    a = lambda v: (v + 255) // 256 * 256
-    for pd in (dict(), dict(io_dtype=0, seqlen=77, chunk_size=64, ngroups=1)):
+    # default: all heads in one batch when 2 dstate <= headdim, else the heads
+    # whose parts fit one fp32 copy of x, at least 1024 / (batch * chunks),
+    # in balanced batches; minimum: the smallest layout over the head counts
+    cases = (dict(), dict(io_dtype=0, seqlen=77, chunk_size=64, ngroups=1),
+             dict(headdim=128, dstate=64), dict(batch=2, seqlen=8192, nheads=80, headdim=64,
+                                                dstate=128, ngroups=1, chunk_size=256),
+             dict(batch=8, seqlen=4096, nheads=64, headdim=64, dstate=256, ngroups=8,
+                  chunk_size=128))
+    for pd in cases:
         p = P(**pd)
-        Bt, L, H, Pd, N, Q = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.chunk_size
-        T = -(-L // Q)
-        G = p.ngroups
-        wide = (2 * a(Bt * L * H * Pd * 4) + 2 * a(Bt * L * G * N * 4)) if p.io_dtype == 1 else 0
-        want = (6 * a(Bt * H * T * Q * 4) + 2 * a(Bt * H * T * Pd * N * 4) + a(Bt * H * Pd * N * 4) +
-                2 * a(Bt * L * H * N * 4) + 2 * a(Bt * H * 8) + a(Bt * T * H * 4) + wide)
-        assert bwd_ws(p) == (OK, want)
+        H, N, Pd = p.nheads, p.dstate, p.headdim
+        T = -(-p.seqlen // p.chunk_size)
+        hb = H
+        if 2 * N > Pd:
+            fit = max(1, H * Pd // (2 * N))
+            hb = balanced(H, min(H, max(fit, -(-1024 // (p.batch * T)))))
+        assert bwd_ws(p) == (OK, bwd_layout(p, hb)), pd
+        want_min = min(bwd_layout(p, balanced(H, c)) for c in range(1, H + 1))
+        assert bwd_ws_min(p) == (OK, want_min), pd
+    # the 2.7B layer shape: 4 batches of 20 heads, under 1 GB
+    p = P(**cases[3])
+    assert bwd_ws(p)[1] == bwd_layout(p, 20) < 10 ** 9
 
 
 @pytest.mark.skipif(not os.path.exists(f"{LLVM}/llvm-objdump"), reason="ROCm LLVM tools not installed")

@@ -28,6 +28,7 @@ import torch
 
 import oracle
 import ssd_synth
+from bwd_layout import balanced, bwd_layout
 from parity_util import errors
 
 pytestmark = pytest.mark.gpu
@@ -149,6 +150,66 @@ def test_bwd_repeatable_and_workspace_reuse():
     for k in a:
         if a[k] is not None:
             assert torch.equal(a[k], b[k]), k
+
+
+def bwd_outputs(p, inp, grads, ws_bytes):
+    prob = lib.make_problem(p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups,
+                            p.chunk_size, lib.SSD_BF16 if p.io_dtype == "bf16" else lib.SSD_F32)
+    if ws_bytes is None:
+        ws_bytes = lib.ssd_bwd_workspace_size(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws.fill_(0x7f)
+    out = lib.ssd_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], p.chunk_size,
+                      inp["init_state"], grads["dy"], grads["dfinal"], want_ddt_bias=True,
+                      workspace=ws)
+    torch.cuda.synchronize()
+    return prob, out
+
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_bwd_head_batches_bitwise_equal(io):
+    # dB and dC are summed over each group's heads in ascending head order
+    # whatever the batches of heads the workspace allows, so every output is
+    # bitwise the same for one head per batch (the minimum workspace), two
+    # heads per batch (batches that cut the groups of three heads: a group's
+    # first, middle and last heads in different batches), the default, and
+    # all heads in one batch
+    p = ssd_synth.Problem(batch=2, seqlen=300, nheads=6, headdim=32, dstate=64, ngroups=2,
+                          chunk_size=64, io_dtype=io, init_std=0.1)
+    inp = {k: (None if v is None else v.cuda()) for k, v in ssd_synth.make_inputs(p, 53).items()}
+    grads = {k: v.cuda() for k, v in ssd_synth.make_grads(p, 53).items()}
+    prob, ref = bwd_outputs(p, inp, grads, None)
+    big = bwd_layout(prob, p.nheads)
+    sizes = {"min": lib.ssd_bwd_workspace_min_size(prob), "hb2": bwd_layout(prob, 2),
+             "hb1": bwd_layout(prob, 1), "one_batch": big}
+    assert sizes["min"] == min(bwd_layout(prob, balanced(p.nheads, c)) for c in range(1, 7))
+    for name, n in sizes.items():
+        _, got = bwd_outputs(p, inp, grads, n)
+        for k in ref:
+            if ref[k] is not None:
+                assert torch.equal(got[k], ref[k]), (name, k)
+    cpu = {k: (None if v is None else v.cpu()) for k, v in inp.items()}
+    ref64 = oracle.recurrence_bwd(cpu["x"], cpu["dt"], cpu["A"], cpu["B"], cpu["C"], cpu["D"],
+                                  cpu["init_state"], grads["dy"].cpu(), grads["dfinal"].cpu())
+    for k in ("dB", "dC"):
+        check(ref[k], ref64[k], io, k)
+
+
+def test_bwd_2p7b_head_batches_equal_one_batch():
+    # at the 2.7B layer shape the default workspace holds the dB/dC parts of
+    # 20 of the 80 heads (four batches); a workspace for all 80 at once must
+    # give bitwise the same gradients
+    p = ssd_synth.CONFIGS["mamba2_2p7b"]
+    inp = {k: (None if v is None else v.cuda()) for k, v in ssd_synth.make_inputs(p, 6).items()}
+    grads = {k: v.cuda() for k, v in ssd_synth.make_grads(p, 6).items()}
+    prob, ref = bwd_outputs(p, inp, grads, None)
+    assert lib.ssd_bwd_workspace_size(prob) == bwd_layout(prob, 20) < 10 ** 9
+    _, got = bwd_outputs(p, inp, grads, bwd_layout(prob, p.nheads))
+    for k in ref:
+        if ref[k] is not None:
+            assert torch.equal(got[k], ref[k]), k
+    del inp, grads, ref, got
+    torch.cuda.empty_cache()
 
 
 def test_bwd_2p7b_sampled_heads():
