@@ -2,8 +2,9 @@
 """Throughput of the Mamba-2 chunked SSD forward pass (libssd) on one MI355X.
 
 One step = one ssd_fwd through the C ABI: the whole hot path over one batch of
-synthetic input (the single-pass fused kernel where it is built, else
-chunk_cumsum -> chunk_state -> state_pass -> compute_out).  Inputs are resident
+synthetic input with the default tile choices: chunk_state (with the
+within-chunk running sums) -> state_pass -> stage 3 (the resident-tile kernel
+where it is built).  Inputs are resident
 in HBM before timing starts.  The headline is the median of the timed steps
 with the 256 MB last-level cache flushed before each by reading a 512 MiB
 buffer (outside the events: the cache then holds clean, unrelated lines);
@@ -455,6 +456,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one captured HIP graph of the whole pass")
     ap.add_argument("--mode", choices=("prefill", "decode", "bwd"), default="prefill")
+    ap.add_argument("--cumsum-heads", type=int, choices=(0, 4, 16), default=None,
+                    help="ssd_config.cumsum_heads (0: running sums inside chunk_state; "
+                         "default: the library's choice)")
     ap.add_argument("--bwd-workspace-bytes", type=int, default=0,
                     help="--mode bwd: workspace size to give ssd_bwd (0: its default)")
     ap.add_argument("--tune", action="store_true",
@@ -523,6 +527,8 @@ def main():
     cfg = ssd.ssd_default_config(pr)
     if args.kernels != "default":
         cfg["fused"] = int(args.kernels == "fused")
+    if args.cumsum_heads is not None:
+        cfg["cumsum_heads"] = args.cumsum_heads
     fused = bool(cfg["fused"])
     ws = torch.empty(ssd.ssd_fwd_workspace_size(pr), dtype=torch.uint8, device=dev)
     y = torch.empty_like(d["x"])
@@ -627,7 +633,10 @@ def main():
                    "ngroups": prob.ngroups, "chunk_size": Q,
                    "init_state": prob.init_std is not None, "accumulate": "fp32",
                    "kernels": "fused single pass" if fused else
-                              "staged (4 kernels; stage 3 %s)" % (
+                              "staged (%d kernels; %s; stage 3 %s)" % (
+                                  3 if cfg["cumsum_heads"] == 0 else 4,
+                                  "running sums inside chunk_state" if cfg["cumsum_heads"] == 0
+                                  else "running sums by chunk_cumsum",
                                   "with the interaction tile resident across heads"
                                   if cfg.get("out_resident") else "per head pair"),
                    "dt": "raw, bias + softplus in the first stage" if args.raw_dt else "prepared"},

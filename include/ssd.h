@@ -158,7 +158,11 @@ typedef struct {
  *                  of heads per group), 0 = the staged kernels; the four
  *                  fields below are checked in both cases and used by the
  *                  staged kernels only;
- *   cumsum_heads : heads per chunk_cumsum workgroup, 4 or 16;
+ *   cumsum_heads : 0 = the running sums G and the prepared step sizes are
+ *                  formed inside the chunk_state kernel (no launch of their
+ *                  own); 4 or 16 = a separate chunk_cumsum launch with that
+ *                  many heads per workgroup (the values are bitwise the same
+ *                  either way);
  *   state_heads  : heads per chunk_state workgroup (they share the chunk's B
  *                  rows), 1, 2 or 4, dividing the heads of a group;
  *   out_heads    : heads per compute_out workgroup (they share the raw tile

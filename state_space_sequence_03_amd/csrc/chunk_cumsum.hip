@@ -94,32 +94,20 @@ chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
     const int h = h0 + hh;
     if (h >= H) break;
     const float a2 = A[h] * kLog2e;
-    float part[TPL], raw[TPL];
-    float run = 0.0f;
+    float gs[TPL], raw[TPL];
 #pragma unroll
-    for (int e = 0; e < TPL; ++e) {
-      raw[e] = lane < LANES ? tile[hh][first + e] : 0.0f;
-      run += raw[e] * a2;
-      part[e] = run;
-    }
-    // inclusive scan of lane totals across the wave
-    float incl = run;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const float o = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += o;
-    }
-    const float carry = incl - run;
+    for (int e = 0; e < TPL; ++e) raw[e] = lane < LANES ? tile[hh][first + e] : 0.0f;
+    wave_chunk_scan<TPL>(raw, a2, gs, lane);
     const int64_t row = ((int64_t)b * H + h) * ld + t0 + first;
     if (lane < LANES && vec_ok && t0 + first + TPL <= Lw) {
       vec_t g, d;
       if constexpr (TPL == 1) {
-        g = carry + part[0];
+        g = gs[0];
         d = raw[0];
       } else {
 #pragma unroll
         for (int e = 0; e < TPL; ++e) {
-          g[e] = carry + part[e];
+          g[e] = gs[e];
           d[e] = raw[e];
         }
       }
@@ -130,7 +118,7 @@ chunk_cumsum_kernel(const float* __restrict__ dt, const float* __restrict__ A,
 #pragma unroll
       for (int e = 0; e < TPL; ++e)
         if (t0 + first + e < Lw) {
-          G[row + e] = carry + part[e];
+          G[row + e] = gs[e];
           dtT[row + e] = raw[e];
         }
     }

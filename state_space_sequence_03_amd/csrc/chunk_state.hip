@@ -118,11 +118,29 @@ __device__ __forceinline__ vec16 scale16<float>(vec16 v, float w) {
   return __builtin_bit_cast(vec16, f);
 }
 
+// Running sums inside chunk_state (stage 1 folded into stage 2a).  With `fold`
+// set the kernel reads the raw step sizes dt [batch, seqlen, nheads] instead
+// of G and dt' rows: its KH heads' dt over the chunk arrive by 4-byte direct
+// loads straight into the rows of the G / w staging (one load instruction per
+// 64 tokens of one head), ahead of the ring's first slots; waves 0..KH-1 then
+// form each head's prepared dt' and running sum G with chunk_cumsum's own
+// scan (wave_chunk_scan: bitwise the same values), and the workgroups of p
+// slice 0 and n slice 0 store both rows for the later stages, which read them
+// as they would read chunk_cumsum's.
+struct CsFold {
+  const float* dt;    // raw dt [batch, seqlen, nheads]
+  const float* A;     // [nheads]
+  DtXform xf;         // the step-size preparation, used when xf_on
+  int xf_on;
+  int on;             // 0: G and dt' rows are inputs (Gw, dtw)
+};
+
 template <typename T, int KH, int NW>
 __global__ void __launch_bounds__((CsCfg<T, KH, NW>::THREADS))
-chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ Gw,
-                   const float* __restrict__ dtw, T* __restrict__ S, int64_t L, int H, int P, int N,
-                   int G, int Q, int T_, int64_t ldw, int nbc, int PB, int NSL, int frag_major) {
+chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __restrict__ Gw,
+                   float* __restrict__ dtw, T* __restrict__ S, int64_t L, int H, int P, int N,
+                   int G, int Q, int T_, int64_t ldw, int nbc, int PB, int NSL, int frag_major,
+                   CsFold fold) {
   typedef CsCfg<T, KH, NW> C;
   typedef typename FragOf<T>::type frag_t;
   constexpr int V = C::V;
@@ -152,6 +170,14 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
   const T* xc = x + ((int64_t)b * L + t0) * xstride + (int64_t)h0 * P;
+  // the scanning waves' A and bias, read before any load into LDS (whose asm
+  // clobbers memory) so that they stay scalar loads and no wait for them
+  // drains the ring's loads
+  float a2f = 0.0f, bias_f = 0.0f;
+  if (fold.on && wave < KH) {
+    a2f = fold.A[h0 + wave] * kLog2e;
+    if (fold.xf_on && fold.xf.bias) bias_f = fold.xf.bias[h0 + wave];
+  }
   const T* Bc = Bm + ((int64_t)b * L + t0) * bstride + (int64_t)g * N;
 
   // Loads of slot k into ring slot k % NSLOT.  Every wave issues exactly LPG
@@ -218,8 +244,31 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
     }
   };
 
-  // ---- prologue: G and dt rows of the KH heads, then the first slots ----------
-  {
+  // ---- prologue: G and dt rows of the KH heads (or raw dt), then the first slots
+  // raw dt with fold set: with 4 heads per workgroup, a token's 4 values are
+  // 16 contiguous bytes, loaded whole as [token][head] into the ring slot
+  // that the prologue leaves empty (64 tokens per instruction); with fewer
+  // heads, 64 tokens of one head per 4-byte gather into its dt' row.  Rows
+  // past the sequence end read its last token (the scan zeroes them).
+  const float* dtst = reinterpret_cast<const float*>(ring + (C::NSLOT - 1) * C::BYTES);
+  static_assert(KH != 4 || C::BYTES >= 4 * 256 * 4, "dt staging fits a ring slot");
+  if (fold.on) {
+    if constexpr (KH == 4) {
+      for (int m = wave; m * 64 < Q; m += C::NWV) {
+        const int j = m * 64 + lane;
+        const int64_t tok = min(t0 + j, L - 1);
+        if (j < Q) dma16(fold.dt + ((int64_t)b * L + tok) * H + h0, dtst + 4 * (j - lane));
+      }
+    } else {
+      const int nins = KH * ((Q + 63) / 64);
+      for (int m = wave; m < nins; m += C::NWV) {
+        const int hh = m / ((Q + 63) / 64), j = (m % ((Q + 63) / 64)) * 64 + lane;
+        const int64_t tok = min(t0 + j, L - 1);
+        if (j < Q) dma4(fold.dt + ((int64_t)b * L + tok) * H + h0 + hh,
+                        reinterpret_cast<unsigned char*>(gd + hh * 2 * Q + Q + j - lane));
+      }
+    }
+  } else {
     const int nchunk = KH * Q / 2;                 // 16-byte chunks of G + dt
     const int ngb = (nchunk + 63) / 64;
     const int ginst = (ngb + C::NWV - 1) / C::NWV;
@@ -236,6 +285,94 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
   for (int k = 0; k < npro; ++k) issue(k);
   wait_groups<C::LPG>(npro);                       // this wave's G/dt loads have landed
   __syncthreads();
+  // vector stores this wave issues after the prologue's slots (the G and dt'
+  // rows, with fold set): the first waits of the slot loop allow for them
+  int late_stores = 0;
+  if (fold.on) {
+    if (wave < KH) {
+      const int hh = wave, h = h0 + hh;
+      float* row = gd + hh * 2 * Q;
+      // token j's raw dt of this head, from where the prologue put it
+      auto raw_dt = [&](int j) { return KH == 4 ? dtst[4 * j + hh] : row[Q + j]; };
+      const float a2 = a2f;
+      const bool writer = pb == 0 && nsl == 0;
+      // the two rows take at least one store instruction each (the compiler
+      // may merge a lane's scalar stores), so counting two never lets a wait
+      // of the slot loop pass before its loads have landed
+      late_stores = writer ? 2 : 0;
+      const int64_t grow = (int64_t)(b * H + h) * ldw + t0;
+      if (Q >= kWave) {
+        constexpr int TPL = 4;                     // Q = 256
+        if (Q == 256) {
+          float raw[TPL], g4[TPL];
+          const int first = lane * TPL;
+#pragma unroll
+          for (int e = 0; e < TPL; ++e) {
+            const float v = raw_dt(first + e);
+            raw[e] = t0 + first + e < L ? (fold.xf_on ? dt_prepare_b(fold.xf, v, bias_f) : v) : 0.0f;
+          }
+          wave_chunk_scan<TPL>(raw, a2, g4, lane);
+          *reinterpret_cast<floatx4*>(row + first) = floatx4{g4[0], g4[1], g4[2], g4[3]};
+          *reinterpret_cast<floatx4*>(row + Q + first) = floatx4{raw[0], raw[1], raw[2], raw[3]};
+          if (writer) {
+            *reinterpret_cast<floatx4*>(Gw + grow + first) = floatx4{g4[0], g4[1], g4[2], g4[3]};
+            *reinterpret_cast<floatx4*>(dtw + grow + first) = floatx4{raw[0], raw[1], raw[2], raw[3]};
+          }
+        } else {
+          // Q = 64 or 128: 1 or 2 tokens per lane
+          const int tpl = Q / kWave;
+          float raw2[2] = {0.0f, 0.0f}, g2[2];
+          const int first = lane * tpl;
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            if (e < tpl) {
+              const float v = raw_dt(first + e);
+              raw2[e] = t0 + first + e < L ? (fold.xf_on ? dt_prepare_b(fold.xf, v, bias_f) : v) : 0.0f;
+            }
+          if (tpl == 2) {
+            wave_chunk_scan<2>(raw2, a2, g2, lane);
+          } else {
+            float r1[1] = {raw2[0]}, o1[1];
+            wave_chunk_scan<1>(r1, a2, o1, lane);
+            g2[0] = o1[0];
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            if (e < tpl) {
+              row[first + e] = g2[e];
+              row[Q + first + e] = raw2[e];
+            }
+          if (writer) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              if (e < tpl) {
+                Gw[grow + first + e] = g2[e];
+                dtw[grow + first + e] = raw2[e];
+              }
+          }
+        }
+      } else {
+        // Q = 32: lanes 0..31 hold one token each
+        float r1[1] = {0.0f}, g1[1];
+        if (lane < Q) {
+          const float v = raw_dt(lane);
+          r1[0] = t0 + lane < L ? (fold.xf_on ? dt_prepare_b(fold.xf, v, bias_f) : v) : 0.0f;
+        }
+        wave_chunk_scan<1>(r1, a2, g1, lane);
+        if (lane < Q) {
+          row[lane] = g1[0];
+          row[Q + lane] = r1[0];
+        }
+        if (writer) {
+          if (lane < Q) {
+            Gw[grow + lane] = g1[0];
+            dtw[grow + lane] = r1[0];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
   // w_j = exp2(G_last - G_j) dt_j in place of dt_j; padding tokens have dt = 0
   // and G flat past the sequence end, so they get w = 0
   for (int idx = tid; idx < KH * Q; idx += C::THREADS) {
@@ -255,7 +392,11 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const floa
     for (int pt = 0; pt < 4; ++pt) acc[nt][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   for (int k = 0; k < ns; ++k) {
-    wait_groups<C::LPG>(min(C::NSLOT - 2, ns - 1 - k));   // this wave's loads of slot k
+    // this wave's loads of slot k
+    if (k < npro && late_stores)
+      wait_groups_plus<C::LPG, 2>(min(C::NSLOT - 2, ns - 1 - k));
+    else
+      wait_groups<C::LPG>(min(C::NSLOT - 2, ns - 1 - k));
     unsigned char* sl = ring + (k % C::NSLOT) * C::BYTES;
     // scale the x rows this wave loaded by their token's weight, in place
 #pragma unroll
@@ -337,9 +478,9 @@ int chunk_state_default_kh(int64_t H, int64_t G) {
 }
 
 template <typename T, int KH, int NW>
-static hipError_t launch_cs(const void* x, const void* Bm, const float* Gw, const float* dtw,
-                            void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                            int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
+static hipError_t launch_cs(const void* x, const void* Bm, float* Gw, float* dtw, void* S,
+                            int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                            int Q, int64_t T_, int64_t ldw, int frag_major, const CsFold& fold,
                             hipStream_t stream) {
   typedef CsCfg<T, KH, NW> C;
   const int PB = (int)((P + kCsP - 1) / kCsP);
@@ -353,16 +494,16 @@ static hipError_t launch_cs(const void* x, const void* Bm, const float* Gw, cons
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(C::THREADS), lds, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm), Gw, dtw,
                      static_cast<T*>(S), L, (int)H, (int)P, (int)N, (int)G, Q, (int)T_, ldw,
-                     (int)nbc, PB, NSL, frag_major);
+                     (int)nbc, PB, NSL, frag_major, fold);
   return hipGetLastError();
 }
 
 template <typename T, int KH>
-static hipError_t launch_cs_nw(const void* x, const void* Bm, const float* Gw, const float* dtw,
-                               void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+static hipError_t launch_cs_nw(const void* x, const void* Bm, float* Gw, float* dtw, void* S,
+                               int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                                int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
-                               hipStream_t stream) {
-#define SSD_CS_ARGS x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, stream
+                               const CsFold& fold, hipStream_t stream) {
+#define SSD_CS_ARGS x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, fold, stream
   switch (state_nw(N)) {
     case 32: return launch_cs<T, KH, 32>(SSD_CS_ARGS);
     case 64: return launch_cs<T, KH, 64>(SSD_CS_ARGS);
@@ -372,11 +513,11 @@ static hipError_t launch_cs_nw(const void* x, const void* Bm, const float* Gw, c
 }
 
 template <typename T>
-static hipError_t launch_cs_t(int kh, const void* x, const void* Bm, const float* Gw,
-                              const float* dtw, void* S, int64_t batch, int64_t L, int64_t H,
-                              int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                              int frag_major, hipStream_t stream) {
-#define SSD_CS_ARGS x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, stream
+static hipError_t launch_cs_t(int kh, const void* x, const void* Bm, float* Gw, float* dtw,
+                              void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                              int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
+                              const CsFold& fold, hipStream_t stream) {
+#define SSD_CS_ARGS x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, fold, stream
   switch (kh) {
     case 4: return launch_cs_nw<T, 4>(SSD_CS_ARGS);
     case 2: return launch_cs_nw<T, 2>(SSD_CS_ARGS);
@@ -386,16 +527,23 @@ static hipError_t launch_cs_t(int kh, const void* x, const void* Bm, const float
 }
 
 // kh: heads per workgroup (1, 2 or 4, dividing the heads of a group; checked
-// by the caller).
-hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, const float* Gw,
-                              const float* dtw, void* S, int64_t batch, int64_t L, int64_t H,
-                              int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                              int frag_major, int kh, hipStream_t stream) {
+// by the caller).  dt_raw == NULL: Gw and dtw hold the running sums and
+// prepared step sizes (chunk_cumsum's rows, or the backward pass's weights);
+// otherwise the kernel forms them from dt_raw, A and the optional
+// preparation xf and writes them to Gw and dtw (rows of ldw floats, every
+// chunk's Q positions).
+hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, float* Gw, float* dtw,
+                              void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                              int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major, int kh,
+                              const float* dt_raw, const float* A, const DtXform* xf,
+                              hipStream_t stream) {
+  CsFold fold{dt_raw, A, xf ? *xf : DtXform{nullptr, 0, 0.0f, 0.0f}, xf ? 1 : 0,
+              dt_raw ? 1 : 0};
   if (io_bf16)
     return launch_cs_t<bf16>(kh, x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major,
-                             stream);
+                             fold, stream);
   return launch_cs_t<float>(kh, x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major,
-                            stream);
+                            fold, stream);
 }
 
 }  // namespace ssd

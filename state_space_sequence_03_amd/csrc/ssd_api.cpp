@@ -27,10 +27,11 @@ hipError_t launch_step(int io_bf16, float* state, const void* x, const float* dt
                        const void* Bm, const void* Cm, const float* D, void* y,
                        const DtXform* xf, int64_t batch, int64_t L, int64_t H, int64_t P,
                        int64_t N, int64_t G, hipStream_t stream);
-hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, const float* Gw,
-                              const float* dtw, void* S, int64_t batch, int64_t L, int64_t H,
-                              int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                              int frag_major, int kh, hipStream_t stream);
+hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, float* Gw, float* dtw,
+                              void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                              int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major, int kh,
+                              const float* dt_raw, const float* A, const DtXform* xf,
+                              hipStream_t stream);
 hipError_t launch_state_pass(int io_bf16, void* S, const float* Gw, const float* init_state,
                              float* final_state, int64_t batch, int64_t H, int64_t P, int64_t N,
                              int Q, int64_t T_, int64_t ldw, int frag_major, int reverse,
@@ -209,9 +210,14 @@ ssd_status check_dt_transform(const ssd_dt_transform* dtx, ssd::DtXform* xf) {
 
 // The kernels' tile choices (ssd_config): the static table, and the checks a
 // caller's choice must pass.
+// Heads per workgroup of the stand-alone running-sum kernel.
+constexpr int kCumsumHeads = 4;
+
 ssd_config default_config(const Plan& pl) {
   ssd_config c;
-  c.cumsum_heads = 4;
+  // the running sums inside chunk_state: no launch of their own, and no
+  // round trip of the raw step sizes through a kernel boundary
+  c.cumsum_heads = 0;
   c.state_heads = ssd::chunk_state_default_kh(pl.H, pl.G);
   c.out_heads = ssd::compute_out_default_kh(pl.bf16, pl.H, pl.G, pl.N);
   // the staged kernels: at the shapes the fused kernel is built for they
@@ -238,8 +244,9 @@ ssd_status check_config(const Plan& pl, const ssd_config& c) {
     return fail(SSD_ERR_BAD_VALUE,
                 "config: out_resident is built for bf16 io, headdim 64, dstate <= 128, "
                 "chunk_size 256 and nheads * headdim <= 2^22");
-  if (c.cumsum_heads != 4 && c.cumsum_heads != 16)
-    return fail(SSD_ERR_BAD_VALUE, "config: cumsum_heads must be 4 or 16 (got %d)", c.cumsum_heads);
+  if (c.cumsum_heads != 0 && c.cumsum_heads != 4 && c.cumsum_heads != 16)
+    return fail(SSD_ERR_BAD_VALUE, "config: cumsum_heads must be 0, 4 or 16 (got %d)",
+                c.cumsum_heads);
   const int64_t hg = pl.H / pl.G;
   if (!(c.state_heads == 1 || c.state_heads == 2 || c.state_heads == 4) || hg % c.state_heads != 0)
     return fail(SSD_ERR_BAD_VALUE,
@@ -568,8 +575,8 @@ ssd_status ssd_chunk_cumsum_ex(const ssd_problem* prob, const ssd_dt_transform* 
     if (st != SSD_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(ssd::launch_chunk_cumsum(dt, A, G_out, dt_out, pl.B, pl.L, pl.H, (int)pl.Qreq,
-                                               pl.L, pl.L, dtx ? &xf : nullptr,
-                                               default_config(pl).cumsum_heads, s),
+                                               pl.L, pl.L, dtx ? &xf : nullptr, kCumsumHeads,
+                                               s),
                       "chunk_cumsum launch");
   } catch (...) {
     return fail(SSD_ERR_INTERNAL, "unexpected exception");
@@ -589,14 +596,21 @@ static ssd_status run_states(const Plan& pl, const ssd_config& cfg, const void* 
   float* Gw = reinterpret_cast<float*>(ws + pl.g_off);
   float* dtw = reinterpret_cast<float*>(ws + pl.dt_off);
   void* Hc = chunk_states ? chunk_states : static_cast<void*>(ws + pl.hc_off);
-  hipError_t e = ssd::launch_chunk_cumsum(dt, A, Gw, dtw, pl.B, pl.L, pl.H, (int)pl.Q, pl.Lp,
-                                          pl.Lp, xf, cfg.cumsum_heads, s);
-  if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
+  // the running sums: a chunk_cumsum launch, or (cumsum_heads = 0) inside
+  // chunk_state, which then writes the same rows
+  const bool fold = cfg.cumsum_heads == 0;
+  hipError_t e = hipSuccess;
+  if (!fold) {
+    e = ssd::launch_chunk_cumsum(dt, A, Gw, dtw, pl.B, pl.L, pl.H, (int)pl.Q, pl.Lp, pl.Lp, xf,
+                                 cfg.cumsum_heads, s);
+    if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
+  }
   // each chunk's own contribution S_c into the state buffer, then the
   // recurrence turns it, in place, into the chunk-start states H_c
   const int frag_major = chunk_states ? 0 : 1;
   e = ssd::launch_chunk_state(pl.bf16, x, B, Gw, dtw, Hc, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
-                              (int)pl.Q, pl.T, pl.Lp, frag_major, cfg.state_heads, s);
+                              (int)pl.Q, pl.T, pl.Lp, frag_major, cfg.state_heads,
+                              fold ? dt : nullptr, A, xf, s);
   if (e != hipSuccess) return hip_status(e, "chunk_state launch");
   e = ssd::launch_state_pass(pl.bf16, Hc, Gw, init_state, final_state, pl.B, pl.H, pl.P, pl.N,
                              (int)pl.Q, pl.T, pl.Lp, frag_major, 0, s);
@@ -816,7 +830,7 @@ ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const 
     // the valid choices, in a fixed order: the fused kernel (where built),
     // then every staged combination
     // (the stage-3 choices: head-pair kernel with 2 or 1 heads, resident tile)
-    constexpr int kMaxCand = 1 + 2 * 3 * 3;
+    constexpr int kMaxCand = 1 + 3 * 3 * 3;
     ssd_config cand[kMaxCand];
     int n = 0;
     if (pl.fused_ok) {
@@ -825,7 +839,7 @@ ssd_status ssd_tune(const ssd_problem* prob, const ssd_dt_transform* dtx, const 
       cand[n++] = c;
     }
     const int okh = ssd::compute_out_default_kh(pl.bf16, pl.H, pl.G, pl.N);
-    for (int ch : {4, 16})
+    for (int ch : {0, 4, 16})
       for (int sh : {4, 2, 1})
         for (int out = 0; out < 3; ++out) {
           const int oh = out == 2 ? okh : 2 - out;
@@ -1016,10 +1030,11 @@ ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const v
     }
     // forward stages: running sums, prepared step sizes, chunk-start states
     hipError_t e = ssd::launch_chunk_cumsum(dt, A, Gw, dtw, pl.B, pl.L, pl.H, (int)pl.Q, pl.Lp,
-                                            pl.Lp, xfp, cfg.cumsum_heads, s);
+                                            pl.Lp, xfp, kCumsumHeads, s);
     if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
     e = ssd::launch_chunk_state(0, x32, B32, Gw, dtw, Hc, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
-                                (int)pl.Q, pl.T, pl.Lp, 0, cfg.state_heads, s);
+                                (int)pl.Q, pl.T, pl.Lp, 0, cfg.state_heads, nullptr, nullptr,
+                                nullptr, s);
     if (e != hipSuccess) return hip_status(e, "chunk_state launch");
     e = ssd::launch_state_pass(0, Hc, Gw, init_state, dfinal ? fin : nullptr, pl.B, pl.H,
                                pl.P, pl.N, (int)pl.Q, pl.T, pl.Lp, 0, 0, s);
@@ -1032,7 +1047,8 @@ ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const v
     e = ssd::launch_bwd_prep(Gw, w2, Gz, pl.B, pl.H, pl.L, pl.Lp, s);
     if (e != hipSuccess) return hip_status(e, "bwd_prep launch");
     e = ssd::launch_chunk_state(0, dy32, C32, Gz, w2, Lam, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
-                                (int)pl.Q, pl.T, pl.Lp, 0, cfg.state_heads, s);
+                                (int)pl.Q, pl.T, pl.Lp, 0, cfg.state_heads, nullptr, nullptr,
+                                nullptr, s);
     if (e != hipSuccess) return hip_status(e, "chunk_state (reverse) launch");
     e = ssd::launch_state_pass(0, Lam, Gw, dfinal, dinit, pl.B, pl.H, pl.P, pl.N, (int)pl.Q,
                                pl.T, pl.Lp, 0, 1, s);

@@ -80,6 +80,51 @@ __device__ __forceinline__ float dt_prepare(const DtXform& f, float v, int h) {
   if (f.softplus) v = softplus_f32(v);
   return fminf(fmaxf(v, f.lo), f.hi);
 }
+// The same with the head's bias already loaded (`bias` is used when f.bias is
+// set): identical arithmetic.
+__device__ __forceinline__ float dt_prepare_b(const DtXform& f, float v, float bias) {
+  if (f.bias) v += bias;
+  if (f.softplus) v = softplus_f32(v);
+  return fminf(fmaxf(v, f.lo), f.hi);
+}
+
+// Within-chunk running sum of one head by one wave, base 2: lane l holds the
+// TPL consecutive tokens l*TPL .. l*TPL + TPL - 1 (raw = prepared dt, 0 on
+// padding and on lanes past the chunk), and gets
+//   g[e] = log2(e) A sum_{k <= l*TPL + e} raw[k]
+// as a serial sum over its own tokens plus an inclusive scan of the lane
+// totals across the wave.  chunk_cumsum and chunk_state both call it, so the
+// running sums are bitwise the same whichever forms them.  The lane scan runs
+// on DPP moves: shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes
+// whose source lies before the row's start add zero), then each row's total
+// broadcast into the next row (row_bcast:15, rows 1 and 3) and the total of
+// rows 0-1 into rows 2 and 3 (row_bcast:31).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_src(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROWS, 0xf, false));
+}
+template <int TPL>
+__device__ __forceinline__ void wave_chunk_scan(const float (&raw)[TPL], float a2, float (&g)[TPL],
+                                                int lane) {
+  (void)lane;
+  float run = 0.0f;
+#pragma unroll
+  for (int e = 0; e < TPL; ++e) {
+    run += raw[e] * a2;
+    g[e] = run;
+  }
+  float incl = run;
+  incl += dpp_src<0x111, 0xf>(incl);   // row_shr:1
+  incl += dpp_src<0x112, 0xf>(incl);   // row_shr:2
+  incl += dpp_src<0x114, 0xf>(incl);   // row_shr:4
+  incl += dpp_src<0x118, 0xf>(incl);   // row_shr:8
+  incl += dpp_src<0x142, 0xa>(incl);   // row_bcast:15 into rows 1, 3
+  incl += dpp_src<0x143, 0xc>(incl);   // row_bcast:31 into rows 2, 3
+  const float carry = incl - run;
+#pragma unroll
+  for (int e = 0; e < TPL; ++e) g[e] = carry + g[e];
+}
 
 // 16-byte vector of io elements: 8 bf16 or 4 fp32.
 typedef uint4 vec16;
@@ -232,6 +277,20 @@ __device__ __forceinline__ void dma16(const void* gaddr, const void* lds) {
       : "memory", "m0");
 }
 
+// A 4-byte direct load: lane i's dword lands at LDS byte lds + 4 i, so one
+// instruction gathers 64 values from any addresses into 64 consecutive
+// floats (`lds` must be the same for every active lane).
+__device__ __forceinline__ void dma4(const void* gaddr, const void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(gaddr), "s"(base)
+      : "memory", "m0");
+}
+
 // The same load with a wave-uniform 64-bit base held in SGPRs and a per-lane
 // 32-bit byte offset (the instruction's saddr form): a stream that advances
 // by whole rows only moves the base, so its per-lane offsets stay in
@@ -263,6 +322,18 @@ __device__ __forceinline__ void wait_groups(int n) {
   else if (n == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per));
   else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(per));
   else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// The same wait when `extra` more vector-memory operations (stores) were
+// issued after the awaited group: at most n groups of `per` plus `extra`
+// remain outstanding.
+template <int per, int extra>
+__device__ __forceinline__ void wait_groups_plus(int n) {
+  if (n >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * per + extra));
+  else if (n == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per + extra));
+  else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(per + extra));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(extra));
   __asm__ __volatile__("" ::: "memory");
 }
 

@@ -360,12 +360,12 @@ def test_fwd_config_check_order_and_default(so):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(batch=2, seqlen=8192, nheads=80, headdim=64, dstate=128, ngroups=1, chunk_size=256),
-     dict(cumsum_heads=4, state_heads=4, out_heads=2, fused=0, out_resident=1)),
+     dict(cumsum_heads=0, state_heads=4, out_heads=2, fused=0, out_resident=1)),
     (dict(batch=8, seqlen=4096, nheads=64, headdim=64, dstate=256, ngroups=8, chunk_size=128),
-     dict(cumsum_heads=4, state_heads=4, out_heads=1, fused=0, out_resident=0)),
-    (dict(nheads=6, ngroups=3), dict(cumsum_heads=4, state_heads=2, out_heads=2, fused=0, out_resident=1)),
-    (dict(nheads=6, ngroups=2), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0, out_resident=1)),
-    (dict(nheads=3, ngroups=3, io_dtype=0), dict(cumsum_heads=4, state_heads=1, out_heads=1, fused=0, out_resident=0)),
+     dict(cumsum_heads=0, state_heads=4, out_heads=1, fused=0, out_resident=0)),
+    (dict(nheads=6, ngroups=3), dict(cumsum_heads=0, state_heads=2, out_heads=2, fused=0, out_resident=1)),
+    (dict(nheads=6, ngroups=2), dict(cumsum_heads=0, state_heads=1, out_heads=1, fused=0, out_resident=1)),
+    (dict(nheads=3, ngroups=3, io_dtype=0), dict(cumsum_heads=0, state_heads=1, out_heads=1, fused=0, out_resident=0)),
 ])
 def test_default_config_is_the_static_table(so, kw, want):
     assert lib.ssd_default_config(P(**kw)) == want

@@ -67,7 +67,7 @@ def valid_configs(p):
             lib.SSD_BF16))
         d["fused"] = 1
         out.append(d)
-    for ch, sh in itertools.product((4, 16), (1, 2, 4)):
+    for ch, sh in itertools.product((0, 4, 16), (1, 2, 4)):
         if hg % sh:
             continue
         for oh in (1, 2):
