@@ -666,35 +666,36 @@ bwd_prep_kernel(const float* __restrict__ Gw, float* __restrict__ w2, float* __r
 // Each element adds its group's heads of the batch in ascending order to the
 // running fp32 sum (starting from zero at the group's first head) and, at the
 // group's last head, stores the io-dtype result: the order of additions is
-// that of one pass over all the heads, whatever the batches.
+// that of one pass over all the heads, whatever the batches.  Only the
+// groups g0 .. g0 + ng - 1 that the batch touches are visited (total = B L ng N).
 template <typename T>
 __global__ void __launch_bounds__(kBwdThreads)
 bwd_group_sum_kernel(const float* __restrict__ dBh, const float* __restrict__ dCh,
                      float* __restrict__ accB, float* __restrict__ accC, T* __restrict__ dB,
                      T* __restrict__ dC, int64_t total, int H, int G, int N, int h0, int nb,
-                     int hb) {
+                     int hb, int g0, int ng) {
   const int hpg = H / G;
   for (int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * kBwdThreads) {
     const int n = (int)(e % N);
-    const int64_t bg = e / N;                 // (b*L + t)*G + g
-    const int64_t bt = bg / G;
-    const int g = (int)(bg % G);
+    const int64_t bq = e / N;                 // (b*L + t)*ng + (g - g0)
+    const int64_t bt = bq / ng;
+    const int g = g0 + (int)(bq % ng);
+    const int64_t o = (bt * G + g) * N + n;   // element of dB, dC and the running sums
     const int ha = max(h0, g * hpg), hz = min(h0 + nb, (g + 1) * hpg);
-    if (ha >= hz) continue;                   // no head of this group in the batch
     const bool first = ha == g * hpg, last = hz == (g + 1) * hpg;
-    float sb = first ? 0.0f : accB[e], sc = first ? 0.0f : accC[e];
+    float sb = first ? 0.0f : accB[o], sc = first ? 0.0f : accC[o];
     const int64_t base = (bt * hb + (ha - h0)) * N + n;
     for (int k = 0; k < hz - ha; ++k) {
       sb += dBh[base + (int64_t)k * N];
       sc += dCh[base + (int64_t)k * N];
     }
     if (last) {
-      dB[e] = to_io<T>(sb);
-      dC[e] = to_io<T>(sc);
+      dB[o] = to_io<T>(sb);
+      dC[o] = to_io<T>(sc);
     } else {
-      accB[e] = sb;
-      accC[e] = sc;
+      accB[o] = sb;
+      accC[o] = sc;
     }
   }
 }
@@ -885,17 +886,19 @@ hipError_t launch_bwd_group_sum(int io_bf16, const float* dBh, const float* dCh,
                                 float* accC, void* dB, void* dC, int64_t batch, int64_t L,
                                 int64_t H, int64_t N, int64_t G, int h0, int nb, int hb,
                                 hipStream_t stream) {
-  const int64_t total = batch * L * G * N;
+  const int hpg = (int)(H / G);
+  const int g0 = h0 / hpg, ng = (h0 + nb - 1) / hpg - g0 + 1;   // the groups the batch touches
+  const int64_t total = batch * L * ng * N;
   const int64_t blocks = (total + kBwdThreads - 1) / kBwdThreads;
   const dim3 g2((unsigned)(blocks < 8192 ? blocks : 8192));
   if (io_bf16)
     hipLaunchKernelGGL(bwd_group_sum_kernel<bf16>, g2, dim3(kBwdThreads), 0, stream, dBh, dCh,
                        accB, accC, static_cast<bf16*>(dB), static_cast<bf16*>(dC), total, (int)H,
-                       (int)G, (int)N, h0, nb, hb);
+                       (int)G, (int)N, h0, nb, hb, g0, ng);
   else
     hipLaunchKernelGGL(bwd_group_sum_kernel<float>, g2, dim3(kBwdThreads), 0, stream, dBh, dCh,
                        accB, accC, static_cast<float*>(dB), static_cast<float*>(dC), total,
-                       (int)H, (int)G, (int)N, h0, nb, hb);
+                       (int)H, (int)G, (int)N, h0, nb, hb, g0, ng);
   return hipGetLastError();
 }
 
