@@ -371,7 +371,6 @@ compute_out_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* _
                    int64_t ldw, int nbc, int PB, int RS) {
   typedef typename FragOf<T>::type frag_t;
   typedef Slot<T, NK, KH> S;
-  constexpr int V = Vec16<T>::n;
   constexpr int NSLOT = S::NSLOT;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int arrived[NSLOT], released[NSLOT];

@@ -253,27 +253,6 @@ __device__ __forceinline__ floatx4 load_flags_sc1(const unsigned long long* p) {
   return v;
 }
 
-// Device-coherent loads of 8 x 16 bytes (the caller's state pieces); the
-// wait sits in the same statement, so the outputs are valid at its end.
-__device__ __forceinline__ void load8_sc1(const float* p0, const float* p1, const float* p2,
-                                          const float* p3, const float* p4, const float* p5,
-                                          const float* p6, const float* p7, floatx4* v) {
-  __asm__ __volatile__(
-      "global_load_dwordx4 %0, %8, off sc1\n\t"
-      "global_load_dwordx4 %1, %9, off sc1\n\t"
-      "global_load_dwordx4 %2, %10, off sc1\n\t"
-      "global_load_dwordx4 %3, %11, off sc1\n\t"
-      "global_load_dwordx4 %4, %12, off sc1\n\t"
-      "global_load_dwordx4 %5, %13, off sc1\n\t"
-      "global_load_dwordx4 %6, %14, off sc1\n\t"
-      "global_load_dwordx4 %7, %15, off sc1\n\t"
-      "s_waitcnt vmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-        "=&v"(v[6]), "=&v"(v[7])
-      : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(p4), "v"(p5), "v"(p6), "v"(p7)
-      : "memory");
-}
-
 // Device-coherent 16-byte store (written through to where every XCD sees it).
 // A store of more than 8 bytes reads its data registers after issue, and the
 // compiler cannot see the store inside the statement to keep the next VALU
