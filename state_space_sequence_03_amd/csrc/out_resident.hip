@@ -30,10 +30,10 @@
 // (S^T = B C^T, lane = row i, 4 + 4 token columns), which is exactly the A
 // operand of the output product once weighted and rounded to bf16.
 //
-// Streaming.  Three head buffers in LDS (x rows with XOR-swizzled 16-byte
-// chunks, the fragment-major state slice, G, dt and the weight table e),
-// filled by direct global->LDS loads two heads ahead; a workgroup barrier
-// per head hands buffers on.  Every wave issues exactly kLoadsPerHead loads
+// Streaming.  Two head buffers in LDS (x rows with XOR-swizzled 16-byte
+// chunks, the fragment-major state slice, G, dt and the off-band weight
+// tables), filled by direct global->LDS loads one head ahead; a workgroup
+// barrier per head hands buffers on.  Every wave issues exactly kLoadsPerHead loads
 // per head and kStoresPerHead stores, so one vmcnt target per head is exact.
 // y is written with buffer stores whose range ends at the chunk's last valid
 // row: rows past the sequence end are dropped by the hardware range check,
@@ -57,14 +57,18 @@ constexpr int kBufX = 0;                                // 256 rows x 128 B
 constexpr int kBufH = kBufX + kRsQ * kRsP * 2;          // fragment-major state, 16 KiB
 constexpr int kBufG = kBufH + kRsP * kRsNK * 32 * 2;    // G (fp32 x 256)
 constexpr int kBufD = kBufG + kRsQ * 4;                 // dt
-constexpr int kBufE = kBufD + kRsQ * 4;                 // e_j = exp2(G_e - G_j) dt_j
-constexpr int kBufBytes = kBufE + kRsQ * 4;             // 52224
-constexpr int kNBuf = 3;
-constexpr int kRsLds = kNBuf * kBufBytes;               // 156672
+constexpr int kBufE = kBufD + kRsQ * 4;                 // off-band weights E_q, q = 1..7
+constexpr int kEElems = 16 * 8 * 7;                     // sum of 32 q over q = 1..7
+constexpr int kBufBytes = kBufE + kEElems * 4;          // 54784
+constexpr int kNBuf = 2;
 // B rows (256 x 256 B) are staged once, from the start of buffer 1
 constexpr int kBOff = kBufBytes;
-static_assert(kBOff + kRsQ * kRsNK * 32 * 2 <= kRsLds, "B staging must fit the head buffers");
+constexpr int kBBytes = kRsQ * kRsNK * 32 * 2;
+constexpr int kRsLds = kNBuf * kBufBytes > kBOff + kBBytes ? kNBuf * kBufBytes : kBOff + kBBytes;
 static_assert(kRsLds <= 160 * 1024, "LDS of one CU");
+
+// Row q of the off-band weight tables: tokens 0 .. 32 q - 1.
+__host__ __device__ constexpr int e_row(int q) { return 16 * q * (q - 1); }
 
 // Per head and wave: 4 of the 32 x blocks of 1 KiB, 2 of the (up to 16)
 // state blocks, and the whole G and dt rows (every wave loads these, so each
@@ -167,27 +171,34 @@ __device__ __forceinline__ void issue_head(unsigned char* buf, const HeadSrc& s,
   for (int k = 0; k < kLoadsPerHead; ++k) issue_load<NK>(k, buf, s, o, xstride, qv, wave, lane);
 }
 
-// e_j = exp2(G_e - G_j) dt_j (e = last token of j's pair, so e_j <= dt_j)
-// for one head, by the first 256 threads, from G and dt rows they loaded
-// themselves.
+// The off-band weights of one head, seen from each row-block reference
+// r = 32 q - 1 (q = 1..7, the last token before the band pair q):
+//   E_q(j) = (exp2(G_e - G_j) dt_j) * exp2(G_r - G_e),  j < 32 q,
+// e = the last token of j's pair, so both factors are <= 1.  Each is the
+// product the tile operand needs (one rounding, the factors formed as the
+// head-pair kernel forms them), made once per head here instead of by every
+// wave per tile.  By the first 224 threads (token j; pair 7 is never
+// off-band), from G and dt rows that all waves loaded.
 __device__ __forceinline__ void weight_table(unsigned char* buf, int tid) {
-  if (tid < kRsQ) {
+  if (tid < 32 * 7) {
     const float* Gs = reinterpret_cast<const float*>(buf + kBufG);
     const float* ds = reinterpret_cast<const float*>(buf + kBufD);
+    float* Es = reinterpret_cast<float*>(buf + kBufE);
     const int j = tid, e = j | 31;
-    reinterpret_cast<float*>(buf + kBufE)[j] = fast_exp2(Gs[e] - Gs[j]) * ds[j];
+    const float ej = fast_exp2(Gs[e] - Gs[j]) * ds[j];
+    const float ge = Gs[e];
+    for (int q = j / 32 + 1; q < 8; ++q) Es[e_row(q) + j] = ej * fast_exp2(Gs[32 * q - 1] - ge);
   }
 }
 
-// Weighted tile -> bf16 A operand, left of the block's band: weight
-// exp2(G_r - G_e) e_j (both factors <= 1).
-__device__ __forceinline__ bf16x8 offband_operand(const floatx4 (&st)[2], floatx4 e0, floatx4 e1,
-                                                  float f) {
+// Weighted tile -> bf16 A operand, left of the block's band: weights E_q of
+// the lane's 4 + 4 tokens.
+__device__ __forceinline__ bf16x8 offband_operand(const floatx4 (&st)[2], floatx4 e0, floatx4 e1) {
   bf16x8 af;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    af[r] = static_cast<bf16>(st[0][r] * (e0[r] * f));
-    af[4 + r] = static_cast<bf16>(st[1][r] * (e1[r] * f));
+    af[r] = static_cast<bf16>(st[0][r] * e0[r]);
+    af[4 + r] = static_cast<bf16>(st[1][r] * e1[r]);
   }
   return af;
 }
@@ -298,34 +309,34 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
   }
   wait_vm_ops(0);                                          // this wave's head-0 loads landed
   weight_table(smem, tid);
-  lds_barrier();     // B rows no longer read; every wave's head-0 loads and e table in place
-  if (nh > 1) issue_head<NK>(smem + kBufBytes, head_src(1), ho, xstride, qv, wave, lane);
+  lds_barrier();     // B rows no longer read; every wave's head-0 loads and weights in place
 
   // per-lane store offsets (bytes, relative to row 0 of the chunk, head 0)
   const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
       y + ((int64_t)b * L + t0) * xstride, (short)0, (int)((int64_t)qv * xstride * 2), 0x00020000);
 
   // Head hh starts after a barrier that follows every wave's wait for its
-  // own loads of hh and the e table of hh (made by the first four waves), so
-  // all of hh is in LDS and every wave is done with head hh-1, whose buffer
-  // takes head hh+2.  (Hand-offs through LDS counters instead of the barrier,
-  // letting the older waves, which win the SIMD's issue arbitration, run up
-  // to one head ahead, measured 1-2% slower.)
+  // own loads of hh and the weight tables of hh (made by the first four
+  // waves), so all of hh is in LDS and every wave is done with head hh-1,
+  // whose buffer takes head hh+1: a head's loads are issued one head ahead,
+  // ~4 us before they are needed.  (Hand-offs through LDS counters instead
+  // of the barrier, letting the older waves, which win the SIMD's issue
+  // arbitration, run up to one head ahead, measured 1-2% slower.)
   for (int hh = 0; hh < nh; ++hh) {
-    // the loads of head hh+2 are spread over the head (two after the carried
+    // the loads of head hh+1 are spread over the head (two after the carried
     // term, two in each of the first three pair steps -- every wave has at
     // least five): issued all at once they queue behind one another and
     // stall the later waves
-    const bool pre = hh + 2 < nh;
-    unsigned char* pbuf = smem + ((hh + 2) % kNBuf) * kBufBytes;
-    const HeadSrc psrc = head_src(hh + 2);
+    const bool pre = hh + 1 < nh;
+    unsigned char* pbuf = smem + ((hh + 1) % kNBuf) * kBufBytes;
+    const HeadSrc psrc = head_src(hh + 1);
     auto prefetch = [&](int k) {
       if (pre) issue_load<NK>(k, pbuf, psrc, ho, xstride, qv, wave, lane);
     };
     unsigned char* buf = smem + (hh % kNBuf) * kBufBytes;
     const float* Gs = reinterpret_cast<const float*>(buf + kBufG);
     const float* ds = reinterpret_cast<const float*>(buf + kBufD);
-    const float* es = reinterpret_cast<const float*>(buf + kBufE);
+    const float* Es = reinterpret_cast<const float*>(buf + kBufE);
     const int h = h_begin + hh;
     const float dh = Dv ? Dv[h] : 0.0f;
 
@@ -409,18 +420,11 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
         band_half(std::integral_constant<int, 0>{}, st, acc, ib, gr, jb, xf);
     };
 
-    // per-pair weights: e of the lane's tokens and G at the pair's last token
-    struct PairW {
-      floatx4 e0, e1;
-      float g_end;
-    };
-    auto pair_w = [&](int jp) {
-      PairW o;
-      const int jb = jp * 32;
-      o.e0 = *reinterpret_cast<const floatx4*>(es + jb + 4 * lg);
-      o.e1 = *reinterpret_cast<const floatx4*>(es + jb + 16 + 4 * lg);
-      o.g_end = Gs[jb + 31];
-      return o;
+    // off-band weights of the lane's tokens {4 lg .. +3, 16 + 4 lg .. +3} of
+    // pair jp, seen from reference q
+    auto offband_w = [&](int q, int jb, floatx4& e0, floatx4& e1) {
+      e0 = *reinterpret_cast<const floatx4*>(Es + e_row(q) + jb + 4 * lg);
+      e1 = *reinterpret_cast<const floatx4*>(Es + e_row(q) + jb + 16 + 4 * lg);
     };
     // The pair steps, specialised per wave class: the early block's band
     // pair Q0 = w/2 (0..3) fixes the late block's, 7 - Q0, so with Q0 a
@@ -452,16 +456,19 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
           prefetch(2 + 2 * jp);
           prefetch(3 + 2 * jp);
         }
-        const PairW cur = pair_w(jp);
         if (jp < Q0) {
-          const bf16x8 af = offband_operand(tile[jp], cur.e0, cur.e1, fast_exp2(gr_e - cur.g_end));
+          floatx4 e0, e1;
+          offband_w(Q0, jb, e0, e1);
+          const bf16x8 af = offband_operand(tile[jp], e0, e1);
 #pragma unroll
           for (int pt = 0; pt < 4; ++pt) acc_e[pt] = mma(acc_e[pt], xf[pt], af);
         } else if (jp == Q0) {
           band(tile[jp], acc_e, ib_e, gr_e, jb, xf);
         }
         if (jp < Q1) {
-          const bf16x8 af = offband_operand(tile[8 - jp], cur.e0, cur.e1, fast_exp2(gr_l - cur.g_end));
+          floatx4 e0, e1;
+          offband_w(Q1, jb, e0, e1);
+          const bf16x8 af = offband_operand(tile[8 - jp], e0, e1);
 #pragma unroll
           for (int pt = 0; pt < 4; ++pt) acc_l[pt] = mma(acc_l[pt], xf[pt], af);
         } else {
@@ -497,10 +504,9 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
                                             (int)(so_l + pt * 32), 0, 0);
     }
     if (hh + 1 < nh) {
-      // this wave's loads of head hh+1 landed: after them it issued the
-      // stores of head hh-1, the loads of head hh+2 and the stores of head hh
-      wait_vm_ops((hh >= 1 ? kStoresPerHead : 0) + (hh + 2 < nh ? kLoadsPerHead : 0) +
-                  kStoresPerHead);
+      // this wave's loads of head hh+1 landed: after them it issued only the
+      // stores of head hh
+      wait_vm_ops(kStoresPerHead);
       weight_table(smem + ((hh + 1) % kNBuf) * kBufBytes, tid);
       lds_barrier();
     }
