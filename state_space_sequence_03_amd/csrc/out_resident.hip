@@ -61,10 +61,15 @@ constexpr int kBufE = kBufD + kRsQ * 4;                 // off-band weights E_q,
 constexpr int kEElems = 16 * 8 * 7;                     // sum of 32 q over q = 1..7
 constexpr int kBufBytes = kBufE + kEElems * 4;          // 54784
 constexpr int kNBuf = 2;
-// B rows (256 x 256 B) are staged once, from the start of buffer 1
+// each wave's y rows (its two blocks, 32 rows x 128 B) on their way out
+constexpr int kYStage = kNBuf * kBufBytes;
+constexpr int kYStageBytes = kRsWaves * 32 * 128;
+// B rows (256 x 256 B) are staged once, from the start of buffer 1 (before
+// any y row is)
 constexpr int kBOff = kBufBytes;
 constexpr int kBBytes = kRsQ * kRsNK * 32 * 2;
-constexpr int kRsLds = kNBuf * kBufBytes > kBOff + kBBytes ? kNBuf * kBufBytes : kBOff + kBBytes;
+constexpr int kRsLds = kYStage + kYStageBytes > kBOff + kBBytes ? kYStage + kYStageBytes
+                                                                : kBOff + kBBytes;
 static_assert(kRsLds <= 160 * 1024, "LDS of one CU");
 
 // Row q of the off-band weight tables: tokens 0 .. 32 q - 1.
@@ -76,7 +81,7 @@ __host__ __device__ constexpr int e_row(int q) { return 16 * q * (q - 1); }
 // state blocks exist (dstate < 128) the extra loads repeat one (identical
 // data to the same place), so the count is fixed.
 constexpr int kLoadsPerHead = 8;
-constexpr int kStoresPerHead = 8;   // 2 blocks x 4 column tiles of 8 bytes per lane
+constexpr int kStoresPerHead = 4;   // 4 x 8 whole rows of 128 bytes
 
 __device__ __forceinline__ int bsw(int r) { return r & 15; }
 __device__ __forceinline__ int xsw(int r) { return ((r >> 1) & 3) << 1; }
@@ -84,14 +89,9 @@ __device__ __forceinline__ int xsw(int r) { return ((r >> 1) & 3) << 1; }
 // Wait until at most n of this wave's vector-memory operations are
 // outstanding, for the few counts the head loop uses; then keep the compiler
 // from moving LDS reads of the awaited data above the wait.
-static_assert(kLoadsPerHead == kStoresPerHead, "the head loop's wait counts are multiples of 8");
-__device__ __forceinline__ void wait_vm_ops(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
-    case 16: __builtin_amdgcn_s_waitcnt(vmcnt_imm(16)); break;
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(24)); break;
-  }
+template <int N>
+__device__ __forceinline__ void wait_vm_ops() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
   __asm__ __volatile__("" ::: "memory");
 }
 
@@ -119,7 +119,7 @@ __device__ __forceinline__ int opaque_v(int v) {
   return v;
 }
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct HeadSrc {
   const bf16* x;      // x rows of the chunk for this head: x + ((b L + t0) H + h) P
@@ -278,7 +278,7 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
     const int tok = min(r, qv - 1);
     dma16(Bc + (int64_t)tok * bstride + gc * 8, smem + kBOff + blk * 1024);
   }
-  wait_vm_ops(0);                                          // C and B landed
+  wait_vm_ops<0>();                                          // C and B landed
   lds_barrier();
   // head 0 -> buffer 0 while the tiles are built (issued after the wait: vector
   // memory completes in order, so a wait for C would otherwise wait for it too)
@@ -307,7 +307,7 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
       }
     }
   }
-  wait_vm_ops(0);                                          // this wave's head-0 loads landed
+  wait_vm_ops<0>();                                          // this wave's head-0 loads landed
   weight_table(smem, tid);
   lds_barrier();     // B rows no longer read; every wave's head-0 loads and weights in place
 
@@ -483,30 +483,48 @@ out_resident_kernel(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
       default: pair_steps(std::integral_constant<int, 3>{}); break;
     }
 
-    // y rows of both blocks: lane holds row i and p = 16 pt + 4 lg .. +3
-    // store offsets (bytes from row 0 of the chunk), formed here from a
-    // laundered lane index rather than kept in registers across the loop
-    const int lrv = opaque_v(lr);
-    const uint32_t hoff = (uint32_t)h * kRsP * 2 + (uint32_t)(4 * lg * 2);
-    const uint32_t so_e = (uint32_t)((ib_e * 16 + lrv) * (int)xstride * 2) + hoff;
-    const uint32_t so_l = (uint32_t)((ib_l * 16 + lrv) * (int)xstride * 2) + hoff;
+    // y rows of both blocks (lane: row lr of each, p = 16 pt + 4 lg .. +3)
+    // through this wave's staging rows -- 0..15 the early block, 16..31 the
+    // late one -- so that each store writes 8 whole 128-byte rows instead of
+    // 16 scattered 32-byte pieces.  In the staging, the 8-byte piece
+    // (row, p) sits in 16-byte chunk (p / 8) ^ (row % 8) and half
+    // (p / 4 % 2) ^ (row / 8 % 2): the 16 rows of one write and the 8 chunks
+    // of one row in a read meet distinct banks.
+    unsigned char* ys = smem + kYStage + wave * (32 * 128);
+    {
+      const int lrv = opaque_v(lr);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      bf16x4 ve, vl;
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ve[e] = static_cast<bf16>(acc_e[pt][e]);
-        vl[e] = static_cast<bf16>(acc_l[pt][e]);
+        for (int pt = 0; pt < 4; ++pt) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(blk ? acc_l[pt][e] : acc_e[pt][e]);
+          const int row = blk * 16 + lrv;
+          const int c = (2 * pt + (lg >> 1)) ^ (row & 7), half = (lg & 1) ^ ((row >> 3) & 1);
+          *reinterpret_cast<bf16x4*>(ys + row * 128 + c * 16 + half * 8) = v;
+        }
+    }
+    wave_sync();
+    {
+      // store s: staging rows 8 s + lane / 8, 16-byte chunk lane % 8 of each;
+      // rows past the sequence end fall outside the store range and are dropped
+      const int rl = opaque_v(lane >> 3), cl = lane & 7;
+      const uint32_t col = (uint32_t)h * kRsP * 2 + (uint32_t)cl * 16;
+#pragma unroll
+      for (int st = 0; st < kStoresPerHead; ++st) {
+        const int row = 8 * st + rl;                 // row % 8 = rl, row / 8 % 2 = st % 2
+        u32x4 v = *reinterpret_cast<const u32x4*>(ys + row * 128 + ((cl ^ rl) * 16));
+        if (st & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        const int grow = st < 2 ? ib_e * 16 + row : ib_l * 16 + row - 16;
+        __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)((uint32_t)(grow * (int)xstride * 2) + col),
+                                               0, 0);
       }
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ve), yr,
-                                            (int)(so_e + pt * 32), 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, vl), yr,
-                                            (int)(so_l + pt * 32), 0, 0);
     }
     if (hh + 1 < nh) {
       // this wave's loads of head hh+1 landed: after them it issued only the
       // stores of head hh
-      wait_vm_ops(kStoresPerHead);
+      wait_vm_ops<kStoresPerHead>();
       weight_table(smem + ((hh + 1) % kNBuf) * kBufBytes, tid);
       lds_barrier();
     }

@@ -561,10 +561,11 @@ def test_bwd_workspace_formula(so):
 @pytest.mark.skipif(not os.path.exists(f"{LLVM}/llvm-objdump"), reason="ROCm LLVM tools not installed")
 def test_resident_kernel_memory_operation_counts(so, tmp_path):
     # The resident-tile kernel waits for one head's loads with a vmcnt target
-    # that counts the stores and loads issued after them: 8 stores of 8 bytes
-    # per wave and head (never merged, never branched around) and 7 direct
-    # loads (4 x blocks, 2 state blocks, one G or dt block).  The built code
-    # must have exactly that shape: 8 buffer_store_dwordx2; the only other
+    # that counts the stores issued after them: 4 stores of 16 bytes per wave
+    # and head (whole y rows out of the wave's LDS staging; never merged,
+    # never branched around), after 8 direct loads of the next head (4 x
+    # blocks, 2 state blocks, the G and dt rows).  The built code must have
+    # exactly that shape: 4 buffer_store_dwordx4; the only other
     # stores write the status word (the call record before the first load,
     # and a bounded wait's timeout report, a path that only a bug takes); and
     # every vector load of the head loop a direct-to-LDS one.
@@ -574,7 +575,7 @@ def test_resident_kernel_memory_operation_counts(so, tmp_path):
     for f in kernels:
         insts = funcs[f]
         stores = [i for i in insts if re.match(r"buffer_store", i)]
-        assert len(stores) == 8 and all(i.startswith("buffer_store_dwordx2") for i in stores), (f, stores)
+        assert len(stores) == 4 and all(i.startswith("buffer_store_dwordx4") for i in stores), (f, stores)
         first_load = min(k for k, i in enumerate(insts) if i.startswith("global_load"))
         others = [k for k, i in enumerate(insts) if re.match(r"(global|flat)_store", i)]
         assert others and others[0] < first_load, (f, [insts[k] for k in others])
