@@ -177,17 +177,20 @@ __device__ __forceinline__ void issue_head(unsigned char* buf, const HeadSrc& s,
 // e = the last token of j's pair, so both factors are <= 1.  Each is the
 // product the tile operand needs (one rounding, the factors formed as the
 // head-pair kernel forms them), made once per head here instead of by every
-// wave per tile.  By the first 224 threads (token j; pair 7 is never
-// off-band), from G and dt rows that all waves loaded.
+// wave per tile: the 896 entries spread over all 512 threads (entry k and
+// k + 512), from G and dt rows that all waves loaded.
 __device__ __forceinline__ void weight_table(unsigned char* buf, int tid) {
-  if (tid < 32 * 7) {
-    const float* Gs = reinterpret_cast<const float*>(buf + kBufG);
-    const float* ds = reinterpret_cast<const float*>(buf + kBufD);
-    float* Es = reinterpret_cast<float*>(buf + kBufE);
-    const int j = tid, e = j | 31;
-    const float ej = fast_exp2(Gs[e] - Gs[j]) * ds[j];
+  const float* Gs = reinterpret_cast<const float*>(buf + kBufG);
+  const float* ds = reinterpret_cast<const float*>(buf + kBufD);
+  float* Es = reinterpret_cast<float*>(buf + kBufE);
+#pragma unroll
+  for (int k = tid; k < kEElems; k += kRsThreads) {
+    int q = 1;
+#pragma unroll
+    for (int r = 2; r < 8; ++r) q = k >= e_row(r) ? r : q;
+    const int j = k - e_row(q), e = j | 31;
     const float ge = Gs[e];
-    for (int q = j / 32 + 1; q < 8; ++q) Es[e_row(q) + j] = ej * fast_exp2(Gs[32 * q - 1] - ge);
+    Es[k] = (fast_exp2(ge - Gs[j]) * ds[j]) * fast_exp2(Gs[32 * q - 1] - ge);
   }
 }
 
