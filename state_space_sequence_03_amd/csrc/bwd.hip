@@ -634,21 +634,6 @@ bwd_dt_kernel(const float* __restrict__ Pb, const float* __restrict__ Qb,
   }
 }
 
-// bf16 -> fp32 copy (inputs of the fp32 state stages), 8 elements (16 bytes
-// in, 32 out) per thread and step; n8 = elements / 8 (every io tensor here has
-// a multiple of 16 elements and 16-byte aligned rows)
-__global__ void __launch_bounds__(kBwdThreads)
-bwd_widen_kernel(const bf16* __restrict__ src, float* __restrict__ dst, int64_t n8) {
-  for (int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x; e < n8;
-       e += (int64_t)gridDim.x * kBwdThreads) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + 8 * e);
-    *reinterpret_cast<floatx4*>(dst + 8 * e) =
-        floatx4{to_f32(v[0]), to_f32(v[1]), to_f32(v[2]), to_f32(v[3])};
-    *reinterpret_cast<floatx4*>(dst + 8 * e + 4) =
-        floatx4{to_f32(v[4]), to_f32(v[5]), to_f32(v[6]), to_f32(v[7])};
-  }
-}
-
 // weights exp2(G) of the reversed chunk contributions (0 on padding tokens),
 // and an all-zero running sum so that chunk_state's exp2(G_last - G_j) is 1
 __global__ void __launch_bounds__(kBwdThreads)
@@ -849,15 +834,6 @@ static hipError_t launch_chunks_t(int TB, const void* x, const void* Bm, const v
   if (N <= 128) return launch_chunks_p<T, 8>(SSD_BWD_ARGS);
   return launch_chunks_p<T, 16>(SSD_BWD_ARGS);
 #undef SSD_BWD_ARGS
-}
-
-hipError_t launch_bwd_widen(const void* src, float* dst, int64_t n, hipStream_t stream) {
-  if (n % 8 != 0) return hipErrorInvalidValue;
-  const int64_t n8 = n / 8;
-  const int64_t blocks = (n8 + kBwdThreads - 1) / kBwdThreads;
-  hipLaunchKernelGGL(bwd_widen_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)),
-                     dim3(kBwdThreads), 0, stream, static_cast<const bf16*>(src), dst, n8);
-  return hipGetLastError();
 }
 
 hipError_t launch_bwd_prep(const float* Gw, float* w2, float* Gz, int64_t batch, int64_t H,

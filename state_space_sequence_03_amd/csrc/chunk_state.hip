@@ -22,6 +22,8 @@
 // direct global->LDS loads; each wave multiplies the x rows it loaded by w_j
 // in place, one barrier per slot publishes them, and both operands are read
 // with transposing LDS reads (ds_read_b64_tr_b16).
+#include <type_traits>
+
 #include "ssd_device.hpp"
 
 namespace ssd {
@@ -55,9 +57,12 @@ struct CsCfg {
   static_assert(BCH % 64 == 0, "B part of a slot must be whole 64-chunk blocks");
   static_assert(NXB % NWV == 0, "x blocks are scaled in place by the wave that loads them");
   static_assert(XC >= 8, "x swizzle needs 8 chunks per row");
-  __host__ __device__ static int gd_bytes(int Q) {      // G + dt staging, whole 1 KiB blocks
-    return (KH * 2 * Q * 4 + 1023) / 1024 * 1024;
+  __host__ __device__ static int gd_bytes(int Q) {      // the w rows, whole 1 KiB blocks
+    return (KH * Q * 4 + 1023) / 1024 * 1024;
   }
+  // the G and dt rows (or the raw dt) are staged in the ring slot the
+  // prologue leaves empty
+  static_assert(KH * 2 * 256 * 4 <= BYTES, "G and dt rows of a 256-token chunk fit a ring slot");
   __host__ __device__ static int lds_bytes(int Q) { return NSLOT * BYTES + gd_bytes(Q); }
   __device__ static int bsw(int r) { return r & BSW; }
   __device__ static int xsw(int r) { return ((r >> 1) & 3) << 1; }
@@ -135,18 +140,26 @@ struct CsFold {
   int on;             // 0: G and dt' rows are inputs (Gw, dtw)
 };
 
-template <typename T, int KH, int NW>
+// S3 (bf16 io only): the chunk contribution in fp32 from the exact bf16
+// inputs, for the backward pass's states.  Each weighted x value w_j x_j is
+// formed in fp32 and split into three bf16 parts hi + mid + lo (~24
+// significant bits: hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi -
+// mid), every difference exact in fp32), and the product with the exact B
+// rows runs as three bf16 MFMAs per K-step; S is stored in fp32.
+template <typename T, int KH, int NW, bool S3 = false>
 __global__ void __launch_bounds__((CsCfg<T, KH, NW>::THREADS))
 chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __restrict__ Gw,
-                   float* __restrict__ dtw, T* __restrict__ S, int64_t L, int H, int P, int N,
-                   int G, int Q, int T_, int64_t ldw, int nbc, int PB, int NSL, int frag_major,
-                   CsFold fold) {
+                   float* __restrict__ dtw, std::conditional_t<S3, float, T>* __restrict__ S,
+                   int64_t L, int H, int P, int N, int G, int Q, int T_, int64_t ldw, int nbc,
+                   int PB, int NSL, int frag_major, CsFold fold) {
   typedef CsCfg<T, KH, NW> C;
+  typedef std::conditional_t<S3, float, T> TO;     // stored type of S
+  static_assert(!S3 || sizeof(T) == 2, "the split form reads bf16 inputs");
   typedef typename FragOf<T>::type frag_t;
   constexpr int V = C::V;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* ring = smem;
-  float* gd = reinterpret_cast<float*>(smem + C::NSLOT * C::BYTES);   // [KH][G row | w row]
+  float* gd = reinterpret_cast<float*>(smem + C::NSLOT * C::BYTES);   // [KH][w row]
 
   // XCD-aware placement: block ids congruent mod 8 run on one XCD, so the
   // workgroups of one (b, chunk) -- which share its B rows -- are dealt to one
@@ -245,13 +258,15 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
   };
 
   // ---- prologue: G and dt rows of the KH heads (or raw dt), then the first slots
-  // raw dt with fold set: with 4 heads per workgroup, a token's 4 values are
-  // 16 contiguous bytes, loaded whole as [token][head] into the ring slot
-  // that the prologue leaves empty (64 tokens per instruction); with fewer
-  // heads, 64 tokens of one head per 4-byte gather into its dt' row.  Rows
-  // past the sequence end read its last token (the scan zeroes them).
-  const float* dtst = reinterpret_cast<const float*>(ring + (C::NSLOT - 1) * C::BYTES);
-  static_assert(KH != 4 || C::BYTES >= 4 * 256 * 4, "dt staging fits a ring slot");
+  // All of it is staged in the ring slot the prologue leaves empty (stg), and
+  // only the weights w stay (gd).  Raw dt with fold set: with 4 heads per
+  // workgroup, a token's 4 values are 16 contiguous bytes, loaded whole as
+  // [token][head] (64 tokens per instruction); with fewer heads, 64 tokens of
+  // one head per 4-byte gather into its row [hh][.. | dt row].  Rows past the
+  // sequence end read its last token (the scan zeroes them).  Without fold,
+  // the G and dt rows arrive as [hh][G row | dt row].
+  unsigned char* stg = ring + (C::NSLOT - 1) * C::BYTES;
+  const float* dtst = reinterpret_cast<const float*>(stg);
   if (fold.on) {
     if constexpr (KH == 4) {
       for (int m = wave; m * 64 < Q; m += C::NWV) {
@@ -265,7 +280,7 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
         const int hh = m / ((Q + 63) / 64), j = (m % ((Q + 63) / 64)) * 64 + lane;
         const int64_t tok = min(t0 + j, L - 1);
         if (j < Q) dma4(fold.dt + ((int64_t)b * L + tok) * H + h0 + hh,
-                        reinterpret_cast<unsigned char*>(gd + hh * 2 * Q + Q + j - lane));
+                        stg + (hh * 2 * Q + Q + j - lane) * 4);
       }
     }
   } else {
@@ -278,7 +293,7 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
       q = q < nchunk ? q : nchunk - 1;
       const int hh = q / (Q / 2), r = q % (Q / 2);
       const float* src = (r < Q / 4 ? Gw : dtw) + (int64_t)(b * H + h0 + hh) * ldw + t0 + 4 * (r % (Q / 4));
-      dma16(src, (reinterpret_cast<unsigned char*>(gd) + blk * 1024));
+      dma16(src, stg + blk * 1024);
     }
   }
   const int npro = min(C::NSLOT - 1, ns);
@@ -289,11 +304,22 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
   // rows, with fold set): the first waits of the slot loop allow for them
   int late_stores = 0;
   if (fold.on) {
+    // waves 0..KH-1 each scan one head and write its weights
+    //   w_j = exp2(G_last - G_j) dt'_j
+    // (padding tokens have dt' = 0, so w = 0), forming exactly the values the
+    // unfolded path forms from stored G and dt rows
     if (wave < KH) {
       const int hh = wave, h = h0 + hh;
-      float* row = gd + hh * 2 * Q;
+      const float* srow = dtst + hh * 2 * Q;
+      float* wrow = gd + hh * Q;
       // token j's raw dt of this head, from where the prologue put it
-      auto raw_dt = [&](int j) { return KH == 4 ? dtst[4 * j + hh] : row[Q + j]; };
+      auto raw_dt = [&](int j) { return KH == 4 ? dtst[4 * j + hh] : srow[Q + j]; };
+      auto prep = [&](int j, float v) {
+        return t0 + j < L ? (fold.xf_on ? dt_prepare_b(fold.xf, v, bias_f) : v) : 0.0f;
+      };
+      auto lane_of = [](float v, int l) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+      };
       const float a2 = a2f;
       const bool writer = pb == 0 && nsl == 0;
       // the two rows take at least one store instruction each (the compiler
@@ -301,68 +327,56 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
       // of the slot loop pass before its loads have landed
       late_stores = writer ? 2 : 0;
       const int64_t grow = (int64_t)(b * H + h) * ldw + t0;
-      if (Q >= kWave) {
-        constexpr int TPL = 4;                     // Q = 256
-        if (Q == 256) {
-          float raw[TPL], g4[TPL];
-          const int first = lane * TPL;
+      if (Q == 256) {
+        constexpr int TPL = 4;
+        float raw[TPL], g4[TPL];
+        const int first = lane * TPL;
 #pragma unroll
-          for (int e = 0; e < TPL; ++e) {
-            const float v = raw_dt(first + e);
-            raw[e] = t0 + first + e < L ? (fold.xf_on ? dt_prepare_b(fold.xf, v, bias_f) : v) : 0.0f;
-          }
-          wave_chunk_scan<TPL>(raw, a2, g4, lane);
-          *reinterpret_cast<floatx4*>(row + first) = floatx4{g4[0], g4[1], g4[2], g4[3]};
-          *reinterpret_cast<floatx4*>(row + Q + first) = floatx4{raw[0], raw[1], raw[2], raw[3]};
-          if (writer) {
-            *reinterpret_cast<floatx4*>(Gw + grow + first) = floatx4{g4[0], g4[1], g4[2], g4[3]};
-            *reinterpret_cast<floatx4*>(dtw + grow + first) = floatx4{raw[0], raw[1], raw[2], raw[3]};
-          }
+        for (int e = 0; e < TPL; ++e) raw[e] = prep(first + e, raw_dt(first + e));
+        wave_chunk_scan<TPL>(raw, a2, g4, lane);
+        const float glast = lane_of(g4[TPL - 1], kWave - 1);
+        floatx4 w;
+#pragma unroll
+        for (int e = 0; e < TPL; ++e) w[e] = fast_exp2(glast - g4[e]) * raw[e];
+        *reinterpret_cast<floatx4*>(wrow + first) = w;
+        if (writer) {
+          *reinterpret_cast<floatx4*>(Gw + grow + first) = floatx4{g4[0], g4[1], g4[2], g4[3]};
+          *reinterpret_cast<floatx4*>(dtw + grow + first) = floatx4{raw[0], raw[1], raw[2], raw[3]};
+        }
+      } else if (Q >= kWave) {
+        // Q = 64 or 128: 1 or 2 tokens per lane
+        const int tpl = Q / kWave;
+        float raw2[2] = {0.0f, 0.0f}, g2[2];
+        const int first = lane * tpl;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (e < tpl) raw2[e] = prep(first + e, raw_dt(first + e));
+        if (tpl == 2) {
+          wave_chunk_scan<2>(raw2, a2, g2, lane);
         } else {
-          // Q = 64 or 128: 1 or 2 tokens per lane
-          const int tpl = Q / kWave;
-          float raw2[2] = {0.0f, 0.0f}, g2[2];
-          const int first = lane * tpl;
+          float r1[1] = {raw2[0]}, o1[1];
+          wave_chunk_scan<1>(r1, a2, o1, lane);
+          g2[0] = o1[0];
+        }
+        const float glast = lane_of(tpl == 2 ? g2[1] : g2[0], kWave - 1);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (e < tpl) wrow[first + e] = fast_exp2(glast - g2[e]) * raw2[e];
+        if (writer) {
 #pragma unroll
           for (int e = 0; e < 2; ++e)
             if (e < tpl) {
-              const float v = raw_dt(first + e);
-              raw2[e] = t0 + first + e < L ? (fold.xf_on ? dt_prepare_b(fold.xf, v, bias_f) : v) : 0.0f;
+              Gw[grow + first + e] = g2[e];
+              dtw[grow + first + e] = raw2[e];
             }
-          if (tpl == 2) {
-            wave_chunk_scan<2>(raw2, a2, g2, lane);
-          } else {
-            float r1[1] = {raw2[0]}, o1[1];
-            wave_chunk_scan<1>(r1, a2, o1, lane);
-            g2[0] = o1[0];
-          }
-#pragma unroll
-          for (int e = 0; e < 2; ++e)
-            if (e < tpl) {
-              row[first + e] = g2[e];
-              row[Q + first + e] = raw2[e];
-            }
-          if (writer) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-              if (e < tpl) {
-                Gw[grow + first + e] = g2[e];
-                dtw[grow + first + e] = raw2[e];
-              }
-          }
         }
       } else {
         // Q = 32: lanes 0..31 hold one token each
         float r1[1] = {0.0f}, g1[1];
-        if (lane < Q) {
-          const float v = raw_dt(lane);
-          r1[0] = t0 + lane < L ? (fold.xf_on ? dt_prepare_b(fold.xf, v, bias_f) : v) : 0.0f;
-        }
+        if (lane < Q) r1[0] = prep(lane, raw_dt(lane));
         wave_chunk_scan<1>(r1, a2, g1, lane);
-        if (lane < Q) {
-          row[lane] = g1[0];
-          row[Q + lane] = r1[0];
-        }
+        const float glast = lane_of(g1[0], Q - 1);
+        if (lane < Q) wrow[lane] = fast_exp2(glast - g1[0]) * r1[0];
         if (writer) {
           if (lane < Q) {
             Gw[grow + lane] = g1[0];
@@ -371,14 +385,14 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
         }
       }
     }
-    __syncthreads();
-  }
-  // w_j = exp2(G_last - G_j) dt_j in place of dt_j; padding tokens have dt = 0
-  // and G flat past the sequence end, so they get w = 0
-  for (int idx = tid; idx < KH * Q; idx += C::THREADS) {
-    const int hh = idx / Q, j = idx % Q;
-    float* row = gd + hh * 2 * Q;
-    row[Q + j] = fast_exp2(row[Q - 1] - row[j]) * row[Q + j];
+  } else {
+    // w_j = exp2(G_last - G_j) dt_j from the staged rows; padding tokens
+    // have dt = 0 and G flat past the sequence end, so they get w = 0
+    for (int idx = tid; idx < KH * Q; idx += C::THREADS) {
+      const int hh = idx / Q, j = idx % Q;
+      const float* srow = dtst + hh * 2 * Q;
+      gd[hh * Q + j] = fast_exp2(srow[Q - 1] - srow[j]) * srow[Q + j];
+    }
   }
   __syncthreads();
 
@@ -398,28 +412,62 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
     else
       wait_groups<C::LPG>(min(C::NSLOT - 2, ns - 1 - k));
     unsigned char* sl = ring + (k % C::NSLOT) * C::BYTES;
-    // scale the x rows this wave loaded by their token's weight, in place
+    if constexpr (!S3) {
+      // scale the x rows this wave loaded by their token's weight, in place
 #pragma unroll
-    for (int i = 0; i < C::XINST; ++i) {
-      const int blk = i * C::NWV + wave;
-      const int q = blk * 64 + lane;
-      const int hq = q / C::XCH, r = q % C::XCH / C::XC;
-      vec16* pch = reinterpret_cast<vec16*>(sl + C::BCH * 16 + q * 16);
-      *pch = scale16<T>(*pch, gd[hq * 2 * Q + Q + k * kCsTok + r]);
+      for (int i = 0; i < C::XINST; ++i) {
+        const int blk = i * C::NWV + wave;
+        const int q = blk * 64 + lane;
+        const int hq = q / C::XCH, r = q % C::XCH / C::XC;
+        vec16* pch = reinterpret_cast<vec16*>(sl + C::BCH * 16 + q * 16);
+        *pch = scale16<T>(*pch, gd[hq * Q + k * kCsTok + r]);
+      }
     }
     __syncthreads();                               // slot k complete; slot k-1 free
     if (k + C::NSLOT - 1 < ns) issue(k + C::NSLOT - 1);
-    frag_t fb[4];
+    if constexpr (S3) {
+      // the lane's 8 tokens {4 lg .. +3, 16 + 4 lg .. +3} of the slot and their weights
+      const int lg = lane / 16;
+      const floatx4 w0 = *reinterpret_cast<const floatx4*>(gd + hh * Q + k * kCsTok + 4 * lg);
+      const floatx4 w1 = *reinterpret_cast<const floatx4*>(gd + hh * Q + k * kCsTok + 16 + 4 * lg);
+      frag_t fa[C::WNT];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-      fb[pt] = slot_tok_frag<T>(sl, [&](int r, int col) { return C::xoff(hh, r, col); },
-                                16 * C::XC * 16, pt * 16, lane);
+      for (int nt = 0; nt < C::WNT; ++nt)
+        fa[nt] = slot_tok_frag<T>(sl, [&](int r, int col) { return C::boff(r, col); },
+                                  16 * C::BC * 16, nw0 + nt * 16, lane);
 #pragma unroll
-    for (int nt = 0; nt < C::WNT; ++nt) {
-      const frag_t fa = slot_tok_frag<T>(sl, [&](int r, int col) { return C::boff(r, col); },
-                                         16 * C::BC * 16, nw0 + nt * 16, lane);
+      for (int pt = 0; pt < 4; ++pt) {
+        const frag_t xr = slot_tok_frag<T>(sl, [&](int r, int col) { return C::xoff(hh, r, col); },
+                                           16 * C::XC * 16, pt * 16, lane);
+        bf16x8 hi, mid, lo;
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[nt][pt] = mma(acc[nt][pt], fa, fb[pt]);
+        for (int e = 0; e < 8; ++e) {
+          const float v = to_f32(xr[e]) * (e < 4 ? w0[e] : w1[e - 4]);
+          hi[e] = static_cast<bf16>(v);
+          const float r1 = v - to_f32(hi[e]);
+          mid[e] = static_cast<bf16>(r1);
+          lo[e] = static_cast<bf16>(r1 - to_f32(mid[e]));
+        }
+#pragma unroll
+        for (int nt = 0; nt < C::WNT; ++nt) {
+          acc[nt][pt] = mma(acc[nt][pt], fa[nt], hi);
+          acc[nt][pt] = mma(acc[nt][pt], fa[nt], mid);
+          acc[nt][pt] = mma(acc[nt][pt], fa[nt], lo);
+        }
+      }
+    } else {
+      frag_t fb[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+        fb[pt] = slot_tok_frag<T>(sl, [&](int r, int col) { return C::xoff(hh, r, col); },
+                                  16 * C::XC * 16, pt * 16, lane);
+#pragma unroll
+      for (int nt = 0; nt < C::WNT; ++nt) {
+        const frag_t fa = slot_tok_frag<T>(sl, [&](int r, int col) { return C::boff(r, col); },
+                                           16 * C::BC * 16, nw0 + nt * 16, lane);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[nt][pt] = mma(acc[nt][pt], fa, fb[pt]);
+      }
     }
   }
 
@@ -427,15 +475,15 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
   const int h = h0 + hh, lr = lane % 16, lg = lane / 16;
   if (frag_major) {
     const HcFrag hf = hc_frag(P, N);
-    T* base = S + ((int64_t)(b * H + h) * T_ + c) * hf.state_elems();
+    TO* base = S + ((int64_t)(b * H + h) * T_ + c) * hf.state_elems();
 #pragma unroll
     for (int nt = 0; nt < C::WNT; ++nt) {
       const int n = n0 + nw0 + nt * 16 + 4 * lg;              // multiple of 4
       const int ks = n / 32, q = (n % 32) / 8, e0 = n % 8;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        T* dst = base + hf.offset(pb, pt, ks, lr + 16 * q) + e0;
-        if constexpr (sizeof(T) == 2) {
+        TO* dst = base + hf.offset(pb, pt, ks, lr + 16 * q) + e0;
+        if constexpr (sizeof(TO) == 2) {
           const bf16x4 v{to_io<T>(acc[nt][pt][0]), to_io<T>(acc[nt][pt][1]),
                          to_io<T>(acc[nt][pt][2]), to_io<T>(acc[nt][pt][3])};
           *reinterpret_cast<bf16x4*>(dst) = v;
@@ -445,7 +493,7 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
       }
     }
   } else {
-    T* base = S + ((int64_t)(b * H + h) * T_ + c) * (int64_t)P * N;
+    TO* base = S + ((int64_t)(b * H + h) * T_ + c) * (int64_t)P * N;
 #pragma unroll
     for (int nt = 0; nt < C::WNT; ++nt) {
       const int n = n0 + nw0 + nt * 16 + 4 * lg;
@@ -453,8 +501,8 @@ chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ Bm, float* __r
       for (int pt = 0; pt < 4; ++pt) {
         const int p = p0 + pt * 16 + lr;
         if (p < P && n < N) {
-          T* dst = base + (int64_t)p * N + n;
-          if constexpr (sizeof(T) == 2) {
+          TO* dst = base + (int64_t)p * N + n;
+          if constexpr (sizeof(TO) == 2) {
             const bf16x4 v{to_io<T>(acc[nt][pt][0]), to_io<T>(acc[nt][pt][1]),
                            to_io<T>(acc[nt][pt][2]), to_io<T>(acc[nt][pt][3])};
             *reinterpret_cast<bf16x4*>(dst) = v;
@@ -477,7 +525,7 @@ int chunk_state_default_kh(int64_t H, int64_t G) {
   return SSD_CS_KH >= 4 && hg % 4 == 0 ? 4 : hg % 2 == 0 ? 2 : 1;
 }
 
-template <typename T, int KH, int NW>
+template <typename T, int KH, int NW, bool S3 = false>
 static hipError_t launch_cs(const void* x, const void* Bm, float* Gw, float* dtw, void* S,
                             int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                             int Q, int64_t T_, int64_t ldw, int frag_major, const CsFold& fold,
@@ -488,40 +536,43 @@ static hipError_t launch_cs(const void* x, const void* Bm, float* Gw, float* dtw
   const int64_t nbc = batch * T_;
   const int64_t nblocks = ((nbc + 7) / 8) * 8 * (H / KH) * PB * NSL;
   const int lds = C::lds_bytes(Q);
-  auto kern = chunk_state_kernel<T, KH, NW>;
-  const hipError_t e = ensure_dyn_lds<chunk_state_kernel<T, KH, NW>>(160 * 1024);
+  typedef std::conditional_t<S3, float, T> TO;
+  auto kern = chunk_state_kernel<T, KH, NW, S3>;
+  // the attribute is the most any launch of this kernel asks for (chunks of
+  // at most 256 tokens), not the CU's whole LDS
+  const hipError_t e = ensure_dyn_lds<chunk_state_kernel<T, KH, NW, S3>>(C::lds_bytes(256));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(C::THREADS), lds, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm), Gw, dtw,
-                     static_cast<T*>(S), L, (int)H, (int)P, (int)N, (int)G, Q, (int)T_, ldw,
+                     static_cast<TO*>(S), L, (int)H, (int)P, (int)N, (int)G, Q, (int)T_, ldw,
                      (int)nbc, PB, NSL, frag_major, fold);
   return hipGetLastError();
 }
 
-template <typename T, int KH>
+template <typename T, int KH, bool S3 = false>
 static hipError_t launch_cs_nw(const void* x, const void* Bm, float* Gw, float* dtw, void* S,
                                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                                int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
                                const CsFold& fold, hipStream_t stream) {
 #define SSD_CS_ARGS x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, fold, stream
   switch (state_nw(N)) {
-    case 32: return launch_cs<T, KH, 32>(SSD_CS_ARGS);
-    case 64: return launch_cs<T, KH, 64>(SSD_CS_ARGS);
-    default: return launch_cs<T, KH, 128>(SSD_CS_ARGS);
+    case 32: return launch_cs<T, KH, 32, S3>(SSD_CS_ARGS);
+    case 64: return launch_cs<T, KH, 64, S3>(SSD_CS_ARGS);
+    default: return launch_cs<T, KH, 128, S3>(SSD_CS_ARGS);
   }
 #undef SSD_CS_ARGS
 }
 
-template <typename T>
+template <typename T, bool S3 = false>
 static hipError_t launch_cs_t(int kh, const void* x, const void* Bm, float* Gw, float* dtw,
                               void* S, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                               int64_t G, int Q, int64_t T_, int64_t ldw, int frag_major,
                               const CsFold& fold, hipStream_t stream) {
 #define SSD_CS_ARGS x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major, fold, stream
   switch (kh) {
-    case 4: return launch_cs_nw<T, 4>(SSD_CS_ARGS);
-    case 2: return launch_cs_nw<T, 2>(SSD_CS_ARGS);
-    default: return launch_cs_nw<T, 1>(SSD_CS_ARGS);
+    case 4: return launch_cs_nw<T, 4, S3>(SSD_CS_ARGS);
+    case 2: return launch_cs_nw<T, 2, S3>(SSD_CS_ARGS);
+    default: return launch_cs_nw<T, 1, S3>(SSD_CS_ARGS);
   }
 #undef SSD_CS_ARGS
 }
@@ -544,6 +595,18 @@ hipError_t launch_chunk_state(int io_bf16, const void* x, const void* Bm, float*
                              fold, stream);
   return launch_cs_t<float>(kh, x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, frag_major,
                             fold, stream);
+}
+
+// The backward pass's states from bf16 inputs: S in fp32 from the exact x and
+// B values with the three-part split of the weighted x (S3 above); plain
+// [B, H, T, P, N] layout, G and w rows given.
+hipError_t launch_chunk_state_split(const void* x, const void* Bm, float* Gw, float* dtw,
+                                    float* S, int64_t batch, int64_t L, int64_t H, int64_t P,
+                                    int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw, int kh,
+                                    hipStream_t stream) {
+  CsFold fold{nullptr, nullptr, DtXform{nullptr, 0, 0.0f, 0.0f}, 0, 0};
+  return launch_cs_t<bf16, true>(kh, x, Bm, Gw, dtw, S, batch, L, H, P, N, G, Q, T_, ldw, 0, fold,
+                                 stream);
 }
 
 }  // namespace ssd

@@ -60,7 +60,10 @@ int compute_out_default_kh(int io_bf16, int64_t H, int64_t G, int64_t N);
 int chunk_state_default_kh(int64_t H, int64_t G);
 int bwd_block_rows(int io_bf16, int Q, int64_t P, int64_t N);
 int64_t bwd_chunk_slots(int io_bf16, int64_t P, int64_t N);
-hipError_t launch_bwd_widen(const void* src, float* dst, int64_t n, hipStream_t stream);
+hipError_t launch_chunk_state_split(const void* x, const void* Bm, float* Gw, float* dtw,
+                                    float* S, int64_t batch, int64_t L, int64_t H, int64_t P,
+                                    int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw, int kh,
+                                    hipStream_t stream);
 hipError_t launch_bwd_prep(const float* Gw, float* w2, float* Gz, int64_t batch, int64_t H,
                            int64_t L, int64_t ldw, hipStream_t stream);
 hipError_t launch_bwd_chunks(int io_bf16, int TB, const void* x, const void* Bm, const void* Cm,
@@ -303,7 +306,7 @@ size_t config_bytes(const Plan& pl, const ssd_config& c) {
 // bf16 io, fp32 copies of x, dy, B and C for the fp32 state stages.
 struct BwdPlan {
   size_t g_off, dt_off, gz_off, w2_off, pb_off, qb_off, hc_off, lam_off, fin_off, dap_off,
-      dbp_off, ddp_off, b32_off, c32_off, acb_off, acc_off, big_off, dbh_off, dch_off, bytes;
+      dbp_off, ddp_off, acb_off, acc_off, dbh_off, dch_off, bytes;
   int TB;
   int hb;    // heads per batch of the chunk kernels (their dB/dC parts are rows of hb heads)
 };
@@ -311,18 +314,14 @@ struct BwdPlan {
 // Workspace of the backward pass for batches of hb heads.  The per-head fp32
 // dB/dC parts are the largest item (2 x B L H N floats); they are produced
 // for hb heads at a time and folded into running per-group sums after each
-// batch, so only one batch's parts exist at a time.  For bf16 io they share
-// one region with the fp32 copies of x and then dy, which are dead once the
-// two chunk_state launches have read them.
+// batch, so only one batch's parts exist at a time.
 BwdPlan bwd_plan(const Plan& pl, int64_t hb) {
   BwdPlan w;
   const size_t tok = align256(size_t(pl.B) * pl.H * pl.Lp * sizeof(float));
   const size_t st = align256(size_t(pl.B) * pl.H * pl.T * pl.P * pl.N * sizeof(float));
-  const size_t xs = size_t(pl.B) * pl.L * pl.H * pl.P * sizeof(float);
   const size_t head_parts = size_t(pl.B) * pl.L * pl.N * sizeof(float);   // one head, one of dB/dC
   w.hb = (int)hb;
   const size_t parts = align256(head_parts * size_t(hb));
-  const size_t bs = pl.bf16 ? align256(size_t(pl.B) * pl.L * pl.G * pl.N * sizeof(float)) : 0;
   const size_t acc = hb < pl.H ? align256(size_t(pl.B) * pl.L * pl.G * pl.N * sizeof(float)) : 0;
   size_t o = 0;
   w.g_off = o; o += tok;
@@ -337,14 +336,10 @@ BwdPlan bwd_plan(const Plan& pl, int64_t hb) {
   w.dap_off = o; o += align256(size_t(pl.B) * pl.H * sizeof(double));
   w.dbp_off = o; o += align256(size_t(pl.B) * pl.H * sizeof(double));
   w.ddp_off = o; o += align256(size_t(pl.B) * pl.T * pl.H * sizeof(float));
-  w.b32_off = o; o += bs;
-  w.c32_off = o; o += bs;
   w.acb_off = o; o += acc;
   w.acc_off = o; o += acc;
-  w.big_off = o;
-  w.dbh_off = o;
-  w.dch_off = o + parts;
-  o += std::max(pl.bf16 ? align256(xs) : size_t(0), 2 * parts);
+  w.dbh_off = o; o += parts;
+  w.dch_off = o; o += parts;
   w.bytes = o;
   w.TB = ssd::bwd_block_rows(pl.bf16, (int)pl.Q, pl.P, pl.N);
   return w;
@@ -358,8 +353,8 @@ int64_t balanced_heads(int64_t H, int64_t cap) {
 }
 
 // The default plan (ssd_bwd_workspace_size): all heads in one batch when
-// their dB/dC parts take no more room than one fp32 copy of x (2 N <= P);
-// otherwise the head count whose parts fit that room, but at least enough
+// their dB/dC parts take no more room than an fp32 copy of x would (2 N <=
+// P); otherwise the head count whose parts fit that room, but at least enough
 // heads for ~1024 workgroups per chunk-kernel launch.
 BwdPlan bwd_default_plan(const Plan& pl) {
   int64_t hb = pl.H;
@@ -1009,46 +1004,30 @@ ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const v
     const ssd::DtXform* xfp = dtx ? &xf : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const ssd_config cfg = default_config(pl);
-    // fp32 operands of the state stages (the io tensors themselves for fp32
-    // io); for bf16 io, x and then dy are widened into one region, which the
-    // dB/dC parts reuse once the two chunk_state launches have read it
-    const int64_t nx = pl.B * pl.L * pl.H * pl.P;
-    const void* x32 = x;
-    const void* dy32 = dy;
-    const void* B32 = B;
-    const void* C32 = C;
-    if (pl.bf16) {
-      const int64_t nb = pl.B * pl.L * pl.G * pl.N;
-      x32 = ws + w.big_off;
-      dy32 = ws + w.big_off;
-      B32 = ws + w.b32_off;
-      C32 = ws + w.c32_off;
-      hipError_t e = ssd::launch_bwd_widen(x, (float*)x32, nx, s);
-      if (e == hipSuccess) e = ssd::launch_bwd_widen(B, (float*)B32, nb, s);
-      if (e == hipSuccess) e = ssd::launch_bwd_widen(C, (float*)C32, nb, s);
-      if (e != hipSuccess) return hip_status(e, "bwd_widen launch");
-    }
     // forward stages: running sums, prepared step sizes, chunk-start states
     hipError_t e = ssd::launch_chunk_cumsum(dt, A, Gw, dtw, pl.B, pl.L, pl.H, (int)pl.Q, pl.Lp,
                                             pl.Lp, xfp, kCumsumHeads, s);
     if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
-    e = ssd::launch_chunk_state(0, x32, B32, Gw, dtw, Hc, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
-                                (int)pl.Q, pl.T, pl.Lp, 0, cfg.state_heads, nullptr, nullptr,
-                                nullptr, s);
+    // fp32 states from the io values: for bf16 io the chunk contributions are
+    // formed from the exact bf16 inputs with the weighted x split into three
+    // bf16 parts (~24 significant bits); for fp32 io on the fp32 MFMA
+    auto states = [&](const void* a, const void* bm, float* g, float* wt, void* out) {
+      return pl.bf16 ? ssd::launch_chunk_state_split(a, bm, g, wt, static_cast<float*>(out), pl.B,
+                                                     pl.L, pl.H, pl.P, pl.N, pl.G, (int)pl.Q,
+                                                     pl.T, pl.Lp, cfg.state_heads, s)
+                     : ssd::launch_chunk_state(0, a, bm, g, wt, out, pl.B, pl.L, pl.H, pl.P,
+                                               pl.N, pl.G, (int)pl.Q, pl.T, pl.Lp, 0,
+                                               cfg.state_heads, nullptr, nullptr, nullptr, s);
+    };
+    e = states(x, B, Gw, dtw, Hc);
     if (e != hipSuccess) return hip_status(e, "chunk_state launch");
     e = ssd::launch_state_pass(0, Hc, Gw, init_state, dfinal ? fin : nullptr, pl.B, pl.H,
                                pl.P, pl.N, (int)pl.Q, pl.T, pl.Lp, 0, 0, s);
     if (e != hipSuccess) return hip_status(e, "state_pass launch");
-    if (pl.bf16) {
-      e = ssd::launch_bwd_widen(dy, (float*)dy32, nx, s);     // over the dead x copy
-      if (e != hipSuccess) return hip_status(e, "bwd_widen launch");
-    }
     // gradients of the chunk-boundary states: the same two stages run backwards
     e = ssd::launch_bwd_prep(Gw, w2, Gz, pl.B, pl.H, pl.L, pl.Lp, s);
     if (e != hipSuccess) return hip_status(e, "bwd_prep launch");
-    e = ssd::launch_chunk_state(0, dy32, C32, Gz, w2, Lam, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G,
-                                (int)pl.Q, pl.T, pl.Lp, 0, cfg.state_heads, nullptr, nullptr,
-                                nullptr, s);
+    e = states(dy, C, Gz, w2, Lam);
     if (e != hipSuccess) return hip_status(e, "chunk_state (reverse) launch");
     e = ssd::launch_state_pass(0, Lam, Gw, dfinal, dinit, pl.B, pl.H, pl.P, pl.N, (int)pl.Q,
                                pl.T, pl.Lp, 0, 1, s);

@@ -3,10 +3,9 @@
 bwd_layout(p, hb) is the byte count ssd_bwd's workspace takes when it forms
 the per-head dB/dC partial gradients for batches of hb heads: token rows (6
 fp32 [batch, H, T*Q] arrays), two fp32 state sets, the final state, the
-scalar parts, (bf16 io) fp32 copies of B and C, (more than one batch of
-heads) two fp32 [batch, L, G, N] running sums, and one region for the larger
-of one fp32 copy of x (bf16 io: x, then dy) and the dB/dC parts of hb heads;
-each piece 256-byte aligned.  `p` is an ssd_problem (io_dtype 1 = bf16).
+scalar parts, (more than one batch of heads) two fp32 [batch, L, G, N]
+running sums, and the dB/dC parts of hb heads; each piece 256-byte aligned.
+`p` is an ssd_problem (io_dtype 1 = bf16).
 """
 
 
@@ -17,12 +16,10 @@ def _a(v):
 def bwd_layout(p, hb):
     Bt, L, H, Pd, N, Q, G = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.chunk_size, p.ngroups
     T = -(-L // Q)
-    bf = p.io_dtype == 1
     fixed = (6 * _a(Bt * H * T * Q * 4) + 2 * _a(Bt * H * T * Pd * N * 4) + _a(Bt * H * Pd * N * 4) +
-             2 * _a(Bt * H * 8) + _a(Bt * T * H * 4) + (2 * _a(Bt * L * G * N * 4) if bf else 0))
+             2 * _a(Bt * H * 8) + _a(Bt * T * H * 4))
     acc = 2 * _a(Bt * L * G * N * 4) if hb < H else 0
-    big = max(_a(Bt * L * H * Pd * 4) if bf else 0, 2 * _a(Bt * L * hb * N * 4))
-    return fixed + acc + big
+    return fixed + acc + 2 * _a(Bt * L * hb * N * 4)
 
 
 def balanced(H, cap):
