@@ -70,21 +70,80 @@ __host__ __device__ inline int bwd_pair_bytes(int P, int N) {   // two io tiles:
   return kBwdTB * (tile_ld<T>(N) + tile_ld<T>(P)) * (int)sizeof(T);
 }
 
-// rows x K io elements (rows `row_stride` apart) into an LDS tile of row
-// stride ld, as 16-byte pieces; rows at or past `rows_valid` and the columns
-// from K to the next multiple of 32 are zero.
-template <typename T>
-__device__ __forceinline__ void tile_to_lds(T* dst, int ld, const T* src, int64_t row_stride,
-                                            int rows_valid, int rows, int K) {
-  constexpr int V = 16 / sizeof(T);
-  const int KC = round32(K) / V;
-  for (int e = threadIdx.x; e < rows * KC; e += kBwdThreads) {
-    const int r = e / KC, c = (e % KC) * V;
-    vec16 v = zero16();
-    if (r < rows_valid && c < K) v = load16(src + r * row_stride + c);
-    store16(dst + r * ld + c, v);
-  }
+// A block's worth of 16-byte pieces per thread, loaded into registers before
+// any is written to LDS: every load of a tile is in flight at once, where a
+// loop of load-then-write pays one memory latency per piece.  MAXP bounds the
+// pieces of one thread (the tile's widest K is known at compile time).  The
+// thread index is taken as redefined at every call, so that each piece's
+// offsets are computed where they are used rather than hoisted out of the
+// block loops and kept live (which spills).
+__device__ __forceinline__ int fresh_tid() {
+  int v = threadIdx.x;
+  __asm__ __volatile__("" : "+v"(v));
+  return v;
 }
+
+// kBwdTB rows x K io elements (rows `row_stride` apart), K <= KMAX, in
+// registers; rows at or past `rows_valid` and the columns from K to the next
+// multiple of 32 are zero.
+template <int KMAX, typename T>
+struct IoTile {
+  static constexpr int V = 16 / sizeof(T);
+  static constexpr int MAXP = (kBwdTB * KMAX / V + kBwdThreads - 1) / kBwdThreads;
+  vec16 v[MAXP];
+  __device__ __forceinline__ void load(const T* src, int64_t row_stride, int rows_valid, int K) {
+    const int KC = round32(K) / V, t = fresh_tid();
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) {
+      const int e = t + k * kBwdThreads, r = e / KC, c = (e % KC) * V;
+      v[k] = zero16();
+      if (e < kBwdTB * KC && r < rows_valid && c < K) v[k] = load16(src + r * row_stride + c);
+    }
+  }
+  // into an LDS tile of row stride ld
+  __device__ __forceinline__ void store(T* dst, int ld, int K) const {
+    const int KC = round32(K) / V, t = fresh_tid();
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) {
+      const int e = t + k * kBwdThreads, r = e / KC, c = (e % KC) * V;
+      if (e < kBwdTB * KC) store16(dst + r * ld + c, v[k]);
+    }
+  }
+};
+
+// 32 fp32 state rows (row r at src + r N, N <= NMAX values, N a multiple of
+// 4) in registers; rows at or past `rows_valid` and the columns from N to NR
+// are zero.
+template <int NMAX>
+struct StateRows {
+  static constexpr int MAXP = (32 * NMAX / 4 + kBwdThreads - 1) / kBwdThreads;
+  float4 v[MAXP];
+  __device__ __forceinline__ void load(const float* src, int rows_valid, int N, int NR) {
+    const int KC = NR / 4, t = fresh_tid();
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) {
+      const int e = t + k * kBwdThreads, r = e / KC, c = (e % KC) * 4;
+      v[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (e < 32 * KC && r < rows_valid && c < N)
+        v[k] = *reinterpret_cast<const float4*>(src + (int64_t)r * N + c);
+    }
+  }
+  // into LDS rows of `lds` floats (padded strides: four scalar writes)
+  __device__ __forceinline__ void store(float* dst, int lds, int NR) const {
+    const int KC = NR / 4, t = fresh_tid();
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) {
+      const int e = t + k * kBwdThreads, r = e / KC, c = (e % KC) * 4;
+      if (e < 32 * KC) {
+        float* d = dst + r * lds + c;
+        d[0] = v[k].x;
+        d[1] = v[k].y;
+        d[2] = v[k].z;
+        d[3] = v[k].w;
+      }
+    }
+  }
+};
 
 __device__ __forceinline__ float sum16(float v) {   // over aligned groups of 16 lanes
 #pragma unroll
@@ -156,8 +215,8 @@ __device__ __forceinline__ floatx8 frag32(const float* p) { return load_frag(p);
 template <typename T, int NKN, int NKP>
 constexpr int bwd_min_waves() { return sizeof(T) == 2 && NKN <= 8 && NKP <= 4 ? 4 : 1; }
 
-template <typename T, int NKN>
-__global__ void __launch_bounds__(kBwdThreads, (bwd_min_waves<T, NKN, 4>()))
+template <typename T, int NKN, int NKP>
+__global__ void __launch_bounds__(kBwdThreads, (bwd_min_waves<T, NKN, NKP>()))
 bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
                   const T* __restrict__ dy, const float* __restrict__ Gw,
                   const float* __restrict__ dtw, const float* __restrict__ Hc,
@@ -198,12 +257,19 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
     const int64_t ti0 = (int64_t)c * Q + I * TB;
     const int vi = valid_rows(L, ti0, TB);
     if (vi == 0) break;                       // the rest of the chunk is padding
-    __syncthreads();
-    tile_to_lds(Ct, ldN, Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, TB, N);
-    tile_to_lds(gt, ldP, dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, TB, P);
-    if (tid < TB) {
-      Gi[tid] = Grow[I * TB + tid];
-      Pacc[tid] = 0.0f;
+    {
+      const float gi = tid < TB ? Grow[I * TB + tid] : 0.0f;
+      IoTile<16 * NKN, T> tc;
+      IoTile<16 * NKP, T> tg;
+      tc.load(Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, N);
+      tg.load(dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, P);
+      __syncthreads();
+      tc.store(Ct, ldN, N);
+      tg.store(gt, ldP, P);
+      if (tid < TB) {
+        Gi[tid] = gi;
+        Pacc[tid] = 0.0f;
+      }
     }
     floatx4 dc[NT];
 #pragma unroll
@@ -211,16 +277,23 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
     for (int J = 0; J <= I; ++J) {
       const int64_t tj0 = (int64_t)c * Q + J * TB;
       const int vj = valid_rows(L, tj0, TB);
-      __syncthreads();
-      tile_to_lds(Bt, ldN, Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, TB, N);
-      tile_to_lds(xt, ldP, x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, TB, P);
-      if (tid < TB) Gj[tid] = Grow[J * TB + tid];
+      const int j = 16 * tj2 + l16;
+      const float dj = drow[J * TB + j];
+      {
+        const float gj = tid < TB ? Grow[J * TB + tid] : 0.0f;
+        IoTile<16 * NKN, T> tb;
+        IoTile<16 * NKP, T> tx;
+        tb.load(Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, N);
+        tx.load(x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, P);
+        __syncthreads();
+        tb.store(Bt, ldN, N);
+        tx.store(xt, ldP, P);
+        if (tid < TB) Gj[tid] = gj;
+      }
       __syncthreads();
       // this wave's tile: rows i = 16 ti2 + 4 (lane / 16) + r, column j = 16 tj2 + lane % 16
       const floatx4 cb = tile_dot(Ct + 16 * ti2 * ldN, Bt + 16 * tj2 * ldN, ldN, NR, lane);
       const floatx4 gx = tile_dot(gt + 16 * ti2 * ldP, xt + 16 * tj2 * ldP, ldP, PR, lane);
-      const int j = 16 * tj2 + l16;
-      const float dj = drow[J * TB + j];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ti2 + 4 * g4 + r;
@@ -267,10 +340,11 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 #pragma unroll
     for (int q = 0; q < NT; ++q) hc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int p0 = 0; p0 < P; p0 += 32) {
-      __syncthreads();
-      for (int e = tid; e < 32 * N; e += kBwdThreads) {
-        const int pr = e / N;
-        Hs[pr * (N + 1) + e % N] = p0 + pr < P ? Hrow[(int64_t)p0 * N + e] : 0.0f;
+      {
+        StateRows<16 * NKN> hs;
+        hs.load(Hrow + (int64_t)p0 * N, P - p0, N, N);
+        __syncthreads();
+        hs.store(Hs, N + 1, N);
       }
       __syncthreads();
       const floatx8 a = frag32(gt + (16 * ib + l16) * ldP + p0 + 8 * g4);
@@ -381,13 +455,21 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
     const int64_t tj0 = (int64_t)c * Q + J * TB;
     const int vj = valid_rows(L, tj0, TB);
     if (vj == 0) break;
-    __syncthreads();
-    tile_to_lds(Bt, ldN, Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, TB, N);
-    tile_to_lds(xt, ldP, x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, TB, P);
-    if (tid < TB) {
-      Gj[tid] = Grow[J * TB + tid];
-      dj[tid] = drow[J * TB + tid];
-      Qacc[tid] = 0.0f;
+    {
+      const float gj = tid < TB ? Grow[J * TB + tid] : 0.0f;
+      const float dv = tid < TB ? drow[J * TB + tid] : 0.0f;
+      IoTile<16 * NKN, T> tb;
+      IoTile<16 * NKP, T> tx;
+      tb.load(Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, N);
+      tx.load(x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, P);
+      __syncthreads();
+      tb.store(Bt, ldN, N);
+      tx.store(xt, ldP, P);
+      if (tid < TB) {
+        Gj[tid] = gj;
+        dj[tid] = dv;
+        Qacc[tid] = 0.0f;
+      }
     }
     floatx4 dba[NT], dxa[PT];
 #pragma unroll
@@ -398,10 +480,17 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       const int64_t ti0 = (int64_t)c * Q + I * TB;
       const int vi = valid_rows(L, ti0, TB);
       if (vi == 0) break;
-      __syncthreads();
-      tile_to_lds(Ct, ldN, Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, TB, N);
-      tile_to_lds(gt, ldP, dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, TB, P);
-      if (tid < TB) Gi[tid] = Grow[I * TB + tid];
+      {
+        const float gi = tid < TB ? Grow[I * TB + tid] : 0.0f;
+        IoTile<16 * NKN, T> tc;
+        IoTile<16 * NKP, T> tg;
+        tc.load(Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, N);
+        tg.load(dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, P);
+        __syncthreads();
+        tc.store(Ct, ldN, N);
+        tg.store(gt, ldP, P);
+        if (tid < TB) Gi[tid] = gi;
+      }
       __syncthreads();
       // this wave's tile: rows j = 16 tj2 + 4 (lane / 16) + r, column i = 16 ti2 + lane % 16
       const floatx4 cb = tile_dot(Bt + 16 * tj2 * ldN, Ct + 16 * ti2 * ldN, ldN, NR, lane);
@@ -475,10 +564,11 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
     const float erow = fast_exp2(Gl - Gj[16 * jb + l16]);
     float qx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int p0 = 0; p0 < P; p0 += 32) {
-      __syncthreads();
-      for (int e = tid; e < 32 * NR; e += kBwdThreads) {
-        const int pr = e / NR, n = e % NR;
-        Ls[pr * lsN + n] = (p0 + pr < P && n < N) ? Lrow[(int64_t)(p0 + pr) * N + n] : 0.0f;
+      {
+        StateRows<16 * NKN> ls;
+        ls.load(Lrow + (int64_t)p0 * N, P - p0, N, NR);
+        __syncthreads();
+        ls.store(Ls, lsN, NR);
       }
       __syncthreads();
       // dx tile (rows j, columns p = p0 + 16 nh + lane % 16) += e_j sum_n B[j][n] L[p][n]
@@ -744,11 +834,11 @@ static int64_t chunk_slots_of(int64_t P, int64_t N) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  if (ensure_dyn_lds<bwd_target_kernel<T, NKN>>(bwd_target_bytes<T>((int)P, (int)N)) != hipSuccess ||
+  if (ensure_dyn_lds<bwd_target_kernel<T, NKN, NKP>>(bwd_target_bytes<T>((int)P, (int)N)) != hipSuccess ||
       ensure_dyn_lds<bwd_source_kernel<T, NKN, NKP>>(bwd_source_bytes<T>((int)P, (int)N)) !=
           hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, bwd_target_kernel<T, NKN>, kBwdThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, bwd_target_kernel<T, NKN, NKP>, kBwdThreads,
                                                    bwd_target_bytes<T>((int)P, (int)N)) !=
           hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, bwd_source_kernel<T, NKN, NKP>,
@@ -786,13 +876,13 @@ static hipError_t launch_chunks(const void* x, const void* Bm, const void* Cm, c
                                 int h0, int nb, int hb, hipStream_t stream) {
   const int ta = bwd_target_bytes<T>((int)P, (int)N);
   const int sb = bwd_source_bytes<T>((int)P, (int)N);
-  hipError_t e = ensure_dyn_lds<bwd_target_kernel<T, NKN>>(ta);
+  hipError_t e = ensure_dyn_lds<bwd_target_kernel<T, NKN, NKP>>(ta);
   if (e != hipSuccess) return e;
   e = ensure_dyn_lds<bwd_source_kernel<T, NKN, NKP>>(sb);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)T_, (unsigned)nb, (unsigned)batch);
   const int hpg = (int)(H / G);
-  hipLaunchKernelGGL((bwd_target_kernel<T, NKN>), grid, dim3(kBwdThreads), ta, stream,
+  hipLaunchKernelGGL((bwd_target_kernel<T, NKN, NKP>), grid, dim3(kBwdThreads), ta, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm),
                      static_cast<const T*>(Cm), static_cast<const T*>(dy), Gw, dtw,
                      static_cast<const float*>(Hc), Pb, dCh, L, (int)H, (int)P, (int)N, (int)G,
