@@ -145,9 +145,49 @@ struct StateRows {
   }
 };
 
-__device__ __forceinline__ float sum16(float v) {   // over aligned groups of 16 lanes
+// Output rows staged in LDS: 32 fp32 rows of K values (K a multiple of 16),
+// row stride K.  When a row holds a multiple of 16 four-value pieces, piece c
+// of row r sits at c ^ 4 ((r >> 2) & 3): the four row groups of an MFMA
+// accumulator (lanes 16 g .. 16 g + 15 hold rows 4 g + r of 16 columns) then
+// write to four different 16-bank groups, and a row reads back as whole
+// 16-byte pieces.
+__device__ __forceinline__ int stage_at(int r, int col, int K) {
+  const int sw = ((K / 4) & 15) == 0 ? 4 * ((r >> 2) & 3) : 0;
+  return r * K + (((col >> 2) ^ sw) << 2) + (col & 3);
+}
+
+// The first rows_valid staged rows to global rows `row_stride` floats apart,
+// as 16-byte pieces (K <= KMAX).
+template <int KMAX>
+__device__ __forceinline__ void stage_to_global(float* dst, int64_t row_stride, const float* st,
+                                                int K, int rows_valid) {
+  constexpr int MAXP = (32 * KMAX / 4 + kBwdThreads - 1) / kBwdThreads;
+  const int KC = K / 4, t = fresh_tid();
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  for (int k = 0; k < MAXP; ++k) {
+    const int e = t + k * kBwdThreads, r = e / KC, c = e % KC;
+    if (e < 32 * KC && r < rows_valid)
+      *reinterpret_cast<float4*>(dst + r * row_stride + 4 * c) =
+          *reinterpret_cast<const float4*>(st + stage_at(r, 4 * c, K));
+  }
+}
+
+// 16 bytes of io values
+template <typename T>
+struct Piece16 {
+  T v[16 / sizeof(T)];
+};
+
+// Sum over aligned groups of 16 lanes on DPP moves (no LDS round trips): the
+// partners at lane xor 1 and xor 2 of each quad, then the mirrored lane of
+// each half row (i <-> 7 - i: the other quad) and of the row (i <-> 15 - i:
+// the other half).  Each step adds two equal partial sums in either order, so
+// every lane of the group ends with the same total.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_src<0xB1, 0xf>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_src<0x4E, 0xf>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_src<0x141, 0xf>(v);   // row_half_mirror
+  v += dpp_src<0x140, 0xf>(v);   // row_mirror
   return v;
 }
 
@@ -230,7 +270,9 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
   const int64_t b = blockIdx.z;
   const int g = h / hpg;
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, wv = tid / kWave, ti2 = wv >> 1, tj2 = wv & 1;
+  // the wave index as a scalar: per-wave tile choices become uniform branches
+  const int lane = tid % kWave, wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int ti2 = wv >> 1, tj2 = wv & 1;
   const int l16 = lane & 15, g4 = lane >> 4;
   // second-stage ownership: rows 16 ib .. +15, column tiles nh, nh + 2, ...
   const int ib = wv & 1, nh = wv >> 1;
@@ -376,17 +418,24 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       }
       pc[r] = sum16(pc[r]);
       if (l16 == 0) Pc[nh * TB + i] = pc[r];
-      if (i < vi) {
-        float* dst = dCh + ((b * L + ti0 + i) * hb + (h - h0)) * (int64_t)N + l16;
+    }
+    // the block's dC rows through LDS where the state rows were, then out as
+    // whole-row pieces
+    __syncthreads();
+    float* Ds = reinterpret_cast<float*>(U);
 #pragma unroll
-        for (int q = 0; q < NT; ++q) {
-          const int nt = nh + 2 * q;
-          if (nt < ntiles) dst[16 * nt] = dc[q][r];
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ib + 4 * g4 + r;
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        const int nt = nh + 2 * q;
+        if (nt < ntiles) Ds[stage_at(i, 16 * nt + l16, N)] = dc[q][r];
       }
     }
     __syncthreads();
     if (tid < vi) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + tid] = Pacc[tid] + Pc[tid] + Pc[TB + tid];
+    stage_to_global<16 * NKN>(dCh + ((b * L + ti0) * hb + (h - h0)) * (int64_t)N, (int64_t)hb * N,
+                              Ds, N, vi);
   }
 }
 
@@ -421,7 +470,9 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
   const int64_t b = blockIdx.z;
   const int g = h / hpg;
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, wv = tid / kWave, tj2 = wv >> 1, ti2 = wv & 1;
+  // the wave index as a scalar: per-wave tile choices become uniform branches
+  const int lane = tid % kWave, wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int tj2 = wv >> 1, ti2 = wv & 1;
   const int l16 = lane & 15, g4 = lane >> 4;
   // second-stage ownership: rows j = 16 jb .. +15, column tiles nh, nh + 2, ...
   const int jb = wv & 1, nh = wv >> 1;
@@ -614,28 +665,68 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       const int j = 16 * jb + 4 * g4 + r;
       const float qs = sum16(qx[r]);
       if (l16 == 0) Qc[nh * TB + j] = qs;
-      if (j < vj) {
-        const float d = dj[j];
-        const int64_t row = (b * L + tj0 + j) * H + h;
+    }
+    // the block's dB rows through LDS where the state rows were, and dx 64
+    // columns at a time where the pair weights were (U and V: 32 x 72
+    // floats), then out as whole-row pieces; dx = dt_j dxa + D dy with dy
+    // read as row pieces alongside, which also gives the dD share
+    __syncthreads();
+    float* Ds = reinterpret_cast<float*>(U);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * jb + 4 * g4 + r;
+      const float d = dj[j];
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        const int nt = nh + 2 * q;
+        if (nt < ntn) Ds[stage_at(j, 16 * nt + l16, N)] = d * dba[q][r];
+      }
+    }
+    float* Xs = Us;
+    for (int pg = 0; 64 * pg < P; ++pg) {
+      if (pg > 0) __syncthreads();                 // the previous group is out
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jb + 4 * g4 + r;
 #pragma unroll
         for (int q = 0; q < PT; ++q) {
           const int pt = nh + 2 * q;
-          if (pt < ntp) {
-            const int p = 16 * pt + l16;
-            const float gv = to_f32(dy[row * P + p]);
-            dx[row * P + p] = to_io<T>(fmaf(d, dxa[q][r], Dh * gv));
-            dsum = fmaf(gv, to_f32(xt[j * ldP + p]), dsum);
-          }
+          if (pt < ntp && pt / 4 == pg) Xs[stage_at(j, 16 * pt + l16 - 64 * pg, 64)] = dxa[q][r];
         }
+      }
+      __syncthreads();
+      if (pg == 0) {
+        if (tid < vj) Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + tid] = Qacc[tid] + Qc[tid] + Qc[TB + tid];
+        stage_to_global<16 * NKN>(dBh + ((b * L + tj0) * hb + (h - h0)) * (int64_t)N,
+                                  (int64_t)hb * N, Ds, N, vj);
+      }
+      // dx pieces of V values: columns 64 pg .. 64 pg + W - 1 of rows j < vj
+      constexpr int V = 16 / sizeof(T), MAXP = (32 * 64 / V + kBwdThreads - 1) / kBwdThreads;
+      const int W = P - 64 * pg < 64 ? P - 64 * pg : 64, KC = W / V, t = fresh_tid();
 #pragma unroll
-        for (int q = 0; q < NT; ++q) {
-          const int nt = nh + 2 * q;
-          if (nt < ntn) dBh[((b * L + tj0 + j) * hb + (h - h0)) * N + 16 * nt + l16] = d * dba[q][r];
+      for (int k = 0; k < MAXP; ++k) {
+        const int e = t + k * kBwdThreads, r = e / KC, col = (e % KC) * V;
+        if (e < 32 * KC && r < vj) {
+          const int64_t off = ((b * L + tj0 + r) * H + h) * P + 64 * pg + col;
+          const Piece16<T> gv = __builtin_bit_cast(Piece16<T>, load16(dy + off));
+          const Piece16<T> xv = __builtin_bit_cast(Piece16<T>, load16(xt + r * ldP + 64 * pg + col));
+          const float d = dj[r];
+          Piece16<T> o;
+#pragma unroll
+          for (int v4 = 0; v4 < V; v4 += 4) {
+            const float4 s = *reinterpret_cast<const float4*>(Xs + stage_at(r, col + v4, 64));
+            const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float g = to_f32(gv.v[v4 + u]);
+              o.v[v4 + u] = to_io<T>(fmaf(d, sv[u], Dh * g));
+              dsum = fmaf(g, to_f32(xv.v[v4 + u]), dsum);
+            }
+          }
+          store16(dx + off, __builtin_bit_cast(vec16, o));
         }
       }
     }
-    __syncthreads();
-    if (tid < vj) Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + tid] = Qacc[tid] + Qc[tid] + Qc[TB + tid];
   }
   // the chunk's share of dD = sum <dy, x>
 #pragma unroll
