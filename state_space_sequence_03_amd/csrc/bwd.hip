@@ -83,6 +83,30 @@ __device__ __forceinline__ int fresh_tid() {
   return v;
 }
 
+// Piece e of rows of KC pieces (e < 1024, KC <= 256) is row e / KC, piece
+// e % KC.  The quotient is (e m) >> 20 with m = floor(2^20 / KC) + 1: for
+// e = q KC + f, e m / 2^20 = q + f / KC + e s / (KC 2^20) with 1 <= s <= KC,
+// below q + 1 while e KC < 2^20, so it is exact here, on full-rate 24-bit
+// multiplies where a division by a run-time value costs a long sequence of
+// quarter-rate ones.  m is kernel-uniform (a scalar, computed once).
+struct PieceRows {
+  unsigned kc, m;
+  __device__ __forceinline__ explicit PieceRows(int KC) : kc((unsigned)KC), m((1u << 20) / (unsigned)KC + 1u) {}
+  __device__ __forceinline__ unsigned row(unsigned e) const { return __umul24(e, m) >> 20; }
+  __device__ __forceinline__ unsigned col(unsigned e, unsigned r) const { return e - __umul24(r, kc); }
+};
+
+// byte offsets from a base pointer: a 32-bit offset from a wave-uniform base
+// is one scalar-base memory instruction, with no 64-bit address arithmetic
+template <typename T>
+__device__ __forceinline__ const T* at_bytes(const T* base, unsigned off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
+template <typename T>
+__device__ __forceinline__ T* at_bytes(T* base, unsigned off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
 // kBwdTB rows x K io elements (rows `row_stride` apart), K <= KMAX, in
 // registers; rows at or past `rows_valid` and the columns from K to the next
 // multiple of 32 are zero.
@@ -92,21 +116,24 @@ struct IoTile {
   static constexpr int MAXP = (kBwdTB * KMAX / V + kBwdThreads - 1) / kBwdThreads;
   vec16 v[MAXP];
   __device__ __forceinline__ void load(const T* src, int64_t row_stride, int rows_valid, int K) {
-    const int KC = round32(K) / V, t = fresh_tid();
+    const PieceRows pr(round32(K) / V);
+    const unsigned t = fresh_tid(), rs = (unsigned)row_stride * sizeof(T);
 #pragma unroll
     for (int k = 0; k < MAXP; ++k) {
-      const int e = t + k * kBwdThreads, r = e / KC, c = (e % KC) * V;
+      const unsigned e = t + k * kBwdThreads, r = pr.row(e), c = pr.col(e, r) * V;
       v[k] = zero16();
-      if (e < kBwdTB * KC && r < rows_valid && c < K) v[k] = load16(src + r * row_stride + c);
+      if (e < kBwdTB * pr.kc && (int)r < rows_valid && (int)c < K)
+        v[k] = load16(at_bytes(src, r * rs + c * sizeof(T)));
     }
   }
   // into an LDS tile of row stride ld
   __device__ __forceinline__ void store(T* dst, int ld, int K) const {
-    const int KC = round32(K) / V, t = fresh_tid();
+    const PieceRows pr(round32(K) / V);
+    const unsigned t = fresh_tid();
 #pragma unroll
     for (int k = 0; k < MAXP; ++k) {
-      const int e = t + k * kBwdThreads, r = e / KC, c = (e % KC) * V;
-      if (e < kBwdTB * KC) store16(dst + r * ld + c, v[k]);
+      const unsigned e = t + k * kBwdThreads, r = pr.row(e), c = pr.col(e, r) * V;
+      if (e < kBwdTB * pr.kc) store16(dst + __umul24(r, (unsigned)ld) + c, v[k]);
     }
   }
 };
@@ -119,23 +146,25 @@ struct StateRows {
   static constexpr int MAXP = (32 * NMAX / 4 + kBwdThreads - 1) / kBwdThreads;
   float4 v[MAXP];
   __device__ __forceinline__ void load(const float* src, int rows_valid, int N, int NR) {
-    const int KC = NR / 4, t = fresh_tid();
+    const PieceRows pr(NR / 4);
+    const unsigned t = fresh_tid();
 #pragma unroll
     for (int k = 0; k < MAXP; ++k) {
-      const int e = t + k * kBwdThreads, r = e / KC, c = (e % KC) * 4;
+      const unsigned e = t + k * kBwdThreads, r = pr.row(e), c = pr.col(e, r) * 4;
       v[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (e < 32 * KC && r < rows_valid && c < N)
-        v[k] = *reinterpret_cast<const float4*>(src + (int64_t)r * N + c);
+      if (e < 32 * pr.kc && (int)r < rows_valid && (int)c < N)
+        v[k] = *at_bytes(reinterpret_cast<const float4*>(src), (__umul24(r, (unsigned)N) + c) * 4);
     }
   }
   // into LDS rows of `lds` floats (padded strides: four scalar writes)
   __device__ __forceinline__ void store(float* dst, int lds, int NR) const {
-    const int KC = NR / 4, t = fresh_tid();
+    const PieceRows pr(NR / 4);
+    const unsigned t = fresh_tid();
 #pragma unroll
     for (int k = 0; k < MAXP; ++k) {
-      const int e = t + k * kBwdThreads, r = e / KC, c = (e % KC) * 4;
-      if (e < 32 * KC) {
-        float* d = dst + r * lds + c;
+      const unsigned e = t + k * kBwdThreads, r = pr.row(e), c = pr.col(e, r) * 4;
+      if (e < 32 * pr.kc) {
+        float* d = dst + __umul24(r, (unsigned)lds) + c;
         d[0] = v[k].x;
         d[1] = v[k].y;
         d[2] = v[k].z;
@@ -162,12 +191,13 @@ template <int KMAX>
 __device__ __forceinline__ void stage_to_global(float* dst, int64_t row_stride, const float* st,
                                                 int K, int rows_valid) {
   constexpr int MAXP = (32 * KMAX / 4 + kBwdThreads - 1) / kBwdThreads;
-  const int KC = K / 4, t = fresh_tid();
+  const PieceRows pr(K / 4);
+  const unsigned t = fresh_tid(), rs = (unsigned)row_stride * 4u;
 #pragma unroll
   for (int k = 0; k < MAXP; ++k) {
-    const int e = t + k * kBwdThreads, r = e / KC, c = e % KC;
-    if (e < 32 * KC && r < rows_valid)
-      *reinterpret_cast<float4*>(dst + r * row_stride + 4 * c) =
+    const unsigned e = t + k * kBwdThreads, r = pr.row(e), c = pr.col(e, r);
+    if (e < 32 * pr.kc && (int)r < rows_valid)
+      *at_bytes(reinterpret_cast<float4*>(dst), r * rs + c * 16) =
           *reinterpret_cast<const float4*>(st + stage_at(r, 4 * c, K));
   }
 }
@@ -702,14 +732,18 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       }
       // dx pieces of V values: columns 64 pg .. 64 pg + W - 1 of rows j < vj
       constexpr int V = 16 / sizeof(T), MAXP = (32 * 64 / V + kBwdThreads - 1) / kBwdThreads;
-      const int W = P - 64 * pg < 64 ? P - 64 * pg : 64, KC = W / V, t = fresh_tid();
+      const int W = P - 64 * pg < 64 ? P - 64 * pg : 64;
+      const PieceRows pr(W / V);
+      const unsigned t = fresh_tid(), rs = (unsigned)(H * P) * sizeof(T);
+      const int64_t base = ((b * L + tj0) * H + h) * P + 64 * pg;   // row 0, column 64 pg
 #pragma unroll
       for (int k = 0; k < MAXP; ++k) {
-        const int e = t + k * kBwdThreads, r = e / KC, col = (e % KC) * V;
-        if (e < 32 * KC && r < vj) {
-          const int64_t off = ((b * L + tj0 + r) * H + h) * P + 64 * pg + col;
-          const Piece16<T> gv = __builtin_bit_cast(Piece16<T>, load16(dy + off));
-          const Piece16<T> xv = __builtin_bit_cast(Piece16<T>, load16(xt + r * ldP + 64 * pg + col));
+        const unsigned e = t + k * kBwdThreads, r = pr.row(e), col = pr.col(e, r) * V;
+        if (e < 32 * pr.kc && (int)r < vj) {
+          const unsigned off = r * rs + col * sizeof(T);
+          const Piece16<T> gv = __builtin_bit_cast(Piece16<T>, load16(at_bytes(dy + base, off)));
+          const Piece16<T> xv = __builtin_bit_cast(
+              Piece16<T>, load16(xt + __umul24(r, (unsigned)ldP) + 64 * pg + col));
           const float d = dj[r];
           Piece16<T> o;
 #pragma unroll
@@ -723,7 +757,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
               dsum = fmaf(g, to_f32(xv.v[v4 + u]), dsum);
             }
           }
-          store16(dx + off, __builtin_bit_cast(vec16, o));
+          store16(at_bytes(dx + base, off), __builtin_bit_cast(vec16, o));
         }
       }
     }
