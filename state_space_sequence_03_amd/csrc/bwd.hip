@@ -107,6 +107,19 @@ __device__ __forceinline__ T* at_bytes(T* base, unsigned off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
 }
 
+// Loads through a buffer resource that spans the valid rows: a raw buffer
+// load past the resource's range returns zero, so rows past the valid ones,
+// the pieces of threads beyond the tile and (given an offset past the range)
+// the pad columns come back zero with no zero-fill or branch.
+constexpr unsigned kOutOfRange = 0x80000000u;
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ vec16 rsrc_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(vec16, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // kBwdTB rows x K io elements (rows `row_stride` apart), K <= KMAX, in
 // registers; rows at or past `rows_valid` and the columns from K to the next
 // multiple of 32 are zero.
@@ -118,12 +131,12 @@ struct IoTile {
   __device__ __forceinline__ void load(const T* src, int64_t row_stride, int rows_valid, int K) {
     const PieceRows pr(round32(K) / V);
     const unsigned t = fresh_tid(), rs = (unsigned)row_stride * sizeof(T);
+    const __amdgpu_buffer_rsrc_t rr = rows_rsrc(src, (unsigned)rows_valid * rs);
 #pragma unroll
     for (int k = 0; k < MAXP; ++k) {
       const unsigned e = t + k * kBwdThreads, r = pr.row(e), c = pr.col(e, r) * V;
-      v[k] = zero16();
-      if (e < kBwdTB * pr.kc && (int)r < rows_valid && (int)c < K)
-        v[k] = load16(at_bytes(src, r * rs + c * sizeof(T)));
+      const bool in = e < kBwdTB * pr.kc && (int)c < K;
+      v[k] = rsrc_load16(rr, in ? r * rs + c * sizeof(T) : kOutOfRange);
     }
   }
   // into an LDS tile of row stride ld
@@ -148,12 +161,12 @@ struct StateRows {
   __device__ __forceinline__ void load(const float* src, int rows_valid, int N, int NR) {
     const PieceRows pr(NR / 4);
     const unsigned t = fresh_tid();
+    const __amdgpu_buffer_rsrc_t rr = rows_rsrc(src, (unsigned)(rows_valid < 32 ? rows_valid : 32) * (unsigned)N * 4u);
 #pragma unroll
     for (int k = 0; k < MAXP; ++k) {
       const unsigned e = t + k * kBwdThreads, r = pr.row(e), c = pr.col(e, r) * 4;
-      v[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (e < 32 * pr.kc && (int)r < rows_valid && (int)c < N)
-        v[k] = *at_bytes(reinterpret_cast<const float4*>(src), (__umul24(r, (unsigned)N) + c) * 4);
+      const bool in = e < 32 * pr.kc && (int)c < N;
+      v[k] = __builtin_bit_cast(float4, rsrc_load16(rr, in ? (__umul24(r, (unsigned)N) + c) * 4 : kOutOfRange));
     }
   }
   // into LDS rows of `lds` floats (padded strides: four scalar writes)
@@ -229,12 +242,15 @@ __device__ __forceinline__ int valid_rows(int64_t L, int64_t t0, int TB) {
 // 16x16 tile of  sum_k A[row][k] B[col][k]  over K (a multiple of 32 after
 // padding) for one wave: A rows a0.., B rows b0.. of io tiles with row stride
 // ld.  The accumulator holds, in lane l, column l % 16 and rows 4 (l / 16) + r.
-template <typename T>
+// K <= KMAX: the K-steps unrolled, each under a uniform test.
+template <int KMAX, typename T>
 __device__ __forceinline__ floatx4 tile_dot(const T* A, const T* B, int ld, int K, int lane) {
   const T* pa = A + (lane & 15) * ld + 8 * (lane >> 4);
   const T* pb = B + (lane & 15) * ld + 8 * (lane >> 4);
   floatx4 c = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < K; k0 += 32) c = mma(c, load_frag(pa + k0), load_frag(pb + k0));
+#pragma unroll
+  for (int k0 = 0; k0 < KMAX; k0 += 32)
+    if (k0 < K) c = mma(c, load_frag(pa + k0), load_frag(pb + k0));
   return c;
 }
 
@@ -364,14 +380,17 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       }
       __syncthreads();
       // this wave's tile: rows i = 16 ti2 + 4 (lane / 16) + r, column j = 16 tj2 + lane % 16
-      const floatx4 cb = tile_dot(Ct + 16 * ti2 * ldN, Bt + 16 * tj2 * ldN, ldN, NR, lane);
-      const floatx4 gx = tile_dot(gt + 16 * ti2 * ldP, xt + 16 * tj2 * ldP, ldP, PR, lane);
+      const floatx4 cb = tile_dot<16 * NKN>(Ct + 16 * ti2 * ldN, Bt + 16 * tj2 * ldN, ldN, NR, lane);
+      const floatx4 gx = tile_dot<16 * NKP>(gt + 16 * ti2 * ldP, xt + 16 * tj2 * ldP, ldP, PR, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ti2 + 4 * g4 + r;
         const bool on = J < I || j <= i;
-        // the mask is applied before exp2, so no masked entry is evaluated
-        const float w = on ? fast_exp2(Gi[i] - Gj[j]) * dj * gx[r] : 0.0f;
+        // every entry is evaluated (the running sums and step sizes are finite
+        // on padding tokens too) and the masked ones selected away: a select,
+        // where a conditional LDS read would be an exec-mask branch
+        const float gi = Gi[i], gj = Gj[j];
+        const float w = on ? fast_exp2(gi - gj) * dj * gx[r] : 0.0f;
         Ws[i * ldW + j] = w;
         const float pr = sum16(w * cb[r]);
         if (l16 == 0) Pp[tj2 * TB + i] = pr;
@@ -574,14 +593,15 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       }
       __syncthreads();
       // this wave's tile: rows j = 16 tj2 + 4 (lane / 16) + r, column i = 16 ti2 + lane % 16
-      const floatx4 cb = tile_dot(Bt + 16 * tj2 * ldN, Ct + 16 * ti2 * ldN, ldN, NR, lane);
-      const floatx4 gx = tile_dot(xt + 16 * tj2 * ldP, gt + 16 * ti2 * ldP, ldP, PR, lane);
+      const floatx4 cb = tile_dot<16 * NKN>(Bt + 16 * tj2 * ldN, Ct + 16 * ti2 * ldN, ldN, NR, lane);
+      const floatx4 gx = tile_dot<16 * NKP>(xt + 16 * tj2 * ldP, gt + 16 * ti2 * ldP, ldP, PR, lane);
       const int i = 16 * ti2 + l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * tj2 + 4 * g4 + r;
         const bool on = I > J || j <= i;
-        const float a = on ? fast_exp2(Gi[i] - Gj[j]) : 0.0f;
+        const float gi = Gi[i], gj = Gj[j];     // read unconditionally: a select, not a branch
+        const float a = on ? fast_exp2(gi - gj) : 0.0f;
         const float u = a * cb[r];
         Us[j * ldW + i] = u;
         Vs[j * ldW + i] = a * gx[r];
