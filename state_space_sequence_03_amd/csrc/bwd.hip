@@ -794,6 +794,12 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 // Step-size gradients of one (b, h): the reverse running sum of P - dt Qr over
 // the whole sequence (fp64), then ddt, the (b, h) shares of dA and of the
 // bias gradient, with the step-size preparation's chain rule when XF is set.
+// The sequence is walked in blocks of 2048 tokens from its end.  Each thread
+// takes 8 contiguous tokens of a block (two 16-byte loads per array, the
+// wave's loads contiguous; past L they load zero), a suffix scan of the
+// threads' sums (within a wave on shuffles, then over the waves) gives each
+// thread the sum of every later token of the block, and a carry, started at
+// <dfinal, final state>, brings the later blocks' total.
 template <bool XF>
 __global__ void __launch_bounds__(kBwdThreads)
 bwd_dt_kernel(const float* __restrict__ Pb, const float* __restrict__ Qb,
@@ -802,11 +808,13 @@ bwd_dt_kernel(const float* __restrict__ Pb, const float* __restrict__ Qb,
               const float* __restrict__ fin, DtXform xf, float* __restrict__ ddt,
               double* __restrict__ dApart, double* __restrict__ dbpart, int64_t L, int H,
               int64_t PN, int64_t ldw) {
-  __shared__ double seg_sum[kBwdThreads];
-  __shared__ double red[2][kBwdThreads / kWave];
+  constexpr int TPT = 8, NW = kBwdThreads / kWave;
+  constexpr int BLK = kBwdThreads * TPT;
+  __shared__ double wsum[NW];
+  __shared__ double red[2][NW];
   const int h = blockIdx.x;
   const int64_t b = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int64_t bh = b * H + h;
 
   // <dfinal, final state>: every token's decay lies before the final state
@@ -815,45 +823,84 @@ bwd_dt_kernel(const float* __restrict__ Pb, const float* __restrict__ Qb,
     for (int64_t e = tid; e < PN; e += kBwdThreads) kf += (double)dfinal[bh * PN + e] * fin[bh * PN + e];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) kf += __shfl_xor(kf, off, kWave);
-  if (tid % kWave == 0) red[0][tid / kWave] = kf;
+  if (lane == 0) red[0][wv] = kf;
+  __syncthreads();
+  double carry = red[0][0] + red[0][1] + red[0][2] + red[0][3];
 
-  const int64_t seg = (L + kBwdThreads - 1) / kBwdThreads;
-  const int64_t t0 = tid * seg, t1 = t0 + seg < L ? t0 + seg : L;
-  const float* Pr = Pb + bh * ldw;
-  const float* Qr = Qb + bh * ldw;
-  const float* dr = dtw + bh * ldw;
-  double s = 0.0;
-  for (int64_t t = t0; t < t1; ++t) s += (double)Pr[t] - (double)dr[t] * Qr[t];
-  seg_sum[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    double run = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    for (int k = kBwdThreads - 1; k >= 0; --k) {   // seg_sum[k] <- K + sum over later segments
-      const double v = seg_sum[k];
-      seg_sum[k] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
   const float a = A[h];
-  double run = seg_sum[tid], da = 0.0, db = 0.0;
-  for (int64_t t = t1 - 1; t >= t0; --t) {
-    run += (double)Pr[t] - (double)dr[t] * Qr[t];
-    const float dl = (float)run;
-    float gdt = fmaf(a, dl, Qr[t]);
-    da += (double)dr[t] * run;
-    if constexpr (XF) {
-      float v = dt_in[(b * L + t) * H + h];
-      if (xf.bias) v += xf.bias[h];
-      float w = v, sig = 1.0f;
-      if (xf.softplus) {
-        w = softplus_f32(v);
-        sig = 1.0f / (1.0f + fast_exp2(-v * kLog2e));
-      }
-      gdt = (w >= xf.lo && w <= xf.hi) ? gdt * sig : 0.0f;
+  const unsigned row_bytes = (unsigned)L * 4u;
+  const __amdgpu_buffer_rsrc_t rp = rows_rsrc(Pb + bh * ldw, row_bytes);
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(Qb + bh * ldw, row_bytes);
+  const __amdgpu_buffer_rsrc_t rd = rows_rsrc(dtw + bh * ldw, row_bytes);
+  double da = 0.0, db = 0.0;
+  for (int64_t blk = (L + BLK - 1) / BLK - 1; blk >= 0; --blk) {
+    const int64_t t0 = blk * BLK + (int64_t)tid * TPT;
+    const unsigned off = (unsigned)t0 * 4u;
+    float pv[TPT], qv[TPT], dv[TPT], xv[TPT];
+#pragma unroll
+    for (int k = 0; k < TPT / 4; ++k) {
+      const float4 p4 = __builtin_bit_cast(float4, rsrc_load16(rp, off + 16 * k));
+      const float4 q4 = __builtin_bit_cast(float4, rsrc_load16(rq, off + 16 * k));
+      const float4 d4 = __builtin_bit_cast(float4, rsrc_load16(rd, off + 16 * k));
+      pv[4 * k] = p4.x; pv[4 * k + 1] = p4.y; pv[4 * k + 2] = p4.z; pv[4 * k + 3] = p4.w;
+      qv[4 * k] = q4.x; qv[4 * k + 1] = q4.y; qv[4 * k + 2] = q4.z; qv[4 * k + 3] = q4.w;
+      dv[4 * k] = d4.x; dv[4 * k + 1] = d4.y; dv[4 * k + 2] = d4.z; dv[4 * k + 3] = d4.w;
     }
-    db += gdt;
-    ddt[(b * L + t) * H + h] = gdt;
+    // a piece that straddles L is not zeroed dword by dword, and the rows
+    // hold stale values past L: tokens from L on are cleared here
+#pragma unroll
+    for (int e = 0; e < TPT; ++e)
+      if (t0 + e >= L) pv[e] = qv[e] = dv[e] = 0.0f;
+    if constexpr (XF) {
+#pragma unroll
+      for (int e = 0; e < TPT; ++e) xv[e] = t0 + e < L ? dt_in[(b * L + t0 + e) * H + h] : 0.0f;
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int e = 0; e < TPT; ++e) s += (double)pv[e] - (double)dv[e] * qv[e];
+    // inclusive sum over this lane and the later lanes of the wave
+    double inc = s;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double v = __shfl_down(inc, o, kWave);
+      if (lane + o < kWave) inc += v;
+    }
+    const double nxt = __shfl_down(inc, 1, kWave);          // every lane takes part
+    const double later_lanes = lane + 1 < kWave ? nxt : 0.0;
+    if (lane == 0) wsum[wv] = inc;
+    __syncthreads();
+    double run = carry, tot = 0.0;
+#pragma unroll
+    for (int w = NW - 1; w >= 0; --w) {
+      if (w > wv) run += wsum[w];
+      tot += wsum[w];
+    }
+    __syncthreads();                             // wsum is rewritten by the next block
+    run += later_lanes;
+    carry += tot;
+    // this thread's tokens, last first
+#pragma unroll
+    for (int e = TPT - 1; e >= 0; --e) {
+      const int64_t t = t0 + e;
+      run += (double)pv[e] - (double)dv[e] * qv[e];
+      if (t < L) {
+        const float dl = (float)run;
+        float gdt = fmaf(a, dl, qv[e]);
+        da += (double)dv[e] * run;
+        if constexpr (XF) {
+          float v = xv[e];
+          if (xf.bias) v += xf.bias[h];
+          float w = v, sig = 1.0f;
+          if (xf.softplus) {
+            w = softplus_f32(v);
+            sig = 1.0f / (1.0f + fast_exp2(-v * kLog2e));
+          }
+          gdt = (w >= xf.lo && w <= xf.hi) ? gdt * sig : 0.0f;
+        }
+        db += gdt;
+        ddt[(b * L + t) * H + h] = gdt;
+      }
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -861,9 +908,9 @@ bwd_dt_kernel(const float* __restrict__ Pb, const float* __restrict__ Qb,
     db += __shfl_xor(db, off, kWave);
   }
   __syncthreads();
-  if (tid % kWave == 0) {
-    red[0][tid / kWave] = da;
-    red[1][tid / kWave] = db;
+  if (lane == 0) {
+    red[0][wv] = da;
+    red[1][wv] = db;
   }
   __syncthreads();
   if (tid == 0) {
