@@ -57,6 +57,11 @@ constexpr int kBwdThreads = 256;
 
 constexpr int kBwdTB = 32;   // token rows per block of a chunk
 
+// Heads per workgroup of the per-chunk kernels at most: a workgroup takes a
+// "part", kh consecutive heads of one group, and sums their dB and dC
+// contributions in its accumulators, so the parts written out number H / kh.
+constexpr int kBwdPartHeadsMax = 8;
+
 // io-dtype tiles in LDS: rows of K values, K rounded up to whole 32-value MFMA
 // K-steps (zero-filled) plus 16 bytes against bank conflicts.
 __host__ __device__ inline int round32(int v) { return (v + 31) / 32 * 32; }
@@ -307,14 +312,14 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
                   const T* __restrict__ dy, const float* __restrict__ Gw,
                   const float* __restrict__ dtw, const float* __restrict__ Hc,
                   float* __restrict__ Pout, float* __restrict__ dCh, int64_t L, int H, int P,
-                  int N, int G, int hpg, int Q, int T_, int64_t ldw, int h0, int hb) {
+                  int N, int G, int hpg, int Q, int T_, int64_t ldw, int p0, int hbp, int kh) {
   constexpr int TB = kBwdTB, ldW = kBwdLdW, NT = NKN / 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  // heads h0 .. h0 + gridDim.y - 1 of this launch; their dC parts are rows
-  // of hb heads
-  const int c = blockIdx.x, h = h0 + (int)blockIdx.y;
+  // part p0 + blockIdx.y of this launch: heads part kh .. part kh + kh - 1,
+  // all of one group; the dC parts of the launch are rows of hbp parts
+  const int c = blockIdx.x, part = p0 + (int)blockIdx.y, hfirst = part * kh;
   const int64_t b = blockIdx.z;
-  const int g = h / hpg;
+  const int g = hfirst / hpg;
   const int tid = threadIdx.x;
   // the wave index as a scalar: per-wave tile choices become uniform branches
   const int lane = tid % kWave, wv = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -336,32 +341,35 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
   float* Pp = Gj + TB;          // [2][TB]: pair shares of P from the two column-half waves
   float* Pc = Pp + 2 * TB;      // [2][TB]: carried shares of P
   float* Pacc = Pc + 2 * TB;
-  const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
-  const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
-  const float* Hrow = Hc + ((b * H + h) * T_ + c) * (int64_t)P * N;
   const int nb = Q / TB, ntiles = N / 16;
 
   for (int I = 0; I < nb; ++I) {
     const int64_t ti0 = (int64_t)c * Q + I * TB;
     const int vi = valid_rows(L, ti0, TB);
     if (vi == 0) break;                       // the rest of the chunk is padding
+    // the block's dC, summed over the part's heads in ascending order
+    floatx4 dc[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) dc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int hh = 0; hh < kh; ++hh) {
+    const int h = hfirst + hh;
+    const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
+    const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
+    const float* Hrow = Hc + ((b * H + h) * T_ + c) * (int64_t)P * N;
     {
       const float gi = tid < TB ? Grow[I * TB + tid] : 0.0f;
-      IoTile<16 * NKN, T> tc;
+      IoTile<16 * NKN, T> tc;            // C rows: the same for every head of the part
       IoTile<16 * NKP, T> tg;
-      tc.load(Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, N);
+      if (hh == 0) tc.load(Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, N);
       tg.load(dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, P);
       __syncthreads();
-      tc.store(Ct, ldN, N);
+      if (hh == 0) tc.store(Ct, ldN, N);
       tg.store(gt, ldP, P);
       if (tid < TB) {
         Gi[tid] = gi;
         Pacc[tid] = 0.0f;
       }
     }
-    floatx4 dc[NT];
-#pragma unroll
-    for (int q = 0; q < NT; ++q) dc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int J = 0; J <= I; ++J) {
       const int64_t tj0 = (int64_t)c * Q + J * TB;
       const int vj = valid_rows(L, tj0, TB);
@@ -468,9 +476,11 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       pc[r] = sum16(pc[r]);
       if (l16 == 0) Pc[nh * TB + i] = pc[r];
     }
-    // the block's dC rows through LDS where the state rows were, then out as
-    // whole-row pieces
     __syncthreads();
+    if (tid < vi) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + tid] = Pacc[tid] + Pc[tid] + Pc[TB + tid];
+    }   // heads of the part
+    // the block's dC rows through LDS where the state rows were (every wave
+    // is past the last head's carried term), then out as whole-row pieces
     float* Ds = reinterpret_cast<float*>(U);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -482,9 +492,8 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       }
     }
     __syncthreads();
-    if (tid < vi) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + tid] = Pacc[tid] + Pc[tid] + Pc[TB + tid];
-    stage_to_global<16 * NKN>(dCh + ((b * L + ti0) * hb + (h - h0)) * (int64_t)N, (int64_t)hb * N,
-                              Ds, N, vi);
+    stage_to_global<16 * NKN>(dCh + ((b * L + ti0) * hbp + (part - p0)) * (int64_t)N,
+                              (int64_t)hbp * N, Ds, N, vi);
   }
 }
 
@@ -500,7 +509,8 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 template <typename T>
 __host__ __device__ inline int bwd_source_bytes(int P, int N) {
   const int pair = bwd_pair_bytes<T>(P, N), st = (32 * (round32(N) + 1) * 4 + 15) / 16 * 16;
-  return pair + (pair > st ? pair : st) + 2 * kBwdTB * kBwdLdW * 4 + 8 * kBwdTB * 4 + 8 * 4;
+  return pair + (pair > st ? pair : st) + 2 * kBwdTB * kBwdLdW * 4 + 8 * kBwdTB * 4 +
+         kBwdPartHeadsMax * (kBwdThreads / kWave) * 4;
 }
 
 template <typename T, int NKN, int NKP>
@@ -510,14 +520,14 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
                   const float* __restrict__ dtw, const float* __restrict__ Lam,
                   const float* __restrict__ Dv, T* __restrict__ dx, float* __restrict__ dBh,
                   float* __restrict__ Qout, float* __restrict__ dDpart, int64_t L, int H, int P,
-                  int N, int G, int hpg, int Q, int T_, int64_t ldw, int h0, int hb) {
+                  int N, int G, int hpg, int Q, int T_, int64_t ldw, int p0, int hbp, int kh) {
   constexpr int TB = kBwdTB, ldW = kBwdLdW, NT = NKN / 2, PT = NKP / 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  // heads h0 .. h0 + gridDim.y - 1 of this launch; their dB parts are rows
-  // of hb heads
-  const int c = blockIdx.x, h = h0 + (int)blockIdx.y;
+  // part p0 + blockIdx.y of this launch: heads part kh .. part kh + kh - 1,
+  // all of one group; the dB parts of the launch are rows of hbp parts
+  const int c = blockIdx.x, part = p0 + (int)blockIdx.y, hfirst = part * kh;
   const int64_t b = blockIdx.z;
-  const int g = h / hpg;
+  const int g = hfirst / hpg;
   const int tid = threadIdx.x;
   // the wave index as a scalar: per-wave tile choices become uniform branches
   const int lane = tid % kWave, wv = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -542,28 +552,37 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
   float* Qp = dj + TB;          // [2][TB]: pair shares of Qr from the two column-half waves
   float* Qc = Qp + 2 * TB;      // [2][TB]: carried shares of Qr
   float* Qacc = Qc + 2 * TB;
-  float* red = Qacc + TB;
-  const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
-  const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
-  const float* Lrow = Lam + ((b * H + h) * T_ + c) * (int64_t)P * N;
+  float* dDw = Qacc + TB;       // [head of the part][wave]: shares of dD
   const int nb = Q / TB, ntn = N / 16, ntp = P / 16;
-  const float Dh = Dv ? Dv[h] : 0.0f;
-  const float Gl = Grow[Q - 1];
-  float dsum = 0.0f;
+  if (lane == 0)
+    for (int hh = 0; hh < kh; ++hh) dDw[hh * (kBwdThreads / kWave) + wv] = 0.0f;
 
   for (int J = 0; J < nb; ++J) {
     const int64_t tj0 = (int64_t)c * Q + J * TB;
     const int vj = valid_rows(L, tj0, TB);
     if (vj == 0) break;
+    // the block's dB, summed over the part's heads in ascending order, each
+    // head's step sizes folded into its operands
+    floatx4 dba[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) dba[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int hh = 0; hh < kh; ++hh) {
+    const int h = hfirst + hh;
+    const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
+    const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
+    const float* Lrow = Lam + ((b * H + h) * T_ + c) * (int64_t)P * N;
+    const float Dh = Dv ? Dv[h] : 0.0f;
+    const float Gl = Grow[Q - 1];
+    float dsum = 0.0f;
     {
       const float gj = tid < TB ? Grow[J * TB + tid] : 0.0f;
       const float dv = tid < TB ? drow[J * TB + tid] : 0.0f;
-      IoTile<16 * NKN, T> tb;
+      IoTile<16 * NKN, T> tb;            // B rows: the same for every head of the part
       IoTile<16 * NKP, T> tx;
-      tb.load(Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, N);
+      if (hh == 0) tb.load(Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, N);
       tx.load(x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, P);
       __syncthreads();
-      tb.store(Bt, ldN, N);
+      if (hh == 0) tb.store(Bt, ldN, N);
       tx.store(xt, ldP, P);
       if (tid < TB) {
         Gj[tid] = gj;
@@ -571,9 +590,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         Qacc[tid] = 0.0f;
       }
     }
-    floatx4 dba[NT], dxa[PT];
-#pragma unroll
-    for (int q = 0; q < NT; ++q) dba[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    floatx4 dxa[PT];
 #pragma unroll
     for (int q = 0; q < PT; ++q) dxa[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int I = J; I < nb; ++I) {
@@ -604,7 +621,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         const float a = on ? fast_exp2(gi - gj) : 0.0f;
         const float u = a * cb[r];
         Us[j * ldW + i] = u;
-        Vs[j * ldW + i] = a * gx[r];
+        Vs[j * ldW + i] = a * gx[r] * dj[j];     // dB's weights carry dt_j
         const float q = sum16(u * gx[r]);
         if (l16 == 0) Qp[ti2 * TB + j] = q;
       }
@@ -663,6 +680,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
     // carried terms, L_{c+1} through LDS 32 state rows (p0 .. p0+31) at a time;
     // this wave's A-operand row j = 16 jb + lane % 16 carries exp2(G_last - G_j)
     const float erow = fast_exp2(Gl - Gj[16 * jb + l16]);
+    const float erow_b = erow * dj[16 * jb + l16];    // dB's rows carry dt_j too
     float qx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int p0 = 0; p0 < P; p0 += 32) {
       {
@@ -697,7 +715,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       // dB tiles (rows j, columns n) += e_j sum_{p in pass} x[j][p] L[p][n]
       floatx8 a = frag32(xt + (16 * jb + l16) * ldP + p0 + 8 * g4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] *= erow;
+      for (int e = 0; e < 8; ++e) a[e] *= erow_b;
 #pragma unroll
       for (int qq = 0; qq < NT; ++qq) {
         const int nt = nh + 2 * qq;
@@ -716,22 +734,10 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       const float qs = sum16(qx[r]);
       if (l16 == 0) Qc[nh * TB + j] = qs;
     }
-    // the block's dB rows through LDS where the state rows were, and dx 64
-    // columns at a time where the pair weights were (U and V: 32 x 72
-    // floats), then out as whole-row pieces; dx = dt_j dxa + D dy with dy
-    // read as row pieces alongside, which also gives the dD share
-    __syncthreads();
-    float* Ds = reinterpret_cast<float*>(U);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 16 * jb + 4 * g4 + r;
-      const float d = dj[j];
-#pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        const int nt = nh + 2 * q;
-        if (nt < ntn) Ds[stage_at(j, 16 * nt + l16, N)] = d * dba[q][r];
-      }
-    }
+    // this head's dx 64 columns at a time through LDS where the pair weights
+    // were (U and V: 32 x 72 floats; the last pair is behind the carried
+    // term's barriers), then out as whole-row pieces; dx = dt_j dxa + D dy
+    // with dy read as row pieces alongside, which also gives the dD share
     float* Xs = Us;
     for (int pg = 0; 64 * pg < P; ++pg) {
       if (pg > 0) __syncthreads();                 // the previous group is out
@@ -745,11 +751,8 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         }
       }
       __syncthreads();
-      if (pg == 0) {
-        if (tid < vj) Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + tid] = Qacc[tid] + Qc[tid] + Qc[TB + tid];
-        stage_to_global<16 * NKN>(dBh + ((b * L + tj0) * hb + (h - h0)) * (int64_t)N,
-                                  (int64_t)hb * N, Ds, N, vj);
-      }
+      if (pg == 0 && tid < vj)
+        Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + tid] = Qacc[tid] + Qc[tid] + Qc[TB + tid];
       // dx pieces of V values: columns 64 pg .. 64 pg + W - 1 of rows j < vj
       constexpr int V = 16 / sizeof(T), MAXP = (32 * 64 / V + kBwdThreads - 1) / kBwdThreads;
       const int W = P - 64 * pg < 64 ? P - 64 * pg : 64;
@@ -781,14 +784,34 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         }
       }
     }
-  }
-  // the chunk's share of dD = sum <dy, x>
+    // this head's share of dD = sum <dy, x> over the block, added to the
+    // wave's slot (each wave its own: no race, a fixed order)
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, kWave);
+    for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, kWave);
+    if (lane == 0) dDw[hh * (kBwdThreads / kWave) + wv] += dsum;
+    }   // heads of the part
+    // the block's dB rows through LDS where the state rows were (every wave
+    // is past the last head's carried term), then out as whole-row pieces
+    float* Ds = reinterpret_cast<float*>(U);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * jb + 4 * g4 + r;
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        const int nt = nh + 2 * q;
+        if (nt < ntn) Ds[stage_at(j, 16 * nt + l16, N)] = dba[q][r];
+      }
+    }
+    __syncthreads();
+    stage_to_global<16 * NKN>(dBh + ((b * L + tj0) * hbp + (part - p0)) * (int64_t)N,
+                              (int64_t)hbp * N, Ds, N, vj);
+  }
+  // the chunk's shares of dD, one per head of the part
   __syncthreads();
-  if (tid % kWave == 0) red[tid / kWave] = dsum;
-  __syncthreads();
-  if (tid == 0) dDpart[(b * T_ + c) * H + h] = red[0] + red[1] + red[2] + red[3];
+  if (tid < kh) {
+    const float* w = dDw + tid * (kBwdThreads / kWave);
+    dDpart[(b * T_ + c) * H + hfirst + tid] = w[0] + w[1] + w[2] + w[3];
+  }
 }
 
 // Step-size gradients of one (b, h): the reverse running sum of P - dt Qr over
@@ -931,12 +954,14 @@ bwd_prep_kernel(const float* __restrict__ Gw, float* __restrict__ w2, float* __r
   }
 }
 
-// dB and dC: sums over the heads of each group of the per-head fp32 parts,
-// one batch of heads h0 .. h0 + nb - 1 at a time (parts in rows of hb heads).
-// Each element adds its group's heads of the batch in ascending order to the
-// running fp32 sum (starting from zero at the group's first head) and, at the
-// group's last head, stores the io-dtype result: the order of additions is
-// that of one pass over all the heads, whatever the batches.  Only the
+// dB and dC: sums over each group of the fp32 parts the chunk kernels write,
+// one part per kh consecutive heads of a group (the part's heads already
+// summed in ascending order).  Here `H` counts parts and `hpg` parts per
+// group; one batch of parts h0 .. h0 + nb - 1 at a time (rows of hb parts).
+// Each element adds its group's parts of the batch in ascending order to the
+// running fp32 sum (starting from zero at the group's first part) and, at the
+// group's last part, stores the io-dtype result: the order of additions is
+// that of one pass over all the parts, whatever the batches.  Only the
 // groups g0 .. g0 + ng - 1 that the batch touches are visited (total = B L ng N).
 template <typename T>
 __global__ void __launch_bounds__(kBwdThreads)
@@ -1006,6 +1031,19 @@ bwd_scalars_kernel(const double* __restrict__ dApart, const double* __restrict__
 
 // ---------------------------------------------------------------- host side
 
+// Heads per part: the largest divisor of the heads per group, at most
+// kBwdPartHeadsMax, that still leaves ~1024 workgroups per chunk-kernel launch
+// over all the parts (B T (H / kh) >= 1024; four workgroups on each of 256
+// CUs), else 1.  It depends on the shape alone, so the parts, and the order
+// in which dB and dC are summed, are the same whatever the workspace.
+int bwd_part_heads(int64_t batch, int64_t T_, int64_t H, int64_t G) {
+  const int64_t hpg = H / G, wg = batch * T_;
+  int kh = 1;
+  for (int k = 2; k <= kBwdPartHeadsMax && k <= hpg; ++k)
+    if (hpg % k == 0 && wg * (H / k) >= 1024) kh = k;
+  return kh;
+}
+
 // Token-block rows of the per-chunk kernels: 32, or 0 when their LDS plan
 // for this headdim and dstate does not fit.  The plans are ~31 and ~35 KiB at
 // headdim 64 / dstate 128 in bf16, so four workgroups share a CU.
@@ -1065,27 +1103,28 @@ static hipError_t launch_chunks(const void* x, const void* Bm, const void* Cm, c
                                 const float* Dv, void* dx, float* Pb, float* Qb, float* dBh,
                                 float* dCh, float* dDpart, int64_t batch, int64_t L, int64_t H,
                                 int64_t P, int64_t N, int64_t G, int Q, int64_t T_, int64_t ldw,
-                                int h0, int nb, int hb, hipStream_t stream) {
+                                int p0, int np, int hbp, int kh, hipStream_t stream) {
   const int ta = bwd_target_bytes<T>((int)P, (int)N);
   const int sb = bwd_source_bytes<T>((int)P, (int)N);
   hipError_t e = ensure_dyn_lds<bwd_target_kernel<T, NKN, NKP>>(ta);
   if (e != hipSuccess) return e;
   e = ensure_dyn_lds<bwd_source_kernel<T, NKN, NKP>>(sb);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)T_, (unsigned)nb, (unsigned)batch);
+  const dim3 grid((unsigned)T_, (unsigned)np, (unsigned)batch);
   const int hpg = (int)(H / G);
+  if (kh < 1 || kh > kBwdPartHeadsMax || hpg % kh != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_target_kernel<T, NKN, NKP>), grid, dim3(kBwdThreads), ta, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm),
                      static_cast<const T*>(Cm), static_cast<const T*>(dy), Gw, dtw,
                      static_cast<const float*>(Hc), Pb, dCh, L, (int)H, (int)P, (int)N, (int)G,
-                     hpg, Q, (int)T_, ldw, h0, hb);
+                     hpg, Q, (int)T_, ldw, p0, hbp, kh);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_source_kernel<T, NKN, NKP>), grid, dim3(kBwdThreads), sb, stream,
                      static_cast<const T*>(x), static_cast<const T*>(Bm),
                      static_cast<const T*>(Cm), static_cast<const T*>(dy), Gw, dtw,
                      static_cast<const float*>(Lam), Dv, static_cast<T*>(dx), dBh, Qb, dDpart, L,
-                     (int)H, (int)P, (int)N, (int)G, hpg, Q, (int)T_, ldw, h0, hb);
+                     (int)H, (int)P, (int)N, (int)G, hpg, Q, (int)T_, ldw, p0, hbp, kh);
   return hipGetLastError();
 }
 
@@ -1095,10 +1134,10 @@ static hipError_t launch_chunks_p(int64_t P, const void* x, const void* Bm, cons
                                   const void* Hc, const void* Lam, const float* Dv, void* dx,
                                   float* Pb, float* Qb, float* dBh, float* dCh, float* dDpart,
                                   int64_t batch, int64_t L, int64_t H, int64_t N, int64_t G, int Q,
-                                  int64_t T_, int64_t ldw, int h0, int nb, int hb,
+                                  int64_t T_, int64_t ldw, int p0, int np, int hbp, int kh,
                                   hipStream_t stream) {
 #define SSD_BWD_ARGS x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh, dDpart, batch, L, H, \
-                     P, N, G, Q, T_, ldw, h0, nb, hb, stream
+                     P, N, G, Q, T_, ldw, p0, np, hbp, kh, stream
   if (P <= 64) return launch_chunks<T, NKN, 4>(SSD_BWD_ARGS);
   if (P <= 128) return launch_chunks<T, NKN, 8>(SSD_BWD_ARGS);
   return launch_chunks<T, NKN, 16>(SSD_BWD_ARGS);
@@ -1111,10 +1150,10 @@ static hipError_t launch_chunks_t(int TB, const void* x, const void* Bm, const v
                                   const void* Hc, const void* Lam, const float* Dv, void* dx,
                                   float* Pb, float* Qb, float* dBh, float* dCh, float* dDpart,
                                   int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                                  int64_t G, int Q, int64_t T_, int64_t ldw, int h0, int nb, int hb,
-                                  hipStream_t stream) {
+                                  int64_t G, int Q, int64_t T_, int64_t ldw, int p0, int np, int hbp,
+                                  int kh, hipStream_t stream) {
 #define SSD_BWD_ARGS P, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh, dDpart, batch, L, \
-                     H, N, G, Q, T_, ldw, h0, nb, hb, stream
+                     H, N, G, Q, T_, ldw, p0, np, hbp, kh, stream
   if (TB != kBwdTB) return hipErrorInvalidValue;
   if (N <= 128) return launch_chunks_p<T, 8>(SSD_BWD_ARGS);
   return launch_chunks_p<T, 16>(SSD_BWD_ARGS);
@@ -1135,14 +1174,16 @@ hipError_t launch_bwd_chunks(int io_bf16, int TB, const void* x, const void* Bm,
                              const void* Lam, const float* Dv, void* dx, float* Pb, float* Qb,
                              float* dBh, float* dCh, float* dDpart, int64_t batch, int64_t L,
                              int64_t H, int64_t P, int64_t N, int64_t G, int Q, int64_t T_,
-                             int64_t ldw, int h0, int nb, int hb, hipStream_t stream) {
+                             int64_t ldw, int p0, int np, int hbp, int kh, hipStream_t stream) {
   if (io_bf16)
     return launch_chunks_t<bf16>(TB, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh,
-                                 dDpart, batch, L, H, P, N, G, Q, T_, ldw, h0, nb, hb, stream);
+                                 dDpart, batch, L, H, P, N, G, Q, T_, ldw, p0, np, hbp, kh, stream);
   return launch_chunks_t<float>(TB, x, Bm, Cm, dy, Gw, dtw, Hc, Lam, Dv, dx, Pb, Qb, dBh, dCh,
-                                dDpart, batch, L, H, P, N, G, Q, T_, ldw, h0, nb, hb, stream);
+                                dDpart, batch, L, H, P, N, G, Q, T_, ldw, p0, np, hbp, kh, stream);
 }
 
+// `H` counts parts here (kh heads each, the units the chunk kernels write),
+// h0 .. h0 + nb - 1 are the batch's parts and hb the parts per row.
 hipError_t launch_bwd_group_sum(int io_bf16, const float* dBh, const float* dCh, float* accB,
                                 float* accC, void* dB, void* dC, int64_t batch, int64_t L,
                                 int64_t H, int64_t N, int64_t G, int h0, int nb, int hb,

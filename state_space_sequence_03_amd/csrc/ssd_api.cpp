@@ -71,7 +71,8 @@ hipError_t launch_bwd_chunks(int io_bf16, int TB, const void* x, const void* Bm,
                              const void* Lam, const float* Dv, void* dx, float* Pb, float* Qb,
                              float* dBh, float* dCh, float* dDpart, int64_t batch, int64_t L,
                              int64_t H, int64_t P, int64_t N, int64_t G, int Q, int64_t T_,
-                             int64_t ldw, int h0, int nb, int hb, hipStream_t stream);
+                             int64_t ldw, int p0, int np, int hbp, int kh, hipStream_t stream);
+int bwd_part_heads(int64_t batch, int64_t T_, int64_t H, int64_t G);
 hipError_t launch_bwd_group_sum(int io_bf16, const float* dBh, const float* dCh, float* accB,
                                 float* accC, void* dB, void* dC, int64_t batch, int64_t L,
                                 int64_t H, int64_t N, int64_t G, int h0, int nb, int hb,
@@ -302,27 +303,31 @@ size_t config_bytes(const Plan& pl, const ssd_config& c) {
 // Backward-pass workspace: running sums and step sizes, the reversed-chunk
 // weights, per-token P and Qr, chunk-start states H_c and boundary-state
 // gradients L_{c+1} ([batch, H, T, P, N] fp32), the final state, the
-// per-head dB/dC parts, the per-(b, h) / per-(b, c, h) scalar parts and, for
-// bf16 io, fp32 copies of x, dy, B and C for the fp32 state stages.
+// per-part dB/dC sums, the per-(b, h) / per-(b, c, h) scalar parts and, with
+// more than one batch of parts, the running per-group sums.
 struct BwdPlan {
   size_t g_off, dt_off, gz_off, w2_off, pb_off, qb_off, hc_off, lam_off, fin_off, dap_off,
       dbp_off, ddp_off, acb_off, acc_off, dbh_off, dch_off, bytes;
   int TB;
-  int hb;    // heads per batch of the chunk kernels (their dB/dC parts are rows of hb heads)
+  int kh;    // heads per part: a chunk-kernel workgroup sums their dB/dC contributions
+  int np;    // parts, H / kh
+  int hb;    // parts per batch of the chunk kernels (their dB/dC sums are rows of hb parts)
 };
 
-// Workspace of the backward pass for batches of hb heads.  The per-head fp32
-// dB/dC parts are the largest item (2 x B L H N floats); they are produced
-// for hb heads at a time and folded into running per-group sums after each
-// batch, so only one batch's parts exist at a time.
+// Workspace of the backward pass for batches of hb parts.  The fp32 dB/dC
+// sums of the parts are the largest item (2 x B L (H / kh) N floats); they
+// are produced for hb parts at a time and folded into running per-group sums
+// after each batch, so only one batch's parts exist at a time.
 BwdPlan bwd_plan(const Plan& pl, int64_t hb) {
   BwdPlan w;
   const size_t tok = align256(size_t(pl.B) * pl.H * pl.Lp * sizeof(float));
   const size_t st = align256(size_t(pl.B) * pl.H * pl.T * pl.P * pl.N * sizeof(float));
-  const size_t head_parts = size_t(pl.B) * pl.L * pl.N * sizeof(float);   // one head, one of dB/dC
+  const size_t one_part = size_t(pl.B) * pl.L * pl.N * sizeof(float);   // one part, one of dB/dC
+  w.kh = ssd::bwd_part_heads(pl.B, pl.T, pl.H, pl.G);
+  w.np = (int)(pl.H / w.kh);
   w.hb = (int)hb;
-  const size_t parts = align256(head_parts * size_t(hb));
-  const size_t acc = hb < pl.H ? align256(size_t(pl.B) * pl.L * pl.G * pl.N * sizeof(float)) : 0;
+  const size_t parts = align256(one_part * size_t(hb));
+  const size_t acc = hb < w.np ? align256(size_t(pl.B) * pl.L * pl.G * pl.N * sizeof(float)) : 0;
   size_t o = 0;
   w.g_off = o; o += tok;
   w.dt_off = o; o += tok;
@@ -345,43 +350,47 @@ BwdPlan bwd_plan(const Plan& pl, int64_t hb) {
   return w;
 }
 
-// Batches of at most `cap` heads, balanced: ceil(H / cap) batches of equal
+// Batches of at most `cap` parts, balanced: ceil(n / cap) batches of equal
 // size but for the last.
-int64_t balanced_heads(int64_t H, int64_t cap) {
-  const int64_t nbat = (H + cap - 1) / cap;
-  return (H + nbat - 1) / nbat;
+int64_t balanced_heads(int64_t n, int64_t cap) {
+  const int64_t nbat = (n + cap - 1) / cap;
+  return (n + nbat - 1) / nbat;
 }
 
-// The default plan (ssd_bwd_workspace_size): all heads in one batch when
-// their dB/dC parts take no more room than an fp32 copy of x would (2 N <=
-// P); otherwise the head count whose parts fit that room, but at least enough
-// heads for ~1024 workgroups per chunk-kernel launch.
+int64_t bwd_parts(const Plan& pl) { return pl.H / ssd::bwd_part_heads(pl.B, pl.T, pl.H, pl.G); }
+
+// The default plan (ssd_bwd_workspace_size): all parts in one batch when
+// their dB/dC sums take no more room than an fp32 copy of x would (2 N parts
+// <= H P); otherwise the part count that fits that room, but at least enough
+// parts for ~1024 workgroups per chunk-kernel launch.
 BwdPlan bwd_default_plan(const Plan& pl) {
-  int64_t hb = pl.H;
-  if (2 * pl.N > pl.P) {
+  const int64_t np = bwd_parts(pl);
+  int64_t hb = np;
+  if (2 * pl.N * np > pl.H * pl.P) {
     const int64_t fit = std::max<int64_t>(1, pl.H * pl.P / (2 * pl.N));
     const int64_t wg = pl.B * pl.T;
-    hb = balanced_heads(pl.H, std::min<int64_t>(pl.H, std::max<int64_t>(fit, (1024 + wg - 1) / wg)));
+    hb = balanced_heads(np, std::min<int64_t>(np, std::max<int64_t>(fit, (1024 + wg - 1) / wg)));
   }
   return bwd_plan(pl, hb);
 }
 
-// The plan for a caller's workspace.  Among the head batchings whose layout
-// fits `bytes` (nbat equal batches of hb = ceil(H / nbat) heads), the one
+// The plan for a caller's workspace.  Among the part batchings whose layout
+// fits `bytes` (nbat equal batches of hb = ceil(np / nbat) parts), the one
 // whose chunk-kernel launches take the fewest rounds of `slots` concurrent
 // workgroups (B T hb workgroups per batch), the fewest batches on a tie; with
-// slots = 0 (unknown), the most heads per batch that fit.  hb = 0 when not
-// even one head per batch fits.
+// slots = 0 (unknown), the most parts per batch that fit.  hb = 0 when not
+// even one part per batch fits.
 BwdPlan bwd_plan_for(const Plan& pl, size_t bytes, int64_t slots) {
   BwdPlan best{};
   int64_t best_rounds = -1;
-  for (int64_t nbat = 1; nbat <= pl.H; ++nbat) {
-    const int64_t hb = (pl.H + nbat - 1) / nbat;
-    if ((pl.H + hb - 1) / hb != nbat) continue;    // the same batching as a smaller nbat
+  const int64_t np = bwd_parts(pl);
+  for (int64_t nbat = 1; nbat <= np; ++nbat) {
+    const int64_t hb = (np + nbat - 1) / nbat;
+    if ((np + hb - 1) / hb != nbat) continue;    // the same batching as a smaller nbat
     const BwdPlan w = bwd_plan(pl, hb);
     if (w.bytes > bytes) continue;
     if (slots <= 0) return w;
-    const int64_t wg = pl.B * pl.T, full = pl.H / hb, rest = pl.H % hb;
+    const int64_t wg = pl.B * pl.T, full = np / hb, rest = np % hb;
     const int64_t rounds = full * ((wg * hb + slots - 1) / slots) + (wg * rest + slots - 1) / slots;
     if (best_rounds < 0 || rounds < best_rounds) {
       best = w;
@@ -395,11 +404,12 @@ BwdPlan bwd_plan_for(const Plan& pl, size_t bytes, int64_t slots) {
   return best;
 }
 
-// The smallest workspace any head batching needs.
+// The smallest workspace any part batching needs.
 size_t bwd_min_bytes(const Plan& pl) {
   size_t m = SIZE_MAX;
-  for (int64_t cap = pl.H; cap >= 1; --cap)
-    m = std::min(m, bwd_plan(pl, balanced_heads(pl.H, cap)).bytes);
+  const int64_t np = bwd_parts(pl);
+  for (int64_t cap = np; cap >= 1; --cap)
+    m = std::min(m, bwd_plan(pl, balanced_heads(np, cap)).bytes);
   return m;
 }
 
@@ -1032,16 +1042,17 @@ ssd_status ssd_bwd(const ssd_problem* prob, const ssd_dt_transform* dtx, const v
     e = ssd::launch_state_pass(0, Lam, Gw, dfinal, dinit, pl.B, pl.H, pl.P, pl.N, (int)pl.Q,
                                pl.T, pl.Lp, 0, 1, s);
     if (e != hipSuccess) return hip_status(e, "state_pass (reverse) launch");
-    // per-chunk gradients, hb heads at a time, each batch's dB/dC parts folded
-    // into the per-group sums before the next batch overwrites them
-    for (int h0 = 0; h0 < pl.H; h0 += w.hb) {
-      const int nb = (int)std::min<int64_t>(w.hb, pl.H - h0);
+    // per-chunk gradients, hb parts (of kh heads) at a time, each batch's
+    // dB/dC sums folded into the per-group sums before the next batch
+    // overwrites them
+    for (int p0 = 0; p0 < w.np; p0 += w.hb) {
+      const int nb = std::min(w.hb, w.np - p0);
       e = ssd::launch_bwd_chunks(pl.bf16, w.TB, x, B, C, dy, Gw, dtw, Hc, Lam, D, dx, Pb, Qb,
                                  dBh, dCh, dDp, pl.B, pl.L, pl.H, pl.P, pl.N, pl.G, (int)pl.Q,
-                                 pl.T, pl.Lp, h0, nb, w.hb, s);
+                                 pl.T, pl.Lp, p0, nb, w.hb, w.kh, s);
       if (e != hipSuccess) return hip_status(e, "bwd chunk kernels launch");
-      e = ssd::launch_bwd_group_sum(pl.bf16, dBh, dCh, acB, acC, dB, dC, pl.B, pl.L, pl.H, pl.N,
-                                    pl.G, h0, nb, w.hb, s);
+      e = ssd::launch_bwd_group_sum(pl.bf16, dBh, dCh, acB, acC, dB, dC, pl.B, pl.L, w.np, pl.N,
+                                    pl.G, p0, nb, w.hb, s);
       if (e != hipSuccess) return hip_status(e, "bwd group sum launch");
     }
     e = ssd::launch_bwd_finish(Pb, Qb, dtw, dt, A, dfinal, fin, xfp, ddt, dAp, dbp, dDp, dA, dD,

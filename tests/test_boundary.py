@@ -9,7 +9,7 @@ import subprocess
 
 import pytest
 
-from bwd_layout import balanced, bwd_layout
+from bwd_layout import balanced, bwd_layout, part_heads, parts
 import state_space_sequence_03_amd as lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -534,28 +534,34 @@ def test_bwd_limits(so):
 
 
 def test_bwd_workspace_formula(so):
-    # default: all heads in one batch when 2 dstate <= headdim, else the heads
-    # whose parts fit one fp32 copy of x, at least 1024 / (batch * chunks),
-    # in balanced batches; minimum: the smallest layout over the head counts
+    # parts of kh heads (part_heads); default: all parts in one batch when
+    # 2 dstate parts <= nheads headdim, else the parts whose sums fit one fp32
+    # copy of x, at least 1024 / (batch * chunks), in balanced batches;
+    # minimum: the smallest layout over the part counts
     cases = (dict(), dict(io_dtype=0, seqlen=77, chunk_size=64, ngroups=1),
              dict(headdim=128, dstate=64), dict(batch=2, seqlen=8192, nheads=80, headdim=64,
                                                 dstate=128, ngroups=1, chunk_size=256),
              dict(batch=8, seqlen=4096, nheads=64, headdim=64, dstate=256, ngroups=8,
-                  chunk_size=128))
+                  chunk_size=128),
+             dict(batch=2, seqlen=2030, nheads=32, headdim=16, dstate=32, ngroups=2, chunk_size=32))
     for pd in cases:
         p = P(**pd)
         H, N, Pd = p.nheads, p.dstate, p.headdim
         T = -(-p.seqlen // p.chunk_size)
-        hb = H
-        if 2 * N > Pd:
+        npart = parts(p)
+        hb = npart
+        if 2 * N * npart > H * Pd:
             fit = max(1, H * Pd // (2 * N))
-            hb = balanced(H, min(H, max(fit, -(-1024 // (p.batch * T)))))
+            hb = balanced(npart, min(npart, max(fit, -(-1024 // (p.batch * T)))))
         assert bwd_ws(p) == (OK, bwd_layout(p, hb)), pd
-        want_min = min(bwd_layout(p, balanced(H, c)) for c in range(1, H + 1))
+        want_min = min(bwd_layout(p, balanced(npart, c)) for c in range(1, npart + 1))
         assert bwd_ws_min(p) == (OK, want_min), pd
-    # the 2.7B layer shape: 4 batches of 20 heads, under 1 GB
+    # the 2.7B layer shape: 16 parts of five heads, all in one batch, under 650 MB
     p = P(**cases[3])
-    assert bwd_ws(p)[1] == bwd_layout(p, 20) < 10 ** 9
+    assert part_heads(p) == 5
+    assert bwd_ws(p)[1] == bwd_layout(p, 16) < 650 * 10 ** 6
+    # four-head parts in two groups at the last case's shape
+    assert part_heads(P(**cases[5])) == 4
 
 
 @pytest.mark.skipif(not os.path.exists(f"{LLVM}/llvm-objdump"), reason="ROCm LLVM tools not installed")

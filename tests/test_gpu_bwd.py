@@ -28,7 +28,7 @@ import torch
 
 import oracle
 import ssd_synth
-from bwd_layout import balanced, bwd_layout
+from bwd_layout import balanced, bwd_layout, part_heads, parts
 from parity_util import errors
 
 pytestmark = pytest.mark.gpu
@@ -83,6 +83,14 @@ CASES = {
     # fewer tokens than one 32-token block
     "bf16_seq5": (dict(batch=3, seqlen=5, nheads=2, headdim=16, dstate=16, ngroups=1,
                        chunk_size=64, io_dtype="bf16", init_std=0.1), True, True, None),
+    # enough workgroups (2 x 64 chunks x 8 parts) for parts of four heads:
+    # each workgroup sums four heads' dB and dC before writing them
+    "bf16_q32_parts4_ragged": (dict(batch=2, seqlen=2030, nheads=32, headdim=16, dstate=32,
+                                    ngroups=2, chunk_size=32, io_dtype="bf16", init_std=0.1),
+                               True, True, None),
+    "fp32_q32_parts4_raw_dt": (dict(batch=2, seqlen=2030, nheads=32, headdim=16, dstate=32,
+                                    ngroups=2, chunk_size=32, io_dtype="fp32", init_std=0.1),
+                               True, True, (True, (0.0, float("inf")))),
 }
 
 
@@ -195,16 +203,38 @@ def test_bwd_head_batches_bitwise_equal(io):
         check(ref[k], ref64[k], io, k)
 
 
-def test_bwd_2p7b_head_batches_equal_one_batch():
-    # at the 2.7B layer shape the default workspace holds the dB/dC parts of
-    # 20 of the 80 heads (four batches); a workspace for all 80 at once must
-    # give bitwise the same gradients
+def test_bwd_part_batches_bitwise_equal():
+    # parts of four heads (two groups of four parts): the part sums and their
+    # ascending per-group sum are the same for one part per batch (the
+    # minimum workspace), three parts per batch (batches that cut the
+    # groups), and all eight parts in one batch (the default)
+    p = ssd_synth.Problem(batch=2, seqlen=2030, nheads=32, headdim=16, dstate=32, ngroups=2,
+                          chunk_size=32, io_dtype="bf16", init_std=0.1)
+    inp = {k: (None if v is None else v.cuda()) for k, v in ssd_synth.make_inputs(p, 54).items()}
+    grads = {k: v.cuda() for k, v in ssd_synth.make_grads(p, 54).items()}
+    prob, ref = bwd_outputs(p, inp, grads, None)
+    assert part_heads(prob) == 4 and parts(prob) == 8
+    assert lib.ssd_bwd_workspace_size(prob) == bwd_layout(prob, 8)
+    sizes = {"min": lib.ssd_bwd_workspace_min_size(prob), "three": bwd_layout(prob, 3)}
+    assert sizes["min"] == bwd_layout(prob, 1)
+    for name, n in sizes.items():
+        _, got = bwd_outputs(p, inp, grads, n)
+        for k in ref:
+            if ref[k] is not None:
+                assert torch.equal(got[k], ref[k]), (name, k)
+
+
+def test_bwd_2p7b_part_batches_equal_one_batch():
+    # at the 2.7B layer shape the default workspace holds the dB/dC sums of
+    # all 16 parts (five heads each) at once; a workspace for four parts at a
+    # time (four batches) must give bitwise the same gradients
     p = ssd_synth.CONFIGS["mamba2_2p7b"]
     inp = {k: (None if v is None else v.cuda()) for k, v in ssd_synth.make_inputs(p, 6).items()}
     grads = {k: v.cuda() for k, v in ssd_synth.make_grads(p, 6).items()}
     prob, ref = bwd_outputs(p, inp, grads, None)
-    assert lib.ssd_bwd_workspace_size(prob) == bwd_layout(prob, 20) < 10 ** 9
-    _, got = bwd_outputs(p, inp, grads, bwd_layout(prob, p.nheads))
+    assert part_heads(prob) == 5
+    assert lib.ssd_bwd_workspace_size(prob) == bwd_layout(prob, 16) < 650 * 10 ** 6
+    _, got = bwd_outputs(p, inp, grads, bwd_layout(prob, 4))
     for k in ref:
         if ref[k] is not None:
             assert torch.equal(got[k], ref[k]), k
