@@ -275,17 +275,22 @@ __host__ __device__ inline int bwd_target_bytes(int P, int N) {
   return pair + (pair > st ? pair : st) + kBwdTB * kBwdLdW * 4 + 7 * kBwdTB * 4;
 }
 
-// 8 fp32 weights (k-contiguous) as two bf16 fragments, hi = bf16(w) and
-// lo = bf16(w - hi): hi + lo carries ~16 significant bits of w, so two bf16
-// MFMAs against an exact bf16 operand give the product to ~2^-16 relative
-__device__ __forceinline__ void split_frag(const float* p, bf16x8& hi, bf16x8& lo) {
-  const floatx8 v = load_frag(p);
+// Four fp32 weights w[r] of one column of a 16 x 16 accumulator tile (rows
+// 4 (lane / 16) + r) as bf16 hi = bf16(w) and lo = bf16(w - hi), written to
+// k-major (transposed) planes: the four values are contiguous there, one
+// 8-byte write per plane, and a consumer reads its row of eight k-values
+// with the transposing LDS read, as for the token-major io tiles.
+constexpr int kBwdLdT = kBwdTB + 4;   // bf16 plane rows: 72 bytes, 8-byte aligned
+static_assert(2 * kBwdTB * kBwdLdT * 2 <= kBwdTB * kBwdLdW * 4, "two planes fill an fp32 weight region");
+__device__ __forceinline__ void split_to_planes(const float (&w)[4], bf16* hi_at, bf16* lo_at) {
+  bf16x4 hi, lo;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const bf16 h = static_cast<bf16>(v[e]);
-    hi[e] = h;
-    lo[e] = static_cast<bf16>(v[e] - static_cast<float>(h));
+  for (int r = 0; r < 4; ++r) {
+    hi[r] = static_cast<bf16>(w[r]);
+    lo[r] = static_cast<bf16>(w[r] - static_cast<float>(hi[r]));
   }
+  *reinterpret_cast<bf16x4*>(hi_at) = hi;
+  *reinterpret_cast<bf16x4*>(lo_at) = lo;
 }
 
 // 8 io values (k-contiguous) as an fp32 MFMA fragment
@@ -390,6 +395,7 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       // this wave's tile: rows i = 16 ti2 + 4 (lane / 16) + r, column j = 16 tj2 + lane % 16
       const floatx4 cb = tile_dot<16 * NKN>(Ct + 16 * ti2 * ldN, Bt + 16 * tj2 * ldN, ldN, NR, lane);
       const floatx4 gx = tile_dot<16 * NKP>(gt + 16 * ti2 * ldP, xt + 16 * tj2 * ldP, ldP, PR, lane);
+      float wr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ti2 + 4 * g4 + r;
@@ -399,18 +405,24 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         // where a conditional LDS read would be an exec-mask branch
         const float gi = Gi[i], gj = Gj[j];
         const float w = on ? fast_exp2(gi - gj) * dj * gx[r] : 0.0f;
-        Ws[i * ldW + j] = w;
+        wr[r] = w;
+        if constexpr (sizeof(T) != 2) Ws[i * ldW + j] = w;
         const float pr = sum16(w * cb[r]);
         if (l16 == 0) Pp[tj2 * TB + i] = pr;
       }
+      // bf16 io: W as hi and lo planes, k-major (row j, columns i)
+      bf16* const Wh = reinterpret_cast<bf16*>(Ws);
+      bf16* const Wl = Wh + TB * kBwdLdT;
+      if constexpr (sizeof(T) == 2)
+        split_to_planes(wr, Wh + j * kBwdLdT + 16 * ti2 + 4 * g4, Wl + j * kBwdLdT + 16 * ti2 + 4 * g4);
       __syncthreads();
       if (tid < TB) Pacc[tid] += Pp[tid] + Pp[TB + tid];
       // dC rows 16 ib + .. += W[rows][0..31] B[0..31][tile columns]
       if constexpr (sizeof(T) == 2) {
-        // bf16 io: W split into bf16 hi + lo, B's token-major fragment by
+        // bf16 io: W's hi and lo planes and B's token-major fragment by
         // transposing LDS reads
-        bf16x8 wh, wl;
-        split_frag(Ws + (16 * ib + l16) * ldW + 8 * g4, wh, wl);
+        const bf16x8 wh = frag_tokens(Wh, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * ib, lane);
+        const bf16x8 wl = frag_tokens(Wl, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * ib, lane);
 #pragma unroll
         for (int q = 0; q < NT; ++q) {
           const int nt = nh + 2 * q;
@@ -613,6 +625,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       const floatx4 cb = tile_dot<16 * NKN>(Bt + 16 * tj2 * ldN, Ct + 16 * ti2 * ldN, ldN, NR, lane);
       const floatx4 gx = tile_dot<16 * NKP>(xt + 16 * tj2 * ldP, gt + 16 * ti2 * ldP, ldP, PR, lane);
       const int i = 16 * ti2 + l16;
+      float ur[4], vr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * tj2 + 4 * g4 + r;
@@ -620,20 +633,34 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         const float gi = Gi[i], gj = Gj[j];     // read unconditionally: a select, not a branch
         const float a = on ? fast_exp2(gi - gj) : 0.0f;
         const float u = a * cb[r];
-        Us[j * ldW + i] = u;
-        Vs[j * ldW + i] = a * gx[r] * dj[j];     // dB's weights carry dt_j
+        ur[r] = u;
+        vr[r] = a * gx[r] * dj[j];              // dB's weights carry dt_j
+        if constexpr (sizeof(T) != 2) {
+          Us[j * ldW + i] = u;
+          Vs[j * ldW + i] = vr[r];
+        }
         const float q = sum16(u * gx[r]);
         if (l16 == 0) Qp[ti2 * TB + j] = q;
+      }
+      // bf16 io: U and V as hi and lo planes, k-major (row i, columns j)
+      bf16* const Uh = reinterpret_cast<bf16*>(Us);
+      bf16* const Ul = Uh + TB * kBwdLdT;
+      bf16* const Vh = reinterpret_cast<bf16*>(Vs);
+      bf16* const Vl = Vh + TB * kBwdLdT;
+      if constexpr (sizeof(T) == 2) {
+        split_to_planes(ur, Uh + i * kBwdLdT + 16 * tj2 + 4 * g4, Ul + i * kBwdLdT + 16 * tj2 + 4 * g4);
+        split_to_planes(vr, Vh + i * kBwdLdT + 16 * tj2 + 4 * g4, Vl + i * kBwdLdT + 16 * tj2 + 4 * g4);
       }
       __syncthreads();
       if (tid < TB) Qacc[tid] += Qp[tid] + Qp[TB + tid];
       // rows 16 jb + ..: dB += V[rows][0..31] C[0..31][tiles], dx += U[rows][..] dy[..][tiles]
       if constexpr (sizeof(T) == 2) {
-        // bf16 io: U and V split into bf16 hi + lo, C's and dy's token-major
+        // bf16 io: U's and V's hi and lo planes, C's and dy's token-major
         // fragments by transposing LDS reads
-        bf16x8 vh, vl, uh, ul;
-        split_frag(Vs + (16 * jb + l16) * ldW + 8 * g4, vh, vl);
-        split_frag(Us + (16 * jb + l16) * ldW + 8 * g4, uh, ul);
+        const bf16x8 vh = frag_tokens(Vh, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
+        const bf16x8 vl = frag_tokens(Vl, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
+        const bf16x8 uh = frag_tokens(Uh, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
+        const bf16x8 ul = frag_tokens(Ul, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
 #pragma unroll
         for (int q = 0; q < NT; ++q) {
           const int nt = nh + 2 * q;
