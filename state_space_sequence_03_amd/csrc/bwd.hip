@@ -345,7 +345,6 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
   float* Gj = Gi + TB;
   float* Pp = Gj + TB;          // [2][TB]: pair shares of P from the two column-half waves
   float* Pc = Pp + 2 * TB;      // [2][TB]: carried shares of P
-  float* Pacc = Pc + 2 * TB;
   const int nb = Q / TB, ntiles = N / 16;
 
   for (int I = 0; I < nb; ++I) {
@@ -370,11 +369,12 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       __syncthreads();
       if (hh == 0) tc.store(Ct, ldN, N);
       tg.store(gt, ldP, P);
-      if (tid < TB) {
-        Gi[tid] = gi;
-        Pacc[tid] = 0.0f;
-      }
+      if (tid < TB) Gi[tid] = gi;
     }
+    // P's pair shares: each lane keeps its rows' products over all the pairs
+    // (its rows and column offset are the same in every pair) and the sums
+    // over the 16 lanes of a row are taken once, after the pairs
+    float pa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int J = 0; J <= I; ++J) {
       const int64_t tj0 = (int64_t)c * Q + J * TB;
       const int vj = valid_rows(L, tj0, TB);
@@ -407,8 +407,7 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         const float w = on ? fast_exp2(gi - gj) * dj * gx[r] : 0.0f;
         wr[r] = w;
         if constexpr (sizeof(T) != 2) Ws[i * ldW + j] = w;
-        const float pr = sum16(w * cb[r]);
-        if (l16 == 0) Pp[tj2 * TB + i] = pr;
+        pa[r] = fmaf(w, cb[r], pa[r]);
       }
       // bf16 io: W as hi and lo planes, k-major (row j, columns i)
       bf16* const Wh = reinterpret_cast<bf16*>(Ws);
@@ -416,7 +415,6 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       if constexpr (sizeof(T) == 2)
         split_to_planes(wr, Wh + j * kBwdLdT + 16 * ti2 + 4 * g4, Wl + j * kBwdLdT + 16 * ti2 + 4 * g4);
       __syncthreads();
-      if (tid < TB) Pacc[tid] += Pp[tid] + Pp[TB + tid];
       // dC rows 16 ib + .. += W[rows][0..31] B[0..31][tile columns]
       if constexpr (sizeof(T) == 2) {
         // bf16 io: W's hi and lo planes and B's token-major fragment by
@@ -445,6 +443,11 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
           }
         }
       }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = sum16(pa[r]);
+      if (l16 == 0) Pp[tj2 * TB + 16 * ti2 + 4 * g4 + r] = s;
     }
     // carried term exp2(G_i) H_c^T dy_i: H_c through LDS 32 state rows at a time
     floatx4 hc[NT];
@@ -489,7 +492,8 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       if (l16 == 0) Pc[nh * TB + i] = pc[r];
     }
     __syncthreads();
-    if (tid < vi) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + tid] = Pacc[tid] + Pc[tid] + Pc[TB + tid];
+    if (tid < vi) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + tid] =
+          (Pp[tid] + Pp[TB + tid]) + (Pc[tid] + Pc[TB + tid]);
     }   // heads of the part
     // the block's dC rows through LDS where the state rows were (every wave
     // is past the last head's carried term), then out as whole-row pieces
@@ -563,8 +567,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
   float* dj = Gj + TB;
   float* Qp = dj + TB;          // [2][TB]: pair shares of Qr from the two column-half waves
   float* Qc = Qp + 2 * TB;      // [2][TB]: carried shares of Qr
-  float* Qacc = Qc + 2 * TB;
-  float* dDw = Qacc + TB;       // [head of the part][wave]: shares of dD
+  float* dDw = Qc + 3 * TB;     // [head of the part][wave]: shares of dD
   const int nb = Q / TB, ntn = N / 16, ntp = P / 16;
   if (lane == 0)
     for (int hh = 0; hh < kh; ++hh) dDw[hh * (kBwdThreads / kWave) + wv] = 0.0f;
@@ -599,12 +602,14 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       if (tid < TB) {
         Gj[tid] = gj;
         dj[tid] = dv;
-        Qacc[tid] = 0.0f;
       }
     }
     floatx4 dxa[PT];
 #pragma unroll
     for (int q = 0; q < PT; ++q) dxa[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    // Qr's pair shares: each lane keeps its rows' products over all the
+    // pairs, summed over the 16 lanes of a row once, after the pairs
+    float qa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int I = J; I < nb; ++I) {
       const int64_t ti0 = (int64_t)c * Q + I * TB;
       const int vi = valid_rows(L, ti0, TB);
@@ -639,8 +644,7 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
           Us[j * ldW + i] = u;
           Vs[j * ldW + i] = vr[r];
         }
-        const float q = sum16(u * gx[r]);
-        if (l16 == 0) Qp[ti2 * TB + j] = q;
+        qa[r] = fmaf(u, gx[r], qa[r]);
       }
       // bf16 io: U and V as hi and lo planes, k-major (row i, columns j)
       bf16* const Uh = reinterpret_cast<bf16*>(Us);
@@ -652,7 +656,6 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
         split_to_planes(vr, Vh + i * kBwdLdT + 16 * tj2 + 4 * g4, Vl + i * kBwdLdT + 16 * tj2 + 4 * g4);
       }
       __syncthreads();
-      if (tid < TB) Qacc[tid] += Qp[tid] + Qp[TB + tid];
       // rows 16 jb + ..: dB += V[rows][0..31] C[0..31][tiles], dx += U[rows][..] dy[..][tiles]
       if constexpr (sizeof(T) == 2) {
         // bf16 io: U's and V's hi and lo planes, C's and dy's token-major
@@ -703,6 +706,11 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
           }
         }
       }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = sum16(qa[r]);
+      if (l16 == 0) Qp[ti2 * TB + 16 * tj2 + 4 * g4 + r] = s;
     }
     // carried terms, L_{c+1} through LDS 32 state rows (p0 .. p0+31) at a time;
     // this wave's A-operand row j = 16 jb + lane % 16 carries exp2(G_last - G_j)
@@ -779,7 +787,8 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
       }
       __syncthreads();
       if (pg == 0 && tid < vj)
-        Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + tid] = Qacc[tid] + Qc[tid] + Qc[TB + tid];
+        Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + tid] =
+            (Qp[tid] + Qp[TB + tid]) + (Qc[tid] + Qc[TB + tid]);
       // dx pieces of V values: columns 64 pg .. 64 pg + W - 1 of rows j < vj
       constexpr int V = 16 / sizeof(T), MAXP = (32 * 64 / V + kBwdThreads - 1) / kBwdThreads;
       const int W = P - 64 * pg < 64 ? P - 64 * pg : 64;
