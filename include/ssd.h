@@ -424,21 +424,25 @@ ssd_status ssd_step(const ssd_problem* prob, const ssd_dt_transform* dtx, float*
 /* Default workspace bytes of ssd_bwd for `prob`, and the least it accepts
  * (errors as for ssd_bwd's shape checks).
  *
- * The largest part of the workspace holds per-head fp32 partial gradients of
- * B and C, which are summed over the heads of each group.  ssd_bwd forms
- * them for a batch of heads at a time and folds each batch into running
- * fp32 sums per group before the next, so the workspace it needs shrinks
- * with the heads per batch.  Given workspace_bytes, ssd_bwd considers the
- * batchings into equal batches whose layout fits and takes the one whose
- * per-chunk kernel launches need the fewest rounds of the workgroups the
- * device runs at once (the fewest batches on a tie).  The default size
- * keeps each batch's partial gradients within the room of one fp32 copy of x
- * (all heads in one batch when 2 dstate <= headdim), but keeps enough heads
- * per batch for about 1024 workgroups per launch; the minimum is the
- * smallest layout over all head counts.  Larger workspaces allow larger
- * batches, up to all heads.  Results do not depend on the batching: the
- * per-group sums add the heads in ascending order either way, so they are
- * bitwise identical for any accepted workspace size. */
+ * The largest part of the workspace holds fp32 partial gradients of B and
+ * C, one per "part" of kh consecutive heads of a group (the per-chunk
+ * kernels sum a part's heads as they go; kh is the largest divisor of the
+ * heads per group, up to 8, that leaves batch * chunks * nheads / kh >= 1024
+ * workgroups, else 1, and depends on the shape alone).  These are summed
+ * over the parts of each group.  ssd_bwd forms them for a batch of parts at
+ * a time and folds each batch into running fp32 sums per group before the
+ * next, so the workspace it needs shrinks with the parts per batch.  Given
+ * workspace_bytes, ssd_bwd considers the batchings into equal batches whose
+ * layout fits and takes the one whose per-chunk kernel launches need the
+ * fewest rounds of the workgroups the device runs at once (the fewest
+ * batches on a tie).  The default size keeps each batch's partial gradients
+ * within the room of one fp32 copy of x (all parts in one batch when
+ * 2 dstate (nheads / kh) <= nheads headdim), but keeps enough parts per
+ * batch for about 1024 workgroups per launch; the minimum is the smallest
+ * layout over all part counts.  Larger workspaces allow larger batches, up
+ * to all parts.  Results do not depend on the batching: a part adds its
+ * heads, and the per-group sums add the parts, in ascending order either
+ * way, so they are bitwise identical for any accepted workspace size. */
 ssd_status ssd_bwd_workspace_size(const ssd_problem* prob, size_t* bytes);
 ssd_status ssd_bwd_workspace_min_size(const ssd_problem* prob, size_t* bytes);
 

@@ -39,16 +39,26 @@
 // stay on the fp32 MFMA: with the split there, both per-chunk kernels spill
 // twice as many registers and the pass measured 5.30 ms against 4.52 ms.)
 //
-// The per-chunk terms: one workgroup per (chunk, head, batch) walks 32-token
-// blocks of the chunk; two kernels, one for the reading side (dC, P) and one
-// for the read side (dx, dB, Qr), each keeping its outputs in registers
-// across the pairs of blocks.  Every product runs on MFMA: the chunk x chunk
-// products C B^T and dy x^T from io-dtype LDS tiles (bf16 operands are exact
-// and the sums fp32; fp32 io uses the fp32 MFMA); the products with the fp32
-// weights W, U, V as split-bf16 MFMAs for bf16 io (fp32 MFMA for fp32 io);
-// the carried terms, which feed the step-size gradient, on the exact fp32
-// MFMA.  dB and dC are written per head in fp32 and summed over the heads of
-// a group by a final pass.
+// The per-chunk terms: one workgroup per (chunk, part, batch), a part being
+// kh consecutive heads of one group, walks 32-token blocks of the chunk; two
+// kernels, one for the reading side (dC, P) and one for the read side (dx,
+// dB, Qr), each keeping its outputs in registers across the pairs of blocks
+// and, for dB and dC, across the part's heads.  Every product runs on MFMA:
+// the chunk x chunk products C B^T and dy x^T from io-dtype LDS tiles (bf16
+// operands are exact and the sums fp32; fp32 io uses the fp32 MFMA); the
+// products with the fp32 weights W, U, V as split-bf16 MFMAs for bf16 io
+// (fp32 MFMA for fp32 io); the carried terms, which feed the step-size
+// gradient, on the exact fp32 MFMA.  dB and dC are written per part in fp32
+// and summed over the parts of a group by a final pass.
+//
+// The two kernels are bound by VALU issue more than by MFMA or memory, so
+// their loops are written for few vector instructions: tile loads issued all
+// at once through buffer resources (zero past the valid rows, no fill or
+// branch), row/piece indexes from a 24-bit multiply by a reciprocal (no
+// run-time division), 16-lane sums on DPP, the wave index as a scalar, the
+// weights split to bf16 once by the wave that forms them, the P and Qr pair
+// shares summed across lanes once per block, and outputs staged through LDS
+// to leave as whole-row 16-byte pieces.
 #include "ssd_device.hpp"
 
 namespace ssd {
@@ -259,14 +269,15 @@ __device__ __forceinline__ floatx4 tile_dot(const T* A, const T* B, int ld, int 
   return c;
 }
 
-// Reading side: dC (per head, fp32) and P for every token of one chunk.
-// Block pairs (I, J <= I) of 32 tokens.  Every product is on MFMA: C B^T and
-// dy x^T from the io-dtype tiles (one 16x16 tile of each per wave; io values
-// are exact operands, sums fp32), then W = mask exp2(G_i - G_j) dt_j (dy.x)
-// through LDS and dC += W B on the exact fp32 MFMA, each wave owning 16 rows
-// and every other 16-column tile of dC in its accumulators for the whole
-// block.  The carried term exp2(G_i) H_c^T dy_i likewise, H_c streamed
-// through LDS 32 state rows (one K-step) at a time.
+// Reading side: dC (summed over the part's heads, fp32) and P for every token
+// of one chunk.  Block pairs (I, J <= I) of 32 tokens, for each head of the
+// part in turn.  Every product is on MFMA: C B^T and dy x^T from the io-dtype
+// tiles (one 16x16 tile of each per wave; io values are exact operands, sums
+// fp32), then W = mask exp2(G_i - G_j) dt_j (dy.x) through LDS (as bf16 hi
+// and lo planes for bf16 io) and dC += W B, each wave owning 16 rows and
+// every other 16-column tile of dC in its accumulators for the whole block
+// and all the part's heads.  The carried term exp2(G_i) H_c^T dy_i likewise,
+// H_c streamed through LDS 32 state rows (one K-step) at a time.
 constexpr int kBwdLdW = kBwdTB + 4;   // fp32 weight rows: 16-byte aligned fragments
 
 template <typename T>
@@ -304,10 +315,11 @@ __device__ __forceinline__ floatx8 frag32(const bf16* p) {
 __device__ __forceinline__ floatx8 frag32(const float* p) { return load_frag(p); }
 
 // Occupancy: both per-chunk kernels fit four workgroups per CU in LDS but
-// need ~150-160 VGPRs (three waves per SIMD).  For bf16 io up to dstate 128 /
-// headdim 64 they are built for four waves per SIMD (128 VGPRs, a ~90-byte
-// spill per lane): 4.90 against 5.10 ms at the 2.7B shape.  The wider
-// instantiations would spill several hundred bytes and keep the default.
+// need more than 128 VGPRs.  For bf16 io up to dstate 128 / headdim 64 they
+// are built for four waves per SIMD (128 VGPRs, a ~100-byte spill per lane,
+// mostly outside the pair loops), which measured faster than three waves
+// with no spill.  The wider instantiations would spill several hundred bytes
+// and keep the default.
 template <typename T, int NKN, int NKP>
 constexpr int bwd_min_waves() { return sizeof(T) == 2 && NKN <= 8 && NKP <= 4 ? 4 : 1; }
 
@@ -356,144 +368,144 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 #pragma unroll
     for (int q = 0; q < NT; ++q) dc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int hh = 0; hh < kh; ++hh) {
-    const int h = hfirst + hh;
-    const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
-    const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
-    const float* Hrow = Hc + ((b * H + h) * T_ + c) * (int64_t)P * N;
-    {
-      const float gi = tid < TB ? Grow[I * TB + tid] : 0.0f;
-      IoTile<16 * NKN, T> tc;            // C rows: the same for every head of the part
-      IoTile<16 * NKP, T> tg;
-      if (hh == 0) tc.load(Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, N);
-      tg.load(dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, P);
-      __syncthreads();
-      if (hh == 0) tc.store(Ct, ldN, N);
-      tg.store(gt, ldP, P);
-      if (tid < TB) Gi[tid] = gi;
-    }
-    // P's pair shares: each lane keeps its rows' products over all the pairs
-    // (its rows and column offset are the same in every pair) and the sums
-    // over the 16 lanes of a row are taken once, after the pairs
-    float pa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int J = 0; J <= I; ++J) {
-      const int64_t tj0 = (int64_t)c * Q + J * TB;
-      const int vj = valid_rows(L, tj0, TB);
-      const int j = 16 * tj2 + l16;
-      const float dj = drow[J * TB + j];
+      const int h = hfirst + hh;
+      const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
+      const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
+      const float* Hrow = Hc + ((b * H + h) * T_ + c) * (int64_t)P * N;
       {
-        const float gj = tid < TB ? Grow[J * TB + tid] : 0.0f;
-        IoTile<16 * NKN, T> tb;
-        IoTile<16 * NKP, T> tx;
-        tb.load(Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, N);
-        tx.load(x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, P);
+        const float gi = tid < TB ? Grow[I * TB + tid] : 0.0f;
+        IoTile<16 * NKN, T> tc;            // C rows: the same for every head of the part
+        IoTile<16 * NKP, T> tg;
+        if (hh == 0) tc.load(Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, N);
+        tg.load(dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, P);
         __syncthreads();
-        tb.store(Bt, ldN, N);
-        tx.store(xt, ldP, P);
-        if (tid < TB) Gj[tid] = gj;
+        if (hh == 0) tc.store(Ct, ldN, N);
+        tg.store(gt, ldP, P);
+        if (tid < TB) Gi[tid] = gi;
       }
-      __syncthreads();
-      // this wave's tile: rows i = 16 ti2 + 4 (lane / 16) + r, column j = 16 tj2 + lane % 16
-      const floatx4 cb = tile_dot<16 * NKN>(Ct + 16 * ti2 * ldN, Bt + 16 * tj2 * ldN, ldN, NR, lane);
-      const floatx4 gx = tile_dot<16 * NKP>(gt + 16 * ti2 * ldP, xt + 16 * tj2 * ldP, ldP, PR, lane);
-      float wr[4];
+      // P's pair shares: each lane keeps its rows' products over all the pairs
+      // (its rows and column offset are the same in every pair) and the sums
+      // over the 16 lanes of a row are taken once, after the pairs
+      float pa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int J = 0; J <= I; ++J) {
+        const int64_t tj0 = (int64_t)c * Q + J * TB;
+        const int vj = valid_rows(L, tj0, TB);
+        const int j = 16 * tj2 + l16;
+        const float dj = drow[J * TB + j];
+        {
+          const float gj = tid < TB ? Grow[J * TB + tid] : 0.0f;
+          IoTile<16 * NKN, T> tb;
+          IoTile<16 * NKP, T> tx;
+          tb.load(Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, N);
+          tx.load(x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, P);
+          __syncthreads();
+          tb.store(Bt, ldN, N);
+          tx.store(xt, ldP, P);
+          if (tid < TB) Gj[tid] = gj;
+        }
+        __syncthreads();
+        // this wave's tile: rows i = 16 ti2 + 4 (lane / 16) + r, column j = 16 tj2 + lane % 16
+        const floatx4 cb = tile_dot<16 * NKN>(Ct + 16 * ti2 * ldN, Bt + 16 * tj2 * ldN, ldN, NR, lane);
+        const floatx4 gx = tile_dot<16 * NKP>(gt + 16 * ti2 * ldP, xt + 16 * tj2 * ldP, ldP, PR, lane);
+        float wr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * ti2 + 4 * g4 + r;
-        const bool on = J < I || j <= i;
-        // every entry is evaluated (the running sums and step sizes are finite
-        // on padding tokens too) and the masked ones selected away: a select,
-        // where a conditional LDS read would be an exec-mask branch
-        const float gi = Gi[i], gj = Gj[j];
-        const float w = on ? fast_exp2(gi - gj) * dj * gx[r] : 0.0f;
-        wr[r] = w;
-        if constexpr (sizeof(T) != 2) Ws[i * ldW + j] = w;
-        pa[r] = fmaf(w, cb[r], pa[r]);
-      }
-      // bf16 io: W as hi and lo planes, k-major (row j, columns i)
-      bf16* const Wh = reinterpret_cast<bf16*>(Ws);
-      bf16* const Wl = Wh + TB * kBwdLdT;
-      if constexpr (sizeof(T) == 2)
-        split_to_planes(wr, Wh + j * kBwdLdT + 16 * ti2 + 4 * g4, Wl + j * kBwdLdT + 16 * ti2 + 4 * g4);
-      __syncthreads();
-      // dC rows 16 ib + .. += W[rows][0..31] B[0..31][tile columns]
-      if constexpr (sizeof(T) == 2) {
-        // bf16 io: W's hi and lo planes and B's token-major fragment by
-        // transposing LDS reads
-        const bf16x8 wh = frag_tokens(Wh, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * ib, lane);
-        const bf16x8 wl = frag_tokens(Wl, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * ib, lane);
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ti2 + 4 * g4 + r;
+          const bool on = J < I || j <= i;
+          // every entry is evaluated (the running sums and step sizes are finite
+          // on padding tokens too) and the masked ones selected away: a select,
+          // where a conditional LDS read would be an exec-mask branch
+          const float gi = Gi[i], gj = Gj[j];
+          const float w = on ? fast_exp2(gi - gj) * dj * gx[r] : 0.0f;
+          wr[r] = w;
+          if constexpr (sizeof(T) != 2) Ws[i * ldW + j] = w;
+          pa[r] = fmaf(w, cb[r], pa[r]);
+        }
+        // bf16 io: W as hi and lo planes, k-major (row j, columns i)
+        bf16* const Wh = reinterpret_cast<bf16*>(Ws);
+        bf16* const Wl = Wh + TB * kBwdLdT;
+        if constexpr (sizeof(T) == 2)
+          split_to_planes(wr, Wh + j * kBwdLdT + 16 * ti2 + 4 * g4, Wl + j * kBwdLdT + 16 * ti2 + 4 * g4);
+        __syncthreads();
+        // dC rows 16 ib + .. += W[rows][0..31] B[0..31][tile columns]
+        if constexpr (sizeof(T) == 2) {
+          // bf16 io: W's hi and lo planes and B's token-major fragment by
+          // transposing LDS reads
+          const bf16x8 wh = frag_tokens(Wh, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * ib, lane);
+          const bf16x8 wl = frag_tokens(Wl, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * ib, lane);
 #pragma unroll
-        for (int q = 0; q < NT; ++q) {
-          const int nt = nh + 2 * q;
-          if (nt < ntiles) {
-            const bf16x8 bq = frag_tokens(reinterpret_cast<const bf16*>(Bt), ldN, 8 * g4,
-                                          8 * g4 + 4, 16 * nt, lane);
-            dc[q] = mma(mma(dc[q], wh, bq), wl, bq);
+          for (int q = 0; q < NT; ++q) {
+            const int nt = nh + 2 * q;
+            if (nt < ntiles) {
+              const bf16x8 bq = frag_tokens(reinterpret_cast<const bf16*>(Bt), ldN, 8 * g4,
+                                            8 * g4 + 4, 16 * nt, lane);
+              dc[q] = mma(mma(dc[q], wh, bq), wl, bq);
+            }
+          }
+        } else {
+          const floatx8 a = load_frag(Ws + (16 * ib + l16) * ldW + 8 * g4);
+#pragma unroll
+          for (int q = 0; q < NT; ++q) {
+            const int nt = nh + 2 * q;
+            if (nt < ntiles) {
+              floatx8 bq;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) bq[e] = to_f32(Bt[(8 * g4 + e) * ldN + 16 * nt + l16]);
+              dc[q] = mma(dc[q], a, bq);
+            }
           }
         }
-      } else {
-        const floatx8 a = load_frag(Ws + (16 * ib + l16) * ldW + 8 * g4);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s = sum16(pa[r]);
+        if (l16 == 0) Pp[tj2 * TB + 16 * ti2 + 4 * g4 + r] = s;
+      }
+      // carried term exp2(G_i) H_c^T dy_i: H_c through LDS 32 state rows at a time
+      floatx4 hc[NT];
+#pragma unroll
+      for (int q = 0; q < NT; ++q) hc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int p0 = 0; p0 < P; p0 += 32) {
+        {
+          StateRows<16 * NKN> hs;
+          hs.load(Hrow + (int64_t)p0 * N, P - p0, N, N);
+          __syncthreads();
+          hs.store(Hs, N + 1, N);
+        }
+        __syncthreads();
+        const floatx8 a = frag32(gt + (16 * ib + l16) * ldP + p0 + 8 * g4);
 #pragma unroll
         for (int q = 0; q < NT; ++q) {
           const int nt = nh + 2 * q;
           if (nt < ntiles) {
             floatx8 bq;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bq[e] = to_f32(Bt[(8 * g4 + e) * ldN + 16 * nt + l16]);
-            dc[q] = mma(dc[q], a, bq);
+            for (int e = 0; e < 8; ++e) bq[e] = Hs[(8 * g4 + e) * (N + 1) + 16 * nt + l16];
+            hc[q] = mma(hc[q], a, bq);
           }
         }
       }
-    }
+      // rows i = 16 ib + 4 (lane / 16) + r, column 16 nt + lane % 16 of each tile
+      float pc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float s = sum16(pa[r]);
-      if (l16 == 0) Pp[tj2 * TB + 16 * ti2 + 4 * g4 + r] = s;
-    }
-    // carried term exp2(G_i) H_c^T dy_i: H_c through LDS 32 state rows at a time
-    floatx4 hc[NT];
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ib + 4 * g4 + r;
+        const float e = fast_exp2(Gi[i]);
 #pragma unroll
-    for (int q = 0; q < NT; ++q) hc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int p0 = 0; p0 < P; p0 += 32) {
-      {
-        StateRows<16 * NKN> hs;
-        hs.load(Hrow + (int64_t)p0 * N, P - p0, N, N);
-        __syncthreads();
-        hs.store(Hs, N + 1, N);
+        for (int q = 0; q < NT; ++q) {
+          const int nt = nh + 2 * q;
+          if (nt < ntiles) {
+            const float v = e * hc[q][r];
+            dc[q][r] += v;
+            pc[r] = fmaf(v, to_f32(Ct[i * ldN + 16 * nt + l16]), pc[r]);
+          }
+        }
+        pc[r] = sum16(pc[r]);
+        if (l16 == 0) Pc[nh * TB + i] = pc[r];
       }
       __syncthreads();
-      const floatx8 a = frag32(gt + (16 * ib + l16) * ldP + p0 + 8 * g4);
-#pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        const int nt = nh + 2 * q;
-        if (nt < ntiles) {
-          floatx8 bq;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bq[e] = Hs[(8 * g4 + e) * (N + 1) + 16 * nt + l16];
-          hc[q] = mma(hc[q], a, bq);
-        }
-      }
-    }
-    // rows i = 16 ib + 4 (lane / 16) + r, column 16 nt + lane % 16 of each tile
-    float pc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * ib + 4 * g4 + r;
-      const float e = fast_exp2(Gi[i]);
-#pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        const int nt = nh + 2 * q;
-        if (nt < ntiles) {
-          const float v = e * hc[q][r];
-          dc[q][r] += v;
-          pc[r] = fmaf(v, to_f32(Ct[i * ldN + 16 * nt + l16]), pc[r]);
-        }
-      }
-      pc[r] = sum16(pc[r]);
-      if (l16 == 0) Pc[nh * TB + i] = pc[r];
-    }
-    __syncthreads();
-    if (tid < vi) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + tid] =
-          (Pp[tid] + Pp[TB + tid]) + (Pc[tid] + Pc[TB + tid]);
+      if (tid < vi) Pout[(b * H + h) * ldw + (int64_t)c * Q + I * TB + tid] =
+            (Pp[tid] + Pp[TB + tid]) + (Pc[tid] + Pc[TB + tid]);
     }   // heads of the part
     // the block's dC rows through LDS where the state rows were (every wave
     // is past the last head's carried term), then out as whole-row pieces
@@ -513,15 +525,16 @@ bwd_target_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
   }
 }
 
-// Read side: dx, dB (per head, fp32), Qr and the chunk's share of dD.  Block
-// pairs (J, I >= J) of 32 tokens, every product on MFMA: B C^T and x dy^T
-// from the io-dtype tiles, U = mask exp2(G_i - G_j) (C.B) and
-// V = mask exp2(G_i - G_j) (dy.x) through LDS, then dx += U dy and dB += V C
-// on the exact fp32 MFMA, each wave owning 16 rows j and every other
-// 16-column tile of dx and dB for the whole block.  The carried terms come
-// from L_{c+1} streamed through LDS 32 state rows at a time:
-// exp2(G_last - G_j) (B_j L^T) into dx and exp2(G_last - G_j) (x_j L) into
-// dB, the factor folded into the row's operand fragment.
+// Read side: dx, dB (summed over the part's heads, fp32), Qr and the chunk's
+// share of dD.  Block pairs (J, I >= J) of 32 tokens, for each head of the
+// part in turn, every product on MFMA: B C^T and x dy^T from the io-dtype
+// tiles, U = mask exp2(G_i - G_j) (C.B) and V = mask exp2(G_i - G_j) dt_j
+// (dy.x) through LDS (bf16 hi and lo planes for bf16 io), then dx += U dy
+// and dB += V C, each wave owning 16 rows j and every other 16-column tile
+// of dx and dB (dB across the part's heads, dx per head).  The carried terms
+// come from L_{c+1} streamed through LDS 32 state rows at a time:
+// exp2(G_last - G_j) (B_j L^T) into dx and exp2(G_last - G_j) dt_j (x_j L)
+// into dB, the factor folded into the row's operand fragment.
 template <typename T>
 __host__ __device__ inline int bwd_source_bytes(int P, int N) {
   const int pair = bwd_pair_bytes<T>(P, N), st = (32 * (round32(N) + 1) * 4 + 15) / 16 * 16;
@@ -582,249 +595,249 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
 #pragma unroll
     for (int q = 0; q < NT; ++q) dba[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int hh = 0; hh < kh; ++hh) {
-    const int h = hfirst + hh;
-    const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
-    const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
-    const float* Lrow = Lam + ((b * H + h) * T_ + c) * (int64_t)P * N;
-    const float Dh = Dv ? Dv[h] : 0.0f;
-    const float Gl = Grow[Q - 1];
-    float dsum = 0.0f;
-    {
-      const float gj = tid < TB ? Grow[J * TB + tid] : 0.0f;
-      const float dv = tid < TB ? drow[J * TB + tid] : 0.0f;
-      IoTile<16 * NKN, T> tb;            // B rows: the same for every head of the part
-      IoTile<16 * NKP, T> tx;
-      if (hh == 0) tb.load(Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, N);
-      tx.load(x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, P);
-      __syncthreads();
-      if (hh == 0) tb.store(Bt, ldN, N);
-      tx.store(xt, ldP, P);
-      if (tid < TB) {
-        Gj[tid] = gj;
-        dj[tid] = dv;
-      }
-    }
-    floatx4 dxa[PT];
-#pragma unroll
-    for (int q = 0; q < PT; ++q) dxa[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    // Qr's pair shares: each lane keeps its rows' products over all the
-    // pairs, summed over the 16 lanes of a row once, after the pairs
-    float qa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int I = J; I < nb; ++I) {
-      const int64_t ti0 = (int64_t)c * Q + I * TB;
-      const int vi = valid_rows(L, ti0, TB);
-      if (vi == 0) break;
+      const int h = hfirst + hh;
+      const float* Grow = Gw + (b * H + h) * ldw + (int64_t)c * Q;
+      const float* drow = dtw + (b * H + h) * ldw + (int64_t)c * Q;
+      const float* Lrow = Lam + ((b * H + h) * T_ + c) * (int64_t)P * N;
+      const float Dh = Dv ? Dv[h] : 0.0f;
+      const float Gl = Grow[Q - 1];
+      float dsum = 0.0f;
       {
-        const float gi = tid < TB ? Grow[I * TB + tid] : 0.0f;
-        IoTile<16 * NKN, T> tc;
-        IoTile<16 * NKP, T> tg;
-        tc.load(Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, N);
-        tg.load(dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, P);
+        const float gj = tid < TB ? Grow[J * TB + tid] : 0.0f;
+        const float dv = tid < TB ? drow[J * TB + tid] : 0.0f;
+        IoTile<16 * NKN, T> tb;            // B rows: the same for every head of the part
+        IoTile<16 * NKP, T> tx;
+        if (hh == 0) tb.load(Bm + ((b * L + tj0) * G + g) * N, (int64_t)G * N, vj, N);
+        tx.load(x + ((b * L + tj0) * H + h) * P, (int64_t)H * P, vj, P);
         __syncthreads();
-        tc.store(Ct, ldN, N);
-        tg.store(gt, ldP, P);
-        if (tid < TB) Gi[tid] = gi;
+        if (hh == 0) tb.store(Bt, ldN, N);
+        tx.store(xt, ldP, P);
+        if (tid < TB) {
+          Gj[tid] = gj;
+          dj[tid] = dv;
+        }
       }
-      __syncthreads();
-      // this wave's tile: rows j = 16 tj2 + 4 (lane / 16) + r, column i = 16 ti2 + lane % 16
-      const floatx4 cb = tile_dot<16 * NKN>(Bt + 16 * tj2 * ldN, Ct + 16 * ti2 * ldN, ldN, NR, lane);
-      const floatx4 gx = tile_dot<16 * NKP>(xt + 16 * tj2 * ldP, gt + 16 * ti2 * ldP, ldP, PR, lane);
-      const int i = 16 * ti2 + l16;
-      float ur[4], vr[4];
+      floatx4 dxa[PT];
+#pragma unroll
+      for (int q = 0; q < PT; ++q) dxa[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      // Qr's pair shares: each lane keeps its rows' products over all the
+      // pairs, summed over the 16 lanes of a row once, after the pairs
+      float qa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int I = J; I < nb; ++I) {
+        const int64_t ti0 = (int64_t)c * Q + I * TB;
+        const int vi = valid_rows(L, ti0, TB);
+        if (vi == 0) break;
+        {
+          const float gi = tid < TB ? Grow[I * TB + tid] : 0.0f;
+          IoTile<16 * NKN, T> tc;
+          IoTile<16 * NKP, T> tg;
+          tc.load(Cm + ((b * L + ti0) * G + g) * N, (int64_t)G * N, vi, N);
+          tg.load(dy + ((b * L + ti0) * H + h) * P, (int64_t)H * P, vi, P);
+          __syncthreads();
+          tc.store(Ct, ldN, N);
+          tg.store(gt, ldP, P);
+          if (tid < TB) Gi[tid] = gi;
+        }
+        __syncthreads();
+        // this wave's tile: rows j = 16 tj2 + 4 (lane / 16) + r, column i = 16 ti2 + lane % 16
+        const floatx4 cb = tile_dot<16 * NKN>(Bt + 16 * tj2 * ldN, Ct + 16 * ti2 * ldN, ldN, NR, lane);
+        const floatx4 gx = tile_dot<16 * NKP>(xt + 16 * tj2 * ldP, gt + 16 * ti2 * ldP, ldP, PR, lane);
+        const int i = 16 * ti2 + l16;
+        float ur[4], vr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * tj2 + 4 * g4 + r;
+          const bool on = I > J || j <= i;
+          const float gi = Gi[i], gj = Gj[j];     // read unconditionally: a select, not a branch
+          const float a = on ? fast_exp2(gi - gj) : 0.0f;
+          const float u = a * cb[r];
+          ur[r] = u;
+          vr[r] = a * gx[r] * dj[j];              // dB's weights carry dt_j
+          if constexpr (sizeof(T) != 2) {
+            Us[j * ldW + i] = u;
+            Vs[j * ldW + i] = vr[r];
+          }
+          qa[r] = fmaf(u, gx[r], qa[r]);
+        }
+        // bf16 io: U and V as hi and lo planes, k-major (row i, columns j)
+        bf16* const Uh = reinterpret_cast<bf16*>(Us);
+        bf16* const Ul = Uh + TB * kBwdLdT;
+        bf16* const Vh = reinterpret_cast<bf16*>(Vs);
+        bf16* const Vl = Vh + TB * kBwdLdT;
+        if constexpr (sizeof(T) == 2) {
+          split_to_planes(ur, Uh + i * kBwdLdT + 16 * tj2 + 4 * g4, Ul + i * kBwdLdT + 16 * tj2 + 4 * g4);
+          split_to_planes(vr, Vh + i * kBwdLdT + 16 * tj2 + 4 * g4, Vl + i * kBwdLdT + 16 * tj2 + 4 * g4);
+        }
+        __syncthreads();
+        // rows 16 jb + ..: dB += V[rows][0..31] C[0..31][tiles], dx += U[rows][..] dy[..][tiles]
+        if constexpr (sizeof(T) == 2) {
+          // bf16 io: U's and V's hi and lo planes, C's and dy's token-major
+          // fragments by transposing LDS reads
+          const bf16x8 vh = frag_tokens(Vh, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
+          const bf16x8 vl = frag_tokens(Vl, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
+          const bf16x8 uh = frag_tokens(Uh, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
+          const bf16x8 ul = frag_tokens(Ul, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
+#pragma unroll
+          for (int q = 0; q < NT; ++q) {
+            const int nt = nh + 2 * q;
+            if (nt < ntn) {
+              const bf16x8 bq = frag_tokens(reinterpret_cast<const bf16*>(Ct), ldN, 8 * g4,
+                                            8 * g4 + 4, 16 * nt, lane);
+              dba[q] = mma(mma(dba[q], vh, bq), vl, bq);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < PT; ++q) {
+            const int pt = nh + 2 * q;
+            if (pt < ntp) {
+              const bf16x8 bq = frag_tokens(reinterpret_cast<const bf16*>(gt), ldP, 8 * g4,
+                                            8 * g4 + 4, 16 * pt, lane);
+              dxa[q] = mma(mma(dxa[q], uh, bq), ul, bq);
+            }
+          }
+        } else {
+          const floatx8 av = load_frag(Vs + (16 * jb + l16) * ldW + 8 * g4);
+          const floatx8 au = load_frag(Us + (16 * jb + l16) * ldW + 8 * g4);
+#pragma unroll
+          for (int q = 0; q < NT; ++q) {
+            const int nt = nh + 2 * q;
+            if (nt < ntn) {
+              floatx8 bq;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) bq[e] = to_f32(Ct[(8 * g4 + e) * ldN + 16 * nt + l16]);
+              dba[q] = mma(dba[q], av, bq);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < PT; ++q) {
+            const int pt = nh + 2 * q;
+            if (pt < ntp) {
+              floatx8 bq;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) bq[e] = to_f32(gt[(8 * g4 + e) * ldP + 16 * pt + l16]);
+              dxa[q] = mma(dxa[q], au, bq);
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * tj2 + 4 * g4 + r;
-        const bool on = I > J || j <= i;
-        const float gi = Gi[i], gj = Gj[j];     // read unconditionally: a select, not a branch
-        const float a = on ? fast_exp2(gi - gj) : 0.0f;
-        const float u = a * cb[r];
-        ur[r] = u;
-        vr[r] = a * gx[r] * dj[j];              // dB's weights carry dt_j
-        if constexpr (sizeof(T) != 2) {
-          Us[j * ldW + i] = u;
-          Vs[j * ldW + i] = vr[r];
-        }
-        qa[r] = fmaf(u, gx[r], qa[r]);
+        const float s = sum16(qa[r]);
+        if (l16 == 0) Qp[ti2 * TB + 16 * tj2 + 4 * g4 + r] = s;
       }
-      // bf16 io: U and V as hi and lo planes, k-major (row i, columns j)
-      bf16* const Uh = reinterpret_cast<bf16*>(Us);
-      bf16* const Ul = Uh + TB * kBwdLdT;
-      bf16* const Vh = reinterpret_cast<bf16*>(Vs);
-      bf16* const Vl = Vh + TB * kBwdLdT;
-      if constexpr (sizeof(T) == 2) {
-        split_to_planes(ur, Uh + i * kBwdLdT + 16 * tj2 + 4 * g4, Ul + i * kBwdLdT + 16 * tj2 + 4 * g4);
-        split_to_planes(vr, Vh + i * kBwdLdT + 16 * tj2 + 4 * g4, Vl + i * kBwdLdT + 16 * tj2 + 4 * g4);
-      }
-      __syncthreads();
-      // rows 16 jb + ..: dB += V[rows][0..31] C[0..31][tiles], dx += U[rows][..] dy[..][tiles]
-      if constexpr (sizeof(T) == 2) {
-        // bf16 io: U's and V's hi and lo planes, C's and dy's token-major
-        // fragments by transposing LDS reads
-        const bf16x8 vh = frag_tokens(Vh, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
-        const bf16x8 vl = frag_tokens(Vl, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
-        const bf16x8 uh = frag_tokens(Uh, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
-        const bf16x8 ul = frag_tokens(Ul, kBwdLdT, 8 * g4, 8 * g4 + 4, 16 * jb, lane);
-#pragma unroll
-        for (int q = 0; q < NT; ++q) {
-          const int nt = nh + 2 * q;
-          if (nt < ntn) {
-            const bf16x8 bq = frag_tokens(reinterpret_cast<const bf16*>(Ct), ldN, 8 * g4,
-                                          8 * g4 + 4, 16 * nt, lane);
-            dba[q] = mma(mma(dba[q], vh, bq), vl, bq);
-          }
+      // carried terms, L_{c+1} through LDS 32 state rows (p0 .. p0+31) at a time;
+      // this wave's A-operand row j = 16 jb + lane % 16 carries exp2(G_last - G_j)
+      const float erow = fast_exp2(Gl - Gj[16 * jb + l16]);
+      const float erow_b = erow * dj[16 * jb + l16];    // dB's rows carry dt_j too
+      float qx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int p0 = 0; p0 < P; p0 += 32) {
+        {
+          StateRows<16 * NKN> ls;
+          ls.load(Lrow + (int64_t)p0 * N, P - p0, N, NR);
+          __syncthreads();
+          ls.store(Ls, lsN, NR);
         }
-#pragma unroll
-        for (int q = 0; q < PT; ++q) {
-          const int pt = nh + 2 * q;
-          if (pt < ntp) {
-            const bf16x8 bq = frag_tokens(reinterpret_cast<const bf16*>(gt), ldP, 8 * g4,
-                                          8 * g4 + 4, 16 * pt, lane);
-            dxa[q] = mma(mma(dxa[q], uh, bq), ul, bq);
-          }
-        }
-      } else {
-        const floatx8 av = load_frag(Vs + (16 * jb + l16) * ldW + 8 * g4);
-        const floatx8 au = load_frag(Us + (16 * jb + l16) * ldW + 8 * g4);
-#pragma unroll
-        for (int q = 0; q < NT; ++q) {
-          const int nt = nh + 2 * q;
-          if (nt < ntn) {
-            floatx8 bq;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bq[e] = to_f32(Ct[(8 * g4 + e) * ldN + 16 * nt + l16]);
-            dba[q] = mma(dba[q], av, bq);
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < PT; ++q) {
-          const int pt = nh + 2 * q;
-          if (pt < ntp) {
-            floatx8 bq;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bq[e] = to_f32(gt[(8 * g4 + e) * ldP + 16 * pt + l16]);
-            dxa[q] = mma(dxa[q], au, bq);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float s = sum16(qa[r]);
-      if (l16 == 0) Qp[ti2 * TB + 16 * tj2 + 4 * g4 + r] = s;
-    }
-    // carried terms, L_{c+1} through LDS 32 state rows (p0 .. p0+31) at a time;
-    // this wave's A-operand row j = 16 jb + lane % 16 carries exp2(G_last - G_j)
-    const float erow = fast_exp2(Gl - Gj[16 * jb + l16]);
-    const float erow_b = erow * dj[16 * jb + l16];    // dB's rows carry dt_j too
-    float qx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int p0 = 0; p0 < P; p0 += 32) {
-      {
-        StateRows<16 * NKN> ls;
-        ls.load(Lrow + (int64_t)p0 * N, P - p0, N, NR);
         __syncthreads();
-        ls.store(Ls, lsN, NR);
-      }
-      __syncthreads();
-      // dx tile (rows j, columns p = p0 + 16 nh + lane % 16) += e_j sum_n B[j][n] L[p][n]
-      const int q = p0 / 32;
-      if (16 * nh + p0 < P) {
-        floatx4 cj = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int k0 = 0; k0 < NR; k0 += 32) {
-          floatx8 a = frag32(Bt + (16 * jb + l16) * ldN + k0 + 8 * g4);
+        // dx tile (rows j, columns p = p0 + 16 nh + lane % 16) += e_j sum_n B[j][n] L[p][n]
+        const int q = p0 / 32;
+        if (16 * nh + p0 < P) {
+          floatx4 cj = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int k0 = 0; k0 < NR; k0 += 32) {
+            floatx8 a = frag32(Bt + (16 * jb + l16) * ldN + k0 + 8 * g4);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a[e] *= erow;
-          floatx8 bq;
+            for (int e = 0; e < 8; ++e) a[e] *= erow;
+            floatx8 bq;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bq[e] = Ls[(16 * nh + l16) * lsN + k0 + 8 * g4 + e];
-          cj = mma(cj, a, bq);
+            for (int e = 0; e < 8; ++e) bq[e] = Ls[(16 * nh + l16) * lsN + k0 + 8 * g4 + e];
+            cj = mma(cj, a, bq);
+          }
+#pragma unroll
+          for (int qq = 0; qq < PT; ++qq)
+            if (qq == q) dxa[qq] += cj;
+          // Qr's carried share: sum_p x[j][p] (e_j B_j L^T)[p]
+          const int p = p0 + 16 * nh + l16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            qx[r] = fmaf(to_f32(xt[(16 * jb + 4 * g4 + r) * ldP + p]), cj[r], qx[r]);
         }
+        // dB tiles (rows j, columns n) += e_j sum_{p in pass} x[j][p] L[p][n]
+        floatx8 a = frag32(xt + (16 * jb + l16) * ldP + p0 + 8 * g4);
 #pragma unroll
-        for (int qq = 0; qq < PT; ++qq)
-          if (qq == q) dxa[qq] += cj;
-        // Qr's carried share: sum_p x[j][p] (e_j B_j L^T)[p]
-        const int p = p0 + 16 * nh + l16;
+        for (int e = 0; e < 8; ++e) a[e] *= erow_b;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          qx[r] = fmaf(to_f32(xt[(16 * jb + 4 * g4 + r) * ldP + p]), cj[r], qx[r]);
-      }
-      // dB tiles (rows j, columns n) += e_j sum_{p in pass} x[j][p] L[p][n]
-      floatx8 a = frag32(xt + (16 * jb + l16) * ldP + p0 + 8 * g4);
+        for (int qq = 0; qq < NT; ++qq) {
+          const int nt = nh + 2 * qq;
+          if (nt < ntn) {
+            floatx8 bq;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] *= erow_b;
-#pragma unroll
-      for (int qq = 0; qq < NT; ++qq) {
-        const int nt = nh + 2 * qq;
-        if (nt < ntn) {
-          floatx8 bq;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bq[e] = Ls[(8 * g4 + e) * lsN + 16 * nt + l16];
-          dba[qq] = mma(dba[qq], a, bq);
+            for (int e = 0; e < 8; ++e) bq[e] = Ls[(8 * g4 + e) * lsN + 16 * nt + l16];
+            dba[qq] = mma(dba[qq], a, bq);
+          }
         }
       }
-    }
-    // rows j = 16 jb + 4 (lane / 16) + r, column 16 tile + lane % 16
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 16 * jb + 4 * g4 + r;
-      const float qs = sum16(qx[r]);
-      if (l16 == 0) Qc[nh * TB + j] = qs;
-    }
-    // this head's dx 64 columns at a time through LDS where the pair weights
-    // were (U and V: 32 x 72 floats; the last pair is behind the carried
-    // term's barriers), then out as whole-row pieces; dx = dt_j dxa + D dy
-    // with dy read as row pieces alongside, which also gives the dD share
-    float* Xs = Us;
-    for (int pg = 0; 64 * pg < P; ++pg) {
-      if (pg > 0) __syncthreads();                 // the previous group is out
+      // rows j = 16 jb + 4 (lane / 16) + r, column 16 tile + lane % 16
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * jb + 4 * g4 + r;
-#pragma unroll
-        for (int q = 0; q < PT; ++q) {
-          const int pt = nh + 2 * q;
-          if (pt < ntp && pt / 4 == pg) Xs[stage_at(j, 16 * pt + l16 - 64 * pg, 64)] = dxa[q][r];
-        }
+        const float qs = sum16(qx[r]);
+        if (l16 == 0) Qc[nh * TB + j] = qs;
       }
-      __syncthreads();
-      if (pg == 0 && tid < vj)
-        Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + tid] =
-            (Qp[tid] + Qp[TB + tid]) + (Qc[tid] + Qc[TB + tid]);
-      // dx pieces of V values: columns 64 pg .. 64 pg + W - 1 of rows j < vj
-      constexpr int V = 16 / sizeof(T), MAXP = (32 * 64 / V + kBwdThreads - 1) / kBwdThreads;
-      const int W = P - 64 * pg < 64 ? P - 64 * pg : 64;
-      const PieceRows pr(W / V);
-      const unsigned t = fresh_tid(), rs = (unsigned)(H * P) * sizeof(T);
-      const int64_t base = ((b * L + tj0) * H + h) * P + 64 * pg;   // row 0, column 64 pg
+      // this head's dx 64 columns at a time through LDS where the pair weights
+      // were (U and V: 32 x 72 floats; the last pair is behind the carried
+      // term's barriers), then out as whole-row pieces; dx = dt_j dxa + D dy
+      // with dy read as row pieces alongside, which also gives the dD share
+      float* Xs = Us;
+      for (int pg = 0; 64 * pg < P; ++pg) {
+        if (pg > 0) __syncthreads();                 // the previous group is out
 #pragma unroll
-      for (int k = 0; k < MAXP; ++k) {
-        const unsigned e = t + k * kBwdThreads, r = pr.row(e), col = pr.col(e, r) * V;
-        if (e < 32 * pr.kc && (int)r < vj) {
-          const unsigned off = r * rs + col * sizeof(T);
-          const Piece16<T> gv = __builtin_bit_cast(Piece16<T>, load16(at_bytes(dy + base, off)));
-          const Piece16<T> xv = __builtin_bit_cast(
-              Piece16<T>, load16(xt + __umul24(r, (unsigned)ldP) + 64 * pg + col));
-          const float d = dj[r];
-          Piece16<T> o;
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jb + 4 * g4 + r;
 #pragma unroll
-          for (int v4 = 0; v4 < V; v4 += 4) {
-            const float4 s = *reinterpret_cast<const float4*>(Xs + stage_at(r, col + v4, 64));
-            const float sv[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float g = to_f32(gv.v[v4 + u]);
-              o.v[v4 + u] = to_io<T>(fmaf(d, sv[u], Dh * g));
-              dsum = fmaf(g, to_f32(xv.v[v4 + u]), dsum);
-            }
+          for (int q = 0; q < PT; ++q) {
+            const int pt = nh + 2 * q;
+            if (pt < ntp && pt / 4 == pg) Xs[stage_at(j, 16 * pt + l16 - 64 * pg, 64)] = dxa[q][r];
           }
-          store16(at_bytes(dx + base, off), __builtin_bit_cast(vec16, o));
+        }
+        __syncthreads();
+        if (pg == 0 && tid < vj)
+          Qout[(b * H + h) * ldw + (int64_t)c * Q + J * TB + tid] =
+              (Qp[tid] + Qp[TB + tid]) + (Qc[tid] + Qc[TB + tid]);
+        // dx pieces of V values: columns 64 pg .. 64 pg + W - 1 of rows j < vj
+        constexpr int V = 16 / sizeof(T), MAXP = (32 * 64 / V + kBwdThreads - 1) / kBwdThreads;
+        const int W = P - 64 * pg < 64 ? P - 64 * pg : 64;
+        const PieceRows pr(W / V);
+        const unsigned t = fresh_tid(), rs = (unsigned)(H * P) * sizeof(T);
+        const int64_t base = ((b * L + tj0) * H + h) * P + 64 * pg;   // row 0, column 64 pg
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+          const unsigned e = t + k * kBwdThreads, r = pr.row(e), col = pr.col(e, r) * V;
+          if (e < 32 * pr.kc && (int)r < vj) {
+            const unsigned off = r * rs + col * sizeof(T);
+            const Piece16<T> gv = __builtin_bit_cast(Piece16<T>, load16(at_bytes(dy + base, off)));
+            const Piece16<T> xv = __builtin_bit_cast(
+                Piece16<T>, load16(xt + __umul24(r, (unsigned)ldP) + 64 * pg + col));
+            const float d = dj[r];
+            Piece16<T> o;
+#pragma unroll
+            for (int v4 = 0; v4 < V; v4 += 4) {
+              const float4 s = *reinterpret_cast<const float4*>(Xs + stage_at(r, col + v4, 64));
+              const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const float g = to_f32(gv.v[v4 + u]);
+                o.v[v4 + u] = to_io<T>(fmaf(d, sv[u], Dh * g));
+                dsum = fmaf(g, to_f32(xv.v[v4 + u]), dsum);
+              }
+            }
+            store16(at_bytes(dx + base, off), __builtin_bit_cast(vec16, o));
+          }
         }
       }
-    }
-    // this head's share of dD = sum <dy, x> over the block, added to the
-    // wave's slot (each wave its own: no race, a fixed order)
+      // this head's share of dD = sum <dy, x> over the block, added to the
+      // wave's slot (each wave its own: no race, a fixed order)
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, kWave);
-    if (lane == 0) dDw[hh * (kBwdThreads / kWave) + wv] += dsum;
+      for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, kWave);
+      if (lane == 0) dDw[hh * (kBwdThreads / kWave) + wv] += dsum;
     }   // heads of the part
     // the block's dB rows through LDS where the state rows were (every wave
     // is past the last head's carried term), then out as whole-row pieces
