@@ -863,25 +863,27 @@ bwd_source_kernel(const T* __restrict__ x, const T* __restrict__ Bm, const T* __
   }
 }
 
+constexpr int kDtThreads = 512;   // threads of the step-size gradient kernel
+
 // Step-size gradients of one (b, h): the reverse running sum of P - dt Qr over
 // the whole sequence (fp64), then ddt, the (b, h) shares of dA and of the
 // bias gradient, with the step-size preparation's chain rule when XF is set.
-// The sequence is walked in blocks of 2048 tokens from its end.  Each thread
-// takes 8 contiguous tokens of a block (two 16-byte loads per array, the
-// wave's loads contiguous; past L they load zero), a suffix scan of the
+// The sequence is walked in blocks of 2048 tokens from its end.  Each of the
+// 512 threads takes 4 contiguous tokens of a block (one 16-byte load per
+// array, the wave's loads contiguous; past L they load zero), a suffix scan of the
 // threads' sums (within a wave on shuffles, then over the waves) gives each
 // thread the sum of every later token of the block, and a carry, started at
 // <dfinal, final state>, brings the later blocks' total.
 template <bool XF>
-__global__ void __launch_bounds__(kBwdThreads)
+__global__ void __launch_bounds__(kDtThreads)
 bwd_dt_kernel(const float* __restrict__ Pb, const float* __restrict__ Qb,
               const float* __restrict__ dtw, const float* __restrict__ dt_in,
               const float* __restrict__ A, const float* __restrict__ dfinal,
               const float* __restrict__ fin, DtXform xf, float* __restrict__ ddt,
               double* __restrict__ dApart, double* __restrict__ dbpart, int64_t L, int H,
               int64_t PN, int64_t ldw) {
-  constexpr int TPT = 8, NW = kBwdThreads / kWave;
-  constexpr int BLK = kBwdThreads * TPT;
+  constexpr int TPT = 4, NW = kDtThreads / kWave;
+  constexpr int BLK = kDtThreads * TPT;
   __shared__ double wsum[NW];
   __shared__ double red[2][NW];
   const int h = blockIdx.x;
@@ -892,12 +894,14 @@ bwd_dt_kernel(const float* __restrict__ Pb, const float* __restrict__ Qb,
   // <dfinal, final state>: every token's decay lies before the final state
   double kf = 0.0;
   if (dfinal)
-    for (int64_t e = tid; e < PN; e += kBwdThreads) kf += (double)dfinal[bh * PN + e] * fin[bh * PN + e];
+    for (int64_t e = tid; e < PN; e += kDtThreads) kf += (double)dfinal[bh * PN + e] * fin[bh * PN + e];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) kf += __shfl_xor(kf, off, kWave);
   if (lane == 0) red[0][wv] = kf;
   __syncthreads();
-  double carry = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  double carry = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) carry += red[0][w];
 
   const float a = A[h];
   const unsigned row_bytes = (unsigned)L * 4u;
@@ -986,8 +990,14 @@ bwd_dt_kernel(const float* __restrict__ Pb, const float* __restrict__ Qb,
   }
   __syncthreads();
   if (tid == 0) {
-    dApart[bh] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    dbpart[bh] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    double sa = 0.0, sb = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      sa += red[0][w];
+      sb += red[1][w];
+    }
+    dApart[bh] = sa;
+    dbpart[bh] = sb;
   }
 }
 
@@ -1261,10 +1271,10 @@ hipError_t launch_bwd_finish(const float* Pb, const float* Qb, const float* dtw,
                              int64_t N, int64_t T_, int64_t ldw, hipStream_t stream) {
   const dim3 g1((unsigned)H, (unsigned)batch);
   if (xf)
-    hipLaunchKernelGGL(bwd_dt_kernel<true>, g1, dim3(kBwdThreads), 0, stream, Pb, Qb, dtw, dt_in,
+    hipLaunchKernelGGL(bwd_dt_kernel<true>, g1, dim3(kDtThreads), 0, stream, Pb, Qb, dtw, dt_in,
                        A, dfinal, fin, *xf, ddt, dApart, dbpart, L, (int)H, P * N, ldw);
   else
-    hipLaunchKernelGGL(bwd_dt_kernel<false>, g1, dim3(kBwdThreads), 0, stream, Pb, Qb, dtw, dt_in,
+    hipLaunchKernelGGL(bwd_dt_kernel<false>, g1, dim3(kDtThreads), 0, stream, Pb, Qb, dtw, dt_in,
                        A, dfinal, fin, DtXform{nullptr, 0, 0.0f, 0.0f}, ddt, dApart, dbpart, L,
                        (int)H, P * N, ldw);
   hipError_t e = hipGetLastError();
