@@ -283,7 +283,7 @@ constexpr int kBwdLdW = kBwdTB + 4;   // fp32 weight rows: 16-byte aligned fragm
 template <typename T>
 __host__ __device__ inline int bwd_target_bytes(int P, int N) {
   const int pair = bwd_pair_bytes<T>(P, N), st = (32 * (N + 1) * 4 + 15) / 16 * 16;
-  return pair + (pair > st ? pair : st) + kBwdTB * kBwdLdW * 4 + 7 * kBwdTB * 4;
+  return pair + (pair > st ? pair : st) + kBwdTB * kBwdLdW * 4 + 6 * kBwdTB * 4;   // Gi Gj Pp Pc
 }
 
 // Four fp32 weights w[r] of one column of a 16 x 16 accumulator tile (rows
@@ -1104,8 +1104,8 @@ int bwd_part_heads(int64_t batch, int64_t T_, int64_t H, int64_t G) {
 }
 
 // Token-block rows of the per-chunk kernels: 32, or 0 when their LDS plan
-// for this headdim and dstate does not fit.  The plans are ~31 and ~35 KiB at
-// headdim 64 / dstate 128 in bf16, so four workgroups share a CU.
+// for this headdim and dstate does not fit.  The plans are ~34.5 and ~39 KiB
+// at headdim 64 / dstate 128 in bf16, so four workgroups share a CU.
 int bwd_block_rows(int io_bf16, int Q, int64_t P, int64_t N) {
   const int lim = 160 * 1024;
   if (Q % kBwdTB != 0 || P > 256 || N > 256) return 0;
